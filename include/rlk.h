@@ -1,0 +1,161 @@
+/*
+ * rlk.h -- C ABI of the fused linear log-prob for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (RL-Kernel Roadmap (2026), P0.2 "Fused CE LogProb without materializing
+ * logits + fused backward"; RL-Kernel integration roadmap for vime, "Operator Integration
+ * Plan", linear_logp): given hidden states h[N,H], the LM-head weight W[V,H], target ids
+ * y[N], an active mask and a temperature T, compute for every active token t
+ *
+ *     z[t,v]  = (h_t . W_v) / T
+ *     lse[t]  = log sum_v exp(z[t,v])
+ *     logp[t] = z[t, y_t] - lse[t]
+ *
+ * without forming the [N,V] logits.  The backward pass of L = -sum_t mask_t adv_t logp_t
+ * recomputes the logits tile by tile (the roadmap's "chunked backward" that trades compute
+ * for memory) and returns dL/dh and dL/dW.
+ *
+ * Batch invariance (RL-Kernel Roadmap (2026), P0.2 "Batch-Invariant Deterministic
+ * LogProb"; vime roadmap, "Consistency Contract"): a token's logp, lse and dL/dh row are
+ * bit-identical whatever else is in the batch, in whatever order, with whatever padding
+ * and active-mask density, on repeat runs and on any stream, for one build of this library
+ * (rlk_build_info names the build).  No atomics touch results; the vocabulary tiling and
+ * every reduction order are constants of the build, independent of N.  dL/dW is a sum over
+ * tokens: it is deterministic run to run and does not depend on padding or inactive rows.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named h, W, targets, mask, adv, lse, logp, dh, dW, idx, n_active, part_*,
+ *     target_logit and workspace are DEVICE pointers owned by the caller.  Arrays are dense
+ *     and row-major.  h and W must be 16-byte aligned, the workspace 256-byte aligned,
+ *     float and int32 arrays 4-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All work is
+ *     enqueued on it; nothing blocks the host; results are valid once the stream reaches
+ *     that point.  The library never allocates or frees device memory.
+ *   - dtype: RLK_BF16 (h and W hold bf16) or RLK_FP32 (float).  Accumulation is fp32.
+ *   - Every argument check happens on the host before anything is enqueued, so a call
+ *     that returns an error has written nothing.  N == 0 returns RLK_SUCCESS at once.
+ *   - An active token whose target is outside [0, V) gets logp = NaN (checking it on the
+ *     host would need a device-to-host copy); its lse is still correct.
+ *   - Inactive tokens (mask == 0) are never read into the products; their h rows and
+ *     targets may hold anything.  Their logp and lse are 0 and their dL/dh row is 0.
+ *   - Calls are reentrant: the only shared state is read-only device properties.
+ *     Calls that share a workspace must be ordered by the caller (same stream).
+ */
+#ifndef RLK_H_
+#define RLK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RLK_SUCCESS = 0,
+  RLK_ERROR_INVALID_VALUE = 1, /* NULL required pointer, N < 0, H or V <= 0, T not finite or <= 0 */
+  RLK_ERROR_UNSUPPORTED = 2,   /* dtype, H % 64 != 0, misalignment, sizes beyond the limits */
+  RLK_ERROR_WORKSPACE = 3,     /* workspace smaller than the *_workspace_size query */
+  RLK_ERROR_DEVICE = 4         /* a HIP launch or runtime call failed */
+} rlk_status_t;
+
+typedef enum { RLK_BF16 = 0, RLK_FP32 = 1 } rlk_dtype_t;
+
+/* Width, in vocabulary entries, of one partial-statistics column (see
+ * rlk_linear_logp_partials).  A constant of the build. */
+#define RLK_VOCAB_PARTIAL 128
+
+/* Static description of a status code.  Never NULL. */
+const char* rlk_status_string(int status);
+
+/* Build fingerprint: target architecture, compiler, tile constants.  The bitwise
+ * batch-invariance claim holds per fingerprint (vime roadmap, "Consistency Contract",
+ * deterministic operator claim).  Never NULL. */
+const char* rlk_build_info(void);
+
+/* Number of partial-statistics columns for a vocabulary of V entries:
+ * ceil(V / RLK_VOCAB_PARTIAL).  Returns 0 for V <= 0. */
+int64_t rlk_num_vocab_partials(int64_t V);
+
+/* Workspace bytes needed by rlk_linear_logp_fwd / rlk_linear_logp_bwd for N tokens
+ * (an upper bound: it assumes every token is active).  Host-only, no device work. */
+rlk_status_t rlk_linear_logp_fwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
+                                                size_t* bytes);
+rlk_status_t rlk_linear_logp_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
+                                                size_t* bytes);
+
+/* Forward: selected-token log-prob.
+ *   h        [N,H]  dtype     hidden states
+ *   W        [V,H]  dtype     LM-head weight
+ *   targets  [N]    int32     target ids; must lie in [0,V) where mask != 0
+ *   mask     [N]    uint8     0 = inactive (prompt, padding), nonzero = active
+ *   temperature               finite and > 0; the logits are divided by it exactly once
+ *   logp     [N]    float     out: z[t,y_t] - lse[t] at active tokens, 0 elsewhere
+ *   lse      [N]    float     out (may be NULL): log-sum-exp of z[t,:], 0 at inactive tokens;
+ *                             rlk_linear_logp_bwd takes it back
+ *   workspace / workspace_bytes: device scratch of at least
+ *                             rlk_linear_logp_fwd_workspace_size bytes; its contents on
+ *                             entry do not matter.
+ * Equivalent to rlk_compact_active + rlk_linear_logp_partials + rlk_linear_logp_merge on
+ * buffers carved out of the workspace. */
+rlk_status_t rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* targets,
+                                 const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
+                                 float temperature, float* logp, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Backward of L = -sum_t mask_t * adv_t * logp_t (bf16 only).
+ *   h, W, targets, mask, N, H, V, dtype, temperature: exactly as passed to the forward
+ *   adv      [N]    float     per-token advantage (the upstream gradient is -adv_t at
+ *                             active tokens; pass adv = -dL/dlogp for another loss)
+ *   lse      [N]    float     the forward's lse output for the same inputs
+ *   dh       [N,H]  float     out, overwritten: dL/dh; rows of inactive tokens are 0
+ *   dW       [V,H]  float     out, overwritten: dL/dW
+ *   workspace: at least rlk_linear_logp_bwd_workspace_size bytes.
+ * The vocabulary is walked in fixed chunks; per chunk the logits are recomputed on MFMA,
+ * turned into dL/dz (rounded to bf16), and multiplied into dh (accumulated in fp32 in
+ * chunk order) and into the chunk's rows of dW. */
+rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* targets,
+                                 const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
+                                 float temperature, const float* adv, const float* lse,
+                                 float* dh, float* dW, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* ---- Building blocks of the forward (the same kernels rlk_linear_logp_fwd runs).  They
+ * expose the per-vocabulary-slice statistics so that slices computed elsewhere (for
+ * example on other devices holding other vocabulary shards) can be merged in a fixed
+ * order (vime roadmap, linear_logp "RL-Kernel backend": explicit local max, global max,
+ * local sum-exp, global sum-exp, selected target logit and final downcast). */
+
+/* Active-row compaction: idx[0..Na) = the positions t with mask[t] != 0, ascending;
+ * *n_active = Na (device int32).  Also sets target_logit[0..N) = NaN and, when logp/lse
+ * are non-NULL, writes 0 to logp[t] and lse[t] at inactive t (active entries are left for
+ * the merge).  idx [N] int32, n_active [1] int32, target_logit [N] float. */
+rlk_status_t rlk_compact_active(const uint8_t* mask, int64_t N, int32_t* idx, int32_t* n_active,
+                                float* target_logit, float* logp, float* lse, void* stream);
+
+/* Partial statistics of the compacted rows.  For compacted row i < Na (token idx[i]) and
+ * vocabulary column j (entries [128 j, min(V, 128 j + 128))):
+ *   part_max[j*N + i] = max_v  z[idx[i], v] * log2(e)
+ *   part_sum[j*N + i] = sum_v  2^(z[idx[i], v] * log2(e) - part_max[j*N + i])
+ * and target_logit[i] = z[idx[i], y] for the one column that holds y = targets[idx[i]]
+ * (left untouched if y is out of range).  part_max and part_sum are
+ * [rlk_num_vocab_partials(V), N] float, row stride N. */
+rlk_status_t rlk_linear_logp_partials(const void* h, const void* W, const int32_t* targets,
+                                      const int32_t* idx, const int32_t* n_active, int64_t N,
+                                      int64_t H, int64_t V, int dtype, float temperature,
+                                      float* part_max, float* part_sum, float* target_logit,
+                                      void* stream);
+
+/* Fixed-order merge: for i < Na, M = max_j part_max[j*N+i], S = sum_j part_sum[j*N+i] *
+ * 2^(part_max[j*N+i] - M) in one fixed association over j = 0..J-1 (J =
+ * rlk_num_vocab_partials(V)), lse = (M + log2 S) * ln 2, logp = target_logit[i] - lse;
+ * both are written at position idx[i] (lse may be NULL). */
+rlk_status_t rlk_linear_logp_merge(const float* part_max, const float* part_sum,
+                                   const float* target_logit, const int32_t* idx,
+                                   const int32_t* n_active, int64_t N, int64_t V, float* logp,
+                                   float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_H_ */

@@ -1,0 +1,272 @@
+"""Pins of the CPU oracle against what mathematics fixes (no GPU).
+
+Each check is chosen so that a plausible slip in the oracle (a dropped temperature, a
+wrong sign, a transposed operand, an off-by-one target index, a missing max shift, a
+wrong upstream gradient) fails at least one of them.  Non-square shapes (N != H != V)
+are used throughout so that a transposed operand cannot pass by accident."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def _rand(seed, N, H, V, scale_w=None):
+    r = np.random.default_rng(seed)
+    h = r.standard_normal((N, H))
+    W = r.standard_normal((V, H)) * (scale_w if scale_w is not None else 1.0 / math.sqrt(H))
+    y = r.integers(0, V, size=N)
+    return h, W, y
+
+
+def _brute_logp(h, W, y, mask, T):
+    """Pure-Python definition: exact-sum dot products, max-shifted log-sum-exp."""
+    N, V = len(h), len(W)
+    out_lp, out_lse = [], []
+    for t in range(N):
+        if not mask[t]:
+            out_lp.append(0.0)
+            out_lse.append(0.0)
+            continue
+        z = [math.fsum(a * b for a, b in zip(h[t], W[v])) / T for v in range(V)]
+        m = max(z)
+        lse = m + math.log(math.fsum(math.exp(zz - m) for zz in z))
+        out_lp.append(z[y[t]] - lse)
+        out_lse.append(lse)
+    return np.array(out_lp), np.array(out_lse)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7, 1.9])
+def test_brute_force_tiny(T):
+    h, W, y = _rand(1, 6, 7, 11)
+    mask = np.array([1, 1, 0, 1, 0, 1], dtype=np.uint8)
+    lp, lse = oracle.linear_logp(h, W, y, mask, T)
+    blp, blse = _brute_logp(h.tolist(), W.tolist(), y.tolist(), mask.tolist(), T)
+    np.testing.assert_allclose(lp, blp, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
+    assert np.all(lp[mask == 0] == 0) and np.all(lse[mask == 0] == 0)
+
+
+def test_brute_force_large_logits():
+    # logits of size ~ +-1e3: the max shift must keep exp in range
+    h, W, y = _rand(2, 4, 5, 9, scale_w=150.0)
+    mask = np.ones(4, dtype=np.uint8)
+    lp, lse = oracle.linear_logp(h, W, y, mask, 0.5)
+    assert np.all(np.isfinite(lp)) and np.abs(lse).max() > 300
+    blp, blse = _brute_logp(h.tolist(), W.tolist(), y.tolist(), mask.tolist(), 0.5)
+    np.testing.assert_allclose(lp, blp, rtol=1e-13, atol=1e-9)
+    np.testing.assert_allclose(lse, blse, rtol=1e-13, atol=1e-9)
+
+
+def test_library_cross_entropy():
+    # -cross_entropy(z, y) is the selected log-prob (torch, float64, CPU)
+    h, W, y = _rand(3, 200, 48, 3001)
+    T = 0.7
+    mask = np.ones(200, dtype=np.uint8)
+    lp, _ = oracle.linear_logp(h, W, y, mask, T)
+    z = torch.from_numpy(h) @ torch.from_numpy(W).T / T
+    ref = -torch.nn.functional.cross_entropy(z, torch.from_numpy(y), reduction="none")
+    np.testing.assert_allclose(lp, ref.numpy(), rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("V", [1, 7, 1000, 151936])
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_zero_weight_closed_form(V, T):
+    h, _, _ = _rand(4, 5, 64, 1)
+    W = np.zeros((V, 64))
+    y = np.random.default_rng(5).integers(0, V, size=5)
+    lp, lse = oracle.linear_logp(h, W, y, np.ones(5, dtype=np.uint8), T)
+    np.testing.assert_allclose(lp, -math.log(V), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, math.log(V), rtol=0, atol=1e-12)
+
+
+def test_single_token_vocab():
+    h, W, _ = _rand(6, 8, 16, 1, scale_w=3.0)
+    lp, _ = oracle.linear_logp(h, W, np.zeros(8, dtype=np.int64), np.ones(8, np.uint8), 0.9)
+    assert np.all(np.abs(lp) < 1e-15)
+
+
+def test_two_token_vocab_softplus():
+    h, W, y = _rand(7, 9, 13, 2, scale_w=2.0)
+    T = 1.3
+    lp, _ = oracle.linear_logp(h, W, y, np.ones(9, np.uint8), T)
+    for t in range(9):
+        zy = math.fsum(a * b for a, b in zip(h[t], W[y[t]])) / T
+        zo = math.fsum(a * b for a, b in zip(h[t], W[1 - y[t]])) / T
+        d = zo - zy
+        softplus = d + math.log1p(math.exp(-d)) if d > 0 else math.log1p(math.exp(d))
+        assert abs(lp[t] + softplus) < 1e-13
+
+
+def test_normalised_and_nonpositive():
+    h, W, _ = _rand(8, 10, 32, 257)
+    flp = oracle.full_logp(h, W, 0.8)
+    assert np.all(flp <= 0)
+    np.testing.assert_allclose(np.exp(flp).sum(axis=1), 1.0, rtol=0, atol=1e-12)
+
+
+def test_temperature_folds_into_h():
+    h, W, y = _rand(9, 12, 40, 500)
+    m = np.ones(12, np.uint8)
+    a, la = oracle.linear_logp(h, W, y, m, 0.7)
+    b, lb = oracle.linear_logp(h / 0.7, W, y, m, 1.0)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=1e-12)
+    c, _ = oracle.linear_logp(h, W, y, m, 1.0)
+    assert np.abs(a - c).max() > 1e-3  # T really enters
+
+
+def test_vocab_permutation_and_duplicates():
+    h, W, y = _rand(10, 7, 24, 300)
+    m = np.ones(7, np.uint8)
+    lp, _ = oracle.linear_logp(h, W, y, m, 1.1)
+    perm = np.random.default_rng(11).permutation(300)
+    inv = np.argsort(perm)
+    lp2, _ = oracle.linear_logp(h, W[perm], inv[y], m, 1.1)
+    np.testing.assert_allclose(lp, lp2, rtol=0, atol=1e-12)
+    Wd = W.copy()
+    Wd[5] = Wd[17]
+    y5 = np.full(7, 5)
+    y17 = np.full(7, 17)
+    np.testing.assert_array_equal(oracle.linear_logp(h, Wd, y5, m, 1.1)[0],
+                                  oracle.linear_logp(h, Wd, y17, m, 1.1)[0])
+
+
+def test_rows_subset_and_invalid_target():
+    h, W, y = _rand(12, 30, 16, 77)
+    m = (np.arange(30) % 3 != 0).astype(np.uint8)
+    lp, lse = oracle.linear_logp(h, W, y, m, 1.0)
+    rows = [29, 1, 2, 14, 3]
+    lp2, lse2 = oracle.linear_logp(h, W, y, m, 1.0, rows=rows)
+    np.testing.assert_array_equal(lp2, lp[rows])
+    np.testing.assert_array_equal(lse2, lse[rows])
+    yb = y.copy()
+    yb[4] = 77
+    with pytest.raises(ValueError):
+        oracle.linear_logp(h, W, yb, m, 1.0)
+    yb[4] = -1
+    yb[3] = 77  # inactive row: ignored
+    with pytest.raises(ValueError):
+        oracle.linear_logp(h, W, yb, m, 1.0)
+    yb[4] = 0
+    oracle.linear_logp(h, W, yb, m, 1.0)
+
+
+# ------------------------------------------------------------------ backward
+
+def _grad_setup(seed, N=9, H=10, V=23):
+    h, W, y = _rand(seed, N, H, V, scale_w=0.8)
+    r = np.random.default_rng(seed + 100)
+    mask = (r.random(N) < 0.7).astype(np.uint8)
+    mask[0] = 1
+    adv = r.standard_normal(N)
+    return h, W, y, mask, adv
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_grads_match_library_autograd(T):
+    h, W, y, mask, adv = _grad_setup(20, N=17, H=12, V=41)
+    dh, dW = oracle.linear_logp_grads(h, W, y, mask, T, adv)
+    th = torch.tensor(h, requires_grad=True)
+    tW = torch.tensor(W, requires_grad=True)
+    logp = -torch.nn.functional.cross_entropy(th @ tW.T / T, torch.tensor(y), reduction="none")
+    loss = -(torch.tensor(mask, dtype=torch.float64) * torch.tensor(adv) * logp).sum()
+    loss.backward()
+    np.testing.assert_allclose(dh, th.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dW, tW.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_grads_finite_differences():
+    h, W, y, mask, adv = _grad_setup(21, N=4, H=5, V=6)
+    T = 0.85
+    dh, dW = oracle.linear_logp_grads(h, W, y, mask, T, adv)
+
+    def loss(hh, WW):
+        lp, _ = oracle.linear_logp(hh, WW, y, mask, T)
+        return -float(np.sum(mask * adv * lp))
+
+    eps = 1e-6
+    for (i, j) in [(0, 0), (1, 3), (3, 4), (2, 2)]:
+        hp, hm = h.copy(), h.copy()
+        hp[i, j] += eps
+        hm[i, j] -= eps
+        assert abs((loss(hp, W) - loss(hm, W)) / (2 * eps) - dh[i, j]) < 1e-7
+    for (i, j) in [(0, 0), (5, 1), (y[0], 2), (3, 4)]:
+        Wp, Wm = W.copy(), W.copy()
+        Wp[i, j] += eps
+        Wm[i, j] -= eps
+        assert abs((loss(h, Wp) - loss(h, Wm)) / (2 * eps) - dW[i, j]) < 1e-7
+
+
+def test_grad_invariants():
+    h, W, y, mask, adv = _grad_setup(22, N=13, H=8, V=31)
+    dh, dW = oracle.linear_logp_grads(h, W, y, mask, 1.2, adv)
+    # every row of dL/dz sums to zero, so the columns of dW sum to zero
+    np.testing.assert_allclose(dW.sum(axis=0), 0.0, atol=1e-13)
+    assert np.all(dh[mask == 0] == 0)
+    z0h, z0W = oracle.linear_logp_grads(h, W, y, mask, 1.2, np.zeros_like(adv))
+    assert not z0h.any() and not z0W.any()
+
+
+def test_grad_zero_weight_closed_form():
+    h, _, y, mask, adv = _grad_setup(23, N=11, H=6, V=19)
+    T = 0.6
+    V = 19
+    W = np.zeros((V, 6))
+    dh, dW = oracle.linear_logp_grads(h, W, y, mask, T, adv)
+    assert not dh.any()
+    ref = np.zeros((V, 6))
+    for t in range(11):
+        g = -float(mask[t]) * adv[t]
+        for v in range(V):
+            ref[v] += g * ((1.0 if v == y[t] else 0.0) - 1.0 / V) * h[t] / T
+    np.testing.assert_allclose(dW, ref, rtol=0, atol=1e-13)
+
+
+def test_grad_row_variants_match_full():
+    h, W, y, mask, adv = _grad_setup(24, N=40, H=9, V=70)
+    T = 0.9
+    dh, dW = oracle.linear_logp_grads(h, W, y, mask, T, adv)
+    rows = [0, 5, 39, 7]
+    np.testing.assert_allclose(oracle.grad_h_rows(h, W, y, mask, T, adv, rows), dh[rows],
+                               rtol=0, atol=1e-14)
+    vr = [0, 69, int(y[0]), 33]
+    np.testing.assert_allclose(oracle.grad_W_rows(h, W, y, mask, T, adv, vr), dW[vr],
+                               rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------------ sampler
+
+def test_sampler_inverse_cdf_walk():
+    h, W, _ = _rand(30, 8, 5, 6, scale_w=1.5)
+    T = 0.9
+    r = np.random.default_rng(31)
+    for t in range(8):
+        us = r.random(25)
+        got = oracle.sample_targets(np.repeat(h[t:t + 1], 25, axis=0), W, T, us)
+        z = [math.fsum(a * b for a, b in zip(h[t], W[v])) / T for v in range(6)]
+        m = max(z)
+        e = [math.exp(zz - m) for zz in z]
+        p = [x / math.fsum(e) for x in e]
+        for k, u in enumerate(us):
+            acc, pick = 0.0, 5
+            for v in range(6):
+                acc += p[v]
+                if acc > u:
+                    pick = v
+                    break
+            assert got[k] == pick
+
+
+def test_sampler_frequencies():
+    from scipy.stats import chisquare
+    h, W, _ = _rand(32, 1, 4, 8, scale_w=1.0)
+    T = 0.7
+    n = 40000
+    u = np.random.default_rng(33).random(n)
+    ys = oracle.sample_targets(np.repeat(h, n, axis=0), W, T, u)
+    p = np.exp(oracle.full_logp(h, W, T)[0])
+    counts = np.bincount(ys, minlength=8)
+    assert chisquare(counts, p * n).pvalue > 1e-4
