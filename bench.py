@@ -1,0 +1,229 @@
+"""Benchmark of the fused linear log-prob on one MI355X.
+
+One step is one pass of the whole path over one batch: active-row compaction, the vocab
+tile kernel with its fused softmax-statistics epilogue, the fixed-order merge (the
+forward), then the chunked backward of L = -sum_t mask_t adv_t logp_t.  The default
+workload is the Qwen3-8B LM-head shape with N=16384 tokens in 64 packed sequences (~60%
+active), T=0.7 and targets sampled from the oracle softmax (stored under tests/golden),
+with per-sequence advantages ~N(0,1) for the backward.  Inputs are seeded synthetic data,
+resident in HBM before the timed region.
+
+Prints one JSON line.  `value` is active tokens per second for the whole step; the
+forward alone, the backward alone, and the roofline of the dominant kernel (the forward
+tile kernel, timed with HIP events on the stream it runs on) are reported beside it, and
+the float64 CPU oracle is timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "active tokens/sec + % bf16 MFMA peak, fused linear logp fwd (and fwd+bwd)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+WORKLOADS = {
+    # name: (config id, use stored sampled targets)
+    "qwen3-8b-head-N16384-T0.7": (3, True),
+    "qwen3-8b-head-N4096-fwdbwd": (5, False),
+    "qwen3-8b-head-N2048": (2, False),
+    "large-hidden-head-N8192-H7168": (4, False),
+}
+DEFAULT_WORKLOAD = "qwen3-8b-head-N16384-T0.7"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    p.add_argument("--mode", default="fwdbwd", choices=["fwd", "fwdbwd"])
+    p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle sample (0 disables it)")
+    return p.parse_args()
+
+
+def make_workload(name):
+    import workloads as wl
+    cfg, sampled = WORKLOADS[name]
+    w = wl.make(cfg)
+    if sampled:
+        t = np.load(os.path.join(ROOT, "tests", "golden", "cfg3_sampled_targets.npy"))
+        w = wl.with_targets(w, t)
+    return w
+
+
+def cpu_baseline(w, mode, target_s):
+    """Time the float64 oracle on a bounded sample of active tokens of the same workload."""
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    act = np.nonzero(w.mask)[0]
+    W64 = wl.as_f64(w.W)
+    h64 = wl.as_f64(w.h[act])
+    m = np.ones(act.size, dtype=np.uint8)
+    y = w.targets[act]
+    adv = w.adv[act]
+    # calibrate on 16 tokens, then run a sample sized for ~target_s seconds
+    k = 16
+    t0 = time.perf_counter()
+    if mode == "fwd":
+        oracle.linear_logp(h64[:k], W64, y[:k], m[:k], w.T)
+    else:
+        oracle.linear_logp(h64[:k], W64, y[:k], m[:k], w.T)
+        oracle.linear_logp_grads(h64[:k], W64, y[:k], m[:k], w.T, adv[:k])
+    per = (time.perf_counter() - t0) / k
+    n = int(min(act.size, max(k, target_s / max(per, 1e-9))))
+    n = max(k, (n // 16) * 16)
+    t0 = time.perf_counter()
+    if mode == "fwd":
+        oracle.linear_logp(h64[:n], W64, y[:n], m[:n], w.T)
+    else:
+        oracle.linear_logp(h64[:n], W64, y[:n], m[:n], w.T)
+        oracle.linear_logp_grads(h64[:n], W64, y[:n], m[:n], w.T, adv[:n])
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "active tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} active tokens of the same workload scored as one batch "
+                      f"({'forward' if mode == 'fwd' else 'forward + dL/dh + dL/dW'}, float64, "
+                      f"numpy/OpenBLAS), {dt:.1f} s"}
+
+
+def traffic_for(kernel_src_files, name):
+    """HBM bytes per launch measured by rocprofv3 counters, if the kernel sources are
+    unchanged since the measurement (profiles/<name>.traffic.json)."""
+    path = os.path.join(ROOT, "profiles", f"{name}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in kernel_src_files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def upload(w, dev):
+    import torch
+
+    def mat(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    return (mat(w.h), mat(w.W), torch.from_numpy(w.targets).to(dev),
+            torch.from_numpy(w.mask).to(dev), torch.from_numpy(w.adv).to(dev))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the path has no "
+                                   "multi-GPU mode (run with --gpus 1)"}))
+        sys.exit(2)
+    import torch
+    import linear_selected_token_amd as rlk
+
+    dev = torch.device("cuda", 0)
+    w = make_workload(args.workload)
+    N, H, V, T = w.N, w.H, w.V, w.T
+    Na = w.n_active
+    h, W, targets, mask, adv = upload(w, dev)
+    bufs = rlk.ForwardBuffers(N, V, dev)
+    do_bwd = args.mode == "fwdbwd"
+    if do_bwd:
+        bws = torch.empty(rlk.bwd_workspace_bytes(N, H, V, 0), dtype=torch.uint8, device=dev)
+        dh = torch.empty((N, H), dtype=torch.float32, device=dev)
+        dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+
+    def step(ev):
+        ev[0].record()
+        rlk.rlk_compact_active(mask, bufs.idx, bufs.n_active, bufs.target_logit, bufs.logp,
+                               bufs.lse)
+        ev[1].record()
+        rlk.rlk_linear_logp_partials(h, W, targets, bufs.idx, bufs.n_active, T, bufs.part_max,
+                                     bufs.part_sum, bufs.target_logit)
+        ev[2].record()
+        rlk.rlk_linear_logp_merge(bufs.part_max, bufs.part_sum, bufs.target_logit, bufs.idx,
+                                  bufs.n_active, N, V, bufs.logp, bufs.lse)
+        ev[3].record()
+        if do_bwd:
+            rlk.rlk_linear_logp_bwd(h, W, targets, mask, T, adv, bufs.lse, workspace=bws, dh=dh,
+                                    dW=dW)
+        ev[4].record()
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    for _ in range(args.warmup):
+        step(events())
+    torch.cuda.synchronize()
+    evs = [events() for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for ev in evs:
+        step(ev)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / args.steps
+    tile_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
+    bwd_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs])) if do_bwd else 0.0
+
+    fwd_flop = 2.0 * Na * H * V
+    bwd_flop = 6.0 * Na * H * V   # recompute + dL/dh + dL/dW, as executed
+    tile_tflops = fwd_flop / (tile_ms * 1e-3) / 1e12
+    srcs = ["linear_selected_token_amd/csrc/fwd.hip", "linear_selected_token_amd/csrc/common.hpp"]
+    roofline = {"bound": "mfma", "kernel": "fwd_tiles_kernel<bf16>",
+                "achieved": round(tile_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tile_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(srcs, "fwd_tiles_kernel"),
+                "algorithmic_flop_per_launch": fwd_flop, "avg_launch_ms": round(tile_ms, 4)}
+    out = {
+        "metric": METRIC,
+        "value": round(Na / (ms * 1e-3), 1),
+        "unit": "active tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded h~N(0,1), W~N(0,1/H) rounded to bf16, packed "
+                "prompt/response sequences",
+        "config": {"workload": args.workload, "mode": args.mode, "N": N, "H": H, "V": V,
+                   "T": T, "n_active": Na, "parallelism": "none (1 GPU)"},
+        "fwd": {"ms": round(fwd_ms, 4), "active_tokens_per_s": round(Na / (fwd_ms * 1e-3), 1),
+                "tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
+                "mfma_frac": round(fwd_flop / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "roofline": roofline,
+    }
+    if do_bwd:
+        out["bwd"] = {"ms": round(bwd_ms, 4),
+                      "tflops_executed": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
+                      "mfma_frac": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        out["fwd_bwd_tflops_executed"] = round((fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12, 2)
+    if args.cpu_baseline_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.mode, args.cpu_baseline_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,21 @@
+"""Fused linear log-prob for AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library ``librlk.so`` (C ABI in include/rlk.h); this package
+binds it.  Importing it requires the built library: there is no other path."""
+from ._lib import RlkError, build_info, lib, status_string  # noqa: F401
+
+lib()  # fail loudly at import when the library is missing
+
+from .ops import (  # noqa: E402,F401
+    ForwardBuffers,
+    LinearLogp,
+    bwd_workspace_bytes,
+    fwd_workspace_bytes,
+    linear_logp,
+    num_vocab_partials,
+    rlk_compact_active,
+    rlk_linear_logp_bwd,
+    rlk_linear_logp_fwd,
+    rlk_linear_logp_merge,
+    rlk_linear_logp_partials,
+)

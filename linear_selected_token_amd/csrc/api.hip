@@ -1,0 +1,214 @@
+// C ABI of the library: argument checks, workspace carving and kernel launches on the
+// caller's stream.  The operation and its contract are described in include/rlk.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+
+#include "kernels.hpp"
+#include "rlk.h"
+#include "validate.hpp"
+
+namespace rlk {
+namespace {
+
+// Compute units of each device, read once (the only state the library keeps).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+hipError_t persistent_grid(int* grid) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int cus = (dev >= 0 && dev < kMaxDevices) ? g_cus[dev].load(std::memory_order_relaxed) : 0;
+  if (cus <= 0) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  // one work-group per CU; a multiple of 8 keeps the XCD-aware tile order exact
+  *grid = cus >= 8 ? (cus & ~7) : cus;
+  return hipSuccess;
+}
+
+inline rlk_status_t dev_status(hipError_t e) { return e == hipSuccess ? RLK_SUCCESS : RLK_ERROR_DEVICE; }
+
+template <class T>
+T* carve(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+const char* build_info_string() {
+  static const char* s =
+      "rlk linear_logp | arch gfx950 | compiler " __clang_version__
+      " | tile 256x256, K stage 128 B, 4 wave64 x 128x128, mfma 32x32x16 bf16 / 32x32x2 f32"
+      " | vocab partial 128 | merge 8 strided slices + fixed tree | bwd chunk 8192";
+  return s;
+}
+
+}  // namespace
+}  // namespace rlk
+
+using namespace rlk;
+
+extern "C" {
+
+const char* rlk_status_string(int status) {
+  switch (status) {
+    case RLK_SUCCESS: return "RLK_SUCCESS";
+    case RLK_ERROR_INVALID_VALUE: return "RLK_ERROR_INVALID_VALUE: invalid argument";
+    case RLK_ERROR_UNSUPPORTED: return "RLK_ERROR_UNSUPPORTED: unsupported dtype, shape or alignment";
+    case RLK_ERROR_WORKSPACE: return "RLK_ERROR_WORKSPACE: workspace too small";
+    case RLK_ERROR_DEVICE: return "RLK_ERROR_DEVICE: HIP launch or runtime failure";
+    default: return "unknown rlk status";
+  }
+}
+
+const char* rlk_build_info(void) { return build_info_string(); }
+
+int64_t rlk_num_vocab_partials(int64_t V) { return num_partials(V); }
+
+rlk_status_t rlk_linear_logp_fwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
+                                                size_t* bytes) {
+  if (!bytes) return RLK_ERROR_INVALID_VALUE;
+  rlk_status_t s = check_shape(N, H, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  *bytes = fwd_layout(N, V).total;
+  return RLK_SUCCESS;
+}
+
+rlk_status_t rlk_linear_logp_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
+                                                size_t* bytes) {
+  if (!bytes) return RLK_ERROR_INVALID_VALUE;
+  rlk_status_t s = check_shape(N, H, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  if (dtype != RLK_BF16 || H % 256 != 0) return RLK_ERROR_UNSUPPORTED;
+  *bytes = bwd_layout(N, H).total;
+  return RLK_SUCCESS;
+}
+
+rlk_status_t rlk_compact_active(const uint8_t* mask, int64_t N, int32_t* idx, int32_t* n_active,
+                                float* target_logit, float* logp, float* lse, void* stream) {
+  if (N < 0) return RLK_ERROR_INVALID_VALUE;
+  if (N > kMaxTokens) return RLK_ERROR_UNSUPPORTED;
+  if (!n_active) return RLK_ERROR_INVALID_VALUE;
+  if (N > 0 && (!mask || !idx)) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(idx, 4) || !aligned(n_active, 4) || (target_logit && !aligned(target_logit, 4)) ||
+      (logp && !aligned(logp, 4)) || (lse && !aligned(lse, 4)))
+    return RLK_ERROR_UNSUPPORTED;
+  CompactArgs a{mask, idx, n_active, target_logit, logp, lse, (int)N};
+  return dev_status(launch_compact(a, static_cast<hipStream_t>(stream)));
+}
+
+rlk_status_t rlk_linear_logp_partials(const void* h, const void* W, const int32_t* targets,
+                                      const int32_t* idx, const int32_t* n_active, int64_t N,
+                                      int64_t H, int64_t V, int dtype, float temperature,
+                                      float* part_max, float* part_sum, float* target_logit,
+                                      void* stream) {
+  rlk_status_t s = check_shape(N, H, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  s = check_temperature(temperature);
+  if (s != RLK_SUCCESS) return s;
+  if (N == 0) return RLK_SUCCESS;
+  if (!h || !W || !targets || !idx || !n_active || !part_max || !part_sum || !target_logit)
+    return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(targets, 4) || !aligned(idx, 4) ||
+      !aligned(n_active, 4) || !aligned(part_max, 4) || !aligned(part_sum, 4) ||
+      !aligned(target_logit, 4))
+    return RLK_ERROR_UNSUPPORTED;
+  int grid = 0;
+  hipError_t e = persistent_grid(&grid);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  FwdTileArgs a{h, W, targets, idx, n_active, (int)N, (int)H, (int)V,
+                (float)(1.0 / (double)temperature), part_max, part_sum, target_logit};
+  return dev_status(launch_fwd_tiles(a, dtype == RLK_BF16, grid, static_cast<hipStream_t>(stream)));
+}
+
+rlk_status_t rlk_linear_logp_merge(const float* part_max, const float* part_sum,
+                                   const float* target_logit, const int32_t* idx,
+                                   const int32_t* n_active, int64_t N, int64_t V, float* logp,
+                                   float* lse, void* stream) {
+  if (N < 0 || V <= 0) return RLK_ERROR_INVALID_VALUE;
+  if (N > kMaxTokens || V > kMaxVocab) return RLK_ERROR_UNSUPPORTED;
+  if (N == 0) return RLK_SUCCESS;
+  if (!part_max || !part_sum || !target_logit || !idx || !n_active || !logp)
+    return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(part_max, 4) || !aligned(part_sum, 4) || !aligned(target_logit, 4) ||
+      !aligned(idx, 4) || !aligned(n_active, 4) || !aligned(logp, 4) || (lse && !aligned(lse, 4)))
+    return RLK_ERROR_UNSUPPORTED;
+  MergeArgs a{part_max, part_sum, target_logit, idx, n_active, (int)N, (int)V, logp, lse};
+  return dev_status(launch_fwd_merge(a, static_cast<hipStream_t>(stream)));
+}
+
+rlk_status_t rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* targets,
+                                 const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
+                                 float temperature, float* logp, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  rlk_status_t s = check_fwd(h, W, targets, mask, N, H, V, dtype, temperature, logp, lse,
+                             workspace, workspace_bytes);
+  if (s != RLK_SUCCESS || N == 0) return s;
+  const FwdLayout L = fwd_layout(N, V);
+  int32_t* idx = carve<int32_t>(workspace, L.idx);
+  int32_t* na = carve<int32_t>(workspace, L.n_active);
+  float* zy = carve<float>(workspace, L.target_logit);
+  float* pm = carve<float>(workspace, L.part_max);
+  float* ps = carve<float>(workspace, L.part_sum);
+  s = rlk_compact_active(mask, N, idx, na, zy, logp, lse, stream);
+  if (s != RLK_SUCCESS) return s;
+  s = rlk_linear_logp_partials(h, W, targets, idx, na, N, H, V, dtype, temperature, pm, ps, zy,
+                               stream);
+  if (s != RLK_SUCCESS) return s;
+  return rlk_linear_logp_merge(pm, ps, zy, idx, na, N, V, logp, lse, stream);
+}
+
+rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* targets,
+                                 const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
+                                 float temperature, const float* adv, const float* lse,
+                                 float* dh, float* dW, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  rlk_status_t s = check_bwd(h, W, targets, mask, N, H, V, dtype, temperature, adv, lse, dh, dW,
+                             workspace, workspace_bytes);
+  if (s != RLK_SUCCESS) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (N == 0) {
+    // nothing to differentiate: dL/dW = 0 (a fill kernel, not a memset node)
+    return dev_status(launch_zero(dW, (size_t)V * (size_t)H, st));
+  }
+  int grid = 0;
+  if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
+  const BwdLayout L = bwd_layout(N, H);
+  BwdArgs a{};
+  a.h = h;
+  a.W = W;
+  a.targets = targets;
+  a.adv = adv;
+  a.lse = lse;
+  int32_t* idx = carve<int32_t>(workspace, L.idx);
+  int32_t* na = carve<int32_t>(workspace, L.n_active);
+  a.idx = idx;
+  a.n_active = na;
+  a.N = (int)N;
+  a.H = (int)H;
+  a.V = (int)V;
+  a.Npad = (int)bwd_npad(N);
+  a.inv_t = (float)(1.0 / (double)temperature);
+  a.dh = dh;
+  a.dW = dW;
+  a.hT = carve<uint16_t>(workspace, L.hT);
+  a.Wt = carve<uint16_t>(workspace, L.Wt);
+  a.Gv = carve<uint16_t>(workspace, L.Gv);
+  a.Gt = carve<uint16_t>(workspace, L.Gt);
+  CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
+  hipError_t e = launch_compact(c, st);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  e = launch_bwd_prepare(a, st);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  const int nchunks = (int)((V + kBwdChunk - 1) / kBwdChunk);
+  for (int c0 = 0; c0 < nchunks; ++c0) {
+    e = launch_bwd_chunk(a, c0, grid, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  }
+  return RLK_SUCCESS;
+}
+
+}  // extern "C"

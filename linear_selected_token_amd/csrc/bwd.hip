@@ -1,0 +1,287 @@
+// Backward kernels of the fused linear log-prob: L = -sum_t mask_t adv_t logp_t.
+//
+// The backward recomputes the logits tile by tile instead of storing them (RL-Kernel
+// Roadmap (2026), P0.2: "the backward path recomputes tiles to trade compute for memory
+// instead of storing full logits/probabilities"); the only saved state is lse[N].  With
+// g_t = -adv_t at active tokens and p = softmax(z_t):
+//
+//   dL/dz[t,v] = g_t (delta(v, y_t) - p[t,v])
+//   dL/dh_t    = (1/T) sum_v dL/dz[t,v] W_v
+//   dL/dW_v    = (1/T) sum_t dL/dz[t,v] h_t
+//
+// The vocabulary is walked in chunks of kBwdChunk entries, in ascending order.  Per chunk:
+//   wt_chunk     W rows of the chunk, transposed to [H, chunk] (zero past V);
+//   dlogits      the forward tile GEMM again, epilogue G = (g_t / T)(delta - p) rounded to
+//                bf16 and stored token-major (Gv) and vocabulary-major (Gt);
+//   dh_chunk     dh[idx] += Gv Wt^T  (K = the chunk, fp32 accumulation, added to dh in
+//                chunk order, so a token's dh row is batch-invariant);
+//   dw_chunk     dW[chunk rows] = Gt hT^T  (K = the active tokens in ascending order).
+// Before the first chunk, bwd_prepare zeroes dh and writes hT = compacted h transposed.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace rlk {
+
+namespace {
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- 64 x 64 transposes
+
+// hT[k][i] = h[idx[i]][k] for i < Na, 0 for Na <= i < Npad.  Grid (Npad/64, H/64).
+__global__ __launch_bounds__(256) void transpose_h_kernel(BwdArgs a) {
+  __shared__ uint16_t t[64][65];
+  const int Na = *a.n_active;
+  const int i0 = blockIdx.x * 64;
+  const int k0 = blockIdx.y * 64;
+  const uint16_t* h = static_cast<const uint16_t*>(a.h);
+  for (int e = threadIdx.x; e < 4096; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    const int i = i0 + r;
+    t[r][c] = i < Na ? h[(size_t)a.idx[i] * a.H + k0 + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 4096; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    a.hT[(size_t)(k0 + r) * a.Npad + i0 + c] = t[c][r];
+  }
+}
+
+// Wt[k][v] = W[c0 + v][k] for c0 + v < V, else 0.  Grid (kBwdChunk/64, H/64).
+__global__ __launch_bounds__(256) void transpose_w_kernel(BwdArgs a, int c0) {
+  __shared__ uint16_t t[64][65];
+  const int v0 = blockIdx.x * 64;
+  const int k0 = blockIdx.y * 64;
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  for (int e = threadIdx.x; e < 4096; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    const int v = c0 + v0 + r;
+    t[r][c] = v < a.V ? W[(size_t)v * a.H + k0 + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 4096; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    a.Wt[(size_t)(k0 + r) * kBwdChunk + v0 + c] = t[c][r];
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float* p, size_t n) {
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256)
+    p[e] = 0.f;
+}
+
+// ---------------------------------------------------------------- dlogits of one chunk
+
+__global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(BwdArgs a, int c0) {
+  __shared__ TileSmem sm;
+  const int Na = *a.n_active;
+  const int vc = min(kBwdChunk, a.V - c0);  // vocabulary entries in this chunk
+  const int nTokTiles = (Na + kTile - 1) / kTile;
+  const int nVocTiles = (vc + kTile - 1) / kTile;
+  const int nTiles = nTokTiles * nVocTiles;
+  const int band = nTokTiles < 8 ? nTokTiles : 8;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const size_t row_bytes = (size_t)a.H * 2;
+  const int nk = (int)(row_bytes / kStageBytes);
+  const float c2 = a.inv_t * kLog2e;
+
+  for (int round = 0;; ++round) {
+    const int u = virtual_tile(round, blockIdx.x, gridDim.x);
+    if (u >= nTiles) break;
+    int vt, tt;
+    tile_coords(u, nVocTiles, nTokTiles, band, vt, tt);
+    const int vbase = c0 + vt * kTile;
+    const int tbase = tt * kTile;
+
+    const uint8_t* a_src[kLoadsPerThread];
+    const uint8_t* b_src[kLoadsPerThread];
+#pragma unroll
+    for (int q = 0; q < kLoadsPerThread; ++q) {
+      const int r = load_row(q, tid);
+      const int v = min(vbase + r, a.V - 1);
+      const int t = a.idx[min(tbase + r, Na - 1)];
+      a_src[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * load_chunk(tid);
+      b_src[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * load_chunk(tid);
+    }
+    const int wv = (wave & 1) * kWaveTile;
+    const int wt = (wave >> 1) * kWaveTile;
+    int tok_i[4], tgt[4];
+    float lse2[4], gs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tok_i[j] = tbase + wt + acc_col(j, lane);
+      const bool ok = tok_i[j] < Na;
+      const int t = ok ? a.idx[tok_i[j]] : 0;
+      tgt[j] = ok ? a.targets[t] : -1;
+      lse2[j] = ok ? a.lse[t] * kLog2e : 0.f;
+      gs[j] = ok ? -a.adv[t] * a.inv_t : 0.f;
+    }
+
+    Acc acc;
+    zero_acc(acc);
+    mainloop<true>(sm, a_src, b_src, nk, acc);
+
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ti = tok_i[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint16_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const int v = vbase + wv + acc_row(i, r, lane);
+            const float p = __builtin_amdgcn_exp2f(acc.c[i][j][r] * c2 - lse2[j]);
+            float G = gs[j] * ((v == tgt[j] ? 1.f : 0.f) - p);
+            if (v >= a.V) G = 0.f;
+            o[e] = to_bf16(G);
+          }
+          const int vl = vbase - c0 + wv + acc_row(i, 4 * g, lane);  // first of 4 consecutive
+          u32x2 pk;
+          pk[0] = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+          pk[1] = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+          *reinterpret_cast<u32x2*>(a.Gv + (size_t)ti * kBwdChunk + vl) = pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a.Gt[(size_t)(vl + e) * a.Npad + ti] = o[e];
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dh += Gv Wt^T
+
+__global__ __launch_bounds__(kThreads, 1) void dh_chunk_kernel(BwdArgs a, int c0) {
+  __shared__ TileSmem sm;
+  const int Na = *a.n_active;
+  const int vc = min(kBwdChunk, a.V - c0);
+  const int kc = (vc + 63) & ~63;  // K extent (zero columns past V)
+  const int nTokTiles = (Na + kTile - 1) / kTile;
+  const int nHTiles = a.H / kTile;
+  const int nTiles = nTokTiles * nHTiles;
+  const int band = nHTiles < 8 ? nHTiles : 8;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const size_t row_bytes = (size_t)kBwdChunk * 2;
+  const int nk = kc * 2 / kStageBytes;
+
+  for (int round = 0;; ++round) {
+    const int u = virtual_tile(round, blockIdx.x, gridDim.x);
+    if (u >= nTiles) break;
+    int tt, ht;
+    tile_coords(u, nTokTiles, nHTiles, band, tt, ht);
+    const int tbase = tt * kTile;
+    const int hbase = ht * kTile;
+    const uint8_t* a_src[kLoadsPerThread];
+    const uint8_t* b_src[kLoadsPerThread];
+#pragma unroll
+    for (int q = 0; q < kLoadsPerThread; ++q) {
+      const int r = load_row(q, tid);
+      a_src[q] = reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)(tbase + r) * row_bytes + 16 * load_chunk(tid);
+      b_src[q] = reinterpret_cast<const uint8_t*>(a.Wt) + (size_t)(hbase + r) * row_bytes + 16 * load_chunk(tid);
+    }
+    Acc acc;
+    zero_acc(acc);
+    mainloop<true>(sm, a_src, b_src, nk, acc);
+
+    const int wa = (wave & 1) * kWaveTile;
+    const int wb = (wave >> 1) * kWaveTile;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = tbase + wa + acc_row(i, r, lane);
+        if (m < Na) {
+          float* row = a.dh + (size_t)a.idx[m] * a.H + hbase + wb;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) row[acc_col(j, lane)] += acc.c[i][j][r];
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dW rows = Gt hT^T
+
+__global__ __launch_bounds__(kThreads, 1) void dw_chunk_kernel(BwdArgs a, int c0) {
+  __shared__ TileSmem sm;
+  const int Na = *a.n_active;
+  const int vc = min(kBwdChunk, a.V - c0);
+  const int nVocTiles = (vc + kTile - 1) / kTile;
+  const int nHTiles = a.H / kTile;
+  const int nTiles = nVocTiles * nHTiles;
+  const int band = nHTiles < 8 ? nHTiles : 8;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const size_t row_bytes = (size_t)a.Npad * 2;
+  const int nk = ((Na + 63) & ~63) * 2 / kStageBytes;
+
+  for (int round = 0;; ++round) {
+    const int u = virtual_tile(round, blockIdx.x, gridDim.x);
+    if (u >= nTiles) break;
+    int vt, ht;
+    tile_coords(u, nVocTiles, nHTiles, band, vt, ht);
+    const int vbase = vt * kTile;  // within the chunk
+    const int hbase = ht * kTile;
+    const uint8_t* a_src[kLoadsPerThread];
+    const uint8_t* b_src[kLoadsPerThread];
+#pragma unroll
+    for (int q = 0; q < kLoadsPerThread; ++q) {
+      const int r = load_row(q, tid);
+      a_src[q] = reinterpret_cast<const uint8_t*>(a.Gt) + (size_t)(vbase + r) * row_bytes + 16 * load_chunk(tid);
+      b_src[q] = reinterpret_cast<const uint8_t*>(a.hT) + (size_t)(hbase + r) * row_bytes + 16 * load_chunk(tid);
+    }
+    Acc acc;
+    zero_acc(acc);
+    mainloop<true>(sm, a_src, b_src, nk, acc);
+
+    const int wa = (wave & 1) * kWaveTile;
+    const int wb = (wave >> 1) * kWaveTile;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = c0 + vbase + wa + acc_row(i, r, lane);
+        if (v < a.V) {
+          float* row = a.dW + (size_t)v * a.H + hbase + wb;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) row[acc_col(j, lane)] = acc.c[i][j][r];
+        }
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_zero(float* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int zb = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream) {
+  hipError_t e = launch_zero(a.dh, (size_t)a.N * a.H, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(transpose_h_kernel, dim3(a.Npad / 64, a.H / 64), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t stream) {
+  const int c0 = chunk * kBwdChunk;
+  hipLaunchKernelGGL(transpose_w_kernel, dim3(kBwdChunk / 64, a.H / 64), dim3(256), 0, stream, a, c0);
+  hipLaunchKernelGGL(dlogits_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  hipLaunchKernelGGL(dh_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  hipLaunchKernelGGL(dw_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  return hipGetLastError();
+}
+
+}  // namespace rlk

@@ -1,0 +1,195 @@
+// Forward kernels of the fused linear log-prob.
+//
+// The forward streams the vocabulary in tiles and keeps only per-row softmax statistics,
+// never the [N, V] logits (RL-Kernel Roadmap (2026), P0.2, "Fused CE LogProb without
+// materializing logits": the forward path streams vocab blocks with online softmax).
+//
+//   fwd_tiles: persistent grid over (vocabulary tile x token tile) pairs.  Each 256 x 256
+//              tile is z = W_tile h_tile^T on bf16 (or fp32) MFMA with fp32 accumulation over
+//              the whole hidden dimension in one fixed K order.  Its epilogue folds 1/T and
+//              log2(e) into one multiply, and for every token and every 128-entry vocabulary
+//              column writes the column maximum and the sum of 2^(z*log2e - max).  The tile
+//              that holds a token's target also writes that target logit.
+//   fwd_merge: per token, combines the columns in one fixed order into lse and logp.
+//
+// Batch invariance (RL-Kernel Roadmap (2026), P0.2, "Batch-Invariant Deterministic
+// LogProb": no atomics, fixed reduction topology and block partition, per-row reduction
+// independent of the batch): the vocabulary tiling is a build constant; a token's column
+// statistics depend only on its own h row, the W tile and the fixed K order; the lane and
+// register order of every reduction is the same for every token position; the merge walks
+// the columns in the same fixed association for every token.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace rlk {
+
+namespace {
+
+template <bool kBF16>
+__global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
+  __shared__ TileSmem sm;
+  const int Na = *a.n_active;
+  const int nTokTiles = (Na + kTile - 1) / kTile;
+  const int nVocTiles = (a.V + kTile - 1) / kTile;
+  const int nTiles = nTokTiles * nVocTiles;
+  const int band = nTokTiles < 8 ? nTokTiles : 8;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int elt = kBF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)a.H * elt;
+  const int nk = (int)(row_bytes / kStageBytes);
+  const float c2 = a.inv_t * kLog2e;
+
+  for (int round = 0;; ++round) {
+    const int u = virtual_tile(round, blockIdx.x, gridDim.x);
+    if (u >= nTiles) break;
+    int vt, tt;
+    tile_coords(u, nVocTiles, nTokTiles, band, vt, tt);
+    const int vbase = vt * kTile;
+    const int tbase = tt * kTile;
+
+    const uint8_t* a_src[kLoadsPerThread];
+    const uint8_t* b_src[kLoadsPerThread];
+#pragma unroll
+    for (int q = 0; q < kLoadsPerThread; ++q) {
+      const int r = load_row(q, tid);
+      const int v = min(vbase + r, a.V - 1);
+      const int i = min(tbase + r, Na - 1);
+      const int t = a.idx[i];
+      a_src[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * load_chunk(tid);
+      b_src[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * load_chunk(tid);
+    }
+
+    // this lane's four tokens (one per 32-column block of its wave quadrant)
+    const int wv = (wave & 1) * kWaveTile;  // vocabulary offset of the quadrant
+    const int wt = (wave >> 1) * kWaveTile; // token offset of the quadrant
+    int tok_i[4];
+    int tgt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tok_i[j] = tbase + wt + acc_col(j, lane);
+      tgt[j] = tok_i[j] < Na ? a.targets[a.idx[tok_i[j]]] : -1;
+    }
+
+    Acc acc;
+    zero_acc(acc);
+    mainloop<kBF16>(sm, a_src, b_src, nk, acc);
+
+    // ---- epilogue: per token, statistics of this wave's 128 vocabulary entries
+    const int vq = vbase + wv;          // first vocabulary entry of the quadrant
+    const int col = vq / kVocabPartial; // partial column (kWaveTile == kVocabPartial)
+    if (vq >= a.V) continue;            // quadrant entirely past the vocabulary
+    const bool tail = vq + kWaveTile > a.V;
+    const int half4 = 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // target capture (rare: only when some lane's target falls in this quadrant)
+      const int d = tgt[j] - vq - half4;
+      float zsel = 0.f;
+      bool hit = false;
+      if (__builtin_amdgcn_ballot_w64(tgt[j] >= vq && tgt[j] < vq + kWaveTile)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool m = (d == 32 * i + 8 * (r >> 2) + (r & 3));
+            zsel = m ? acc.c[i][j][r] : zsel;
+            hit = hit || m;
+          }
+      }
+      // scale into log2 units and mask the vocabulary tail
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = acc.c[i][j][r] * c2;
+          if (tail && vq + acc_row(i, r, lane) >= a.V) x = -INFINITY;
+          acc.c[i][j][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          s0 += __builtin_amdgcn_exp2f(acc.c[i][j][r + 0] - mx);
+          s1 += __builtin_amdgcn_exp2f(acc.c[i][j][r + 1] - mx);
+          s2 += __builtin_amdgcn_exp2f(acc.c[i][j][r + 2] - mx);
+          s3 += __builtin_amdgcn_exp2f(acc.c[i][j][r + 3] - mx);
+        }
+      float s = (s0 + s1) + (s2 + s3);
+      s = s + __shfl_xor(s, 32);
+      const int ti = tok_i[j];
+      if (ti < Na) {
+        if (lane < 32) {
+          a.part_max[(size_t)col * a.N + ti] = mx;
+          a.part_sum[(size_t)col * a.N + ti] = s;
+        }
+        if (hit) a.target_logit[ti] = zsel * a.inv_t;
+      }
+    }
+  }
+}
+
+// One work-group of 256 threads merges 32 compacted rows: thread (row = tid & 31,
+// slice = tid >> 5) walks columns slice, slice + 8, ... in ascending order; the eight slice
+// sums are added in a fixed tree.
+__global__ __launch_bounds__(256) void fwd_merge_kernel(MergeArgs a) {
+  __shared__ float red[8][33];
+  const int Na = *a.n_active;
+  const int i0 = blockIdx.x * 32;
+  if (i0 >= Na) return;
+  const int r = threadIdx.x & 31;
+  const int sl = threadIdx.x >> 5;
+  const int i = i0 + r;
+  const bool ok = i < Na;
+  const int J = (a.V + kVocabPartial - 1) / kVocabPartial;
+
+  float m = -INFINITY;
+  if (ok)
+    for (int j = sl; j < J; j += 8) m = fmaxf(m, a.part_max[(size_t)j * a.N + i]);
+  red[sl][r] = m;
+  __syncthreads();
+  float M = red[0][r];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) M = fmaxf(M, red[k][r]);
+  __syncthreads();
+
+  float s = 0.f;
+  if (ok)
+    for (int j = sl; j < J; j += 8) {
+      const size_t o = (size_t)j * a.N + i;
+      s += a.part_sum[o] * __builtin_amdgcn_exp2f(a.part_max[o] - M);
+    }
+  red[sl][r] = s;
+  __syncthreads();
+  if (sl == 0 && ok) {
+    const float S = ((red[0][r] + red[1][r]) + (red[2][r] + red[3][r])) +
+                    ((red[4][r] + red[5][r]) + (red[6][r] + red[7][r]));
+    const float lse = (M + __builtin_amdgcn_logf(S)) * kLn2;
+    const int t = a.idx[i];
+    a.logp[t] = a.target_logit[i] - lse;
+    if (a.lse) a.lse[t] = lse;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream_t stream) {
+  if (bf16)
+    hipLaunchKernelGGL(fwd_tiles_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(fwd_tiles_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t stream) {
+  const int grid = (int)((a.N + 31) / 32);
+  hipLaunchKernelGGL(fwd_merge_kernel, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace rlk

@@ -1,0 +1,74 @@
+// Kernel argument blocks and launchers (host-visible, internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rlk {
+
+constexpr int kVocabPartial = 128;  // vocabulary entries per partial-statistics column
+constexpr int kBwdChunk = 8192;     // vocabulary entries per backward chunk (build constant)
+
+struct CompactArgs {
+  const uint8_t* mask;
+  int32_t* idx;
+  int32_t* n_active;
+  float* target_logit;  // [N], set to NaN (may be null)
+  float* logp;          // may be null: 0 at inactive tokens
+  float* lse;           // may be null: 0 at inactive tokens
+  int N;
+};
+
+struct FwdTileArgs {
+  const void* h;
+  const void* W;
+  const int32_t* targets;
+  const int32_t* idx;
+  const int32_t* n_active;
+  int N, H, V;
+  float inv_t;
+  float* part_max;
+  float* part_sum;
+  float* target_logit;
+};
+
+struct MergeArgs {
+  const float* part_max;
+  const float* part_sum;
+  const float* target_logit;
+  const int32_t* idx;
+  const int32_t* n_active;
+  int N, V;
+  float* logp;
+  float* lse;
+};
+
+// Backward buffers (bf16 stored as uint16_t).
+struct BwdArgs {
+  const void* h;          // [N, H] bf16
+  const void* W;          // [V, H] bf16
+  const int32_t* targets; // [N]
+  const float* adv;       // [N]
+  const float* lse;       // [N]
+  const int32_t* idx;     // [N] compacted active positions
+  const int32_t* n_active;
+  int N, H, V, Npad;      // Npad: token capacity of the G / hT buffers (multiple of 256)
+  float inv_t;
+  float* dh;              // [N, H]
+  float* dW;              // [V, H]
+  uint16_t* hT;           // [H, Npad]   compacted h, transposed, zero past Na
+  uint16_t* Wt;           // [H, kBwdChunk] one vocabulary chunk of W, transposed
+  uint16_t* Gv;           // [Npad, kBwdChunk] dL/dz of the chunk, token-major
+  uint16_t* Gt;           // [kBwdChunk, Npad] dL/dz of the chunk, vocabulary-major
+};
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
+hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream_t stream);
+hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t stream);
+
+// Backward phases.
+hipError_t launch_zero(float* p, size_t n, hipStream_t stream);
+hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream);          // dh = 0, hT
+hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t stream);
+
+}  // namespace rlk

@@ -1,0 +1,123 @@
+// Host-side argument checks of the C ABI.  Pure functions: no HIP call, no device access,
+// so every error path is decided before anything is enqueued.
+#pragma once
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rlk.h"
+
+namespace rlk {
+
+constexpr int64_t kMaxTokens = int64_t(1) << 22;
+constexpr int64_t kMaxVocab = int64_t(1) << 22;
+constexpr int64_t kMaxHidden = int64_t(1) << 16;
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int64_t num_partials(int64_t V) { return V <= 0 ? 0 : (V + 127) / 128; }
+
+inline int elt_size(int dtype) { return dtype == RLK_BF16 ? 2 : 4; }
+
+// Shapes, dtype and temperature shared by every entry point.
+inline rlk_status_t check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
+  if (N < 0 || H <= 0 || V <= 0) return RLK_ERROR_INVALID_VALUE;
+  if (dtype != RLK_BF16 && dtype != RLK_FP32) return RLK_ERROR_UNSUPPORTED;
+  if (H % 64 != 0) return RLK_ERROR_UNSUPPORTED;
+  if (N > kMaxTokens || V > kMaxVocab || H > kMaxHidden) return RLK_ERROR_UNSUPPORTED;
+  return RLK_SUCCESS;
+}
+
+inline rlk_status_t check_temperature(float T) {
+  if (!isfinite(T) || !(T > 0.f)) return RLK_ERROR_INVALID_VALUE;
+  // 1/T must be finite and nonzero in fp32
+  const float inv = (float)(1.0 / (double)T);
+  if (!isfinite(inv) || inv == 0.f) return RLK_ERROR_INVALID_VALUE;
+  return RLK_SUCCESS;
+}
+
+// Workspace layout of the forward: idx[N] | n_active | target_logit[N] | part_max | part_sum.
+struct FwdLayout {
+  size_t idx, n_active, target_logit, part_max, part_sum, total;
+};
+
+inline FwdLayout fwd_layout(int64_t N, int64_t V) {
+  FwdLayout L;
+  const size_t n = (size_t)(N > 0 ? N : 1);
+  const size_t np = (size_t)num_partials(V);
+  size_t o = 0;
+  L.idx = o;          o = align_up(o + 4 * n, 256);
+  L.n_active = o;     o = align_up(o + 4, 256);
+  L.target_logit = o; o = align_up(o + 4 * n, 256);
+  L.part_max = o;     o = align_up(o + 4 * n * np, 256);
+  L.part_sum = o;     o = align_up(o + 4 * n * np, 256);
+  L.total = o;
+  return L;
+}
+
+constexpr int64_t kBwdChunkEntries = 8192;
+
+inline int64_t bwd_npad(int64_t N) { return ((N > 0 ? N : 1) + 255) / 256 * 256; }
+
+// Workspace layout of the backward: idx[N] | n_active | hT[H, Npad] | Wt[H, chunk] |
+// Gv[Npad, chunk] | Gt[chunk, Npad]  (bf16 buffers).
+struct BwdLayout {
+  size_t idx, n_active, hT, Wt, Gv, Gt, total;
+};
+
+inline BwdLayout bwd_layout(int64_t N, int64_t H) {
+  BwdLayout L;
+  const size_t n = (size_t)(N > 0 ? N : 1);
+  const size_t np = (size_t)bwd_npad(N);
+  const size_t c = (size_t)kBwdChunkEntries;
+  size_t o = 0;
+  L.idx = o;      o = align_up(o + 4 * n, 256);
+  L.n_active = o; o = align_up(o + 4, 256);
+  L.hT = o;       o = align_up(o + 2 * (size_t)H * np, 256);
+  L.Wt = o;       o = align_up(o + 2 * (size_t)H * c, 256);
+  L.Gv = o;       o = align_up(o + 2 * np * c, 256);
+  L.Gt = o;       o = align_up(o + 2 * c * np, 256);
+  L.total = o;
+  return L;
+}
+
+inline rlk_status_t check_fwd(const void* h, const void* W, const int32_t* targets,
+                              const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
+                              float T, const float* logp, const float* lse, const void* ws,
+                              size_t ws_bytes) {
+  rlk_status_t s = check_shape(N, H, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  s = check_temperature(T);
+  if (s != RLK_SUCCESS) return s;
+  if (N == 0) return RLK_SUCCESS;
+  if (!h || !W || !targets || !mask || !logp || !ws) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(targets, 4) || !aligned(logp, 4) ||
+      (lse && !aligned(lse, 4)) || !aligned(ws, 256))
+    return RLK_ERROR_UNSUPPORTED;
+  if (ws_bytes < fwd_layout(N, V).total) return RLK_ERROR_WORKSPACE;
+  return RLK_SUCCESS;
+}
+
+inline rlk_status_t check_bwd(const void* h, const void* W, const int32_t* targets,
+                              const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
+                              float T, const float* adv, const float* lse, const float* dh,
+                              const float* dW, const void* ws, size_t ws_bytes) {
+  rlk_status_t s = check_shape(N, H, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  s = check_temperature(T);
+  if (s != RLK_SUCCESS) return s;
+  if (dtype != RLK_BF16 || H % 256 != 0) return RLK_ERROR_UNSUPPORTED;
+  if (!dW) return RLK_ERROR_INVALID_VALUE;
+  if (N == 0) return RLK_SUCCESS;  // dW is still zeroed by the caller-visible contract
+  if (!h || !W || !targets || !mask || !adv || !lse || !dh || !ws) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(targets, 4) || !aligned(adv, 4) ||
+      !aligned(lse, 4) || !aligned(dh, 4) || !aligned(dW, 4) || !aligned(ws, 256))
+    return RLK_ERROR_UNSUPPORTED;
+  if (ws_bytes < bwd_layout(N, H).total) return RLK_ERROR_WORKSPACE;
+  return RLK_SUCCESS;
+}
+
+}  // namespace rlk

@@ -1,0 +1,198 @@
+"""Python binding of the C ABI (include/rlk.h), with the same names.
+
+Argument marshalling only: tensors must already live on the GPU; PyTorch provides device
+memory (outputs and workspaces) and the current stream, and every step of the path runs
+in the library's HIP kernels.  Errors from the library raise ``RlkError``."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib as L
+
+RlkError = L.RlkError
+
+
+def _vp(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return L.RLK_BF16
+    if t.dtype == torch.float32:
+        return L.RLK_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}: bf16 or float32")
+
+
+def _mask_u8(mask: torch.Tensor) -> torch.Tensor:
+    if mask.dtype == torch.bool:
+        return mask.view(torch.uint8)
+    if mask.dtype != torch.uint8:
+        raise TypeError("mask must be uint8 or bool")
+    return mask
+
+
+def _check(h, W, targets, mask):
+    for name, t in (("h", h), ("W", W), ("targets", targets), ("mask", mask)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if h.dim() != 2 or W.dim() != 2 or h.shape[1] != W.shape[1]:
+        raise ValueError("h must be [N, H] and W [V, H]")
+    if h.dtype != W.dtype:
+        raise TypeError("h and W must share a dtype")
+    if targets.dtype != torch.int32 or targets.shape != (h.shape[0],):
+        raise ValueError("targets must be int32 [N]")
+    if mask.shape != (h.shape[0],):
+        raise ValueError("mask must be [N]")
+
+
+def num_vocab_partials(V: int) -> int:
+    return int(L.lib().rlk_num_vocab_partials(V))
+
+
+def fwd_workspace_bytes(N: int, H: int, V: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_linear_logp_fwd_workspace_size(N, H, V, dtype, ctypes.byref(out)),
+            "rlk_linear_logp_fwd_workspace_size")
+    return int(out.value)
+
+
+def bwd_workspace_bytes(N: int, H: int, V: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_linear_logp_bwd_workspace_size(N, H, V, dtype, ctypes.byref(out)),
+            "rlk_linear_logp_bwd_workspace_size")
+    return int(out.value)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def rlk_linear_logp_fwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                        mask: torch.Tensor, temperature: float,
+                        workspace: Optional[torch.Tensor] = None,
+                        ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Selected-token log-prob; returns (logp [N] float32, lse [N] float32)."""
+    mask = _mask_u8(mask)
+    _check(h, W, targets, mask)
+    N, H = h.shape
+    V = W.shape[0]
+    dt = _dtype_code(h)
+    logp = torch.empty(N, dtype=torch.float32, device=h.device)
+    lse = torch.empty(N, dtype=torch.float32, device=h.device)
+    ws = _workspace(fwd_workspace_bytes(N, H, V, dt), h.device, workspace)
+    L.check(L.lib().rlk_linear_logp_fwd(_vp(h), _vp(W), _vp(targets), _vp(mask), N, H, V, dt,
+                                        float(temperature), _vp(logp), _vp(lse), _vp(ws),
+                                        ws.numel() * ws.element_size(), _stream(h.device)),
+            "rlk_linear_logp_fwd")
+    return logp, lse
+
+
+def rlk_linear_logp_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                        mask: torch.Tensor, temperature: float, adv: torch.Tensor,
+                        lse: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                        dh: Optional[torch.Tensor] = None, dW: Optional[torch.Tensor] = None,
+                        ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gradients of L = -sum_t mask_t adv_t logp_t; returns (dh [N,H], dW [V,H]) float32."""
+    mask = _mask_u8(mask)
+    _check(h, W, targets, mask)
+    N, H = h.shape
+    V = W.shape[0]
+    dt = _dtype_code(h)
+    for name, t in (("adv", adv), ("lse", lse)):
+        if not t.is_cuda or t.dtype != torch.float32 or t.shape != (N,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor [N]")
+    if dh is None:
+        dh = torch.empty((N, H), dtype=torch.float32, device=h.device)
+    if dW is None:
+        dW = torch.empty((V, H), dtype=torch.float32, device=h.device)
+    ws = _workspace(bwd_workspace_bytes(N, H, V, dt), h.device, workspace)
+    L.check(L.lib().rlk_linear_logp_bwd(_vp(h), _vp(W), _vp(targets), _vp(mask), N, H, V, dt,
+                                        float(temperature), _vp(adv), _vp(lse), _vp(dh), _vp(dW),
+                                        _vp(ws), ws.numel() * ws.element_size(),
+                                        _stream(h.device)),
+            "rlk_linear_logp_bwd")
+    return dh, dW
+
+
+# ---- building blocks of the forward
+
+def rlk_compact_active(mask: torch.Tensor, idx: torch.Tensor, n_active: torch.Tensor,
+                       target_logit: Optional[torch.Tensor] = None,
+                       logp: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None) -> None:
+    mask = _mask_u8(mask)
+    L.check(L.lib().rlk_compact_active(_vp(mask), mask.numel(), _vp(idx), _vp(n_active),
+                                       _vp(target_logit), _vp(logp), _vp(lse),
+                                       _stream(mask.device)), "rlk_compact_active")
+
+
+def rlk_linear_logp_partials(h, W, targets, idx, n_active, temperature, part_max, part_sum,
+                             target_logit) -> None:
+    N, H = h.shape
+    V = W.shape[0]
+    L.check(L.lib().rlk_linear_logp_partials(_vp(h), _vp(W), _vp(targets), _vp(idx),
+                                             _vp(n_active), N, H, V, _dtype_code(h),
+                                             float(temperature), _vp(part_max), _vp(part_sum),
+                                             _vp(target_logit), _stream(h.device)),
+            "rlk_linear_logp_partials")
+
+
+def rlk_linear_logp_merge(part_max, part_sum, target_logit, idx, n_active, N, V, logp,
+                          lse=None) -> None:
+    L.check(L.lib().rlk_linear_logp_merge(_vp(part_max), _vp(part_sum), _vp(target_logit),
+                                          _vp(idx), _vp(n_active), N, V, _vp(logp), _vp(lse),
+                                          _stream(logp.device)), "rlk_linear_logp_merge")
+
+
+class ForwardBuffers:
+    """Preallocated buffers for calling the three forward building blocks in sequence."""
+
+    def __init__(self, N: int, V: int, device):
+        J = num_vocab_partials(V)
+        self.idx = torch.empty(max(N, 1), dtype=torch.int32, device=device)
+        self.n_active = torch.empty(1, dtype=torch.int32, device=device)
+        self.target_logit = torch.empty(max(N, 1), dtype=torch.float32, device=device)
+        self.part_max = torch.empty((J, max(N, 1)), dtype=torch.float32, device=device)
+        self.part_sum = torch.empty((J, max(N, 1)), dtype=torch.float32, device=device)
+        self.logp = torch.empty(max(N, 1), dtype=torch.float32, device=device)
+        self.lse = torch.empty(max(N, 1), dtype=torch.float32, device=device)
+
+
+# ---- autograd
+
+class LinearLogp(torch.autograd.Function):
+    """logp = linear_logp(h, W, targets, mask, T); backward through rlk_linear_logp_bwd
+    with adv = -dL/dlogp."""
+
+    @staticmethod
+    def forward(ctx, h, W, targets, mask, temperature):
+        logp, lse = rlk_linear_logp_fwd(h, W, targets, mask, temperature)
+        ctx.save_for_backward(h, W, targets, mask, lse)
+        ctx.temperature = float(temperature)
+        return logp
+
+    @staticmethod
+    def backward(ctx, grad_logp):
+        h, W, targets, mask, lse = ctx.saved_tensors
+        adv = (-grad_logp).to(torch.float32).contiguous()
+        dh, dW = rlk_linear_logp_bwd(h, W, targets, mask, ctx.temperature, adv, lse)
+        return dh.to(h.dtype), dW.to(W.dtype), None, None, None
+
+
+def linear_logp(h, W, targets, mask, temperature) -> torch.Tensor:
+    """Differentiable selected-token log-prob [N] (float32)."""
+    return LinearLogp.apply(h, W, targets, mask, temperature)

@@ -1,0 +1,158 @@
+"""The C-ABI library loads, exports every symbol include/rlk.h declares, and rejects bad
+arguments on the host before any device work (no GPU needed: only calls that return
+before touching HIP are made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rlk.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from linear_selected_token_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from linear_selected_token_amd import build
+        build.build()
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlk_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("rlk_linear_logp_fwd", "rlk_linear_logp_bwd", "rlk_status_string",
+              "rlk_build_info", "rlk_linear_logp_fwd_workspace_size",
+              "rlk_linear_logp_bwd_workspace_size"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = L.lib()
+    names = declared_functions()
+    assert set(names) == set(L.SIGNATURES), "binding signatures out of step with the header"
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\b(rlk_\w+)\b", out))
+    assert set(names) <= exported
+
+
+def test_library_carries_gfx950_code(L):
+    # the embedded offload bundle names its target (our own build output)
+    data = open(L.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in data
+
+
+def test_status_and_build_info(L):
+    lib = L.lib()
+    for s in range(5):
+        assert lib.rlk_status_string(s).decode().startswith("RLK_")
+    assert b"unknown" in lib.rlk_status_string(99)
+    info = lib.rlk_build_info().decode()
+    assert "gfx950" in info and "vocab partial 128" in info
+    assert lib.rlk_num_vocab_partials(151936) == 1187
+    assert lib.rlk_num_vocab_partials(1000) == 8
+    assert lib.rlk_num_vocab_partials(128) == 1
+    assert lib.rlk_num_vocab_partials(0) == 0
+
+
+def _ws(lib, fn, *args):
+    out = ctypes.c_size_t(0)
+    st = getattr(lib, fn)(*args, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_queries(L):
+    lib = L.lib()
+    st, a = _ws(lib, "rlk_linear_logp_fwd_workspace_size", 16384, 4096, 151936, L.RLK_BF16)
+    assert st == 0 and a >= 2 * 4 * 16384 * 1187
+    st, b = _ws(lib, "rlk_linear_logp_fwd_workspace_size", 8192, 4096, 151936, L.RLK_BF16)
+    assert st == 0 and b < a
+    st, c = _ws(lib, "rlk_linear_logp_bwd_workspace_size", 4096, 4096, 151936, L.RLK_BF16)
+    assert st == 0 and c > 0
+    assert _ws(lib, "rlk_linear_logp_bwd_workspace_size", 4096, 4096, 151936, L.RLK_FP32)[0] == \
+        L.RLK_ERROR_UNSUPPORTED
+    assert _ws(lib, "rlk_linear_logp_fwd_workspace_size", 10, 100, 50, L.RLK_BF16)[0] == \
+        L.RLK_ERROR_UNSUPPORTED
+    assert _ws(lib, "rlk_linear_logp_fwd_workspace_size", -1, 64, 50, L.RLK_BF16)[0] == \
+        L.RLK_ERROR_INVALID_VALUE
+    assert lib.rlk_linear_logp_fwd_workspace_size(4, 64, 8, 0, None) == L.RLK_ERROR_INVALID_VALUE
+
+
+FAKE = 1 << 20  # aligned non-null stand-in address: these calls fail validation first
+
+
+def _fwd(lib, h=FAKE, W=FAKE, tg=FAKE, m=FAKE, N=8, H=64, V=100, dt=0, T=1.0, lp=FAKE,
+         lse=FAKE, ws=FAKE, wsb=1 << 30):
+    return lib.rlk_linear_logp_fwd(h, W, tg, m, N, H, V, dt, T, lp, lse, ws, wsb, None)
+
+
+def test_forward_argument_errors(L):
+    lib = L.lib()
+    E = L
+    assert _fwd(lib, N=0) == E.RLK_SUCCESS  # nothing to do, nothing touched
+    assert _fwd(lib, h=None) == E.RLK_ERROR_INVALID_VALUE
+    assert _fwd(lib, W=None) == E.RLK_ERROR_INVALID_VALUE
+    assert _fwd(lib, tg=None) == E.RLK_ERROR_INVALID_VALUE
+    assert _fwd(lib, m=None) == E.RLK_ERROR_INVALID_VALUE
+    assert _fwd(lib, lp=None) == E.RLK_ERROR_INVALID_VALUE
+    assert _fwd(lib, ws=None) == E.RLK_ERROR_INVALID_VALUE
+    for T in (0.0, -1.0, float("nan"), float("inf"), 1e-45):
+        assert _fwd(lib, T=T) == E.RLK_ERROR_INVALID_VALUE, T
+    assert _fwd(lib, N=-1) == E.RLK_ERROR_INVALID_VALUE
+    assert _fwd(lib, V=0) == E.RLK_ERROR_INVALID_VALUE
+    assert _fwd(lib, H=0) == E.RLK_ERROR_INVALID_VALUE
+    assert _fwd(lib, dt=2) == E.RLK_ERROR_UNSUPPORTED
+    assert _fwd(lib, H=96) == E.RLK_ERROR_UNSUPPORTED
+    assert _fwd(lib, N=1 << 23) == E.RLK_ERROR_UNSUPPORTED
+    assert _fwd(lib, h=FAKE + 8) == E.RLK_ERROR_UNSUPPORTED
+    assert _fwd(lib, W=FAKE + 4) == E.RLK_ERROR_UNSUPPORTED
+    assert _fwd(lib, ws=FAKE + 16) == E.RLK_ERROR_UNSUPPORTED
+    assert _fwd(lib, wsb=1000) == E.RLK_ERROR_WORKSPACE
+
+
+def test_backward_argument_errors(L):
+    lib = L.lib()
+    E = L
+
+    def bwd(h=FAKE, adv=FAKE, lse=FAKE, dh=FAKE, dW=FAKE, N=8, H=256, dt=0, T=1.0, wsb=1 << 30):
+        return lib.rlk_linear_logp_bwd(h, FAKE, FAKE, FAKE, N, H, 100, dt, T, adv, lse, dh, dW,
+                                       FAKE, wsb, None)
+
+    assert bwd(adv=None) == E.RLK_ERROR_INVALID_VALUE
+    assert bwd(lse=None) == E.RLK_ERROR_INVALID_VALUE
+    assert bwd(dh=None) == E.RLK_ERROR_INVALID_VALUE
+    assert bwd(dW=None) == E.RLK_ERROR_INVALID_VALUE
+    assert bwd(T=0.0) == E.RLK_ERROR_INVALID_VALUE
+    assert bwd(dt=1) == E.RLK_ERROR_UNSUPPORTED
+    assert bwd(H=192) == E.RLK_ERROR_UNSUPPORTED
+    assert bwd(wsb=10) == E.RLK_ERROR_WORKSPACE
+
+
+def test_building_block_argument_errors(L):
+    lib = L.lib()
+    E = L
+    assert lib.rlk_compact_active(FAKE, -1, FAKE, FAKE, None, None, None, None) == \
+        E.RLK_ERROR_INVALID_VALUE
+    assert lib.rlk_compact_active(None, 5, FAKE, FAKE, None, None, None, None) == \
+        E.RLK_ERROR_INVALID_VALUE
+    assert lib.rlk_compact_active(FAKE, 5, FAKE, None, None, None, None, None) == \
+        E.RLK_ERROR_INVALID_VALUE
+    assert lib.rlk_linear_logp_partials(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 10, 0, 0.0, FAKE,
+                                        FAKE, FAKE, None) == E.RLK_ERROR_INVALID_VALUE
+    assert lib.rlk_linear_logp_partials(FAKE, FAKE, FAKE, FAKE, None, 4, 64, 10, 0, 1.0, FAKE,
+                                        FAKE, FAKE, None) == E.RLK_ERROR_INVALID_VALUE
+    assert lib.rlk_linear_logp_merge(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0, FAKE, None, None) == \
+        E.RLK_ERROR_INVALID_VALUE
+    assert lib.rlk_linear_logp_merge(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 10, FAKE, None, None) == \
+        E.RLK_SUCCESS

@@ -1,0 +1,89 @@
+"""Bitwise batch invariance of the HIP path (needs an MI355X).
+
+A token's logp and lse must be bit-identical whether its sequence is scored alone, in
+the full batch, in shuffled order, with extra padding, with its prompt tokens also
+active, on a repeat run or on another stream (RL-Kernel integration roadmap for vime,
+"Consistency Contract": same-backend bitwise stability across batch size, row position,
+dense vs indexed rows, sparse-row density and stream/repeat runs)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import bits, flush, run_fwd, upload
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _keyed(w, lp, lse, only_active_of=None):
+    out = {}
+    for i, k in enumerate(w.key()):
+        if k[0] < 0 or not w.mask[i]:
+            continue
+        out[k] = (int(bits(lp[i:i + 1])[0]), int(bits(lse[i:i + 1])[0]))
+    return out
+
+
+def _mismatches(ref, got):
+    n = 0
+    for k, v in got.items():
+        if k in ref and ref[k] != v:
+            n += 1
+    return n
+
+
+def _sweep(fam, n_alone, label):
+    base = fam.batch()
+    ref = _keyed(base, *run_fwd(base))
+    cases = []
+    for s in range(min(n_alone, fam.n_seq)):
+        cases.append((f"alone {s}", fam.alone(s)))
+    for k in range(3):
+        cases.append((f"shuffle {k}", fam.shuffled(100 + k)))
+        cases.append((f"padded {k}", fam.padded(200 + k)))
+    cases.append(("all active", fam.all_active()))
+    cases.append(("subset", fam.subset(list(range(0, fam.n_seq, 3)))))
+    total = 0
+    checked = 0
+    for name, w in cases:
+        got = _keyed(w, *run_fwd(w))
+        common = [k for k in got if k in ref]
+        m = _mismatches(ref, got)
+        total += m
+        checked += len(common)
+        if m:
+            flush(f"  {label} {name}: {m} mismatches of {len(common)}")
+    # repeat runs and a second stream on the full batch
+    d = upload(base)
+    import linear_selected_token_amd as rlk
+    outs = []
+    for k in range(3):
+        outs.append(rlk.rlk_linear_logp_fwd(d["h"], d["W"], d["targets"], d["mask"], base.T))
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        outs.append(rlk.rlk_linear_logp_fwd(d["h"], d["W"], d["targets"], d["mask"], base.T))
+    torch.cuda.synchronize()
+    for lp, lse in outs:
+        got = _keyed(base, lp.cpu().numpy(), lse.cpu().numpy())
+        total += _mismatches(ref, got)
+        checked += len(got)
+    flush(f"  {label}: {total} mismatches over {checked} active-token comparisons")
+    return total
+
+
+def test_invariance_small():
+    fam = wl.Family(wl.scaled_spec(2, N=1500, H=256, V=2000, n_seq=8, len_lo=64, len_hi=400,
+                                   seed=90, T=0.7))
+    assert _sweep(fam, 8, "small") == 0
+
+
+def test_invariance_config3_full():
+    """The N=16384, T=0.7 workload with its sampled targets: every sequence alone, the full
+    batch, shuffles, paddings, all-active density, repeats and a second stream."""
+    fam = wl.Family(wl.CONFIGS[3])
+    fam.use_targets(np.load(os.path.join(HERE, "golden", "cfg3_sampled_targets.npy")))
+    assert _sweep(fam, fam.n_seq, "config3") == 0
