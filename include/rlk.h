@@ -34,7 +34,8 @@
  *   - Every argument check happens on the host before anything is enqueued, so a call
  *     that returns an error has written nothing.  N == 0 returns RLK_SUCCESS at once.
  *   - An active token whose target is outside [0, V) gets logp = NaN (checking it on the
- *     host would need a device-to-host copy); its lse is still correct.
+ *     host would need a device-to-host copy); its lse is still correct, and in the
+ *     backward its dL/dz has no target term (only -g_t p[t,v]).
  *   - Inactive tokens (mask == 0) are never read into the products; their h rows and
  *     targets may hold anything.  Their logp and lse are 0 and their dL/dh row is 0.
  *   - Calls are reentrant: the only shared state is read-only device properties.

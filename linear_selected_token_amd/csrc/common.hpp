@@ -24,6 +24,7 @@ namespace rlk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -51,10 +52,14 @@ __device__ __forceinline__ void mma_step(f32x16& acc, const u32x4& a, const u32x
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
   } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[e]),
-                                                  __builtin_bit_cast(float, b[e]), acc, 0, 0, 0);
+    // Cast the whole vector, then take named elements: a bit_cast of a single vector
+    // element (a[e]) is lowered to element 0 by this compiler.
+    const f32x4 af = __builtin_bit_cast(f32x4, a);
+    const f32x4 bf = __builtin_bit_cast(f32x4, b);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af.x, bf.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af.y, bf.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af.z, bf.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af.w, bf.w, acc, 0, 0, 0);
   }
 }
 

@@ -69,7 +69,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       tok_i[j] = tbase + wt + acc_col(j, lane);
-      tgt[j] = tok_i[j] < Na ? a.targets[a.idx[tok_i[j]]] : -1;
+      const int y = tok_i[j] < Na ? a.targets[a.idx[tok_i[j]]] : -1;
+      tgt[j] = (y >= 0 && y < a.V) ? y : -1;  // out of range: no tile captures it
     }
 
     Acc acc;
