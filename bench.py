@@ -50,7 +50,23 @@ def parse():
     p.add_argument("--mode", default="fwdbwd", choices=["fwd", "fwdbwd"])
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample (0 disables it)")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="only run a plain device-to-device copy of this many MiB (to scale "
+                        "the profiler's HBM byte counters) and exit")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy kernel of known size: reads and writes `mib` MiB once."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
 
 
 def make_workload(name):
@@ -78,24 +94,20 @@ def cpu_baseline(w, mode, target_s):
     m = np.ones(act.size, dtype=np.uint8)
     y = w.targets[act]
     adv = w.adv[act]
-    # calibrate on 16 tokens, then run a sample sized for ~target_s seconds
-    k = 16
-    t0 = time.perf_counter()
-    if mode == "fwd":
-        oracle.linear_logp(h64[:k], W64, y[:k], m[:k], w.T)
-    else:
-        oracle.linear_logp(h64[:k], W64, y[:k], m[:k], w.T)
-        oracle.linear_logp_grads(h64[:k], W64, y[:k], m[:k], w.T, adv[:k])
-    per = (time.perf_counter() - t0) / k
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.linear_logp(h64[:n], W64, y[:n], m[:n], w.T)
+        if mode != "fwd":
+            oracle.linear_logp_grads(h64[:n], W64, y[:n], m[:n], w.T, adv[:n])
+        return time.perf_counter() - t0
+
+    # one calibration run (its fixed costs make the per-token estimate an overestimate, so
+    # the sample stays within about target_s seconds), then the timed sample
+    k = min(act.size, 128)
+    per = run(k) / k
     n = int(min(act.size, max(k, target_s / max(per, 1e-9))))
-    n = max(k, (n // 16) * 16)
-    t0 = time.perf_counter()
-    if mode == "fwd":
-        oracle.linear_logp(h64[:n], W64, y[:n], m[:n], w.T)
-    else:
-        oracle.linear_logp(h64[:n], W64, y[:n], m[:n], w.T)
-        oracle.linear_logp_grads(h64[:n], W64, y[:n], m[:n], w.T, adv[:n])
-    dt = time.perf_counter() - t0
+    n = max(16, (n // 16) * 16)
+    dt = run(n)
     return {"value": n / dt, "unit": "active tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} active tokens of the same workload scored as one batch "
                       f"({'forward' if mode == 'fwd' else 'forward + dL/dh + dL/dW'}, float64, "
@@ -135,6 +147,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; the path has no "
                                    "multi-GPU mode (run with --gpus 1)"}))
         sys.exit(2)
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
+        return
     import torch
     import linear_selected_token_amd as rlk
 

@@ -19,6 +19,7 @@
 // Before the first chunk, bwd_prepare zeroes dh and writes hT = compacted h transposed.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mainloop.hpp"
 
 namespace rlk {
 
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, size_t n) {
 // ---------------------------------------------------------------- dlogits of one chunk
 
 __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(BwdArgs a, int c0) {
-  __shared__ TileSmem sm;
+  __shared__ RingSmem sm;
   const int Na = *a.n_active;
   const int vc = min(kBwdChunk, a.V - c0);  // vocabulary entries in this chunk
   const int nTokTiles = (Na + kTile - 1) / kTile;
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(BwdArgs a, int c0)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const size_t row_bytes = (size_t)a.H * 2;
-  const int nk = (int)(row_bytes / kStageBytes);
+  const int nk = (int)(row_bytes / kKBytes);
   const float c2 = a.inv_t * kLog2e;
 
   for (int round = 0;; ++round) {
@@ -99,15 +100,16 @@ __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(BwdArgs a, int c0)
     const int vbase = c0 + vt * kTile;
     const int tbase = tt * kTile;
 
-    const uint8_t* a_src[kLoadsPerThread];
-    const uint8_t* b_src[kLoadsPerThread];
+    const uint8_t* a_src[4];
+    const uint8_t* b_src[4];
 #pragma unroll
-    for (int q = 0; q < kLoadsPerThread; ++q) {
-      const int r = load_row(q, tid);
+    for (int q = 0; q < 4; ++q) {
+      const int r = dma_row(q, wave, lane);
+      const int c = dma_chunk(q, wave, lane);
       const int v = min(vbase + r, a.V - 1);
       const int t = a.idx[min(tbase + r, Na - 1)];
-      a_src[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * load_chunk(tid);
-      b_src[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * load_chunk(tid);
+      a_src[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * c;
+      b_src[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * c;
     }
     const int wv = (wave & 1) * kWaveTile;
     const int wt = (wave >> 1) * kWaveTile;
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(BwdArgs a, int c0)
 
     Acc acc;
     zero_acc(acc);
-    mainloop<true>(sm, a_src, b_src, nk, acc);
+    ring_mainloop<true>(sm, a_src, b_src, nk, acc);
 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(BwdArgs a, int c0)
 // ---------------------------------------------------------------- dh += Gv Wt^T
 
 __global__ __launch_bounds__(kThreads, 1) void dh_chunk_kernel(BwdArgs a, int c0) {
-  __shared__ TileSmem sm;
+  __shared__ RingSmem sm;
   const int Na = *a.n_active;
   const int vc = min(kBwdChunk, a.V - c0);
   const int kc = (vc + 63) & ~63;  // K extent (zero columns past V)
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void dh_chunk_kernel(BwdArgs a, int c0
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const size_t row_bytes = (size_t)kBwdChunk * 2;
-  const int nk = kc * 2 / kStageBytes;
+  const int nk = kc * 2 / kKBytes;
 
   for (int round = 0;; ++round) {
     const int u = virtual_tile(round, blockIdx.x, gridDim.x);
@@ -180,17 +182,18 @@ __global__ __launch_bounds__(kThreads, 1) void dh_chunk_kernel(BwdArgs a, int c0
     tile_coords(u, nTokTiles, nHTiles, band, tt, ht);
     const int tbase = tt * kTile;
     const int hbase = ht * kTile;
-    const uint8_t* a_src[kLoadsPerThread];
-    const uint8_t* b_src[kLoadsPerThread];
+    const uint8_t* a_src[4];
+    const uint8_t* b_src[4];
 #pragma unroll
-    for (int q = 0; q < kLoadsPerThread; ++q) {
-      const int r = load_row(q, tid);
-      a_src[q] = reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)(tbase + r) * row_bytes + 16 * load_chunk(tid);
-      b_src[q] = reinterpret_cast<const uint8_t*>(a.Wt) + (size_t)(hbase + r) * row_bytes + 16 * load_chunk(tid);
+    for (int q = 0; q < 4; ++q) {
+      const int r = dma_row(q, wave, lane);
+      const int c = dma_chunk(q, wave, lane);
+      a_src[q] = reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)(tbase + r) * row_bytes + 16 * c;
+      b_src[q] = reinterpret_cast<const uint8_t*>(a.Wt) + (size_t)(hbase + r) * row_bytes + 16 * c;
     }
     Acc acc;
     zero_acc(acc);
-    mainloop<true>(sm, a_src, b_src, nk, acc);
+    ring_mainloop<true>(sm, a_src, b_src, nk, acc);
 
     const int wa = (wave & 1) * kWaveTile;
     const int wb = (wave >> 1) * kWaveTile;
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void dh_chunk_kernel(BwdArgs a, int c0
 // ---------------------------------------------------------------- dW rows = Gt hT^T
 
 __global__ __launch_bounds__(kThreads, 1) void dw_chunk_kernel(BwdArgs a, int c0) {
-  __shared__ TileSmem sm;
+  __shared__ RingSmem sm;
   const int Na = *a.n_active;
   const int vc = min(kBwdChunk, a.V - c0);
   const int nVocTiles = (vc + kTile - 1) / kTile;
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_chunk_kernel(BwdArgs a, int c0
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const size_t row_bytes = (size_t)a.Npad * 2;
-  const int nk = ((Na + 63) & ~63) * 2 / kStageBytes;
+  const int nk = ((Na + 63) & ~63) * 2 / kKBytes;
 
   for (int round = 0;; ++round) {
     const int u = virtual_tile(round, blockIdx.x, gridDim.x);
@@ -231,17 +234,18 @@ __global__ __launch_bounds__(kThreads, 1) void dw_chunk_kernel(BwdArgs a, int c0
     tile_coords(u, nVocTiles, nHTiles, band, vt, ht);
     const int vbase = vt * kTile;  // within the chunk
     const int hbase = ht * kTile;
-    const uint8_t* a_src[kLoadsPerThread];
-    const uint8_t* b_src[kLoadsPerThread];
+    const uint8_t* a_src[4];
+    const uint8_t* b_src[4];
 #pragma unroll
-    for (int q = 0; q < kLoadsPerThread; ++q) {
-      const int r = load_row(q, tid);
-      a_src[q] = reinterpret_cast<const uint8_t*>(a.Gt) + (size_t)(vbase + r) * row_bytes + 16 * load_chunk(tid);
-      b_src[q] = reinterpret_cast<const uint8_t*>(a.hT) + (size_t)(hbase + r) * row_bytes + 16 * load_chunk(tid);
+    for (int q = 0; q < 4; ++q) {
+      const int r = dma_row(q, wave, lane);
+      const int c = dma_chunk(q, wave, lane);
+      a_src[q] = reinterpret_cast<const uint8_t*>(a.Gt) + (size_t)(vbase + r) * row_bytes + 16 * c;
+      b_src[q] = reinterpret_cast<const uint8_t*>(a.hT) + (size_t)(hbase + r) * row_bytes + 16 * c;
     }
     Acc acc;
     zero_acc(acc);
-    mainloop<true>(sm, a_src, b_src, nk, acc);
+    ring_mainloop<true>(sm, a_src, b_src, nk, acc);
 
     const int wa = (wave & 1) * kWaveTile;
     const int wb = (wave >> 1) * kWaveTile;

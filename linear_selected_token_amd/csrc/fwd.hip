@@ -20,6 +20,7 @@
 // the columns in the same fixed association for every token.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mainloop.hpp"
 
 namespace rlk {
 
@@ -27,7 +28,7 @@ namespace {
 
 template <bool kBF16>
 __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
-  __shared__ TileSmem sm;
+  __shared__ RingSmem sm;
   const int Na = *a.n_active;
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nVocTiles = (a.V + kTile - 1) / kTile;
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   const int wave = tid >> 6;
   const int elt = kBF16 ? 2 : 4;
   const size_t row_bytes = (size_t)a.H * elt;
-  const int nk = (int)(row_bytes / kStageBytes);
+  const int nk = (int)(row_bytes / kKBytes);
   const float c2 = a.inv_t * kLog2e;
 
   for (int round = 0;; ++round) {
@@ -49,16 +50,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
     const int vbase = vt * kTile;
     const int tbase = tt * kTile;
 
-    const uint8_t* a_src[kLoadsPerThread];
-    const uint8_t* b_src[kLoadsPerThread];
+    const uint8_t* a_src[4];
+    const uint8_t* b_src[4];
 #pragma unroll
-    for (int q = 0; q < kLoadsPerThread; ++q) {
-      const int r = load_row(q, tid);
+    for (int q = 0; q < 4; ++q) {
+      const int r = dma_row(q, wave, lane);
+      const int c = dma_chunk(q, wave, lane);
       const int v = min(vbase + r, a.V - 1);
-      const int i = min(tbase + r, Na - 1);
-      const int t = a.idx[i];
-      a_src[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * load_chunk(tid);
-      b_src[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * load_chunk(tid);
+      const int t = a.idx[min(tbase + r, Na - 1)];
+      a_src[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * c;
+      b_src[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * c;
     }
 
     // this lane's four tokens (one per 32-column block of its wave quadrant)
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
 
     Acc acc;
     zero_acc(acc);
-    mainloop<kBF16>(sm, a_src, b_src, nk, acc);
+    ring_mainloop<kBF16>(sm, a_src, b_src, nk, acc);
 
     // ---- epilogue: per token, statistics of this wave's 128 vocabulary entries
     const int vq = vbase + wv;          // first vocabulary entry of the quadrant
@@ -100,27 +101,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
           }
       }
       // scale into log2 units and mask the vocabulary tail
+      float x[64];
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = acc.c[i][j][r] * c2;
-          if (tail && vq + acc_row(i, r, lane) >= a.V) x = -INFINITY;
-          acc.c[i][j][r] = x;
-          mx = fmaxf(mx, x);
+          float v = acc.c[i][j][r] * c2;
+          if (tail && vq + acc_row(i, r, lane) >= a.V) v = -INFINITY;
+          x[16 * i + r] = v;
+          mx = fmaxf(mx, v);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          s0 += __builtin_amdgcn_exp2f(acc.c[i][j][r + 0] - mx);
-          s1 += __builtin_amdgcn_exp2f(acc.c[i][j][r + 1] - mx);
-          s2 += __builtin_amdgcn_exp2f(acc.c[i][j][r + 2] - mx);
-          s3 += __builtin_amdgcn_exp2f(acc.c[i][j][r + 3] - mx);
-        }
+      for (int e = 0; e < 64; e += 4) {
+        s0 += __builtin_amdgcn_exp2f(x[e + 0] - mx);
+        s1 += __builtin_amdgcn_exp2f(x[e + 1] - mx);
+        s2 += __builtin_amdgcn_exp2f(x[e + 2] - mx);
+        s3 += __builtin_amdgcn_exp2f(x[e + 3] - mx);
+      }
       float s = (s0 + s1) + (s2 + s3);
       s = s + __shfl_xor(s, 32);
       const int ti = tok_i[j];
