@@ -77,76 +77,73 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, size_t n) {
 
 // ---------------------------------------------------------------- dlogits of one chunk
 
-__global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(BwdArgs a, int c0) {
+struct DlogitsCtx {
+  int vbase;   // first vocabulary entry of the tile
+  int tok[kBlkB];  // compacted token index of each of this lane's four columns
+  int tgt[kBlkB];
+  float lse2[kBlkB], gs[kBlkB];
+};
+
+__global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
   __shared__ RingSmem sm;
   const int Na = *a.n_active;
   const int vc = min(kBwdChunk, a.V - c0);  // vocabulary entries in this chunk
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nVocTiles = (vc + kTile - 1) / kTile;
-  const int nTiles = nTokTiles * nVocTiles;
   const int band = nTokTiles < 8 ? nTokTiles : 8;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const size_t row_bytes = (size_t)a.H * 2;
   const int nk = (int)(row_bytes / kKBytes);
   const float c2 = a.inv_t * kLog2e;
+  const int wv = wave_a0(wave);
+  const int wt = wave_b0(wave);
 
-  for (int round = 0;; ++round) {
-    const int u = virtual_tile(round, blockIdx.x, gridDim.x);
-    if (u >= nTiles) break;
+  auto setup = [&](int u, TileSrc& src, DlogitsCtx& c) {
     int vt, tt;
     tile_coords(u, nVocTiles, nTokTiles, band, vt, tt);
     const int vbase = c0 + vt * kTile;
     const int tbase = tt * kTile;
-
-    const uint8_t* a_src[4];
-    const uint8_t* b_src[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kDmaPerWave; ++q) {
       const int r = dma_row(q, wave, lane);
-      const int c = dma_chunk(q, wave, lane);
+      const int ch = dma_chunk(q, wave, lane);
       const int v = min(vbase + r, a.V - 1);
       const int t = a.idx[min(tbase + r, Na - 1)];
-      a_src[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * c;
-      b_src[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * c;
+      src.a[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * ch;
+      src.b[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * ch;
     }
-    const int wv = (wave & 1) * kWaveTile;
-    const int wt = (wave >> 1) * kWaveTile;
-    int tok_i[4], tgt[4];
-    float lse2[4], gs[4];
+    c.vbase = vbase;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      tok_i[j] = tbase + wt + acc_col(j, lane);
-      const bool ok = tok_i[j] < Na;
-      const int t = ok ? a.idx[tok_i[j]] : 0;
-      tgt[j] = ok ? a.targets[t] : -1;
-      lse2[j] = ok ? a.lse[t] * kLog2e : 0.f;
-      gs[j] = ok ? -a.adv[t] * a.inv_t : 0.f;
+    for (int j = 0; j < kBlkB; ++j) {
+      c.tok[j] = tbase + wt + acc_col(j, lane);
+      const bool ok = c.tok[j] < Na;
+      const int t = ok ? a.idx[c.tok[j]] : 0;
+      c.tgt[j] = ok ? a.targets[t] : -1;
+      c.lse2[j] = ok ? a.lse[t] * kLog2e : 0.f;
+      c.gs[j] = ok ? -a.adv[t] * a.inv_t : 0.f;
     }
+  };
 
-    Acc acc;
-    zero_acc(acc);
-    ring_mainloop<true>(sm, a_src, b_src, nk, acc);
-
+  auto epilogue = [&](const DlogitsCtx& c, Acc& acc) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ti = tok_i[j];
+    for (int j = 0; j < kBlkB; ++j) {
+      const int ti = c.tok[j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           uint16_t o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            const int v = vbase + wv + acc_row(i, r, lane);
-            const float p = __builtin_amdgcn_exp2f(acc.c[i][j][r] * c2 - lse2[j]);
-            float G = gs[j] * ((v == tgt[j] ? 1.f : 0.f) - p);
+            const int v = c.vbase + wv + acc_row(i, r, lane);
+            const float p = __builtin_amdgcn_exp2f(acc.c[i][j][r] * c2 - c.lse2[j]);
+            float G = c.gs[j] * ((v == c.tgt[j] ? 1.f : 0.f) - p);
             if (v >= a.V) G = 0.f;
             o[e] = to_bf16(G);
           }
-          const int vl = vbase - c0 + wv + acc_row(i, 4 * g, lane);  // first of 4 consecutive
+          const int vl = c.vbase - c0 + wv + acc_row(i, 4 * g, lane);  // first of 4 consecutive
           u32x2 pk;
           pk[0] = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
           pk[1] = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
@@ -155,112 +152,108 @@ __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(BwdArgs a, int c0)
           for (int e = 0; e < 4; ++e) a.Gt[(size_t)(vl + e) * a.Npad + ti] = o[e];
         }
     }
-  }
+  };
+
+  persistent_tiles<true, DlogitsCtx>(sm, nTokTiles * nVocTiles, nk, setup, epilogue);
 }
 
 // ---------------------------------------------------------------- dh += Gv Wt^T
 
-__global__ __launch_bounds__(kThreads, 1) void dh_chunk_kernel(BwdArgs a, int c0) {
+struct RowColCtx {
+  int abase, bbase;  // first A row and first B row of the tile
+};
+
+__global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
   __shared__ RingSmem sm;
   const int Na = *a.n_active;
   const int vc = min(kBwdChunk, a.V - c0);
   const int kc = (vc + 63) & ~63;  // K extent (zero columns past V)
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nHTiles = a.H / kTile;
-  const int nTiles = nTokTiles * nHTiles;
   const int band = nHTiles < 8 ? nHTiles : 8;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const size_t row_bytes = (size_t)kBwdChunk * 2;
   const int nk = kc * 2 / kKBytes;
+  const int wa = wave_a0(wave);
+  const int wb = wave_b0(wave);
 
-  for (int round = 0;; ++round) {
-    const int u = virtual_tile(round, blockIdx.x, gridDim.x);
-    if (u >= nTiles) break;
+  auto setup = [&](int u, TileSrc& src, RowColCtx& c) {
     int tt, ht;
     tile_coords(u, nTokTiles, nHTiles, band, tt, ht);
-    const int tbase = tt * kTile;
-    const int hbase = ht * kTile;
-    const uint8_t* a_src[4];
-    const uint8_t* b_src[4];
+    c.abase = tt * kTile;
+    c.bbase = ht * kTile;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kDmaPerWave; ++q) {
       const int r = dma_row(q, wave, lane);
-      const int c = dma_chunk(q, wave, lane);
-      a_src[q] = reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)(tbase + r) * row_bytes + 16 * c;
-      b_src[q] = reinterpret_cast<const uint8_t*>(a.Wt) + (size_t)(hbase + r) * row_bytes + 16 * c;
+      const int ch = dma_chunk(q, wave, lane);
+      src.a[q] = reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)(c.abase + r) * row_bytes + 16 * ch;
+      src.b[q] = reinterpret_cast<const uint8_t*>(a.Wt) + (size_t)(c.bbase + r) * row_bytes + 16 * ch;
     }
-    Acc acc;
-    zero_acc(acc);
-    ring_mainloop<true>(sm, a_src, b_src, nk, acc);
+  };
 
-    const int wa = (wave & 1) * kWaveTile;
-    const int wb = (wave >> 1) * kWaveTile;
+  auto epilogue = [&](const RowColCtx& c, Acc& acc) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = tbase + wa + acc_row(i, r, lane);
+        const int m = c.abase + wa + acc_row(i, r, lane);
         if (m < Na) {
-          float* row = a.dh + (size_t)a.idx[m] * a.H + hbase + wb;
+          float* row = a.dh + (size_t)a.idx[m] * a.H + c.bbase + wb;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) row[acc_col(j, lane)] += acc.c[i][j][r];
+          for (int j = 0; j < kBlkB; ++j) row[acc_col(j, lane)] += acc.c[i][j][r];
         }
       }
-  }
+  };
+
+  persistent_tiles<true, RowColCtx>(sm, nTokTiles * nHTiles, nk, setup, epilogue);
 }
 
 // ---------------------------------------------------------------- dW rows = Gt hT^T
 
-__global__ __launch_bounds__(kThreads, 1) void dw_chunk_kernel(BwdArgs a, int c0) {
+__global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
   __shared__ RingSmem sm;
   const int Na = *a.n_active;
   const int vc = min(kBwdChunk, a.V - c0);
   const int nVocTiles = (vc + kTile - 1) / kTile;
   const int nHTiles = a.H / kTile;
-  const int nTiles = nVocTiles * nHTiles;
   const int band = nHTiles < 8 ? nHTiles : 8;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const size_t row_bytes = (size_t)a.Npad * 2;
   const int nk = ((Na + 63) & ~63) * 2 / kKBytes;
+  const int wa = wave_a0(wave);
+  const int wb = wave_b0(wave);
 
-  for (int round = 0;; ++round) {
-    const int u = virtual_tile(round, blockIdx.x, gridDim.x);
-    if (u >= nTiles) break;
+  auto setup = [&](int u, TileSrc& src, RowColCtx& c) {
     int vt, ht;
     tile_coords(u, nVocTiles, nHTiles, band, vt, ht);
-    const int vbase = vt * kTile;  // within the chunk
-    const int hbase = ht * kTile;
-    const uint8_t* a_src[4];
-    const uint8_t* b_src[4];
+    c.abase = vt * kTile;  // within the chunk
+    c.bbase = ht * kTile;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kDmaPerWave; ++q) {
       const int r = dma_row(q, wave, lane);
-      const int c = dma_chunk(q, wave, lane);
-      a_src[q] = reinterpret_cast<const uint8_t*>(a.Gt) + (size_t)(vbase + r) * row_bytes + 16 * c;
-      b_src[q] = reinterpret_cast<const uint8_t*>(a.hT) + (size_t)(hbase + r) * row_bytes + 16 * c;
+      const int ch = dma_chunk(q, wave, lane);
+      src.a[q] = reinterpret_cast<const uint8_t*>(a.Gt) + (size_t)(c.abase + r) * row_bytes + 16 * ch;
+      src.b[q] = reinterpret_cast<const uint8_t*>(a.hT) + (size_t)(c.bbase + r) * row_bytes + 16 * ch;
     }
-    Acc acc;
-    zero_acc(acc);
-    ring_mainloop<true>(sm, a_src, b_src, nk, acc);
+  };
 
-    const int wa = (wave & 1) * kWaveTile;
-    const int wb = (wave >> 1) * kWaveTile;
+  auto epilogue = [&](const RowColCtx& c, Acc& acc) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = c0 + vbase + wa + acc_row(i, r, lane);
+        const int v = c0 + c.abase + wa + acc_row(i, r, lane);
         if (v < a.V) {
-          float* row = a.dW + (size_t)v * a.H + hbase + wb;
+          float* row = a.dW + (size_t)v * a.H + c.bbase + wb;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) row[acc_col(j, lane)] = acc.c[i][j][r];
+          for (int j = 0; j < kBlkB; ++j) row[acc_col(j, lane)] = acc.c[i][j][r];
         }
       }
-  }
+  };
+
+  persistent_tiles<true, RowColCtx>(sm, nVocTiles * nHTiles, nk, setup, epilogue);
 }
 
 }  // namespace

@@ -26,73 +26,66 @@ namespace rlk {
 
 namespace {
 
+struct FwdCtx {
+  int vq;      // first vocabulary entry of this wave's quadrant
+  int tok[kBlkB];  // compacted token index of each of this lane's token columns
+  int tgt[kBlkB];  // their targets (-1: none or out of range)
+};
+
 template <bool kBF16>
-__global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
+__global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
   __shared__ RingSmem sm;
   const int Na = *a.n_active;
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nVocTiles = (a.V + kTile - 1) / kTile;
-  const int nTiles = nTokTiles * nVocTiles;
   const int band = nTokTiles < 8 ? nTokTiles : 8;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int elt = kBF16 ? 2 : 4;
-  const size_t row_bytes = (size_t)a.H * elt;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const size_t row_bytes = (size_t)a.H * (kBF16 ? 2 : 4);
   const int nk = (int)(row_bytes / kKBytes);
   const float c2 = a.inv_t * kLog2e;
+  const int wv = wave_a0(wave);  // vocabulary offset of the wave sub-tile
+  const int wt = wave_b0(wave);  // token offset of the wave sub-tile
 
-  for (int round = 0;; ++round) {
-    const int u = virtual_tile(round, blockIdx.x, gridDim.x);
-    if (u >= nTiles) break;
+  auto setup = [&](int u, TileSrc& src, FwdCtx& c) {
     int vt, tt;
     tile_coords(u, nVocTiles, nTokTiles, band, vt, tt);
     const int vbase = vt * kTile;
     const int tbase = tt * kTile;
-
-    const uint8_t* a_src[4];
-    const uint8_t* b_src[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kDmaPerWave; ++q) {
       const int r = dma_row(q, wave, lane);
-      const int c = dma_chunk(q, wave, lane);
+      const int ch = dma_chunk(q, wave, lane);
       const int v = min(vbase + r, a.V - 1);
       const int t = a.idx[min(tbase + r, Na - 1)];
-      a_src[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * c;
-      b_src[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * c;
+      src.a[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * ch;
+      src.b[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * ch;
     }
-
-    // this lane's four tokens (one per 32-column block of its wave quadrant)
-    const int wv = (wave & 1) * kWaveTile;  // vocabulary offset of the quadrant
-    const int wt = (wave >> 1) * kWaveTile; // token offset of the quadrant
-    int tok_i[4];
-    int tgt[4];
+    c.vq = vbase + wv;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      tok_i[j] = tbase + wt + acc_col(j, lane);
-      const int y = tok_i[j] < Na ? a.targets[a.idx[tok_i[j]]] : -1;
-      tgt[j] = (y >= 0 && y < a.V) ? y : -1;  // out of range: no tile captures it
+    for (int j = 0; j < kBlkB; ++j) {
+      c.tok[j] = tbase + wt + acc_col(j, lane);
+      const int y = c.tok[j] < Na ? a.targets[a.idx[c.tok[j]]] : -1;
+      c.tgt[j] = (y >= 0 && y < a.V) ? y : -1;  // out of range: no tile captures it
     }
+  };
 
-    Acc acc;
-    zero_acc(acc);
-    ring_mainloop<kBF16>(sm, a_src, b_src, nk, acc);
-
-    // ---- epilogue: per token, statistics of this wave's 128 vocabulary entries
-    const int vq = vbase + wv;          // first vocabulary entry of the quadrant
-    const int col = vq / kVocabPartial; // partial column (kWaveTile == kVocabPartial)
-    if (vq >= a.V) continue;            // quadrant entirely past the vocabulary
-    const bool tail = vq + kWaveTile > a.V;
+  // Per token column: statistics of this wave's 128 vocabulary entries.
+  auto epilogue = [&](const FwdCtx& c, Acc& acc) {
+    const int vq = c.vq;
+    if (vq >= a.V) return;  // quadrant entirely past the vocabulary
+    const int col = vq / kVocabPartial;  // partial column (kWaveA == kVocabPartial)
+    const bool tail = vq + kWaveA > a.V;
     const int half4 = 4 * (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kBlkB; ++j) {
       // target capture (rare: only when some lane's target falls in this quadrant)
-      const int d = tgt[j] - vq - half4;
+      const int d = c.tgt[j] - vq - half4;
       float zsel = 0.f;
       bool hit = false;
-      if (__builtin_amdgcn_ballot_w64(tgt[j] >= vq && tgt[j] < vq + kWaveTile)) {
+      if (__builtin_amdgcn_ballot_w64(c.tgt[j] >= vq && c.tgt[j] < vq + kWaveA)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const bool m = (d == 32 * i + 8 * (r >> 2) + (r & 3));
@@ -104,7 +97,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
       float x[64];
       float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float v = acc.c[i][j][r] * c2;
@@ -123,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
       }
       float s = (s0 + s1) + (s2 + s3);
       s = s + __shfl_xor(s, 32);
-      const int ti = tok_i[j];
+      const int ti = c.tok[j];
       if (ti < Na) {
         if (lane < 32) {
           a.part_max[(size_t)col * a.N + ti] = mx;
@@ -132,7 +125,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
         if (hit) a.target_logit[ti] = zsel * a.inv_t;
       }
     }
-  }
+  };
+
+  persistent_tiles<kBF16, FwdCtx>(sm, nTokTiles * nVocTiles, nk, setup, epilogue);
 }
 
 // One work-group of 256 threads merges 32 compacted rows: thread (row = tid & 31,
