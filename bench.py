@@ -39,6 +39,10 @@ WORKLOADS = {
     "large-hidden-head-N8192-H7168": (4, False),
 }
 DEFAULT_WORKLOAD = "qwen3-8b-head-N16384-T0.7"
+# Sources of the forward tile kernel: a stored traffic measurement is used only while these
+# are byte-identical to what was profiled.
+FWD_TILE_SOURCES = [f"linear_selected_token_amd/csrc/{f}"
+                    for f in ("fwd.hip", "common.hpp", "mainloop.hpp", "kernels.hpp")]
 
 
 def parse():
@@ -115,18 +119,22 @@ def cpu_baseline(w, mode, target_s):
 
 
 def traffic_for(kernel_src_files, name):
-    """HBM bytes per launch measured by rocprofv3 counters, if the kernel sources are
-    unchanged since the measurement (profiles/<name>.traffic.json)."""
-    path = os.path.join(ROOT, "profiles", f"{name}.traffic.json")
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/<name>.traffic.md), or
+    None once the kernel's sources differ from the ones that were profiled."""
+    path = os.path.join(ROOT, "profiles", f"{name}.traffic.md")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
+    rec = {}
+    for line in open(path):
+        k, sep, v = line.partition(":")
+        if sep and k.strip() in ("source_sha256", "bytes_per_launch"):
+            rec[k.strip()] = v.strip()
     h = hashlib.sha256()
     for f in kernel_src_files:
         h.update(open(os.path.join(ROOT, f), "rb").read())
-    if rec.get("source_sha256") != h.hexdigest():
+    if rec.get("source_sha256") != h.hexdigest() or "bytes_per_launch" not in rec:
         return None
-    return rec.get("bytes_per_launch")
+    return int(rec["bytes_per_launch"])
 
 
 def upload(w, dev):
@@ -205,7 +213,7 @@ def main():
     fwd_flop = 2.0 * Na * H * V
     bwd_flop = 6.0 * Na * H * V   # recompute + dL/dh + dL/dW, as executed
     tile_tflops = fwd_flop / (tile_ms * 1e-3) / 1e12
-    srcs = ["linear_selected_token_amd/csrc/fwd.hip", "linear_selected_token_amd/csrc/common.hpp"]
+    srcs = FWD_TILE_SOURCES
     roofline = {"bound": "mfma", "kernel": "fwd_tiles_kernel<bf16>",
                 "achieved": round(tile_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tile_tflops / PEAK_BF16_TFLOPS, 4),
