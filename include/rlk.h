@@ -31,6 +31,9 @@
  *     enqueued on it; nothing blocks the host; results are valid once the stream reaches
  *     that point.  The library never allocates or frees device memory.
  *   - dtype: RLK_BF16 (h and W hold bf16) or RLK_FP32 (float).  Accumulation is fp32.
+ *   - Size limits (beyond them: RLK_ERROR_UNSUPPORTED): N <= 2^22, V <= 2^22, H <= 2^16,
+ *     H a multiple of 64, and h at most 2^31 - 1 bytes (N * H * element size), because the
+ *     tile loads address token rows with 32-bit offsets from h.
  *   - Every argument check happens on the host before anything is enqueued, so a call
  *     that returns an error has written nothing.  N == 0 returns RLK_SUCCESS at once.
  *   - An active token whose target is outside [0, V) gets logp = NaN (checking it on the

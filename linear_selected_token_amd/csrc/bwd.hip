@@ -104,14 +104,18 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
     tile_coords(u, nVocTiles, nTokTiles, band, vt, tt);
     const int vbase = c0 + vt * kTile;
     const int tbase = tt * kTile;
+    src.a = uniform_ptr(static_cast<const uint8_t*>(a.W) + (size_t)vbase * row_bytes);
+    src.b = uniform_ptr(a.h);
+    src.a_bytes = operand_bytes((size_t)(a.V - vbase) * row_bytes);
+    src.b_bytes = operand_bytes((size_t)a.N * row_bytes);
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       const int r = dma_row(q, wave, lane);
       const int ch = dma_chunk(q, wave, lane);
       const int v = min(vbase + r, a.V - 1);
       const int t = a.idx[min(tbase + r, Na - 1)];
-      src.a[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * ch;
-      src.b[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * ch;
+      src.ao[q] = (uint32_t)((size_t)(v - vbase) * row_bytes) + 16 * ch;
+      src.bo[q] = (uint32_t)((size_t)t * row_bytes) + 16 * ch;
     }
     c.vbase = vbase;
 #pragma unroll
@@ -183,12 +187,16 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
     tile_coords(u, nTokTiles, nHTiles, band, tt, ht);
     c.abase = tt * kTile;
     c.bbase = ht * kTile;
+    src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)c.abase * row_bytes);
+    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Wt) + (size_t)c.bbase * row_bytes);
+    src.a_bytes = operand_bytes((size_t)(a.Npad - c.abase) * row_bytes);
+    src.b_bytes = operand_bytes((size_t)(a.H - c.bbase) * row_bytes);
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       const int r = dma_row(q, wave, lane);
       const int ch = dma_chunk(q, wave, lane);
-      src.a[q] = reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)(c.abase + r) * row_bytes + 16 * ch;
-      src.b[q] = reinterpret_cast<const uint8_t*>(a.Wt) + (size_t)(c.bbase + r) * row_bytes + 16 * ch;
+      src.ao[q] = (uint32_t)(r * row_bytes) + 16 * ch;
+      src.bo[q] = (uint32_t)(r * row_bytes) + 16 * ch;
     }
   };
 
@@ -230,12 +238,16 @@ __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
     tile_coords(u, nVocTiles, nHTiles, band, vt, ht);
     c.abase = vt * kTile;  // within the chunk
     c.bbase = ht * kTile;
+    src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gt) + (size_t)c.abase * row_bytes);
+    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.hT) + (size_t)c.bbase * row_bytes);
+    src.a_bytes = operand_bytes((size_t)(kBwdChunk - c.abase) * row_bytes);
+    src.b_bytes = operand_bytes((size_t)(a.H - c.bbase) * row_bytes);
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       const int r = dma_row(q, wave, lane);
       const int ch = dma_chunk(q, wave, lane);
-      src.a[q] = reinterpret_cast<const uint8_t*>(a.Gt) + (size_t)(c.abase + r) * row_bytes + 16 * ch;
-      src.b[q] = reinterpret_cast<const uint8_t*>(a.hT) + (size_t)(c.bbase + r) * row_bytes + 16 * ch;
+      src.ao[q] = (uint32_t)((size_t)r * row_bytes) + 16 * ch;
+      src.bo[q] = (uint32_t)((size_t)r * row_bytes) + 16 * ch;
     }
   };
 

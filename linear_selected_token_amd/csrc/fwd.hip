@@ -52,14 +52,18 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
     tile_coords(u, nVocTiles, nTokTiles, band, vt, tt);
     const int vbase = vt * kTile;
     const int tbase = tt * kTile;
+    src.a = uniform_ptr(static_cast<const uint8_t*>(a.W) + (size_t)vbase * row_bytes);
+    src.b = uniform_ptr(a.h);
+    src.a_bytes = operand_bytes((size_t)(a.V - vbase) * row_bytes);
+    src.b_bytes = operand_bytes((size_t)a.N * row_bytes);
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       const int r = dma_row(q, wave, lane);
       const int ch = dma_chunk(q, wave, lane);
       const int v = min(vbase + r, a.V - 1);
       const int t = a.idx[min(tbase + r, Na - 1)];
-      src.a[q] = static_cast<const uint8_t*>(a.W) + (size_t)v * row_bytes + 16 * ch;
-      src.b[q] = static_cast<const uint8_t*>(a.h) + (size_t)t * row_bytes + 16 * ch;
+      src.ao[q] = (uint32_t)((size_t)(v - vbase) * row_bytes) + 16 * ch;
+      src.bo[q] = (uint32_t)((size_t)t * row_bytes) + 16 * ch;
     }
     c.vq = vbase + wv;
 #pragma unroll

@@ -5,7 +5,7 @@
 //
 // Data movement (gfx950):
 //   - K advances 128 bytes per stage (64 bf16 / 32 fp32 values per row).  The direct-to-LDS
-//     loads (global_load_lds_dwordx4, 16 B per lane, no registers) then move whole 128-byte
+//     loads (buffer_load_dwordx4 ... lds, 16 B per lane, no registers) then move whole 128-byte
 //     lines, 8 rows per wave instruction; with 64-byte row pieces they move half as many
 //     bytes per clock, because every line touched is only half used;
 //   - the A panel (256 rows x 128 B = 32 KiB) has a ring of three stages and is loaded two
@@ -79,52 +79,90 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmemRead = 0x020;
-constexpr int kSchedDsRead = 0x100;
+// A scheduling fence: nothing moves across it, so code between two fences issues in
+// program order relative to the code around it.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Load sources of one tile: this lane's 16-byte chunk of panel row dma_row(q) at K = 0.
+// Load sources of one tile.  Each operand is a uniform base address (kept in scalar
+// registers) plus this lane's byte offset, per panel slot q, of its 16-byte chunk of panel
+// row dma_row(q) at K = 0; the stage's K offset is added as a scalar offset.  The loads are
+// buffer loads (raw, unswizzled) whose range check returns zeros for any offset at or past
+// the operand's byte size, so a load can never touch memory outside its operand.
 struct TileSrc {
-  const uint8_t* a[kDmaPerWave];
-  const uint8_t* b[kDmaPerWave];
+  const uint8_t* a;
+  const uint8_t* b;
+  uint32_t a_bytes, b_bytes;  // readable bytes from each base
+  uint32_t ao[kDmaPerWave];
+  uint32_t bo[kDmaPerWave];
 };
 
+// The same value in every lane, held in scalar registers.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// Readable bytes of an operand from a base, capped to what a 32-bit buffer offset reaches.
+__device__ __forceinline__ uint32_t operand_bytes(size_t n) {
+  return n < 0x7fffffffu ? (uint32_t)n : 0x7fffffffu;
+}
+
+// Buffer descriptor word 3 for raw (untyped, unswizzled) loads on gfx9-family parts.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // Loads of panel slots q in [q0, q0 + n) of stage k.
-__device__ __forceinline__ void dma_panel(uint8_t* panel, const uint8_t* const (&src)[kDmaPerWave],
-                                          int k, int q0, int n) {
+__device__ __forceinline__ void dma_panel(uint8_t* panel, const uint8_t* base, uint32_t bytes,
+                                          const uint32_t (&off)[kDmaPerWave], int k, int q0,
+                                          int n) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const size_t koff = (size_t)k * kKBytes;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes,
+                                        kRawBufferWord3);
+  const int koff = k * kKBytes;
 #pragma unroll
   for (int q = q0; q < q0 + n; ++q)
-    __builtin_amdgcn_global_load_lds(src[q] + koff, to_lds(panel + (wave * kDmaPerWave + q) * 1024),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, to_lds(panel + (wave * kDmaPerWave + q) * 1024), 16, (int)off[q], koff, 0, 0);
 }
 __device__ __forceinline__ void dma_a(RingSmem& sm, const TileSrc& t, int k, int q0 = 0,
                                       int n = kDmaPerWave) {
-  dma_panel(sm.a[k % kRingA], t.a, k, q0, n);
+  dma_panel(sm.a[k % kRingA], t.a, t.a_bytes, t.ao, k, q0, n);
 }
 __device__ __forceinline__ void dma_b(RingSmem& sm, const TileSrc& t, int k, int q0 = 0,
                                       int n = kDmaPerWave) {
-  dma_panel(sm.b[k % kRingB], t.b, k, q0, n);
+  dma_panel(sm.b[k % kRingB], t.b, t.b_bytes, t.bo, k, q0, n);
 }
 
 // The loads a tile's K loop expects in flight when it starts, in this order: A stage 0,
-// B stage 0, A stage 1.  May be issued early (for example under the previous tile's
-// epilogue) once every wave has passed the previous loop's final barrier.
+// B stage 0, the first half of B stage 1, A stage 1.  May be issued early (for example
+// under the previous tile's epilogue) once every wave has passed the previous loop's final
+// barrier.
 __device__ __forceinline__ void ring_prologue(RingSmem& sm, const TileSrc& t, int nk) {
   if (nk <= 0) return;
   dma_a(sm, t, 0);
   dma_b(sm, t, 0);
-  if (nk > 1) dma_a(sm, t, 1);
+  if (nk > 1) {
+    dma_b(sm, t, 1, 0, kDmaPerWave / 2);
+    dma_a(sm, t, 1);
+  }
 }
 
 // nk stages of the tile whose ring_prologue was issued.  On return all waves have passed a
 // barrier after their last LDS read, so the next tile's prologue may be issued.
+//
+// A stage is four 32-byte K slices.  Each slice issues its kBlkA x kBlkB MFMAs in a fixed
+// order with, between them, the LDS fragment reads of the next slice (in the order that
+// slice consumes them, so its first MFMA waits only for the first two reads) and up to
+// kHalf direct-to-LDS loads (one after every other MFMA, so no wave issues a burst of
+// loads while its matrix pipe drains).  Every instruction group is fenced: the order below
+// is the issue order.
 template <bool kBF16>
 __device__ __forceinline__ void ring_mainloop(RingSmem& sm, const TileSrc& t, int nk, Acc& acc) {
   if (nk <= 0) return;
   constexpr int kHalf = kDmaPerWave / 2;
+  constexpr int kReads = kBlkA + kBlkB;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wa = wave_a0(wave);
@@ -135,77 +173,81 @@ __device__ __forceinline__ void ring_mainloop(RingSmem& sm, const TileSrc& t, in
 #pragma unroll
   for (int s = 0; s < 4; ++s) off[s] = fr * kKBytes + 16 * ((2 * s + (lane >> 5)) ^ g);
 
-  auto frag = [&](int k, int s, u32x4 (&fa)[kBlkA], u32x4 (&fb)[kBlkB]) {
+  // Fragment read e of slice s of stage k: a[0], b[0 .. kBlkB), a[1 .. kBlkA).
+  auto read1 = [&](int k, int s, int e, u32x4 (&fa)[kBlkA], u32x4 (&fb)[kBlkB]) {
     const uint8_t* pa = sm.a[k % kRingA] + wa * kKBytes + off[s];
     const uint8_t* pb = sm.b[k % kRingB] + wb * kKBytes + off[s];
-#pragma unroll
-    for (int i = 0; i < kBlkA; ++i) fa[i] = *reinterpret_cast<const u32x4*>(pa + i * 32 * kKBytes);
-#pragma unroll
-    for (int j = 0; j < kBlkB; ++j) fb[j] = *reinterpret_cast<const u32x4*>(pb + j * 32 * kKBytes);
+    if (e == 0)
+      fa[0] = *reinterpret_cast<const u32x4*>(pa);
+    else if (e <= kBlkB)
+      fb[e - 1] = *reinterpret_cast<const u32x4*>(pb + (e - 1) * 32 * kKBytes);
+    else
+      fa[e - kBlkB] = *reinterpret_cast<const u32x4*>(pa + (e - kBlkB) * 32 * kKBytes);
   };
-  auto mma = [&](const u32x4 (&fa)[kBlkA], const u32x4 (&fb)[kBlkB]) {
-#pragma unroll
-    for (int i = 0; i < kBlkA; ++i)
-#pragma unroll
-      for (int j = 0; j < kBlkB; ++j) mma_step<kBF16>(acc.c[i][j], fa[i], fb[j]);
-  };
-  // Issue order inside one K slice (8 MFMA steps): the 6 LDS reads of the next slice go
-  // between the first MFMAs, the slice's loads (0 or kHalf) between later ones.  Each slice
-  // is its own scheduling region (sched_barrier at the end): otherwise the compiler pulls
-  // MFMAs of the next slice up behind the LDS reads that feed them, which collapses the
-  // register double-buffering into read-wait-MFMA chains.
-  auto interleave = [&](int n_dma) {
+  // One slice: MFMAs on (ca, cb); if rd, the reads of slice (k2, s2) into (na, nb); the n
+  // loads dma(0 .. n).
+  auto slice = [&](const u32x4 (&ca)[kBlkA], const u32x4 (&cb)[kBlkB], bool rd, int k2, int s2,
+                   u32x4 (&na)[kBlkA], u32x4 (&nb)[kBlkB], int n, auto&& dma) {
+    int r = 0;
 #pragma unroll
     for (int m = 0; m < kBlkA * kBlkB; ++m) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kBF16 ? 1 : 4, 0);
-      if (m < kBlkA + kBlkB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      if (m < n_dma) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      mma_step<kBF16>(acc.c[m / kBlkB][m % kBlkB], ca[m / kBlkB], cb[m % kBlkB]);
+      fence();
+      if ((m & 1) == 0 && (m >> 1) < n) {
+        dma(m >> 1);
+        fence();
+      }
+      if (rd && r < kReads) {
+        read1(k2, s2, r, na, nb);
+        ++r;
+        fence();
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (; rd && r < kReads; ++r) read1(k2, s2, r, na, nb);
+    fence();
   };
-  // Stage k with its first slice in (a0, b0).  Loads: B stage k + 1 in slices 0-1, A stage
-  // k + 2 in slices 2-3 (slice 3 runs after the barrier; A's ring slot for k + 2 stays free
-  // until stage k + 2).  The first slice of stage k + 1 is read after the barrier.
+  auto no_dma = [&](int) {};
+
   u32x4 a0[kBlkA], b0[kBlkB], a1[kBlkA], b1[kBlkB];
-  auto stage = [&](int k, bool dma_b_next, bool dma_a_next) {
-    if (dma_b_next) dma_b(sm, t, k + 1, 0, kHalf);
-    frag(k, 1, a1, b1);
-    mma(a0, b0);
-    interleave(dma_b_next ? kHalf : 0);
-    if (dma_b_next) dma_b(sm, t, k + 1, kHalf, kHalf);
-    frag(k, 2, a0, b0);
-    mma(a1, b1);
-    interleave(dma_b_next ? kHalf : 0);
-    if (dma_a_next) dma_a(sm, t, k + 2, 0, kHalf);
-    frag(k, 3, a1, b1);
-    mma(a0, b0);
-    interleave(dma_a_next ? kHalf : 0);
+  // A ring slot is free once every wave has passed the barrier after its last fragment
+  // read, so each load goes out right after the barrier that frees its slot:
+  //   slice 3 of stage k - 1 (after barrier k - 1) and slice 0 of stage k: B stage k + 1,
+  //     which stage k + 1 reads after barrier k (about one stage in flight);
+  //   slices 1 and 2 of stage k: A stage k + 2 (about one and a half stages in flight).
+  // Barrier k waits until only A stage k + 2 may still be in flight.
+  auto stage = [&](int k, bool more_b, bool more_a) {  // slices 0-2 of stage k
+    auto db = [&](int q) { dma_b(sm, t, k + 1, kHalf + q, 1); };
+    auto da0 = [&](int q) { dma_a(sm, t, k + 2, q, 1); };
+    auto da1 = [&](int q) { dma_a(sm, t, k + 2, kHalf + q, 1); };
+    slice(a0, b0, true, k, 1, a1, b1, more_b ? kHalf : 0, db);
+    slice(a1, b1, true, k, 2, a0, b0, more_a ? kHalf : 0, da0);
+    slice(a0, b0, true, k, 3, a1, b1, more_a ? kHalf : 0, da1);
   };
 
-  // stage 0 visible: A0 and B0 landed (A1 may still be in flight)
-  if (nk > 1) stage_barrier<kDmaPerWave>();
+  // stage 0 visible: A0 and B0 landed (half of B1 and A1 may still be in flight)
+  if (nk > 1) stage_barrier<kHalf + kDmaPerWave>();
   else stage_barrier<0>();
-  frag(0, 0, a0, b0);
+#pragma unroll
+  for (int e = 0; e < kReads; ++e) read1(0, 0, e, a0, b0);
+  fence();
   int k = 0;
   for (; k + 2 < nk; ++k) {
     stage(k, true, true);
-    stage_barrier<kHalf>();  // A k+1, B k+1 landed; half of A k+2 may be in flight
-    dma_a(sm, t, k + 2, kHalf, kHalf);
-    frag(k + 1, 0, a0, b0);
-    mma(a1, b1);
-    interleave(kHalf);
+    stage_barrier<kDmaPerWave>();  // A k+1, B k+1 landed; A k+2 may be in flight
+    const int kk = k;
+    auto db = [&](int q) { dma_b(sm, t, kk + 2, q, 1); };
+    slice(a1, b1, true, k + 1, 0, a0, b0, kHalf, db);
   }
-  if (k + 1 < nk) {  // stage nk - 2: only B nk - 1 left to load
+  if (k + 1 < nk) {  // stage nk - 2: only the second half of B nk - 1 left to load
     stage(k, true, false);
     stage_barrier<0>();
-    frag(k + 1, 0, a0, b0);
-    mma(a1, b1);
-    interleave(0);
+    slice(a1, b1, true, k + 1, 0, a0, b0, 0, no_dma);
     ++k;
   }
   stage(k, false, false);  // last stage
   stage_barrier<0>();
-  mma(a1, b1);
+  slice(a1, b1, false, 0, 0, a0, b0, 0, no_dma);
 }
 
 // Persistent tile driver.  Tiles u = virtual_tile(round, blockIdx.x, gridDim.x) for

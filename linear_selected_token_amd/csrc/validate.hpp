@@ -13,6 +13,8 @@ namespace rlk {
 constexpr int64_t kMaxTokens = int64_t(1) << 22;
 constexpr int64_t kMaxVocab = int64_t(1) << 22;
 constexpr int64_t kMaxHidden = int64_t(1) << 16;
+// The tile loads gather token rows of h with 32-bit buffer offsets from its base.
+constexpr int64_t kMaxHiddenStateBytes = (int64_t(1) << 31) - 1;
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -28,6 +30,7 @@ inline rlk_status_t check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
   if (dtype != RLK_BF16 && dtype != RLK_FP32) return RLK_ERROR_UNSUPPORTED;
   if (H % 64 != 0) return RLK_ERROR_UNSUPPORTED;
   if (N > kMaxTokens || V > kMaxVocab || H > kMaxHidden) return RLK_ERROR_UNSUPPORTED;
+  if (N * H * elt_size(dtype) > kMaxHiddenStateBytes) return RLK_ERROR_UNSUPPORTED;
   return RLK_SUCCESS;
 }
 

@@ -115,6 +115,10 @@ def test_forward_argument_errors(L):
     assert _fwd(lib, dt=2) == E.RLK_ERROR_UNSUPPORTED
     assert _fwd(lib, H=96) == E.RLK_ERROR_UNSUPPORTED
     assert _fwd(lib, N=1 << 23) == E.RLK_ERROR_UNSUPPORTED
+    # h of 2 GiB: past the 32-bit row offsets of the tile loads
+    assert _fwd(lib, N=1 << 18, H=4096) == E.RLK_ERROR_UNSUPPORTED
+    # one row less passes the shape checks (and stops at the workspace size, before any launch)
+    assert _fwd(lib, N=(1 << 18) - 1, H=4096, wsb=1000) == E.RLK_ERROR_WORKSPACE
     assert _fwd(lib, h=FAKE + 8) == E.RLK_ERROR_UNSUPPORTED
     assert _fwd(lib, W=FAKE + 4) == E.RLK_ERROR_UNSUPPORTED
     assert _fwd(lib, ws=FAKE + 16) == E.RLK_ERROR_UNSUPPORTED
