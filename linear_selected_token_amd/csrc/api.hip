@@ -41,8 +41,9 @@ T* carve(void* ws, size_t off) {
 const char* build_info_string() {
   static const char* s =
       "rlk linear_logp | arch gfx950 | compiler " __clang_version__
-      " | tile 256x256, K stage 128 B, 4 wave64 x 128x128, mfma 32x32x16 bf16 / 32x32x2 f32"
-      " | vocab partial 128 | merge 8 strided slices + fixed tree | bwd chunk 8192";
+      " | tile 256x256, K stage 128 B, 8 wave64 x 128x64, mfma 32x32x16 bf16 / 32x32x2 f32"
+      " | vocab partial 128 | merge 8 strided slices + fixed tree"
+      " | bwd chunk 16384, dh split at 8192";
   return s;
 }
 
@@ -198,6 +199,7 @@ rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* ta
   a.Wt = carve<uint16_t>(workspace, L.Wt);
   a.Gv = carve<uint16_t>(workspace, L.Gv);
   a.Gt = carve<uint16_t>(workspace, L.Gt);
+  a.dh1 = carve<float>(workspace, L.dh1);
   CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
   hipError_t e = launch_compact(c, st);
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
@@ -208,7 +210,7 @@ rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* ta
     e = launch_bwd_chunk(a, c0, grid, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
   }
-  return RLK_SUCCESS;
+  return dev_status(launch_bwd_finish(a, st));
 }
 
 }  // extern "C"

@@ -13,10 +13,14 @@
 //   wt_chunk     W rows of the chunk, transposed to [H, chunk] (zero past V);
 //   dlogits      the forward tile GEMM again, epilogue G = (g_t / T)(delta - p) rounded to
 //                bf16 and stored token-major (Gv) and vocabulary-major (Gt);
-//   dh_chunk     dh[idx] += Gv Wt^T  (K = the chunk, fp32 accumulation, added to dh in
-//                chunk order, so a token's dh row is batch-invariant);
+//   dh_chunk     Gv Wt^T in two K halves of kDhSplitK entries each (fp32 accumulation):
+//                the first half is added to dh[idx], the second to dh1 (compacted rows),
+//                both in chunk order; the halves are independent tiles, so a chunk
+//                fills the machine even when few tokens are active;
 //   dw_chunk     dW[chunk rows] = Gt hT^T  (K = the active tokens in ascending order).
-// Before the first chunk, bwd_prepare zeroes dh and writes hT = compacted h transposed.
+// Before the first chunk, bwd_prepare zeroes dh and dh1 and writes hT = compacted h
+// transposed; after the last, bwd_finish adds dh1 into dh.  The split point is a build
+// constant, so a token's dh row is the same sum in the same order in every batch.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mainloop.hpp"
@@ -104,6 +108,7 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
     tile_coords(u, nVocTiles, nTokTiles, band, vt, tt);
     const int vbase = c0 + vt * kTile;
     const int tbase = tt * kTile;
+    src.nk = nk;
     src.a = uniform_ptr(static_cast<const uint8_t*>(a.W) + (size_t)vbase * row_bytes);
     src.b = uniform_ptr(a.h);
     src.a_bytes = operand_bytes((size_t)(a.V - vbase) * row_bytes);
@@ -158,13 +163,14 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
     }
   };
 
-  persistent_tiles<true, DlogitsCtx>(sm, nTokTiles * nVocTiles, nk, setup, epilogue);
+  persistent_tiles<true, DlogitsCtx>(sm, nTokTiles * nVocTiles, setup, epilogue);
 }
 
 // ---------------------------------------------------------------- dh += Gv Wt^T
 
 struct RowColCtx {
   int abase, bbase;  // first A row and first B row of the tile
+  int half;          // dh_chunk: which K half of the chunk (0: into dh, 1: into dh1)
 };
 
 __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
@@ -172,25 +178,31 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
   const int Na = *a.n_active;
   const int vc = min(kBwdChunk, a.V - c0);
   const int kc = (vc + 63) & ~63;  // K extent (zero columns past V)
+  const int nhalf = kc > kDhSplitK ? 2 : 1;
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nHTiles = a.H / kTile;
+  const int per_half = nTokTiles * nHTiles;
   const int band = nHTiles < 8 ? nHTiles : 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const size_t row_bytes = (size_t)kBwdChunk * 2;
-  const int nk = kc * 2 / kKBytes;
   const int wa = wave_a0(wave);
   const int wb = wave_b0(wave);
 
   auto setup = [&](int u, TileSrc& src, RowColCtx& c) {
+    const int half = u >= per_half ? 1 : 0;
     int tt, ht;
-    tile_coords(u, nTokTiles, nHTiles, band, tt, ht);
+    tile_coords(u - half * per_half, nTokTiles, nHTiles, band, tt, ht);
     c.abase = tt * kTile;
     c.bbase = ht * kTile;
-    src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)c.abase * row_bytes);
-    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Wt) + (size_t)c.bbase * row_bytes);
-    src.a_bytes = operand_bytes((size_t)(a.Npad - c.abase) * row_bytes);
-    src.b_bytes = operand_bytes((size_t)(a.H - c.bbase) * row_bytes);
+    c.half = half;
+    const int k0 = half * kDhSplitK;  // first K entry of this half
+    const int k1 = half ? kc : min(kc, kDhSplitK);
+    src.nk = (k1 - k0) * 2 / kKBytes;
+    src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)c.abase * row_bytes + 2 * k0);
+    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Wt) + (size_t)c.bbase * row_bytes + 2 * k0);
+    src.a_bytes = operand_bytes((size_t)(a.Npad - c.abase) * row_bytes - 2 * k0);
+    src.b_bytes = operand_bytes((size_t)(a.H - c.bbase) * row_bytes - 2 * k0);
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       const int r = dma_row(q, wave, lane);
@@ -207,14 +219,26 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
       for (int r = 0; r < 16; ++r) {
         const int m = c.abase + wa + acc_row(i, r, lane);
         if (m < Na) {
-          float* row = a.dh + (size_t)a.idx[m] * a.H + c.bbase + wb;
+          float* row = c.half ? a.dh1 + (size_t)m * a.H + c.bbase + wb
+                              : a.dh + (size_t)a.idx[m] * a.H + c.bbase + wb;
 #pragma unroll
           for (int j = 0; j < kBlkB; ++j) row[acc_col(j, lane)] += acc.c[i][j][r];
         }
       }
   };
 
-  persistent_tiles<true, RowColCtx>(sm, nTokTiles * nHTiles, nk, setup, epilogue);
+  persistent_tiles<true, RowColCtx>(sm, per_half * nhalf, setup, epilogue);
+}
+
+// dh[idx[m]] += dh1[m] for every active row m (dh is only 4-byte aligned: scalar accesses).
+__global__ __launch_bounds__(256) void dh_finish_kernel(BwdArgs a) {
+  const int Na = *a.n_active;
+  const size_t n = (size_t)Na * a.H;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
+    const size_t m = e / a.H;
+    const size_t k = e - m * a.H;
+    a.dh[(size_t)a.idx[m] * a.H + k] += a.dh1[e];
+  }
 }
 
 // ---------------------------------------------------------------- dW rows = Gt hT^T
@@ -238,6 +262,8 @@ __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
     tile_coords(u, nVocTiles, nHTiles, band, vt, ht);
     c.abase = vt * kTile;  // within the chunk
     c.bbase = ht * kTile;
+    c.half = 0;
+    src.nk = nk;
     src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gt) + (size_t)c.abase * row_bytes);
     src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.hT) + (size_t)c.bbase * row_bytes);
     src.a_bytes = operand_bytes((size_t)(kBwdChunk - c.abase) * row_bytes);
@@ -265,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
       }
   };
 
-  persistent_tiles<true, RowColCtx>(sm, nVocTiles * nHTiles, nk, setup, epilogue);
+  persistent_tiles<true, RowColCtx>(sm, nVocTiles * nHTiles, setup, epilogue);
 }
 
 }  // namespace
@@ -280,6 +306,8 @@ hipError_t launch_zero(float* p, size_t n, hipStream_t stream) {
 hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = launch_zero(a.dh, (size_t)a.N * a.H, stream);
   if (e != hipSuccess) return e;
+  e = launch_zero(a.dh1, (size_t)a.Npad * a.H, stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(transpose_h_kernel, dim3(a.Npad / 64, a.H / 64), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -290,6 +318,11 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t s
   hipLaunchKernelGGL(dlogits_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   hipLaunchKernelGGL(dh_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   hipLaunchKernelGGL(dw_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(dh_finish_kernel, dim3(2048), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

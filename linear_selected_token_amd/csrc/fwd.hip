@@ -52,6 +52,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
     tile_coords(u, nVocTiles, nTokTiles, band, vt, tt);
     const int vbase = vt * kTile;
     const int tbase = tt * kTile;
+    src.nk = nk;
     src.a = uniform_ptr(static_cast<const uint8_t*>(a.W) + (size_t)vbase * row_bytes);
     src.b = uniform_ptr(a.h);
     src.a_bytes = operand_bytes((size_t)(a.V - vbase) * row_bytes);
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
     }
   };
 
-  persistent_tiles<kBF16, FwdCtx>(sm, nTokTiles * nVocTiles, nk, setup, epilogue);
+  persistent_tiles<kBF16, FwdCtx>(sm, nTokTiles * nVocTiles, setup, epilogue);
 }
 
 // One work-group of 256 threads merges 32 compacted rows: thread (row = tid & 31,

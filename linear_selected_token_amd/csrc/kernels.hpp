@@ -7,7 +7,8 @@
 namespace rlk {
 
 constexpr int kVocabPartial = 128;  // vocabulary entries per partial-statistics column
-constexpr int kBwdChunk = 8192;     // vocabulary entries per backward chunk (build constant)
+constexpr int kBwdChunk = 16384;    // vocabulary entries per backward chunk (build constant)
+constexpr int kDhSplitK = 8192;     // dL/dh sums each chunk's first and second 8192 entries apart
 
 struct CompactArgs {
   const uint8_t* mask;
@@ -60,6 +61,7 @@ struct BwdArgs {
   uint16_t* Wt;           // [H, kBwdChunk] one vocabulary chunk of W, transposed
   uint16_t* Gv;           // [Npad, kBwdChunk] dL/dz of the chunk, token-major
   uint16_t* Gt;           // [kBwdChunk, Npad] dL/dz of the chunk, vocabulary-major
+  float* dh1;             // [Npad, H] dL/dh from the second half of every chunk, compacted rows
 };
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
@@ -70,5 +72,6 @@ hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_zero(float* p, size_t n, hipStream_t stream);
 hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream);          // dh = 0, hT
 hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t stream);
+hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);          // dh += dh1
 
 }  // namespace rlk

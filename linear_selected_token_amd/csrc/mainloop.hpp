@@ -89,6 +89,7 @@ __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 // buffer loads (raw, unswizzled) whose range check returns zeros for any offset at or past
 // the operand's byte size, so a load can never touch memory outside its operand.
 struct TileSrc {
+  int nk;  // K stages of the tile
   const uint8_t* a;
   const uint8_t* b;
   uint32_t a_bytes, b_bytes;  // readable bytes from each base
@@ -252,11 +253,11 @@ __device__ __forceinline__ void ring_mainloop(RingSmem& sm, const TileSrc& t, in
 
 // Persistent tile driver.  Tiles u = virtual_tile(round, blockIdx.x, gridDim.x) for
 // round = 0, 1, ... while u < n_tiles.  setup(u, src, ctx) prepares a tile's load sources
-// and its epilogue context; epilogue(ctx, acc) consumes the accumulators (registers and
-// global memory only, no LDS).  The next tile's first loads are issued before the current
-// tile's epilogue, so their latency hides behind it.
+// (including its number of K stages) and its epilogue context; epilogue(ctx, acc) consumes
+// the accumulators (registers and global memory only, no LDS).  The next tile's first
+// loads are issued before the current tile's epilogue, so their latency hides behind it.
 template <bool kBF16, class Ctx, class Setup, class Epilogue>
-__device__ __forceinline__ void persistent_tiles(RingSmem& sm, int n_tiles, int nk, Setup setup,
+__device__ __forceinline__ void persistent_tiles(RingSmem& sm, int n_tiles, Setup setup,
                                                  Epilogue epilogue) {
   int round = 0;
   int u = virtual_tile(round, blockIdx.x, gridDim.x);
@@ -264,17 +265,17 @@ __device__ __forceinline__ void persistent_tiles(RingSmem& sm, int n_tiles, int 
   TileSrc src;
   Ctx ctx;
   setup(u, src, ctx);
-  ring_prologue(sm, src, nk);
+  ring_prologue(sm, src, src.nk);
   while (true) {
     Acc acc;
     zero_acc(acc);
-    ring_mainloop<kBF16>(sm, src, nk, acc);
+    ring_mainloop<kBF16>(sm, src, src.nk, acc);
     const int un = virtual_tile(++round, blockIdx.x, gridDim.x);
     const bool more = un < n_tiles;
     Ctx cur = ctx;
     if (more) {
       setup(un, src, ctx);
-      ring_prologue(sm, src, nk);
+      ring_prologue(sm, src, src.nk);
     }
     epilogue(cur, acc);
     if (!more) break;
