@@ -43,7 +43,7 @@ const char* build_info_string() {
       "rlk linear_logp | arch gfx950 | compiler " __clang_version__
       " | tile 256x256, K stage 128 B, 8 wave64 x 128x64, mfma 32x32x16 bf16 / 32x32x2 f32"
       " | vocab partial 128 | merge 8 strided slices + fixed tree"
-      " | bwd chunk 16384, dh split at 8192";
+      " | bwd chunk 32768, dh split at 16384";
   return s;
 }
 

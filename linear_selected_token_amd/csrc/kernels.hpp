@@ -7,8 +7,8 @@
 namespace rlk {
 
 constexpr int kVocabPartial = 128;  // vocabulary entries per partial-statistics column
-constexpr int kBwdChunk = 16384;    // vocabulary entries per backward chunk (build constant)
-constexpr int kDhSplitK = 8192;     // dL/dh sums each chunk's first and second 8192 entries apart
+constexpr int kBwdChunk = 32768;    // vocabulary entries per backward chunk (build constant)
+constexpr int kDhSplitK = 16384;    // dL/dh sums each chunk's first and second 16384 entries apart
 
 struct CompactArgs {
   const uint8_t* mask;

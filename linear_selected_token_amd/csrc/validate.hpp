@@ -61,7 +61,7 @@ inline FwdLayout fwd_layout(int64_t N, int64_t V) {
   return L;
 }
 
-constexpr int64_t kBwdChunkEntries = 16384;
+constexpr int64_t kBwdChunkEntries = 32768;
 
 inline int64_t bwd_npad(int64_t N) { return ((N > 0 ? N : 1) + 255) / 256 * 256; }
 

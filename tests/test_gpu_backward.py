@@ -34,10 +34,21 @@ def test_small_full(T):
                                          len_hi=300, seed=95, T=T)))
 
 
+def _chunking():
+    """(vocabulary entries per backward chunk, split point of dL/dh) of the loaded build."""
+    import re
+    import linear_selected_token_amd as rlk
+    m = re.search(r"bwd chunk (\d+), dh split at (\d+)", rlk.build_info())
+    assert m, rlk.build_info()
+    return int(m.group(1)), int(m.group(2))
+
+
 def test_two_chunks_ragged():
-    # vocabulary spans two backward chunks with a ragged tail; a ragged token tile
-    _full_compare(wl.make(wl.scaled_spec(5, N=300, H=256, V=8192 + 300, n_seq=2, len_lo=100,
-                                         len_hi=200, seed=96)))
+    # the vocabulary spans two backward chunks, both with entries past the dL/dh split point,
+    # the second with a ragged tail; a ragged token tile
+    chunk, split = _chunking()
+    _full_compare(wl.make(wl.scaled_spec(5, N=300, H=256, V=chunk + split + 300, n_seq=2,
+                                         len_lo=100, len_hi=200, seed=96)))
 
 
 def test_all_masked_backward():
