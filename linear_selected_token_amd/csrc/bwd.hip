@@ -29,10 +29,10 @@ namespace rlk {
 
 namespace {
 
-__device__ __forceinline__ uint16_t to_bf16(float x) {
-  uint32_t u = __builtin_bit_cast(uint32_t, x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // ---------------------------------------------------------------- 64 x 64 transposes
@@ -129,7 +129,8 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
       const bool ok = c.tok[j] < Na;
       const int t = ok ? a.idx[c.tok[j]] : 0;
       c.tgt[j] = ok ? a.targets[t] : -1;
-      c.lse2[j] = ok ? a.lse[t] * kLog2e : 0.f;
+      // padded columns: p = 2^(x - inf) = 0 exactly, so G is 0 whatever the logit
+      c.lse2[j] = ok ? a.lse[t] * kLog2e : INFINITY;
       c.gs[j] = ok ? -a.adv[t] * a.inv_t : 0.f;
     }
   };
@@ -142,23 +143,26 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
       for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          uint16_t o[4];
+          float G[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             const int v = c.vbase + wv + acc_row(i, r, lane);
             const float p = __builtin_amdgcn_exp2f(acc.c[i][j][r] * c2 - c.lse2[j]);
-            float G = c.gs[j] * ((v == c.tgt[j] ? 1.f : 0.f) - p);
-            if (v >= a.V) G = 0.f;
-            o[e] = to_bf16(G);
+            G[e] = c.gs[j] * ((v == c.tgt[j] ? 1.f : 0.f) - p);
+            if (v >= a.V) G[e] = 0.f;
           }
           const int vl = c.vbase - c0 + wv + acc_row(i, 4 * g, lane);  // first of 4 consecutive
           u32x2 pk;
-          pk[0] = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-          pk[1] = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+          pk[0] = pack_bf16(G[0], G[1]);
+          pk[1] = pack_bf16(G[2], G[3]);
           *reinterpret_cast<u32x2*>(a.Gv + (size_t)ti * kBwdChunk + vl) = pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a.Gt[(size_t)(vl + e) * a.Npad + ti] = o[e];
+          a.Gt[(size_t)(vl + 0) * a.Npad + ti] = (uint16_t)pk[0];
+          a.Gt[(size_t)(vl + 1) * a.Npad + ti] = (uint16_t)(pk[0] >> 16);
+          a.Gt[(size_t)(vl + 2) * a.Npad + ti] = (uint16_t)pk[1];
+          a.Gt[(size_t)(vl + 3) * a.Npad + ti] = (uint16_t)(pk[1] >> 16);
+          // one group of 4 rows at a time: keeps the live ranges short (no spills)
+          __builtin_amdgcn_sched_barrier(0);
         }
     }
   };
