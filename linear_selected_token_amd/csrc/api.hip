@@ -196,9 +196,7 @@ rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* ta
   a.dh = dh;
   a.dW = dW;
   a.hT = carve<uint16_t>(workspace, L.hT);
-  a.Wt = carve<uint16_t>(workspace, L.Wt);
   a.Gv = carve<uint16_t>(workspace, L.Gv);
-  a.Gt = carve<uint16_t>(workspace, L.Gt);
   a.dh1 = carve<float>(workspace, L.dh1);
   CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
   hipError_t e = launch_compact(c, st);

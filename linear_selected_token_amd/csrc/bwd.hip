@@ -10,14 +10,15 @@
 //   dL/dW_v    = (1/T) sum_t dL/dz[t,v] h_t
 //
 // The vocabulary is walked in chunks of kBwdChunk entries, in ascending order.  Per chunk:
-//   wt_chunk     W rows of the chunk, transposed to [H, chunk] (zero past V);
 //   dlogits      the forward tile GEMM again, epilogue G = (g_t / T)(delta - p) rounded to
-//                bf16 and stored token-major (Gv) and vocabulary-major (Gt);
-//   dh_chunk     Gv Wt^T in two K halves of kDhSplitK entries each (fp32 accumulation):
+//                bf16 and stored token-major (Gv);
+//   dh_chunk     Gv W[chunk] in two K halves of kDhSplitK entries each (fp32 accumulation;
+//                W rows are read as a K-strided panel, rows past V as zeros):
 //                the first half is added to dh[idx], the second to dh1 (compacted rows),
 //                both in chunk order; the halves are independent tiles, so a chunk
 //                fills the machine even when few tokens are active;
-//   dw_chunk     dW[chunk rows] = Gt hT^T  (K = the active tokens in ascending order).
+//   dw_chunk     dW[chunk rows] = Gv^T hT^T  (K = the active tokens in ascending order; Gv
+//                is read as a K-strided panel).
 // Before the first chunk, bwd_prepare zeroes dh and dh1 and writes hT = compacted h
 // transposed; after the last, bwd_finish adds dh1 into dh.  The split point is a build
 // constant, so a token's dh row is the same sum in the same order in every batch.
@@ -56,24 +57,6 @@ __global__ __launch_bounds__(256) void transpose_h_kernel(BwdArgs a) {
   }
 }
 
-// Wt[k][v] = W[c0 + v][k] for c0 + v < V, else 0.  Grid (kBwdChunk/64, H/64).
-__global__ __launch_bounds__(256) void transpose_w_kernel(BwdArgs a, int c0) {
-  __shared__ uint16_t t[64][65];
-  const int v0 = blockIdx.x * 64;
-  const int k0 = blockIdx.y * 64;
-  const uint16_t* W = static_cast<const uint16_t*>(a.W);
-  for (int e = threadIdx.x; e < 4096; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    const int v = c0 + v0 + r;
-    t[r][c] = v < a.V ? W[(size_t)v * a.H + k0 + c] : (uint16_t)0;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 4096; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    a.Wt[(size_t)(k0 + r) * kBwdChunk + v0 + c] = t[c][r];
-  }
-}
-
 __global__ __launch_bounds__(256) void zero_kernel(float* p, size_t n) {
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256)
     p[e] = 0.f;
@@ -109,6 +92,7 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
     const int vbase = c0 + vt * kTile;
     const int tbase = tt * kTile;
     src.nk = nk;
+    src.a_kstep = src.b_kstep = kKBytes;
     src.a = uniform_ptr(static_cast<const uint8_t*>(a.W) + (size_t)vbase * row_bytes);
     src.b = uniform_ptr(a.h);
     src.a_bytes = operand_bytes((size_t)(a.V - vbase) * row_bytes);
@@ -157,10 +141,6 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
           pk[0] = pack_bf16(G[0], G[1]);
           pk[1] = pack_bf16(G[2], G[3]);
           *reinterpret_cast<u32x2*>(a.Gv + (size_t)ti * kBwdChunk + vl) = pk;
-          a.Gt[(size_t)(vl + 0) * a.Npad + ti] = (uint16_t)pk[0];
-          a.Gt[(size_t)(vl + 1) * a.Npad + ti] = (uint16_t)(pk[0] >> 16);
-          a.Gt[(size_t)(vl + 2) * a.Npad + ti] = (uint16_t)pk[1];
-          a.Gt[(size_t)(vl + 3) * a.Npad + ti] = (uint16_t)(pk[1] >> 16);
           // one group of 4 rows at a time: keeps the live ranges short (no spills)
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -170,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
   persistent_tiles<true, DlogitsCtx>(sm, nTokTiles * nVocTiles, setup, epilogue);
 }
 
-// ---------------------------------------------------------------- dh += Gv Wt^T
+// ---------------------------------------------------------------- dh += Gv W[chunk]
 
 struct RowColCtx {
   int abase, bbase;  // first A row and first B row of the tile
@@ -190,6 +170,7 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const size_t row_bytes = (size_t)kBwdChunk * 2;
+  const uint32_t w_pitch = (uint32_t)a.H * 2;  // bytes per W row
   const int wa = wave_a0(wave);
   const int wb = wave_b0(wave);
 
@@ -203,16 +184,20 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
     const int k0 = half * kDhSplitK;  // first K entry of this half
     const int k1 = half ? kc : min(kc, kDhSplitK);
     src.nk = (k1 - k0) * 2 / kKBytes;
+    src.a_kstep = kKBytes;
+    src.b_kstep = 64 * w_pitch;
     src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)c.abase * row_bytes + 2 * k0);
-    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Wt) + (size_t)c.bbase * row_bytes + 2 * k0);
+    // W rows c0 + k0 ... of this tile's 256 columns; rows past V read as zeros
+    const size_t v0 = (size_t)c0 + k0;
+    src.b = uniform_ptr(static_cast<const uint8_t*>(a.W) + v0 * w_pitch + 2 * (size_t)c.bbase);
     src.a_bytes = operand_bytes((size_t)(a.Npad - c.abase) * row_bytes - 2 * k0);
-    src.b_bytes = operand_bytes((size_t)(a.H - c.bbase) * row_bytes - 2 * k0);
+    src.b_bytes = operand_bytes(((size_t)a.V - v0) * w_pitch - 2 * (size_t)c.bbase);
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       const int r = dma_row(q, wave, lane);
       const int ch = dma_chunk(q, wave, lane);
       src.ao[q] = (uint32_t)(r * row_bytes) + 16 * ch;
-      src.bo[q] = (uint32_t)(r * row_bytes) + 16 * ch;
+      src.bo[q] = (uint32_t)(tdma_row(q, wave, lane) * w_pitch) + 16 * tdma_chunk(q, wave, lane);
     }
   };
 
@@ -231,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
       }
   };
 
-  persistent_tiles<true, RowColCtx>(sm, per_half * nhalf, setup, epilogue);
+  persistent_tiles<true, RowColCtx, false, true>(sm, per_half * nhalf, setup, epilogue);
 }
 
 // dh[idx[m]] += dh1[m] for every active row m (dh is only 4-byte aligned: scalar accesses).
@@ -245,7 +230,7 @@ __global__ __launch_bounds__(256) void dh_finish_kernel(BwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- dW rows = Gt hT^T
+// ---------------------------------------------------------------- dW rows = Gv^T hT^T
 
 __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
   __shared__ RingSmem sm;
@@ -256,7 +241,8 @@ __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
   const int band = nHTiles < 8 ? nHTiles : 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const size_t row_bytes = (size_t)a.Npad * 2;
+  const size_t row_bytes = (size_t)a.Npad * 2;         // hT rows
+  const uint32_t g_pitch = (uint32_t)kBwdChunk * 2;   // Gv rows (one token each)
   const int nk = ((Na + 63) & ~63) * 2 / kKBytes;
   const int wa = wave_a0(wave);
   const int wb = wave_b0(wave);
@@ -268,15 +254,17 @@ __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
     c.bbase = ht * kTile;
     c.half = 0;
     src.nk = nk;
-    src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gt) + (size_t)c.abase * row_bytes);
+    src.a_kstep = 64 * g_pitch;  // 64 token rows of Gv per stage
+    src.b_kstep = kKBytes;
+    src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + 2 * (size_t)c.abase);
     src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.hT) + (size_t)c.bbase * row_bytes);
-    src.a_bytes = operand_bytes((size_t)(kBwdChunk - c.abase) * row_bytes);
+    src.a_bytes = operand_bytes((size_t)a.Npad * g_pitch - 2 * (size_t)c.abase);
     src.b_bytes = operand_bytes((size_t)(a.H - c.bbase) * row_bytes);
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       const int r = dma_row(q, wave, lane);
       const int ch = dma_chunk(q, wave, lane);
-      src.ao[q] = (uint32_t)((size_t)r * row_bytes) + 16 * ch;
+      src.ao[q] = (uint32_t)(tdma_row(q, wave, lane) * g_pitch) + 16 * tdma_chunk(q, wave, lane);
       src.bo[q] = (uint32_t)((size_t)r * row_bytes) + 16 * ch;
     }
   };
@@ -295,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
       }
   };
 
-  persistent_tiles<true, RowColCtx>(sm, nVocTiles * nHTiles, setup, epilogue);
+  persistent_tiles<true, RowColCtx, true, false>(sm, nVocTiles * nHTiles, setup, epilogue);
 }
 
 }  // namespace
@@ -318,7 +306,6 @@ hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t stream) {
   const int c0 = chunk * kBwdChunk;
-  hipLaunchKernelGGL(transpose_w_kernel, dim3(kBwdChunk / 64, a.H / 64), dim3(256), 0, stream, a, c0);
   hipLaunchKernelGGL(dlogits_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   hipLaunchKernelGGL(dh_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   hipLaunchKernelGGL(dw_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);

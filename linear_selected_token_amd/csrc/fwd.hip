@@ -53,6 +53,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
     const int vbase = vt * kTile;
     const int tbase = tt * kTile;
     src.nk = nk;
+    src.a_kstep = src.b_kstep = kKBytes;
     src.a = uniform_ptr(static_cast<const uint8_t*>(a.W) + (size_t)vbase * row_bytes);
     src.b = uniform_ptr(a.h);
     src.a_bytes = operand_bytes((size_t)(a.V - vbase) * row_bytes);

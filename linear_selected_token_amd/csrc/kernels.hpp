@@ -58,9 +58,7 @@ struct BwdArgs {
   float* dh;              // [N, H]
   float* dW;              // [V, H]
   uint16_t* hT;           // [H, Npad]   compacted h, transposed, zero past Na
-  uint16_t* Wt;           // [H, kBwdChunk] one vocabulary chunk of W, transposed
   uint16_t* Gv;           // [Npad, kBwdChunk] dL/dz of the chunk, token-major
-  uint16_t* Gt;           // [kBwdChunk, Npad] dL/dz of the chunk, vocabulary-major
   float* dh1;             // [Npad, H] dL/dh from the second half of every chunk, compacted rows
 };
 

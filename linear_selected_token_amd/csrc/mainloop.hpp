@@ -52,7 +52,49 @@ __device__ __forceinline__ int dma_chunk(int q, int wave, int lane) {
   return (lane & 7) ^ ring_swz(dma_row(q, wave, lane));
 }
 
+// K-strided ("T") panels, for an operand stored with K as its row index (K-rows of M
+// values): a stage holds 64 K-rows of the tile's 256 M values, 512 B per K-row.  Chunk c
+// (16 B = 8 M values) of K-row kk sits at physical chunk c ^ tswz(kk), so the transposing
+// fragment reads (4 K-rows x 16 M values per 16-lane group) hit distinct banks.  A wave's
+// load q fills K-rows 2 (wave kDmaPerWave + q) + (lane >> 5), the lane at physical chunk
+// lane & 31.
+__device__ __forceinline__ int tswz(int kk) { return 4 * (kk & 3); }
+__device__ __forceinline__ int tdma_row(int q, int wave, int lane) {
+  return 2 * (wave * kDmaPerWave + q) + (lane >> 5);
+}
+__device__ __forceinline__ int tdma_chunk(int q, int wave, int lane) {
+  return (lane & 31) ^ tswz(tdma_row(q, wave, lane));
+}
+// Byte offset in a T panel of this lane's first transposing read for the 32-row M block at
+// m0, K slice 0: K-row 8 (lane >> 5) + ((lane & 15) >> 2), M values m0 + 16 ((lane >> 4) & 1)
+// + 4 (lane & 3) .. + 3.  K slice s adds 16 s K-rows, the second read of a fragment 4 more;
+// neither changes kk & 3, so both are plain offsets.
+__device__ __forceinline__ int tfrag_off(int m0, int lane) {
+  const int kk = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int m = m0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  return kk * 512 + (((m >> 3) ^ tswz(kk)) << 4) + (m & 7) * 2;
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// One MFMA fragment from a T panel: two transposing reads give this lane 4 + 4 consecutive K
+// values of its M row (within a 16-lane group, lane i receives element e of the 4-element
+// words loaded by lanes 4e .. 4e + 3, i.e. K-row e at M value i).
+__device__ __forceinline__ u32x4 tfrag_read(const uint8_t* p) {
+  const lds_i16x4* q = (const lds_i16x4*)((__attribute__((address_space(3))) uint8_t*)(p));
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(q));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(q + 4 * 512 / 8));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+  const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+  u32x4 r;
+  r.x = l2.x;
+  r.y = l2.y;
+  r.z = h2.x;
+  r.w = h2.y;
+  return r;
+}
 
 __device__ __forceinline__ lds_ptr_t to_lds(void* p) {
   return (lds_ptr_t)((__attribute__((address_space(3))) uint8_t*)(p));
@@ -84,15 +126,18 @@ __device__ __forceinline__ void stage_barrier() {
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Load sources of one tile.  Each operand is a uniform base address (kept in scalar
-// registers) plus this lane's byte offset, per panel slot q, of its 16-byte chunk of panel
-// row dma_row(q) at K = 0; the stage's K offset is added as a scalar offset.  The loads are
+// registers), advanced by a_kstep / b_kstep bytes per K stage, plus this lane's byte offset,
+// per panel slot q, of the 16-byte chunk it loads at stage 0 (K-contiguous panels: row
+// dma_row(q), kstep 128; T panels: K-row tdma_row(q), kstep 64 K-rows).  The loads are
 // buffer loads (raw, unswizzled) whose range check returns zeros for any offset at or past
-// the operand's byte size, so a load can never touch memory outside its operand.
+// the operand's remaining bytes, so a load can never touch memory outside its operand, and
+// rows past the end of an operand read as zeros.
 struct TileSrc {
   int nk;  // K stages of the tile
   const uint8_t* a;
   const uint8_t* b;
-  uint32_t a_bytes, b_bytes;  // readable bytes from each base
+  uint64_t a_bytes, b_bytes;  // readable bytes from each base
+  uint32_t a_kstep, b_kstep;  // bytes per K stage
   uint32_t ao[kDmaPerWave];
   uint32_t bo[kDmaPerWave];
 };
@@ -105,48 +150,89 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
   return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 
-// Readable bytes of an operand from a base, capped to what a 32-bit buffer offset reaches.
-__device__ __forceinline__ uint32_t operand_bytes(size_t n) {
-  return n < 0x7fffffffu ? (uint32_t)n : 0x7fffffffu;
-}
+// Readable bytes of an operand from a base.
+__device__ __forceinline__ uint64_t operand_bytes(size_t n) { return (uint64_t)n; }
 
 // Buffer descriptor word 3 for raw (untyped, unswizzled) loads on gfx9-family parts.
 constexpr int kRawBufferWord3 = 0x00020000;
 
-// Loads of panel slots q in [q0, q0 + n) of stage k.
-__device__ __forceinline__ void dma_panel(uint8_t* panel, const uint8_t* base, uint32_t bytes,
-                                          const uint32_t (&off)[kDmaPerWave], int k, int q0,
-                                          int n) {
+// Loads of panel slots q in [q0, q0 + n) of stage k, as buffer_load_dwordx4 ... lds (16 B per
+// lane; lane i lands at byte 16 i of the slot's 1 KiB, the slot's LDS address in M0).
+//
+// kAsm == false (no K-strided panel in the loop): the compiler intrinsic, with the tile's base
+// fixed and the stage's offset k * kstep as the scalar offset.
+//
+// kAsm == true (a K-strided panel is read with transposing LDS reads): inline assembly.  Issued
+// through the intrinsic, a load into LDS makes the compiler drain every outstanding load
+// (s_waitcnt vmcnt(0)) before each transposing read of the same shared object, although the
+// ring slot being read is never one being filled.  The explicit waits of stage_barrier order
+// the loads against the reads instead; the memory clobber keeps LDS reads from moving across
+// a load, and waits the compiler computes for its own loads can only over-wait, because vmcnt
+// retires in order.  The base advances k * kstep bytes per stage (64-bit, so K-strided
+// operands of any size stay addressable), and the descriptor's byte count shrinks with it so
+// that rows past the operand's end still read as zeros.  A stage's first row always lies
+// inside the operand, so the remaining byte count is positive.
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+template <bool kAsm>
+__device__ __forceinline__ void dma_panel(uint8_t* panel, const uint8_t* base, uint64_t bytes,
+                                          uint32_t kstep, const uint32_t (&off)[kDmaPerWave],
+                                          int k, int q0, int n) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes,
-                                        kRawBufferWord3);
-  const int koff = k * kKBytes;
+  if constexpr (!kAsm) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(base), (short)0, (int)(bytes < 0x7fffffffu ? bytes : 0x7fffffffu),
+        kRawBufferWord3);
+    const int koff = k * (int)kstep;
 #pragma unroll
-  for (int q = q0; q < q0 + n; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, to_lds(panel + (wave * kDmaPerWave + q) * 1024), 16, (int)off[q], koff, 0, 0);
+    for (int q = q0; q < q0 + n; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, to_lds(panel + (wave * kDmaPerWave + q) * 1024), 16, (int)off[q], koff, 0, 0);
+  } else {
+    const uint64_t koff = (uint64_t)(uint32_t)k * kstep;
+    const uint64_t left = bytes - koff;
+    const uint64_t addr = reinterpret_cast<uint64_t>(base) + koff;
+    u32x4s rs;  // raw buffer descriptor: base, stride 0, byte count, word 3
+    rs.x = (uint32_t)addr;
+    rs.y = (uint32_t)(addr >> 32) & 0xffffu;
+    rs.z = (uint32_t)(left >> 31) != 0 ? 0x7fffffffu : (uint32_t)left;
+    rs.w = (uint32_t)kRawBufferWord3;
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(to_lds(panel));
+#pragma unroll
+    for (int q = q0; q < q0 + n; ++q) {
+      const uint32_t m0 = lds0 + (uint32_t)((wave * kDmaPerWave + q) * 1024);
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %1, %2, 0 offen lds"
+          :
+          : "s"(m0), "v"(off[q]), "s"(rs)
+          : "memory", "m0");
+    }
+  }
 }
+template <bool kAsm = false>
 __device__ __forceinline__ void dma_a(RingSmem& sm, const TileSrc& t, int k, int q0 = 0,
                                       int n = kDmaPerWave) {
-  dma_panel(sm.a[k % kRingA], t.a, t.a_bytes, t.ao, k, q0, n);
+  dma_panel<kAsm>(sm.a[k % kRingA], t.a, t.a_bytes, t.a_kstep, t.ao, k, q0, n);
 }
+template <bool kAsm = false>
 __device__ __forceinline__ void dma_b(RingSmem& sm, const TileSrc& t, int k, int q0 = 0,
                                       int n = kDmaPerWave) {
-  dma_panel(sm.b[k % kRingB], t.b, t.b_bytes, t.bo, k, q0, n);
+  dma_panel<kAsm>(sm.b[k % kRingB], t.b, t.b_bytes, t.b_kstep, t.bo, k, q0, n);
 }
 
 // The loads a tile's K loop expects in flight when it starts, in this order: A stage 0,
 // B stage 0, the first half of B stage 1, A stage 1.  May be issued early (for example
 // under the previous tile's epilogue) once every wave has passed the previous loop's final
 // barrier.
+template <bool kAsm = false>
 __device__ __forceinline__ void ring_prologue(RingSmem& sm, const TileSrc& t, int nk) {
   if (nk <= 0) return;
-  dma_a(sm, t, 0);
-  dma_b(sm, t, 0);
+  dma_a<kAsm>(sm, t, 0);
+  dma_b<kAsm>(sm, t, 0);
   if (nk > 1) {
-    dma_b(sm, t, 1, 0, kDmaPerWave / 2);
-    dma_a(sm, t, 1);
+    dma_b<kAsm>(sm, t, 1, 0, kDmaPerWave / 2);
+    dma_a<kAsm>(sm, t, 1);
   }
 }
 
@@ -159,8 +245,10 @@ __device__ __forceinline__ void ring_prologue(RingSmem& sm, const TileSrc& t, in
 // kHalf direct-to-LDS loads (one after every other MFMA, so no wave issues a burst of
 // loads while its matrix pipe drains).  Every instruction group is fenced: the order below
 // is the issue order.
-template <bool kBF16>
+template <bool kBF16, bool kTA, bool kTB>
 __device__ __forceinline__ void ring_mainloop(RingSmem& sm, const TileSrc& t, int nk, Acc& acc) {
+  static_assert(kBF16 || (!kTA && !kTB), "T panels hold bf16 operands");
+  constexpr bool kAsm = kTA || kTB;
   if (nk <= 0) return;
   constexpr int kHalf = kDmaPerWave / 2;
   constexpr int kReads = kBlkA + kBlkB;
@@ -173,17 +261,34 @@ __device__ __forceinline__ void ring_mainloop(RingSmem& sm, const TileSrc& t, in
   int off[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) off[s] = fr * kKBytes + 16 * ((2 * s + (lane >> 5)) ^ g);
+  int toa[kBlkA], tob[kBlkB];  // T panels: per-block offsets of the transposing reads
+#pragma unroll
+  for (int i = 0; i < kBlkA; ++i) toa[i] = kTA ? tfrag_off(wa + 32 * i, lane) : 0;
+#pragma unroll
+  for (int j = 0; j < kBlkB; ++j) tob[j] = kTB ? tfrag_off(wb + 32 * j, lane) : 0;
 
+  auto frag_a = [&](int k, int s, int i) __attribute__((always_inline)) -> u32x4 {
+    if constexpr (kTA)
+      return tfrag_read(sm.a[k % kRingA] + toa[i] + s * 16 * 512);
+    else
+      return *reinterpret_cast<const u32x4*>(sm.a[k % kRingA] + wa * kKBytes + off[s] +
+                                             i * 32 * kKBytes);
+  };
+  auto frag_b = [&](int k, int s, int j) __attribute__((always_inline)) -> u32x4 {
+    if constexpr (kTB)
+      return tfrag_read(sm.b[k % kRingB] + tob[j] + s * 16 * 512);
+    else
+      return *reinterpret_cast<const u32x4*>(sm.b[k % kRingB] + wb * kKBytes + off[s] +
+                                             j * 32 * kKBytes);
+  };
   // Fragment read e of slice s of stage k: a[0], b[0 .. kBlkB), a[1 .. kBlkA).
   auto read1 = [&](int k, int s, int e, u32x4 (&fa)[kBlkA], u32x4 (&fb)[kBlkB]) {
-    const uint8_t* pa = sm.a[k % kRingA] + wa * kKBytes + off[s];
-    const uint8_t* pb = sm.b[k % kRingB] + wb * kKBytes + off[s];
     if (e == 0)
-      fa[0] = *reinterpret_cast<const u32x4*>(pa);
+      fa[0] = frag_a(k, s, 0);
     else if (e <= kBlkB)
-      fb[e - 1] = *reinterpret_cast<const u32x4*>(pb + (e - 1) * 32 * kKBytes);
+      fb[e - 1] = frag_b(k, s, e - 1);
     else
-      fa[e - kBlkB] = *reinterpret_cast<const u32x4*>(pa + (e - kBlkB) * 32 * kKBytes);
+      fa[e - kBlkB] = frag_a(k, s, e - kBlkB);
   };
   // One slice: MFMAs on (ca, cb); if rd, the reads of slice (k2, s2) into (na, nb); the n
   // loads dma(0 .. n).
@@ -218,9 +323,9 @@ __device__ __forceinline__ void ring_mainloop(RingSmem& sm, const TileSrc& t, in
   //   slices 1 and 2 of stage k: A stage k + 2 (about one and a half stages in flight).
   // Barrier k waits until only A stage k + 2 may still be in flight.
   auto stage = [&](int k, bool more_b, bool more_a) {  // slices 0-2 of stage k
-    auto db = [&](int q) { dma_b(sm, t, k + 1, kHalf + q, 1); };
-    auto da0 = [&](int q) { dma_a(sm, t, k + 2, q, 1); };
-    auto da1 = [&](int q) { dma_a(sm, t, k + 2, kHalf + q, 1); };
+    auto db = [&](int q) { dma_b<kAsm>(sm, t, k + 1, kHalf + q, 1); };
+    auto da0 = [&](int q) { dma_a<kAsm>(sm, t, k + 2, q, 1); };
+    auto da1 = [&](int q) { dma_a<kAsm>(sm, t, k + 2, kHalf + q, 1); };
     slice(a0, b0, true, k, 1, a1, b1, more_b ? kHalf : 0, db);
     slice(a1, b1, true, k, 2, a0, b0, more_a ? kHalf : 0, da0);
     slice(a0, b0, true, k, 3, a1, b1, more_a ? kHalf : 0, da1);
@@ -237,7 +342,7 @@ __device__ __forceinline__ void ring_mainloop(RingSmem& sm, const TileSrc& t, in
     stage(k, true, true);
     stage_barrier<kDmaPerWave>();  // A k+1, B k+1 landed; A k+2 may be in flight
     const int kk = k;
-    auto db = [&](int q) { dma_b(sm, t, kk + 2, q, 1); };
+    auto db = [&](int q) { dma_b<kAsm>(sm, t, kk + 2, q, 1); };
     slice(a1, b1, true, k + 1, 0, a0, b0, kHalf, db);
   }
   if (k + 1 < nk) {  // stage nk - 2: only the second half of B nk - 1 left to load
@@ -256,7 +361,7 @@ __device__ __forceinline__ void ring_mainloop(RingSmem& sm, const TileSrc& t, in
 // (including its number of K stages) and its epilogue context; epilogue(ctx, acc) consumes
 // the accumulators (registers and global memory only, no LDS).  The next tile's first
 // loads are issued before the current tile's epilogue, so their latency hides behind it.
-template <bool kBF16, class Ctx, class Setup, class Epilogue>
+template <bool kBF16, class Ctx, bool kTA = false, bool kTB = false, class Setup, class Epilogue>
 __device__ __forceinline__ void persistent_tiles(RingSmem& sm, int n_tiles, Setup setup,
                                                  Epilogue epilogue) {
   int round = 0;
@@ -265,17 +370,17 @@ __device__ __forceinline__ void persistent_tiles(RingSmem& sm, int n_tiles, Setu
   TileSrc src;
   Ctx ctx;
   setup(u, src, ctx);
-  ring_prologue(sm, src, src.nk);
+  ring_prologue<kTA || kTB>(sm, src, src.nk);
   while (true) {
     Acc acc;
     zero_acc(acc);
-    ring_mainloop<kBF16>(sm, src, src.nk, acc);
+    ring_mainloop<kBF16, kTA, kTB>(sm, src, src.nk, acc);
     const int un = virtual_tile(++round, blockIdx.x, gridDim.x);
     const bool more = un < n_tiles;
     Ctx cur = ctx;
     if (more) {
       setup(un, src, ctx);
-      ring_prologue(sm, src, src.nk);
+      ring_prologue<kTA || kTB>(sm, src, src.nk);
     }
     epilogue(cur, acc);
     if (!more) break;
