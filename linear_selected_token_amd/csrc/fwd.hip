@@ -99,27 +99,34 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
             hit = hit || m;
           }
       }
-      // scale into log2 units and mask the vocabulary tail
-      float x[64];
-      float mx = -INFINITY;
+      // Column maximum in log2 units.  c2 > 0 and rounding is monotonic, so the maximum of
+      // the scaled logits is the scaled maximum of the accumulators: take it on the raw
+      // values (entries past the vocabulary set to -inf in place), then form each exponent
+      // with one fma.
+      if (tail) {
+#pragma unroll
+        for (int i = 0; i < kBlkA; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (vq + acc_row(i, r, lane) >= a.V) acc.c[i][j][r] = -INFINITY;
+      }
+      float am = -INFINITY;
 #pragma unroll
       for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = acc.c[i][j][r] * c2;
-          if (tail && vq + acc_row(i, r, lane) >= a.V) v = -INFINITY;
-          x[16 * i + r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int r = 0; r < 16; ++r) am = fmaxf(am, acc.c[i][j][r]);
+      am = fmaxf(am, __shfl_xor(am, 32));
+      const float mx = am * c2;
       float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-      for (int e = 0; e < 64; e += 4) {
-        s0 += __builtin_amdgcn_exp2f(x[e + 0] - mx);
-        s1 += __builtin_amdgcn_exp2f(x[e + 1] - mx);
-        s2 += __builtin_amdgcn_exp2f(x[e + 2] - mx);
-        s3 += __builtin_amdgcn_exp2f(x[e + 3] - mx);
-      }
+      for (int i = 0; i < kBlkA; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc.c[i][j][r + 0], c2, -mx));
+          s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc.c[i][j][r + 1], c2, -mx));
+          s2 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc.c[i][j][r + 2], c2, -mx));
+          s3 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc.c[i][j][r + 3], c2, -mx));
+        }
       float s = (s0 + s1) + (s2 + s3);
       s = s + __shfl_xor(s, 32);
       const int ti = c.tok[j];
