@@ -149,6 +149,32 @@ rlk_status_t rlk_linear_logp_partials(const void* h, const void* W, const int32_
                                       float* part_max, float* part_sum, float* target_logit,
                                       void* stream);
 
+/* Partial statistics for one vocabulary shard, for vocabulary-parallel scoring (RL-Kernel
+ * integration roadmap for vime, "Operator Integration Plan", linear_logp: the hook passes the
+ * local vocabulary start and the global vocabulary size, and the backend makes the
+ * vocabulary-shard merge of local max, local sum-exp and target logit explicit).
+ *   W            [V,H] dtype   rows vocab_start .. vocab_start + V - 1 of the full LM head
+ *   vocab_start               global index of W's first row; a multiple of RLK_VOCAB_PARTIAL
+ *   V_global                  size of the full vocabulary; vocab_start + V <= V_global, and V
+ *                             is a multiple of RLK_VOCAB_PARTIAL unless the shard ends at
+ *                             V_global (the last shard)
+ *   part_max, part_sum        the full-vocabulary arrays, [rlk_num_vocab_partials(V_global), N]:
+ *                             this call writes the shard's columns vocab_start / 128 ..
+ *   target_logit [N]          written for tokens whose target lies in this shard, untouched
+ *                             for the others (rlk_compact_active sets it to NaN first)
+ * Other arguments as for rlk_linear_logp_partials, which is this call with vocab_start = 0
+ * and V_global = V.  Once every shard has run (in any order, on any streams ordered before
+ * the merge), rlk_linear_logp_merge with V_global gives logp and lse bit-identical to the
+ * single-call forward: a column's statistics are the same arithmetic whichever call computes
+ * it.  Errors: RLK_ERROR_INVALID_VALUE for a shard outside [0, V_global),
+ * RLK_ERROR_UNSUPPORTED for a shard that would split a column. */
+rlk_status_t rlk_linear_logp_partials_shard(const void* h, const void* W, const int32_t* targets,
+                                            const int32_t* idx, const int32_t* n_active,
+                                            int64_t N, int64_t H, int64_t V, int64_t vocab_start,
+                                            int64_t V_global, int dtype, float temperature,
+                                            float* part_max, float* part_sum,
+                                            float* target_logit, void* stream);
+
 /* Fixed-order merge: for i < Na, M = max_j part_max[j*N+i], S = sum_j part_sum[j*N+i] *
  * 2^(part_max[j*N+i] - M) in one fixed association over j = 0..J-1 (J =
  * rlk_num_vocab_partials(V)), lse = (M + log2 S) * ln 2, logp = target_logit[i] - lse;

@@ -18,4 +18,5 @@ from .ops import (  # noqa: E402,F401
     rlk_linear_logp_fwd,
     rlk_linear_logp_merge,
     rlk_linear_logp_partials,
+    rlk_linear_logp_partials_shard,
 )

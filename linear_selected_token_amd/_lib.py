@@ -37,6 +37,8 @@ SIGNATURES = {
     "rlk_compact_active": (_int, [_p, _i64, _p, _p, _p, _p, _p, _p]),
     "rlk_linear_logp_partials": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p,
                                         _p, _p]),
+    "rlk_linear_logp_partials_shard": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64,
+                                              _int, _f, _p, _p, _p, _p]),
     "rlk_linear_logp_merge": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p]),
 }
 

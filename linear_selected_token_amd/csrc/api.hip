@@ -101,14 +101,17 @@ rlk_status_t rlk_compact_active(const uint8_t* mask, int64_t N, int32_t* idx, in
   return dev_status(launch_compact(a, static_cast<hipStream_t>(stream)));
 }
 
-rlk_status_t rlk_linear_logp_partials(const void* h, const void* W, const int32_t* targets,
-                                      const int32_t* idx, const int32_t* n_active, int64_t N,
-                                      int64_t H, int64_t V, int dtype, float temperature,
-                                      float* part_max, float* part_sum, float* target_logit,
-                                      void* stream) {
+rlk_status_t rlk_linear_logp_partials_shard(const void* h, const void* W, const int32_t* targets,
+                                            const int32_t* idx, const int32_t* n_active,
+                                            int64_t N, int64_t H, int64_t V, int64_t vocab_start,
+                                            int64_t V_global, int dtype, float temperature,
+                                            float* part_max, float* part_sum,
+                                            float* target_logit, void* stream) {
   rlk_status_t s = check_shape(N, H, V, dtype);
   if (s != RLK_SUCCESS) return s;
   s = check_temperature(temperature);
+  if (s != RLK_SUCCESS) return s;
+  s = check_shard(V, vocab_start, V_global);
   if (s != RLK_SUCCESS) return s;
   if (N == 0) return RLK_SUCCESS;
   if (!h || !W || !targets || !idx || !n_active || !part_max || !part_sum || !target_logit)
@@ -121,8 +124,18 @@ rlk_status_t rlk_linear_logp_partials(const void* h, const void* W, const int32_
   hipError_t e = persistent_grid(&grid);
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
   FwdTileArgs a{h, W, targets, idx, n_active, (int)N, (int)H, (int)V,
-                (float)(1.0 / (double)temperature), part_max, part_sum, target_logit};
+                (float)(1.0 / (double)temperature), part_max, part_sum, target_logit,
+                (int)vocab_start};
   return dev_status(launch_fwd_tiles(a, dtype == RLK_BF16, grid, static_cast<hipStream_t>(stream)));
+}
+
+rlk_status_t rlk_linear_logp_partials(const void* h, const void* W, const int32_t* targets,
+                                      const int32_t* idx, const int32_t* n_active, int64_t N,
+                                      int64_t H, int64_t V, int dtype, float temperature,
+                                      float* part_max, float* part_sum, float* target_logit,
+                                      void* stream) {
+  return rlk_linear_logp_partials_shard(h, W, targets, idx, n_active, N, H, V, 0, V, dtype,
+                                        temperature, part_max, part_sum, target_logit, stream);
 }
 
 rlk_status_t rlk_linear_logp_merge(const float* part_max, const float* part_sum,

@@ -71,8 +71,9 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
 #pragma unroll
     for (int j = 0; j < kBlkB; ++j) {
       c.tok[j] = tbase + wt + acc_col(j, lane);
-      const int y = c.tok[j] < Na ? a.targets[a.idx[c.tok[j]]] : -1;
-      c.tgt[j] = (y >= 0 && y < a.V) ? y : -1;  // out of range: no tile captures it
+      // target as a row of this W (out of range or in another vocabulary shard: none)
+      const int y = c.tok[j] < Na ? a.targets[a.idx[c.tok[j]]] - a.vstart : -1;
+      c.tgt[j] = (y >= 0 && y < a.V) ? y : -1;
     }
   };
 
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
   auto epilogue = [&](const FwdCtx& c, Acc& acc) {
     const int vq = c.vq;
     if (vq >= a.V) return;  // quadrant entirely past the vocabulary
-    const int col = vq / kVocabPartial;  // partial column (kWaveA == kVocabPartial)
+    const int col = (a.vstart + vq) / kVocabPartial;  // global partial column (kWaveA == kVocabPartial)
     const bool tail = vq + kWaveA > a.V;
     const int half4 = 4 * (lane >> 5);
 #pragma unroll

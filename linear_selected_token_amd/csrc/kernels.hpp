@@ -31,6 +31,7 @@ struct FwdTileArgs {
   float* part_max;
   float* part_sum;
   float* target_logit;
+  int vstart;  // global vocabulary index of W row 0 (a multiple of kVocabPartial)
 };
 
 struct MergeArgs {

@@ -34,6 +34,18 @@ inline rlk_status_t check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
   return RLK_SUCCESS;
 }
 
+// A vocabulary shard [vocab_start, vocab_start + V) of a vocabulary of V_global entries.  Its
+// partial columns must be whole columns of the full vocabulary: it starts on a column boundary
+// and, unless it is the last shard, ends on one.
+inline rlk_status_t check_shard(int64_t V, int64_t vocab_start, int64_t V_global) {
+  if (vocab_start < 0 || V_global <= 0 || vocab_start + V > V_global)
+    return RLK_ERROR_INVALID_VALUE;
+  if (V_global > kMaxVocab) return RLK_ERROR_UNSUPPORTED;
+  if (vocab_start % 128 != 0) return RLK_ERROR_UNSUPPORTED;
+  if (V % 128 != 0 && vocab_start + V != V_global) return RLK_ERROR_UNSUPPORTED;
+  return RLK_SUCCESS;
+}
+
 inline rlk_status_t check_temperature(float T) {
   if (!isfinite(T) || !(T > 0.f)) return RLK_ERROR_INVALID_VALUE;
   // 1/T must be finite and nonzero in fp32

@@ -151,6 +151,18 @@ def rlk_linear_logp_partials(h, W, targets, idx, n_active, temperature, part_max
             "rlk_linear_logp_partials")
 
 
+def rlk_linear_logp_partials_shard(h, W_shard, targets, idx, n_active, vocab_start, V_global,
+                                   temperature, part_max, part_sum, target_logit) -> None:
+    """Partial statistics of the vocabulary rows vocab_start .. vocab_start + len(W_shard) - 1,
+    written into the full-vocabulary part_max / part_sum ([num_vocab_partials(V_global), N])."""
+    N, H = h.shape
+    V = W_shard.shape[0]
+    L.check(L.lib().rlk_linear_logp_partials_shard(
+        _vp(h), _vp(W_shard), _vp(targets), _vp(idx), _vp(n_active), N, H, V, int(vocab_start),
+        int(V_global), _dtype_code(h), float(temperature), _vp(part_max), _vp(part_sum),
+        _vp(target_logit), _stream(h.device)), "rlk_linear_logp_partials_shard")
+
+
 def rlk_linear_logp_merge(part_max, part_sum, target_logit, idx, n_active, N, V, logp,
                           lse=None) -> None:
     L.check(L.lib().rlk_linear_logp_merge(_vp(part_max), _vp(part_sum), _vp(target_logit),

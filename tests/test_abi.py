@@ -160,3 +160,23 @@ def test_building_block_argument_errors(L):
         E.RLK_ERROR_INVALID_VALUE
     assert lib.rlk_linear_logp_merge(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 10, FAKE, None, None) == \
         E.RLK_SUCCESS
+
+
+def _shard(lib, V=256, start=0, Vg=1000, N=4, H=64, h=FAKE, idx=FAKE):
+    return lib.rlk_linear_logp_partials_shard(h, FAKE, FAKE, idx, FAKE, N, H, V, start, Vg, 0,
+                                              1.0, FAKE, FAKE, FAKE, None)
+
+
+def test_vocabulary_shard_argument_errors(L):
+    # every case below is decided on the host, before anything could be launched
+    lib = L.lib()
+    E = L
+    assert _shard(lib, start=-128) == E.RLK_ERROR_INVALID_VALUE       # before the vocabulary
+    assert _shard(lib, start=768, V=256) == E.RLK_ERROR_INVALID_VALUE  # past its end
+    assert _shard(lib, Vg=0) == E.RLK_ERROR_INVALID_VALUE
+    assert _shard(lib, start=64) == E.RLK_ERROR_UNSUPPORTED            # splits a column
+    assert _shard(lib, V=200, start=128) == E.RLK_ERROR_UNSUPPORTED    # ends inside a column
+    assert _shard(lib, Vg=1 << 23, V=256) == E.RLK_ERROR_UNSUPPORTED
+    # a ragged last shard passes the shard checks (and stops at the missing index buffer)
+    assert _shard(lib, V=1000 - 896, start=896, idx=None) == E.RLK_ERROR_INVALID_VALUE
+    assert _shard(lib, N=0, V=1000 - 896, start=896) == E.RLK_SUCCESS
