@@ -51,7 +51,10 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
-    p.add_argument("--mode", default="fwdbwd", choices=["fwd", "fwdbwd"])
+    p.add_argument("--mode", default="fwdbwd", choices=["fwd", "fwdbwd", "logits"],
+                   help="fwdbwd: the fused forward and backward (the headline); fwd: forward "
+                        "only; logits: log-prob from existing bf16 logits of the same shape "
+                        "(an HBM-bound path, reported against HBM bandwidth)")
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample (0 disables it)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -149,6 +152,53 @@ def upload(w, dev):
             torch.from_numpy(w.mask).to(dev), torch.from_numpy(w.adv).to(dev))
 
 
+def bench_logits(args, w):
+    """Log-prob from existing logits: bf16 logits [N, V] of the workload's shape, drawn on the
+    device from a seeded generator (synthetic), resident before the timed region."""
+    import torch
+    import linear_selected_token_amd as rlk
+    dev = torch.device("cuda", 0)
+    N, V, T, Na = w.N, w.V, w.T, w.n_active
+    g = torch.Generator(device=dev)
+    g.manual_seed(1003)
+    logits = torch.empty((N, V), dtype=torch.bfloat16, device=dev)
+    for r0 in range(0, N, 1024):
+        logits[r0:r0 + 1024] = (torch.randn((min(1024, N - r0), V), generator=g, device=dev)
+                                * 3.0).to(torch.bfloat16)
+    targets = torch.from_numpy(w.targets).to(dev)
+    mask = torch.from_numpy(w.mask).to(dev)
+    ws = torch.empty(rlk.logits_workspace_bytes(N, V), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        rlk.rlk_logp_from_logits(logits, targets, mask, T, workspace=ws)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        rlk.rlk_logp_from_logits(logits, targets, mask, T, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # active logits rows once; mask, index and target reads; logp and lse written
+    nbytes = Na * V * 2 + N + 4 * N + 4 * Na + 8 * N
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "active tokens/sec, log-prob from existing bf16 logits",
+        "value": round(Na / (ms * 1e-3), 1), "unit": "active tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0, 3^2) logits rounded to bf16",
+        "config": {"workload": args.workload, "mode": "logits", "N": N, "V": V, "T": T,
+                   "n_active": Na, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "logits_logp_kernel<bf16>",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_step": nbytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -163,6 +213,9 @@ def main():
 
     dev = torch.device("cuda", 0)
     w = make_workload(args.workload)
+    if args.mode == "logits":
+        bench_logits(args, w)
+        return
     N, H, V, T = w.N, w.H, w.V, w.T
     Na = w.n_active
     h, W, targets, mask, adv = upload(w, dev)

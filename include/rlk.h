@@ -106,6 +106,26 @@ rlk_status_t rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* ta
                                  float temperature, float* logp, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* Selected-token log-prob from logits that already exist: the reference-scoring sibling of
+ * the fused path, with the same log-softmax contract (RL-Kernel integration roadmap for vime,
+ * "Operator Integration Plan", logp Reference Scoring: a deterministic policy with a fixed
+ * row-local reduction topology and an explicit max / sum-exp contract).
+ *   logits   [N, ld] dtype    row t holds the logits of token t in entries 0 .. V-1 (entries
+ *                             V .. ld-1 are ignored); ld >= V, ld * element size a multiple
+ *                             of 16 bytes, logits 16-byte aligned
+ *   targets, mask, temperature, logp, lse: as for rlk_linear_logp_fwd (z = logit / T)
+ *   workspace: at least rlk_logp_from_logits_workspace_size bytes (the active-row index).
+ * V is at most 1,024,000 (a row's column statistics are kept on chip).
+ * Per active token and 128-entry vocabulary column the column maximum and sum-exp are formed
+ * in log2 units exactly as in rlk_linear_logp_partials, then merged in the association of
+ * rlk_linear_logp_merge: a token's result depends only on its own row and is bit-identical in
+ * any batch.  An active token whose target is outside [0, V) gets logp = NaN. */
+rlk_status_t rlk_logp_from_logits_workspace_size(int64_t N, int64_t V, size_t* bytes);
+rlk_status_t rlk_logp_from_logits(const void* logits, int64_t ld, const int32_t* targets,
+                                  const uint8_t* mask, int64_t N, int64_t V, int dtype,
+                                  float temperature, float* logp, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Backward of L = -sum_t mask_t * adv_t * logp_t (bf16 only).
  *   h, W, targets, mask, N, H, V, dtype, temperature: exactly as passed to the forward
  *   adv      [N]    float     per-token advantage (the upstream gradient is -adv_t at

@@ -12,6 +12,7 @@ from .ops import (  # noqa: E402,F401
     bwd_workspace_bytes,
     fwd_workspace_bytes,
     linear_logp,
+    logits_workspace_bytes,
     num_vocab_partials,
     rlk_compact_active,
     rlk_linear_logp_bwd,
@@ -19,4 +20,5 @@ from .ops import (  # noqa: E402,F401
     rlk_linear_logp_merge,
     rlk_linear_logp_partials,
     rlk_linear_logp_partials_shard,
+    rlk_logp_from_logits,
 )

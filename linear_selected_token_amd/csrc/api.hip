@@ -154,6 +154,31 @@ rlk_status_t rlk_linear_logp_merge(const float* part_max, const float* part_sum,
   return dev_status(launch_fwd_merge(a, static_cast<hipStream_t>(stream)));
 }
 
+rlk_status_t rlk_logp_from_logits_workspace_size(int64_t N, int64_t V, size_t* bytes) {
+  if (!bytes) return RLK_ERROR_INVALID_VALUE;
+  if (N < 0 || V <= 0) return RLK_ERROR_INVALID_VALUE;
+  if (N > kMaxTokens || V > kMaxLogitsVocab) return RLK_ERROR_UNSUPPORTED;
+  *bytes = logits_layout(N).total;
+  return RLK_SUCCESS;
+}
+
+rlk_status_t rlk_logp_from_logits(const void* logits, int64_t ld, const int32_t* targets,
+                                  const uint8_t* mask, int64_t N, int64_t V, int dtype,
+                                  float temperature, float* logp, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  rlk_status_t s = check_logits(logits, N, V, ld, dtype, temperature, targets, mask, logp, lse,
+                                workspace, workspace_bytes);
+  if (s != RLK_SUCCESS || N == 0) return s;
+  const LogitsLayout L = logits_layout(N);
+  int32_t* idx = carve<int32_t>(workspace, L.idx);
+  int32_t* na = carve<int32_t>(workspace, L.n_active);
+  s = rlk_compact_active(mask, N, idx, na, nullptr, logp, lse, stream);
+  if (s != RLK_SUCCESS) return s;
+  LogitsArgs a{logits, targets, idx, na, (int)N, (int)V, (int)ld,
+               (float)(1.0 / (double)temperature), logp, lse};
+  return dev_status(launch_logits_logp(a, dtype == RLK_BF16, static_cast<hipStream_t>(stream)));
+}
+
 rlk_status_t rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* targets,
                                  const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
                                  float temperature, float* logp, float* lse, void* workspace,

@@ -45,6 +45,18 @@ struct MergeArgs {
   float* lse;
 };
 
+// Log-prob from existing logits rows.
+struct LogitsArgs {
+  const void* logits;     // [N, ld] bf16 or fp32; entries 0 .. V-1 of each row are the logits
+  const int32_t* targets;
+  const int32_t* idx;
+  const int32_t* n_active;
+  int N, V, ld;
+  float inv_t;
+  float* logp;            // [N], written at active tokens
+  float* lse;             // [N] or null
+};
+
 // Backward buffers (bf16 stored as uint16_t).
 struct BwdArgs {
   const void* h;          // [N, H] bf16
@@ -66,6 +78,7 @@ struct BwdArgs {
 hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
 hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream_t stream);
 hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_logits_logp(const LogitsArgs& a, bool bf16, hipStream_t stream);
 
 // Backward phases.
 hipError_t launch_zero(float* p, size_t n, hipStream_t stream);

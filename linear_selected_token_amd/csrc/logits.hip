@@ -1,0 +1,149 @@
+// Selected-token log-prob from logits that already exist: the reference-scoring sibling of
+// the fused path (RL-Kernel integration roadmap for vime, "Operator Integration Plan", logp
+// Reference Scoring: a deterministic policy with a fixed row-local reduction topology, a
+// fixed launch configuration and an explicit log-softmax contract).
+//
+// The contract is the fused forward's: for every active token and every 128-entry vocabulary
+// column, the column maximum and the sum of 2^(z log2 e - max) in log2 units, with z = logit
+// / T applied once, followed by the fused forward's fixed-order merge.  The kernel is a pure
+// HBM stream: one work-group of 4 waves per active token row keeps its row's column
+// statistics in LDS (8 bytes per column) and merges them itself; each wave step reads
+// 4 KiB of the row (four 16-byte loads per lane), i.e. 16 bf16 columns (4 lanes each) or 8
+// fp32 columns (8 lanes each).  Every reduction is a fixed in-lane order followed by a fixed
+// xor tree, so a row's results depend only on that row.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace rlk {
+
+namespace {
+
+template <bool kBF16>
+__device__ __forceinline__ float logit_at(const uint8_t* row, int v) {
+  if constexpr (kBF16) {
+    const uint32_t b = reinterpret_cast<const uint16_t*>(row)[v];
+    return __builtin_bit_cast(float, b << 16);
+  } else {
+    return reinterpret_cast<const float*>(row)[v];
+  }
+}
+
+template <bool kBF16>
+__global__ __launch_bounds__(256) void logits_logp_kernel(LogitsArgs a) {
+  extern __shared__ float col_stats[];       // [2][J]: column max, then column sum
+  constexpr int kPer = kBF16 ? 8 : 4;        // values per lane per 16-byte load
+  constexpr int kGroup = 128 / kPer;         // lanes per column: 16 (bf16) or 32 (fp32)
+  constexpr int kCols = 64 / kGroup;         // columns per wave step
+  constexpr int kUnroll = 4;                 // wave steps per loop iteration
+  const int Na = *a.n_active;
+  const int i = blockIdx.x;
+  if (i >= Na) return;
+  const int t = a.idx[i];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const size_t esize = kBF16 ? 2 : 4;
+  const uint8_t* row = static_cast<const uint8_t*>(a.logits) + (size_t)t * a.ld * esize;
+  const float c2 = a.inv_t * kLog2e;
+  const int J = (a.V + 127) / 128;
+  float* cmax = col_stats;
+  float* csum = col_stats + J;
+
+  // 1. Column statistics.  Wave w takes column blocks w, w + 4, ... of kCols columns each.
+  for (int jb = wave * kCols; jb < J; jb += 4 * kCols * kUnroll) {
+    float x[kUnroll][kPer];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = jb + u * 4 * kCols + lane / kGroup;
+      const int v0 = j * 128 + (lane % kGroup) * kPer;
+      if (j < J && v0 < a.V) {
+        // v0 and ld are multiples of kPer, so the 16 bytes stay inside the row's ld entries
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(row + (size_t)v0 * esize);
+        if constexpr (kBF16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[u][2 * e] = __builtin_bit_cast(float, raw[e] << 16);
+            x[u][2 * e + 1] = __builtin_bit_cast(float, raw[e] & 0xffff0000u);
+          }
+        } else {
+          // cast the whole vector: a bit_cast of one vector element is lowered to element 0
+          const f32x4 f = __builtin_bit_cast(f32x4, raw);
+          x[u][0] = f.x;
+          x[u][1] = f.y;
+          x[u][2] = f.z;
+          x[u][3] = f.w;
+        }
+        if (v0 + kPer > a.V) {  // the vocabulary tail
+#pragma unroll
+          for (int e = 0; e < kPer; ++e)
+            if (v0 + e >= a.V) x[u][e] = -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) x[u][e] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = jb + u * 4 * kCols + lane / kGroup;
+      // column maximum on the raw logits (c2 > 0, rounding monotonic), in log2 units
+      float m = x[u][0];
+#pragma unroll
+      for (int e = 1; e < kPer; ++e) m = fmaxf(m, x[u][e]);
+#pragma unroll
+      for (int o = kGroup / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      const float mx = m * c2;
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) s += __builtin_amdgcn_exp2f(__builtin_fmaf(x[u][e], c2, -mx));
+#pragma unroll
+      for (int o = kGroup / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      if (lane % kGroup == 0 && j < J) {
+        cmax[j] = mx;
+        csum[j] = s;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. The merge of the fused forward (fwd_merge_kernel), in the same association: slice
+  // sl = 0..7 walks columns sl, sl + 8, ... in ascending order; the 8 slice sums are added in
+  // one fixed tree.
+  __shared__ float red[8];
+  const int sl = threadIdx.x;
+  float m = -INFINITY;
+  if (sl < 8)
+    for (int j = sl; j < J; j += 8) m = fmaxf(m, cmax[j]);
+  if (sl < 8) red[sl] = m;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) M = fmaxf(M, red[k]);
+  __syncthreads();
+  float s = 0.f;
+  if (sl < 8)
+    for (int j = sl; j < J; j += 8) s += csum[j] * __builtin_amdgcn_exp2f(cmax[j] - M);
+  if (sl < 8) red[sl] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float S = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+    const float lse = (M + __builtin_amdgcn_logf(S)) * kLn2;
+    const int y = a.targets[t];
+    const float zy = (y >= 0 && y < a.V) ? logit_at<kBF16>(row, y) * a.inv_t : NAN;
+    a.logp[t] = zy - lse;
+    if (a.lse) a.lse[t] = lse;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_logits_logp(const LogitsArgs& a, bool bf16, hipStream_t stream) {
+  const int grid = a.N > 0 ? a.N : 1;
+  const size_t lds = 2 * sizeof(float) * (size_t)((a.V + 127) / 128);
+  if (bf16)
+    hipLaunchKernelGGL(logits_logp_kernel<true>, dim3(grid), dim3(256), lds, stream, a);
+  else
+    hipLaunchKernelGGL(logits_logp_kernel<false>, dim3(grid), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace rlk

@@ -98,6 +98,44 @@ inline BwdLayout bwd_layout(int64_t N, int64_t H) {
   return L;
 }
 
+// Workspace of the log-prob from existing logits: idx[N] | n_active.
+struct LogitsLayout {
+  size_t idx, n_active, total;
+};
+
+inline LogitsLayout logits_layout(int64_t N) {
+  LogitsLayout L;
+  const size_t n = (size_t)(N > 0 ? N : 1);
+  L.idx = 0;
+  L.n_active = align_up(4 * n, 256);
+  L.total = align_up(L.n_active + 4, 256);
+  return L;
+}
+
+// The logits path keeps a row's column statistics in LDS (8 bytes per 128-entry column), at
+// most 64000 bytes: up to 8000 columns.
+constexpr int64_t kMaxLogitsVocab = int64_t(128) * 8000;
+
+// Existing logits [N, ld] with V <= ld entries per row: rows are addressed in 16-byte units.
+inline rlk_status_t check_logits(const void* logits, int64_t N, int64_t V, int64_t ld, int dtype,
+                                 float T, const int32_t* targets, const uint8_t* mask,
+                                 const float* logp, const float* lse, const void* ws,
+                                 size_t ws_bytes) {
+  if (N < 0 || V <= 0 || ld < V) return RLK_ERROR_INVALID_VALUE;
+  if (dtype != RLK_BF16 && dtype != RLK_FP32) return RLK_ERROR_UNSUPPORTED;
+  if (N > kMaxTokens || V > kMaxLogitsVocab || ld > (int64_t(1) << 24)) return RLK_ERROR_UNSUPPORTED;
+  if ((ld * elt_size(dtype)) % 16 != 0) return RLK_ERROR_UNSUPPORTED;
+  const float inv = (float)(1.0 / (double)T);
+  if (!isfinite(T) || !(T > 0.f) || !isfinite(inv) || inv == 0.f) return RLK_ERROR_INVALID_VALUE;
+  if (N == 0) return RLK_SUCCESS;
+  if (!logits || !targets || !mask || !logp || !ws) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(logits, 16) || !aligned(targets, 4) || !aligned(logp, 4) ||
+      (lse && !aligned(lse, 4)) || !aligned(ws, 256))
+    return RLK_ERROR_UNSUPPORTED;
+  if (ws_bytes < logits_layout(N).total) return RLK_ERROR_WORKSPACE;
+  return RLK_SUCCESS;
+}
+
 inline rlk_status_t check_fwd(const void* h, const void* W, const int32_t* targets,
                               const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
                               float T, const float* logp, const float* lse, const void* ws,

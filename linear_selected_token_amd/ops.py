@@ -101,6 +101,40 @@ def rlk_linear_logp_fwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     return logp, lse
 
 
+def logits_workspace_bytes(N: int, V: int) -> int:
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_logp_from_logits_workspace_size(N, V, ctypes.byref(out)),
+            "rlk_logp_from_logits_workspace_size")
+    return int(out.value)
+
+
+def rlk_logp_from_logits(logits: torch.Tensor, targets: torch.Tensor, mask: torch.Tensor,
+                         temperature: float, V: Optional[int] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Selected-token log-prob from existing logits [N, ld] (the first V entries of each row,
+    V = ld by default); returns (logp [N] float32, lse [N] float32)."""
+    mask = _mask_u8(mask)
+    if not (logits.is_cuda and targets.is_cuda and mask.is_cuda):
+        raise ValueError("logits, targets and mask must be GPU tensors")
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [N, ld] with unit stride along the vocabulary")
+    if targets.dtype != torch.int32 or targets.shape != (logits.shape[0],) or \
+            mask.shape != (logits.shape[0],) or not targets.is_contiguous():
+        raise ValueError("targets must be int32 [N] and mask [N]")
+    N, ld = logits.shape[0], logits.stride(0) if logits.shape[0] > 1 else logits.shape[1]
+    V = logits.shape[1] if V is None else int(V)
+    dt = _dtype_code(logits)
+    logp = torch.empty(N, dtype=torch.float32, device=logits.device)
+    lse = torch.empty(N, dtype=torch.float32, device=logits.device)
+    ws = _workspace(logits_workspace_bytes(N, V), logits.device, workspace)
+    L.check(L.lib().rlk_logp_from_logits(_vp(logits), ld, _vp(targets), _vp(mask), N, V, dt,
+                                         float(temperature), _vp(logp), _vp(lse), _vp(ws),
+                                         ws.numel() * ws.element_size(),
+                                         _stream(logits.device)), "rlk_logp_from_logits")
+    return logp, lse
+
+
 def rlk_linear_logp_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                         mask: torch.Tensor, temperature: float, adv: torch.Tensor,
                         lse: torch.Tensor, workspace: Optional[torch.Tensor] = None,

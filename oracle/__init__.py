@@ -7,6 +7,7 @@ from .linear_logp import (  # noqa: F401
     linear_logp,
     linear_logp_grads,
     logits,
+    logp_from_logits,
     logsumexp_rows,
     sample_targets,
 )

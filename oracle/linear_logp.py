@@ -100,6 +100,30 @@ def full_logp(h: np.ndarray, W: np.ndarray, T: float) -> np.ndarray:
     return z - logsumexp_rows(z)[:, None]
 
 
+def logp_from_logits(z_raw: np.ndarray, targets: np.ndarray, mask: np.ndarray, T: float,
+                     ) -> Tuple[np.ndarray, np.ndarray]:
+    """Selected-token log-prob and log-sum-exp from logits that already exist (the
+    reference-scoring sibling of the fused path: RL-Kernel integration roadmap for vime,
+    "Operator Integration Plan", logp Reference Scoring).  z = z_raw / T, applied once;
+    returns (logp, lse) with 0 at inactive tokens.  An active token whose target is outside
+    [0, V) raises ValueError."""
+    z_raw = _f64(z_raw)
+    V = z_raw.shape[1]
+    targets = np.asarray(targets).astype(np.int64)
+    active = np.nonzero(np.asarray(mask).astype(bool))[0]
+    if active.size and ((targets[active] < 0) | (targets[active] >= V)).any():
+        raise ValueError("target out of range for an active token")
+    logp = np.zeros(z_raw.shape[0])
+    lse = np.zeros(z_raw.shape[0])
+    for b0 in range(0, active.size, ROW_BLOCK):
+        t = active[b0:b0 + ROW_BLOCK]
+        z = z_raw[t] / float(T)
+        l = logsumexp_rows(z)
+        lse[t] = l
+        logp[t] = z[np.arange(t.size), targets[t]] - l
+    return logp, lse
+
+
 def _upstream(adv: np.ndarray, mask: np.ndarray) -> np.ndarray:
     """g_t = dL/dlogp_t = -mask_t * adv_t for L = -sum_t mask_t adv_t logp_t."""
     return -np.asarray(mask).astype(bool).astype(np.float64) * np.asarray(adv, dtype=np.float64)

@@ -180,3 +180,26 @@ def test_vocabulary_shard_argument_errors(L):
     # a ragged last shard passes the shard checks (and stops at the missing index buffer)
     assert _shard(lib, V=1000 - 896, start=896, idx=None) == E.RLK_ERROR_INVALID_VALUE
     assert _shard(lib, N=0, V=1000 - 896, start=896) == E.RLK_SUCCESS
+
+
+def _lg(lib, lg=FAKE, ld=1008, N=4, V=1000, dt=0, T=1.0, ws=FAKE, wsb=1 << 30):
+    return lib.rlk_logp_from_logits(lg, ld, FAKE, FAKE, N, V, dt, T, FAKE, FAKE, ws, wsb, None)
+
+
+def test_logits_path_argument_errors(L):
+    # every case is decided on the host, before anything could be launched
+    lib = L.lib()
+    E = L
+    assert _lg(lib, N=0) == E.RLK_SUCCESS
+    assert _lg(lib, lg=None) == E.RLK_ERROR_INVALID_VALUE
+    assert _lg(lib, ld=999) == E.RLK_ERROR_INVALID_VALUE          # row shorter than V
+    assert _lg(lib, ld=1004) == E.RLK_ERROR_UNSUPPORTED           # 2008-byte rows
+    assert _lg(lib, dt=1, ld=1002) == E.RLK_ERROR_UNSUPPORTED     # 4008-byte rows
+    assert _lg(lib, lg=FAKE + 8) == E.RLK_ERROR_UNSUPPORTED
+    assert _lg(lib, dt=2) == E.RLK_ERROR_UNSUPPORTED
+    assert _lg(lib, T=0.0) == E.RLK_ERROR_INVALID_VALUE
+    assert _lg(lib, wsb=100) == E.RLK_ERROR_WORKSPACE
+    assert _lg(lib, V=1024001, ld=1024008) == E.RLK_ERROR_UNSUPPORTED  # past the LDS budget
+    size = ctypes.c_size_t(0)
+    assert lib.rlk_logp_from_logits_workspace_size(4, 1000, ctypes.byref(size)) == E.RLK_SUCCESS
+    assert size.value > 0

@@ -270,3 +270,49 @@ def test_sampler_frequencies():
     p = np.exp(oracle.full_logp(h, W, T)[0])
     counts = np.bincount(ys, minlength=8)
     assert chisquare(counts, p * n).pvalue > 1e-4
+
+
+# ---------------------------------------------------------------- log-prob from existing logits
+
+def test_logits_path_equals_fused_definition():
+    # logits formed from h and W give exactly what the fused definition gives
+    r = np.random.default_rng(31)
+    N, H, V, T = 37, 24, 301, 0.7
+    h = r.standard_normal((N, H))
+    W = r.standard_normal((V, H)) / np.sqrt(H)
+    y = r.integers(0, V, N)
+    m = (r.random(N) < 0.7).astype(np.uint8)
+    a_lp, a_lse = oracle.logp_from_logits(h @ W.T, y, m, T)
+    b_lp, b_lse = oracle.linear_logp(h, W, y, m, T)
+    assert np.allclose(a_lp, b_lp, rtol=0, atol=1e-12)
+    assert np.allclose(a_lse, b_lse, rtol=0, atol=1e-12)
+    assert not a_lp[m == 0].any() and not a_lse[m == 0].any()
+
+
+def test_logits_path_brute_force_and_library():
+    # pure-Python brute force with math.fsum, and the library cross-entropy
+    r = np.random.default_rng(32)
+    N, V, T = 9, 13, 1.3
+    z = r.standard_normal((N, V)) * 4
+    y = r.integers(0, V, N)
+    m = np.ones(N, dtype=np.uint8)
+    lp, lse = oracle.logp_from_logits(z, y, m, T)
+    for t in range(N):
+        zt = [float(v) / T for v in z[t]]
+        mx = max(zt)
+        l = mx + math.log(math.fsum(math.exp(v - mx) for v in zt))
+        assert abs(lse[t] - l) < 1e-12 and abs(lp[t] - (zt[y[t]] - l)) < 1e-12
+    ce = torch.nn.functional.cross_entropy(torch.from_numpy(z / T), torch.from_numpy(y),
+                                           reduction="none").numpy()
+    assert np.allclose(lp, -ce, rtol=0, atol=1e-12)
+
+
+def test_logits_path_closed_forms_and_errors():
+    # constant logits: logp = -ln V at any temperature; an out-of-range target raises
+    z = np.full((4, 50), 3.25)
+    lp, lse = oracle.logp_from_logits(z, np.array([0, 7, 49, 3]), np.ones(4, np.uint8), 0.3)
+    assert np.allclose(lp, -math.log(50), rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.logp_from_logits(z, np.array([0, 50, 1, 1]), np.ones(4, np.uint8), 1.0)
+    # but an inactive token's target is never looked at
+    oracle.logp_from_logits(z, np.array([0, 50, 1, 1]), np.array([1, 0, 1, 1], np.uint8), 1.0)

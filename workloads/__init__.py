@@ -35,6 +35,7 @@ STREAM_UNIFORM = 4
 STREAM_ADV = 5
 STREAM_PAD = 6
 STREAM_PAD_H = 7
+STREAM_LOGITS = 8
 
 W_BLOCK_ROWS = 4096  # rows of W drawn per independent sub-stream
 
@@ -79,6 +80,20 @@ def normal_rows(seed: int, stream: int, index: int, rows: int, cols: int, scale:
     if scale != 1.0:
         x *= np.float32(scale)
     return bf16_bits(x) if dtype == "bf16" else x
+
+
+def logits_rows(seed: int, rows: int, V: int, scale: float, dtype: str,
+                ld: Optional[int] = None) -> np.ndarray:
+    """rows x V logits drawn N(0, scale^2), one sub-stream per row (so a row is the same bytes
+    in any batch), as bf16 bits or float32; with ld > V each row is padded to ld entries
+    (padding holds a large value that must never be read)."""
+    ld = V if ld is None else ld
+    out = np.empty((rows, ld), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    pad = bf16_bits(np.array([1e30], np.float32))[0] if dtype == "bf16" else np.float32(1e30)
+    for r in range(rows):
+        out[r, :V] = normal_rows(seed, STREAM_LOGITS, r, 1, V, scale, dtype)[0]
+        out[r, V:] = pad
+    return out
 
 
 def weight_matrix(seed: int, V: int, H: int, dtype: str) -> np.ndarray:
