@@ -1,6 +1,7 @@
 """CPU float64 oracle (test infrastructure only; see linear_logp.py)."""
 from .linear_logp import (  # noqa: F401
     dlogits,
+    entropy,
     full_logp,
     grad_W_rows,
     grad_h_rows,

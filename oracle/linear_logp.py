@@ -100,6 +100,24 @@ def full_logp(h: np.ndarray, W: np.ndarray, T: float) -> np.ndarray:
     return z - logsumexp_rows(z)[:, None]
 
 
+def entropy(h: np.ndarray, W: np.ndarray, mask: np.ndarray, T: float) -> np.ndarray:
+    """Entropy of the temperature-scaled next-token distribution, H_t = -sum_v p[t,v] log
+    p[t,v] with p = softmax(h_t W^T / T), at active tokens (0 elsewhere): the entropy
+    statistic the RL-Kernel Roadmap (2026) lists beside the fused log-prob (P0.2 and the
+    entropy item of its RL-loss list).  Computed from the definition, one block of rows at a
+    time."""
+    h = _f64(h)
+    W = _f64(W)
+    active = np.nonzero(np.asarray(mask).astype(bool))[0]
+    out = np.zeros(h.shape[0])
+    for b0 in range(0, active.size, ROW_BLOCK):
+        t = active[b0:b0 + ROW_BLOCK]
+        z = logits(h[t], W, T)
+        lp = z - logsumexp_rows(z)[:, None]
+        out[t] = -np.sum(np.exp(lp) * lp, axis=1)
+    return out
+
+
 def logp_from_logits(z_raw: np.ndarray, targets: np.ndarray, mask: np.ndarray, T: float,
                      ) -> Tuple[np.ndarray, np.ndarray]:
     """Selected-token log-prob and log-sum-exp from logits that already exist (the

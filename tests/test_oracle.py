@@ -316,3 +316,56 @@ def test_logits_path_closed_forms_and_errors():
         oracle.logp_from_logits(z, np.array([0, 50, 1, 1]), np.ones(4, np.uint8), 1.0)
     # but an inactive token's target is never looked at
     oracle.logp_from_logits(z, np.array([0, 50, 1, 1]), np.array([1, 0, 1, 1], np.uint8), 1.0)
+
+
+# ---------------------------------------------------------------- entropy
+
+def test_entropy_brute_force_and_library():
+    r = np.random.default_rng(41)
+    N, H, V, T = 7, 6, 11, 0.8
+    h = r.standard_normal((N, H)) * 2
+    W = r.standard_normal((V, H))
+    m = np.array([1, 1, 0, 1, 1, 0, 1], dtype=np.uint8)
+    ent = oracle.entropy(h, W, m, T)
+    for t in range(N):
+        if not m[t]:
+            assert ent[t] == 0.0
+            continue
+        z = [math.fsum(h[t, k] * W[v, k] for k in range(H)) / T for v in range(V)]
+        mx = max(z)
+        e = [math.exp(v - mx) for v in z]
+        S = math.fsum(e)
+        want = -math.fsum((x / S) * math.log(x / S) for x in e)
+        assert abs(ent[t] - want) < 1e-12
+    lib = torch.distributions.Categorical(logits=torch.from_numpy(h @ W.T / T)).entropy().numpy()
+    assert np.allclose(ent[m == 1], lib[m == 1], rtol=0, atol=1e-12)
+
+
+def test_entropy_closed_forms():
+    r = np.random.default_rng(42)
+    h = r.standard_normal((5, 8))
+    ones = np.ones(5, dtype=np.uint8)
+    # uniform distribution: ln V; one entry: 0
+    assert np.allclose(oracle.entropy(h, np.zeros((37, 8)), ones, 0.6), math.log(37),
+                       rtol=0, atol=1e-12)
+    assert np.allclose(oracle.entropy(h, r.standard_normal((1, 8)), ones, 1.0), 0.0,
+                       rtol=0, atol=1e-12)
+    # two entries: the binary entropy of sigmoid(z1 - z0)
+    W = r.standard_normal((2, 8))
+    d = (h @ (W[1] - W[0])) / 1.7
+    q = 1 / (1 + np.exp(-d))
+    want = -(q * np.log(q) + (1 - q) * np.log(1 - q))
+    assert np.allclose(oracle.entropy(h, W, ones, 1.7), want, rtol=0, atol=1e-12)
+
+
+def test_entropy_equals_lse_minus_mean_logit():
+    # H = lse - E_p[z]: the form the fused epilogue accumulates
+    r = np.random.default_rng(43)
+    h = r.standard_normal((9, 16))
+    W = r.standard_normal((200, 16)) / 4
+    T = 0.9
+    ones = np.ones(9, dtype=np.uint8)
+    z = h @ W.T / T
+    lse = oracle.logsumexp_rows(z)
+    ez = np.sum(np.exp(z - lse[:, None]) * z, axis=1)
+    assert np.allclose(oracle.entropy(h, W, ones, T), lse - ez, rtol=0, atol=1e-11)
