@@ -51,10 +51,13 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
-    p.add_argument("--mode", default="fwdbwd", choices=["fwd", "fwdbwd", "logits"],
+    p.add_argument("--mode", default="fwdbwd",
+                   choices=["fwd", "fwdbwd", "entropy", "logits"],
                    help="fwdbwd: the fused forward and backward (the headline); fwd: forward "
-                        "only; logits: log-prob from existing bf16 logits of the same shape "
-                        "(an HBM-bound path, reported against HBM bandwidth)")
+                        "only; entropy: the forward that also returns each token's entropy "
+                        "(timed beside the plain forward); logits: log-prob from existing "
+                        "bf16 logits of the same shape (an HBM-bound path, reported against "
+                        "HBM bandwidth)")
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample (0 disables it)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -104,7 +107,9 @@ def cpu_baseline(w, mode, target_s):
     def run(n):
         t0 = time.perf_counter()
         oracle.linear_logp(h64[:n], W64, y[:n], m[:n], w.T)
-        if mode != "fwd":
+        if mode == "entropy":
+            oracle.entropy(h64[:n], W64, m[:n], w.T)
+        elif mode != "fwd":
             oracle.linear_logp_grads(h64[:n], W64, y[:n], m[:n], w.T, adv[:n])
         return time.perf_counter() - t0
 
@@ -115,10 +120,10 @@ def cpu_baseline(w, mode, target_s):
     n = int(min(act.size, max(k, target_s / max(per, 1e-9))))
     n = max(16, (n // 16) * 16)
     dt = run(n)
+    what = {"fwd": "forward", "entropy": "forward + entropy"}.get(mode, "forward + dL/dh + dL/dW")
     return {"value": n / dt, "unit": "active tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} active tokens of the same workload scored as one batch "
-                      f"({'forward' if mode == 'fwd' else 'forward + dL/dh + dL/dW'}, float64, "
-                      f"numpy/OpenBLAS), {dt:.1f} s"}
+                      f"({what}, float64, numpy/OpenBLAS), {dt:.1f} s"}
 
 
 def traffic_for(kernel_src_files, name):
@@ -199,6 +204,63 @@ def bench_logits(args, w):
     print(json.dumps(out), flush=True)
 
 
+def bench_entropy(args, w):
+    """The forward with each token's entropy, timed whole on the caller's stream, beside the
+    plain forward on the same inputs (the entropy's overhead)."""
+    import torch
+    import linear_selected_token_amd as rlk
+    dev = torch.device("cuda", 0)
+    N, H, V, T, Na = w.N, w.H, w.V, w.T, w.n_active
+    h, W, targets, mask, _ = upload(w, dev)
+    dt = 0 if w.dtype == "bf16" else 1
+    ws_e = torch.empty(rlk.fwd_entropy_workspace_bytes(N, H, V, dt), dtype=torch.uint8,
+                       device=dev)
+    ws_p = torch.empty(rlk.fwd_workspace_bytes(N, H, V, dt), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms = timed(lambda: rlk.rlk_linear_logp_fwd_entropy(h, W, targets, mask, T, workspace=ws_e))
+    plain_ms = timed(lambda: rlk.rlk_linear_logp_fwd(h, W, targets, mask, T, workspace=ws_p))
+    flop = 2.0 * Na * H * V
+    tf = flop / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "active tokens/sec, fused linear logp forward with per-token entropy",
+        "value": round(Na / (ms * 1e-3), 1), "unit": "active tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded h~N(0,1), W~N(0,1/H) rounded to bf16, packed "
+                "prompt/response sequences",
+        "config": {"workload": args.workload, "mode": "entropy", "N": N, "H": H, "V": V,
+                   "T": T, "n_active": Na, "parallelism": "none (1 GPU)"},
+        "plain_fwd_ms": round(plain_ms, 4),
+        "entropy_overhead_frac": round(ms / plain_ms - 1.0, 4),
+        # the whole forward (compaction + tile kernel + merge) counted against the tile
+        # kernel's flops: a lower bound of the tile kernel's own rate
+        "roofline": {"bound": "mfma", "kernel": "whole entropy forward (fwd_tiles_kernel"
+                     "<bf16, entropy> + compaction + merge)",
+                     "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flop_per_launch": flop, "avg_launch_ms": round(ms, 4)},
+    }
+    if args.cpu_baseline_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, "entropy", args.cpu_baseline_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -215,6 +277,9 @@ def main():
     w = make_workload(args.workload)
     if args.mode == "logits":
         bench_logits(args, w)
+        return
+    if args.mode == "entropy":
+        bench_entropy(args, w)
         return
     N, H, V, T = w.N, w.H, w.V, w.T
     Na = w.n_active

@@ -106,6 +106,31 @@ rlk_status_t rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* ta
                                  float temperature, float* logp, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* Forward with the entropy of each active token's distribution, in the same pass:
+ * entropy[t] = -sum_v p[t,v] log p[t,v] with p[t,:] = softmax(z[t,:]), z = h W^T / T (the
+ * entropy statistic the RL-Kernel Roadmap (2026) lists next to the fused log-prob, "operator
+ * backlog"; vime roadmap, "Fast and Consistency Compatibility", entropy without
+ * materialising the logits).
+ *   h, W, targets, mask, N, H, V, dtype, temperature, logp, lse: as for rlk_linear_logp_fwd;
+ *                             logp and lse are bit-identical to what rlk_linear_logp_fwd
+ *                             returns for the same inputs
+ *   entropy  [N]    float     out: the entropy at active tokens (natural log, clamped at 0
+ *                             against rounding), 0 elsewhere
+ *   workspace: at least rlk_linear_logp_fwd_entropy_workspace_size bytes (the forward's
+ *              workspace plus one more float per token and 128-entry vocabulary column).
+ * Per active token and vocabulary column the tile epilogue also forms
+ * sum_v 2^(x_v - m) (x_v - m) (x = z log2 e, m the column maximum); the merge rescales these
+ * to the global maximum M in the forward's fixed association and returns
+ * ln 2 * (log2 S - sum_v 2^(x_v - M) (x_v - M) / S), S = sum_v 2^(x_v - M).  Batch-invariant
+ * like logp. */
+rlk_status_t rlk_linear_logp_fwd_entropy_workspace_size(int64_t N, int64_t H, int64_t V,
+                                                        int dtype, size_t* bytes);
+rlk_status_t rlk_linear_logp_fwd_entropy(const void* h, const void* W, const int32_t* targets,
+                                         const uint8_t* mask, int64_t N, int64_t H, int64_t V,
+                                         int dtype, float temperature, float* logp, float* lse,
+                                         float* entropy, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
 /* Selected-token log-prob from logits that already exist: the reference-scoring sibling of
  * the fused path, with the same log-softmax contract (RL-Kernel integration roadmap for vime,
  * "Operator Integration Plan", logp Reference Scoring: a deterministic policy with a fixed

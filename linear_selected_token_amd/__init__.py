@@ -10,6 +10,7 @@ from .ops import (  # noqa: E402,F401
     ForwardBuffers,
     LinearLogp,
     bwd_workspace_bytes,
+    fwd_entropy_workspace_bytes,
     fwd_workspace_bytes,
     linear_logp,
     logits_workspace_bytes,
@@ -17,6 +18,7 @@ from .ops import (  # noqa: E402,F401
     rlk_compact_active,
     rlk_linear_logp_bwd,
     rlk_linear_logp_fwd,
+    rlk_linear_logp_fwd_entropy,
     rlk_linear_logp_merge,
     rlk_linear_logp_partials,
     rlk_linear_logp_partials_shard,

@@ -1,4 +1,4 @@
-"""ctypes loader of ``librlk.so`` (built in-tree by ``linear_selected_token_amd.build``).
+"""ctypes loader of ``librlk.so`` (built in-tree by ``linear_selected_token_amd/build.py``).
 
 There is no fallback: if the library is missing or cannot be loaded, importing the
 binding raises, so a run never silently computes on another path."""
@@ -32,6 +32,10 @@ SIGNATURES = {
     "rlk_linear_logp_fwd_workspace_size": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]),
     "rlk_linear_logp_bwd_workspace_size": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]),
     "rlk_linear_logp_fwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p, _p, _sz, _p]),
+    "rlk_linear_logp_fwd_entropy_workspace_size": (_int, [_i64, _i64, _i64, _int,
+                                                          ctypes.POINTER(_sz)]),
+    "rlk_linear_logp_fwd_entropy": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p,
+                                           _p, _p, _sz, _p]),
     "rlk_linear_logp_bwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p, _p, _p,
                                    _p, _sz, _p]),
     "rlk_compact_active": (_int, [_p, _i64, _p, _p, _p, _p, _p, _p]),
@@ -59,7 +63,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: run `python -m linear_selected_token_amd.build`")
+            raise ImportError(f"{LIB_PATH} is missing: run `python linear_selected_token_amd/build.py`")
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)

@@ -1,6 +1,6 @@
 """Compile the HIP library ``librlk.so`` in-tree for gfx950.
 
-Usage: ``python -m linear_selected_token_amd.build`` (or ``build()`` from Python).  Each
+Usage: ``python linear_selected_token_amd/build.py`` (or ``build()`` of ``__graft_entry__``).  Each
 ``csrc/*.hip`` file is compiled to an object in parallel, then linked into a shared
 library next to this file.
 """

@@ -78,6 +78,15 @@ rlk_status_t rlk_linear_logp_fwd_workspace_size(int64_t N, int64_t H, int64_t V,
   return RLK_SUCCESS;
 }
 
+rlk_status_t rlk_linear_logp_fwd_entropy_workspace_size(int64_t N, int64_t H, int64_t V,
+                                                        int dtype, size_t* bytes) {
+  if (!bytes) return RLK_ERROR_INVALID_VALUE;
+  rlk_status_t s = check_shape(N, H, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  *bytes = fwd_layout(N, V, true).total;
+  return RLK_SUCCESS;
+}
+
 rlk_status_t rlk_linear_logp_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
                                                 size_t* bytes) {
   if (!bytes) return RLK_ERROR_INVALID_VALUE;
@@ -198,6 +207,39 @@ rlk_status_t rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* ta
                                stream);
   if (s != RLK_SUCCESS) return s;
   return rlk_linear_logp_merge(pm, ps, zy, idx, na, N, V, logp, lse, stream);
+}
+
+rlk_status_t rlk_linear_logp_fwd_entropy(const void* h, const void* W, const int32_t* targets,
+                                         const uint8_t* mask, int64_t N, int64_t H, int64_t V,
+                                         int dtype, float temperature, float* logp, float* lse,
+                                         float* entropy, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  rlk_status_t s = check_fwd(h, W, targets, mask, N, H, V, dtype, temperature, logp, lse,
+                             workspace, workspace_bytes, true);
+  if (s != RLK_SUCCESS || N == 0) return s;
+  if (!entropy) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(entropy, 4)) return RLK_ERROR_UNSUPPORTED;
+  const FwdLayout L = fwd_layout(N, V, true);
+  int32_t* idx = carve<int32_t>(workspace, L.idx);
+  int32_t* na = carve<int32_t>(workspace, L.n_active);
+  float* zy = carve<float>(workspace, L.target_logit);
+  float* pm = carve<float>(workspace, L.part_max);
+  float* ps = carve<float>(workspace, L.part_sum);
+  float* pw = carve<float>(workspace, L.part_w);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the compaction zeroes logp and lse at every token; entropy gets the same treatment
+  CompactArgs c{mask, idx, na, zy, logp, lse, (int)N, entropy};
+  hipError_t e = launch_compact(c, st);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  int grid = 0;
+  e = persistent_grid(&grid);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  FwdTileArgs a{h, W, targets, idx, na, (int)N, (int)H, (int)V,
+                (float)(1.0 / (double)temperature), pm, ps, zy, 0, pw};
+  e = launch_fwd_tiles(a, dtype == RLK_BF16, grid, st);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  MergeArgs m{pm, ps, zy, idx, na, (int)N, (int)V, logp, lse, pw, entropy};
+  return dev_status(launch_fwd_merge(m, st));
 }
 
 rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* targets,

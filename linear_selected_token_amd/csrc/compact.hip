@@ -34,6 +34,7 @@ __global__ __launch_bounds__(1024) void compact_kernel(CompactArgs a) {
         if (!f[k]) {
           if (a.logp) a.logp[t] = 0.f;
           if (a.lse) a.lse[t] = 0.f;
+          if (a.entropy) a.entropy[t] = 0.f;
         }
       }
       cnt += f[k];

@@ -32,7 +32,11 @@ struct FwdCtx {
   int tgt[kBlkB];  // their targets (-1: none or out of range)
 };
 
-template <bool kBF16>
+// kEnt: also the entropy statistic of each column, part_w = sum_v e_v max(d_v, -126) with
+// d_v = x_v - max (log2 units) and e_v = 2^d_v; the clamp only touches terms whose e_v is 0
+// (entries past the vocabulary, or underflowed), so the column's sum_v e_v x_v is
+// part_w + max * part_sum.  The max and sum are computed exactly as without it.
+template <bool kBF16, bool kEnt>
 __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
   __shared__ RingSmem sm;
   const int Na = *a.n_active;
@@ -119,22 +123,43 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
       am = fmaxf(am, __shfl_xor(am, 32));
       const float mx = am * c2;
       float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+      float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
 #pragma unroll
       for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
-          s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc.c[i][j][r + 0], c2, -mx));
-          s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc.c[i][j][r + 1], c2, -mx));
-          s2 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc.c[i][j][r + 2], c2, -mx));
-          s3 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc.c[i][j][r + 3], c2, -mx));
+          const float d0 = __builtin_fmaf(acc.c[i][j][r + 0], c2, -mx);
+          const float d1 = __builtin_fmaf(acc.c[i][j][r + 1], c2, -mx);
+          const float d2 = __builtin_fmaf(acc.c[i][j][r + 2], c2, -mx);
+          const float d3 = __builtin_fmaf(acc.c[i][j][r + 3], c2, -mx);
+          const float e0 = __builtin_amdgcn_exp2f(d0);
+          const float e1 = __builtin_amdgcn_exp2f(d1);
+          const float e2 = __builtin_amdgcn_exp2f(d2);
+          const float e3 = __builtin_amdgcn_exp2f(d3);
+          s0 += e0;
+          s1 += e1;
+          s2 += e2;
+          s3 += e3;
+          if constexpr (kEnt) {
+            w0 = __builtin_fmaf(e0, fmaxf(d0, -126.f), w0);
+            w1 = __builtin_fmaf(e1, fmaxf(d1, -126.f), w1);
+            w2 = __builtin_fmaf(e2, fmaxf(d2, -126.f), w2);
+            w3 = __builtin_fmaf(e3, fmaxf(d3, -126.f), w3);
+          }
         }
       float s = (s0 + s1) + (s2 + s3);
       s = s + __shfl_xor(s, 32);
+      float w = 0.f;
+      if constexpr (kEnt) {
+        w = (w0 + w1) + (w2 + w3);
+        w = w + __shfl_xor(w, 32);
+      }
       const int ti = c.tok[j];
       if (ti < Na) {
         if (lane < 32) {
           a.part_max[(size_t)col * a.N + ti] = mx;
           a.part_sum[(size_t)col * a.N + ti] = s;
+          if constexpr (kEnt) a.part_w[(size_t)col * a.N + ti] = w;
         }
         if (hit) a.target_logit[ti] = zsel * a.inv_t;
       }
@@ -149,6 +174,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
 // sums are added in a fixed tree.
 __global__ __launch_bounds__(256) void fwd_merge_kernel(MergeArgs a) {
   __shared__ float red[8][33];
+  __shared__ float wred[8][33];
   const int Na = *a.n_active;
   const int i0 = blockIdx.x * 32;
   if (i0 >= Na) return;
@@ -168,31 +194,48 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(MergeArgs a) {
   for (int k = 1; k < 8; ++k) M = fmaxf(M, red[k][r]);
   __syncthreads();
 
-  float s = 0.f;
+  float s = 0.f, w = 0.f;
   if (ok)
     for (int j = sl; j < J; j += 8) {
       const size_t o = (size_t)j * a.N + i;
-      s += a.part_sum[o] * __builtin_amdgcn_exp2f(a.part_max[o] - M);
+      const float f = __builtin_amdgcn_exp2f(a.part_max[o] - M);
+      s += a.part_sum[o] * f;
+      // sum_v 2^(x_v - M) (x_v - M) over the column, for the entropy
+      if (a.part_w) w += (a.part_w[o] + (a.part_max[o] - M) * a.part_sum[o]) * f;
     }
   red[sl][r] = s;
+  wred[sl][r] = w;
   __syncthreads();
   if (sl == 0 && ok) {
     const float S = ((red[0][r] + red[1][r]) + (red[2][r] + red[3][r])) +
                     ((red[4][r] + red[5][r]) + (red[6][r] + red[7][r]));
-    const float lse = (M + __builtin_amdgcn_logf(S)) * kLn2;
+    const float log2S = __builtin_amdgcn_logf(S);
+    const float lse = (M + log2S) * kLn2;
     const int t = a.idx[i];
     a.logp[t] = a.target_logit[i] - lse;
     if (a.lse) a.lse[t] = lse;
+    if (a.part_w) {
+      // H = lse - E_p[z] = ln2 (log2 S - E_p[x - M]) in log2 units x = z log2 e
+      const float A = ((wred[0][r] + wred[1][r]) + (wred[2][r] + wred[3][r])) +
+                      ((wred[4][r] + wred[5][r]) + (wred[6][r] + wred[7][r]));
+      // rounding can leave a near-certain token a few ulp below zero; the entropy is >= 0
+      a.entropy[t] = fmaxf((log2S - A / S) * kLn2, 0.f);
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream_t stream) {
-  if (bf16)
-    hipLaunchKernelGGL(fwd_tiles_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+  const bool ent = a.part_w != nullptr;
+  if (bf16 && !ent)
+    hipLaunchKernelGGL((fwd_tiles_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (bf16)
+    hipLaunchKernelGGL((fwd_tiles_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (!ent)
+    hipLaunchKernelGGL((fwd_tiles_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(fwd_tiles_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fwd_tiles_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ struct CompactArgs {
   float* logp;          // may be null: 0 at inactive tokens
   float* lse;           // may be null: 0 at inactive tokens
   int N;
+  float* entropy = nullptr;  // may be null: 0 at inactive tokens
 };
 
 struct FwdTileArgs {
@@ -32,6 +33,7 @@ struct FwdTileArgs {
   float* part_sum;
   float* target_logit;
   int vstart;  // global vocabulary index of W row 0 (a multiple of kVocabPartial)
+  float* part_w = nullptr;  // [J][N] entropy statistic per column, or null
 };
 
 struct MergeArgs {
@@ -43,6 +45,8 @@ struct MergeArgs {
   int N, V;
   float* logp;
   float* lse;
+  const float* part_w = nullptr;  // entropy statistics, or null
+  float* entropy = nullptr;       // [N], written at active tokens when part_w is given
 };
 
 // Log-prob from existing logits rows.

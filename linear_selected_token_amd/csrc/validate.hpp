@@ -56,10 +56,11 @@ inline rlk_status_t check_temperature(float T) {
 
 // Workspace layout of the forward: idx[N] | n_active | target_logit[N] | part_max | part_sum.
 struct FwdLayout {
-  size_t idx, n_active, target_logit, part_max, part_sum, total;
+  size_t idx, n_active, target_logit, part_max, part_sum, part_w, total;
 };
 
-inline FwdLayout fwd_layout(int64_t N, int64_t V) {
+// entropy: also room for the per-column entropy statistic (part_w)
+inline FwdLayout fwd_layout(int64_t N, int64_t V, bool entropy = false) {
   FwdLayout L;
   const size_t n = (size_t)(N > 0 ? N : 1);
   const size_t np = (size_t)num_partials(V);
@@ -69,6 +70,7 @@ inline FwdLayout fwd_layout(int64_t N, int64_t V) {
   L.target_logit = o; o = align_up(o + 4 * n, 256);
   L.part_max = o;     o = align_up(o + 4 * n * np, 256);
   L.part_sum = o;     o = align_up(o + 4 * n * np, 256);
+  L.part_w = o;       if (entropy) o = align_up(o + 4 * n * np, 256);
   L.total = o;
   return L;
 }
@@ -139,7 +141,7 @@ inline rlk_status_t check_logits(const void* logits, int64_t N, int64_t V, int64
 inline rlk_status_t check_fwd(const void* h, const void* W, const int32_t* targets,
                               const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
                               float T, const float* logp, const float* lse, const void* ws,
-                              size_t ws_bytes) {
+                              size_t ws_bytes, bool entropy = false) {
   rlk_status_t s = check_shape(N, H, V, dtype);
   if (s != RLK_SUCCESS) return s;
   s = check_temperature(T);
@@ -149,7 +151,7 @@ inline rlk_status_t check_fwd(const void* h, const void* W, const int32_t* targe
   if (!aligned(h, 16) || !aligned(W, 16) || !aligned(targets, 4) || !aligned(logp, 4) ||
       (lse && !aligned(lse, 4)) || !aligned(ws, 256))
     return RLK_ERROR_UNSUPPORTED;
-  if (ws_bytes < fwd_layout(N, V).total) return RLK_ERROR_WORKSPACE;
+  if (ws_bytes < fwd_layout(N, V, entropy).total) return RLK_ERROR_WORKSPACE;
   return RLK_SUCCESS;
 }
 

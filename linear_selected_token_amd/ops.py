@@ -101,6 +101,37 @@ def rlk_linear_logp_fwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     return logp, lse
 
 
+def fwd_entropy_workspace_bytes(N: int, H: int, V: int, dtype_code: int) -> int:
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_linear_logp_fwd_entropy_workspace_size(N, H, V, dtype_code,
+                                                               ctypes.byref(out)),
+            "rlk_linear_logp_fwd_entropy_workspace_size")
+    return int(out.value)
+
+
+def rlk_linear_logp_fwd_entropy(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                                mask: torch.Tensor, temperature: float,
+                                workspace: Optional[torch.Tensor] = None,
+                                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Selected-token log-prob and the entropy of each token's distribution; returns
+    (logp, lse, entropy), each [N] float32."""
+    mask = _mask_u8(mask)
+    _check(h, W, targets, mask)
+    N, H = h.shape
+    V = W.shape[0]
+    dt = _dtype_code(h)
+    logp = torch.empty(N, dtype=torch.float32, device=h.device)
+    lse = torch.empty(N, dtype=torch.float32, device=h.device)
+    ent = torch.empty(N, dtype=torch.float32, device=h.device)
+    ws = _workspace(fwd_entropy_workspace_bytes(N, H, V, dt), h.device, workspace)
+    L.check(L.lib().rlk_linear_logp_fwd_entropy(_vp(h), _vp(W), _vp(targets), _vp(mask), N, H,
+                                                V, dt, float(temperature), _vp(logp), _vp(lse),
+                                                _vp(ent), _vp(ws), ws.numel() * ws.element_size(),
+                                                _stream(h.device)),
+            "rlk_linear_logp_fwd_entropy")
+    return logp, lse, ent
+
+
 def logits_workspace_bytes(N: int, V: int) -> int:
     out = ctypes.c_size_t(0)
     L.check(L.lib().rlk_logp_from_logits_workspace_size(N, V, ctypes.byref(out)),

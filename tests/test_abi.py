@@ -14,10 +14,10 @@ HEADER = os.path.join(ROOT, "include", "rlk.h")
 
 @pytest.fixture(scope="module")
 def L():
+    if not os.path.exists(os.path.join(ROOT, "linear_selected_token_amd", "librlk.so")):
+        import __graft_entry__
+        __graft_entry__.build()
     from linear_selected_token_amd import _lib
-    if not os.path.exists(_lib.LIB_PATH):
-        from linear_selected_token_amd import build
-        build.build()
     return _lib
 
 
@@ -203,3 +203,29 @@ def test_logits_path_argument_errors(L):
     size = ctypes.c_size_t(0)
     assert lib.rlk_logp_from_logits_workspace_size(4, 1000, ctypes.byref(size)) == E.RLK_SUCCESS
     assert size.value > 0
+
+
+def _ent(lib, ent=FAKE, N=8, H=64, V=1000, dt=0, T=1.0, ws=FAKE, wsb=1 << 30):
+    return lib.rlk_linear_logp_fwd_entropy(FAKE, FAKE, FAKE, FAKE, N, H, V, dt, T, FAKE, FAKE,
+                                           ent, ws, wsb, None)
+
+
+def test_entropy_forward_workspace_and_argument_errors(L):
+    # every case is decided on the host, before anything could be launched
+    lib = L.lib()
+    E = L
+    N, H, V = 16384, 4096, 151936
+    st, plain = _ws(lib, "rlk_linear_logp_fwd_workspace_size", N, H, V, L.RLK_BF16)
+    st2, ent = _ws(lib, "rlk_linear_logp_fwd_entropy_workspace_size", N, H, V, L.RLK_BF16)
+    assert st == 0 and st2 == 0
+    # one more float per token and 128-entry column
+    assert ent - plain == 4 * N * 1187
+    assert _ws(lib, "rlk_linear_logp_fwd_entropy_workspace_size", 10, 100, 50, 0)[0] == \
+        E.RLK_ERROR_UNSUPPORTED
+    _, small = _ws(lib, "rlk_linear_logp_fwd_workspace_size", 8, 64, 1000, 0)
+    assert _ent(lib, N=0) == E.RLK_SUCCESS
+    assert _ent(lib, wsb=small) == E.RLK_ERROR_WORKSPACE   # the plain forward's is too small
+    assert _ent(lib, ent=None) == E.RLK_ERROR_INVALID_VALUE
+    assert _ent(lib, ent=FAKE + 2) == E.RLK_ERROR_UNSUPPORTED
+    assert _ent(lib, T=float("nan")) == E.RLK_ERROR_INVALID_VALUE
+    assert _ent(lib, H=96) == E.RLK_ERROR_UNSUPPORTED
