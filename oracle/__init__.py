@@ -2,10 +2,12 @@
 from .linear_logp import (  # noqa: F401
     dlogits,
     entropy,
+    entropy_dlogits,
     full_logp,
     grad_W_rows,
     grad_h_rows,
     linear_logp,
+    linear_logp_entropy_grads,
     linear_logp_grads,
     logits,
     logp_from_logits,

@@ -157,6 +157,48 @@ def dlogits(h: np.ndarray, W: np.ndarray, targets: np.ndarray, g: np.ndarray, T:
     return G * np.asarray(g, dtype=np.float64)[:, None]
 
 
+def entropy_dlogits(h: np.ndarray, W: np.ndarray, b: np.ndarray, T: float,
+                    lse: Optional[np.ndarray] = None, ent: Optional[np.ndarray] = None,
+                    ) -> np.ndarray:
+    """dL/dz for a loss that depends on the entropy, for a block of rows, [rows, V]:
+    b_t = dL/dH_t times dH_t/dz[t, v] = -p[t, v] (log p[t, v] + H_t), the derivative of
+    H = -sum_v p_v log p_v through the softmax."""
+    z = logits(h, W, T)
+    l = logsumexp_rows(z) if lse is None else np.asarray(lse, dtype=np.float64)
+    lp = z - l[:, None]
+    p = np.exp(lp)
+    H = -np.sum(p * lp, axis=1) if ent is None else np.asarray(ent, dtype=np.float64)
+    return -np.asarray(b, dtype=np.float64)[:, None] * p * (lp + H[:, None])
+
+
+def _entropy_upstream(ent_coef: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """b_t = dL/dH_t = -mask_t * c_t for L = -sum_t mask_t (adv_t logp_t + c_t H_t)."""
+    return -np.asarray(mask).astype(bool).astype(np.float64) * np.asarray(ent_coef,
+                                                                           dtype=np.float64)
+
+
+def linear_logp_entropy_grads(h: np.ndarray, W: np.ndarray, targets: np.ndarray,
+                              mask: np.ndarray, T: float, adv: np.ndarray,
+                              ent_coef: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(dL/dh, dL/dW) in float64 for the policy-gradient loss with an entropy bonus,
+    L = -sum_t mask_t (adv_t logp_t + c_t H_t) (the entropy-bonus term the RL-Kernel Roadmap
+    (2026) lists in its operator backlog).  dL/dz is the log-prob term of dlogits plus
+    entropy_dlogits; dh and dW follow from it as for linear_logp_grads."""
+    h = _f64(h)
+    W = _f64(W)
+    g = _upstream(adv, mask)
+    b = _entropy_upstream(ent_coef, mask)
+    dh = np.zeros_like(h)
+    dW = np.zeros_like(W)
+    act = np.nonzero(np.asarray(mask).astype(bool))[0]
+    for b0 in range(0, act.size, ROW_BLOCK):
+        t = act[b0:b0 + ROW_BLOCK]
+        G = dlogits(h[t], W, np.asarray(targets)[t], g[t], T) + entropy_dlogits(h[t], W, b[t], T)
+        dh[t] = (G @ W) / T
+        dW += (G.T @ h[t]) / T
+    return dh, dW
+
+
 def linear_logp_grads(h: np.ndarray, W: np.ndarray, targets: np.ndarray, mask: np.ndarray,
                       T: float, adv: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """(dL/dh [N, H], dL/dW [V, H]) in float64 for L = -sum_t mask_t adv_t logp_t.
@@ -177,26 +219,34 @@ def linear_logp_grads(h: np.ndarray, W: np.ndarray, targets: np.ndarray, mask: n
 
 
 def grad_h_rows(h: np.ndarray, W: np.ndarray, targets: np.ndarray, mask: np.ndarray,
-                T: float, adv: np.ndarray, rows: Sequence[int]) -> np.ndarray:
-    """dL/dh for the listed token rows only, [len(rows), H]."""
+                T: float, adv: np.ndarray, rows: Sequence[int],
+                ent_coef: Optional[np.ndarray] = None) -> np.ndarray:
+    """dL/dh for the listed token rows only, [len(rows), H] (with ``ent_coef``, of the loss
+    with the entropy bonus, as in linear_logp_entropy_grads)."""
     h = _f64(h)
     W = _f64(W)
     rows = np.asarray(rows, dtype=np.int64)
     g = _upstream(adv, mask)[rows]
+    b = None if ent_coef is None else _entropy_upstream(ent_coef, mask)[rows]
     out = np.zeros((rows.size, h.shape[1]))
     for b0 in range(0, rows.size, ROW_BLOCK):
         r = rows[b0:b0 + ROW_BLOCK]
         G = dlogits(h[r], W, np.asarray(targets)[r], g[b0:b0 + ROW_BLOCK], T)
+        if b is not None:
+            G += entropy_dlogits(h[r], W, b[b0:b0 + ROW_BLOCK], T)
         out[b0:b0 + r.size] = (G @ W) / T
     return out
 
 
 def grad_W_rows(h: np.ndarray, W: np.ndarray, targets: np.ndarray, mask: np.ndarray,
                 T: float, adv: np.ndarray, vocab_rows: Sequence[int],
-                lse: Optional[np.ndarray] = None) -> np.ndarray:
+                lse: Optional[np.ndarray] = None, ent_coef: Optional[np.ndarray] = None,
+                entropy_: Optional[np.ndarray] = None) -> np.ndarray:
     """dL/dW for the listed vocabulary rows only, [len(vocab_rows), H].
 
-    Needs every active token's lse; pass ``lse`` (from ``linear_logp``) to reuse it."""
+    Needs every active token's lse; pass ``lse`` (from ``linear_logp``) to reuse it.  With
+    ``ent_coef``, of the loss with the entropy bonus; it then needs every active token's
+    entropy too (``entropy_``, from ``entropy``, or computed here)."""
     h = _f64(h)
     W = _f64(W)
     vocab_rows = np.asarray(vocab_rows, dtype=np.int64)
@@ -210,6 +260,12 @@ def grad_W_rows(h: np.ndarray, W: np.ndarray, targets: np.ndarray, mask: np.ndar
     G = -p
     G += (y[:, None] == vocab_rows[None, :])
     G *= g[:, None]
+    if ent_coef is not None:
+        if entropy_ is None:
+            entropy_ = entropy(h, W, mask, T)
+        b = _entropy_upstream(ent_coef, mask)[act]
+        lp = z - np.asarray(lse, dtype=np.float64)[act][:, None]
+        G -= b[:, None] * p * (lp + np.asarray(entropy_, dtype=np.float64)[act][:, None])
     return (G.T @ h[act]) / T
 
 

@@ -369,3 +369,79 @@ def test_entropy_equals_lse_minus_mean_logit():
     lse = oracle.logsumexp_rows(z)
     ez = np.sum(np.exp(z - lse[:, None]) * z, axis=1)
     assert np.allclose(oracle.entropy(h, W, ones, T), lse - ez, rtol=0, atol=1e-11)
+
+
+# ------------------------------------------------------------------ entropy-bonus gradients
+
+def _ent_loss(h, W, y, mask, T, adv, c):
+    lp, _ = oracle.linear_logp(h, W, y, mask, T)
+    H = oracle.entropy(h, W, mask, T)
+    return -float(np.sum(mask * (adv * lp + c * H)))
+
+
+def test_entropy_grads_finite_differences():
+    h, W, y, mask, adv = _grad_setup(40, N=5, H=4, V=7)
+    c = np.random.default_rng(41).uniform(0.2, 2.0, 5)
+    T = 0.8
+    dh, dW = oracle.linear_logp_entropy_grads(h, W, y, mask, T, adv, c)
+    eps = 1e-6
+    for (i, j) in [(0, 0), (1, 3), (4, 2), (2, 1)]:
+        hp, hm = h.copy(), h.copy()
+        hp[i, j] += eps
+        hm[i, j] -= eps
+        fd = (_ent_loss(hp, W, y, mask, T, adv, c) - _ent_loss(hm, W, y, mask, T, adv, c)) / (2 * eps)
+        assert abs(fd - dh[i, j]) < 1e-7, (i, j, fd, dh[i, j])
+    for (i, j) in [(0, 0), (6, 3), (int(y[0]), 2), (3, 1)]:
+        Wp, Wm = W.copy(), W.copy()
+        Wp[i, j] += eps
+        Wm[i, j] -= eps
+        fd = (_ent_loss(h, Wp, y, mask, T, adv, c) - _ent_loss(h, Wm, y, mask, T, adv, c)) / (2 * eps)
+        assert abs(fd - dW[i, j]) < 1e-7, (i, j, fd, dW[i, j])
+
+
+def test_entropy_grads_match_library_autograd():
+    h, W, y, mask, adv = _grad_setup(42, N=19, H=11, V=37)
+    c = np.random.default_rng(43).standard_normal(19)
+    T = 1.3
+    dh, dW = oracle.linear_logp_entropy_grads(h, W, y, mask, T, adv, c)
+    th = torch.tensor(h, requires_grad=True)
+    tW = torch.tensor(W, requires_grad=True)
+    lsm = torch.log_softmax(th @ tW.T / T, dim=1)
+    logp = lsm.gather(1, torch.tensor(y)[:, None])[:, 0]
+    ent = -(lsm.exp() * lsm).sum(1)
+    m = torch.tensor(mask, dtype=torch.float64)
+    loss = -(m * (torch.tensor(adv) * logp + torch.tensor(c) * ent)).sum()
+    loss.backward()
+    np.testing.assert_allclose(dh, th.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dW, tW.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_entropy_grads_special_cases():
+    h, W, y, mask, adv = _grad_setup(44, N=13, H=6, V=23)
+    T = 0.9
+    # no entropy bonus: the plain gradients
+    dh0, dW0 = oracle.linear_logp_grads(h, W, y, mask, T, adv)
+    dh1, dW1 = oracle.linear_logp_entropy_grads(h, W, y, mask, T, adv, np.zeros(13))
+    np.testing.assert_array_equal(dh0, dh1)
+    np.testing.assert_array_equal(dW0, dW1)
+    # W = 0: every distribution is uniform, where the entropy is at its maximum and its
+    # gradient vanishes; with adv = 0 nothing is left
+    dh, dW = oracle.linear_logp_entropy_grads(h, np.zeros((23, 6)), y, mask, T, np.zeros(13),
+                                              np.ones(13))
+    assert np.abs(dh).max() < 1e-15 and np.abs(dW).max() < 1e-15
+    # every row of dL/dz sums to zero (p-weighted log p + H has mean zero), so dW's columns do
+    _, dW = oracle.linear_logp_entropy_grads(h, W, y, mask, T, adv, np.full(13, 0.5))
+    np.testing.assert_allclose(dW.sum(axis=0), 0.0, atol=1e-13)
+
+
+def test_entropy_grad_row_variants_match_full():
+    h, W, y, mask, adv = _grad_setup(45, N=30, H=7, V=50)
+    c = np.random.default_rng(46).uniform(0, 1, 30)
+    T = 0.75
+    dh, dW = oracle.linear_logp_entropy_grads(h, W, y, mask, T, adv, c)
+    rows = [0, 29, 11, 4]
+    np.testing.assert_allclose(oracle.grad_h_rows(h, W, y, mask, T, adv, rows, ent_coef=c),
+                               dh[rows], rtol=0, atol=1e-14)
+    vr = [0, 49, int(y[0]), 17]
+    np.testing.assert_allclose(oracle.grad_W_rows(h, W, y, mask, T, adv, vr, ent_coef=c),
+                               dW[vr], rtol=0, atol=1e-14)
