@@ -54,8 +54,8 @@ def parse():
     p.add_argument("--mode", default="fwdbwd",
                    choices=["fwd", "fwdbwd", "entropy", "logits"],
                    help="fwdbwd: the fused forward and backward (the headline); fwd: forward "
-                        "only; entropy: the forward that also returns each token's entropy "
-                        "(timed beside the plain forward); logits: log-prob from existing "
+                        "only; entropy: a step with an entropy bonus (the entropy forward and "
+                        "its backward); logits: log-prob from existing "
                         "bf16 logits of the same shape (an HBM-bound path, reported against "
                         "HBM bandwidth)")
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
@@ -109,6 +109,8 @@ def cpu_baseline(w, mode, target_s):
         oracle.linear_logp(h64[:n], W64, y[:n], m[:n], w.T)
         if mode == "entropy":
             oracle.entropy(h64[:n], W64, m[:n], w.T)
+            oracle.linear_logp_entropy_grads(h64[:n], W64, y[:n], m[:n], w.T, adv[:n],
+                                             np.full(n, 0.01))
         elif mode != "fwd":
             oracle.linear_logp_grads(h64[:n], W64, y[:n], m[:n], w.T, adv[:n])
         return time.perf_counter() - t0
@@ -120,7 +122,9 @@ def cpu_baseline(w, mode, target_s):
     n = int(min(act.size, max(k, target_s / max(per, 1e-9))))
     n = max(16, (n // 16) * 16)
     dt = run(n)
-    what = {"fwd": "forward", "entropy": "forward + entropy"}.get(mode, "forward + dL/dh + dL/dW")
+    what = {"fwd": "forward",
+            "entropy": "forward + entropy + gradients with an entropy bonus"}.get(
+        mode, "forward + dL/dh + dL/dW")
     return {"value": n / dt, "unit": "active tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} active tokens of the same workload scored as one batch "
                       f"({what}, float64, numpy/OpenBLAS), {dt:.1f} s"}
@@ -205,17 +209,23 @@ def bench_logits(args, w):
 
 
 def bench_entropy(args, w):
-    """The forward with each token's entropy, timed whole on the caller's stream, beside the
-    plain forward on the same inputs (the entropy's overhead)."""
+    """A training step with an entropy bonus: the forward that also returns each token's
+    entropy, then the backward of L = -sum_t mask_t (adv_t logp_t + c_t H_t) (c_t = 0.01),
+    timed whole on the caller's stream; the entropy forward alone and the plain forward are
+    timed beside it (the entropy's overhead)."""
     import torch
     import linear_selected_token_amd as rlk
     dev = torch.device("cuda", 0)
     N, H, V, T, Na = w.N, w.H, w.V, w.T, w.n_active
-    h, W, targets, mask, _ = upload(w, dev)
+    h, W, targets, mask, adv = upload(w, dev)
     dt = 0 if w.dtype == "bf16" else 1
+    coef = torch.full((N,), 0.01, dtype=torch.float32, device=dev)
     ws_e = torch.empty(rlk.fwd_entropy_workspace_bytes(N, H, V, dt), dtype=torch.uint8,
                        device=dev)
     ws_p = torch.empty(rlk.fwd_workspace_bytes(N, H, V, dt), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(rlk.bwd_workspace_bytes(N, H, V, dt), dtype=torch.uint8, device=dev)
+    dh = torch.empty((N, H), dtype=torch.float32, device=dev)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
 
     def timed(fn):
         for _ in range(args.warmup):
@@ -230,12 +240,19 @@ def bench_entropy(args, w):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    ms = timed(lambda: rlk.rlk_linear_logp_fwd_entropy(h, W, targets, mask, T, workspace=ws_e))
+    def step():
+        _, lse, ent = rlk.rlk_linear_logp_fwd_entropy(h, W, targets, mask, T, workspace=ws_e)
+        rlk.rlk_linear_logp_bwd_entropy(h, W, targets, mask, T, adv, coef, lse, ent,
+                                        workspace=ws_b, dh=dh, dW=dW)
+
+    ms = timed(step)
+    fwd_ms = timed(lambda: rlk.rlk_linear_logp_fwd_entropy(h, W, targets, mask, T,
+                                                           workspace=ws_e))
     plain_ms = timed(lambda: rlk.rlk_linear_logp_fwd(h, W, targets, mask, T, workspace=ws_p))
-    flop = 2.0 * Na * H * V
+    flop = 8.0 * Na * H * V   # forward + recompute + dL/dh + dL/dW, as executed
     tf = flop / (ms * 1e-3) / 1e12
     out = {
-        "metric": "active tokens/sec, fused linear logp forward with per-token entropy",
+        "metric": "active tokens/sec, fused linear logp fwd+bwd with an entropy bonus",
         "value": round(Na / (ms * 1e-3), 1), "unit": "active tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -243,16 +260,16 @@ def bench_entropy(args, w):
         "data": "synthetic: seeded h~N(0,1), W~N(0,1/H) rounded to bf16, packed "
                 "prompt/response sequences",
         "config": {"workload": args.workload, "mode": "entropy", "N": N, "H": H, "V": V,
-                   "T": T, "n_active": Na, "parallelism": "none (1 GPU)"},
+                   "T": T, "n_active": Na, "ent_coef": 0.01, "parallelism": "none (1 GPU)"},
+        "fwd_entropy_ms": round(fwd_ms, 4),
         "plain_fwd_ms": round(plain_ms, 4),
-        "entropy_overhead_frac": round(ms / plain_ms - 1.0, 4),
-        # the whole forward (compaction + tile kernel + merge) counted against the tile
-        # kernel's flops: a lower bound of the tile kernel's own rate
-        "roofline": {"bound": "mfma", "kernel": "whole entropy forward (fwd_tiles_kernel"
-                     "<bf16, entropy> + compaction + merge)",
-                     "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "algorithmic_flop_per_launch": flop, "avg_launch_ms": round(ms, 4)},
+        "entropy_fwd_overhead_frac": round(fwd_ms / plain_ms - 1.0, 4),
+        # the whole step's executed flops over its time: a lower bound of every kernel's rate
+        "roofline": {"bound": "mfma", "kernel": "whole step (entropy forward + entropy-bonus "
+                     "backward)", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flop_per_launch": flop,
+                     "avg_launch_ms": round(ms, 4)},
     }
     if args.cpu_baseline_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, "entropy", args.cpu_baseline_seconds)

@@ -168,6 +168,26 @@ rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* ta
                                  float* dh, float* dW, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* Backward of the policy-gradient loss with an entropy bonus (bf16 only),
+ *   L = -sum_t mask_t (adv_t logp_t + c_t H_t)
+ * with H_t the entropy of softmax(z[t,:]) (RL-Kernel Roadmap (2026), "operator backlog":
+ * fused entropy / entropy-bonus kernel).  dL/dz[t,v] = -adv_t (delta(v, y_t) - p[t,v]) +
+ * c_t p[t,v] (log p[t,v] + H_t); the rest is rlk_linear_logp_bwd's chunked walk.
+ *   h, W, targets, mask, N, H, V, dtype, temperature, adv, lse, dh, dW, workspace: as for
+ *                             rlk_linear_logp_bwd (same workspace size)
+ *   ent_coef [N]    float     c_t, the entropy-bonus weight of each token (masked tokens
+ *                             ignore it)
+ *   entropy  [N]    float     H_t as returned by rlk_linear_logp_fwd_entropy for the same
+ *                             inputs (lse likewise)
+ * With c = 0 the result equals rlk_linear_logp_bwd's up to the rounding of one extra fma
+ * per logit. */
+rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int32_t* targets,
+                                         const uint8_t* mask, int64_t N, int64_t H, int64_t V,
+                                         int dtype, float temperature, const float* adv,
+                                         const float* ent_coef, const float* lse,
+                                         const float* entropy, float* dh, float* dW,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- Building blocks of the forward (the same kernels rlk_linear_logp_fwd runs).  They
  * expose the per-vocabulary-slice statistics so that slices computed elsewhere (for
  * example on other devices holding other vocabulary shards) can be merged in a fixed

@@ -17,6 +17,7 @@ from .ops import (  # noqa: E402,F401
     num_vocab_partials,
     rlk_compact_active,
     rlk_linear_logp_bwd,
+    rlk_linear_logp_bwd_entropy,
     rlk_linear_logp_fwd,
     rlk_linear_logp_fwd_entropy,
     rlk_linear_logp_merge,

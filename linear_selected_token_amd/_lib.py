@@ -38,6 +38,8 @@ SIGNATURES = {
                                            _p, _p, _sz, _p]),
     "rlk_linear_logp_bwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p, _p, _p,
                                    _p, _sz, _p]),
+    "rlk_linear_logp_bwd_entropy": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p, _p,
+                                           _p, _p, _p, _p, _sz, _p]),
     "rlk_compact_active": (_int, [_p, _i64, _p, _p, _p, _p, _p, _p]),
     "rlk_linear_logp_partials": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p,
                                         _p, _p]),

@@ -47,6 +47,60 @@ const char* build_info_string() {
   return s;
 }
 
+// The backward behind rlk_linear_logp_bwd and rlk_linear_logp_bwd_entropy (ent_coef and
+// entropy null for the former).
+rlk_status_t run_bwd(const void* h, const void* W, const int32_t* targets, const uint8_t* mask,
+                     int64_t N, int64_t H, int64_t V, int dtype, float temperature,
+                     const float* adv, const float* lse, const float* ent_coef,
+                     const float* entropy, float* dh, float* dW, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  rlk_status_t s = check_bwd(h, W, targets, mask, N, H, V, dtype, temperature, adv, lse, dh, dW,
+                             workspace, workspace_bytes);
+  if (s != RLK_SUCCESS) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (N == 0) {
+    // nothing to differentiate: dL/dW = 0 (a fill kernel, not a memset node)
+    return dev_status(launch_zero(dW, (size_t)V * (size_t)H, st));
+  }
+  int grid = 0;
+  if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
+  const BwdLayout L = bwd_layout(N, H);
+  BwdArgs a{};
+  a.h = h;
+  a.W = W;
+  a.targets = targets;
+  a.adv = adv;
+  a.lse = lse;
+  a.ent_coef = ent_coef;
+  a.entropy = entropy;
+  int32_t* idx = carve<int32_t>(workspace, L.idx);
+  int32_t* na = carve<int32_t>(workspace, L.n_active);
+  a.idx = idx;
+  a.n_active = na;
+  a.N = (int)N;
+  a.H = (int)H;
+  a.V = (int)V;
+  a.Npad = (int)bwd_npad(N);
+  a.inv_t = (float)(1.0 / (double)temperature);
+  a.dh = dh;
+  a.dW = dW;
+  a.hT = carve<uint16_t>(workspace, L.hT);
+  a.Gv = carve<uint16_t>(workspace, L.Gv);
+  a.dh1 = carve<float>(workspace, L.dh1);
+  CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
+  hipError_t e = launch_compact(c, st);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  e = launch_bwd_prepare(a, st);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  const int nchunks = (int)((V + kBwdChunk - 1) / kBwdChunk);
+  for (int c0 = 0; c0 < nchunks; ++c0) {
+    e = launch_bwd_chunk(a, c0, grid, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  }
+  return dev_status(launch_bwd_finish(a, st));
+}
+
+
 }  // namespace
 }  // namespace rlk
 
@@ -247,48 +301,20 @@ rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* ta
                                  float temperature, const float* adv, const float* lse,
                                  float* dh, float* dW, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  rlk_status_t s = check_bwd(h, W, targets, mask, N, H, V, dtype, temperature, adv, lse, dh, dW,
-                             workspace, workspace_bytes);
-  if (s != RLK_SUCCESS) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (N == 0) {
-    // nothing to differentiate: dL/dW = 0 (a fill kernel, not a memset node)
-    return dev_status(launch_zero(dW, (size_t)V * (size_t)H, st));
-  }
-  int grid = 0;
-  if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
-  const BwdLayout L = bwd_layout(N, H);
-  BwdArgs a{};
-  a.h = h;
-  a.W = W;
-  a.targets = targets;
-  a.adv = adv;
-  a.lse = lse;
-  int32_t* idx = carve<int32_t>(workspace, L.idx);
-  int32_t* na = carve<int32_t>(workspace, L.n_active);
-  a.idx = idx;
-  a.n_active = na;
-  a.N = (int)N;
-  a.H = (int)H;
-  a.V = (int)V;
-  a.Npad = (int)bwd_npad(N);
-  a.inv_t = (float)(1.0 / (double)temperature);
-  a.dh = dh;
-  a.dW = dW;
-  a.hT = carve<uint16_t>(workspace, L.hT);
-  a.Gv = carve<uint16_t>(workspace, L.Gv);
-  a.dh1 = carve<float>(workspace, L.dh1);
-  CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
-  hipError_t e = launch_compact(c, st);
-  if (e != hipSuccess) return RLK_ERROR_DEVICE;
-  e = launch_bwd_prepare(a, st);
-  if (e != hipSuccess) return RLK_ERROR_DEVICE;
-  const int nchunks = (int)((V + kBwdChunk - 1) / kBwdChunk);
-  for (int c0 = 0; c0 < nchunks; ++c0) {
-    e = launch_bwd_chunk(a, c0, grid, st);
-    if (e != hipSuccess) return RLK_ERROR_DEVICE;
-  }
-  return dev_status(launch_bwd_finish(a, st));
+  return run_bwd(h, W, targets, mask, N, H, V, dtype, temperature, adv, lse, nullptr, nullptr,
+                 dh, dW, workspace, workspace_bytes, stream);
+}
+
+rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int32_t* targets,
+                                         const uint8_t* mask, int64_t N, int64_t H, int64_t V,
+                                         int dtype, float temperature, const float* adv,
+                                         const float* ent_coef, const float* lse,
+                                         const float* entropy, float* dh, float* dW,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (N > 0 && (!ent_coef || !entropy)) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(ent_coef, 4) || !aligned(entropy, 4)) return RLK_ERROR_UNSUPPORTED;
+  return run_bwd(h, W, targets, mask, N, H, V, dtype, temperature, adv, lse, ent_coef, entropy,
+                 dh, dW, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

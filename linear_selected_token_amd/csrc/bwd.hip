@@ -9,6 +9,10 @@
 //   dL/dh_t    = (1/T) sum_v dL/dz[t,v] W_v
 //   dL/dW_v    = (1/T) sum_t dL/dz[t,v] h_t
 //
+// With an entropy bonus, L = -sum_t mask_t (adv_t logp_t + c_t H_t) and dL/dz gains
+// c_t p[t,v] (log p[t,v] + H_t), the derivative of -c_t H_t = c_t sum_v p log p through the
+// softmax; H_t comes from the entropy forward.
+//
 // The vocabulary is walked in chunks of kBwdChunk entries, in ascending order.  Per chunk:
 //   dlogits      the forward tile GEMM again, epilogue G = (g_t / T)(delta - p) rounded to
 //                bf16 and stored token-major (Gv);
@@ -69,8 +73,10 @@ struct DlogitsCtx {
   int tok[kBlkB];  // compacted token index of each of this lane's four columns
   int tgt[kBlkB];
   float lse2[kBlkB], gs[kBlkB];
+  float bs[kBlkB], hn[kBlkB];  // entropy bonus: c_t / T and H_t
 };
 
+template <bool kEnt>
 __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
   __shared__ RingSmem sm;
   const int Na = *a.n_active;
@@ -116,6 +122,10 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
       // padded columns: p = 2^(x - inf) = 0 exactly, so G is 0 whatever the logit
       c.lse2[j] = ok ? a.lse[t] * kLog2e : INFINITY;
       c.gs[j] = ok ? -a.adv[t] * a.inv_t : 0.f;
+      if constexpr (kEnt) {
+        c.bs[j] = ok ? a.ent_coef[t] * a.inv_t : 0.f;
+        c.hn[j] = ok ? a.entropy[t] : 0.f;
+      }
     }
   };
 
@@ -134,6 +144,11 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
             const int v = c.vbase + wv + acc_row(i, r, lane);
             const float p = __builtin_amdgcn_exp2f(acc.c[i][j][r] * c2 - c.lse2[j]);
             G[e] = c.gs[j] * ((v == c.tgt[j] ? 1.f : 0.f) - p);
+            if constexpr (kEnt) {
+              // log p, clamped where p is 0 (underflow, padded columns) so that 0 * log p = 0
+              const float lp = fmaxf(acc.c[i][j][r] * c2 - c.lse2[j], -126.f) * kLn2;
+              G[e] = __builtin_fmaf(c.bs[j] * p, lp + c.hn[j], G[e]);
+            }
             if (v >= a.V) G[e] = 0.f;
           }
           const int vl = c.vbase - c0 + wv + acc_row(i, 4 * g, lane);  // first of 4 consecutive
@@ -306,7 +321,10 @@ hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t stream) {
   const int c0 = chunk * kBwdChunk;
-  hipLaunchKernelGGL(dlogits_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  if (a.ent_coef)
+    hipLaunchKernelGGL(dlogits_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  else
+    hipLaunchKernelGGL(dlogits_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   hipLaunchKernelGGL(dh_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   hipLaunchKernelGGL(dw_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   return hipGetLastError();

@@ -77,6 +77,9 @@ struct BwdArgs {
   uint16_t* hT;           // [H, Npad]   compacted h, transposed, zero past Na
   uint16_t* Gv;           // [Npad, kBwdChunk] dL/dz of the chunk, token-major
   float* dh1;             // [Npad, H] dL/dh from the second half of every chunk, compacted rows
+  // entropy bonus (both null without it): L gains -sum_t mask_t c_t H_t
+  const float* ent_coef = nullptr;  // [N] c_t
+  const float* entropy = nullptr;   // [N] H_t from the entropy forward
 };
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);

@@ -193,6 +193,37 @@ def rlk_linear_logp_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     return dh, dW
 
 
+def rlk_linear_logp_bwd_entropy(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                                mask: torch.Tensor, temperature: float, adv: torch.Tensor,
+                                ent_coef: torch.Tensor, lse: torch.Tensor, entropy: torch.Tensor,
+                                workspace: Optional[torch.Tensor] = None,
+                                dh: Optional[torch.Tensor] = None,
+                                dW: Optional[torch.Tensor] = None,
+                                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gradients of L = -sum_t mask_t (adv_t logp_t + ent_coef_t H_t), with lse and entropy
+    from rlk_linear_logp_fwd_entropy; returns (dh [N,H], dW [V,H]) float32."""
+    mask = _mask_u8(mask)
+    _check(h, W, targets, mask)
+    N, H = h.shape
+    V = W.shape[0]
+    dt = _dtype_code(h)
+    for name, t in (("adv", adv), ("ent_coef", ent_coef), ("lse", lse), ("entropy", entropy)):
+        if not t.is_cuda or t.dtype != torch.float32 or t.shape != (N,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor [N]")
+    if dh is None:
+        dh = torch.empty((N, H), dtype=torch.float32, device=h.device)
+    if dW is None:
+        dW = torch.empty((V, H), dtype=torch.float32, device=h.device)
+    ws = _workspace(bwd_workspace_bytes(N, H, V, dt), h.device, workspace)
+    L.check(L.lib().rlk_linear_logp_bwd_entropy(_vp(h), _vp(W), _vp(targets), _vp(mask), N, H,
+                                                V, dt, float(temperature), _vp(adv),
+                                                _vp(ent_coef), _vp(lse), _vp(entropy), _vp(dh),
+                                                _vp(dW), _vp(ws), ws.numel() * ws.element_size(),
+                                                _stream(h.device)),
+            "rlk_linear_logp_bwd_entropy")
+    return dh, dW
+
+
 # ---- building blocks of the forward
 
 def rlk_compact_active(mask: torch.Tensor, idx: torch.Tensor, n_active: torch.Tensor,

@@ -229,3 +229,19 @@ def test_entropy_forward_workspace_and_argument_errors(L):
     assert _ent(lib, ent=FAKE + 2) == E.RLK_ERROR_UNSUPPORTED
     assert _ent(lib, T=float("nan")) == E.RLK_ERROR_INVALID_VALUE
     assert _ent(lib, H=96) == E.RLK_ERROR_UNSUPPORTED
+
+
+def test_entropy_backward_argument_errors(L):
+    lib = L.lib()
+    E = L
+
+    def bwd(c=FAKE, ent=FAKE, N=8, H=256, dt=0, wsb=1 << 30):
+        return lib.rlk_linear_logp_bwd_entropy(FAKE, FAKE, FAKE, FAKE, N, H, 100, dt, 1.0, FAKE,
+                                               c, FAKE, ent, FAKE, FAKE, FAKE, wsb, None)
+
+    assert bwd(c=None) == E.RLK_ERROR_INVALID_VALUE
+    assert bwd(ent=None) == E.RLK_ERROR_INVALID_VALUE
+    assert bwd(c=FAKE + 2) == E.RLK_ERROR_UNSUPPORTED
+    assert bwd(dt=1) == E.RLK_ERROR_UNSUPPORTED
+    assert bwd(H=192) == E.RLK_ERROR_UNSUPPORTED
+    assert bwd(wsb=10) == E.RLK_ERROR_WORKSPACE

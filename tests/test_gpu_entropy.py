@@ -1,12 +1,17 @@
-"""Entropy forward against the float64 oracle (needs an MI355X).
+"""Entropy forward and entropy-bonus backward against the float64 oracle (needs an MI355X).
 
 rlk_linear_logp_fwd_entropy returns logp and lse bit-identical to rlk_linear_logp_fwd and,
 per active token, the entropy of softmax(h W^T / T).  Gates: logp and lse as for the plain
 forward; |dH| <= 1e-3 absolute against the oracle (H = lse - E_p[z], so an error of delta
 in every logit moves it by at most 2 delta, the bound the logp gate already puts on lse);
-a token's entropy is bit-identical in any batch; 0 at inactive tokens."""
+a token's entropy is bit-identical in any batch; 0 at inactive tokens.
+
+rlk_linear_logp_bwd_entropy: gradients of L = -sum_t mask_t (adv_t logp_t + c_t H_t) within
+rel-L2 1e-2 of the oracle's, a token's dL/dh row bit-identical across batch layouts, and
+with c = 0 exactly the plain backward."""
 import dataclasses
 import math
+import os
 
 import numpy as np
 import pytest
@@ -14,12 +19,13 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import (MAX_ABS_DLOGP, bits, flush, oracle_inputs, run_fwd, sample_rows,
-                      upload)
+from gpu_util import (GRAD_REL_L2, bits, flush, oracle_inputs, rel_l2, run_bwd, run_fwd,
+                      sample_rows, upload)
 
 pytestmark = pytest.mark.gpu
 
 MAX_ABS_DH = 1e-3
+HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def _run(w, d=None):
@@ -125,11 +131,138 @@ def test_qwen_head_sampled():
     _same_as_plain(w, lp, lse, d)
 
 
+def _full_size():
+    # the benchmark step: 16384 tokens, the Qwen3-8B head, T = 0.7, stored sampled targets
+    flush("qwen3-8b-head N=16384 T=0.7: generating inputs")
+    targets = np.load(os.path.join(HERE, "golden", "cfg3_sampled_targets.npy"))
+    return wl.with_targets(wl.make(3), targets)
+
+
 def test_full_size_sampled():
-    # the full-size step (16384 tokens, the Qwen3-8B head), oracle on sampled rows
-    flush("config 2: generating inputs")
-    w = wl.make(2)
+    w = _full_size()
     d = upload(w)
     lp, lse, ent = _run(w, d)
     _check(w, ent, rows=sample_rows(w, 24, seed=2))
     _same_as_plain(w, lp, lse, d)
+
+
+# ------------------------------------------------------------------ entropy-bonus backward
+
+def _ent_coef(w, seed, lo=0.5, hi=1.5):
+    return np.random.default_rng(seed).uniform(lo, hi, w.N).astype(np.float32)
+
+
+def _run_bwd(w, c, d=None, adv=None):
+    import linear_selected_token_amd as rlk
+    d = d or upload(w)
+    dev = d["h"].device
+    _, lse, ent = rlk.rlk_linear_logp_fwd_entropy(d["h"], d["W"], d["targets"], d["mask"], w.T)
+    a = d["adv"] if adv is None else torch.from_numpy(adv).to(dev)
+    dh, dW = rlk.rlk_linear_logp_bwd_entropy(d["h"], d["W"], d["targets"], d["mask"], w.T, a,
+                                             torch.from_numpy(c).to(dev), lse, ent)
+    torch.cuda.synchronize()
+    return dh, dW
+
+
+def _bwd_full_compare(w, c, adv=None):
+    dh, dW = _run_bwd(w, c, adv=adv)
+    dh, dW = dh.cpu().numpy(), dW.cpu().numpy()
+    h64, W64 = oracle_inputs(w)
+    odh, odW = oracle.linear_logp_entropy_grads(h64, W64, w.targets, w.mask, w.T,
+                                                w.adv if adv is None else adv, c)
+    eh, ew = rel_l2(dh, odh), rel_l2(dW, odW)
+    flush(f"  entropy bwd {w.spec.name} N={w.N} H={w.H} V={w.V} adv={'0' if adv is not None else 'w'}: "
+          f"relL2(dh)={eh:.3e} relL2(dW)={ew:.3e}")
+    assert eh <= GRAD_REL_L2 and ew <= GRAD_REL_L2
+    assert not dh[w.mask == 0].any()
+
+
+BWD_SMALL = wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300, seed=97,
+                           T=0.8)
+
+
+def test_bwd_small_full():
+    w = wl.make(BWD_SMALL)
+    _bwd_full_compare(w, _ent_coef(w, 1))
+    # the entropy term alone
+    _bwd_full_compare(w, _ent_coef(w, 2), adv=np.zeros(w.N, np.float32))
+
+
+def test_bwd_two_chunks_ragged():
+    import re
+    import linear_selected_token_amd as rlk
+    m = re.search(r"bwd chunk (\d+), dh split at (\d+)", rlk.build_info())
+    chunk, split = int(m.group(1)), int(m.group(2))
+    w = wl.make(wl.scaled_spec(5, N=300, H=256, V=chunk + split + 300, n_seq=2, len_lo=100,
+                               len_hi=200, seed=98))
+    _bwd_full_compare(w, _ent_coef(w, 3))
+
+
+def test_bwd_zero_coefficient_is_plain_backward():
+    w = wl.make(BWD_SMALL)
+    d = upload(w)
+    dh, dW = _run_bwd(w, np.zeros(w.N, np.float32), d)
+    _, _, dh0, dW0 = run_bwd(w, d)
+    assert torch.equal(dh, dh0) and torch.equal(dW, dW0)
+
+
+def test_bwd_dh_invariance():
+    fam = wl.Family(BWD_SMALL)
+    base = fam.batch()
+    c_of = {}
+    r = np.random.default_rng(4)
+    for k in base.key():
+        c_of[k] = np.float32(r.uniform(0.5, 1.5))
+
+    def coef(w):
+        return np.array([c_of.get(k, np.float32(0)) for k in w.key()], np.float32)
+
+    dh, _ = _run_bwd(base, coef(base))
+    dh = dh.cpu().numpy()
+    ref = {k: dh[i] for i, k in enumerate(base.key()) if base.mask[i]}
+    for w in (fam.alone(1), fam.shuffled(7), fam.padded(8)):
+        dh2, _ = _run_bwd(w, coef(w))
+        dh2 = dh2.cpu().numpy()
+        for i, k in enumerate(w.key()):
+            if k[0] >= 0 and w.mask[i]:
+                assert np.array_equal(bits(dh2[i]), bits(ref[k])), k
+
+
+def test_bwd_qwen_head_sampled():
+    # the Qwen3-8B LM head, 1024 tokens: sampled dh rows and dW rows against the oracle
+    w = wl.make(wl.scaled_spec(5, N=1024, n_seq=4, len_lo=200, len_hi=300, seed=99))
+    c = _ent_coef(w, 5)
+    dh, dW = _run_bwd(w, c)
+    h64, W64 = oracle_inputs(w)
+    rows = sample_rows(w, 16, seed=99)
+    odh = oracle.grad_h_rows(h64, W64, w.targets, w.mask, w.T, w.adv, rows, ent_coef=c)
+    eh = rel_l2(dh[torch.from_numpy(rows).to(dh.device)].cpu().numpy(), odh)
+    flush(f"  entropy bwd qwen head: relL2(dh)={eh:.3e} over {rows.size} rows")
+    assert eh <= GRAD_REL_L2
+    _, olse = oracle.linear_logp(h64, W64, w.targets, w.mask, w.T)
+    oent = oracle.entropy(h64, W64, w.mask, w.T)
+    act = np.nonzero(w.mask)[0]
+    vr = np.unique(np.concatenate([w.targets[act[:8]],
+                                   np.random.default_rng(6).integers(0, w.V, 16), [0, w.V - 1]]))
+    odW = oracle.grad_W_rows(h64, W64, w.targets, w.mask, w.T, w.adv, vr, lse=olse,
+                             ent_coef=c, entropy_=oent)
+    ew = rel_l2(dW[torch.from_numpy(vr).to(dW.device)].cpu().numpy(), odW)
+    flush(f"  entropy bwd qwen head: relL2(dW)={ew:.3e} over {vr.size} vocabulary rows")
+    assert ew <= GRAD_REL_L2
+
+
+def test_bwd_full_size_sampled():
+    # the benchmark step: sampled dh rows against the oracle, and the columns of dW sum to ~0
+    # (every row of dL/dz does)
+    w = _full_size()
+    c = _ent_coef(w, 7, lo=0.005, hi=0.02)
+    dh, dW = _run_bwd(w, c)
+    h64, W64 = oracle_inputs(w)
+    rows = sample_rows(w, 12, seed=7)
+    odh = oracle.grad_h_rows(h64, W64, w.targets, w.mask, w.T, w.adv, rows, ent_coef=c)
+    eh = rel_l2(dh[torch.from_numpy(rows).to(dh.device)].cpu().numpy(), odh)
+    flush(f"  entropy bwd full size: relL2(dh)={eh:.3e} over {rows.size} rows")
+    assert eh <= GRAD_REL_L2
+    colsum = dW.double().sum(0).abs().max().item()
+    scale = dW.double().abs().sum(0).max().item()
+    assert colsum <= 1e-3 * scale
