@@ -52,10 +52,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     p.add_argument("--mode", default="fwdbwd",
-                   choices=["fwd", "fwdbwd", "entropy", "logits"],
+                   choices=["fwd", "fwdbwd", "entropy", "ppo", "logits"],
                    help="fwdbwd: the fused forward and backward (the headline); fwd: forward "
                         "only; entropy: a step with an entropy bonus (the entropy forward and "
-                        "its backward); logits: log-prob from existing "
+                        "its backward); ppo: forward, clipped policy-gradient loss with a KL "
+                        "penalty, backward, plus the dlogp diagnostics; logits: log-prob from existing "
                         "bf16 logits of the same shape (an HBM-bound path, reported against "
                         "HBM bandwidth)")
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
@@ -278,6 +279,77 @@ def bench_entropy(args, w):
     print(json.dumps(out), flush=True)
 
 
+def bench_ppo(args, w):
+    """A PPO/GRPO-style step: the forward, the clipped policy-gradient loss with a KL penalty
+    on the fresh log-prob (old and reference log-probs are seeded perturbations of it, made
+    before the timed region), and the backward driven by the loss's -dloss/dlogp; the loss
+    fragment and the dlogp diagnostics are also timed alone."""
+    import torch
+    import linear_selected_token_amd as rlk
+    dev = torch.device("cuda", 0)
+    N, H, V, T, Na = w.N, w.H, w.V, w.T, w.n_active
+    h, W, targets, mask, adv = upload(w, dev)
+    dt = 0 if w.dtype == "bf16" else 1
+    ws_f = torch.empty(rlk.fwd_workspace_bytes(N, H, V, dt), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(rlk.bwd_workspace_bytes(N, H, V, dt), dtype=torch.uint8, device=dev)
+    dh = torch.empty((N, H), dtype=torch.float32, device=dev)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    logp0, _ = rlk.rlk_linear_logp_fwd(h, W, targets, mask, T, workspace=ws_f)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1007)
+    old = logp0 + 0.05 * torch.randn(N, generator=g, device=dev)
+    ref = logp0 + 0.05 * torch.randn(N, generator=g, device=dev)
+    scale = 1.0 / max(Na, 1)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    def step():
+        logp, lse = rlk.rlk_linear_logp_fwd(h, W, targets, mask, T, workspace=ws_f)
+        _, badv, _, _ = rlk.rlk_ratio_kl_loss(logp, old, ref, adv, mask, 0.2, 0.28, 0.01, scale)
+        rlk.rlk_linear_logp_bwd(h, W, targets, mask, T, badv, lse, workspace=ws_b, dh=dh, dW=dW)
+
+    ms = timed(step)
+    loss_ms = timed(lambda: rlk.rlk_ratio_kl_loss(logp0, old, ref, adv, mask, 0.2, 0.28, 0.01,
+                                                  scale))
+    diag_ms = timed(lambda: rlk.rlk_dlogp_diagnostics(logp0, old, mask, 0.2))
+    flop = 8.0 * Na * H * V
+    tf = flop / (ms * 1e-3) / 1e12
+    loss_bytes = N * (4 * 4 + 1 + 4 * 2) + 32 * ((N + 1023) // 1024)
+    out = {
+        "metric": "active tokens/sec, fused linear logp fwd + clipped PG/KL loss + bwd",
+        "value": round(Na / (ms * 1e-3), 1), "unit": "active tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded h~N(0,1), W~N(0,1/H) rounded to bf16, packed "
+                "prompt/response sequences; old/ref log-probs = logp + N(0, 0.05^2)",
+        "config": {"workload": args.workload, "mode": "ppo", "N": N, "H": H, "V": V, "T": T,
+                   "n_active": Na, "eps_lo": 0.2, "eps_hi": 0.28, "beta": 0.01,
+                   "parallelism": "none (1 GPU)"},
+        "loss_fragment": {"ms": round(loss_ms, 5), "bytes": loss_bytes,
+                          "gbs": round(loss_bytes / (loss_ms * 1e-3) / 1e9, 1)},
+        "diagnostics_ms": round(diag_ms, 5),
+        "roofline": {"bound": "mfma", "kernel": "whole step (forward + loss fragment + "
+                     "backward)", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flop_per_launch": flop,
+                     "avg_launch_ms": round(ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -297,6 +369,9 @@ def main():
         return
     if args.mode == "entropy":
         bench_entropy(args, w)
+        return
+    if args.mode == "ppo":
+        bench_ppo(args, w)
         return
     N, H, V, T = w.N, w.H, w.V, w.T
     Na = w.n_active

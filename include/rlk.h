@@ -188,6 +188,52 @@ rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int
                                          const float* entropy, float* dh, float* dW,
                                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Loss fragments that consume the log-prob (RL-Kernel integration roadmap for vime,
+ * "RL Loss Operators: ratio_kl, GRPO/PPO/DPO Loss Fragments": optional fused ratio / KL
+ * fragments whose contract states mask handling, aggregation, dtype and reduction order).
+ * Every pointer is device memory; all per-token arrays are [N] float32 unless stated. */
+
+/* Per-token clipped policy-gradient loss with a KL penalty towards a reference policy:
+ *   r_t   = exp(logp_t - old_logp_t)
+ *   pg_t  = max(-A_t r_t, -A_t clip(r_t, 1 - eps_lo, 1 + eps_hi))
+ *   kl_t  = exp(d_t) - 1 - d_t with d_t = ref_logp_t - logp_t (the function the pages use
+ *           for approx_kl0; a non-negative estimate of KL(policy || reference))
+ *   loss_t    = scale * (pg_t + beta * kl_t)                 at active tokens, else 0
+ *   bwd_adv_t = -dloss_t/dlogp_t = scale * (A_t r_t [unclipped] - beta (1 - exp(d_t)))
+ *               (0 where the clipped term is the larger one), ready to be passed as `adv`
+ *               to rlk_linear_logp_bwd, which differentiates -sum adv * logp
+ *   ratio_t   = r_t at active tokens, else 0 (ratio may be NULL)
+ *   sums      double[4] (may be NULL): sum_t loss_t, the number of clipped tokens,
+ *             sum_t kl_t, the number of active tokens
+ * ref_logp NULL: no KL term (beta ignored).  The caller owns the aggregation: scale is applied
+ * per token (for a token mean pass 1 / number of active tokens).  Per-token values are fp32
+ * and depend only on the token's own inputs; the sums are fp64 in a fixed order for a given
+ * N.  eps_lo must lie in [0, 1), eps_hi >= 0, beta and scale finite (else INVALID_VALUE).
+ * workspace: rlk_ratio_kl_loss_workspace_size bytes (256-byte aligned). */
+rlk_status_t rlk_ratio_kl_loss_workspace_size(int64_t N, size_t* bytes);
+rlk_status_t rlk_ratio_kl_loss(const float* logp, const float* old_logp, const float* ref_logp,
+                               const float* adv, const uint8_t* mask, int64_t N, float eps_lo,
+                               float eps_hi, float beta, float scale, float* loss,
+                               float* bwd_adv, float* ratio, double* sums, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* dlogp diagnostics over the active tokens (vime roadmap, "Consistency Contract", minimum
+ * diagnostics), dlogp_t = logp_a_t - logp_b_t formed in fp64:
+ *   out[0] active tokens   out[1] mean |dlogp|   out[2] max |dlogp|
+ *   out[3..5] 50th, 90th, 99th percentile of |dlogp| (linear interpolation between the
+ *             order statistics at floor and ceil of q (n - 1) / 100; the order statistics
+ *             are exact, found by radix selection)
+ *   out[6] mean ratio0 = exp(dlogp)   out[7] clipfrac0 = fraction with |ratio0 - 1| > clip_eps
+ *   out[8] approx_kl0 = mean(exp(dlogp) - 1 - dlogp)
+ *   worst: the first token index of largest |dlogp| (-1 when no token is active)
+ * With no active token every out[] entry is 0.  out (double[9]) and worst are device
+ * memory, written on the stream.  workspace: rlk_dlogp_diagnostics_workspace_size bytes. */
+rlk_status_t rlk_dlogp_diagnostics_workspace_size(int64_t N, size_t* bytes);
+rlk_status_t rlk_dlogp_diagnostics(const float* logp_a, const float* logp_b,
+                                   const uint8_t* mask, int64_t N, float clip_eps, double* out,
+                                   int64_t* worst, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* ---- Building blocks of the forward (the same kernels rlk_linear_logp_fwd runs).  They
  * expose the per-vocabulary-slice statistics so that slices computed elsewhere (for
  * example on other devices holding other vocabulary shards) can be merged in a fixed

@@ -7,6 +7,7 @@ from ._lib import RlkError, build_info, lib, status_string  # noqa: F401
 lib()  # fail loudly at import when the library is missing
 
 from .ops import (  # noqa: E402,F401
+    DIAG_FIELDS,
     ForwardBuffers,
     LinearLogp,
     bwd_workspace_bytes,
@@ -16,6 +17,7 @@ from .ops import (  # noqa: E402,F401
     logits_workspace_bytes,
     num_vocab_partials,
     rlk_compact_active,
+    rlk_dlogp_diagnostics,
     rlk_linear_logp_bwd,
     rlk_linear_logp_bwd_entropy,
     rlk_linear_logp_fwd,
@@ -24,4 +26,5 @@ from .ops import (  # noqa: E402,F401
     rlk_linear_logp_partials,
     rlk_linear_logp_partials_shard,
     rlk_logp_from_logits,
+    rlk_ratio_kl_loss,
 )

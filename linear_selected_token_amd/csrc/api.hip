@@ -2,6 +2,8 @@
 // caller's stream.  The operation and its contract are described in include/rlk.h.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
+
 #include <atomic>
 #include <cstdio>
 
@@ -294,6 +296,70 @@ rlk_status_t rlk_linear_logp_fwd_entropy(const void* h, const void* W, const int
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
   MergeArgs m{pm, ps, zy, idx, na, (int)N, (int)V, logp, lse, pw, entropy};
   return dev_status(launch_fwd_merge(m, st));
+}
+
+rlk_status_t rlk_ratio_kl_loss_workspace_size(int64_t N, size_t* bytes) {
+  if (!bytes || N < 0) return RLK_ERROR_INVALID_VALUE;
+  if (N > kMaxTokens) return RLK_ERROR_UNSUPPORTED;
+  *bytes = loss_workspace(N);
+  return RLK_SUCCESS;
+}
+
+rlk_status_t rlk_ratio_kl_loss(const float* logp, const float* old_logp, const float* ref_logp,
+                               const float* adv, const uint8_t* mask, int64_t N, float eps_lo,
+                               float eps_hi, float beta, float scale, float* loss,
+                               float* bwd_adv, float* ratio, double* sums, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (N < 0) return RLK_ERROR_INVALID_VALUE;
+  if (N > kMaxTokens) return RLK_ERROR_UNSUPPORTED;
+  if (!(eps_lo >= 0.f && eps_lo < 1.f) || !(eps_hi >= 0.f && eps_hi <= 1e30f) ||
+      !(fabsf(beta) <= 1e30f) || !(fabsf(scale) <= 1e30f))
+    return RLK_ERROR_INVALID_VALUE;
+  if (N > 0 && (!logp || !old_logp || !adv || !mask || !loss || !bwd_adv))
+    return RLK_ERROR_INVALID_VALUE;
+  if (!workspace) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(logp, 4) || !aligned(old_logp, 4) || !aligned(ref_logp, 4) || !aligned(adv, 4) ||
+      !aligned(loss, 4) || !aligned(bwd_adv, 4) || !aligned(ratio, 4) || !aligned(sums, 8) ||
+      !aligned(workspace, 256))
+    return RLK_ERROR_UNSUPPORTED;
+  if (workspace_bytes < loss_workspace(N)) return RLK_ERROR_WORKSPACE;
+  LossArgs a{logp, old_logp, ref_logp, adv, mask, (int)N, eps_lo, eps_hi, beta, scale, loss,
+             bwd_adv, ratio, static_cast<double*>(workspace)};
+  return dev_status(launch_ratio_kl_loss(a, sums, static_cast<hipStream_t>(stream)));
+}
+
+rlk_status_t rlk_dlogp_diagnostics_workspace_size(int64_t N, size_t* bytes) {
+  if (!bytes || N < 0) return RLK_ERROR_INVALID_VALUE;
+  if (N > kMaxTokens) return RLK_ERROR_UNSUPPORTED;
+  *bytes = diag_layout(N).total;
+  return RLK_SUCCESS;
+}
+
+rlk_status_t rlk_dlogp_diagnostics(const float* logp_a, const float* logp_b,
+                                   const uint8_t* mask, int64_t N, float clip_eps, double* out,
+                                   int64_t* worst, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (N < 0) return RLK_ERROR_INVALID_VALUE;
+  if (N > kMaxTokens) return RLK_ERROR_UNSUPPORTED;
+  if (!(clip_eps >= 0.f && clip_eps <= 1e30f)) return RLK_ERROR_INVALID_VALUE;
+  if (!out || !worst || !workspace) return RLK_ERROR_INVALID_VALUE;
+  if (N > 0 && (!logp_a || !logp_b || !mask)) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(logp_a, 4) || !aligned(logp_b, 4) || !aligned(out, 8) || !aligned(worst, 8) ||
+      !aligned(workspace, 256))
+    return RLK_ERROR_UNSUPPORTED;
+  if (workspace_bytes < diag_layout(N).total) return RLK_ERROR_WORKSPACE;
+  const DiagLayout L = diag_layout(N);
+  int32_t* idx = carve<int32_t>(workspace, L.idx);
+  int32_t* na = carve<int32_t>(workspace, L.n_active);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
+  hipError_t e = launch_compact(c, st);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  DiagArgs a{logp_a, logp_b, idx, na, (int)N, clip_eps,
+             carve<uint64_t>(workspace, L.keys), carve<double>(workspace, L.part),
+             carve<uint64_t>(workspace, L.pmax), carve<int>(workspace, L.ptok),
+             carve<int>(workspace, L.hist), out, worst};
+  return dev_status(launch_dlogp_diagnostics(a, st));
 }
 
 rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* targets,

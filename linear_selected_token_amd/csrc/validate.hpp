@@ -75,6 +75,32 @@ inline FwdLayout fwd_layout(int64_t N, int64_t V, bool entropy = false) {
   return L;
 }
 
+// Loss fragments: the per-work-group partial sums.
+inline size_t loss_workspace(int64_t N) {
+  const size_t nblk = (size_t)((N + 1023) / 1024);
+  return align_up(32 * (nblk > 0 ? nblk : 1), 256);
+}
+
+struct DiagLayout {
+  size_t idx, n_active, keys, part, pmax, ptok, hist, total;
+};
+
+inline DiagLayout diag_layout(int64_t N) {
+  DiagLayout L;
+  const size_t n = (size_t)(N > 0 ? N : 1);
+  const size_t nblk = (n + 1023) / 1024;
+  size_t o = 0;
+  L.idx = o;      o = align_up(o + 4 * n, 256);
+  L.n_active = o; o = align_up(o + 4, 256);
+  L.keys = o;     o = align_up(o + 8 * n, 256);
+  L.part = o;     o = align_up(o + 32 * nblk, 256);
+  L.pmax = o;     o = align_up(o + 8 * nblk, 256);
+  L.ptok = o;     o = align_up(o + 4 * nblk, 256);
+  L.hist = o;     o = align_up(o + 4 * 8 * 6 * 256, 256);
+  L.total = o;
+  return L;
+}
+
 constexpr int64_t kBwdChunkEntries = 32768;
 
 inline int64_t bwd_npad(int64_t N) { return ((N > 0 ? N : 1) + 255) / 256 * 256; }

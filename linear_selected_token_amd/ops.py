@@ -304,3 +304,68 @@ class LinearLogp(torch.autograd.Function):
 def linear_logp(h, W, targets, mask, temperature) -> torch.Tensor:
     """Differentiable selected-token log-prob [N] (float32)."""
     return LinearLogp.apply(h, W, targets, mask, temperature)
+
+
+# ---- loss fragments on the log-prob
+
+def _vec(name: str, t: torch.Tensor, N: int, dtype=torch.float32) -> None:
+    if not t.is_cuda or t.dtype != dtype or t.shape != (N,) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor [{N}]")
+
+
+def rlk_ratio_kl_loss(logp: torch.Tensor, old_logp: torch.Tensor,
+                      ref_logp: Optional[torch.Tensor], adv: torch.Tensor, mask: torch.Tensor,
+                      eps_lo: float, eps_hi: float, beta: float = 0.0, scale: float = 1.0,
+                      want_ratio: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Clipped policy-gradient loss with a KL penalty, per token.  Returns (loss [N],
+    bwd_adv [N] = -dloss/dlogp, ratio [N] or None, sums [4] float64 on the device:
+    sum loss, clipped count, sum kl, active count)."""
+    mask = _mask_u8(mask)
+    N = logp.shape[0]
+    for name, t in (("logp", logp), ("old_logp", old_logp), ("adv", adv)):
+        _vec(name, t, N)
+    if ref_logp is not None:
+        _vec("ref_logp", ref_logp, N)
+    _vec("mask", mask, N, torch.uint8)
+    dev = logp.device
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    badv = torch.empty(N, dtype=torch.float32, device=dev)
+    ratio = torch.empty(N, dtype=torch.float32, device=dev) if want_ratio else None
+    sums = torch.empty(4, dtype=torch.float64, device=dev)
+    nb = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_ratio_kl_loss_workspace_size(N, ctypes.byref(nb)),
+            "rlk_ratio_kl_loss_workspace_size")
+    ws = _workspace(int(nb.value), dev, workspace)
+    L.check(L.lib().rlk_ratio_kl_loss(_vp(logp), _vp(old_logp), _vp(ref_logp), _vp(adv),
+                                      _vp(mask), N, float(eps_lo), float(eps_hi), float(beta),
+                                      float(scale), _vp(loss), _vp(badv), _vp(ratio), _vp(sums),
+                                      _vp(ws), ws.numel() * ws.element_size(), _stream(dev)),
+            "rlk_ratio_kl_loss")
+    return loss, badv, ratio, sums
+
+
+DIAG_FIELDS = ("active", "mean", "max", "p50", "p90", "p99", "ratio_mean", "clipfrac",
+               "approx_kl")
+
+
+def rlk_dlogp_diagnostics(logp_a: torch.Tensor, logp_b: torch.Tensor, mask: torch.Tensor,
+                          clip_eps: float, workspace: Optional[torch.Tensor] = None):
+    """dlogp diagnostics over active tokens; returns (out [9] float64, worst [1] int64), both
+    on the device (fields in DIAG_FIELDS order)."""
+    mask = _mask_u8(mask)
+    N = logp_a.shape[0]
+    _vec("logp_a", logp_a, N)
+    _vec("logp_b", logp_b, N)
+    _vec("mask", mask, N, torch.uint8)
+    dev = logp_a.device
+    out = torch.empty(9, dtype=torch.float64, device=dev)
+    worst = torch.empty(1, dtype=torch.int64, device=dev)
+    nb = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_dlogp_diagnostics_workspace_size(N, ctypes.byref(nb)),
+            "rlk_dlogp_diagnostics_workspace_size")
+    ws = _workspace(int(nb.value), dev, workspace)
+    L.check(L.lib().rlk_dlogp_diagnostics(_vp(logp_a), _vp(logp_b), _vp(mask), N,
+                                          float(clip_eps), _vp(out), _vp(worst), _vp(ws),
+                                          ws.numel() * ws.element_size(), _stream(dev)),
+            "rlk_dlogp_diagnostics")
+    return out, worst

@@ -46,7 +46,8 @@ def ratio_kl_loss(logp, old_logp, ref_logp: Optional[np.ndarray], adv, mask, eps
                   eps_hi: float, beta: float, scale: float,
                   ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray, Dict[str, float]]:
     """(loss [N], dL/dlogp [N], ratio [N], clipped [N] int, sums) in float64; 0 at
-    inactive tokens.  ref_logp None means no KL term."""
+    inactive tokens.  ref_logp None means no KL term; with a reference the KL sum is
+    reported even when beta = 0 (monitoring without a penalty)."""
     lp = _f64(logp)
     m = np.asarray(mask).astype(bool)
     A = _f64(adv)
@@ -56,7 +57,7 @@ def ratio_kl_loss(logp, old_logp, ref_logp: Optional[np.ndarray], adv, mask, eps
     pg = np.maximum(unclipped, clipped_term)
     clipped = clipped_term > unclipped
     dpg = np.where(clipped, 0.0, -A * r)
-    if ref_logp is not None and beta != 0.0:
+    if ref_logp is not None:
         d = _f64(ref_logp) - lp
         kl = np.exp(d) - 1.0 - d
         dkl = 1.0 - np.exp(d)

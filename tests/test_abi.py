@@ -245,3 +245,41 @@ def test_entropy_backward_argument_errors(L):
     assert bwd(dt=1) == E.RLK_ERROR_UNSUPPORTED
     assert bwd(H=192) == E.RLK_ERROR_UNSUPPORTED
     assert bwd(wsb=10) == E.RLK_ERROR_WORKSPACE
+
+
+def test_loss_fragment_argument_errors(L):
+    # every case is decided on the host, before anything could be launched
+    lib = L.lib()
+    E = L
+
+    def loss(N=8, eps_lo=0.2, eps_hi=0.2, beta=0.0, scale=1.0, lp=FAKE, ws=FAKE, wsb=1 << 20):
+        return lib.rlk_ratio_kl_loss(lp, FAKE, None, FAKE, FAKE, N, eps_lo, eps_hi, beta, scale,
+                                     FAKE, FAKE, None, None, ws, wsb, None)
+
+    assert loss(N=-1) == E.RLK_ERROR_INVALID_VALUE
+    assert loss(N=1 << 23) == E.RLK_ERROR_UNSUPPORTED
+    assert loss(eps_lo=1.0) == E.RLK_ERROR_INVALID_VALUE
+    assert loss(eps_lo=-0.1) == E.RLK_ERROR_INVALID_VALUE
+    assert loss(eps_hi=float("nan")) == E.RLK_ERROR_INVALID_VALUE
+    assert loss(beta=float("inf")) == E.RLK_ERROR_INVALID_VALUE
+    assert loss(scale=float("nan")) == E.RLK_ERROR_INVALID_VALUE
+    assert loss(lp=None) == E.RLK_ERROR_INVALID_VALUE
+    assert loss(ws=None) == E.RLK_ERROR_INVALID_VALUE
+    assert loss(lp=FAKE + 2) == E.RLK_ERROR_UNSUPPORTED
+    assert loss(ws=FAKE + 64) == E.RLK_ERROR_UNSUPPORTED
+    assert loss(wsb=16) == E.RLK_ERROR_WORKSPACE
+    st, b1 = _ws(lib, "rlk_ratio_kl_loss_workspace_size", 1 << 20)
+    assert st == 0 and b1 >= 32 * 1024
+
+    def diag(N=8, eps=0.2, a=FAKE, out=FAKE, worst=FAKE, wsb=1 << 20):
+        return lib.rlk_dlogp_diagnostics(a, FAKE, FAKE, N, eps, out, worst, FAKE, wsb, None)
+
+    assert diag(N=-1) == E.RLK_ERROR_INVALID_VALUE
+    assert diag(eps=-1.0) == E.RLK_ERROR_INVALID_VALUE
+    assert diag(out=None) == E.RLK_ERROR_INVALID_VALUE
+    assert diag(worst=None) == E.RLK_ERROR_INVALID_VALUE
+    assert diag(a=None) == E.RLK_ERROR_INVALID_VALUE
+    assert diag(out=FAKE + 4) == E.RLK_ERROR_UNSUPPORTED
+    assert diag(wsb=100) == E.RLK_ERROR_WORKSPACE
+    st, b2 = _ws(lib, "rlk_dlogp_diagnostics_workspace_size", 1 << 20)
+    assert st == 0 and b2 >= 12 * (1 << 20)

@@ -130,3 +130,15 @@ def test_diagnostics_ties_and_empty():
     assert out["worst"] == 0 and out["p50"] == 0.5 and out["max"] == 0.5
     empty = rl.dlogp_diagnostics(a, b, np.zeros(4, np.uint8), 0.1)
     assert empty["active"] == 0 and empty["worst"] == -1
+
+
+def test_kl_reported_without_penalty():
+    logp, old, ref, adv, mask = _inputs(5, 200)
+    l0, g0, _, _, s0 = rl.ratio_kl_loss(logp, old, None, adv, mask, 0.2, 0.2, 0.0, 1.0)
+    l1, g1, _, _, s1 = rl.ratio_kl_loss(logp, old, ref, adv, mask, 0.2, 0.2, 0.0, 1.0)
+    np.testing.assert_array_equal(l0, l1)
+    np.testing.assert_array_equal(g0, g1)
+    m = mask.astype(bool)
+    d = ref[m] - logp[m]
+    assert s0["kl"] == 0
+    assert abs(s1["kl"] - math.fsum(math.exp(x) - 1 - x for x in d)) < 1e-10
