@@ -52,11 +52,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     p.add_argument("--mode", default="fwdbwd",
-                   choices=["fwd", "fwdbwd", "entropy", "ppo", "logits"],
+                   choices=["fwd", "fwdbwd", "entropy", "ppo", "kl", "logits"],
                    help="fwdbwd: the fused forward and backward (the headline); fwd: forward "
                         "only; entropy: a step with an entropy bonus (the entropy forward and "
                         "its backward); ppo: forward, clipped policy-gradient loss with a KL "
-                        "penalty, backward, plus the dlogp diagnostics; logits: log-prob from existing "
+                        "penalty, backward, plus the dlogp diagnostics; kl: full-vocabulary KL "
+                        "to a teacher head of the same shape, forward and backward; logits: log-prob from existing "
                         "bf16 logits of the same shape (an HBM-bound path, reported against "
                         "HBM bandwidth)")
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
@@ -350,6 +351,76 @@ def bench_ppo(args, w):
     print(json.dumps(out), flush=True)
 
 
+def bench_kl(args, w):
+    """Distillation step: forward and reverse full-vocabulary KL between the workload's student
+    head and a teacher head of the same shape (seeded N(0,1) hidden states, N(0,1/H) weights,
+    drawn on the device, bf16), then the backward of the forward KL into the student."""
+    import torch
+    import linear_selected_token_amd as rlk
+    dev = torch.device("cuda", 0)
+    N, H, V, T, Na = w.N, w.H, w.V, w.T, w.n_active
+    h, W, _, mask, _ = upload(w, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1011)
+    ht = torch.randn((N, H), generator=g, device=dev).to(torch.bfloat16)
+    Wt = torch.empty((V, H), dtype=torch.bfloat16, device=dev)
+    for r0 in range(0, V, 8192):
+        r1 = min(V, r0 + 8192)
+        Wt[r0:r1] = (torch.randn((r1 - r0, H), generator=g, device=dev) / H ** 0.5).to(
+            torch.bfloat16)
+    coef = torch.full((N,), 1.0 / max(Na, 1), dtype=torch.float32, device=dev)
+    import ctypes
+    nb = ctypes.c_size_t(0)
+    rlk.lib().rlk_linear_kl_fwd_workspace_size(N, H, H, V, 0, ctypes.byref(nb))
+    ws_f = torch.empty(int(nb.value), dtype=torch.uint8, device=dev)
+    rlk.lib().rlk_linear_kl_bwd_workspace_size(N, H, H, V, 0, ctypes.byref(nb))
+    ws_b = torch.empty(int(nb.value), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    def fwd():
+        return rlk.rlk_linear_kl_fwd(h, W, ht, Wt, mask, T, workspace=ws_f)
+
+    def step():
+        _, kr, ls, lt = fwd()
+        rlk.rlk_linear_kl_bwd(h, W, ht, Wt, mask, T, False, coef, ls, lt, kr, workspace=ws_b)
+
+    ms = timed(step)
+    fwd_ms = timed(fwd)
+    flop = 12.0 * Na * H * V   # 2 heads forward + 2 heads recomputed + dL/dh + dL/dW
+    tf = flop / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "active tokens/sec, full-vocabulary KL to a teacher head, fwd + bwd",
+        "value": round(Na / (ms * 1e-3), 1), "unit": "active tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: the workload's student head; teacher h~N(0,1), W~N(0,1/H) drawn "
+                "on the device, bf16",
+        "config": {"workload": args.workload, "mode": "kl", "N": N, "H_s": H, "H_t": H, "V": V,
+                   "T": T, "n_active": Na, "parallelism": "none (1 GPU)"},
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_tflops": round(4.0 * Na * H * V / (fwd_ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "kernel": "whole step (both heads' tile GEMMs per chunk, "
+                     "cross/grad streams, dL/dh, dL/dW)", "achieved": round(tf, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flop_per_launch": flop, "avg_launch_ms": round(ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -372,6 +443,9 @@ def main():
         return
     if args.mode == "ppo":
         bench_ppo(args, w)
+        return
+    if args.mode == "kl":
+        bench_kl(args, w)
         return
     N, H, V, T = w.N, w.H, w.V, w.T
     Na = w.n_active

@@ -188,6 +188,47 @@ rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int
                                          const float* entropy, float* dh, float* dW,
                                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Full-vocabulary KL between a student and a teacher LM head (RL-Kernel Roadmap (2026),
+ * operator backlog: chunked full-vocabulary / distillation KL fused with the LM head, forward
+ * and reverse, beyond the sampled-token path).
+ *   h_s [N,H_s], W_s [V,H_s]   student hidden states and LM head (dtype)
+ *   h_t [N,H_t], W_t [V,H_t]   teacher (the same dtype, vocabulary and temperature)
+ *   z_s = h_s W_s^T / T, z_t = h_t W_t^T / T, p = softmax(z)
+ *   kl_fwd[t] = sum_v p_t (log p_t - log p_s),  kl_rev[t] = sum_v p_s (log p_s - log p_t)
+ * at active tokens, 0 elsewhere (both clamped at 0 against rounding).  The vocabulary is walked
+ * in chunks of 32768 entries: per chunk each head's tile GEMM writes its column statistics
+ * and its logits of that chunk only (fp32, [N rounded up to 256] x 32768 in the workspace),
+ * a streaming kernel pairs the two entry by entry, and a fixed-order merge gives the results.
+ * Batch-invariant like logp.  H_s and H_t: multiples of 64; each h at most 2^31 - 1 bytes.
+ *   lse_s, lse_t [N] float     out (may be NULL): each head's log-sum-exp, which the backward
+ *                              takes back
+ *   workspace: rlk_linear_kl_fwd_workspace_size bytes (about 8 N (V/128) * 6 + 2 chunks). */
+rlk_status_t rlk_linear_kl_fwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
+                                              int dtype, size_t* bytes);
+rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t,
+                               const void* W_t, const uint8_t* mask, int64_t N, int64_t H_s,
+                               int64_t H_t, int64_t V, int dtype, float temperature,
+                               float* kl_fwd, float* kl_rev, float* lse_s, float* lse_t,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of L = sum_t mask_t coef_t KL[t] into the student (bf16, H_s a multiple of 256); the
+ * teacher is frozen.  reverse = 0: KL = kl_fwd, dL/dz_s = coef (p_s - p_t); reverse != 0:
+ * KL = kl_rev, dL/dz_s = coef p_s (log p_s - log p_t - kl_rev).  Per chunk both heads' logits
+ * are recomputed on MFMA, dL/dz is formed in a streaming kernel and rounded to bf16, and the
+ * chunk's dL/dh_s and dL/dW_s follow as in rlk_linear_logp_bwd.
+ *   coef [N] float; lse_s, lse_t [N] and (reverse only) kl_rev [N] from rlk_linear_kl_fwd
+ *   dh_s [N,H_s], dW_s [V,H_s] float   out, overwritten
+ *   workspace: rlk_linear_kl_bwd_workspace_size bytes. */
+rlk_status_t rlk_linear_kl_bwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
+                                              int dtype, size_t* bytes);
+rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t,
+                               const void* W_t, const uint8_t* mask, int64_t N, int64_t H_s,
+                               int64_t H_t, int64_t V, int dtype, float temperature,
+                               int reverse, const float* coef, const float* lse_s,
+                               const float* lse_t, const float* kl_rev, float* dh_s,
+                               float* dW_s, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* ---- Loss fragments that consume the log-prob (RL-Kernel integration roadmap for vime,
  * "RL Loss Operators: ratio_kl, GRPO/PPO/DPO Loss Fragments": optional fused ratio / KL
  * fragments whose contract states mask handling, aggregation, dtype and reduction order).

@@ -18,6 +18,8 @@ from .ops import (  # noqa: E402,F401
     num_vocab_partials,
     rlk_compact_active,
     rlk_dlogp_diagnostics,
+    rlk_linear_kl_bwd,
+    rlk_linear_kl_fwd,
     rlk_linear_logp_bwd,
     rlk_linear_logp_bwd_entropy,
     rlk_linear_logp_fwd,

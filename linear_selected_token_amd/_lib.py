@@ -46,6 +46,14 @@ SIGNATURES = {
     "rlk_linear_logp_partials_shard": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64,
                                               _int, _f, _p, _p, _p, _p]),
     "rlk_linear_logp_merge": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p]),
+    "rlk_linear_kl_fwd_workspace_size": (_int, [_i64, _i64, _i64, _i64, _int,
+                                                ctypes.POINTER(_sz)]),
+    "rlk_linear_kl_fwd": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _f, _p, _p, _p,
+                                 _p, _p, _sz, _p]),
+    "rlk_linear_kl_bwd_workspace_size": (_int, [_i64, _i64, _i64, _i64, _int,
+                                                ctypes.POINTER(_sz)]),
+    "rlk_linear_kl_bwd": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _f, _int, _p,
+                                 _p, _p, _p, _p, _p, _p, _sz, _p]),
     "rlk_ratio_kl_loss_workspace_size": (_int, [_i64, ctypes.POINTER(_sz)]),
     "rlk_ratio_kl_loss": (_int, [_p, _p, _p, _p, _p, _i64, _f, _f, _f, _f, _p, _p, _p, _p, _p,
                                  _sz, _p]),

@@ -191,7 +191,8 @@ rlk_status_t rlk_linear_logp_partials_shard(const void* h, const void* W, const 
   FwdTileArgs a{h, W, targets, idx, n_active, (int)N, (int)H, (int)V,
                 (float)(1.0 / (double)temperature), part_max, part_sum, target_logit,
                 (int)vocab_start};
-  return dev_status(launch_fwd_tiles(a, dtype == RLK_BF16, grid, static_cast<hipStream_t>(stream)));
+  return dev_status(
+      launch_fwd_tiles(a, dtype == RLK_BF16, grid, static_cast<hipStream_t>(stream), kFwdPlain));
 }
 
 rlk_status_t rlk_linear_logp_partials(const void* h, const void* W, const int32_t* targets,
@@ -292,7 +293,7 @@ rlk_status_t rlk_linear_logp_fwd_entropy(const void* h, const void* W, const int
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
   FwdTileArgs a{h, W, targets, idx, na, (int)N, (int)H, (int)V,
                 (float)(1.0 / (double)temperature), pm, ps, zy, 0, pw};
-  e = launch_fwd_tiles(a, dtype == RLK_BF16, grid, st);
+  e = launch_fwd_tiles(a, dtype == RLK_BF16, grid, st, kFwdEntropy);
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
   MergeArgs m{pm, ps, zy, idx, na, (int)N, (int)V, logp, lse, pw, entropy};
   return dev_status(launch_fwd_merge(m, st));
@@ -360,6 +361,170 @@ rlk_status_t rlk_dlogp_diagnostics(const float* logp_a, const float* logp_b,
              carve<uint64_t>(workspace, L.pmax), carve<int>(workspace, L.ptok),
              carve<int>(workspace, L.hist), out, worst};
   return dev_status(launch_dlogp_diagnostics(a, st));
+}
+
+rlk_status_t rlk_linear_kl_fwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
+                                              int dtype, size_t* bytes) {
+  if (!bytes) return RLK_ERROR_INVALID_VALUE;
+  rlk_status_t s = check_shape(N, H_s, V, dtype);
+  if (s == RLK_SUCCESS) s = check_shape(N, H_t, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  *bytes = kl_fwd_layout(N, V).total;
+  return RLK_SUCCESS;
+}
+
+rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t,
+                               const void* W_t, const uint8_t* mask, int64_t N, int64_t H_s,
+                               int64_t H_t, int64_t V, int dtype, float temperature,
+                               float* kl_fwd, float* kl_rev, float* lse_s, float* lse_t,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  rlk_status_t s = check_kl(h_s, W_s, h_t, W_t, mask, N, H_s, H_t, V, dtype, temperature,
+                            workspace);
+  if (s != RLK_SUCCESS || N == 0) return s;
+  if (!kl_fwd || !kl_rev) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(kl_fwd, 4) || !aligned(kl_rev, 4) || !aligned(lse_s, 4) || !aligned(lse_t, 4))
+    return RLK_ERROR_UNSUPPORTED;
+  if (workspace_bytes < kl_fwd_layout(N, V).total) return RLK_ERROR_WORKSPACE;
+  const KlLayout L = kl_fwd_layout(N, V);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* idx = carve<int32_t>(workspace, L.idx);
+  int32_t* na = carve<int32_t>(workspace, L.n_active);
+  CompactArgs c{mask, idx, na, nullptr, kl_fwd, lse_s, (int)N, kl_rev, lse_t};
+  hipError_t e = launch_compact(c, st);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  int grid = 0;
+  if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
+  const float inv_t = (float)(1.0 / (double)temperature);
+  const size_t es = dtype == RLK_BF16 ? 2 : 4;
+  KlArgs k{};
+  k.idx = idx;
+  k.n_active = na;
+  k.N = (int)N;
+  k.V = (int)V;
+  k.inv_t = inv_t;
+  k.xs = carve<float>(workspace, L.xs);
+  k.xt = carve<float>(workspace, L.xt);
+  k.s_max = carve<float>(workspace, L.smax);
+  k.s_sum = carve<float>(workspace, L.ssum);
+  k.t_max = carve<float>(workspace, L.tmax);
+  k.t_sum = carve<float>(workspace, L.tsum);
+  k.wf = carve<float>(workspace, L.wf);
+  k.wr = carve<float>(workspace, L.wr);
+  k.kl_fwd = kl_fwd;
+  k.kl_rev = kl_rev;
+  k.lse_s = lse_s;
+  k.lse_t = lse_t;
+  for (int64_t c0 = 0; c0 < V; c0 += kBwdChunk) {
+    const int vc = (int)(V - c0 < kBwdChunk ? V - c0 : kBwdChunk);
+    FwdTileArgs t{h_t, static_cast<const uint8_t*>(W_t) + (size_t)c0 * H_t * es, nullptr, idx, na,
+                  (int)N, (int)H_t, vc, inv_t, const_cast<float*>(k.t_max),
+                  const_cast<float*>(k.t_sum), nullptr, (int)c0, nullptr,
+                  const_cast<float*>(k.xt)};
+    e = launch_fwd_tiles(t, dtype == RLK_BF16, grid, st, kFwdStoreX);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    FwdTileArgs u{h_s, static_cast<const uint8_t*>(W_s) + (size_t)c0 * H_s * es, nullptr, idx, na,
+                  (int)N, (int)H_s, vc, inv_t, const_cast<float*>(k.s_max),
+                  const_cast<float*>(k.s_sum), nullptr, (int)c0, nullptr,
+                  const_cast<float*>(k.xs)};
+    e = launch_fwd_tiles(u, dtype == RLK_BF16, grid, st, kFwdStoreX);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    e = launch_kl_cross(k, (int)c0, (int)N, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  }
+  return dev_status(launch_kl_merge(k, st));
+}
+
+rlk_status_t rlk_linear_kl_bwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
+                                              int dtype, size_t* bytes) {
+  if (!bytes) return RLK_ERROR_INVALID_VALUE;
+  rlk_status_t s = check_shape(N, H_s, V, dtype);
+  if (s == RLK_SUCCESS) s = check_shape(N, H_t, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  if (dtype != RLK_BF16 || H_s % 256 != 0) return RLK_ERROR_UNSUPPORTED;
+  *bytes = kl_bwd_bytes(N, H_s);
+  return RLK_SUCCESS;
+}
+
+rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t,
+                               const void* W_t, const uint8_t* mask, int64_t N, int64_t H_s,
+                               int64_t H_t, int64_t V, int dtype, float temperature,
+                               int reverse, const float* coef, const float* lse_s,
+                               const float* lse_t, const float* kl_rev, float* dh_s,
+                               float* dW_s, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  rlk_status_t s = check_kl(h_s, W_s, h_t, W_t, mask, N, H_s, H_t, V, dtype, temperature,
+                            workspace);
+  if (s != RLK_SUCCESS) return s;
+  if (dtype != RLK_BF16 || H_s % 256 != 0) return RLK_ERROR_UNSUPPORTED;
+  if (!dW_s) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(dW_s, 4)) return RLK_ERROR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (N == 0) return dev_status(launch_zero(dW_s, (size_t)V * (size_t)H_s, st));
+  if (!coef || !lse_s || !lse_t || !dh_s || (reverse && !kl_rev)) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(coef, 4) || !aligned(lse_s, 4) || !aligned(lse_t, 4) || !aligned(kl_rev, 4) ||
+      !aligned(dh_s, 4))
+    return RLK_ERROR_UNSUPPORTED;
+  if (workspace_bytes < kl_bwd_bytes(N, H_s)) return RLK_ERROR_WORKSPACE;
+  int grid = 0;
+  if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
+  const BwdLayout L = bwd_layout(N, H_s);
+  const float inv_t = (float)(1.0 / (double)temperature);
+  int32_t* idx = carve<int32_t>(workspace, L.idx);
+  int32_t* na = carve<int32_t>(workspace, L.n_active);
+  BwdArgs a{};
+  a.h = h_s;
+  a.W = W_s;
+  a.idx = idx;
+  a.n_active = na;
+  a.N = (int)N;
+  a.H = (int)H_s;
+  a.V = (int)V;
+  a.Npad = (int)bwd_npad(N);
+  a.inv_t = inv_t;
+  a.dh = dh_s;
+  a.dW = dW_s;
+  a.hT = carve<uint16_t>(workspace, L.hT);
+  a.Gv = carve<uint16_t>(workspace, L.Gv);
+  a.dh1 = carve<float>(workspace, L.dh1);
+  float* xs = carve<float>(workspace, L.total);
+  float* xt = carve<float>(workspace, L.total + kl_chunk_bytes(N));
+  KlArgs k{};
+  k.idx = idx;
+  k.n_active = na;
+  k.N = (int)N;
+  k.V = (int)V;
+  k.inv_t = inv_t;
+  k.xs = xs;
+  k.xt = xt;
+  k.lse_s_in = lse_s;
+  k.lse_t_in = lse_t;
+  k.kl_rev_in = kl_rev;
+  k.coef = coef;
+  k.Gv = a.Gv;
+  CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
+  hipError_t e = launch_compact(c, st);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  e = launch_bwd_prepare(a, st);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  const int nchunks = (int)((V + kBwdChunk - 1) / kBwdChunk);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int64_t c0 = (int64_t)ch * kBwdChunk;
+    const int vc = (int)(V - c0 < kBwdChunk ? V - c0 : kBwdChunk);
+    // both heads' x of the chunk (no statistics), then dL/dz of the chunk into Gv
+    FwdTileArgs t{h_t, static_cast<const uint8_t*>(W_t) + (size_t)c0 * H_t * 2, nullptr, idx, na,
+                  (int)N, (int)H_t, vc, inv_t, nullptr, nullptr, nullptr, (int)c0, nullptr, xt};
+    e = launch_fwd_tiles(t, true, grid, st, kFwdStoreX);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    FwdTileArgs u{h_s, static_cast<const uint8_t*>(W_s) + (size_t)c0 * H_s * 2, nullptr, idx, na,
+                  (int)N, (int)H_s, vc, inv_t, nullptr, nullptr, nullptr, (int)c0, nullptr, xs};
+    e = launch_fwd_tiles(u, true, grid, st, kFwdStoreX);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    e = launch_kl_grad(k, (int)c0, a.Npad, reverse != 0, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    e = launch_bwd_chunk_gemms(a, ch, grid, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  }
+  return dev_status(launch_bwd_finish(a, st));
 }
 
 rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* targets,

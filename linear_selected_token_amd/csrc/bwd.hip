@@ -330,6 +330,13 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t s
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, hipStream_t stream) {
+  const int c0 = chunk * kBwdChunk;
+  hipLaunchKernelGGL(dh_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  hipLaunchKernelGGL(dw_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(dh_finish_kernel, dim3(2048), dim3(256), 0, stream, a);
   return hipGetLastError();

@@ -35,6 +35,7 @@ __global__ __launch_bounds__(1024) void compact_kernel(CompactArgs a) {
           if (a.logp) a.logp[t] = 0.f;
           if (a.lse) a.lse[t] = 0.f;
           if (a.entropy) a.entropy[t] = 0.f;
+          if (a.extra) a.extra[t] = 0.f;
         }
       }
       cnt += f[k];

@@ -32,12 +32,21 @@ struct FwdCtx {
   int tgt[kBlkB];  // their targets (-1: none or out of range)
 };
 
-// kEnt: also the entropy statistic of each column, part_w = sum_v e_v max(d_v, -126) with
-// d_v = x_v - max (log2 units) and e_v = 2^d_v; the clamp only touches terms whose e_v is 0
-// (entries past the vocabulary, or underflowed), so the column's sum_v e_v x_v is
-// part_w + max * part_sum.  The max and sum are computed exactly as without it.
-template <bool kBF16, bool kEnt>
+// Epilogue modes.  The column maximum and sum are computed the same way in every mode.
+//   kFwdPlain    column max and sum, target logit.
+//   kFwdEntropy  also part_w = sum_v e_v max(d_v, -126) with d_v = x_v - max (log2 units)
+//                and e_v = 2^d_v; the clamp only touches terms whose e_v is 0 (entries past
+//                the vocabulary, or underflowed), so the column's sum_v e_v x_v is
+//                part_w + max * part_sum.
+//   kFwdStoreX   also stores x = z log2 e of every entry of the tile into xbuf, token-major
+//                with kBwdChunk entries per compacted token (the vocabulary is walked one
+//                chunk per launch, as a shard); the column statistics are written only when
+//                part_max is given.  No target.  The full-vocabulary KL between two heads
+//                pairs their x entry by entry from two such buffers.
+template <bool kBF16, int kMode>
 __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
+  constexpr bool kEnt = kMode == kFwdEntropy;
+  constexpr bool kNoTarget = kMode == kFwdStoreX;
   __shared__ RingSmem sm;
   const int Na = *a.n_active;
   const int nTokTiles = (Na + kTile - 1) / kTile;
@@ -76,8 +85,12 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
     for (int j = 0; j < kBlkB; ++j) {
       c.tok[j] = tbase + wt + acc_col(j, lane);
       // target as a row of this W (out of range or in another vocabulary shard: none)
-      const int y = c.tok[j] < Na ? a.targets[a.idx[c.tok[j]]] - a.vstart : -1;
-      c.tgt[j] = (y >= 0 && y < a.V) ? y : -1;
+      if constexpr (kNoTarget) {
+        c.tgt[j] = -1;
+      } else {
+        const int y = c.tok[j] < Na ? a.targets[a.idx[c.tok[j]]] - a.vstart : -1;
+        c.tgt[j] = (y >= 0 && y < a.V) ? y : -1;
+      }
     }
   };
 
@@ -155,10 +168,29 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
         w = w + __shfl_xor(w, 32);
       }
       const int ti = c.tok[j];
+      if constexpr (kMode == kFwdStoreX) {
+        // x of every entry (tail entries hold -inf), four consecutive entries per store
+        if (ti < Na) {
+          float* xrow = a.xbuf + (size_t)ti * kBwdChunk + vq;
+#pragma unroll
+          for (int i = 0; i < kBlkA; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4 x;
+              x.x = acc.c[i][j][4 * g + 0] * c2;
+              x.y = acc.c[i][j][4 * g + 1] * c2;
+              x.z = acc.c[i][j][4 * g + 2] * c2;
+              x.w = acc.c[i][j][4 * g + 3] * c2;
+              *reinterpret_cast<f32x4*>(xrow + acc_row(i, 4 * g, lane)) = x;
+            }
+        }
+      }
       if (ti < Na) {
         if (lane < 32) {
-          a.part_max[(size_t)col * a.N + ti] = mx;
-          a.part_sum[(size_t)col * a.N + ti] = s;
+          if (kMode != kFwdStoreX || a.part_max) {
+            a.part_max[(size_t)col * a.N + ti] = mx;
+            a.part_sum[(size_t)col * a.N + ti] = s;
+          }
           if constexpr (kEnt) a.part_w[(size_t)col * a.N + ti] = w;
         }
         if (hit) a.target_logit[ti] = zsel * a.inv_t;
@@ -226,16 +258,22 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(MergeArgs a) {
 
 }  // namespace
 
-hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream_t stream) {
-  const bool ent = a.part_w != nullptr;
-  if (bf16 && !ent)
-    hipLaunchKernelGGL((fwd_tiles_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
-  else if (bf16)
-    hipLaunchKernelGGL((fwd_tiles_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
-  else if (!ent)
-    hipLaunchKernelGGL((fwd_tiles_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+template <int kMode>
+void launch_mode(const FwdTileArgs& a, bool bf16, int grid, hipStream_t stream) {
+  if (bf16)
+    hipLaunchKernelGGL((fwd_tiles_kernel<true, kMode>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_tiles_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fwd_tiles_kernel<false, kMode>), dim3(grid), dim3(kThreads), 0, stream, a);
+}
+
+hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream_t stream,
+                            int mode) {
+  switch (mode) {
+    case kFwdPlain: launch_mode<kFwdPlain>(a, bf16, grid, stream); break;
+    case kFwdEntropy: launch_mode<kFwdEntropy>(a, bf16, grid, stream); break;
+    case kFwdStoreX: launch_mode<kFwdStoreX>(a, bf16, grid, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ struct CompactArgs {
   float* lse;           // may be null: 0 at inactive tokens
   int N;
   float* entropy = nullptr;  // may be null: 0 at inactive tokens
+  float* extra = nullptr;    // may be null: 0 at inactive tokens
 };
 
 struct FwdTileArgs {
@@ -33,8 +34,11 @@ struct FwdTileArgs {
   float* part_sum;
   float* target_logit;
   int vstart;  // global vocabulary index of W row 0 (a multiple of kVocabPartial)
-  float* part_w = nullptr;  // [J][N] entropy statistic per column, or null
+  float* part_w = nullptr;  // [J][N] entropy statistic per column (kFwdEntropy)
+  float* xbuf = nullptr;    // [Npad][kBwdChunk] x = z log2 e of one vocabulary chunk (kFwdStoreX)
 };
+
+enum FwdMode { kFwdPlain = 0, kFwdEntropy = 1, kFwdStoreX = 2 };
 
 struct MergeArgs {
   const float* part_max;
@@ -117,17 +121,49 @@ struct DiagArgs {
   int64_t* worst;
 };
 
+// Full-vocabulary KL between a student (s) and a teacher (t) head.
+struct KlArgs {
+  const int32_t* idx;
+  const int32_t* n_active;
+  int N, V;
+  float inv_t;
+  const float* xs;     // [Npad][kBwdChunk] student x of the current chunk
+  const float* xt;     // teacher
+  const float* s_max;  // [J][N] column statistics
+  const float* s_sum;
+  const float* t_max;
+  const float* t_sum;
+  float* wf;           // [J][N] forward-KL cross term per column
+  float* wr;           // reverse
+  float* kl_fwd;       // [N] outputs of the merge
+  float* kl_rev;
+  float* lse_s;        // may be null
+  float* lse_t;        // may be null
+  // backward
+  const float* lse_s_in;
+  const float* lse_t_in;
+  const float* kl_rev_in;  // reverse KL only
+  const float* coef;       // [N] c_t
+  uint16_t* Gv;            // [Npad][kBwdChunk]
+};
+
 hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
-hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream_t stream);
+hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream_t stream,
+                            int mode);
 hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_logits_logp(const LogitsArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_ratio_kl_loss(const LossArgs& a, double* sums, hipStream_t stream);
 hipError_t launch_dlogp_diagnostics(const DiagArgs& a, hipStream_t stream);
+hipError_t launch_kl_cross(const KlArgs& a, int c0, int rows, hipStream_t stream);
+hipError_t launch_kl_merge(const KlArgs& a, hipStream_t stream);
+hipError_t launch_kl_grad(const KlArgs& a, int c0, int rows, bool reverse, hipStream_t stream);
 
 // Backward phases.
 hipError_t launch_zero(float* p, size_t n, hipStream_t stream);
 hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream);          // dh = 0, hT
 hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t stream);
+// dL/dh and dL/dW of one chunk from a Gv written elsewhere
+hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, hipStream_t stream);
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);          // dh += dh1
 
 }  // namespace rlk

@@ -1,0 +1,216 @@
+// Full-vocabulary KL between a teacher and a student LM head (RL-Kernel Roadmap (2026),
+// operator backlog: chunked full-vocabulary / distillation KL fused with the LM head,
+// forward and reverse).
+//
+// The vocabulary is walked in chunks of kBwdChunk entries.  Per chunk, each head's tile
+// kernel (fwd_tiles_kernel in its kFwdStoreX mode, run as a vocabulary shard) writes its
+// column statistics and x = z log2 e of the chunk, token-major, into a chunk buffer; the
+// kernels below pair the two buffers entry by entry.  At most one chunk of each head's
+// logits exists at a time.
+//
+//   kl_cross    per token and 128-entry column:
+//                 wf = sum_v 2^(x_t - m_t) (x_t - x_s)   (forward KL's cross term)
+//                 wr = sum_v 2^(x_s - m_s) (x_s - x_t)   (reverse KL's)
+//               with m_t, m_s the columns' maxima.
+//   kl_merge    per token, in the forward merge's fixed association: both heads' M and S,
+//                 KL_fwd = ln2 (A_f / S_t - (M_t + log2 S_t) + (M_s + log2 S_s))
+//                 KL_rev = ln2 (A_r / S_s - (M_s + log2 S_s) + (M_t + log2 S_t))
+//               with A_f = sum_j 2^(m_t,j - M_t) wf_j and A_r likewise.
+//   kl_grad     the backward's dL/dz of one chunk for L = sum_t c_t KL_t, rounded to bf16 in
+//               the token-major layout the dL/dh and dL/dW GEMMs read (Gv):
+//                 forward KL: (c_t / T)(p_s - p_t)
+//                 reverse KL: (c_t / T) p_s (ln p_s - ln p_t - KL_rev)
+//
+// Every reduction is a fixed in-lane order followed by a fixed xor tree, and the columns
+// are merged in one fixed order, so a token's results depend only on its own rows.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace rlk {
+
+namespace {
+
+// One work-group of 4 waves per compacted token row; each 32-lane half of a wave takes one
+// 128-entry column (4 entries per lane), so a wave step covers 2 columns.
+__global__ __launch_bounds__(256) void kl_cross_kernel(KlArgs a, int c0) {
+  const int Na = *a.n_active;
+  const int i = blockIdx.x;
+  if (i >= Na) return;
+  const int vc = min(kBwdChunk, a.V - c0);
+  const int ncol = (vc + 127) / 128;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const float* xs_row = a.xs + (size_t)i * kBwdChunk;
+  const float* xt_row = a.xt + (size_t)i * kBwdChunk;
+  for (int jc = 2 * wave + half; jc < ncol; jc += 8) {
+    const int col = c0 / 128 + jc;
+    const float ms = a.s_max[(size_t)col * a.N + i];
+    const float mt = a.t_max[(size_t)col * a.N + i];
+    const int v0 = jc * 128 + 4 * l32;
+    const f32x4 xs = *reinterpret_cast<const f32x4*>(xs_row + v0);
+    const f32x4 xt = *reinterpret_cast<const f32x4*>(xt_row + v0);
+    const float s4[4] = {xs.x, xs.y, xs.z, xs.w};
+    const float t4[4] = {xt.x, xt.y, xt.z, xt.w};
+    float wf = 0.f, wr = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (v0 + e < vc) {  // entries past the vocabulary hold -inf in both buffers
+        const float d = t4[e] - s4[e];
+        wf = __builtin_fmaf(__builtin_amdgcn_exp2f(t4[e] - mt), d, wf);
+        wr = __builtin_fmaf(__builtin_amdgcn_exp2f(s4[e] - ms), -d, wr);
+      }
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+      wf += __shfl_xor(wf, o);
+      wr += __shfl_xor(wr, o);
+    }
+    if (l32 == 0) {
+      a.wf[(size_t)col * a.N + i] = wf;
+      a.wr[(size_t)col * a.N + i] = wr;
+    }
+  }
+}
+
+// 32 compacted rows per work-group of 256 threads; thread (row = tid & 31, slice = tid >> 5)
+// walks columns slice, slice + 8, ... in ascending order, the 8 slices are added in a fixed
+// tree (the forward merge's association).
+__global__ __launch_bounds__(256) void kl_merge_kernel(KlArgs a) {
+  __shared__ float red[6][8][33];
+  const int Na = *a.n_active;
+  const int r = threadIdx.x & 31;
+  const int sl = threadIdx.x >> 5;
+  const int i = blockIdx.x * 32 + r;
+  const bool ok = i < Na;
+  const int J = (a.V + 127) / 128;
+  float mt = -INFINITY, ms = -INFINITY;
+  if (ok)
+    for (int j = sl; j < J; j += 8) {
+      mt = fmaxf(mt, a.t_max[(size_t)j * a.N + i]);
+      ms = fmaxf(ms, a.s_max[(size_t)j * a.N + i]);
+    }
+  red[0][sl][r] = mt;
+  red[1][sl][r] = ms;
+  __syncthreads();
+  float Mt = red[0][0][r], Ms = red[1][0][r];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) {
+    Mt = fmaxf(Mt, red[0][k][r]);
+    Ms = fmaxf(Ms, red[1][k][r]);
+  }
+  __syncthreads();
+  float st = 0.f, ss = 0.f, af = 0.f, ar = 0.f;
+  if (ok)
+    for (int j = sl; j < J; j += 8) {
+      const size_t o = (size_t)j * a.N + i;
+      const float ft = __builtin_amdgcn_exp2f(a.t_max[o] - Mt);
+      const float fs = __builtin_amdgcn_exp2f(a.s_max[o] - Ms);
+      st += a.t_sum[o] * ft;
+      ss += a.s_sum[o] * fs;
+      af += a.wf[o] * ft;
+      ar += a.wr[o] * fs;
+    }
+  red[2][sl][r] = st;
+  red[3][sl][r] = ss;
+  red[4][sl][r] = af;
+  red[5][sl][r] = ar;
+  __syncthreads();
+  if (sl == 0 && ok) {
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float (*x)[33] = red[2 + q];
+      v[q] = ((x[0][r] + x[1][r]) + (x[2][r] + x[3][r])) + ((x[4][r] + x[5][r]) + (x[6][r] + x[7][r]));
+    }
+    const float lt2 = Mt + __builtin_amdgcn_logf(v[0]);  // lse_t in log2 units
+    const float ls2 = Ms + __builtin_amdgcn_logf(v[1]);
+    const int t = a.idx[i];
+    // KL >= 0; rounding can leave a near-zero divergence a few ulp below it
+    a.kl_fwd[t] = fmaxf((v[2] / v[0] - lt2 + ls2) * kLn2, 0.f);
+    a.kl_rev[t] = fmaxf((v[3] / v[1] - ls2 + lt2) * kLn2, 0.f);
+    if (a.lse_s) a.lse_s[t] = ls2 * kLn2;
+    if (a.lse_t) a.lse_t[t] = lt2 * kLn2;
+  }
+}
+
+// Two floats to packed bf16, round to nearest even.
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// One work-group per row of Gv (rows up to the active count rounded to the tile, the rest
+// exit); each thread forms 4 consecutive entries per step.  Rows past the active count and
+// entries past the vocabulary are written as 0, since the GEMMs that follow read them.
+template <bool kReverse>
+__global__ __launch_bounds__(256) void kl_grad_kernel(KlArgs a, int c0) {
+  const int Na = *a.n_active;
+  const int i = blockIdx.x;
+  const int rows = (Na + 255) / 256 * 256;
+  if (i >= rows) return;
+  const int vc = min(kBwdChunk, a.V - c0);
+  const int vt = (vc + 255) / 256 * 256;  // entries the tiles of the chunk cover
+  const bool act = i < Na;
+  float lse2s = 0.f, lse2t = 0.f, cs = 0.f, klr = 0.f;
+  if (act) {
+    const int t = a.idx[i];
+    lse2s = a.lse_s_in[t] * kLog2e;
+    lse2t = a.lse_t_in[t] * kLog2e;
+    cs = a.coef[t] * a.inv_t;
+    if constexpr (kReverse) klr = a.kl_rev_in[t];
+  }
+  const float* xs_row = a.xs + (size_t)i * kBwdChunk;
+  const float* xt_row = a.xt + (size_t)i * kBwdChunk;
+  uint16_t* g_row = a.Gv + (size_t)i * kBwdChunk;
+  for (int v0 = 4 * threadIdx.x; v0 < vt; v0 += 1024) {
+    float G[4] = {0.f, 0.f, 0.f, 0.f};
+    if (act && v0 < vc) {
+      const f32x4 xs = *reinterpret_cast<const f32x4*>(xs_row + v0);
+      const f32x4 xt = *reinterpret_cast<const f32x4*>(xt_row + v0);
+      const float s4[4] = {xs.x, xs.y, xs.z, xs.w};
+      const float t4[4] = {xt.x, xt.y, xt.z, xt.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (v0 + e < vc) {
+          const float ls = s4[e] - lse2s;  // log2 p_s
+          const float lt = t4[e] - lse2t;
+          const float ps = __builtin_amdgcn_exp2f(ls);
+          if constexpr (kReverse)
+            G[e] = cs * ps * __builtin_fmaf(ls - lt, kLn2, -klr);
+          else
+            G[e] = cs * (ps - __builtin_amdgcn_exp2f(lt));
+        }
+      }
+    }
+    u32x2 pk;
+    pk[0] = pack2(G[0], G[1]);
+    pk[1] = pack2(G[2], G[3]);
+    *reinterpret_cast<u32x2*>(g_row + v0) = pk;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kl_cross(const KlArgs& a, int c0, int rows, hipStream_t stream) {
+  if (rows > 0) hipLaunchKernelGGL(kl_cross_kernel, dim3(rows), dim3(256), 0, stream, a, c0);
+  return hipGetLastError();
+}
+
+hipError_t launch_kl_merge(const KlArgs& a, hipStream_t stream) {
+  const int blocks = (a.N + 31) / 32;
+  if (blocks > 0) hipLaunchKernelGGL(kl_merge_kernel, dim3(blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kl_grad(const KlArgs& a, int c0, int rows, bool reverse, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (reverse)
+    hipLaunchKernelGGL(kl_grad_kernel<true>, dim3(rows), dim3(256), 0, stream, a, c0);
+  else
+    hipLaunchKernelGGL(kl_grad_kernel<false>, dim3(rows), dim3(256), 0, stream, a, c0);
+  return hipGetLastError();
+}
+
+}  // namespace rlk

@@ -200,4 +200,54 @@ inline rlk_status_t check_bwd(const void* h, const void* W, const int32_t* targe
   return RLK_SUCCESS;
 }
 
+// Full-vocabulary KL: one chunk of each head's x, [Npad][chunk] fp32.
+inline size_t kl_chunk_bytes(int64_t N) {
+  return align_up(4 * (size_t)bwd_npad(N) * (size_t)kBwdChunkEntries, 256);
+}
+
+struct KlLayout {
+  size_t idx, n_active, tmax, tsum, smax, ssum, wf, wr, xs, xt, total;
+};
+
+inline KlLayout kl_fwd_layout(int64_t N, int64_t V) {
+  KlLayout L;
+  const size_t n = (size_t)(N > 0 ? N : 1);
+  const size_t jn = 4 * n * (size_t)num_partials(V);
+  size_t o = 0;
+  L.idx = o;      o = align_up(o + 4 * n, 256);
+  L.n_active = o; o = align_up(o + 4, 256);
+  L.tmax = o;     o = align_up(o + jn, 256);
+  L.tsum = o;     o = align_up(o + jn, 256);
+  L.smax = o;     o = align_up(o + jn, 256);
+  L.ssum = o;     o = align_up(o + jn, 256);
+  L.wf = o;       o = align_up(o + jn, 256);
+  L.wr = o;       o = align_up(o + jn, 256);
+  L.xs = o;       o += kl_chunk_bytes(N);
+  L.xt = o;       o += kl_chunk_bytes(N);
+  L.total = o;
+  return L;
+}
+
+// The backward's workspace, then the two chunk buffers.
+inline size_t kl_bwd_bytes(int64_t N, int64_t H) {
+  return bwd_layout(N, H).total + 2 * kl_chunk_bytes(N);
+}
+
+inline rlk_status_t check_kl(const void* hs, const void* Ws, const void* ht, const void* Wt,
+                             const uint8_t* mask, int64_t N, int64_t Hs, int64_t Ht, int64_t V,
+                             int dtype, float T, const void* ws) {
+  rlk_status_t s = check_shape(N, Hs, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  s = check_shape(N, Ht, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  s = check_temperature(T);
+  if (s != RLK_SUCCESS) return s;
+  if (N == 0) return RLK_SUCCESS;
+  if (!hs || !Ws || !ht || !Wt || !mask || !ws) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(hs, 16) || !aligned(Ws, 16) || !aligned(ht, 16) || !aligned(Wt, 16) ||
+      !aligned(ws, 256))
+    return RLK_ERROR_UNSUPPORTED;
+  return RLK_SUCCESS;
+}
+
 }  // namespace rlk

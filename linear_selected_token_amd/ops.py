@@ -369,3 +369,74 @@ def rlk_dlogp_diagnostics(logp_a: torch.Tensor, logp_b: torch.Tensor, mask: torc
                                           ws.numel() * ws.element_size(), _stream(dev)),
             "rlk_dlogp_diagnostics")
     return out, worst
+
+
+# ---- full-vocabulary KL between two LM heads
+
+def _check_kl(h_s, W_s, h_t, W_t, mask):
+    for name, t in (("h_s", h_s), ("W_s", W_s), ("h_t", h_t), ("W_t", W_t), ("mask", mask)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if h_s.dim() != 2 or W_s.dim() != 2 or h_s.shape[1] != W_s.shape[1]:
+        raise ValueError("h_s must be [N, H_s] and W_s [V, H_s]")
+    if h_t.dim() != 2 or W_t.dim() != 2 or h_t.shape[1] != W_t.shape[1]:
+        raise ValueError("h_t must be [N, H_t] and W_t [V, H_t]")
+    if h_t.shape[0] != h_s.shape[0] or W_t.shape[0] != W_s.shape[0]:
+        raise ValueError("student and teacher must share N and V")
+    if len({h_s.dtype, W_s.dtype, h_t.dtype, W_t.dtype}) != 1:
+        raise TypeError("all four operands must share a dtype")
+    if mask.shape != (h_s.shape[0],):
+        raise ValueError("mask must be [N]")
+
+
+def rlk_linear_kl_fwd(h_s, W_s, h_t, W_t, mask, temperature: float,
+                      workspace: Optional[torch.Tensor] = None):
+    """Forward and reverse full-vocabulary KL per token; returns (kl_fwd, kl_rev, lse_s, lse_t),
+    each [N] float32."""
+    mask = _mask_u8(mask)
+    _check_kl(h_s, W_s, h_t, W_t, mask)
+    N, Hs = h_s.shape
+    Ht = h_t.shape[1]
+    V = W_s.shape[0]
+    dt = _dtype_code(h_s)
+    dev = h_s.device
+    outs = [torch.empty(N, dtype=torch.float32, device=dev) for _ in range(4)]
+    nb = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_linear_kl_fwd_workspace_size(N, Hs, Ht, V, dt, ctypes.byref(nb)),
+            "rlk_linear_kl_fwd_workspace_size")
+    ws = _workspace(int(nb.value), dev, workspace)
+    L.check(L.lib().rlk_linear_kl_fwd(_vp(h_s), _vp(W_s), _vp(h_t), _vp(W_t), _vp(mask), N, Hs,
+                                      Ht, V, dt, float(temperature), *(_vp(o) for o in outs),
+                                      _vp(ws), ws.numel() * ws.element_size(), _stream(dev)),
+            "rlk_linear_kl_fwd")
+    return tuple(outs)
+
+
+def rlk_linear_kl_bwd(h_s, W_s, h_t, W_t, mask, temperature: float, reverse: bool,
+                      coef: torch.Tensor, lse_s: torch.Tensor, lse_t: torch.Tensor,
+                      kl_rev: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None):
+    """Gradients of L = sum_t mask_t coef_t KL[t] into the student; returns (dh_s, dW_s)."""
+    mask = _mask_u8(mask)
+    _check_kl(h_s, W_s, h_t, W_t, mask)
+    N, Hs = h_s.shape
+    Ht = h_t.shape[1]
+    V = W_s.shape[0]
+    dt = _dtype_code(h_s)
+    dev = h_s.device
+    for name, t in (("coef", coef), ("lse_s", lse_s), ("lse_t", lse_t)) + (
+            (("kl_rev", kl_rev),) if reverse else ()):
+        _vec(name, t, N)
+    dh = torch.empty((N, Hs), dtype=torch.float32, device=dev)
+    dW = torch.empty((V, Hs), dtype=torch.float32, device=dev)
+    nb = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_linear_kl_bwd_workspace_size(N, Hs, Ht, V, dt, ctypes.byref(nb)),
+            "rlk_linear_kl_bwd_workspace_size")
+    ws = _workspace(int(nb.value), dev, workspace)
+    L.check(L.lib().rlk_linear_kl_bwd(_vp(h_s), _vp(W_s), _vp(h_t), _vp(W_t), _vp(mask), N, Hs,
+                                      Ht, V, dt, float(temperature), int(bool(reverse)),
+                                      _vp(coef), _vp(lse_s), _vp(lse_t), _vp(kl_rev), _vp(dh),
+                                      _vp(dW), _vp(ws), ws.numel() * ws.element_size(),
+                                      _stream(dev)),
+            "rlk_linear_kl_bwd")
+    return dh, dW

@@ -283,3 +283,37 @@ def test_loss_fragment_argument_errors(L):
     assert diag(wsb=100) == E.RLK_ERROR_WORKSPACE
     st, b2 = _ws(lib, "rlk_dlogp_diagnostics_workspace_size", 1 << 20)
     assert st == 0 and b2 >= 12 * (1 << 20)
+
+
+def test_kl_argument_errors(L):
+    # every case is decided on the host, before anything could be launched
+    lib = L.lib()
+    E = L
+
+    def fwd(N=8, Hs=64, Ht=128, V=1000, dt=0, T=1.0, hs=FAKE, ht=FAKE, kf=FAKE, wsb=1 << 40):
+        return lib.rlk_linear_kl_fwd(hs, FAKE, ht, FAKE, FAKE, N, Hs, Ht, V, dt, T, kf, FAKE, None,
+                                     None, FAKE, wsb, None)
+
+    assert fwd(N=0) == E.RLK_SUCCESS
+    assert fwd(hs=None) == E.RLK_ERROR_INVALID_VALUE
+    assert fwd(ht=None) == E.RLK_ERROR_INVALID_VALUE
+    assert fwd(kf=None) == E.RLK_ERROR_INVALID_VALUE
+    assert fwd(Ht=96) == E.RLK_ERROR_UNSUPPORTED
+    assert fwd(ht=FAKE + 8) == E.RLK_ERROR_UNSUPPORTED
+    assert fwd(T=0.0) == E.RLK_ERROR_INVALID_VALUE
+    assert fwd(wsb=1000) == E.RLK_ERROR_WORKSPACE
+    st, b = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 16384, 4096, 2048, 151936, 0)
+    # six [J][N] statistics plus two fp32 chunks of [N rounded to 256] x 32768
+    assert st == 0 and b >= 6 * 4 * 16384 * 1187 + 2 * 4 * 16384 * 32768
+
+    def bwd(Hs=256, dt=0, rev=0, kr=FAKE, coef=FAKE, wsb=1 << 40):
+        return lib.rlk_linear_kl_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 8, Hs, 64, 1000, dt, 1.0, rev,
+                                     coef, FAKE, FAKE, kr, FAKE, FAKE, FAKE, wsb, None)
+
+    assert bwd(Hs=64) == E.RLK_ERROR_UNSUPPORTED
+    assert bwd(dt=1) == E.RLK_ERROR_UNSUPPORTED
+    assert bwd(coef=None) == E.RLK_ERROR_INVALID_VALUE
+    assert bwd(rev=1, kr=None) == E.RLK_ERROR_INVALID_VALUE
+    assert bwd(wsb=1000) == E.RLK_ERROR_WORKSPACE
+    assert _ws(lib, "rlk_linear_kl_bwd_workspace_size", 8, 64, 64, 1000, 0)[0] == \
+        E.RLK_ERROR_UNSUPPORTED

@@ -1,0 +1,197 @@
+"""Full-vocabulary KL between a student and a teacher head against the float64 oracle (needs
+an MI355X).
+
+Gates: |dKL| <= 1e-3 in both directions (KL is a difference of log-sum-exps and a
+probability-weighted mean of logits, each within the logp gate's reach of per-logit error),
+each head's lse as for the plain forward; a token's results bit-identical in any batch;
+identical heads give exactly 0.  Backward: rel-L2 of dh_s and dW_s <= 1e-2 for both
+directions."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.distill as od
+import workloads as wl
+from gpu_util import (GRAD_REL_L2, MAX_ABS_DLOGP, bits, device, flush, rel_l2, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _teacher(w, Ht, seed, close=None):
+    """Teacher hidden states and head for workload w: independent draws, or (close = eps) the
+    student's own head with N(0, eps^2 / H) added to W."""
+    if close is not None:
+        Wt = wl.bf16_to_f32(w.W) + wl.normal_rows(seed, 97, 0, w.V, w.H, close / np.sqrt(w.H),
+                                                  "fp32")
+        return w.h.copy(), (wl.bf16_bits(Wt) if w.dtype == "bf16" else Wt)
+    ht = wl.normal_rows(seed, 96, 0, w.N, Ht, 1.0, w.dtype)
+    return ht, wl.weight_matrix(seed + 7, w.V, Ht, w.dtype)
+
+
+def _dev(x):
+    dev = device()
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def _fwd(w, ht, Wt, mask=None):
+    import linear_selected_token_amd as rlk
+    m = w.mask if mask is None else mask
+    out = rlk.rlk_linear_kl_fwd(_dev(w.h), _dev(w.W), _dev(ht), _dev(Wt), _dev(m), w.T)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in out]
+
+
+def _lse(h64, W64, T, rows):
+    z = oracle.logits(h64[rows], W64, T)
+    return oracle.logsumexp_rows(z)
+
+
+def _check_fwd(w, ht, Wt, rows=None, tol=MAX_ABS_DLOGP):
+    kf, kr, ls, lt = _fwd(w, ht, Wt)
+    hs64, Ws64, ht64, Wt64 = (wl.as_f64(x) for x in (w.h, w.W, ht, Wt))
+    act = w.mask.astype(bool)
+    if rows is None:
+        of, orv = od.kl_divergences(hs64, Ws64, ht64, Wt64, w.mask, w.T)
+        rows = np.nonzero(act)[0]
+        assert not kf[~act].any() and not kr[~act].any() and not ls[~act].any()
+        of, orv = of[rows], orv[rows]
+    else:
+        of, orv = od.kl_divergences(hs64[rows], Ws64, ht64[rows], Wt64,
+                                    np.ones(rows.size, np.uint8), w.T)
+    ef = np.abs(kf[rows] - of).max()
+    er = np.abs(kr[rows] - orv).max()
+    els = np.abs(ls[rows] - _lse(hs64, Ws64, w.T, rows)).max()
+    elt = np.abs(lt[rows] - _lse(ht64, Wt64, w.T, rows)).max()
+    flush(f"  KL {w.dtype} N={w.N} Hs={w.H} Ht={ht.shape[1]} V={w.V}: KL_fwd~{of.mean():.3g} "
+          f"max|d|={ef:.2e}  KL_rev~{orv.mean():.3g} max|d|={er:.2e}  lse {els:.1e}/{elt:.1e} "
+          f"over {rows.size} tokens")
+    assert ef <= tol and er <= tol and els <= tol and elt <= tol
+    return kf, kr, ls, lt
+
+
+SMALL = wl.scaled_spec(2, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300, seed=111,
+                       T=0.8)
+
+
+def test_small_full_independent_heads():
+    w = wl.make(SMALL)
+    ht, Wt = _teacher(w, 256, 112)
+    _check_fwd(w, ht, Wt)
+
+
+def test_small_full_close_heads():
+    # a teacher near the student: small divergences, where the cancellation matters most
+    w = wl.make(SMALL)
+    ht, Wt = _teacher(w, w.H, 113, close=0.05)
+    kf, kr, _, _ = _check_fwd(w, ht, Wt, tol=2e-5)
+    act = w.mask.astype(bool)
+    assert (kf[act] < 0.05).all()
+
+
+def test_fp32_ragged_and_two_chunks():
+    w = wl.make(wl.scaled_spec(1, N=200, H=128, V=777, n_seq=2, len_lo=50, len_hi=150,
+                               prompt="floor_half", seed=114, T=1.2))
+    ht, Wt = _teacher(w, 64, 115)
+    _check_fwd(w, ht, Wt, tol=1e-4)
+    # two vocabulary chunks, the second ragged
+    w2 = wl.make(wl.scaled_spec(2, N=260, H=256, V=32768 + 300, n_seq=2, len_lo=100,
+                                len_hi=200, seed=116))
+    ht2, Wt2 = _teacher(w2, 192, 117)
+    _check_fwd(w2, ht2, Wt2)
+
+
+def test_identical_heads_and_invariance():
+    w = wl.make(SMALL)
+    kf, kr, ls, lt = _fwd(w, w.h, w.W)
+    act = w.mask.astype(bool)
+    assert not kf.any() and not kr.any()
+    assert np.array_equal(bits(ls), bits(lt))
+    # a reversed subset of the tokens in a batch of its own, some masked
+    ht, Wt = _teacher(w, 320, 118)
+    full = _fwd(w, ht, Wt)
+    sel = np.nonzero(act)[0][::-3].copy()
+    import dataclasses
+    sub = dataclasses.replace(w, h=np.ascontiguousarray(w.h[sel]), targets=w.targets[sel],
+                              mask=w.mask[sel].copy(), adv=w.adv[sel], u=w.u[sel],
+                              seq_id=w.seq_id[sel], pos=w.pos[sel])
+    sub.mask[::4] = 0
+    part = _fwd(sub, np.ascontiguousarray(ht[sel]), Wt)
+    keep = sub.mask.astype(bool)
+    mism = sum(int((bits(p[keep]) != bits(f[sel][keep])).sum()) for p, f in zip(part, full))
+    flush(f"  KL invariance: {mism} mismatches over {int(keep.sum())} tokens x 4 outputs")
+    assert mism == 0
+
+
+def test_qwen_head_sampled():
+    # the Qwen3-8B student head (H=4096, V=151936) against a smaller teacher (H=2048)
+    w = wl.make(wl.scaled_spec(2, N=512, n_seq=2, len_lo=200, len_hi=300, seed=119, T=0.7))
+    ht, Wt = _teacher(w, 2048, 120)
+    _check_fwd(w, ht, Wt, rows=sample_rows(w, 16, seed=121))
+
+
+# ------------------------------------------------------------------ backward
+
+def _bwd(w, ht, Wt, reverse, coef):
+    import linear_selected_token_amd as rlk
+    d = [_dev(x) for x in (w.h, w.W, ht, Wt, w.mask)]
+    kf, kr, ls, lt = rlk.rlk_linear_kl_fwd(*d, w.T)
+    dh, dW = rlk.rlk_linear_kl_bwd(*d, w.T, reverse, _dev(coef), ls, lt, kr)
+    torch.cuda.synchronize()
+    return dh.cpu().numpy(), dW.cpu().numpy()
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_bwd_small_full(reverse):
+    w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
+                               seed=122, T=0.9))
+    ht, Wt = _teacher(w, 256, 123)
+    c = np.random.default_rng(124).uniform(0.5, 1.5, w.N).astype(np.float32)
+    dh, dW = _bwd(w, ht, Wt, reverse, c)
+    odh, odW = od.kl_grads(*(wl.as_f64(x) for x in (w.h, w.W, ht, Wt)), w.mask, w.T, c, reverse)
+    eh, ew = rel_l2(dh, odh), rel_l2(dW, odW)
+    flush(f"  KL bwd reverse={reverse}: relL2(dh)={eh:.3e} relL2(dW)={ew:.3e}")
+    assert eh <= GRAD_REL_L2 and ew <= GRAD_REL_L2
+    assert not dh[w.mask == 0].any()
+
+
+def test_bwd_two_chunks_and_dh_invariance():
+    w = wl.make(wl.scaled_spec(5, N=260, H=256, V=32768 + 16384 + 300, n_seq=2, len_lo=100,
+                               len_hi=200, seed=125))
+    ht, Wt = _teacher(w, 128, 126)
+    c = np.random.default_rng(127).uniform(0.5, 1.5, w.N).astype(np.float32)
+    dh, dW = _bwd(w, ht, Wt, False, c)
+    odh, odW = od.kl_grads(*(wl.as_f64(x) for x in (w.h, w.W, ht, Wt)), w.mask, w.T, c, False)
+    eh, ew = rel_l2(dh, odh), rel_l2(dW, odW)
+    flush(f"  KL bwd two chunks: relL2(dh)={eh:.3e} relL2(dW)={ew:.3e}")
+    assert eh <= GRAD_REL_L2 and ew <= GRAD_REL_L2
+    # the first 100 tokens alone give the same dh rows, bit for bit
+    import dataclasses
+    k = 100
+    sub = dataclasses.replace(w, h=np.ascontiguousarray(w.h[:k]), targets=w.targets[:k],
+                              mask=w.mask[:k].copy(), adv=w.adv[:k], u=w.u[:k],
+                              seq_id=w.seq_id[:k], pos=w.pos[:k])
+    dh2, _ = _bwd(sub, np.ascontiguousarray(ht[:k]), Wt, False, c[:k])
+    act = sub.mask.astype(bool)
+    assert np.array_equal(bits(dh2[act]), bits(dh[:k][act]))
+
+
+def test_bwd_qwen_head_sampled():
+    w = wl.make(wl.scaled_spec(5, N=512, n_seq=2, len_lo=200, len_hi=300, seed=128, T=0.7))
+    ht, Wt = _teacher(w, 1024, 129)
+    c = np.full(w.N, 1.0 / 256, np.float32)
+    dh, dW = _bwd(w, ht, Wt, True, c)
+    hs64, Ws64, ht64, Wt64 = (wl.as_f64(x) for x in (w.h, w.W, ht, Wt))
+    rows = sample_rows(w, 12, seed=130)
+    odh = od.kl_grad_h_rows(hs64, Ws64, ht64, Wt64, w.mask, w.T, c, True, rows)
+    eh = rel_l2(dh[rows], odh)
+    act = np.nonzero(w.mask)[0]
+    vr = np.unique(np.concatenate([np.random.default_rng(131).integers(0, w.V, 20),
+                                   [0, w.V - 1]]))
+    odW = od.kl_grad_W_rows(hs64, Ws64, ht64, Wt64, w.mask, w.T, c, True, vr)
+    ew = rel_l2(dW[vr], odW)
+    flush(f"  KL bwd qwen head (reverse): relL2(dh)={eh:.3e} over {rows.size} rows, "
+          f"relL2(dW)={ew:.3e} over {vr.size} vocabulary rows ({act.size} active tokens)")
+    assert eh <= GRAD_REL_L2 and ew <= GRAD_REL_L2
