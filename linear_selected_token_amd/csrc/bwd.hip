@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
           u32x2 pk;
           pk[0] = pack_bf16(G[0], G[1]);
           pk[1] = pack_bf16(G[2], G[3]);
-          *reinterpret_cast<u32x2*>(a.Gv + (size_t)ti * kBwdChunk + vl) = pk;
+          *reinterpret_cast<u32x2*>(a.Gv + (size_t)ti * kGvPitch + vl) = pk;
           // one group of 4 rows at a time: keeps the live ranges short (no spills)
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
   const int band = nHTiles < 8 ? nHTiles : 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const size_t row_bytes = (size_t)kBwdChunk * 2;
+  const size_t row_bytes = (size_t)kGvPitch * 2;
   const uint32_t w_pitch = (uint32_t)a.H * 2;  // bytes per W row
   const int wa = wave_a0(wave);
   const int wb = wave_b0(wave);
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const size_t row_bytes = (size_t)a.Npad * 2;         // hT rows
-  const uint32_t g_pitch = (uint32_t)kBwdChunk * 2;   // Gv rows (one token each)
+  const uint32_t g_pitch = (uint32_t)kGvPitch * 2;   // Gv rows (one token each)
   const int nk = ((Na + 63) & ~63) * 2 / kKBytes;
   const int wa = wave_a0(wave);
   const int wb = wave_b0(wave);

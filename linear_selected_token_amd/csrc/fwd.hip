@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
       if constexpr (kMode == kFwdStoreX) {
         // x of every entry (tail entries hold -inf), four consecutive entries per store
         if (ti < Na) {
-          float* xrow = a.xbuf + (size_t)ti * kBwdChunk + vq;
+          float* xrow = a.xbuf + (size_t)ti * kXPitch + vq;
 #pragma unroll
           for (int i = 0; i < kBlkA; ++i)
 #pragma unroll

@@ -9,6 +9,10 @@ namespace rlk {
 constexpr int kVocabPartial = 128;  // vocabulary entries per partial-statistics column
 constexpr int kBwdChunk = 32768;    // vocabulary entries per backward chunk (build constant)
 constexpr int kDhSplitK = 16384;    // dL/dh sums each chunk's first and second 16384 entries apart
+// Row pitch (entries) of the token-major chunk buffers: the chunk plus 128 bytes, so that the
+// rows a wave writes at once (32 tokens) do not all start at the same 64 KiB-aligned offset.
+constexpr int kGvPitch = kBwdChunk + 64;  // bf16 dL/dz
+constexpr int kXPitch = kBwdChunk + 32;   // fp32 x of the KL path
 
 struct CompactArgs {
   const uint8_t* mask;
@@ -35,7 +39,7 @@ struct FwdTileArgs {
   float* target_logit;
   int vstart;  // global vocabulary index of W row 0 (a multiple of kVocabPartial)
   float* part_w = nullptr;  // [J][N] entropy statistic per column (kFwdEntropy)
-  float* xbuf = nullptr;    // [Npad][kBwdChunk] x = z log2 e of one vocabulary chunk (kFwdStoreX)
+  float* xbuf = nullptr;    // [Npad][kXPitch] x = z log2 e of one vocabulary chunk (kFwdStoreX)
 };
 
 enum FwdMode { kFwdPlain = 0, kFwdEntropy = 1, kFwdStoreX = 2 };
@@ -79,7 +83,7 @@ struct BwdArgs {
   float* dh;              // [N, H]
   float* dW;              // [V, H]
   uint16_t* hT;           // [H, Npad]   compacted h, transposed, zero past Na
-  uint16_t* Gv;           // [Npad, kBwdChunk] dL/dz of the chunk, token-major
+  uint16_t* Gv;           // [Npad, kGvPitch] dL/dz of the chunk, token-major
   float* dh1;             // [Npad, H] dL/dh from the second half of every chunk, compacted rows
   // entropy bonus (both null without it): L gains -sum_t mask_t c_t H_t
   const float* ent_coef = nullptr;  // [N] c_t
@@ -127,7 +131,7 @@ struct KlArgs {
   const int32_t* n_active;
   int N, V;
   float inv_t;
-  const float* xs;     // [Npad][kBwdChunk] student x of the current chunk
+  const float* xs;     // [Npad][kXPitch] student x of the current chunk
   const float* xt;     // teacher
   const float* s_max;  // [J][N] column statistics
   const float* s_sum;
@@ -144,7 +148,7 @@ struct KlArgs {
   const float* lse_t_in;
   const float* kl_rev_in;  // reverse KL only
   const float* coef;       // [N] c_t
-  uint16_t* Gv;            // [Npad][kBwdChunk]
+  uint16_t* Gv;            // [Npad][kGvPitch]
 };
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);

@@ -42,8 +42,8 @@ __global__ __launch_bounds__(256) void kl_cross_kernel(KlArgs a, int c0) {
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const float* xs_row = a.xs + (size_t)i * kBwdChunk;
-  const float* xt_row = a.xt + (size_t)i * kBwdChunk;
+  const float* xs_row = a.xs + (size_t)i * kXPitch;
+  const float* xt_row = a.xt + (size_t)i * kXPitch;
   for (int jc = 2 * wave + half; jc < ncol; jc += 8) {
     const int col = c0 / 128 + jc;
     const float ms = a.s_max[(size_t)col * a.N + i];
@@ -161,9 +161,9 @@ __global__ __launch_bounds__(256) void kl_grad_kernel(KlArgs a, int c0) {
     cs = a.coef[t] * a.inv_t;
     if constexpr (kReverse) klr = a.kl_rev_in[t];
   }
-  const float* xs_row = a.xs + (size_t)i * kBwdChunk;
-  const float* xt_row = a.xt + (size_t)i * kBwdChunk;
-  uint16_t* g_row = a.Gv + (size_t)i * kBwdChunk;
+  const float* xs_row = a.xs + (size_t)i * kXPitch;
+  const float* xt_row = a.xt + (size_t)i * kXPitch;
+  uint16_t* g_row = a.Gv + (size_t)i * kGvPitch;
   for (int v0 = 4 * threadIdx.x; v0 < vt; v0 += 1024) {
     float G[4] = {0.f, 0.f, 0.f, 0.f};
     if (act && v0 < vc) {

@@ -120,7 +120,7 @@ inline BwdLayout bwd_layout(int64_t N, int64_t H) {
   L.idx = o;      o = align_up(o + 4 * n, 256);
   L.n_active = o; o = align_up(o + 4, 256);
   L.hT = o;       o = align_up(o + 2 * (size_t)H * np, 256);
-  L.Gv = o;       o = align_up(o + 2 * np * c, 256);
+  L.Gv = o;       o = align_up(o + 2 * np * (c + 64), 256);  // rows of kGvPitch entries
   L.dh1 = o;      o = align_up(o + 4 * np * (size_t)H, 256);
   L.total = o;
   return L;
@@ -202,7 +202,7 @@ inline rlk_status_t check_bwd(const void* h, const void* W, const int32_t* targe
 
 // Full-vocabulary KL: one chunk of each head's x, [Npad][chunk] fp32.
 inline size_t kl_chunk_bytes(int64_t N) {
-  return align_up(4 * (size_t)bwd_npad(N) * (size_t)kBwdChunkEntries, 256);
+  return align_up(4 * (size_t)bwd_npad(N) * (size_t)(kBwdChunkEntries + 32), 256);  // kXPitch
 }
 
 struct KlLayout {
