@@ -266,3 +266,20 @@ def test_bwd_full_size_sampled():
     colsum = dW.double().sum(0).abs().max().item()
     scale = dW.double().abs().sum(0).max().item()
     assert colsum <= 1e-3 * scale
+
+
+def test_empty_and_all_masked():
+    import linear_selected_token_amd as rlk
+    w = wl.make(SPECS[1])
+    d = upload(w)
+    d["mask"].zero_()
+    lp, lse, ent = rlk.rlk_linear_logp_fwd_entropy(d["h"], d["W"], d["targets"], d["mask"], w.T)
+    c = torch.ones(w.N, dtype=torch.float32, device=d["h"].device)
+    dh, dW = rlk.rlk_linear_logp_bwd_entropy(d["h"], d["W"], d["targets"], d["mask"], w.T,
+                                             d["adv"], c, lse, ent)
+    torch.cuda.synchronize()
+    assert not lp.any() and not lse.any() and not ent.any() and not dh.any() and not dW.any()
+    e = d["h"][:0]
+    lp0, _, ent0 = rlk.rlk_linear_logp_fwd_entropy(e, d["W"], d["targets"][:0], d["mask"][:0],
+                                                   1.0)
+    assert lp0.numel() == 0 and ent0.numel() == 0

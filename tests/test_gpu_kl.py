@@ -195,3 +195,27 @@ def test_bwd_qwen_head_sampled():
     flush(f"  KL bwd qwen head (reverse): relL2(dh)={eh:.3e} over {rows.size} rows, "
           f"relL2(dW)={ew:.3e} over {vr.size} vocabulary rows ({act.size} active tokens)")
     assert eh <= GRAD_REL_L2 and ew <= GRAD_REL_L2
+
+
+def test_empty_and_all_masked():
+    import linear_selected_token_amd as rlk
+    w = wl.make(SMALL)
+    ht, Wt = _teacher(w, 256, 132)
+    # all tokens masked: every output is 0, dW_s is 0
+    m0 = np.zeros(w.N, np.uint8)
+    outs = _fwd(w, ht, Wt, mask=m0)
+    assert not any(o.any() for o in outs)
+    d = [_dev(x) for x in (w.h, w.W, ht, Wt)]
+    z = torch.zeros(w.N, dtype=torch.float32, device=d[0].device)
+    dh, dW = rlk.rlk_linear_kl_bwd(*d, _dev(m0), w.T, False, z + 1, z, z)
+    torch.cuda.synchronize()
+    assert not dh.any() and not dW.any()
+    # no tokens at all
+    e = [x[:0] for x in d[:1]] + [d[1]] + [d[2][:0], d[3]]
+    em = torch.zeros(0, dtype=torch.uint8, device=d[0].device)
+    out0 = rlk.rlk_linear_kl_fwd(e[0], e[1], e[2], e[3], em, 1.0)
+    assert all(o.numel() == 0 for o in out0)
+    z0 = torch.zeros(0, dtype=torch.float32, device=d[0].device)
+    dh0, dW0 = rlk.rlk_linear_kl_bwd(e[0], e[1], e[2], e[3], em, 1.0, True, z0, z0, z0, z0)
+    torch.cuda.synchronize()
+    assert dh0.numel() == 0 and not dW0.any()
