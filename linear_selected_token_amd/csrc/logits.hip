@@ -8,8 +8,9 @@
 // / T applied once, followed by the fused forward's fixed-order merge.  The kernel is a pure
 // HBM stream: one work-group of 4 waves per active token row keeps its row's column
 // statistics in LDS (8 bytes per column) and merges them itself; each wave step reads
-// 4 KiB of the row (four 16-byte loads per lane), i.e. 16 bf16 columns (4 lanes each) or 8
-// fp32 columns (8 lanes each).  Every reduction is a fixed in-lane order followed by a fixed
+// 4 KiB of the row (four 16-byte loads per lane), i.e. 16 bf16 columns (16 lanes each) or 8
+// fp32 columns (32 lanes each), and the next step's loads are issued before the current step
+// is reduced.  Every reduction is a fixed in-lane order followed by a fixed
 // xor tree, so a row's results depend only on that row.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -48,53 +49,54 @@ __global__ __launch_bounds__(256) void logits_logp_kernel(LogitsArgs a) {
   float* cmax = col_stats;
   float* csum = col_stats + J;
 
-  // 1. Column statistics.  Wave w takes column blocks w, w + 4, ... of kCols columns each.
-  for (int jb = wave * kCols; jb < J; jb += 4 * kCols * kUnroll) {
-    float x[kUnroll][kPer];
+  // 1. Column statistics.  Wave w takes column blocks w, w + 4, ... of kCols columns each;
+  // the raw 16-byte loads of the next kUnroll blocks are in flight while the current ones are
+  // reduced (two register buffers).
+  constexpr int kStep = 4 * kCols * kUnroll;  // columns per work-group iteration
+  auto load = [&](int jb, u32x4 (&raw)[kUnroll]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int j = jb + u * 4 * kCols + lane / kGroup;
       const int v0 = j * 128 + (lane % kGroup) * kPer;
-      if (j < J && v0 < a.V) {
-        // v0 and ld are multiples of kPer, so the 16 bytes stay inside the row's ld entries
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(row + (size_t)v0 * esize);
-        if constexpr (kBF16) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[u][2 * e] = __builtin_bit_cast(float, raw[e] << 16);
-            x[u][2 * e + 1] = __builtin_bit_cast(float, raw[e] & 0xffff0000u);
-          }
-        } else {
-          // cast the whole vector: a bit_cast of one vector element is lowered to element 0
-          const f32x4 f = __builtin_bit_cast(f32x4, raw);
-          x[u][0] = f.x;
-          x[u][1] = f.y;
-          x[u][2] = f.z;
-          x[u][3] = f.w;
-        }
-        if (v0 + kPer > a.V) {  // the vocabulary tail
-#pragma unroll
-          for (int e = 0; e < kPer; ++e)
-            if (v0 + e >= a.V) x[u][e] = -INFINITY;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) x[u][e] = -INFINITY;
-      }
+      // v0 and ld are multiples of kPer, so the 16 bytes stay inside the row's ld entries
+      raw[u] = (j < J && v0 < a.V) ? *reinterpret_cast<const u32x4*>(row + (size_t)v0 * esize)
+                                   : u32x4{0u, 0u, 0u, 0u};
     }
+  };
+  auto reduce = [&](int jb, const u32x4 (&raw)[kUnroll]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int j = jb + u * 4 * kCols + lane / kGroup;
-      // column maximum on the raw logits (c2 > 0, rounding monotonic), in log2 units
-      float m = x[u][0];
+      const int v0 = j * 128 + (lane % kGroup) * kPer;
+      float x[kPer];
+      if constexpr (kBF16) {
 #pragma unroll
-      for (int e = 1; e < kPer; ++e) m = fmaxf(m, x[u][e]);
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = __builtin_bit_cast(float, raw[u][e] << 16);
+          x[2 * e + 1] = __builtin_bit_cast(float, raw[u][e] & 0xffff0000u);
+        }
+      } else {
+        // cast the whole vector: a bit_cast of one vector element is lowered to element 0
+        const f32x4 f = __builtin_bit_cast(f32x4, raw[u]);
+        x[0] = f.x;
+        x[1] = f.y;
+        x[2] = f.z;
+        x[3] = f.w;
+      }
+      // entries past the vocabulary (and lanes past the last column) count as -inf
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (j >= J || v0 + e >= a.V) x[e] = -INFINITY;
+      // column maximum on the raw logits (c2 > 0, rounding monotonic), in log2 units
+      float m = x[0];
+#pragma unroll
+      for (int e = 1; e < kPer; ++e) m = fmaxf(m, x[e]);
 #pragma unroll
       for (int o = kGroup / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
       const float mx = m * c2;
       float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) s += __builtin_amdgcn_exp2f(__builtin_fmaf(x[u][e], c2, -mx));
+      for (int e = 0; e < kPer; ++e) s += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, -mx));
 #pragma unroll
       for (int o = kGroup / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
       if (lane % kGroup == 0 && j < J) {
@@ -102,6 +104,18 @@ __global__ __launch_bounds__(256) void logits_logp_kernel(LogitsArgs a) {
         csum[j] = s;
       }
     }
+  };
+  u32x4 r0[kUnroll], r1[kUnroll];
+  int jb = wave * kCols;
+  load(jb, r0);
+  while (jb < J) {
+    load(jb + kStep, r1);
+    reduce(jb, r0);
+    jb += kStep;
+    if (jb >= J) break;
+    load(jb + kStep, r0);
+    reduce(jb, r1);
+    jb += kStep;
   }
   __syncthreads();
 
