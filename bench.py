@@ -490,6 +490,7 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms = total_ms / args.steps
+    step_ms = [e[0].elapsed_time(e[4]) for e in evs]
     tile_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     fwd_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
     bwd_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs])) if do_bwd else 0.0
@@ -509,6 +510,8 @@ def main():
         "unit": "active tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms_median": round(float(np.median(step_ms)), 4),
+        "step_ms_min": round(float(np.min(step_ms)), 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic: seeded h~N(0,1), W~N(0,1/H) rounded to bf16, packed "
@@ -525,8 +528,12 @@ def main():
                       "tflops_executed": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
                       "mfma_frac": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         out["fwd_bwd_tflops_executed"] = round((fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12, 2)
+        # without the recompute the step would need 6 H V flops per active token
+        out["fwd_bwd_tflops_no_recompute_basis"] = round(
+            6.0 * Na * H * V / (ms * 1e-3) / 1e12, 2)
     if args.cpu_baseline_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.mode, args.cpu_baseline_seconds)
+        out["gpu_over_cpu_baseline"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
