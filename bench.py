@@ -52,12 +52,14 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     p.add_argument("--mode", default="fwdbwd",
-                   choices=["fwd", "fwdbwd", "entropy", "ppo", "kl", "logits"],
+                   choices=["fwd", "fwdbwd", "entropy", "ppo", "kl", "logits", "gemm-reference"],
                    help="fwdbwd: the fused forward and backward (the headline); fwd: forward "
                         "only; entropy: a step with an entropy bonus (the entropy forward and "
                         "its backward); ppo: forward, clipped policy-gradient loss with a KL "
                         "penalty, backward, plus the dlogp diagnostics; kl: full-vocabulary KL "
-                        "to a teacher head of the same shape, forward and backward; logits: log-prob from existing "
+                        "to a teacher head of the same shape, forward and backward; gemm-reference: "
+                        "the vendor library's plain bf16 GEMM of the forward's shape (it writes "
+                        "the logits), as a reference point for the tile kernel; logits: log-prob from existing "
                         "bf16 logits of the same shape (an HBM-bound path, reported against "
                         "HBM bandwidth)")
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
@@ -421,6 +423,48 @@ def bench_kl(args, w):
     print(json.dumps(out), flush=True)
 
 
+def bench_gemm_reference(args, w):
+    """The library GEMM (torch.matmul, hipBLASLt on ROCm) of the tile kernel's shape: the
+    active tokens' h [Na, H] times W^T [H, V] into bf16 logits [Na, V].  It does none of the
+    softmax work and writes the logits the fused path never forms; a reference point for
+    what the matrix cores sustain on this shape."""
+    import torch
+    dev = torch.device("cuda", 0)
+    N, H, V, Na = w.N, w.H, w.V, w.n_active
+    h, W, _, mask, _ = upload(w, dev)
+    ha = h[torch.from_numpy(np.nonzero(w.mask)[0]).to(dev)].contiguous()
+    out = torch.empty((Na, V), dtype=h.dtype, device=dev)
+    Wt = W.t()
+
+    for _ in range(args.warmup):
+        torch.matmul(ha, Wt, out=out)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record()
+        torch.matmul(ha, Wt, out=out)
+        e1.record()
+    torch.cuda.synchronize()
+    ts = [e0.elapsed_time(e1) for e0, e1 in evs]
+    ms = float(np.mean(ts))
+    flop = 2.0 * Na * H * V
+    tf = flop / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "TFLOP/s, library bf16 GEMM of the forward tile kernel's shape (reference)",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "step_ms_min": round(float(np.min(ts)), 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "mode": "gemm-reference", "M": Na, "K": H,
+                   "N": V, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "library GEMM (torch.matmul)",
+                     "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flop_per_launch": flop, "avg_launch_ms": round(ms, 4)},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -446,6 +490,9 @@ def main():
         return
     if args.mode == "kl":
         bench_kl(args, w)
+        return
+    if args.mode == "gemm-reference":
+        bench_gemm_reference(args, w)
         return
     N, H, V, T = w.N, w.H, w.V, w.T
     Na = w.n_active
