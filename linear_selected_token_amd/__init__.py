@@ -9,11 +9,15 @@ lib()  # fail loudly at import when the library is missing
 from .ops import (  # noqa: E402,F401
     DIAG_FIELDS,
     ForwardBuffers,
+    LinearKL,
     LinearLogp,
+    LinearLogpEntropy,
     bwd_workspace_bytes,
     fwd_entropy_workspace_bytes,
     fwd_workspace_bytes,
+    linear_kl,
     linear_logp,
+    linear_logp_entropy,
     logits_workspace_bytes,
     num_vocab_partials,
     rlk_compact_active,

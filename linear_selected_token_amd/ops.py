@@ -306,6 +306,37 @@ def linear_logp(h, W, targets, mask, temperature) -> torch.Tensor:
     return LinearLogp.apply(h, W, targets, mask, temperature)
 
 
+class LinearLogpEntropy(torch.autograd.Function):
+    """(logp, entropy) = linear_logp_entropy(h, W, targets, mask, T); backward through
+    rlk_linear_logp_bwd_entropy with adv = -dL/dlogp and ent_coef = -dL/dentropy (through
+    rlk_linear_logp_bwd when no gradient reaches the entropy)."""
+
+    @staticmethod
+    def forward(ctx, h, W, targets, mask, temperature):
+        logp, lse, ent = rlk_linear_logp_fwd_entropy(h, W, targets, mask, temperature)
+        ctx.save_for_backward(h, W, targets, mask, lse, ent)
+        ctx.temperature = float(temperature)
+        return logp, ent
+
+    @staticmethod
+    def backward(ctx, grad_logp, grad_ent):
+        h, W, targets, mask, lse, ent = ctx.saved_tensors
+        adv = (torch.zeros_like(lse) if grad_logp is None else
+               (-grad_logp).to(torch.float32).contiguous())
+        if grad_ent is None:
+            dh, dW = rlk_linear_logp_bwd(h, W, targets, mask, ctx.temperature, adv, lse)
+        else:
+            coef = (-grad_ent).to(torch.float32).contiguous()
+            dh, dW = rlk_linear_logp_bwd_entropy(h, W, targets, mask, ctx.temperature, adv, coef,
+                                                 lse, ent)
+        return dh.to(h.dtype), dW.to(W.dtype), None, None, None
+
+
+def linear_logp_entropy(h, W, targets, mask, temperature):
+    """Differentiable selected-token log-prob and entropy, each [N] (float32)."""
+    return LinearLogpEntropy.apply(h, W, targets, mask, temperature)
+
+
 # ---- loss fragments on the log-prob
 
 def _vec(name: str, t: torch.Tensor, N: int, dtype=torch.float32) -> None:
@@ -440,3 +471,38 @@ def rlk_linear_kl_bwd(h_s, W_s, h_t, W_t, mask, temperature: float, reverse: boo
                                       _stream(dev)),
             "rlk_linear_kl_bwd")
     return dh, dW
+
+
+class LinearKL(torch.autograd.Function):
+    """(kl_fwd, kl_rev) = linear_kl(h_s, W_s, h_t, W_t, mask, T); gradients reach the student
+    only, through rlk_linear_kl_bwd with coef = dL/dKL (once per direction that receives a
+    gradient, the two results added)."""
+
+    @staticmethod
+    def forward(ctx, h_s, W_s, h_t, W_t, mask, temperature):
+        kf, kr, ls, lt = rlk_linear_kl_fwd(h_s, W_s, h_t, W_t, mask, temperature)
+        ctx.save_for_backward(h_s, W_s, h_t, W_t, mask, ls, lt, kr)
+        ctx.temperature = float(temperature)
+        return kf, kr
+
+    @staticmethod
+    def backward(ctx, grad_fwd, grad_rev):
+        h_s, W_s, h_t, W_t, mask, ls, lt, kr = ctx.saved_tensors
+        dh = dW = None
+        for g, reverse in ((grad_fwd, False), (grad_rev, True)):
+            if g is None:
+                continue
+            a, b = rlk_linear_kl_bwd(h_s, W_s, h_t, W_t, mask, ctx.temperature, reverse,
+                                     g.to(torch.float32).contiguous(), ls, lt, kr)
+            dh = a if dh is None else dh + a
+            dW = b if dW is None else dW + b
+        if dh is None:
+            dh, dW = torch.zeros_like(h_s, dtype=torch.float32), torch.zeros_like(W_s,
+                                                                               dtype=torch.float32)
+        return dh.to(h_s.dtype), dW.to(W_s.dtype), None, None, None, None
+
+
+def linear_kl(h_s, W_s, h_t, W_t, mask, temperature):
+    """Differentiable forward and reverse full-vocabulary KL per token, each [N] (float32);
+    the teacher (h_t, W_t) receives no gradient."""
+    return LinearKL.apply(h_s, W_s, h_t, W_t, mask, temperature)

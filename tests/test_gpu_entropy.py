@@ -283,3 +283,19 @@ def test_empty_and_all_masked():
     lp0, _, ent0 = rlk.rlk_linear_logp_fwd_entropy(e, d["W"], d["targets"][:0], d["mask"][:0],
                                                    1.0)
     assert lp0.numel() == 0 and ent0.numel() == 0
+
+
+def test_autograd_matches_direct_calls():
+    import linear_selected_token_amd as rlk
+    w = wl.make(BWD_SMALL)
+    d = upload(w)
+    h = d["h"].clone().requires_grad_(True)
+    W = d["W"].clone().requires_grad_(True)
+    lp, ent = rlk.linear_logp_entropy(h, W, d["targets"], d["mask"], w.T)
+    m = d["mask"].float()
+    c = torch.from_numpy(_ent_coef(w, 9)).to(h.device)
+    loss = -(m * (d["adv"] * lp + c * ent)).sum()
+    loss.backward()
+    dh, dW = _run_bwd(w, c.cpu().numpy(), d)
+    assert torch.equal(h.grad, dh.to(torch.bfloat16))
+    assert torch.equal(W.grad, dW.to(torch.bfloat16))

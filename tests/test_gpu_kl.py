@@ -219,3 +219,24 @@ def test_empty_and_all_masked():
     dh0, dW0 = rlk.rlk_linear_kl_bwd(e[0], e[1], e[2], e[3], em, 1.0, True, z0, z0, z0, z0)
     torch.cuda.synchronize()
     assert dh0.numel() == 0 and not dW0.any()
+
+
+def test_autograd_matches_direct_calls():
+    import linear_selected_token_amd as rlk
+    w = wl.make(wl.scaled_spec(5, N=300, H=256, V=2000, n_seq=2, len_lo=100, len_hi=200,
+                               seed=133))
+    ht, Wt = _teacher(w, 128, 134)
+    d = [_dev(x) for x in (w.h, w.W, ht, Wt, w.mask)]
+    hs = d[0].clone().requires_grad_(True)
+    Ws = d[1].clone().requires_grad_(True)
+    kf, kr = rlk.linear_kl(hs, Ws, d[2], d[3], d[4], w.T)
+    cf = torch.from_numpy(np.random.default_rng(135).uniform(0.5, 1.5, w.N).astype(np.float32))
+    cr = torch.from_numpy(np.random.default_rng(136).uniform(0.5, 1.5, w.N).astype(np.float32))
+    cf, cr = cf.to(hs.device), cr.to(hs.device)
+    ((cf * kf).sum() + (cr * kr).sum()).backward()
+    _, kr0, ls, lt = rlk.rlk_linear_kl_fwd(*d, w.T)
+    a1, b1 = rlk.rlk_linear_kl_bwd(*d, w.T, False, cf, ls, lt, kr0)
+    a2, b2 = rlk.rlk_linear_kl_bwd(*d, w.T, True, cr, ls, lt, kr0)
+    torch.cuda.synchronize()
+    assert torch.equal(hs.grad, (a1 + a2).to(torch.bfloat16))
+    assert torch.equal(Ws.grad, (b1 + b2).to(torch.bfloat16))
