@@ -1,0 +1,94 @@
+"""The forward at the largest sizes the library accepts (needs an MI355X).
+
+  - h of 2^31 - 1 bytes or just under (the tile loads address token rows of h with 31-bit
+    offsets): the last rows of h are scored correctly;
+  - N = 2^22 tokens (the compaction walks 1024 blocks of 4096);
+  - V = 2^22 entries (32768 partial columns per token in the merge);
+  - the logits path at its largest vocabulary, 1,024,000 entries (a row's column statistics,
+    8 bytes per 128-entry column, fill 64 KB of LDS).
+Inputs are seeded normal draws made on the device; the oracle scores sampled rows from exact
+copies of them, within the 1e-3 gate."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import MAX_ABS_DLOGP, device, flush
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(shape, seed, scale=1.0):
+    g = torch.Generator(device=device())
+    g.manual_seed(seed)
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device())
+    rows = max(1, (1 << 26) // shape[1])
+    for r0 in range(0, shape[0], rows):
+        r1 = min(shape[0], r0 + rows)
+        out[r0:r1] = (torch.randn((r1 - r0, shape[1]), generator=g, device=device()) *
+                      scale).to(torch.bfloat16)
+    return out
+
+
+def _f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _run(N, H, V, T, seed, rows_extra=16):
+    import linear_selected_token_amd as rlk
+    r = np.random.default_rng(seed)
+    h = _draw((N, H), seed)
+    W = _draw((V, H), seed + 1, 1.0 / np.sqrt(H))
+    y = r.integers(0, V, N).astype(np.int32)
+    m = np.ones(N, np.uint8)
+    m[::7] = 0
+    logp, lse = rlk.rlk_linear_logp_fwd(h, W, torch.from_numpy(y).to(h.device),
+                                        torch.from_numpy(m).to(h.device), T)
+    torch.cuda.synchronize()
+    act = np.nonzero(m)[0]
+    rows = np.unique(np.concatenate([act[:2], act[-3:], r.choice(act, rows_extra)]))
+    W64 = _f64(W)
+    h64 = _f64(h[torch.from_numpy(rows).to(h.device)])
+    olp, olse = oracle.linear_logp(h64, W64, y[rows], np.ones(rows.size, np.uint8), T)
+    lp = logp.cpu().numpy()
+    ls = lse.cpu().numpy()
+    err = float(np.abs(lp[rows] - olp).max())
+    flush(f"  N={N} H={H} V={V}: max_abs_dlogp={err:.3e} over {rows.size} sampled rows "
+          f"(last row {rows[-1]})")
+    assert err <= MAX_ABS_DLOGP
+    assert float(np.abs(ls[rows] - olse).max()) <= MAX_ABS_DLOGP
+    inact = np.nonzero(m == 0)[0]
+    assert not lp[inact].any() and not ls[inact].any()
+
+
+def test_hidden_states_at_the_byte_limit():
+    H = 4096
+    N = ((1 << 31) - 1) // (2 * H)   # 262143 rows: 2^31 - 8192 bytes
+    _run(N, H, 1000, 0.9, 41)
+
+
+def test_most_tokens():
+    _run(1 << 22, 64, 1000, 1.0, 42)
+
+
+def test_largest_vocabulary():
+    _run(300, 64, 1 << 22, 1.0, 43, rows_extra=6)
+
+
+def test_logits_path_largest_vocabulary():
+    import linear_selected_token_amd as rlk
+    N, V, T = 40, 1024000, 0.8
+    z = _draw((N, V), 44, 3.0)
+    r = np.random.default_rng(44)
+    y = r.integers(0, V, N).astype(np.int32)
+    m = np.ones(N, np.uint8)
+    logp, lse = rlk.rlk_logp_from_logits(z, torch.from_numpy(y).to(z.device),
+                                         torch.from_numpy(m).to(z.device), T)
+    torch.cuda.synchronize()
+    rows = np.array([0, 17, N - 1])
+    olp, olse = oracle.logp_from_logits(_f64(z[torch.from_numpy(rows).to(z.device)]), y[rows],
+                                        np.ones(rows.size, np.uint8), T)
+    err = float(np.abs(logp.cpu().numpy()[rows] - olp).max())
+    flush(f"  logits path V={V}: max_abs_dlogp={err:.3e}")
+    assert err <= MAX_ABS_DLOGP
+    assert float(np.abs(lse.cpu().numpy()[rows] - olse).max()) <= MAX_ABS_DLOGP
