@@ -14,6 +14,12 @@
  * recomputes the logits tile by tile (the roadmap's "chunked backward" that trades compute
  * for memory) and returns dL/dh and dL/dW.
  *
+ * Also exported, under the same conventions: the forward with each token's entropy and the
+ * backward with an entropy bonus; the log-prob from logits that already exist; the forward
+ * and reverse full-vocabulary KL between a student and a teacher head, with its backward; the
+ * clipped policy-gradient loss fragment with a KL penalty and the dlogp diagnostics; and the
+ * building blocks of the forward (compaction, per-column partials, vocabulary shards, merge).
+ *
  * Batch invariance (RL-Kernel Roadmap (2026), P0.2 "Batch-Invariant Deterministic
  * LogProb"; vime roadmap, "Consistency Contract"): a token's logp, lse and dL/dh row are
  * bit-identical whatever else is in the batch, in whatever order, with whatever padding
@@ -23,10 +29,10 @@
  * tokens: it is deterministic run to run and does not depend on padding or inactive rows.
  *
  * Conventions for every entry point:
- *   - Pointers named h, W, targets, mask, adv, lse, logp, dh, dW, idx, n_active, part_*,
- *     target_logit and workspace are DEVICE pointers owned by the caller.  Arrays are dense
- *     and row-major.  h and W must be 16-byte aligned, the workspace 256-byte aligned,
- *     float and int32 arrays 4-byte aligned.
+ *   - Every array argument is a DEVICE pointer owned by the caller (the `bytes` result of
+ *     the *_workspace_size queries is the only host pointer).  Arrays are dense and
+ *     row-major.  Hidden states and weights must be 16-byte aligned, the workspace 256-byte
+ *     aligned, float and int32 arrays 4-byte aligned, double and int64 arrays 8-byte.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All work is
  *     enqueued on it; nothing blocks the host; results are valid once the stream reaches
  *     that point.  The library never allocates or frees device memory.
