@@ -108,9 +108,11 @@ def cpu_baseline(w, mode, target_s):
     m = np.ones(act.size, dtype=np.uint8)
     y = w.targets[act]
     adv = w.adv[act]
+    res = {}
+
     def run(n):
         t0 = time.perf_counter()
-        oracle.linear_logp(h64[:n], W64, y[:n], m[:n], w.T)
+        res["logp"], _ = oracle.linear_logp(h64[:n], W64, y[:n], m[:n], w.T)
         if mode == "entropy":
             oracle.entropy(h64[:n], W64, m[:n], w.T)
             oracle.linear_logp_entropy_grads(h64[:n], W64, y[:n], m[:n], w.T, adv[:n],
@@ -129,9 +131,28 @@ def cpu_baseline(w, mode, target_s):
     what = {"fwd": "forward",
             "entropy": "forward + entropy + gradients with an entropy bonus"}.get(
         mode, "forward + dL/dh + dL/dW")
-    return {"value": n / dt, "unit": "active tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} active tokens of the same workload scored as one batch "
-                      f"({what}, float64, numpy/OpenBLAS), {dt:.1f} s"}
+    out = {"value": n / dt, "unit": "active tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"first {n} active tokens of the same workload scored as one batch "
+                     f"({what}, float64, numpy/OpenBLAS), {dt:.1f} s"}
+    return out, act[:n], res["logp"]
+
+
+def sample_parity(logp_gpu, rows, oracle_logp):
+    """max |dlogp| of the measured run's logp against the oracle's on the CPU sample, and the
+    dlogp diagnostics of the same comparison computed by the library on the GPU."""
+    import torch
+    import linear_selected_token_amd as rlk
+    dev = logp_gpu.device
+    idx = torch.from_numpy(np.asarray(rows)).to(dev)
+    a = logp_gpu[idx].contiguous()
+    b = torch.from_numpy(np.asarray(oracle_logp, dtype=np.float32)).to(dev)
+    m = torch.ones(a.numel(), dtype=torch.uint8, device=dev)
+    diag, worst = rlk.rlk_dlogp_diagnostics(a, b, m, 0.2)
+    d = dict(zip(rlk.DIAG_FIELDS, [float(x) for x in diag.cpu().tolist()]))
+    err = float(np.max(np.abs(a.double().cpu().numpy() - np.asarray(oracle_logp))))
+    return {"sample_tokens": int(a.numel()), "max_abs_dlogp_vs_oracle": err,
+            "diagnostics": {k: (int(v) if k == "active" else float(f"{v:.4g}")) for k, v in d.items()},
+            "worst_sample_row": int(rows[int(worst.item())]) if int(worst.item()) >= 0 else None}
 
 
 def traffic_for(kernel_src_files, name):
@@ -276,7 +297,7 @@ def bench_entropy(args, w):
                      "avg_launch_ms": round(ms, 4)},
     }
     if args.cpu_baseline_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, "entropy", args.cpu_baseline_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, "entropy", args.cpu_baseline_seconds)[0]
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
@@ -579,8 +600,9 @@ def main():
         out["fwd_bwd_tflops_no_recompute_basis"] = round(
             6.0 * Na * H * V / (ms * 1e-3) / 1e12, 2)
     if args.cpu_baseline_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, args.mode, args.cpu_baseline_seconds)
+        out["cpu_baseline"], rows, olp = cpu_baseline(w, args.mode, args.cpu_baseline_seconds)
         out["gpu_over_cpu_baseline"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
+        out["parity"] = sample_parity(bufs.logp[:N], rows, olp)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
