@@ -204,9 +204,11 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
 // One work-group of 256 threads merges 32 compacted rows: thread (row = tid & 31,
 // slice = tid >> 5) walks columns slice, slice + 8, ... in ascending order; the eight slice
 // sums are added in a fixed tree.
+template <bool kEnt>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(MergeArgs a) {
   __shared__ float red[8][33];
   __shared__ float wred[8][33];
+  constexpr int kU = 8;  // columns in flight per thread (the walk order is unchanged)
   const int Na = *a.n_active;
   const int i0 = blockIdx.x * 32;
   if (i0 >= Na) return;
@@ -215,10 +217,22 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(MergeArgs a) {
   const int i = i0 + r;
   const bool ok = i < Na;
   const int J = (a.V + kVocabPartial - 1) / kVocabPartial;
+  const float* pmax = a.part_max + i;
+  const float* psum = a.part_sum + i;
+  const size_t N = a.N;
 
   float m = -INFINITY;
-  if (ok)
-    for (int j = sl; j < J; j += 8) m = fmaxf(m, a.part_max[(size_t)j * a.N + i]);
+  if (ok) {
+    int j = sl;
+    for (; j + 8 * (kU - 1) < J; j += 8 * kU) {
+      float x[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) x[u] = pmax[(size_t)(j + 8 * u) * N];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) m = fmaxf(m, x[u]);
+    }
+    for (; j < J; j += 8) m = fmaxf(m, pmax[(size_t)j * N]);
+  }
   red[sl][r] = m;
   __syncthreads();
   float M = red[0][r];
@@ -226,15 +240,33 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(MergeArgs a) {
   for (int k = 1; k < 8; ++k) M = fmaxf(M, red[k][r]);
   __syncthreads();
 
+  // column j adds part_sum 2^(part_max - M) to s and, for the entropy, sum_v 2^(x_v - M)
+  // (x_v - M) over the column to w; columns sl, sl + 8, ... in ascending order
   float s = 0.f, w = 0.f;
-  if (ok)
-    for (int j = sl; j < J; j += 8) {
-      const size_t o = (size_t)j * a.N + i;
-      const float f = __builtin_amdgcn_exp2f(a.part_max[o] - M);
-      s += a.part_sum[o] * f;
-      // sum_v 2^(x_v - M) (x_v - M) over the column, for the entropy
-      if (a.part_w) w += (a.part_w[o] + (a.part_max[o] - M) * a.part_sum[o]) * f;
+  auto add = [&](float pm, float ps, float pw) __attribute__((always_inline)) {
+    const float f = __builtin_amdgcn_exp2f(pm - M);
+    s += ps * f;
+    if constexpr (kEnt) w += (pw + (pm - M) * ps) * f;
+  };
+  if (ok) {
+    int j = sl;
+    for (; j + 8 * (kU - 1) < J; j += 8 * kU) {
+      float x[kU], y[kU], z[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const size_t o = (size_t)(j + 8 * u) * N;
+        x[u] = pmax[o];
+        y[u] = psum[o];
+        z[u] = kEnt ? a.part_w[o + i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) add(x[u], y[u], z[u]);
     }
+    for (; j < J; j += 8) {
+      const size_t o = (size_t)j * N;
+      add(pmax[o], psum[o], kEnt ? a.part_w[o + i] : 0.f);
+    }
+  }
   red[sl][r] = s;
   wred[sl][r] = w;
   __syncthreads();
@@ -246,7 +278,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(MergeArgs a) {
     const int t = a.idx[i];
     a.logp[t] = a.target_logit[i] - lse;
     if (a.lse) a.lse[t] = lse;
-    if (a.part_w) {
+    if constexpr (kEnt) {
       // H = lse - E_p[z] = ln2 (log2 S - E_p[x - M]) in log2 units x = z log2 e
       const float A = ((wred[0][r] + wred[1][r]) + (wred[2][r] + wred[3][r])) +
                       ((wred[4][r] + wred[5][r]) + (wred[6][r] + wred[7][r]));
@@ -279,7 +311,10 @@ hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream
 
 hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t stream) {
   const int grid = (int)((a.N + 31) / 32);
-  hipLaunchKernelGGL(fwd_merge_kernel, dim3(grid), dim3(256), 0, stream, a);
+  if (a.part_w)
+    hipLaunchKernelGGL(fwd_merge_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(fwd_merge_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
