@@ -85,12 +85,28 @@ __global__ __launch_bounds__(256) void kl_merge_kernel(KlArgs a) {
   const int i = blockIdx.x * 32 + r;
   const bool ok = i < Na;
   const int J = (a.V + 127) / 128;
+  constexpr int kU = 8;  // columns in flight per thread (the walk order is unchanged)
   float mt = -INFINITY, ms = -INFINITY;
-  if (ok)
-    for (int j = sl; j < J; j += 8) {
+  if (ok) {
+    int j = sl;
+    for (; j + 8 * (kU - 1) < J; j += 8 * kU) {
+      float xt[kU], xs[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        xt[u] = a.t_max[(size_t)(j + 8 * u) * a.N + i];
+        xs[u] = a.s_max[(size_t)(j + 8 * u) * a.N + i];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        mt = fmaxf(mt, xt[u]);
+        ms = fmaxf(ms, xs[u]);
+      }
+    }
+    for (; j < J; j += 8) {
       mt = fmaxf(mt, a.t_max[(size_t)j * a.N + i]);
       ms = fmaxf(ms, a.s_max[(size_t)j * a.N + i]);
     }
+  }
   red[0][sl][r] = mt;
   red[1][sl][r] = ms;
   __syncthreads();
@@ -102,16 +118,22 @@ __global__ __launch_bounds__(256) void kl_merge_kernel(KlArgs a) {
   }
   __syncthreads();
   float st = 0.f, ss = 0.f, af = 0.f, ar = 0.f;
-  if (ok)
-    for (int j = sl; j < J; j += 8) {
-      const size_t o = (size_t)j * a.N + i;
-      const float ft = __builtin_amdgcn_exp2f(a.t_max[o] - Mt);
-      const float fs = __builtin_amdgcn_exp2f(a.s_max[o] - Ms);
-      st += a.t_sum[o] * ft;
-      ss += a.s_sum[o] * fs;
-      af += a.wf[o] * ft;
-      ar += a.wr[o] * fs;
+  auto add = [&](size_t o) __attribute__((always_inline)) {
+    const float ft = __builtin_amdgcn_exp2f(a.t_max[o] - Mt);
+    const float fs = __builtin_amdgcn_exp2f(a.s_max[o] - Ms);
+    st += a.t_sum[o] * ft;
+    ss += a.s_sum[o] * fs;
+    af += a.wf[o] * ft;
+    ar += a.wr[o] * fs;
+  };
+  if (ok) {
+    int j = sl;
+    for (; j + 8 * (kU - 1) < J; j += 8 * kU) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) add((size_t)(j + 8 * u) * a.N + i);
     }
+    for (; j < J; j += 8) add((size_t)j * a.N + i);
+  }
   red[2][sl][r] = st;
   red[3][sl][r] = ss;
   red[4][sl][r] = af;
