@@ -1,6 +1,6 @@
 """Bitwise batch invariance of the HIP path (needs an MI355X).
 
-A token's logp and lse must be bit-identical whether its sequence is scored alone, in
+A token's logp and lse (and, from the entropy forward, its entropy) must be bit-identical whether its sequence is scored alone, in
 the full batch, in shuffled order, with extra padding, with its prompt tokens also
 active, on a repeat run or on another stream (RL-Kernel integration roadmap for vime,
 "Consistency Contract": same-backend bitwise stability across batch size, row position,
@@ -19,13 +19,21 @@ pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def _keyed(w, lp, lse, only_active_of=None):
+def _keyed(w, *outs):
     out = {}
     for i, k in enumerate(w.key()):
         if k[0] < 0 or not w.mask[i]:
             continue
-        out[k] = (int(bits(lp[i:i + 1])[0]), int(bits(lse[i:i + 1])[0]))
+        out[k] = tuple(int(bits(o[i:i + 1])[0]) for o in outs)
     return out
+
+
+def _fwd_entropy(w, d=None):
+    import linear_selected_token_amd as rlk
+    d = d or upload(w)
+    outs = rlk.rlk_linear_logp_fwd_entropy(d["h"], d["W"], d["targets"], d["mask"], w.T)
+    torch.cuda.synchronize()
+    return tuple(o.cpu().numpy() for o in outs)
 
 
 def _mismatches(ref, got):
@@ -36,9 +44,9 @@ def _mismatches(ref, got):
     return n
 
 
-def _sweep(fam, n_alone, label):
+def _sweep(fam, n_alone, label, fwd=run_fwd):
     base = fam.batch()
-    ref = _keyed(base, *run_fwd(base))
+    ref = _keyed(base, *fwd(base))
     cases = []
     for s in range(min(n_alone, fam.n_seq)):
         cases.append((f"alone {s}", fam.alone(s)))
@@ -50,7 +58,7 @@ def _sweep(fam, n_alone, label):
     total = 0
     checked = 0
     for name, w in cases:
-        got = _keyed(w, *run_fwd(w))
+        got = _keyed(w, *fwd(w))
         common = [k for k in got if k in ref]
         m = _mismatches(ref, got)
         total += m
@@ -60,15 +68,16 @@ def _sweep(fam, n_alone, label):
     # repeat runs and a second stream on the full batch
     d = upload(base)
     import linear_selected_token_amd as rlk
+    call = (rlk.rlk_linear_logp_fwd if fwd is run_fwd else rlk.rlk_linear_logp_fwd_entropy)
     outs = []
     for k in range(3):
-        outs.append(rlk.rlk_linear_logp_fwd(d["h"], d["W"], d["targets"], d["mask"], base.T))
+        outs.append(call(d["h"], d["W"], d["targets"], d["mask"], base.T))
     st = torch.cuda.Stream()
     with torch.cuda.stream(st):
-        outs.append(rlk.rlk_linear_logp_fwd(d["h"], d["W"], d["targets"], d["mask"], base.T))
+        outs.append(call(d["h"], d["W"], d["targets"], d["mask"], base.T))
     torch.cuda.synchronize()
-    for lp, lse in outs:
-        got = _keyed(base, lp.cpu().numpy(), lse.cpu().numpy())
+    for o in outs:
+        got = _keyed(base, *(x.cpu().numpy() for x in o))
         total += _mismatches(ref, got)
         checked += len(got)
     flush(f"  {label}: {total} mismatches over {checked} active-token comparisons")
@@ -87,3 +96,18 @@ def test_invariance_config3_full():
     fam = wl.Family(wl.CONFIGS[3])
     fam.use_targets(np.load(os.path.join(HERE, "golden", "cfg3_sampled_targets.npy")))
     assert _sweep(fam, fam.n_seq, "config3") == 0
+
+
+def test_entropy_invariance_small():
+    # logp, lse and entropy of the entropy forward, over the same kinds of layouts
+    fam = wl.Family(wl.scaled_spec(2, N=1500, H=256, V=2000, n_seq=8, len_lo=64, len_hi=400,
+                                   seed=91, T=0.7))
+    assert _sweep(fam, 8, "entropy small", fwd=_fwd_entropy) == 0
+
+
+def test_entropy_invariance_config3():
+    """The entropy forward on the N=16384 workload: 8 sequences alone, shuffles, paddings,
+    all-active density, a subset, repeats and a second stream."""
+    fam = wl.Family(wl.CONFIGS[3])
+    fam.use_targets(np.load(os.path.join(HERE, "golden", "cfg3_sampled_targets.npy")))
+    assert _sweep(fam, 8, "entropy config3", fwd=_fwd_entropy) == 0
