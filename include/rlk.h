@@ -208,7 +208,9 @@ rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int
  * Batch-invariant like logp.  H_s and H_t: multiples of 64; each h at most 2^31 - 1 bytes.
  *   lse_s, lse_t [N] float     out (may be NULL): each head's log-sum-exp, which the backward
  *                              takes back
- *   workspace: rlk_linear_kl_fwd_workspace_size bytes (about 8 N (V/128) * 6 + 2 chunks). */
+ *   workspace: rlk_linear_kl_fwd_workspace_size bytes: six float arrays of ceil(V/128) x N
+ *              (both heads' column statistics and the two cross terms) and two chunk buffers of
+ *              32800 floats per token, N rounded up to 256 (4.7 GB at N = 16384, V = 151936). */
 rlk_status_t rlk_linear_kl_fwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
                                               int dtype, size_t* bytes);
 rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t,
@@ -224,7 +226,8 @@ rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t
  * chunk's dL/dh_s and dL/dW_s follow as in rlk_linear_logp_bwd.
  *   coef [N] float; lse_s, lse_t [N] and (reverse only) kl_rev [N] from rlk_linear_kl_fwd
  *   dh_s [N,H_s], dW_s [V,H_s] float   out, overwritten
- *   workspace: rlk_linear_kl_bwd_workspace_size bytes. */
+ *   workspace: rlk_linear_kl_bwd_workspace_size bytes: rlk_linear_logp_bwd's workspace plus the
+ *              two chunk buffers of the forward. */
 rlk_status_t rlk_linear_kl_bwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
                                               int dtype, size_t* bytes);
 rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t,
