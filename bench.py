@@ -43,6 +43,8 @@ DEFAULT_WORKLOAD = "qwen3-8b-head-N16384-T0.7"
 # are byte-identical to what was profiled.
 FWD_TILE_SOURCES = [f"linear_selected_token_amd/csrc/{f}"
                     for f in ("fwd.hip", "common.hpp", "mainloop.hpp", "kernels.hpp")]
+LOGITS_SOURCES = [f"linear_selected_token_amd/csrc/{f}"
+                  for f in ("logits.hip", "common.hpp", "kernels.hpp")]
 
 
 def parse():
@@ -226,7 +228,8 @@ def bench_logits(args, w):
                    "n_active": Na, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "logits_logp_kernel<bf16>",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for(LOGITS_SOURCES, "logits_logp_kernel"),
                      "algorithmic_bytes_per_step": nbytes},
         "cpu_baseline": None,
     }
