@@ -359,7 +359,8 @@ rlk_status_t rlk_dlogp_diagnostics(const float* logp_a, const float* logp_b,
   DiagArgs a{logp_a, logp_b, idx, na, (int)N, clip_eps,
              carve<uint64_t>(workspace, L.keys), carve<double>(workspace, L.part),
              carve<uint64_t>(workspace, L.pmax), carve<int>(workspace, L.ptok),
-             carve<int>(workspace, L.hist), out, worst};
+             carve<int>(workspace, L.hist), carve<uint64_t>(workspace, L.sel),
+             carve<int64_t>(workspace, L.sel + 8 * kDiagRanks), out, worst};
   return dev_status(launch_dlogp_diagnostics(a, st));
 }
 

@@ -121,6 +121,8 @@ struct DiagArgs {
   uint64_t* pmax;   // [nblk]
   int* ptok;        // [nblk]
   int* hist;        // [8][kDiagRanks][256]
+  uint64_t* sel_prefix;  // [kDiagRanks] bytes selected so far, most significant first
+  int64_t* sel_rank;     // [kDiagRanks] rank left under that prefix
   double* out;      // [kDiagOut]
   int64_t* worst;
 };

@@ -13,8 +13,9 @@
 // magnitude), the sums in fp64 as above; the percentiles of |dlogp| come from an exact
 // radix select over the fp64 bit patterns (non-negative doubles order like their bits):
 // eight passes of one byte each, most significant first, each counting with integer
-// atomics (exact, so order-independent) the keys that match the prefix selected so far.
-// Every work-group of a pass re-derives that prefix from the earlier passes' histograms.
+// atomics (exact, so order-independent) the keys that match the prefix selected so far
+// (ranks with equal prefixes share one count), then one work-group scans the counts and
+// stores each rank's extended prefix and remaining rank for the next pass.
 #include <math.h>
 
 #include "common.hpp"
@@ -117,22 +118,12 @@ __device__ __forceinline__ void percentile_ranks(int n, int64_t* rk, double* fra
   }
 }
 
-// Replays passes 0 .. npass-1: the byte chosen at each pass and the rank left inside it.
-__device__ void select_prefix(const int* hist, int npass, int r, int64_t rank, uint64_t* prefix,
-                              int64_t* left) {
-  uint64_t pf = 0;
-  int64_t k = rank;
-  for (int p = 0; p < npass; ++p) {
-    const int* h = hist + ((size_t)p * kDiagRanks + r) * 256;
-    int d = 0;
-    for (; d < 255; ++d) {
-      if (k < h[d]) break;
-      k -= h[d];
-    }
-    pf |= (uint64_t)d << (56 - 8 * p);
-  }
-  *prefix = pf;
-  *left = k;
+// Ranks whose selected prefixes are equal share one histogram: the first such rank owns it.
+__device__ __forceinline__ int prefix_owner(const uint64_t* pf, int r) {
+  int o = r;
+  for (int q = r - 1; q >= 0; --q)
+    if (pf[q] == pf[r]) o = q;
+  return o;
 }
 
 // keys, per-block sums (|d|, exp(d), clipped, exp(d) - 1 - d) and the block's largest key
@@ -192,24 +183,32 @@ __global__ __launch_bounds__(kRThreads) void diag_keys_kernel(DiagArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kRThreads) void diag_zero_kernel(int* p, int n) {
-  for (int e = blockIdx.x * kRThreads + threadIdx.x; e < n; e += gridDim.x * kRThreads) p[e] = 0;
+// Clears the histograms and starts the selection: empty prefixes, the ranks themselves.
+__global__ __launch_bounds__(kRThreads) void diag_zero_kernel(DiagArgs a) {
+  const int n = 8 * kDiagRanks * 256;
+  for (int e = blockIdx.x * kRThreads + threadIdx.x; e < n; e += gridDim.x * kRThreads)
+    a.hist[e] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < kDiagRanks) {
+    const int Na = *a.n_active;
+    int64_t rk[kDiagRanks];
+    double frac[3];
+    percentile_ranks(Na > 0 ? Na : 1, rk, frac);
+    a.sel_prefix[threadIdx.x] = 0;
+    a.sel_rank[threadIdx.x] = rk[threadIdx.x];
+  }
 }
 
 // Pass p: per rank, count the keys that match the selected prefix, by their byte p.
 __global__ __launch_bounds__(kRThreads) void diag_hist_kernel(DiagArgs a, int pass) {
   __shared__ int cnt[kDiagRanks][256];
   __shared__ uint64_t pf[kDiagRanks];
+  __shared__ int own[kDiagRanks];
   const int tid = threadIdx.x;
   const int Na = *a.n_active;
   for (int e = tid; e < kDiagRanks * 256; e += kRThreads) (&cnt[0][0])[e] = 0;
-  if (tid < kDiagRanks) {
-    int64_t rk[kDiagRanks];
-    double frac[3];
-    percentile_ranks(Na, rk, frac);
-    int64_t left;
-    select_prefix(a.hist, pass, tid, rk[tid], &pf[tid], &left);
-  }
+  if (tid < kDiagRanks) pf[tid] = a.sel_prefix[tid];
+  __syncthreads();
+  if (tid < kDiagRanks) own[tid] = prefix_owner(pf, tid);
   __syncthreads();
   const int shift = 56 - 8 * pass;
   const uint64_t hi_mask = pass == 0 ? 0 : (~0ull << (shift + 8));
@@ -218,13 +217,41 @@ __global__ __launch_bounds__(kRThreads) void diag_hist_kernel(DiagArgs a, int pa
     const int d = (int)((key >> shift) & 255);
 #pragma unroll
     for (int r = 0; r < kDiagRanks; ++r)
-      if ((key & hi_mask) == pf[r]) atomicAdd(&cnt[r][d], 1);
+      if (own[r] == r && (key & hi_mask) == pf[r]) atomicAdd(&cnt[r][d], 1);
   }
   __syncthreads();
   int* h = a.hist + (size_t)pass * kDiagRanks * 256;
   for (int e = tid; e < kDiagRanks * 256; e += kRThreads) {
     const int c = (&cnt[0][0])[e];
     if (c) atomicAdd(h + e, c);
+  }
+}
+
+// One work-group, after pass `pass`: for each rank, the byte of that pass under which its order
+// statistic lies (an inclusive scan of the owner's 256 counts) and the rank left inside it.
+__global__ __launch_bounds__(256) void diag_select_kernel(DiagArgs a, int pass) {
+  __shared__ int cum[256];
+  __shared__ uint64_t pf[kDiagRanks];
+  const int tid = threadIdx.x;
+  if (tid < kDiagRanks) pf[tid] = a.sel_prefix[tid];
+  __syncthreads();
+  for (int r = 0; r < kDiagRanks; ++r) {
+    const int o = prefix_owner(pf, r);
+    const int64_t k = a.sel_rank[r];
+    cum[tid] = a.hist[((size_t)pass * kDiagRanks + o) * 256 + tid];
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = tid >= off ? cum[tid - off] : 0;
+      __syncthreads();
+      cum[tid] += v;
+      __syncthreads();
+    }
+    const int64_t below = tid > 0 ? cum[tid - 1] : 0;
+    if (k >= below && k < (int64_t)cum[tid]) {  // exactly one byte holds rank k
+      a.sel_prefix[r] = pf[r] | ((uint64_t)tid << (56 - 8 * pass));
+      a.sel_rank[r] = k - below;
+    }
+    __syncthreads();
   }
 }
 
@@ -270,12 +297,7 @@ __global__ __launch_bounds__(kRThreads) void diag_final_kernel(DiagArgs a, int n
   int64_t rk[kDiagRanks];
   double frac[3];
   percentile_ranks(Na > 0 ? Na : 1, rk, frac);
-  if (tid < kDiagRanks) {
-    uint64_t pf;
-    int64_t left;
-    select_prefix(a.hist, 8, tid, rk[tid], &pf, &left);
-    ostat[tid] = __builtin_bit_cast(double, pf);
-  }
+  if (tid < kDiagRanks) ostat[tid] = __builtin_bit_cast(double, a.sel_prefix[tid]);
   __syncthreads();
   if (tid == 0) {
     double* o = a.out;
@@ -313,11 +335,12 @@ hipError_t launch_dlogp_diagnostics(const DiagArgs& a, hipStream_t stream) {
   const int nblk = (a.N + kLossBlock - 1) / kLossBlock;  // enough for every active token
   const int nb = nblk > 0 ? nblk : 1;
   hipLaunchKernelGGL(diag_keys_kernel, dim3(nb), dim3(kRThreads), 0, stream, a);
-  hipLaunchKernelGGL(diag_zero_kernel, dim3(8), dim3(kRThreads), 0, stream, a.hist,
-                     8 * kDiagRanks * 256);
+  hipLaunchKernelGGL(diag_zero_kernel, dim3(8), dim3(kRThreads), 0, stream, a);
   const int hb = nb < 1024 ? nb : 1024;
-  for (int p = 0; p < 8; ++p)
+  for (int p = 0; p < 8; ++p) {
     hipLaunchKernelGGL(diag_hist_kernel, dim3(hb), dim3(kRThreads), 0, stream, a, p);
+    hipLaunchKernelGGL(diag_select_kernel, dim3(1), dim3(256), 0, stream, a, p);
+  }
   hipLaunchKernelGGL(diag_final_kernel, dim3(1), dim3(kRThreads), 0, stream, a, nb);
   return hipGetLastError();
 }

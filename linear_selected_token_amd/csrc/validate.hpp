@@ -82,7 +82,7 @@ inline size_t loss_workspace(int64_t N) {
 }
 
 struct DiagLayout {
-  size_t idx, n_active, keys, part, pmax, ptok, hist, total;
+  size_t idx, n_active, keys, part, pmax, ptok, hist, sel, total;
 };
 
 inline DiagLayout diag_layout(int64_t N) {
@@ -97,6 +97,7 @@ inline DiagLayout diag_layout(int64_t N) {
   L.pmax = o;     o = align_up(o + 8 * nblk, 256);
   L.ptok = o;     o = align_up(o + 4 * nblk, 256);
   L.hist = o;     o = align_up(o + 4 * 8 * 6 * 256, 256);
+  L.sel = o;      o = align_up(o + 16 * 6, 256);
   L.total = o;
   return L;
 }
