@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cstdio>
 
+#include "aux_kernels.hpp"
 #include "kernels.hpp"
 #include "rlk.h"
 #include "validate.hpp"

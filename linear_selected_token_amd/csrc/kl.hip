@@ -24,6 +24,7 @@
 // Every reduction is a fixed in-lane order followed by a fixed xor tree, and the columns
 // are merged in one fixed order, so a token's results depend only on its own rows.
 #include "common.hpp"
+#include "aux_kernels.hpp"
 #include "kernels.hpp"
 
 namespace rlk {

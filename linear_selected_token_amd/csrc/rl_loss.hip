@@ -19,6 +19,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "aux_kernels.hpp"
 #include "kernels.hpp"
 
 namespace rlk {
