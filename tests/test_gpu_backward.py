@@ -119,3 +119,23 @@ def test_config5_full_size_sampled():
     scale = dW.double().abs().sum(0).max().item()
     flush(f"  config5 |sum_v dW_v|max={colsum:.3e} (column abs-sum {scale:.3e})")
     assert colsum <= 1e-3 * scale
+
+
+def test_large_hidden_head_sampled():
+    # the large-hidden head (H = 7168, V = 129280): 28 hidden tiles, W rows of 14 KiB
+    w = wl.make(wl.scaled_spec(4, N=512, n_seq=2, len_lo=200, len_hi=300, prompt="floor_half",
+                               seed=150, backward=True))
+    _, _, dh, dW = run_bwd(w)
+    h64, W64 = oracle_inputs(w)
+    act = np.nonzero(w.mask)[0]
+    r = np.random.default_rng(151)
+    rows = np.unique(np.concatenate([act[:2], act[-2:], r.choice(act, 12, replace=False)]))
+    odh = oracle.grad_h_rows(h64, W64, w.targets, w.mask, w.T, w.adv, rows)
+    eh = rel_l2(dh[torch.from_numpy(rows).to(dh.device)].cpu().numpy(), odh)
+    _, olse = oracle.linear_logp(h64, W64, w.targets, w.mask, w.T)
+    vr = np.unique(np.concatenate([w.targets[act[:8]], r.integers(0, w.V, 12), [0, w.V - 1]]))
+    odW = oracle.grad_W_rows(h64, W64, w.targets, w.mask, w.T, w.adv, vr, lse=olse)
+    ew = rel_l2(dW[torch.from_numpy(vr).to(dW.device)].cpu().numpy(), odW)
+    flush(f"  large-hidden head N={w.N} H={w.H} V={w.V}: relL2(dh)={eh:.3e} over {rows.size} rows, "
+          f"relL2(dW)={ew:.3e} over {vr.size} vocabulary rows")
+    assert eh <= GRAD_REL_L2 and ew <= GRAD_REL_L2
