@@ -227,6 +227,7 @@ def bench_logits(args, w):
         "config": {"workload": args.workload, "mode": "logits", "N": N, "V": V, "T": T,
                    "n_active": Na, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "logits_logp_kernel<bf16>",
+                     "timed": "the whole call per step (compaction + the kernel)",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic_for(LOGITS_SOURCES, "logits_logp_kernel"),

@@ -32,7 +32,9 @@ namespace rlk {
 namespace {
 
 // One work-group of 4 waves per compacted token row; each 32-lane half of a wave takes one
-// 128-entry column (4 entries per lane), so a wave step covers 2 columns.
+// 128-entry column (4 entries per lane), so a wave step covers 2 columns.  A half takes its
+// columns two at a time (both columns' loads issued before either is reduced); the chunk
+// buffers are read once, with non-temporal loads.
 __global__ __launch_bounds__(256) void kl_cross_kernel(KlArgs a, int c0) {
   const int Na = *a.n_active;
   const int i = blockIdx.x;
@@ -45,13 +47,13 @@ __global__ __launch_bounds__(256) void kl_cross_kernel(KlArgs a, int c0) {
   const int l32 = lane & 31;
   const float* xs_row = a.xs + (size_t)i * kXPitch;
   const float* xt_row = a.xt + (size_t)i * kXPitch;
-  for (int jc = 2 * wave + half; jc < ncol; jc += 8) {
+  auto ld = [&](const float* r, int v0) __attribute__((always_inline)) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + v0));
+  };
+  auto col_terms = [&](int jc, const f32x4& xs, const f32x4& xt, float ms,
+                       float mt) __attribute__((always_inline)) {
     const int col = c0 / 128 + jc;
-    const float ms = a.s_max[(size_t)col * a.N + i];
-    const float mt = a.t_max[(size_t)col * a.N + i];
     const int v0 = jc * 128 + 4 * l32;
-    const f32x4 xs = *reinterpret_cast<const f32x4*>(xs_row + v0);
-    const f32x4 xt = *reinterpret_cast<const f32x4*>(xt_row + v0);
     const float s4[4] = {xs.x, xs.y, xs.z, xs.w};
     const float t4[4] = {xt.x, xt.y, xt.z, xt.w};
     float wf = 0.f, wr = 0.f;
@@ -72,6 +74,23 @@ __global__ __launch_bounds__(256) void kl_cross_kernel(KlArgs a, int c0) {
       a.wf[(size_t)col * a.N + i] = wf;
       a.wr[(size_t)col * a.N + i] = wr;
     }
+  };
+  for (int jc = 2 * wave + half; jc < ncol; jc += 16) {
+    const bool two = jc + 8 < ncol;
+    const int colA = c0 / 128 + jc, colB = colA + 8;
+    const f32x4 xsA = ld(xs_row, jc * 128 + 4 * l32), xtA = ld(xt_row, jc * 128 + 4 * l32);
+    f32x4 xsB = {0.f, 0.f, 0.f, 0.f}, xtB = {0.f, 0.f, 0.f, 0.f};
+    float msB = 0.f, mtB = 0.f;
+    if (two) {
+      xsB = ld(xs_row, (jc + 8) * 128 + 4 * l32);
+      xtB = ld(xt_row, (jc + 8) * 128 + 4 * l32);
+      msB = a.s_max[(size_t)colB * a.N + i];
+      mtB = a.t_max[(size_t)colB * a.N + i];
+    }
+    const float msA = a.s_max[(size_t)colA * a.N + i];
+    const float mtA = a.t_max[(size_t)colA * a.N + i];
+    col_terms(jc, xsA, xtA, msA, mtA);
+    if (two) col_terms(jc + 8, xsB, xtB, msB, mtB);
   }
 }
 
@@ -165,7 +184,8 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 // One work-group per row of Gv (rows up to the active count rounded to the tile, the rest
-// exit); each thread forms 4 consecutive entries per step.  Rows past the active count and
+// exit); each thread forms 4 consecutive entries per step, two steps at a time (both steps'
+// non-temporal loads issued first).  Rows past the active count and
 // entries past the vocabulary are written as 0, since the GEMMs that follow read them.
 template <bool kReverse>
 __global__ __launch_bounds__(256) void kl_grad_kernel(KlArgs a, int c0) {
@@ -187,11 +207,9 @@ __global__ __launch_bounds__(256) void kl_grad_kernel(KlArgs a, int c0) {
   const float* xs_row = a.xs + (size_t)i * kXPitch;
   const float* xt_row = a.xt + (size_t)i * kXPitch;
   uint16_t* g_row = a.Gv + (size_t)i * kGvPitch;
-  for (int v0 = 4 * threadIdx.x; v0 < vt; v0 += 1024) {
+  auto grad4 = [&](int v0, const f32x4& xs, const f32x4& xt) __attribute__((always_inline)) {
     float G[4] = {0.f, 0.f, 0.f, 0.f};
     if (act && v0 < vc) {
-      const f32x4 xs = *reinterpret_cast<const f32x4*>(xs_row + v0);
-      const f32x4 xt = *reinterpret_cast<const f32x4*>(xt_row + v0);
       const float s4[4] = {xs.x, xs.y, xs.z, xs.w};
       const float t4[4] = {xt.x, xt.y, xt.z, xt.w};
 #pragma unroll
@@ -211,6 +229,17 @@ __global__ __launch_bounds__(256) void kl_grad_kernel(KlArgs a, int c0) {
     pk[0] = pack2(G[0], G[1]);
     pk[1] = pack2(G[2], G[3]);
     *reinterpret_cast<u32x2*>(g_row + v0) = pk;
+  };
+  auto ld = [&](const float* r, int v0) __attribute__((always_inline)) {
+    return (act && v0 < vc) ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + v0))
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  for (int v0 = 4 * threadIdx.x; v0 < vt; v0 += 2048) {
+    const int v1 = v0 + 1024;
+    const f32x4 xs0 = ld(xs_row, v0), xt0 = ld(xt_row, v0);
+    const f32x4 xs1 = ld(xs_row, v1), xt1 = ld(xt_row, v1);
+    grad4(v0, xs0, xt0);
+    if (v1 < vt) grad4(v1, xs1, xt1);
   }
 }
 

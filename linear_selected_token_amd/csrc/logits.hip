@@ -8,10 +8,10 @@
 // / T applied once, followed by the fused forward's fixed-order merge.  The kernel is a pure
 // HBM stream: one work-group of 4 waves per active token row keeps its row's column
 // statistics in LDS (8 bytes per column) and merges them itself; each wave step reads
-// 4 KiB of the row (four 16-byte loads per lane), i.e. 16 bf16 columns (16 lanes each) or 8
-// fp32 columns (32 lanes each), and the next step's loads are issued before the current step
-// is reduced.  Every reduction is a fixed in-lane order followed by a fixed
-// xor tree, so a row's results depend only on that row.
+// 4 KiB of the row (four 16-byte non-temporal loads per lane: the row is read once), i.e. 16
+// bf16 columns (16 lanes each) or 8 fp32 columns (32 lanes each), and the next step's loads
+// are issued before the current step is reduced.  Every reduction is a fixed in-lane order
+// followed by a fixed xor tree, so a row's results depend only on that row.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,6 +48,12 @@ __global__ __launch_bounds__(256) void logits_logp_kernel(LogitsArgs a) {
   const int J = (a.V + 127) / 128;
   float* cmax = col_stats;
   float* csum = col_stats + J;
+  // the target logit, requested first so that its latency hides behind the row's stream
+  float zy = 0.f;
+  if (threadIdx.x == 0) {
+    const int y = a.targets[t];
+    zy = (y >= 0 && y < a.V) ? logit_at<kBF16>(row, y) * a.inv_t : NAN;
+  }
 
   // 1. Column statistics.  Wave w takes column blocks w, w + 4, ... of kCols columns each;
   // the raw 16-byte loads of the next kUnroll blocks are in flight while the current ones are
@@ -59,7 +65,8 @@ __global__ __launch_bounds__(256) void logits_logp_kernel(LogitsArgs a) {
       const int j = jb + u * 4 * kCols + lane / kGroup;
       const int v0 = j * 128 + (lane % kGroup) * kPer;
       // v0 and ld are multiples of kPer, so the 16 bytes stay inside the row's ld entries
-      raw[u] = (j < J && v0 < a.V) ? *reinterpret_cast<const u32x4*>(row + (size_t)v0 * esize)
+      raw[u] = (j < J && v0 < a.V) ? __builtin_nontemporal_load(
+                                       reinterpret_cast<const u32x4*>(row + (size_t)v0 * esize))
                                    : u32x4{0u, 0u, 0u, 0u};
     }
   };
@@ -120,29 +127,42 @@ __global__ __launch_bounds__(256) void logits_logp_kernel(LogitsArgs a) {
   __syncthreads();
 
   // 2. The merge of the fused forward (fwd_merge_kernel), in the same association: slice
-  // sl = 0..7 walks columns sl, sl + 8, ... in ascending order; the 8 slice sums are added in
-  // one fixed tree.
+  // sl = 0..7 adds the columns sl, sl + 8, ... in ascending order, s = fma(sum_j, 2^(max_j -
+  // M), s), and the 8 slice sums are added in one fixed tree.  The maximum M (exact in any
+  // order) and the factors 2^(max_j - M) are formed by all threads; only the eight ordered
+  // sums run serially, with their LDS reads batched ahead of the chain.
   __shared__ float red[8];
-  const int sl = threadIdx.x;
   float m = -INFINITY;
-  if (sl < 8)
-    for (int j = sl; j < J; j += 8) m = fmaxf(m, cmax[j]);
-  if (sl < 8) red[sl] = m;
-  __syncthreads();
-  float M = red[0];
+  for (int j = threadIdx.x; j < J; j += 256) m = fmaxf(m, cmax[j]);
 #pragma unroll
-  for (int k = 1; k < 8; ++k) M = fmaxf(M, red[k]);
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red[wave] = m;
   __syncthreads();
-  float s = 0.f;
-  if (sl < 8)
-    for (int j = sl; j < J; j += 8) s += csum[j] * __builtin_amdgcn_exp2f(cmax[j] - M);
-  if (sl < 8) red[sl] = s;
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  for (int j = threadIdx.x; j < J; j += 256) cmax[j] = __builtin_amdgcn_exp2f(cmax[j] - M);
+  __syncthreads();
+  const int sl = threadIdx.x;
+  if (sl < 8) {
+    float s = 0.f;
+    int j = sl;
+    constexpr int kB = 8;  // columns per batch of LDS reads
+    for (; j + 8 * (kB - 1) < J; j += 8 * kB) {
+      float c[kB], e[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        c[u] = csum[j + 8 * u];
+        e[u] = cmax[j + 8 * u];
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) s = __builtin_fmaf(c[u], e[u], s);
+    }
+    for (; j < J; j += 8) s = __builtin_fmaf(csum[j], cmax[j], s);
+    red[sl] = s;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     const float S = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
     const float lse = (M + __builtin_amdgcn_logf(S)) * kLn2;
-    const int y = a.targets[t];
-    const float zy = (y >= 0 && y < a.V) ? logit_at<kBF16>(row, y) * a.inv_t : NAN;
     a.logp[t] = zy - lse;
     if (a.lse) a.lse[t] = lse;
   }
