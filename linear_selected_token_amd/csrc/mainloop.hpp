@@ -200,13 +200,15 @@ __device__ __forceinline__ void dma_panel(uint8_t* panel, const uint8_t* base, u
 #pragma unroll
     for (int q = q0; q < q0 + n; ++q) {
       const uint32_t m0 = lds0 + (uint32_t)((wave * kDmaPerWave + q) * 1024);
+      // M0 (the slot's LDS address) is an input bound to that register, so the compiler
+      // writes it and knows it is read; the s_nop is the wait state the hardware needs between
+      // a write of M0 and a load into LDS that uses it.
       asm volatile(
-          "s_mov_b32 m0, %0\n\t"
           "s_nop 0\n\t"
-          "buffer_load_dwordx4 %1, %2, 0 offen lds"
+          "buffer_load_dwordx4 %0, %1, 0 offen lds"
           :
-          : "s"(m0), "v"(off[q]), "s"(rs)
-          : "memory", "m0");
+          : "v"(off[q]), "s"(rs), "{m0}"(m0)
+          : "memory");
     }
   }
 }
