@@ -129,12 +129,17 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
     }
   };
 
+  // Per block, lane l < 32 holds the rows 8 g + 0..3 of group g and lane l + 32 the rows
+  // 8 g + 4..7 (same token).  v_permlane32_swap on the packed groups (2h, 2h + 1) hands lane
+  // l the rows 16 h + 0..7 and lane l + 32 the rows 16 h + 8..15, so each store writes 16 B
+  // per lane, 32 contiguous bytes per token row.
   auto epilogue = [&](const DlogitsCtx& c, Acc& acc) {
 #pragma unroll
     for (int j = 0; j < kBlkB; ++j) {
       const int ti = c.tok[j];
 #pragma unroll
-      for (int i = 0; i < kBlkA; ++i)
+      for (int i = 0; i < kBlkA; ++i) {
+        u32x2 pk[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float G[4];
@@ -151,14 +156,26 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
             }
             if (v >= a.V) G[e] = 0.f;
           }
-          const int vl = c.vbase - c0 + wv + acc_row(i, 4 * g, lane);  // first of 4 consecutive
-          u32x2 pk;
-          pk[0] = pack_bf16(G[0], G[1]);
-          pk[1] = pack_bf16(G[2], G[3]);
-          *reinterpret_cast<u32x2*>(a.Gv + (size_t)ti * kGvPitch + vl) = pk;
-          // one group of 4 rows at a time: keeps the live ranges short (no spills)
-          __builtin_amdgcn_sched_barrier(0);
+          pk[g][0] = pack_bf16(G[0], G[1]);
+          pk[g][1] = pack_bf16(G[2], G[3]);
         }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // lanes 32-63 of x trade places with lanes 0-31 of y:
+          // x' = [x lanes 0-31, y lanes 0-31], y' = [x lanes 32-63, y lanes 32-63]
+          const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * h][0], pk[2 * h + 1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * h][1], pk[2 * h + 1][1], false, false);
+          u32x4 q;
+          q.x = s0[0];
+          q.y = s1[0];
+          q.z = s0[1];
+          q.w = s1[1];
+          const int vl = c.vbase - c0 + wv + 32 * i + 16 * h + 8 * (lane >> 5);  // first of 8
+          *reinterpret_cast<u32x4*>(a.Gv + (size_t)ti * kGvPitch + vl) = q;
+        }
+        // one block at a time: keeps the live ranges short (no spills)
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
