@@ -133,28 +133,49 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
   // 8 g + 4..7 (same token).  v_permlane32_swap on the packed groups (2h, 2h + 1) hands lane
   // l the rows 16 h + 0..7 and lane l + 32 the rows 16 h + 8..15, so each store writes 16 B
   // per lane, 32 contiguous bytes per token row.
+  //
+  // Entry (i, r) of a block sits at row offset ro = 32 i + 8 (r >> 2) + (r & 3) from this
+  // lane's first row base.  Every entry takes the non-target form gs (0 - p); the rare
+  // blocks that hold some lane's target (a wave-uniform ballot) redo that entry with
+  // gs (1 - p), and in the quadrant that reaches past V the entries at ro >= V - base
+  // become 0, so the per-entry work is the exponential and one multiply.
   auto epilogue = [&](const DlogitsCtx& c, Acc& acc) {
+    const int base = c.vbase + wv + 4 * (lane >> 5);
+    const bool tail = __builtin_amdgcn_readfirstlane(c.vbase + wv + kWaveA > a.V ? 1 : 0) != 0;
+    const int lim = a.V - base;
 #pragma unroll
     for (int j = 0; j < kBlkB; ++j) {
       const int ti = c.tok[j];
+      const int dt = c.tgt[j] - base;  // row offset of the target (no entry matches if < 0)
+      auto gval = [&](float acc_v, float delta) __attribute__((always_inline)) {
+        const float x = acc_v * c2 - c.lse2[j];
+        const float p = __builtin_amdgcn_exp2f(x);
+        float G = c.gs[j] * (delta - p);
+        if constexpr (kEnt) {
+          // log p, clamped where p is 0 (underflow, padded columns) so that 0 * log p = 0
+          const float lp = fmaxf(x, -126.f) * kLn2;
+          G = __builtin_fmaf(c.bs[j] * p, lp + c.hn[j], G);
+        }
+        return G;
+      };
 #pragma unroll
       for (int i = 0; i < kBlkA; ++i) {
+        const bool hit = __builtin_amdgcn_ballot_w64(dt >= 32 * i && dt < 32 * i + 32) != 0;
         u32x2 pk[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float G[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            const int v = c.vbase + wv + acc_row(i, r, lane);
-            const float p = __builtin_amdgcn_exp2f(acc.c[i][j][r] * c2 - c.lse2[j]);
-            G[e] = c.gs[j] * ((v == c.tgt[j] ? 1.f : 0.f) - p);
-            if constexpr (kEnt) {
-              // log p, clamped where p is 0 (underflow, padded columns) so that 0 * log p = 0
-              const float lp = fmaxf(acc.c[i][j][r] * c2 - c.lse2[j], -126.f) * kLn2;
-              G[e] = __builtin_fmaf(c.bs[j] * p, lp + c.hn[j], G[e]);
-            }
-            if (v >= a.V) G[e] = 0.f;
+          for (int e = 0; e < 4; ++e) G[e] = gval(acc.c[i][j][4 * g + e], 0.f);
+          if (hit) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (32 * i + 8 * g + e == dt) G[e] = gval(acc.c[i][j][4 * g + e], 1.f);
+          }
+          if (tail) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (32 * i + 8 * g + e >= lim) G[e] = 0.f;
           }
           pk[g][0] = pack_bf16(G[0], G[1]);
           pk[g][1] = pack_bf16(G[2], G[3]);
