@@ -89,6 +89,7 @@ rlk_status_t run_bwd(const void* h, const void* W, const int32_t* targets, const
   a.dW = dW;
   a.hT = carve<uint16_t>(workspace, L.hT);
   a.Gv = carve<uint16_t>(workspace, L.Gv);
+  a.dh0 = carve<float>(workspace, L.dh0);
   a.dh1 = carve<float>(workspace, L.dh1);
   CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
   hipError_t e = launch_compact(c, st);
@@ -487,6 +488,7 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
   a.dW = dW_s;
   a.hT = carve<uint16_t>(workspace, L.hT);
   a.Gv = carve<uint16_t>(workspace, L.Gv);
+  a.dh0 = carve<float>(workspace, L.dh0);
   a.dh1 = carve<float>(workspace, L.dh1);
   float* xs = carve<float>(workspace, L.total);
   float* xt = carve<float>(workspace, L.total + kl_chunk_bytes(N));

@@ -16,15 +16,17 @@
 // The vocabulary is walked in chunks of kBwdChunk entries, in ascending order.  Per chunk:
 //   dlogits      the forward tile GEMM again, epilogue G = (g_t / T)(delta - p) rounded to
 //                bf16 and stored token-major (Gv);
-//   dh_chunk     Gv W[chunk] in two K halves of kDhSplitK entries each (fp32 accumulation;
-//                W rows are read as a K-strided panel, rows past V as zeros):
-//                the first half is added to dh[idx], the second to dh1 (compacted rows),
-//                both in chunk order; the halves are independent tiles, so a chunk
-//                fills the machine even when few tokens are active;
+//   dh_chunk     (Gv W[chunk])^T = W[chunk]^T Gv^T in two K halves of kDhSplitK entries each
+//                (fp32 accumulation): W is the first operand, read as a K-strided panel on
+//                the three-stage ring (rows past V as zeros), so the operand that streams
+//                from memory is the one loaded two stages ahead; a tile is 256 hidden
+//                columns x 256 tokens.  The first half is added to dh0, the second to dh1
+//                (both compacted rows), in chunk order; the halves are independent tiles,
+//                so a chunk fills the machine even when few tokens are active;
 //   dw_chunk     dW[chunk rows] = Gv^T hT^T  (K = the active tokens in ascending order; Gv
 //                is read as a K-strided panel).
-// Before the first chunk, bwd_prepare zeroes dh and dh1 and writes hT = compacted h
-// transposed; after the last, bwd_finish adds dh1 into dh.  The split point is a build
+// Before the first chunk, bwd_prepare zeroes dh, dh0 and dh1 and writes hT = compacted h
+// transposed; after the last, bwd_finish writes dh[idx[m]] = dh0[m] + dh1[m].  The split point is a build
 // constant, so a token's dh row is the same sum in the same order in every batch.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
 
 struct RowColCtx {
   int abase, bbase;  // first A row and first B row of the tile
-  int half;          // dh_chunk: which K half of the chunk (0: into dh, 1: into dh1)
+  int half;          // dh_chunk: which K half of the chunk (0: into dh0, 1: into dh1)
 };
 
 __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
@@ -219,67 +221,78 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nHTiles = a.H / kTile;
   const int per_half = nTokTiles * nHTiles;
-  const int band = nHTiles < 8 ? nHTiles : 8;
+  const int band = nTokTiles < 8 ? nTokTiles : 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const size_t row_bytes = (size_t)kGvPitch * 2;
+  const size_t g_row = (size_t)kGvPitch * 2;   // bytes per Gv row (one token)
   const uint32_t w_pitch = (uint32_t)a.H * 2;  // bytes per W row
   const int wa = wave_a0(wave);
   const int wb = wave_b0(wave);
 
+  // A = W[c0 + k0 ..][hidden columns abase ..] (K-strided), B = Gv rows of tokens bbase ..
   auto setup = [&](int u, TileSrc& src, RowColCtx& c) {
     const int half = u >= per_half ? 1 : 0;
-    int tt, ht;
-    tile_coords(u - half * per_half, nTokTiles, nHTiles, band, tt, ht);
-    c.abase = tt * kTile;
-    c.bbase = ht * kTile;
+    int ht, tt;
+    tile_coords(u - half * per_half, nHTiles, nTokTiles, band, ht, tt);
+    c.abase = ht * kTile;
+    c.bbase = tt * kTile;
     c.half = half;
     const int k0 = half * kDhSplitK;  // first K entry of this half
     const int k1 = half ? kc : min(kc, kDhSplitK);
     src.nk = (k1 - k0) * 2 / kKBytes;
-    src.a_kstep = kKBytes;
-    src.b_kstep = 64 * w_pitch;
-    src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)c.abase * row_bytes + 2 * k0);
+    src.a_kstep = 64 * w_pitch;  // 64 W rows per stage
+    src.b_kstep = kKBytes;
     // W rows c0 + k0 ... of this tile's 256 columns; rows past V read as zeros
     const size_t v0 = (size_t)c0 + k0;
-    src.b = uniform_ptr(static_cast<const uint8_t*>(a.W) + v0 * w_pitch + 2 * (size_t)c.bbase);
-    src.a_bytes = operand_bytes((size_t)(a.Npad - c.abase) * row_bytes - 2 * k0);
-    src.b_bytes = operand_bytes(((size_t)a.V - v0) * w_pitch - 2 * (size_t)c.bbase);
+    src.a = uniform_ptr(static_cast<const uint8_t*>(a.W) + v0 * w_pitch + 2 * (size_t)c.abase);
+    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)c.bbase * g_row + 2 * k0);
+    src.a_bytes = operand_bytes(((size_t)a.V - v0) * w_pitch - 2 * (size_t)c.abase);
+    src.b_bytes = operand_bytes((size_t)(a.Npad - c.bbase) * g_row - 2 * k0);
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
-      const int r = dma_row(q, wave, lane);
-      const int ch = dma_chunk(q, wave, lane);
-      src.ao[q] = (uint32_t)(r * row_bytes) + 16 * ch;
-      src.bo[q] = (uint32_t)(tdma_row(q, wave, lane) * w_pitch) + 16 * tdma_chunk(q, wave, lane);
+      src.ao[q] = (uint32_t)(tdma_row(q, wave, lane) * w_pitch) + 16 * tdma_chunk(q, wave, lane);
+      src.bo[q] = (uint32_t)(dma_row(q, wave, lane) * g_row) + 16 * dma_chunk(q, wave, lane);
     }
   };
 
+  // Accumulator rows are hidden columns, columns are tokens: a lane holds 4 consecutive
+  // hidden columns per register group, added into its token's compacted row 16 bytes at a
+  // time (dh0 / dh1 rows start 16-byte aligned: 256-byte aligned buffers, H % 256 == 0).
   auto epilogue = [&](const RowColCtx& c, Acc& acc) {
+    float* out = c.half ? a.dh1 : a.dh0;
 #pragma unroll
-    for (int i = 0; i < kBlkA; ++i)
+    for (int j = 0; j < kBlkB; ++j) {
+      const int m = c.bbase + wb + acc_col(j, lane);
+      if (m < Na) {
+        float* row = out + (size_t)m * a.H + c.abase + wa;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = c.abase + wa + acc_row(i, r, lane);
-        if (m < Na) {
-          float* row = c.half ? a.dh1 + (size_t)m * a.H + c.bbase + wb
-                              : a.dh + (size_t)a.idx[m] * a.H + c.bbase + wb;
+        for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
-          for (int j = 0; j < kBlkB; ++j) row[acc_col(j, lane)] += acc.c[i][j][r];
-        }
+          for (int g = 0; g < 4; ++g) {
+            f32x4* p = reinterpret_cast<f32x4*>(row + acc_row(i, 4 * g, lane));
+            f32x4 v = *p;
+            v.x += acc.c[i][j][4 * g + 0];
+            v.y += acc.c[i][j][4 * g + 1];
+            v.z += acc.c[i][j][4 * g + 2];
+            v.w += acc.c[i][j][4 * g + 3];
+            *p = v;
+          }
       }
+    }
   };
 
-  persistent_tiles<true, RowColCtx, false, true>(sm, per_half * nhalf, setup, epilogue);
+  persistent_tiles<true, RowColCtx, true, false>(sm, per_half * nhalf, setup, epilogue);
 }
 
-// dh[idx[m]] += dh1[m] for every active row m (dh is only 4-byte aligned: scalar accesses).
+// dh[idx[m]] = dh0[m] + dh1[m] for every active row m (dh is only 4-byte aligned: scalar
+// accesses).
 __global__ __launch_bounds__(256) void dh_finish_kernel(BwdArgs a) {
   const int Na = *a.n_active;
   const size_t n = (size_t)Na * a.H;
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
     const size_t m = e / a.H;
     const size_t k = e - m * a.H;
-    a.dh[(size_t)a.idx[m] * a.H + k] += a.dh1[e];
+    a.dh[(size_t)a.idx[m] * a.H + k] = a.dh0[e] + a.dh1[e];
   }
 }
 
@@ -350,6 +363,8 @@ hipError_t launch_zero(float* p, size_t n, hipStream_t stream) {
 
 hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = launch_zero(a.dh, (size_t)a.N * a.H, stream);
+  if (e != hipSuccess) return e;
+  e = launch_zero(a.dh0, (size_t)a.Npad * a.H, stream);
   if (e != hipSuccess) return e;
   e = launch_zero(a.dh1, (size_t)a.Npad * a.H, stream);
   if (e != hipSuccess) return e;

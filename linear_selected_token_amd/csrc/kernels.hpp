@@ -84,6 +84,7 @@ struct BwdArgs {
   float* dW;              // [V, H]
   uint16_t* hT;           // [H, Npad]   compacted h, transposed, zero past Na
   uint16_t* Gv;           // [Npad, kGvPitch] dL/dz of the chunk, token-major
+  float* dh0;             // [Npad, H] dL/dh from the first half of every chunk, compacted rows
   float* dh1;             // [Npad, H] dL/dh from the second half of every chunk, compacted rows
   // entropy bonus (both null without it): L gains -sum_t mask_t c_t H_t
   const float* ent_coef = nullptr;  // [N] c_t
@@ -102,6 +103,6 @@ hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream);          //
 hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t stream);
 // dL/dh and dL/dW of one chunk from a Gv written elsewhere
 hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, hipStream_t stream);
-hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);          // dh += dh1
+hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dh[idx] = dh0 + dh1
 
 }  // namespace rlk

@@ -107,9 +107,9 @@ constexpr int64_t kBwdChunkEntries = 32768;
 inline int64_t bwd_npad(int64_t N) { return ((N > 0 ? N : 1) + 255) / 256 * 256; }
 
 // Workspace layout of the backward: idx[N] | n_active | hT[H, Npad] | Gv[Npad, chunk] (bf16)
-// | dh1[Npad, H] (fp32).
+// | dh0[Npad, H] | dh1[Npad, H] (fp32).
 struct BwdLayout {
-  size_t idx, n_active, hT, Gv, dh1, total;
+  size_t idx, n_active, hT, Gv, dh0, dh1, total;
 };
 
 inline BwdLayout bwd_layout(int64_t N, int64_t H) {
@@ -122,6 +122,7 @@ inline BwdLayout bwd_layout(int64_t N, int64_t H) {
   L.n_active = o; o = align_up(o + 4, 256);
   L.hT = o;       o = align_up(o + 2 * (size_t)H * np, 256);
   L.Gv = o;       o = align_up(o + 2 * np * (c + 64), 256);  // rows of kGvPitch entries
+  L.dh0 = o;      o = align_up(o + 4 * np * (size_t)H, 256);
   L.dh1 = o;      o = align_up(o + 4 * np * (size_t)H, 256);
   L.total = o;
   return L;
