@@ -25,8 +25,9 @@
 //                so a chunk fills the machine even when few tokens are active;
 //   dw_chunk     dW[chunk rows] = Gv^T hT^T  (K = the active tokens in ascending order; Gv
 //                is read as a K-strided panel).
-// Before the first chunk, bwd_prepare zeroes dh, dh0 and dh1 and writes hT = compacted h
-// transposed; after the last, bwd_finish writes dh[idx[m]] = dh0[m] + dh1[m].  The split point is a build
+// Before the first chunk, bwd_prepare zeroes dh (its inactive rows stay 0) and writes hT =
+// compacted h transposed; the first chunk's dL/dh tiles store into dh0 / dh1 and later chunks
+// add to them; after the last, bwd_finish writes dh[idx[m]] = dh0[m] + dh1[m].  The split point is a build
 // constant, so a token's dh row is the same sum in the same order in every batch.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -42,24 +43,38 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// ---------------------------------------------------------------- 64 x 64 transposes
+// ---------------------------------------------------------------- transpose of the active h rows
 
-// hT[k][i] = h[idx[i]][k] for i < Na, 0 for Na <= i < Npad.  Grid (Npad/64, H/64).
+// hT[k][i] = h[idx[i]][k] for i < Na, 0 for Na <= i < Npad.  Grid (Npad / 64, H / 256), four
+// waves per work-group, each wave one 64-token x 64-column block.  Lane (tb, kb) = (lane & 7,
+// lane >> 3) loads 8 columns of 8 token rows as eight 16-byte vectors, transposes the 8 x 8
+// block of bf16 in registers and stores 8 hT rows of 8 tokens: both the loads and the stores
+// are 128 contiguous bytes per 8 lanes, with no LDS.
 __global__ __launch_bounds__(256) void transpose_h_kernel(BwdArgs a) {
-  __shared__ uint16_t t[64][65];
   const int Na = *a.n_active;
-  const int i0 = blockIdx.x * 64;
-  const int k0 = blockIdx.y * 64;
+  const int lane = threadIdx.x & 63;
+  const int tb = lane & 7, kb = lane >> 3;
+  const int i0 = blockIdx.x * 64 + 8 * tb;                        // first of this lane's tokens
+  const int k0 = blockIdx.y * 256 + (threadIdx.x >> 6) * 64 + 8 * kb;  // first of its columns
   const uint16_t* h = static_cast<const uint16_t*>(a.h);
-  for (int e = threadIdx.x; e < 4096; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    const int i = i0 + r;
-    t[r][c] = i < Na ? h[(size_t)a.idx[i] * a.H + k0 + c] : (uint16_t)0;
+  u32x4 in[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = i0 + q;
+    in[q] = u32x4{0u, 0u, 0u, 0u};
+    if (i < Na) in[q] = *reinterpret_cast<const u32x4*>(h + (size_t)a.idx[i] * a.H + k0);
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 4096; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    a.hT[(size_t)(k0 + r) * a.Npad + i0 + c] = t[c][r];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {  // column k0 + p: element p of every token's vector
+    const int sh = 16 * (p & 1);
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {  // tokens 2t (low half) and 2t + 1 (high half)
+      const uint32_t lo = (in[2 * t][p >> 1] >> sh) & 0xffffu;
+      const uint32_t hi = (in[2 * t + 1][p >> 1] >> sh) & 0xffffu;
+      w[t] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(a.hT + (size_t)(k0 + p) * a.Npad + i0) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -212,6 +227,8 @@ struct RowColCtx {
   int half;          // dh_chunk: which K half of the chunk (0: into dh0, 1: into dh1)
 };
 
+// kFirst: the first chunk, whose tiles store their sums (later chunks add to them).
+template <bool kFirst>
 __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
   __shared__ RingSmem sm;
   const int Na = *a.n_active;
@@ -270,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             f32x4* p = reinterpret_cast<f32x4*>(row + acc_row(i, 4 * g, lane));
-            f32x4 v = *p;
+            f32x4 v = kFirst ? f32x4{0.f, 0.f, 0.f, 0.f} : *p;
             v.x += acc.c[i][j][4 * g + 0];
             v.y += acc.c[i][j][4 * g + 1];
             v.z += acc.c[i][j][4 * g + 2];
@@ -284,15 +301,33 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
   persistent_tiles<true, RowColCtx, true, false>(sm, per_half * nhalf, setup, epilogue);
 }
 
-// dh[idx[m]] = dh0[m] + dh1[m] for every active row m (dh is only 4-byte aligned: scalar
-// accesses).
+// dh[idx[m]] = dh0[m] + dh1[m] for every active row m.  dh1 holds sums only when the first
+// chunk has a second K half (every later chunk that has one adds to them); otherwise nothing
+// wrote it and dh = dh0.  A work-group walks rows m = blockIdx.x, blockIdx.x + gridDim.x, ...;
+// its threads read 4 consecutive entries of dh0 / dh1 (16-byte aligned rows) and store them one
+// by one (dh is only 4-byte aligned).
+template <bool kTwo>
 __global__ __launch_bounds__(256) void dh_finish_kernel(BwdArgs a) {
   const int Na = *a.n_active;
-  const size_t n = (size_t)Na * a.H;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
-    const size_t m = e / a.H;
-    const size_t k = e - m * a.H;
-    a.dh[(size_t)a.idx[m] * a.H + k] = a.dh0[e] + a.dh1[e];
+  const int h4 = a.H / 4;
+  for (int m = blockIdx.x; m < Na; m += gridDim.x) {
+    const f32x4* r0 = reinterpret_cast<const f32x4*>(a.dh0 + (size_t)m * a.H);
+    const f32x4* r1 = reinterpret_cast<const f32x4*>(a.dh1 + (size_t)m * a.H);
+    float* out = a.dh + (size_t)a.idx[m] * a.H;
+    for (int k = threadIdx.x; k < h4; k += 256) {
+      f32x4 v = r0[k];
+      if constexpr (kTwo) {
+        const f32x4 w = r1[k];
+        v.x += w.x;
+        v.y += w.y;
+        v.z += w.z;
+        v.w += w.w;
+      }
+      out[4 * k + 0] = v.x;
+      out[4 * k + 1] = v.y;
+      out[4 * k + 2] = v.z;
+      out[4 * k + 3] = v.w;
+    }
   }
 }
 
@@ -364,11 +399,7 @@ hipError_t launch_zero(float* p, size_t n, hipStream_t stream) {
 hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = launch_zero(a.dh, (size_t)a.N * a.H, stream);
   if (e != hipSuccess) return e;
-  e = launch_zero(a.dh0, (size_t)a.Npad * a.H, stream);
-  if (e != hipSuccess) return e;
-  e = launch_zero(a.dh1, (size_t)a.Npad * a.H, stream);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(transpose_h_kernel, dim3(a.Npad / 64, a.H / 64), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(transpose_h_kernel, dim3(a.Npad / 64, a.H / 256), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -378,20 +409,30 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t s
     hipLaunchKernelGGL(dlogits_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   else
     hipLaunchKernelGGL(dlogits_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-  hipLaunchKernelGGL(dh_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  if (c0 == 0)
+    hipLaunchKernelGGL(dh_chunk_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  else
+    hipLaunchKernelGGL(dh_chunk_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   hipLaunchKernelGGL(dw_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, hipStream_t stream) {
   const int c0 = chunk * kBwdChunk;
-  hipLaunchKernelGGL(dh_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  if (c0 == 0)
+    hipLaunchKernelGGL(dh_chunk_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  else
+    hipLaunchKernelGGL(dh_chunk_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   hipLaunchKernelGGL(dw_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(dh_finish_kernel, dim3(2048), dim3(256), 0, stream, a);
+  const bool two = ((a.V < kBwdChunk ? a.V : kBwdChunk) + 63) / 64 * 64 > kDhSplitK;
+  if (two)
+    hipLaunchKernelGGL(dh_finish_kernel<true>, dim3(2048), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(dh_finish_kernel<false>, dim3(2048), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
