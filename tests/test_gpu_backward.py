@@ -51,6 +51,16 @@ def test_two_chunks_ragged():
                                          len_lo=100, len_hi=200, seed=96)))
 
 
+@pytest.mark.parametrize("dv", [0, 64, 3616])
+def test_one_chunk_around_dh_split(dv):
+    # one backward chunk whose vocabulary ends exactly at the dL/dh split point (one K half:
+    # the second-half buffer is never written), one 64-entry stage past it, and well past it
+    # (both halves stored by the first chunk's tiles)
+    _, split = _chunking()
+    _full_compare(wl.make(wl.scaled_spec(5, N=300, H=256, V=split + dv, n_seq=2, len_lo=100,
+                                         len_hi=200, seed=97)))
+
+
 def test_all_masked_backward():
     import linear_selected_token_amd as rlk
     w = wl.make(SMALL)
