@@ -27,8 +27,9 @@
 //                is read as a K-strided panel).
 // Before the first chunk, bwd_prepare zeroes dh (its inactive rows stay 0) and writes hT =
 // compacted h transposed; the first chunk's dL/dh tiles store into dh0 / dh1 and later chunks
-// add to them; after the last, bwd_finish writes dh[idx[m]] = dh0[m] + dh1[m].  The split point is a build
-// constant, so a token's dh row is the same sum in the same order in every batch.
+// add to them; after the last, bwd_finish writes dh[idx[m]] = dh0[m] + dh1[m].  The split
+// point is a build constant, so a token's dh row is the same sum in the same order in every
+// batch.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mainloop.hpp"
@@ -201,8 +202,10 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
         for (int h = 0; h < 2; ++h) {
           // lanes 32-63 of x trade places with lanes 0-31 of y:
           // x' = [x lanes 0-31, y lanes 0-31], y' = [x lanes 32-63, y lanes 32-63]
-          const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * h][0], pk[2 * h + 1][0], false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * h][1], pk[2 * h + 1][1], false, false);
+          const auto s0 =
+              __builtin_amdgcn_permlane32_swap(pk[2 * h][0], pk[2 * h + 1][0], false, false);
+          const auto s1 =
+              __builtin_amdgcn_permlane32_swap(pk[2 * h][1], pk[2 * h + 1][1], false, false);
           u32x4 q;
           q.x = s0[0];
           q.y = s1[0];
