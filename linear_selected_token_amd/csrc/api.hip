@@ -12,6 +12,9 @@
 #include "rlk.h"
 #include "validate.hpp"
 
+static_assert(rlk::kBwdChunkEntries == rlk::kBwdChunk && rlk::kBwdDhPieces == rlk::kDhPieces,
+              "host workspace layout and device chunking agree");
+
 namespace rlk {
 namespace {
 
@@ -46,7 +49,7 @@ const char* build_info_string() {
       "rlk linear_logp | arch gfx950 | compiler " __clang_version__
       " | tile 256x256, K stage 128 B, 8 wave64 x 128x64, mfma 32x32x16 bf16 / 32x32x2 f32"
       " | vocab partial 128 | merge 8 strided slices + fixed tree"
-      " | bwd chunk 32768, dh split at 16384";
+      " | bwd chunk 65536, dh split at 16384 (four pieces per chunk)";
   return s;
 }
 
@@ -89,8 +92,7 @@ rlk_status_t run_bwd(const void* h, const void* W, const int32_t* targets, const
   a.dW = dW;
   a.hT = carve<uint16_t>(workspace, L.hT);
   a.Gv = carve<uint16_t>(workspace, L.Gv);
-  a.dh0 = carve<float>(workspace, L.dh0);
-  a.dh1 = carve<float>(workspace, L.dh1);
+  for (int q = 0; q < kDhPieces; ++q) a.dhp[q] = carve<float>(workspace, L.dhp[q]);
   CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
   hipError_t e = launch_compact(c, st);
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
@@ -488,8 +490,7 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
   a.dW = dW_s;
   a.hT = carve<uint16_t>(workspace, L.hT);
   a.Gv = carve<uint16_t>(workspace, L.Gv);
-  a.dh0 = carve<float>(workspace, L.dh0);
-  a.dh1 = carve<float>(workspace, L.dh1);
+  for (int q = 0; q < kDhPieces; ++q) a.dhp[q] = carve<float>(workspace, L.dhp[q]);
   float* xs = carve<float>(workspace, L.total);
   float* xt = carve<float>(workspace, L.total + kl_chunk_bytes(N));
   KlArgs k{};

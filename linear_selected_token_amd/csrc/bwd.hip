@@ -16,20 +16,20 @@
 // The vocabulary is walked in chunks of kBwdChunk entries, in ascending order.  Per chunk:
 //   dlogits      the forward tile GEMM again, epilogue G = (g_t / T)(delta - p) rounded to
 //                bf16 and stored token-major (Gv);
-//   dh_chunk     (Gv W[chunk])^T = W[chunk]^T Gv^T in two K halves of kDhSplitK entries each
-//                (fp32 accumulation): W is the first operand, read as a K-strided panel on
-//                the three-stage ring (rows past V as zeros), so the operand that streams
-//                from memory is the one loaded two stages ahead; a tile is 256 hidden
-//                columns x 256 tokens.  The first half is added to dh0, the second to dh1
-//                (both compacted rows), in chunk order; the halves are independent tiles,
-//                so a chunk fills the machine even when few tokens are active;
+//   dh_chunk     (Gv W[chunk])^T = W[chunk]^T Gv^T in K pieces of kDhSplitK entries
+//                (fp32 accumulation; four per full chunk): W is the first operand, read as
+//                a K-strided panel on the three-stage ring (rows past V as zeros), so the
+//                operand that streams from memory is the one loaded two stages ahead; a tile
+//                is 256 hidden columns x 256 tokens.  Piece q is added to dhp[q] (compacted
+//                rows), in chunk order; the pieces are independent tiles, so a chunk fills the
+//                machine even when few tokens are active;
 //   dw_chunk     dW[chunk rows] = Gv^T hT^T  (K = the active tokens in ascending order; Gv
 //                is read as a K-strided panel).
 // Before the first chunk, bwd_prepare zeroes dh (its inactive rows stay 0) and writes hT =
-// compacted h transposed; the first chunk's dL/dh tiles store into dh0 / dh1 and later chunks
-// add to them; after the last, bwd_finish writes dh[idx[m]] = dh0[m] + dh1[m].  The split
-// point is a build constant, so a token's dh row is the same sum in the same order in every
-// batch.
+// compacted h transposed; the first chunk's dL/dh tiles store into the piece buffers and
+// later chunks add to them; after the last, bwd_finish writes dh[idx[m]] as the sum of the
+// pieces in ascending order.  The chunks and pieces are build constants, so a token's dh row
+// is the same sum in the same order in every batch.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mainloop.hpp"
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
 
 struct RowColCtx {
   int abase, bbase;  // first A row and first B row of the tile
-  int half;          // dh_chunk: which K half of the chunk (0: into dh0, 1: into dh1)
+  int piece;         // dh_chunk: which K piece of the chunk (into dhp[piece])
 };
 
 // kFirst: the first chunk, whose tiles store their sums (later chunks add to them).
@@ -237,10 +237,10 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
   const int Na = *a.n_active;
   const int vc = min(kBwdChunk, a.V - c0);
   const int kc = (vc + 63) & ~63;  // K extent (zero columns past V)
-  const int nhalf = kc > kDhSplitK ? 2 : 1;
+  const int npiece = (kc + kDhSplitK - 1) / kDhSplitK;
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nHTiles = a.H / kTile;
-  const int per_half = nTokTiles * nHTiles;
+  const int per_piece = nTokTiles * nHTiles;
   const int band = nTokTiles < 8 ? nTokTiles : 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -251,14 +251,14 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
 
   // A = W[c0 + k0 ..][hidden columns abase ..] (K-strided), B = Gv rows of tokens bbase ..
   auto setup = [&](int u, TileSrc& src, RowColCtx& c) {
-    const int half = u >= per_half ? 1 : 0;
+    const int piece = u / per_piece;
     int ht, tt;
-    tile_coords(u - half * per_half, nHTiles, nTokTiles, band, ht, tt);
+    tile_coords(u - piece * per_piece, nHTiles, nTokTiles, band, ht, tt);
     c.abase = ht * kTile;
     c.bbase = tt * kTile;
-    c.half = half;
-    const int k0 = half * kDhSplitK;  // first K entry of this half
-    const int k1 = half ? kc : min(kc, kDhSplitK);
+    c.piece = piece;
+    const int k0 = piece * kDhSplitK;  // K entries [k0, k1) of this piece
+    const int k1 = min(kc, k0 + kDhSplitK);
     src.nk = (k1 - k0) * 2 / kKBytes;
     src.a_kstep = 64 * w_pitch;  // 64 W rows per stage
     src.b_kstep = kKBytes;
@@ -277,9 +277,10 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
 
   // Accumulator rows are hidden columns, columns are tokens: a lane holds 4 consecutive
   // hidden columns per register group, added into its token's compacted row 16 bytes at a
-  // time (dh0 / dh1 rows start 16-byte aligned: 256-byte aligned buffers, H % 256 == 0).
+  // time (dhp rows start 16-byte aligned: 256-byte aligned buffers, H % 256 == 0).
   auto epilogue = [&](const RowColCtx& c, Acc& acc) {
-    float* out = c.half ? a.dh1 : a.dh0;
+    static_assert(kDhPieces == 4, "piece buffers");
+    float* out = c.piece == 0 ? a.dhp[0] : c.piece == 1 ? a.dhp[1] : c.piece == 2 ? a.dhp[2] : a.dhp[3];
 #pragma unroll
     for (int j = 0; j < kBlkB; ++j) {
       const int m = c.bbase + wb + acc_col(j, lane);
@@ -301,26 +302,25 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
     }
   };
 
-  persistent_tiles<true, RowColCtx, true, false>(sm, per_half * nhalf, setup, epilogue);
+  persistent_tiles<true, RowColCtx, true, false>(sm, per_piece * npiece, setup, epilogue);
 }
 
-// dh[idx[m]] = dh0[m] + dh1[m] for every active row m.  dh1 holds sums only when the first
-// chunk has a second K half (every later chunk that has one adds to them); otherwise nothing
-// wrote it and dh = dh0.  A work-group walks rows m = blockIdx.x, blockIdx.x + gridDim.x, ...;
-// its threads read 4 consecutive entries of dh0 / dh1 (16-byte aligned rows) and store them one
-// by one (dh is only 4-byte aligned).
-template <bool kTwo>
+// dh[idx[m]] = ((dhp[0][m] + dhp[1][m]) + dhp[2][m]) + dhp[3][m] over the kP pieces the first
+// chunk has (every later chunk has at most as many, and adds to them; the others were never
+// written).  A work-group walks rows m = blockIdx.x, blockIdx.x + gridDim.x, ...; its threads
+// read 4 consecutive entries of each piece (16-byte aligned rows) and store them one by one
+// (dh is only 4-byte aligned).
+template <int kP>
 __global__ __launch_bounds__(256) void dh_finish_kernel(BwdArgs a) {
   const int Na = *a.n_active;
   const int h4 = a.H / 4;
   for (int m = blockIdx.x; m < Na; m += gridDim.x) {
-    const f32x4* r0 = reinterpret_cast<const f32x4*>(a.dh0 + (size_t)m * a.H);
-    const f32x4* r1 = reinterpret_cast<const f32x4*>(a.dh1 + (size_t)m * a.H);
     float* out = a.dh + (size_t)a.idx[m] * a.H;
     for (int k = threadIdx.x; k < h4; k += 256) {
-      f32x4 v = r0[k];
-      if constexpr (kTwo) {
-        const f32x4 w = r1[k];
+      f32x4 v = reinterpret_cast<const f32x4*>(a.dhp[0] + (size_t)m * a.H)[k];
+#pragma unroll
+      for (int q = 1; q < kP; ++q) {
+        const f32x4 w = reinterpret_cast<const f32x4*>(a.dhp[q] + (size_t)m * a.H)[k];
         v.x += w.x;
         v.y += w.y;
         v.z += w.z;
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
     tile_coords(u, nVocTiles, nHTiles, band, vt, ht);
     c.abase = vt * kTile;  // within the chunk
     c.bbase = ht * kTile;
-    c.half = 0;
+    c.piece = 0;
     src.nk = nk;
     src.a_kstep = 64 * g_pitch;  // 64 token rows of Gv per stage
     src.b_kstep = kKBytes;
@@ -431,11 +431,13 @@ hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, hipStre
 }
 
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {
-  const bool two = ((a.V < kBwdChunk ? a.V : kBwdChunk) + 63) / 64 * 64 > kDhSplitK;
-  if (two)
-    hipLaunchKernelGGL(dh_finish_kernel<true>, dim3(2048), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(dh_finish_kernel<false>, dim3(2048), dim3(256), 0, stream, a);
+  const int kc0 = ((a.V < kBwdChunk ? a.V : kBwdChunk) + 63) / 64 * 64;  // first chunk's K extent
+  switch ((kc0 + kDhSplitK - 1) / kDhSplitK) {
+    case 1: hipLaunchKernelGGL(dh_finish_kernel<1>, dim3(2048), dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(dh_finish_kernel<2>, dim3(2048), dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(dh_finish_kernel<3>, dim3(2048), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(dh_finish_kernel<4>, dim3(2048), dim3(256), 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

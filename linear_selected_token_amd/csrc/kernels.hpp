@@ -7,8 +7,9 @@
 namespace rlk {
 
 constexpr int kVocabPartial = 128;  // vocabulary entries per partial-statistics column
-constexpr int kBwdChunk = 32768;    // vocabulary entries per backward chunk (build constant)
-constexpr int kDhSplitK = 16384;    // dL/dh sums each chunk's first and second 16384 entries apart
+constexpr int kBwdChunk = 65536;    // vocabulary entries per backward chunk (build constant)
+constexpr int kDhSplitK = 16384;    // dL/dh sums each 16384-entry piece of a chunk apart
+constexpr int kDhPieces = kBwdChunk / kDhSplitK;  // pieces of a full chunk (4)
 // Row pitch (entries) of the token-major chunk buffers: the chunk plus 128 bytes, so that the
 // rows a wave writes at once (32 tokens) do not all start at the same 64 KiB-aligned offset.
 constexpr int kGvPitch = kBwdChunk + 64;  // bf16 dL/dz
@@ -84,8 +85,7 @@ struct BwdArgs {
   float* dW;              // [V, H]
   uint16_t* hT;           // [H, Npad]   compacted h, transposed, zero past Na
   uint16_t* Gv;           // [Npad, kGvPitch] dL/dz of the chunk, token-major
-  float* dh0;             // [Npad, H] dL/dh from the first half of every chunk, compacted rows
-  float* dh1;             // [Npad, H] dL/dh from the second half of every chunk, compacted rows
+  float* dhp[kDhPieces];  // [Npad, H] each: dL/dh from piece q of every chunk, compacted rows
   // entropy bonus (both null without it): L gains -sum_t mask_t c_t H_t
   const float* ent_coef = nullptr;  // [N] c_t
   const float* entropy = nullptr;   // [N] H_t from the entropy forward
@@ -103,6 +103,6 @@ hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream);          //
 hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t stream);
 // dL/dh and dL/dW of one chunk from a Gv written elsewhere
 hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, hipStream_t stream);
-hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dh[idx] = dh0 + dh1
+hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dh[idx] = sum of pieces
 
 }  // namespace rlk

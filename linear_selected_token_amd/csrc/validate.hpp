@@ -102,14 +102,15 @@ inline DiagLayout diag_layout(int64_t N) {
   return L;
 }
 
-constexpr int64_t kBwdChunkEntries = 32768;
+constexpr int64_t kBwdChunkEntries = 65536;
+constexpr int kBwdDhPieces = 4;  // dL/dh pieces of a full chunk (16384 entries each)
 
 inline int64_t bwd_npad(int64_t N) { return ((N > 0 ? N : 1) + 255) / 256 * 256; }
 
 // Workspace layout of the backward: idx[N] | n_active | hT[H, Npad] | Gv[Npad, chunk] (bf16)
-// | dh0[Npad, H] | dh1[Npad, H] (fp32).
+// | dhp[4][Npad, H] (fp32).
 struct BwdLayout {
-  size_t idx, n_active, hT, Gv, dh0, dh1, total;
+  size_t idx, n_active, hT, Gv, dhp[kBwdDhPieces], total;
 };
 
 inline BwdLayout bwd_layout(int64_t N, int64_t H) {
@@ -122,8 +123,10 @@ inline BwdLayout bwd_layout(int64_t N, int64_t H) {
   L.n_active = o; o = align_up(o + 4, 256);
   L.hT = o;       o = align_up(o + 2 * (size_t)H * np, 256);
   L.Gv = o;       o = align_up(o + 2 * np * (c + 64), 256);  // rows of kGvPitch entries
-  L.dh0 = o;      o = align_up(o + 4 * np * (size_t)H, 256);
-  L.dh1 = o;      o = align_up(o + 4 * np * (size_t)H, 256);
+  for (int q = 0; q < kBwdDhPieces; ++q) {
+    L.dhp[q] = o;
+    o = align_up(o + 4 * np * (size_t)H, 256);
+  }
   L.total = o;
   return L;
 }

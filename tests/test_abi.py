@@ -303,8 +303,10 @@ def test_kl_argument_errors(L):
     assert fwd(T=0.0) == E.RLK_ERROR_INVALID_VALUE
     assert fwd(wsb=1000) == E.RLK_ERROR_WORKSPACE
     st, b = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 16384, 4096, 2048, 151936, 0)
-    # six [J][N] statistics plus two fp32 chunks of [N rounded to 256] x 32768
-    assert st == 0 and b >= 6 * 4 * 16384 * 1187 + 2 * 4 * 16384 * 32768
+    # six [J][N] statistics plus two fp32 chunks of [N rounded to 256] x (chunk entries)
+    import re
+    chunk = int(re.search(r"bwd chunk (\d+)", lib.rlk_build_info().decode()).group(1))
+    assert st == 0 and b >= 6 * 4 * 16384 * 1187 + 2 * 4 * 16384 * chunk
 
     def bwd(Hs=256, dt=0, rev=0, kr=FAKE, coef=FAKE, wsb=1 << 40):
         return lib.rlk_linear_kl_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 8, Hs, 64, 1000, dt, 1.0, rev,

@@ -91,13 +91,23 @@ def test_small_full_close_heads():
     assert (kf[act] < 0.05).all()
 
 
+def _chunk():
+    """Vocabulary entries per backward / KL chunk of the loaded build."""
+    import re
+    import linear_selected_token_amd as rlk
+    m = re.search(r"bwd chunk (\d+), dh split at (\d+)", rlk.build_info())
+    assert m, rlk.build_info()
+    return int(m.group(1)), int(m.group(2))
+
+
 def test_fp32_ragged_and_two_chunks():
     w = wl.make(wl.scaled_spec(1, N=200, H=128, V=777, n_seq=2, len_lo=50, len_hi=150,
                                prompt="floor_half", seed=114, T=1.2))
     ht, Wt = _teacher(w, 64, 115)
     _check_fwd(w, ht, Wt, tol=1e-4)
     # two vocabulary chunks, the second ragged
-    w2 = wl.make(wl.scaled_spec(2, N=260, H=256, V=32768 + 300, n_seq=2, len_lo=100,
+    chunk, _ = _chunk()
+    w2 = wl.make(wl.scaled_spec(2, N=260, H=256, V=chunk + 300, n_seq=2, len_lo=100,
                                 len_hi=200, seed=116))
     ht2, Wt2 = _teacher(w2, 192, 117)
     _check_fwd(w2, ht2, Wt2)
@@ -158,7 +168,8 @@ def test_bwd_small_full(reverse):
 
 
 def test_bwd_two_chunks_and_dh_invariance():
-    w = wl.make(wl.scaled_spec(5, N=260, H=256, V=32768 + 16384 + 300, n_seq=2, len_lo=100,
+    chunk, split = _chunk()
+    w = wl.make(wl.scaled_spec(5, N=260, H=256, V=chunk + split + 300, n_seq=2, len_lo=100,
                                len_hi=200, seed=125))
     ht, Wt = _teacher(w, 128, 126)
     c = np.random.default_rng(127).uniform(0.5, 1.5, w.N).astype(np.float32)
