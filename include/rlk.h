@@ -202,8 +202,8 @@ rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int
  *   z_s = h_s W_s^T / T, z_t = h_t W_t^T / T, p = softmax(z)
  *   kl_fwd[t] = sum_v p_t (log p_t - log p_s),  kl_rev[t] = sum_v p_s (log p_s - log p_t)
  * at active tokens, 0 elsewhere (both clamped at 0 against rounding).  The vocabulary is walked
- * in chunks of 32768 entries: per chunk each head's tile GEMM writes its column statistics
- * and its logits of that chunk only (fp32, [N rounded up to 256] x 32768 in the workspace),
+ * in chunks of 65536 entries: per chunk each head's tile GEMM writes its column statistics
+ * and its logits of that chunk only (fp32, [N rounded up to 256] x 65536 in the workspace),
  * a streaming kernel pairs the two entry by entry, and a fixed-order merge gives the results.
  * Batch-invariant like logp.  H_s and H_t: multiples of 64; each h at most 2^31 - 1 bytes.
  *   lse_s, lse_t [N] float     out (may be NULL): each head's log-sum-exp, which the backward
