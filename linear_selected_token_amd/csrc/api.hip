@@ -93,6 +93,7 @@ rlk_status_t run_bwd(const void* h, const void* W, const int32_t* targets, const
   a.hT = carve<uint16_t>(workspace, L.hT);
   a.Gv = carve<uint16_t>(workspace, L.Gv);
   for (int q = 0; q < kDhPieces; ++q) a.dhp[q] = carve<float>(workspace, L.dhp[q]);
+  a.sched = carve<int>(workspace, L.sched);
   CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
   hipError_t e = launch_compact(c, st);
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
@@ -491,6 +492,7 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
   a.hT = carve<uint16_t>(workspace, L.hT);
   a.Gv = carve<uint16_t>(workspace, L.Gv);
   for (int q = 0; q < kDhPieces; ++q) a.dhp[q] = carve<float>(workspace, L.dhp[q]);
+  a.sched = carve<int>(workspace, L.sched);
   float* xs = carve<float>(workspace, L.total);
   float* xt = carve<float>(workspace, L.total + kl_chunk_bytes(N));
   KlArgs k{};

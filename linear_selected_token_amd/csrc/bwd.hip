@@ -25,6 +25,8 @@
 //                machine even when few tokens are active;
 //   dw_chunk     dW[chunk rows] = Gv^T hT^T  (K = the active tokens in ascending order; Gv
 //                is read as a K-strided panel).
+// dh_chunk and dw_chunk run as the two sections of one launch (grad_chunk_kernel): the
+// dL/dW tiles are claimed at run time, so they fill the last round of dL/dh tiles.
 // Before the first chunk, bwd_prepare zeroes dh (its inactive rows stay 0) and writes hT =
 // compacted h transposed; the first chunk's dL/dh tiles store into the piece buffers and
 // later chunks add to them; after the last, bwd_finish writes dh[idx[m]] as the sum of the
@@ -231,9 +233,10 @@ struct RowColCtx {
 };
 
 // kFirst: the first chunk, whose tiles store their sums (later chunks add to them).
-template <bool kFirst>
-__global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
-  __shared__ RingSmem sm;
+// kSpread: a last, partial round of tiles is dealt out across the XCDs (for the combined
+// launch, whose work-groups go on to claim dL/dW tiles from their XCD's counter).
+template <bool kFirst, bool kSpread>
+__device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, int c0) {
   const int Na = *a.n_active;
   const int vc = min(kBwdChunk, a.V - c0);
   const int kc = (vc + 63) & ~63;  // K extent (zero columns past V)
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
     }
   };
 
-  persistent_tiles<true, RowColCtx, true, false>(sm, per_piece * npiece, setup, epilogue);
+  persistent_tiles<true, RowColCtx, true, false, kSpread>(sm, per_piece * npiece, setup, epilogue);
 }
 
 // dh[idx[m]] = ((dhp[0][m] + dhp[1][m]) + dhp[2][m]) + dhp[3][m] over the kP pieces the first
@@ -336,8 +339,10 @@ __global__ __launch_bounds__(256) void dh_finish_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dW rows = Gv^T hT^T
 
-__global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
-  __shared__ RingSmem sm;
+// kClaimed: tiles claimed from the XCD counters in a.sched (claimed_tiles) instead of the fixed
+// order.
+template <bool kClaimed>
+__device__ __forceinline__ void dw_chunk_tiles(RingSmem& sm, const BwdArgs& a, int c0) {
   const int Na = *a.n_active;
   const int vc = min(kBwdChunk, a.V - c0);
   const int nVocTiles = (vc + kTile - 1) / kTile;
@@ -387,7 +392,34 @@ __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
       }
   };
 
-  persistent_tiles<true, RowColCtx, true, false>(sm, nVocTiles * nHTiles, setup, epilogue);
+  if constexpr (kClaimed)
+    claimed_tiles<true, RowColCtx, true, false>(sm, nVocTiles * nHTiles, a.sched, setup, epilogue);
+  else
+    persistent_tiles<true, RowColCtx, true, false>(sm, nVocTiles * nHTiles, setup, epilogue);
+}
+
+template <bool kFirst>
+__global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
+  __shared__ RingSmem sm;
+  dh_chunk_tiles<kFirst, false>(sm, a, c0);
+}
+
+__global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
+  __shared__ RingSmem sm;
+  dw_chunk_tiles<false>(sm, a, c0);
+}
+
+// Both GEMMs of a chunk in one launch: each work-group first takes its dL/dh tiles in the
+// fixed order (a partial last round spread over the XCDs), then claims dL/dW tiles
+// (claim_tile) until none are left, so the work-groups that got one dL/dh tile fewer fill the
+// last round of dL/dh with dL/dW tiles.  The two are independent (both read Gv; dL/dh writes
+// dhp, dL/dW writes dW), and which work-group computes a tile changes no result: the
+// separate launches give the same bits.
+template <bool kFirst>
+__global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, int c0) {
+  __shared__ RingSmem sm;
+  dh_chunk_tiles<kFirst, true>(sm, a, c0);
+  dw_chunk_tiles<true>(sm, a, c0);
 }
 
 }  // namespace
@@ -406,28 +438,43 @@ hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The combined launch for batches of at most this many tokens.  There the GEMMs have few
+// tiles per chunk (at 2053 active tokens, 576 dL/dh tiles: 2.25 rounds of 256 work-groups)
+// and the combined launch made the backward 6% faster; at 16384 tokens (9831 active) it was
+// ~1% slower than two launches: the chip is at its power limit there, and dL/dW tiles started
+// at staggered times share fewer L2 panels.  A scheduling choice only: the bits are the same.
+constexpr int64_t kCombinedMaxTokens = 4096;
+
+static hipError_t launch_grad_chunk(const BwdArgs& a, int c0, int grid, hipStream_t stream) {
+  if (a.N <= kCombinedMaxTokens) {
+    hipError_t e = launch_zero(reinterpret_cast<float*>(a.sched), 8, stream);  // claim counters
+    if (e != hipSuccess) return e;
+    if (c0 == 0)
+      hipLaunchKernelGGL(grad_chunk_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+    else
+      hipLaunchKernelGGL(grad_chunk_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  } else {
+    if (c0 == 0)
+      hipLaunchKernelGGL(dh_chunk_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+    else
+      hipLaunchKernelGGL(dh_chunk_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+    hipLaunchKernelGGL(dw_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t stream) {
   const int c0 = chunk * kBwdChunk;
   if (a.ent_coef)
     hipLaunchKernelGGL(dlogits_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   else
     hipLaunchKernelGGL(dlogits_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-  if (c0 == 0)
-    hipLaunchKernelGGL(dh_chunk_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-  else
-    hipLaunchKernelGGL(dh_chunk_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-  hipLaunchKernelGGL(dw_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-  return hipGetLastError();
+  return launch_grad_chunk(a, c0, grid, stream);
 }
 
 hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, hipStream_t stream) {
   const int c0 = chunk * kBwdChunk;
-  if (c0 == 0)
-    hipLaunchKernelGGL(dh_chunk_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-  else
-    hipLaunchKernelGGL(dh_chunk_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-  hipLaunchKernelGGL(dw_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-  return hipGetLastError();
+  return launch_grad_chunk(a, c0, grid, stream);
 }
 
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {

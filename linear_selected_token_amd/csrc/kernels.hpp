@@ -86,6 +86,7 @@ struct BwdArgs {
   uint16_t* hT;           // [H, Npad]   compacted h, transposed, zero past Na
   uint16_t* Gv;           // [Npad, kGvPitch] dL/dz of the chunk, token-major
   float* dhp[kDhPieces];  // [Npad, H] each: dL/dh from piece q of every chunk, compacted rows
+  int* sched;             // [8] tile-claim counters of the dL/dW section (zeroed per launch)
   // entropy bonus (both null without it): L gains -sum_t mask_t c_t H_t
   const float* ent_coef = nullptr;  // [N] c_t
   const float* entropy = nullptr;   // [N] H_t from the entropy forward

@@ -358,16 +358,31 @@ __device__ __forceinline__ void ring_mainloop(RingSmem& sm, const TileSrc& t, in
   slice(a1, b1, false, 0, 0, a0, b0, 0, no_dma);
 }
 
+// virtual_tile, except that a last, partial round (fewer than grid tiles left) is dealt out
+// across the XCDs: tile round * grid + b, and work-group b runs on XCD b % 8.  Each XCD then
+// gets its share of that round, which matters when the work-groups go on to other work.
+__device__ __forceinline__ int virtual_tile_spread(int round, int b, int grid, int n_tiles) {
+  if ((round + 1) * grid > n_tiles) return round * grid + b;
+  return virtual_tile(round, b, grid);
+}
+
 // Persistent tile driver.  Tiles u = virtual_tile(round, blockIdx.x, gridDim.x) for
 // round = 0, 1, ... while u < n_tiles.  setup(u, src, ctx) prepares a tile's load sources
 // (including its number of K stages) and its epilogue context; epilogue(ctx, acc) consumes
 // the accumulators (registers and global memory only, no LDS).  The next tile's first
 // loads are issued before the current tile's epilogue, so their latency hides behind it.
-template <bool kBF16, class Ctx, bool kTA = false, bool kTB = false, class Setup, class Epilogue>
+//
+// kSpreadTail: the last, partial round is dealt out across the XCDs (virtual_tile_spread).
+template <bool kBF16, class Ctx, bool kTA = false, bool kTB = false, bool kSpreadTail = false,
+          class Setup, class Epilogue>
 __device__ __forceinline__ void persistent_tiles(RingSmem& sm, int n_tiles, Setup setup,
                                                  Epilogue epilogue) {
+  auto tile_of = [&](int round) __attribute__((always_inline)) {
+    return kSpreadTail ? virtual_tile_spread(round, blockIdx.x, gridDim.x, n_tiles)
+                       : virtual_tile(round, blockIdx.x, gridDim.x);
+  };
   int round = 0;
-  int u = virtual_tile(round, blockIdx.x, gridDim.x);
+  int u = tile_of(round);
   if (u >= n_tiles) return;
   TileSrc src;
   Ctx ctx;
@@ -377,7 +392,67 @@ __device__ __forceinline__ void persistent_tiles(RingSmem& sm, int n_tiles, Setu
     Acc acc;
     zero_acc(acc);
     ring_mainloop<kBF16, kTA, kTB>(sm, src, src.nk, acc);
-    const int un = virtual_tile(++round, blockIdx.x, gridDim.x);
+    const int un = tile_of(++round);
+    const bool more = un < n_tiles;
+    Ctx cur = ctx;
+    if (more) {
+      setup(un, src, ctx);
+      ring_prologue<kTA || kTB>(sm, src, src.nk);
+    }
+    epilogue(cur, acc);
+    if (!more) break;
+  }
+}
+
+// Tiles claimed at run time instead of by a fixed rule.  The work-group's XCD x = blockIdx.x & 7
+// hands out claim numbers i = 0, 1, ... from counter[x] (one atomic add per tile, by one
+// lane); claim i is virtual tile (i / per) * grid + x * per + i % per with per = grid / 8, and
+// past the full rounds tile full * grid + 8 (i - full * per) + x: the tiles
+// virtual_tile_spread gives XCD x, in the same order.  So the tiles in flight on an XCD are
+// still the ones that share its L2, while work-groups that finished earlier work sooner take
+// more of them.  Every claim number is handed out once and an XCD's tiles increase with it, so
+// each tile below n_tiles is computed exactly once and a work-group stops at its first claim
+// past n_tiles.  The claim is broadcast through the first word of the A ring while the ring is
+// idle (every wave has passed the barrier after its last fragment read and no load into LDS is
+// in flight); the counters must be zero when the launch starts.
+__device__ __forceinline__ int claim_tile(RingSmem& sm, int* counter, int n_tiles) {
+  int* slot = reinterpret_cast<int*>(sm.a[0]);
+  if (threadIdx.x == 0) {
+    const int grid = gridDim.x;
+    int u;
+    if ((grid & 7) == 0) {
+      const int x = blockIdx.x & 7;
+      const int per = grid >> 3;
+      const int full = n_tiles / grid;  // full rounds
+      const int i = atomicAdd(counter + x, 1);
+      u = i < full * per ? (i / per) * grid + x * per + i % per
+                         : full * grid + 8 * (i - full * per) + x;
+    } else {
+      u = atomicAdd(counter, 1);
+    }
+    *slot = u;
+  }
+  __syncthreads();
+  const int u = __builtin_amdgcn_readfirstlane(*slot);
+  __syncthreads();  // every wave has read the slot before it is written or loaded into again
+  return u;
+}
+
+// persistent_tiles with claimed tiles (see claim_tile); the same setup / epilogue contract.
+template <bool kBF16, class Ctx, bool kTA = false, bool kTB = false, class Setup, class Epilogue>
+__device__ __forceinline__ void claimed_tiles(RingSmem& sm, int n_tiles, int* counter, Setup setup,
+                                              Epilogue epilogue) {
+  int u = claim_tile(sm, counter, n_tiles);
+  if (u >= n_tiles) return;
+  TileSrc src;
+  Ctx ctx;
+  setup(u, src, ctx);
+  ring_prologue<kTA || kTB>(sm, src, src.nk);
+  while (true) {
+    Acc acc;
+    zero_acc(acc);
+    ring_mainloop<kBF16, kTA, kTB>(sm, src, src.nk, acc);
+    const int un = claim_tile(sm, counter, n_tiles);
     const bool more = un < n_tiles;
     Ctx cur = ctx;
     if (more) {

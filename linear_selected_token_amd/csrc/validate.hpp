@@ -107,10 +107,10 @@ constexpr int kBwdDhPieces = 4;  // dL/dh pieces of a full chunk (16384 entries 
 
 inline int64_t bwd_npad(int64_t N) { return ((N > 0 ? N : 1) + 255) / 256 * 256; }
 
-// Workspace layout of the backward: idx[N] | n_active | hT[H, Npad] | Gv[Npad, chunk] (bf16)
+// Workspace layout of the backward: idx[N] | n_active | sched[8] | hT[H, Npad] | Gv[Npad, chunk] (bf16)
 // | dhp[4][Npad, H] (fp32).
 struct BwdLayout {
-  size_t idx, n_active, hT, Gv, dhp[kBwdDhPieces], total;
+  size_t idx, n_active, sched, hT, Gv, dhp[kBwdDhPieces], total;
 };
 
 inline BwdLayout bwd_layout(int64_t N, int64_t H) {
@@ -121,6 +121,7 @@ inline BwdLayout bwd_layout(int64_t N, int64_t H) {
   size_t o = 0;
   L.idx = o;      o = align_up(o + 4 * n, 256);
   L.n_active = o; o = align_up(o + 4, 256);
+  L.sched = o;    o = align_up(o + 4 * 8, 256);
   L.hT = o;       o = align_up(o + 2 * (size_t)H * np, 256);
   L.Gv = o;       o = align_up(o + 2 * np * (c + 64), 256);  // rows of kGvPitch entries
   for (int q = 0; q < kBwdDhPieces; ++q) {
