@@ -61,6 +61,34 @@ def test_one_chunk_around_dh_split(dv):
                                          len_hi=200, seed=97)))
 
 
+def test_schedules_agree_across_4096_tokens():
+    # Batches of up to 4096 tokens run dL/dh and dL/dW of a chunk as one launch with claimed
+    # tiles, larger ones as two launches in a fixed order.  The same tokens with 8 inactive
+    # padding rows appended (4104 tokens) take the other schedule; every active dL/dh row and
+    # all of dL/dW keep their bits (dL/dW sums the active tokens in the same order).
+    import dataclasses
+    w = wl.make(wl.scaled_spec(5, N=4096, H=256, V=70000, n_seq=16, len_lo=64, len_hi=512,
+                               seed=131))
+    pad = 8
+    w2 = dataclasses.replace(
+        w, h=np.concatenate([w.h, w.h[:pad]]),
+        targets=np.concatenate([w.targets, np.zeros(pad, np.int32)]),
+        mask=np.concatenate([w.mask, np.zeros(pad, np.uint8)]),
+        adv=np.concatenate([w.adv, np.zeros(pad, np.float32)]),
+        u=np.concatenate([w.u, np.zeros(pad)]),
+        seq_id=np.concatenate([w.seq_id, np.full(pad, -1, np.int32)]),
+        pos=np.concatenate([w.pos, np.zeros(pad, np.int32)]))
+    _, _, dh1, dW1 = run_bwd(w)
+    _, _, dh2, dW2 = run_bwd(w2)
+    act = w.mask.astype(bool)
+    dh1 = dh1.cpu().numpy()
+    dh2 = dh2.cpu().numpy()[:w.N]
+    flush(f"  N={w.N} vs {w2.N}, {int(act.sum())} active, V={w.V}")
+    assert np.array_equal(bits(dh1[act]), bits(dh2[act]))
+    assert not dh2[~act].any()
+    assert np.array_equal(bits(dW1.cpu().numpy()), bits(dW2.cpu().numpy()))
+
+
 def test_all_masked_backward():
     import linear_selected_token_amd as rlk
     w = wl.make(SMALL)
