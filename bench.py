@@ -29,10 +29,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "active tokens/sec + % bf16 MFMA peak, fused linear logp fwd (and fwd+bwd)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 WORKLOADS = {
     # name: (config id, use stored sampled targets)
+    "tiny-fp32-N64-H256-V1000": (1, False),
     "qwen3-8b-head-N16384-T0.7": (3, True),
     "qwen3-8b-head-N4096-fwdbwd": (5, False),
     "qwen3-8b-head-N2048": (2, False),
@@ -66,6 +68,9 @@ def parse():
                         "HBM bandwidth)")
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample (0 disables it)")
+    p.add_argument("--configs", type=int, default=1,
+                   help="with the default workload and mode, also time the other workloads "
+                        "(configs 1, 2, 4, 5) and add them under 'configs' (0 skips them)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB (to scale "
                         "the profiler's HBM byte counters) and exit")
@@ -99,11 +104,12 @@ def cpu_baseline(w, mode, target_s):
     """Time the float64 oracle on a bounded sample of active tokens of the same workload."""
     import oracle
     import workloads as wl
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        blas = 1
     act = np.nonzero(w.mask)[0]
     W64 = wl.as_f64(w.W)
     h64 = wl.as_f64(w.h[act])
@@ -133,7 +139,10 @@ def cpu_baseline(w, mode, target_s):
     what = {"fwd": "forward",
             "entropy": "forward + entropy + gradients with an entropy bonus"}.get(
         mode, "forward + dL/dh + dL/dW")
-    out = {"value": n / dt, "unit": "active tokens/s", "cores": int(threads), "kind": "oracle",
+    # the oracle's work is its BLAS calls, so the threads it used are the BLAS pool's, at most
+    # the CPUs this process may run on
+    out = {"value": n / dt, "unit": "active tokens/s", "cores": int(min(blas, affinity)),
+           "kind": "oracle", "blas_threads": int(blas), "cpus_in_affinity": int(affinity),
            "sample": f"first {n} active tokens of the same workload scored as one batch "
                      f"({what}, float64, numpy/OpenBLAS), {dt:.1f} s"}
     return out, act[:n], res["logp"]
@@ -519,97 +528,193 @@ def main():
     if args.mode == "gemm-reference":
         bench_gemm_reference(args, w)
         return
-    N, H, V, T = w.N, w.H, w.V, w.T
-    Na = w.n_active
-    h, W, targets, mask, adv = upload(w, dev)
-    bufs = rlk.ForwardBuffers(N, V, dev)
-    do_bwd = args.mode == "fwdbwd"
-    if do_bwd:
-        bws = torch.empty(rlk.bwd_workspace_bytes(N, H, V, 0), dtype=torch.uint8, device=dev)
-        dh = torch.empty((N, H), dtype=torch.float32, device=dev)
-        dW = torch.empty((V, H), dtype=torch.float32, device=dev)
-
-    def step(ev):
-        ev[0].record()
-        rlk.rlk_compact_active(mask, bufs.idx, bufs.n_active, bufs.target_logit, bufs.logp,
-                               bufs.lse)
-        ev[1].record()
-        rlk.rlk_linear_logp_partials(h, W, targets, bufs.idx, bufs.n_active, T, bufs.part_max,
-                                     bufs.part_sum, bufs.target_logit)
-        ev[2].record()
-        rlk.rlk_linear_logp_merge(bufs.part_max, bufs.part_sum, bufs.target_logit, bufs.idx,
-                                  bufs.n_active, N, V, bufs.logp, bufs.lse)
-        ev[3].record()
-        if do_bwd:
-            rlk.rlk_linear_logp_bwd(h, W, targets, mask, T, adv, bufs.lse, workspace=bws, dh=dh,
-                                    dW=dW)
-        ev[4].record()
-
-    def events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-
-    for _ in range(args.warmup):
-        step(events())
-    torch.cuda.synchronize()
-    evs = [events() for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for ev in evs:
-        step(ev)
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms = total_ms / args.steps
-    step_ms = [e[0].elapsed_time(e[4]) for e in evs]
-    tile_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
-    bwd_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs])) if do_bwd else 0.0
-
-    fwd_flop = 2.0 * Na * H * V
-    bwd_flop = 6.0 * Na * H * V   # recompute + dL/dh + dL/dW, as executed
-    tile_tflops = fwd_flop / (tile_ms * 1e-3) / 1e12
-    srcs = FWD_TILE_SOURCES
-    roofline = {"bound": "mfma", "kernel": "fwd_tiles_kernel<bf16>",
-                "achieved": round(tile_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tile_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_for(srcs, "fwd_tiles_kernel"),
-                "algorithmic_flop_per_launch": fwd_flop, "avg_launch_ms": round(tile_ms, 4)}
+    m = measure(w, dev, args.steps, args.warmup, args.mode == "fwdbwd")
+    N, H, V, T, Na = w.N, w.H, w.V, w.T, w.n_active
     out = {
         "metric": METRIC,
-        "value": round(Na / (ms * 1e-3), 1),
+        "value": round(Na / (m["ms"] * 1e-3), 1),
         "unit": "active tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "step_ms_median": round(float(np.median(step_ms)), 4),
-        "step_ms_min": round(float(np.min(step_ms)), 4),
+        "ms_per_step": round(m["ms"], 4),
+        "step_ms_median": m["step_ms_median"],
+        "step_ms_min": m["step_ms_min"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic: seeded h~N(0,1), W~N(0,1/H) rounded to bf16, packed "
                 "prompt/response sequences",
         "config": {"workload": args.workload, "mode": args.mode, "N": N, "H": H, "V": V,
                    "T": T, "n_active": Na, "parallelism": "none (1 GPU)"},
-        "fwd": {"ms": round(fwd_ms, 4), "active_tokens_per_s": round(Na / (fwd_ms * 1e-3), 1),
-                "tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
-                "mfma_frac": round(fwd_flop / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
-        "roofline": roofline,
+        "timed": "rlk_linear_logp_fwd then rlk_linear_logp_bwd per step, on the current stream",
+        "fwd": m["fwd"],
+        "roofline": m["roofline"],
     }
-    if do_bwd:
-        out["bwd"] = {"ms": round(bwd_ms, 4),
-                      "tflops_executed": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
-                      "mfma_frac": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        out["fwd_bwd_tflops_executed"] = round((fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12, 2)
-        # without the recompute the step would need 6 H V flops per active token
-        out["fwd_bwd_tflops_no_recompute_basis"] = round(
-            6.0 * Na * H * V / (ms * 1e-3) / 1e12, 2)
+    for k in ("bwd", "fwd_bwd_tflops_executed", "fwd_bwd_tflops_no_recompute_basis",
+              "fwd_bwd_mfma_frac", "workspace_bytes"):
+        if k in m:
+            out[k] = m[k]
+    logp = m.pop("_logp")
+    del m
     if args.cpu_baseline_seconds > 0:
         out["cpu_baseline"], rows, olp = cpu_baseline(w, args.mode, args.cpu_baseline_seconds)
         out["gpu_over_cpu_baseline"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
-        out["parity"] = sample_parity(bufs.logp[:N], rows, olp)
+        out["parity"] = sample_parity(logp, rows, olp)
     else:
         out["cpu_baseline"] = None
+    del logp
+    if args.configs and args.workload == DEFAULT_WORKLOAD and args.mode == "fwdbwd":
+        out["configs"] = bench_configs(args, dev)
     print(json.dumps(out), flush=True)
+
+
+def measure(w, dev, steps, warmup, do_bwd):
+    """Time the public entry points on one workload.
+
+    A step is rlk_linear_logp_fwd (compaction, tile kernel, merge) and, if do_bwd,
+    rlk_linear_logp_bwd, enqueued on the current stream; HIP events bracket the forward and
+    the backward of every step and the whole timed region.  The tile kernel alone is timed in
+    a second loop that calls the forward's three stages as separate entry points, with events
+    on the stream the tile kernel runs on (the roofline's launch duration)."""
+    import torch
+    import linear_selected_token_amd as rlk
+    N, H, V, T, Na = w.N, w.H, w.V, w.T, w.n_active
+    dt = 0 if w.dtype == "bf16" else 1
+    h, W, targets, mask, adv = upload(w, dev)
+    fws = torch.empty(rlk.fwd_workspace_bytes(N, H, V, dt), dtype=torch.uint8, device=dev)
+    ws_bytes = {"fwd": fws.numel()}
+    if do_bwd:
+        bws = torch.empty(rlk.bwd_workspace_bytes(N, H, V, dt), dtype=torch.uint8, device=dev)
+        dh = torch.empty((N, H), dtype=torch.float32, device=dev)
+        dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+        ws_bytes["bwd"] = bws.numel()
+    res = {}
+
+    def step(ev):
+        ev[0].record()
+        logp, lse = rlk.rlk_linear_logp_fwd(h, W, targets, mask, T, workspace=fws)
+        ev[1].record()
+        if do_bwd:
+            rlk.rlk_linear_logp_bwd(h, W, targets, mask, T, adv, lse, workspace=bws, dh=dh, dW=dW)
+        ev[2].record()
+        res["logp"] = logp
+
+    def events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    for _ in range(warmup):
+        step(events(3))
+    torch.cuda.synchronize()
+    evs = [events(3) for _ in range(steps)]
+    t0, t1 = events(2)
+    torch.cuda.synchronize()
+    t0.record()
+    for ev in evs:
+        step(ev)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if do_bwd else 0.0
+
+    # the tile kernel alone: the forward's stages as separate calls
+    bufs = rlk.ForwardBuffers(N, V, dev)
+
+    def stages(ev):
+        rlk.rlk_compact_active(mask, bufs.idx, bufs.n_active, bufs.target_logit, bufs.logp,
+                               bufs.lse)
+        ev[0].record()
+        rlk.rlk_linear_logp_partials(h, W, targets, bufs.idx, bufs.n_active, T, bufs.part_max,
+                                     bufs.part_sum, bufs.target_logit)
+        ev[1].record()
+        rlk.rlk_linear_logp_merge(bufs.part_max, bufs.part_sum, bufs.target_logit, bufs.idx,
+                                  bufs.n_active, N, V, bufs.logp, bufs.lse)
+
+    for _ in range(warmup):
+        stages(events(2))
+    tevs = [events(2) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for ev in tevs:
+        stages(ev)
+    torch.cuda.synchronize()
+    tile_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in tevs]))
+    assert torch.equal(bufs.logp[:N], res["logp"]), "stage calls and rlk_linear_logp_fwd differ"
+
+    bf16 = w.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    fwd_flop = 2.0 * Na * H * V
+    bwd_flop = 6.0 * Na * H * V   # recompute + dL/dh + dL/dW, as executed
+    tile_tflops = fwd_flop / (tile_ms * 1e-3) / 1e12
+    srcs = FWD_TILE_SOURCES
+    roofline = {"bound": "mfma", "kernel": f"fwd_tiles_kernel<{'bf16' if bf16 else 'fp32'}>",
+                "achieved": round(tile_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tile_tflops / peak, 4),
+                "traffic": traffic_for(srcs, "fwd_tiles_kernel") if bf16 and w.spec.seed == 1003
+                else None,
+                "algorithmic_flop_per_launch": fwd_flop, "avg_launch_ms": round(tile_ms, 4)}
+    m = {"ms": ms, "step_ms_median": round(float(np.median(step_ms)), 4),
+         "step_ms_min": round(float(np.min(step_ms)), 4),
+         "fwd": {"ms": round(fwd_ms, 4), "active_tokens_per_s": round(Na / (fwd_ms * 1e-3), 1),
+                 "tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
+                 "mfma_frac": round(fwd_flop / (fwd_ms * 1e-3) / 1e12 / peak, 4)},
+         "roofline": roofline, "workspace_bytes": ws_bytes, "_logp": res["logp"]}
+    if do_bwd:
+        m["bwd"] = {"ms": round(bwd_ms, 4),
+                    "tflops_executed": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
+                    "mfma_frac": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / peak, 4)}
+        m["fwd_bwd_tflops_executed"] = round((fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12, 2)
+        m["fwd_bwd_mfma_frac"] = round((fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12 / peak, 4)
+        # without the recompute the step would need 6 H V flops per active token
+        m["fwd_bwd_tflops_no_recompute_basis"] = round(
+            6.0 * Na * H * V / (ms * 1e-3) / 1e12, 2)
+    return m
+
+
+def config_parity(w, logp, k=32, seed=7):
+    """max |dlogp| of the GPU logp against the oracle on k sampled active tokens (all of them
+    when there are at most k)."""
+    import oracle
+    import workloads as wl
+    act = np.nonzero(w.mask)[0]
+    rows = act if act.size <= k else np.sort(np.random.default_rng(seed).choice(act, k, False))
+    olp, _ = oracle.linear_logp(wl.as_f64(w.h[rows]), wl.as_f64(w.W), w.targets[rows],
+                                np.ones(rows.size, np.uint8), w.T)
+    got = logp[rows].astype(np.float64)
+    return {"rows": int(rows.size), "max_abs_dlogp_vs_oracle": float(np.max(np.abs(got - olp)))}
+
+
+def bench_configs(args, dev):
+    """The other workloads, each timed the same way as the headline (forward + backward for
+    bf16 heads, forward only for the fp32 one), with the oracle's logp on sampled tokens."""
+    import torch
+    out = {}
+    for name, (cfg, _) in sorted(WORKLOADS.items(), key=lambda kv: kv[1][0]):
+        if name == DEFAULT_WORKLOAD:
+            continue
+        t0 = time.perf_counter()
+        w = make_workload(name)
+        do_bwd = w.dtype == "bf16"
+        m = measure(w, dev, args.steps, args.warmup, do_bwd)
+        Na = w.n_active
+        rec = {"config": cfg, "workload": name, "N": w.N, "H": w.H, "V": w.V, "T": w.T,
+               "dtype": w.dtype, "n_active": Na,
+               "fwd_ms": m["fwd"]["ms"], "fwd_active_tokens_per_s": m["fwd"]["active_tokens_per_s"],
+               "fwd_tflops": m["fwd"]["tflops"], "fwd_mfma_frac": m["fwd"]["mfma_frac"],
+               "tile_kernel_ms": m["roofline"]["avg_launch_ms"],
+               "tile_kernel_frac": m["roofline"]["frac"], "peak_tflops": m["roofline"]["peak"],
+               "workspace_bytes": m["workspace_bytes"]}
+        if do_bwd:
+            rec.update({"fwd_bwd_ms": round(m["ms"], 4),
+                        "fwd_bwd_active_tokens_per_s": round(Na / (m["ms"] * 1e-3), 1),
+                        "bwd_ms": m["bwd"]["ms"], "bwd_mfma_frac": m["bwd"]["mfma_frac"],
+                        "fwd_bwd_mfma_frac": m["fwd_bwd_mfma_frac"]})
+        logp = m.pop("_logp").cpu().numpy()
+        del m
+        torch.cuda.empty_cache()
+        rec["parity"] = config_parity(w, logp)
+        rec["wall_s"] = round(time.perf_counter() - t0, 1)
+        out[str(cfg)] = rec
+        print(f"# config {cfg} ({name}) done in {rec['wall_s']} s", file=sys.stderr, flush=True)
+    return out
 
 
 if __name__ == "__main__":

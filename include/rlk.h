@@ -210,7 +210,8 @@ rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int
  *                              takes back
  *   workspace: rlk_linear_kl_fwd_workspace_size bytes: six float arrays of ceil(V/128) x N
  *              (both heads' column statistics and the two cross terms) and two chunk buffers of
- *              32800 floats per token, N rounded up to 256 (4.7 GB at N = 16384, V = 151936). */
+ *              65568 floats per token, N rounded up to 256 (9.06 GB in all at N = 16384,
+ *              V = 151936). */
 rlk_status_t rlk_linear_kl_fwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
                                               int dtype, size_t* bytes);
 rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t,
