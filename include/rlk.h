@@ -112,6 +112,26 @@ rlk_status_t rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* ta
                                  float temperature, float* logp, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* The forward without a workspace argument, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * library's own scratch serves as the workspace: a static device array of
+ * RLK_NOALLOC_SCRATCH_BYTES per device, held from the time the library's code is loaded on a
+ * device until the process ends; the call allocates and frees nothing.
+ *   h, W, targets, mask, N, H, V, dtype, temperature, logp, lse: as for rlk_linear_logp_fwd;
+ *                             the outputs are bit-identical to rlk_linear_logp_fwd's.
+ * The forward's workspace must fit the scratch: rlk_linear_logp_fwd_workspace_size(N, H, V)
+ * <= RLK_NOALLOC_SCRATCH_BYTES (about 9.5 KB per token at V = 151936, i.e. up to ~7000 tokens;
+ * about 2 KB per token at V = 32000), else RLK_ERROR_WORKSPACE and nothing is written.  Every
+ * call on a device shares that device's scratch and leaves its contents there; each call
+ * overwrites everything it reads (nothing needs to start at zero).  Calls that overlap on one
+ * device (several host threads or streams at once) race on the scratch: the caller orders
+ * them, for example on one stream. */
+#define RLK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+rlk_status_t rlk_linear_logp_fwd_noalloc(const void* h, const void* W, const int32_t* targets,
+                                         const uint8_t* mask, int64_t N, int64_t H, int64_t V,
+                                         int dtype, float temperature, float* logp, float* lse,
+                                         void* stream);
+
 /* Forward with the entropy of each active token's distribution, in the same pass:
  * entropy[t] = -sum_v p[t,v] log p[t,v] with p[t,:] = softmax(z[t,:]), z = h W^T / T (the
  * entropy statistic the RL-Kernel Roadmap (2026) lists next to the fused log-prob, "operator

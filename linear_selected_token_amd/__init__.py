@@ -28,6 +28,7 @@ from .ops import (  # noqa: E402,F401
     rlk_linear_logp_bwd_entropy,
     rlk_linear_logp_fwd,
     rlk_linear_logp_fwd_entropy,
+    rlk_linear_logp_fwd_noalloc,
     rlk_linear_logp_merge,
     rlk_linear_logp_partials,
     rlk_linear_logp_partials_shard,

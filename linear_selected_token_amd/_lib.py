@@ -17,6 +17,7 @@ RLK_ERROR_DEVICE = 4
 RLK_BF16 = 0
 RLK_FP32 = 1
 RLK_VOCAB_PARTIAL = 128
+RLK_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -32,6 +33,8 @@ SIGNATURES = {
     "rlk_linear_logp_fwd_workspace_size": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]),
     "rlk_linear_logp_bwd_workspace_size": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]),
     "rlk_linear_logp_fwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p, _p, _sz, _p]),
+    "rlk_linear_logp_fwd_noalloc": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p,
+                                           _p]),
     "rlk_linear_logp_fwd_entropy_workspace_size": (_int, [_i64, _i64, _i64, _int,
                                                           ctypes.POINTER(_sz)]),
     "rlk_linear_logp_fwd_entropy": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p,

@@ -37,6 +37,34 @@ hipError_t persistent_grid(int* grid) {
   return hipSuccess;
 }
 
+// Scratch of rlk_linear_logp_fwd_noalloc: the forward's workspace in a static device array, so
+// that the call needs no allocation.  Each device holds its own copy (at its own address) from
+// the time the library's code is loaded on it until the process ends.  In host code the name
+// `scratch` is a host-side stand-in, never a device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device, read once per device.
+constexpr size_t kNoAllocScratchBytes = RLK_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoAllocScratchBytes % 256 == 0, "the forward's workspace is carved in 256-byte units");
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::atomic<uintptr_t> g_scratch[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uintptr_t p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == 0) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (q == nullptr || reinterpret_cast<uintptr_t>(q) % 256 != 0) return hipErrorInvalidSymbol;
+    p = reinterpret_cast<uintptr_t>(q);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = reinterpret_cast<void*>(p);
+  return hipSuccess;
+}
+
 inline rlk_status_t dev_status(hipError_t e) { return e == hipSuccess ? RLK_SUCCESS : RLK_ERROR_DEVICE; }
 
 template <class T>
@@ -269,6 +297,20 @@ rlk_status_t rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* ta
                                stream);
   if (s != RLK_SUCCESS) return s;
   return rlk_linear_logp_merge(pm, ps, zy, idx, na, N, V, logp, lse, stream);
+}
+
+rlk_status_t rlk_linear_logp_fwd_noalloc(const void* h, const void* W, const int32_t* targets,
+                                         const uint8_t* mask, int64_t N, int64_t H, int64_t V,
+                                         int dtype, float temperature, float* logp, float* lse,
+                                         void* stream) {
+  // every argument check first, against a stand-in for the scratch (256-byte aligned, non-null)
+  rlk_status_t s = check_fwd(h, W, targets, mask, N, H, V, dtype, temperature, logp, lse,
+                             reinterpret_cast<void*>(uintptr_t(256)), kNoAllocScratchBytes);
+  if (s != RLK_SUCCESS || N == 0) return s;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return RLK_ERROR_DEVICE;
+  return rlk_linear_logp_fwd(h, W, targets, mask, N, H, V, dtype, temperature, logp, lse, ws,
+                             kNoAllocScratchBytes, stream);
 }
 
 rlk_status_t rlk_linear_logp_fwd_entropy(const void* h, const void* W, const int32_t* targets,

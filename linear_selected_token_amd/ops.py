@@ -101,6 +101,34 @@ def rlk_linear_logp_fwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     return logp, lse
 
 
+def rlk_linear_logp_fwd_noalloc(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                                mask: torch.Tensor, temperature: float,
+                                logp: Optional[torch.Tensor] = None,
+                                lse: Optional[torch.Tensor] = None,
+                                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """rlk_linear_logp_fwd with the library's static scratch as its workspace (the library
+    allocates nothing); returns (logp, lse).  Pass preallocated logp and lse ([N] float32) to
+    make the call allocate nothing at all."""
+    mask = _mask_u8(mask)
+    _check(h, W, targets, mask)
+    N, H = h.shape
+    V = W.shape[0]
+    dt = _dtype_code(h)
+    for name, t in (("logp", logp), ("lse", lse)):
+        if t is not None and (not t.is_cuda or t.dtype != torch.float32 or t.shape != (N,)
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor [N]")
+    if logp is None:
+        logp = torch.empty(N, dtype=torch.float32, device=h.device)
+    if lse is None:
+        lse = torch.empty(N, dtype=torch.float32, device=h.device)
+    L.check(L.lib().rlk_linear_logp_fwd_noalloc(_vp(h), _vp(W), _vp(targets), _vp(mask), N, H, V,
+                                                dt, float(temperature), _vp(logp), _vp(lse),
+                                                _stream(h.device)),
+            "rlk_linear_logp_fwd_noalloc")
+    return logp, lse
+
+
 def fwd_entropy_workspace_bytes(N: int, H: int, V: int, dtype_code: int) -> int:
     out = ctypes.c_size_t(0)
     L.check(L.lib().rlk_linear_logp_fwd_entropy_workspace_size(N, H, V, dtype_code,
