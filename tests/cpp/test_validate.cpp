@@ -1,0 +1,278 @@
+// Host-side argument checks and workspace layouts of the C ABI (csrc/validate.hpp), compiled
+// for the CPU alone and run under AddressSanitizer and UndefinedBehaviorSanitizer by
+// tests/test_validate_cpp.py.  Every status path of every check, the layouts' alignment and
+// disjointness, and the arithmetic at the size limits (N and V at 2^22, H at 2^16, h at
+// 2^31 - 1 bytes), where a 32-bit intermediate or a size_t wrap would show.
+//
+// The checks only compare pointer values (null, alignment); they never dereference them, so
+// the pointers below are plain numbers with the wanted alignment.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <limits>
+#include <vector>
+
+#include "validate.hpp"
+
+using namespace rlk;
+
+static int g_fail = 0;
+static int g_checks = 0;
+
+#define EXPECT(cond)                                                          \
+  do {                                                                        \
+    ++g_checks;                                                               \
+    if (!(cond)) {                                                            \
+      ++g_fail;                                                               \
+      std::fprintf(stderr, "%s:%d: expected %s\n", __FILE__, __LINE__, #cond); \
+    }                                                                         \
+  } while (0)
+
+static const void* P(uintptr_t v) { return reinterpret_cast<const void*>(v); }
+template <class T>
+static T* PT(uintptr_t v) { return reinterpret_cast<T*>(v); }
+
+// 256-byte aligned stand-ins, and one that is only 2-byte aligned
+constexpr uintptr_t A = 0x10000;
+constexpr uintptr_t ODD = 0x10002;
+
+static void test_shape() {
+  EXPECT(check_shape(16, 4096, 151936, RLK_BF16) == RLK_SUCCESS);
+  EXPECT(check_shape(0, 64, 1, RLK_FP32) == RLK_SUCCESS);
+  EXPECT(check_shape(-1, 64, 10, RLK_BF16) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_shape(1, 0, 10, RLK_BF16) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_shape(1, -64, 10, RLK_BF16) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_shape(1, 64, 0, RLK_BF16) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_shape(1, 64, 10, 2) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(check_shape(1, 64, 10, -1) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(check_shape(1, 96, 10, RLK_BF16) == RLK_ERROR_UNSUPPORTED);  // H % 64
+  // the size limits, at and one past
+  EXPECT(check_shape(1, 64, kMaxVocab, RLK_BF16) == RLK_SUCCESS);
+  EXPECT(check_shape(1, 64, kMaxVocab + 1, RLK_BF16) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(check_shape(1, kMaxHidden, 10, RLK_BF16) == RLK_SUCCESS);
+  EXPECT(check_shape(1, kMaxHidden + 64, 10, RLK_BF16) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(check_shape(kMaxTokens + 1, 64, 10, RLK_BF16) == RLK_ERROR_UNSUPPORTED);
+  // h at most 2^31 - 1 bytes: 2^22 - 1 tokens x 256 bf16 = 2^31 - 512 bytes fits, 2^22 does not
+  EXPECT(check_shape(kMaxTokens - 1, 256, 10, RLK_BF16) == RLK_SUCCESS);
+  EXPECT(check_shape(kMaxTokens, 256, 10, RLK_BF16) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(check_shape(kMaxTokens - 1, 128, 10, RLK_FP32) == RLK_SUCCESS);
+  EXPECT(check_shape(kMaxTokens, 128, 10, RLK_FP32) == RLK_ERROR_UNSUPPORTED);
+  // the largest N x H products stay exact in 64 bits
+  EXPECT(check_shape(kMaxTokens, kMaxHidden, kMaxVocab, RLK_FP32) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(check_shape(int64_t(1) << 40, 64, 10, RLK_BF16) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(check_shape(std::numeric_limits<int64_t>::max(), 64, 10, RLK_BF16) ==
+         RLK_ERROR_UNSUPPORTED);
+}
+
+static void test_shard() {
+  EXPECT(check_shard(151936, 0, 151936) == RLK_SUCCESS);
+  EXPECT(check_shard(1024, 128, 151936) == RLK_SUCCESS);
+  EXPECT(check_shard(128, 151936 - 128, 151936) == RLK_SUCCESS);
+  EXPECT(check_shard(100, 151936 - 100, 151936) == RLK_ERROR_UNSUPPORTED);  // start off-column
+  EXPECT(check_shard(1000, 151936 - 1000 - 24, 151936) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(check_shard(200, 0, 151936) == RLK_ERROR_UNSUPPORTED);  // ends inside a column
+  EXPECT(check_shard(200, 0, 200) == RLK_SUCCESS);                // ... unless it is the last
+  EXPECT(check_shard(10, -128, 151936) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_shard(256, 151936 - 128, 151936) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_shard(10, 0, 0) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_shard(128, 0, kMaxVocab + 1) == RLK_ERROR_UNSUPPORTED);
+}
+
+static void test_temperature() {
+  EXPECT(check_temperature(1.0f) == RLK_SUCCESS);
+  EXPECT(check_temperature(0.7f) == RLK_SUCCESS);
+  EXPECT(check_temperature(std::numeric_limits<float>::max()) == RLK_SUCCESS);
+  EXPECT(check_temperature(0.f) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_temperature(-0.f) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_temperature(-1.f) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_temperature(std::nanf("")) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_temperature(std::numeric_limits<float>::infinity()) == RLK_ERROR_INVALID_VALUE);
+  // 1/T overflows fp32 for the smallest positive floats
+  EXPECT(check_temperature(std::numeric_limits<float>::denorm_min()) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(check_temperature(1e-39f) == RLK_ERROR_INVALID_VALUE);
+}
+
+// Offsets of a layout's pieces: each 256-byte aligned, in order, each past the previous piece's
+// end, and the total past the last one.
+static void expect_layout(const std::vector<size_t>& off, const std::vector<size_t>& size,
+                          size_t total) {
+  size_t end = 0;
+  for (size_t i = 0; i < off.size(); ++i) {
+    EXPECT(off[i] % 256 == 0);
+    EXPECT(off[i] >= end);
+    EXPECT(off[i] + size[i] >= off[i]);  // no wrap
+    end = off[i] + size[i];
+  }
+  EXPECT(total >= end);
+  EXPECT(total % 256 == 0);
+}
+
+static void test_fwd_layout(int64_t N, int64_t V, bool ent) {
+  const FwdLayout L = fwd_layout(N, V, ent);
+  const size_t n = (size_t)(N > 0 ? N : 1), j = (size_t)num_partials(V);
+  std::vector<size_t> off = {L.idx, L.n_active, L.target_logit, L.part_max, L.part_sum};
+  std::vector<size_t> sz = {4 * n, 4, 4 * n, 4 * n * j, 4 * n * j};
+  if (ent) {
+    off.push_back(L.part_w);
+    sz.push_back(4 * n * j);
+  }
+  expect_layout(off, sz, L.total);
+}
+
+static void test_layouts() {
+  for (int64_t N : {int64_t(0), int64_t(1), int64_t(255), int64_t(16384), kMaxTokens})
+    for (int64_t V : {int64_t(1), int64_t(1000), int64_t(151936), kMaxVocab}) {
+      test_fwd_layout(N, V, false);
+      test_fwd_layout(N, V, true);
+    }
+  EXPECT(num_partials(0) == 0 && num_partials(1) == 1 && num_partials(128) == 1 &&
+         num_partials(129) == 2 && num_partials(151936) == 1187);
+  // at the limits the forward's workspace is 2^40 bytes and more: exact in size_t
+  EXPECT(fwd_layout(kMaxTokens, kMaxVocab).part_sum == fwd_layout(kMaxTokens, kMaxVocab).part_max +
+                                                            (size_t(4) << 37));
+  for (int64_t N : {int64_t(1), int64_t(300), int64_t(4096), int64_t(16384), kMaxTokens})
+    for (int64_t H : {int64_t(256), int64_t(4096), int64_t(7168), kMaxHidden}) {
+      const BwdLayout L = bwd_layout(N, H);
+      const size_t np = (size_t)bwd_npad(N);
+      std::vector<size_t> off = {L.idx, L.n_active, L.sched, L.hT, L.Gv};
+      std::vector<size_t> sz = {4 * (size_t)N, 4, 32, 2 * (size_t)H * np,
+                                2 * np * (size_t)(kBwdChunkEntries + 64)};
+      for (int q = 0; q < kBwdDhPieces; ++q) {
+        off.push_back(L.dhp[q]);
+        sz.push_back(4 * np * (size_t)H);
+      }
+      expect_layout(off, sz, L.total);
+      EXPECT(np % 256 == 0 && np >= (size_t)N);
+    }
+  for (int64_t N : {int64_t(0), int64_t(1), int64_t(1023), int64_t(1024), int64_t(1) << 20,
+                    kMaxTokens}) {
+    const DiagLayout D = diag_layout(N);
+    const size_t n = (size_t)(N > 0 ? N : 1), nb = (n + 1023) / 1024;
+    expect_layout({D.idx, D.n_active, D.keys, D.part, D.pmax, D.ptok, D.hist, D.sel},
+                  {4 * n, 4, 8 * n, 32 * nb, 8 * nb, 4 * nb, 4 * 8 * 6 * 256, 16 * 6}, D.total);
+    const LogitsLayout G = logits_layout(N);
+    expect_layout({G.idx, G.n_active}, {4 * n, 4}, G.total);
+    EXPECT(loss_workspace(N) >= 32 * nb && loss_workspace(N) % 256 == 0);
+    for (int64_t V : {int64_t(1), int64_t(151936), kMaxVocab}) {
+      const KlLayout K = kl_fwd_layout(N, V);
+      const size_t jn = 4 * n * (size_t)num_partials(V), c = kl_chunk_bytes(N);
+      expect_layout({K.idx, K.n_active, K.tmax, K.tsum, K.smax, K.ssum, K.wf, K.wr, K.xs, K.xt},
+                    {4 * n, 4, jn, jn, jn, jn, jn, jn, c, c}, K.total);
+    }
+  }
+}
+
+static void test_fwd() {
+  const size_t ws = fwd_layout(1000, 151936).total;
+  auto call = [&](const void* h, const void* W, uintptr_t tg, uintptr_t mk, int64_t N, int64_t H,
+                  int64_t V, int dt, float T, uintptr_t lp, uintptr_t ls, const void* w,
+                  size_t bytes) {
+    return check_fwd(h, W, PT<const int32_t>(tg), PT<const uint8_t>(mk), N, H, V, dt, T,
+                     PT<const float>(lp), PT<const float>(ls), w, bytes);
+  };
+  EXPECT(call(P(A), P(A), A, A, 1000, 4096, 151936, RLK_BF16, 1.f, A, A, P(A), ws) ==
+         RLK_SUCCESS);
+  EXPECT(call(P(A), P(A), A, A, 1000, 4096, 151936, RLK_BF16, 1.f, A, 0, P(A), ws) ==
+         RLK_SUCCESS);  // lse may be NULL
+  EXPECT(call(P(A), P(A), A, A, 1000, 4096, 151936, RLK_BF16, 1.f, A, A, P(A), ws - 1) ==
+         RLK_ERROR_WORKSPACE);
+  // N == 0: nothing is read, NULL pointers are fine
+  EXPECT(call(nullptr, nullptr, 0, 0, 0, 4096, 151936, RLK_BF16, 1.f, 0, 0, nullptr, 0) ==
+         RLK_SUCCESS);
+  // shape and temperature errors come before pointer checks
+  EXPECT(call(nullptr, nullptr, 0, 0, 0, 4096, 151936, RLK_BF16, 0.f, 0, 0, nullptr, 0) ==
+         RLK_ERROR_INVALID_VALUE);
+  EXPECT(call(nullptr, nullptr, 0, 0, 5, 100, 151936, RLK_BF16, 1.f, 0, 0, nullptr, 0) ==
+         RLK_ERROR_UNSUPPORTED);
+  const uintptr_t ptrs[6] = {A, A, A, A, A, A};
+  for (int k = 0; k < 6; ++k) {  // each required pointer NULL in turn
+    uintptr_t p[6];
+    for (int i = 0; i < 6; ++i) p[i] = ptrs[i];
+    p[k] = 0;
+    EXPECT(call(P(p[0]), P(p[1]), p[2], p[3], 1000, 4096, 151936, RLK_BF16, 1.f, p[4], A,
+                P(p[5]), ws) == RLK_ERROR_INVALID_VALUE);
+  }
+  // misalignment: h, W 16 B; targets, logp, lse 4 B; workspace 256 B (mask: any)
+  EXPECT(call(P(ODD), P(A), A, A, 1000, 4096, 151936, RLK_BF16, 1.f, A, A, P(A), ws) ==
+         RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(P(A), P(A + 8), A, A, 1000, 4096, 151936, RLK_BF16, 1.f, A, A, P(A), ws) ==
+         RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(P(A), P(A), ODD, A, 1000, 4096, 151936, RLK_BF16, 1.f, A, A, P(A), ws) ==
+         RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(P(A), P(A), A, ODD + 1, 1000, 4096, 151936, RLK_BF16, 1.f, A, A, P(A), ws) ==
+         RLK_SUCCESS);
+  EXPECT(call(P(A), P(A), A, A, 1000, 4096, 151936, RLK_BF16, 1.f, ODD, A, P(A), ws) ==
+         RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(P(A), P(A), A, A, 1000, 4096, 151936, RLK_BF16, 1.f, A, ODD, P(A), ws) ==
+         RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(P(A), P(A), A, A, 1000, 4096, 151936, RLK_BF16, 1.f, A, A, P(A + 128), ws) ==
+         RLK_ERROR_UNSUPPORTED);
+  // the entropy forward needs the larger workspace
+  EXPECT(check_fwd(P(A), P(A), PT<const int32_t>(A), PT<const uint8_t>(A), 1000, 4096, 151936,
+                   RLK_BF16, 1.f, PT<const float>(A), nullptr, P(A), ws, true) ==
+         RLK_ERROR_WORKSPACE);
+}
+
+static void test_bwd() {
+  const size_t ws = bwd_layout(300, 4096).total;
+  auto call = [&](int64_t N, int64_t H, int dt, uintptr_t dh, uintptr_t dW, uintptr_t w,
+                  size_t bytes, uintptr_t adv = A) {
+    return check_bwd(P(A), P(A), PT<const int32_t>(A), PT<const uint8_t>(A), N, H, 151936, dt,
+                     1.f, PT<const float>(adv), PT<const float>(A), PT<const float>(dh),
+                     PT<const float>(dW), P(w), bytes);
+  };
+  EXPECT(call(300, 4096, RLK_BF16, A, A, A, ws) == RLK_SUCCESS);
+  EXPECT(call(300, 4096, RLK_BF16, A, A, A, ws - 256) == RLK_ERROR_WORKSPACE);
+  EXPECT(call(300, 4096, RLK_FP32, A, A, A, ws) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(300, 4160, RLK_BF16, A, A, A, ws) == RLK_ERROR_UNSUPPORTED);  // H % 256
+  EXPECT(call(300, 4096, RLK_BF16, A, 0, A, ws) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(call(0, 4096, RLK_BF16, 0, A, 0, 0) == RLK_SUCCESS);  // N == 0 still zeroes dW
+  EXPECT(call(0, 4096, RLK_BF16, 0, 0, 0, 0) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(call(300, 4096, RLK_BF16, 0, A, A, ws) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(call(300, 4096, RLK_BF16, A, A, A, ws, 0) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(call(300, 4096, RLK_BF16, ODD, A, A, ws) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(300, 4096, RLK_BF16, A, A, A + 64, ws) == RLK_ERROR_UNSUPPORTED);
+}
+
+static void test_logits() {
+  const size_t ws = logits_layout(100).total;
+  auto call = [&](int64_t N, int64_t V, int64_t ld, int dt, float T, uintptr_t lg, size_t bytes) {
+    return check_logits(P(lg), N, V, ld, dt, T, PT<const int32_t>(A), PT<const uint8_t>(A),
+                        PT<const float>(A), nullptr, P(A), bytes);
+  };
+  EXPECT(call(100, 1000, 1000, RLK_FP32, 1.f, A, ws) == RLK_SUCCESS);
+  EXPECT(call(100, 1000, 1000, RLK_BF16, 1.f, A, ws) == RLK_SUCCESS);
+  EXPECT(call(100, 1000, 1004, RLK_BF16, 1.f, A, ws) == RLK_ERROR_UNSUPPORTED);  // 16 B rows
+  EXPECT(call(100, 1000, 999, RLK_FP32, 1.f, A, ws) == RLK_ERROR_INVALID_VALUE);  // ld < V
+  EXPECT(call(100, kMaxLogitsVocab + 1, kMaxLogitsVocab + 8, RLK_FP32, 1.f, A, ws) ==
+         RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(100, 1000, 1000, RLK_FP32, -1.f, A, ws) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(call(100, 1000, 1000, RLK_FP32, 1.f, 0, ws) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(call(100, 1000, 1000, RLK_FP32, 1.f, A + 4, ws) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(100, 1000, 1000, RLK_FP32, 1.f, A, ws - 1) == RLK_ERROR_WORKSPACE);
+  EXPECT(call(0, 1000, 1000, RLK_FP32, 1.f, 0, 0) == RLK_SUCCESS);
+}
+
+static void test_kl() {
+  auto call = [&](int64_t Hs, int64_t Ht, uintptr_t ws) {
+    return check_kl(P(A), P(A), P(A), P(A), PT<const uint8_t>(A), 64, Hs, Ht, 1000, RLK_BF16,
+                    1.f, P(ws));
+  };
+  EXPECT(call(512, 256, A) == RLK_SUCCESS);
+  EXPECT(call(512, 100, A) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(512, 256, 0) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(call(512, 256, A + 16) == RLK_ERROR_UNSUPPORTED);
+}
+
+int main() {
+  test_shape();
+  test_shard();
+  test_temperature();
+  test_layouts();
+  test_fwd();
+  test_bwd();
+  test_logits();
+  test_kl();
+  std::printf("validate: %d checks, %d failed\n", g_checks, g_fail);
+  return g_fail == 0 ? 0 : 1;
+}
