@@ -77,7 +77,9 @@ const char* build_info_string() {
       "rlk linear_logp | arch gfx950 | compiler " __clang_version__
       " | tile 256x256, K stage 128 B, 8 wave64 x 128x64, mfma 32x32x16 bf16 / 32x32x2 f32"
       " | vocab partial 128 | merge 8 strided slices + fixed tree"
-      " | bwd chunk 65536, dh split at 16384 (four pieces per chunk)";
+      " | bwd chunk 65536, dh split at 16384 (four pieces per chunk)"
+      " | bwd token blocks: equal blocks of at most the largest multiple of 256 tokens whose"
+      " buffers (131200 + 14 H bytes per token) fit 1000000000 bytes";
   return s;
 }
 
@@ -109,30 +111,47 @@ rlk_status_t run_bwd(const void* h, const void* W, const int32_t* targets, const
   a.entropy = entropy;
   int32_t* idx = carve<int32_t>(workspace, L.idx);
   int32_t* na = carve<int32_t>(workspace, L.n_active);
-  a.idx = idx;
-  a.n_active = na;
+  int32_t* desc = carve<int32_t>(workspace, L.block_desc);
+  int32_t* bidx = carve<int32_t>(workspace, L.bidx);
+  int32_t* bn = carve<int32_t>(workspace, L.bn);
   a.N = (int)N;
   a.H = (int)H;
   a.V = (int)V;
-  a.Npad = (int)bwd_npad(N);
+  a.Npad = (int)bwd_npad(N, H);
   a.inv_t = (float)(1.0 / (double)temperature);
   a.dh = dh;
   a.dW = dW;
   a.hT = carve<uint16_t>(workspace, L.hT);
   a.Gv = carve<uint16_t>(workspace, L.Gv);
-  for (int q = 0; q < kDhPieces; ++q) a.dhp[q] = carve<float>(workspace, L.dhp[q]);
+  a.dhp[0] = nullptr;  // piece 0 accumulates in dh's rows
+  for (int q = 1; q < kDhPieces; ++q) a.dhp[q] = carve<float>(workspace, L.dhp[q]);
   a.sched = carve<int>(workspace, L.sched);
+  a.idx = bidx;
+  a.n_active = bn;
+  const int nblk = bwd_blocks(N, H);
   CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
+  c.block_desc = desc;
+  c.nblk = nblk;
+  c.block_cap = (int)bwd_token_cap(H);
   hipError_t e = launch_compact(c, st);
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
-  e = launch_bwd_prepare(a, st);
+  e = launch_zero(dh, (size_t)N * (size_t)H, st);  // inactive rows stay 0
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
   const int nchunks = (int)((V + kBwdChunk - 1) / kBwdChunk);
-  for (int c0 = 0; c0 < nchunks; ++c0) {
-    e = launch_bwd_chunk(a, c0, grid, st);
+  for (int b = 0; b < nblk; ++b) {
+    // the block's compacted indices and count, copied for the kernels that follow
+    e = launch_select_block(idx, desc, b, a.Npad, bidx, bn, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    e = launch_bwd_transpose(a, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    for (int c0 = 0; c0 < nchunks; ++c0) {
+      e = launch_bwd_chunk(a, c0, grid, b > 0, st);
+      if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    }
+    e = launch_bwd_finish(a, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
   }
-  return dev_status(launch_bwd_finish(a, st));
+  return RLK_SUCCESS;
 }
 
 
@@ -417,7 +436,7 @@ rlk_status_t rlk_linear_kl_fwd_workspace_size(int64_t N, int64_t H_s, int64_t H_
   rlk_status_t s = check_shape(N, H_s, V, dtype);
   if (s == RLK_SUCCESS) s = check_shape(N, H_t, V, dtype);
   if (s != RLK_SUCCESS) return s;
-  *bytes = kl_fwd_layout(N, V).total;
+  *bytes = kl_fwd_layout(N, H_s, V).total;
   return RLK_SUCCESS;
 }
 
@@ -432,12 +451,18 @@ rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t
   if (!kl_fwd || !kl_rev) return RLK_ERROR_INVALID_VALUE;
   if (!aligned(kl_fwd, 4) || !aligned(kl_rev, 4) || !aligned(lse_s, 4) || !aligned(lse_t, 4))
     return RLK_ERROR_UNSUPPORTED;
-  if (workspace_bytes < kl_fwd_layout(N, V).total) return RLK_ERROR_WORKSPACE;
-  const KlLayout L = kl_fwd_layout(N, V);
+  if (workspace_bytes < kl_fwd_layout(N, H_s, V).total) return RLK_ERROR_WORKSPACE;
+  const KlLayout L = kl_fwd_layout(N, H_s, V);
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* idx = carve<int32_t>(workspace, L.idx);
   int32_t* na = carve<int32_t>(workspace, L.n_active);
+  int32_t* counts = carve<int32_t>(workspace, L.block_count);
+  const int nblk = bwd_blocks(N, H_s);
+  const int cap = (int)bwd_token_cap(H_s);
   CompactArgs c{mask, idx, na, nullptr, kl_fwd, lse_s, (int)N, kl_rev, lse_t};
+  c.block_count = counts;
+  c.nblk = nblk;
+  c.block_cap = cap;
   hipError_t e = launch_compact(c, st);
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
   int grid = 0;
@@ -462,22 +487,38 @@ rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t
   k.kl_rev = kl_rev;
   k.lse_s = lse_s;
   k.lse_t = lse_t;
-  for (int64_t c0 = 0; c0 < V; c0 += kBwdChunk) {
-    const int vc = (int)(V - c0 < kBwdChunk ? V - c0 : kBwdChunk);
-    FwdTileArgs t{h_t, static_cast<const uint8_t*>(W_t) + (size_t)c0 * H_t * es, nullptr, idx, na,
-                  (int)N, (int)H_t, vc, inv_t, const_cast<float*>(k.t_max),
-                  const_cast<float*>(k.t_sum), nullptr, (int)c0, nullptr,
-                  const_cast<float*>(k.xt)};
-    e = launch_fwd_tiles(t, dtype == RLK_BF16, grid, st, kFwdStoreX);
-    if (e != hipSuccess) return RLK_ERROR_DEVICE;
-    FwdTileArgs u{h_s, static_cast<const uint8_t*>(W_s) + (size_t)c0 * H_s * es, nullptr, idx, na,
-                  (int)N, (int)H_s, vc, inv_t, const_cast<float*>(k.s_max),
-                  const_cast<float*>(k.s_sum), nullptr, (int)c0, nullptr,
-                  const_cast<float*>(k.xs)};
-    e = launch_fwd_tiles(u, dtype == RLK_BF16, grid, st, kFwdStoreX);
-    if (e != hipSuccess) return RLK_ERROR_DEVICE;
-    e = launch_kl_cross(k, (int)c0, (int)N, st);
-    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  // Per token block (the chunk buffers hold one block's rows): per chunk, both heads' column
+  // statistics and x, then the cross terms.  The [J][N] arrays are addressed from the block's
+  // first compacted index, so each block writes its own columns of them.
+  for (int b = 0; b < nblk; ++b) {
+    const size_t t0 = (size_t)b * cap;
+    const int rows = (int)(N - (int64_t)t0 < cap ? N - (int64_t)t0 : cap);
+    KlArgs kb = k;
+    kb.idx = idx + t0;
+    kb.n_active = counts + b;
+    kb.s_max = k.s_max + t0;
+    kb.s_sum = k.s_sum + t0;
+    kb.t_max = k.t_max + t0;
+    kb.t_sum = k.t_sum + t0;
+    kb.wf = k.wf + t0;
+    kb.wr = k.wr + t0;
+    for (int64_t c0 = 0; c0 < V; c0 += kBwdChunk) {
+      const int vc = (int)(V - c0 < kBwdChunk ? V - c0 : kBwdChunk);
+      FwdTileArgs t{h_t, static_cast<const uint8_t*>(W_t) + (size_t)c0 * H_t * es, nullptr,
+                    kb.idx, kb.n_active, (int)N, (int)H_t, vc, inv_t,
+                    const_cast<float*>(kb.t_max), const_cast<float*>(kb.t_sum), nullptr, (int)c0,
+                    nullptr, const_cast<float*>(k.xt)};
+      e = launch_fwd_tiles(t, dtype == RLK_BF16, grid, st, kFwdStoreX);
+      if (e != hipSuccess) return RLK_ERROR_DEVICE;
+      FwdTileArgs u{h_s, static_cast<const uint8_t*>(W_s) + (size_t)c0 * H_s * es, nullptr,
+                    kb.idx, kb.n_active, (int)N, (int)H_s, vc, inv_t,
+                    const_cast<float*>(kb.s_max), const_cast<float*>(kb.s_sum), nullptr, (int)c0,
+                    nullptr, const_cast<float*>(k.xs)};
+      e = launch_fwd_tiles(u, dtype == RLK_BF16, grid, st, kFwdStoreX);
+      if (e != hipSuccess) return RLK_ERROR_DEVICE;
+      e = launch_kl_cross(kb, (int)c0, rows, st);
+      if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    }
   }
   return dev_status(launch_kl_merge(k, st));
 }
@@ -510,7 +551,7 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
   if (N == 0) return dev_status(launch_zero(dW_s, (size_t)V * (size_t)H_s, st));
   if (!coef || !lse_s || !lse_t || !dh_s || (reverse && !kl_rev)) return RLK_ERROR_INVALID_VALUE;
   if (!aligned(coef, 4) || !aligned(lse_s, 4) || !aligned(lse_t, 4) || !aligned(kl_rev, 4) ||
-      !aligned(dh_s, 4))
+      !aligned(dh_s, 16))
     return RLK_ERROR_UNSUPPORTED;
   if (workspace_bytes < kl_bwd_bytes(N, H_s)) return RLK_ERROR_WORKSPACE;
   int grid = 0;
@@ -519,27 +560,31 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
   const float inv_t = (float)(1.0 / (double)temperature);
   int32_t* idx = carve<int32_t>(workspace, L.idx);
   int32_t* na = carve<int32_t>(workspace, L.n_active);
+  int32_t* desc = carve<int32_t>(workspace, L.block_desc);
+  int32_t* bidx = carve<int32_t>(workspace, L.bidx);
+  int32_t* bn = carve<int32_t>(workspace, L.bn);
   BwdArgs a{};
   a.h = h_s;
   a.W = W_s;
-  a.idx = idx;
-  a.n_active = na;
   a.N = (int)N;
   a.H = (int)H_s;
   a.V = (int)V;
-  a.Npad = (int)bwd_npad(N);
+  a.Npad = (int)bwd_npad(N, H_s);
   a.inv_t = inv_t;
   a.dh = dh_s;
   a.dW = dW_s;
   a.hT = carve<uint16_t>(workspace, L.hT);
   a.Gv = carve<uint16_t>(workspace, L.Gv);
-  for (int q = 0; q < kDhPieces; ++q) a.dhp[q] = carve<float>(workspace, L.dhp[q]);
+  a.dhp[0] = nullptr;  // piece 0 accumulates in dh_s's rows
+  for (int q = 1; q < kDhPieces; ++q) a.dhp[q] = carve<float>(workspace, L.dhp[q]);
   a.sched = carve<int>(workspace, L.sched);
+  a.idx = bidx;
+  a.n_active = bn;
   float* xs = carve<float>(workspace, L.total);
-  float* xt = carve<float>(workspace, L.total + kl_chunk_bytes(N));
+  float* xt = carve<float>(workspace, L.total + kl_chunk_bytes(N, H_s));
   KlArgs k{};
-  k.idx = idx;
-  k.n_active = na;
+  k.idx = bidx;
+  k.n_active = bn;
   k.N = (int)N;
   k.V = (int)V;
   k.inv_t = inv_t;
@@ -550,30 +595,45 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
   k.kl_rev_in = kl_rev;
   k.coef = coef;
   k.Gv = a.Gv;
+  const int nblk = bwd_blocks(N, H_s);
   CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
+  c.block_desc = desc;
+  c.nblk = nblk;
+  c.block_cap = (int)bwd_token_cap(H_s);
   hipError_t e = launch_compact(c, st);
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
-  e = launch_bwd_prepare(a, st);
+  e = launch_zero(dh_s, (size_t)N * (size_t)H_s, st);  // inactive rows stay 0
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
   const int nchunks = (int)((V + kBwdChunk - 1) / kBwdChunk);
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int64_t c0 = (int64_t)ch * kBwdChunk;
-    const int vc = (int)(V - c0 < kBwdChunk ? V - c0 : kBwdChunk);
-    // both heads' x of the chunk (no statistics), then dL/dz of the chunk into Gv
-    FwdTileArgs t{h_t, static_cast<const uint8_t*>(W_t) + (size_t)c0 * H_t * 2, nullptr, idx, na,
-                  (int)N, (int)H_t, vc, inv_t, nullptr, nullptr, nullptr, (int)c0, nullptr, xt};
-    e = launch_fwd_tiles(t, true, grid, st, kFwdStoreX);
+  for (int b = 0; b < nblk; ++b) {
+    // the token block's compacted indices and count, copied for the kernels that follow
+    e = launch_select_block(idx, desc, b, a.Npad, bidx, bn, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
-    FwdTileArgs u{h_s, static_cast<const uint8_t*>(W_s) + (size_t)c0 * H_s * 2, nullptr, idx, na,
-                  (int)N, (int)H_s, vc, inv_t, nullptr, nullptr, nullptr, (int)c0, nullptr, xs};
-    e = launch_fwd_tiles(u, true, grid, st, kFwdStoreX);
+    e = launch_bwd_transpose(a, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
-    e = launch_kl_grad(k, (int)c0, a.Npad, reverse != 0, st);
-    if (e != hipSuccess) return RLK_ERROR_DEVICE;
-    e = launch_bwd_chunk_gemms(a, ch, grid, st);
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int64_t c0 = (int64_t)ch * kBwdChunk;
+      const int vc = (int)(V - c0 < kBwdChunk ? V - c0 : kBwdChunk);
+      // both heads' x of the chunk (no statistics), then dL/dz of the chunk into Gv
+      FwdTileArgs t{h_t, static_cast<const uint8_t*>(W_t) + (size_t)c0 * H_t * 2, nullptr, a.idx,
+                    a.n_active, (int)N, (int)H_t, vc, inv_t, nullptr, nullptr, nullptr, (int)c0,
+                    nullptr, xt};
+      e = launch_fwd_tiles(t, true, grid, st, kFwdStoreX);
+      if (e != hipSuccess) return RLK_ERROR_DEVICE;
+      FwdTileArgs u{h_s, static_cast<const uint8_t*>(W_s) + (size_t)c0 * H_s * 2, nullptr, a.idx,
+                    a.n_active, (int)N, (int)H_s, vc, inv_t, nullptr, nullptr, nullptr, (int)c0,
+                    nullptr, xs};
+      e = launch_fwd_tiles(u, true, grid, st, kFwdStoreX);
+      if (e != hipSuccess) return RLK_ERROR_DEVICE;
+      e = launch_kl_grad(k, (int)c0, a.Npad, reverse != 0, st);
+      if (e != hipSuccess) return RLK_ERROR_DEVICE;
+      e = launch_bwd_chunk_gemms(a, ch, grid, b > 0, st);
+      if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    }
+    e = launch_bwd_finish(a, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
   }
-  return dev_status(launch_bwd_finish(a, st));
+  return RLK_SUCCESS;
 }
 
 rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* targets,

@@ -27,11 +27,16 @@
 //                is read as a K-strided panel).
 // dh_chunk and dw_chunk run as the two sections of one launch (grad_chunk_kernel): the
 // dL/dW tiles are claimed at run time, so they fill the last round of dL/dh tiles.
-// Before the first chunk, bwd_prepare zeroes dh (its inactive rows stay 0) and writes hT =
-// compacted h transposed; the first chunk's dL/dh tiles store into the piece buffers and
-// later chunks add to them; after the last, bwd_finish writes dh[idx[m]] as the sum of the
-// pieces in ascending order.  The chunks and pieces are build constants, so a token's dh row
-// is the same sum in the same order in every batch.
+// The active tokens are taken in blocks (compacted order, at most the buffers' capacity, all of
+// one size but the last), each block a batch of its own for every kernel here (idx and
+// n_active hold the block's indices and count), so the buffers hold one block and the workspace
+// stops growing with N.  dh is zeroed once (its inactive rows stay 0).  Per block: hT = the
+// block's h rows transposed; per chunk the three steps above, the first chunk's dL/dh tiles
+// storing into the token's dh row (piece 0) and the piece buffers and later chunks adding to
+// them, the first block's dL/dW tiles storing and later blocks adding; after the last chunk,
+// bwd_finish adds the other pieces to dh[idx[m]] in ascending order.  The chunks and
+// pieces are build constants, so a token's dh row is the same sum in the same order in every
+// batch, whatever block it falls in; dW sums the blocks in ascending order.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mainloop.hpp"
@@ -279,16 +284,27 @@ __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
   };
 
   // Accumulator rows are hidden columns, columns are tokens: a lane holds 4 consecutive
-  // hidden columns per register group, added into its token's compacted row 16 bytes at a
-  // time (dhp rows start 16-byte aligned: 256-byte aligned buffers, H % 256 == 0).
+  // hidden columns per register group, added into its token's row 16 bytes at a time.  Piece
+  // 0 accumulates in dh's own row of the token (idx[m]); pieces 1-3 in the token's compacted
+  // row of dhp[piece].  Every row starts 16-byte aligned: dh and the 256-byte aligned dhp
+  // buffers are 16-byte aligned and H % 256 == 0.
+  //
+  // The piece's buffer is chosen once per tile, in wave-uniform code before the per-lane
+  // branch: chosen inside it (a nested select under a divergent mask), this compiler sent
+  // piece 3's stores of half the lanes to piece 1's buffer.
   auto epilogue = [&](const RowColCtx& c, Acc& acc) {
     static_assert(kDhPieces == 4, "piece buffers");
-    float* out = c.piece == 0 ? a.dhp[0] : c.piece == 1 ? a.dhp[1] : c.piece == 2 ? a.dhp[2] : a.dhp[3];
+    float* const base = c.piece == 0   ? a.dh
+                        : c.piece == 1 ? a.dhp[1]
+                        : c.piece == 2 ? a.dhp[2]
+                                       : a.dhp[3];
+    const bool in_dh = c.piece == 0;
 #pragma unroll
     for (int j = 0; j < kBlkB; ++j) {
       const int m = c.bbase + wb + acc_col(j, lane);
       if (m < Na) {
-        float* row = out + (size_t)m * a.H + c.abase + wa;
+        const size_t r = in_dh ? (size_t)a.idx[m] : (size_t)m;
+        float* row = base + r * a.H + c.abase + wa;
 #pragma unroll
         for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
@@ -308,19 +324,18 @@ __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
   persistent_tiles<true, RowColCtx, true, false, kSpread>(sm, per_piece * npiece, setup, epilogue);
 }
 
-// dh[idx[m]] = ((dhp[0][m] + dhp[1][m]) + dhp[2][m]) + dhp[3][m] over the kP pieces the first
+// dh[idx[m]] = ((dh[idx[m]] + dhp[1][m]) + dhp[2][m]) + dhp[3][m] over the kP pieces the first
 // chunk has (every later chunk has at most as many, and adds to them; the others were never
-// written).  A work-group walks rows m = blockIdx.x, blockIdx.x + gridDim.x, ...; its threads
-// read 4 consecutive entries of each piece (16-byte aligned rows) and store them one by one
-// (dh is only 4-byte aligned).
+// written), piece 0 being the sum dh[idx[m]] already holds.  A work-group walks rows
+// m = blockIdx.x, blockIdx.x + gridDim.x, ...; its threads take 4 consecutive entries at a time.
 template <int kP>
 __global__ __launch_bounds__(256) void dh_finish_kernel(BwdArgs a) {
   const int Na = *a.n_active;
   const int h4 = a.H / 4;
   for (int m = blockIdx.x; m < Na; m += gridDim.x) {
-    float* out = a.dh + (size_t)a.idx[m] * a.H;
+    f32x4* out = reinterpret_cast<f32x4*>(a.dh + (size_t)a.idx[m] * a.H);
     for (int k = threadIdx.x; k < h4; k += 256) {
-      f32x4 v = reinterpret_cast<const f32x4*>(a.dhp[0] + (size_t)m * a.H)[k];
+      f32x4 v = out[k];
 #pragma unroll
       for (int q = 1; q < kP; ++q) {
         const f32x4 w = reinterpret_cast<const f32x4*>(a.dhp[q] + (size_t)m * a.H)[k];
@@ -329,10 +344,7 @@ __global__ __launch_bounds__(256) void dh_finish_kernel(BwdArgs a) {
         v.z += w.z;
         v.w += w.w;
       }
-      out[4 * k + 0] = v.x;
-      out[4 * k + 1] = v.y;
-      out[4 * k + 2] = v.z;
-      out[4 * k + 3] = v.w;
+      out[k] = v;
     }
   }
 }
@@ -340,10 +352,13 @@ __global__ __launch_bounds__(256) void dh_finish_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- dW rows = Gv^T hT^T
 
 // kClaimed: tiles claimed from the XCD counters in a.sched (claimed_tiles) instead of the fixed
-// order.
-template <bool kClaimed>
+// order.  kAccum: a later token block, whose sums are added to the dL/dW rows the earlier blocks
+// stored (the first block stores, so dW is the blocks' sums in ascending block order); an empty
+// later block changes nothing and returns at once.
+template <bool kClaimed, bool kAccum>
 __device__ __forceinline__ void dw_chunk_tiles(RingSmem& sm, const BwdArgs& a, int c0) {
   const int Na = *a.n_active;
+  if (kAccum && Na == 0) return;
   const int vc = min(kBwdChunk, a.V - c0);
   const int nVocTiles = (vc + kTile - 1) / kTile;
   const int nHTiles = a.H / kTile;
@@ -378,18 +393,35 @@ __device__ __forceinline__ void dw_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
     }
   };
 
+  // A later block adds to the stored rows: per 32-row block of the tile, all 32 of the lane's
+  // old values are loaded before any is added and stored back, so the loads are in flight
+  // together instead of one load-add-store chain after another.
   auto epilogue = [&](const RowColCtx& c, Acc& acc) {
 #pragma unroll
-    for (int i = 0; i < kBlkA; ++i)
+    for (int i = 0; i < kBlkA; ++i) {
+      float old[16][kBlkB];
+      if constexpr (kAccum) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = c0 + c.abase + wa + acc_row(i, r, lane);
+          const float* row = a.dW + (size_t)(v < a.V ? v : a.V - 1) * a.H + c.bbase + wb;
+#pragma unroll
+          for (int j = 0; j < kBlkB; ++j) old[r][j] = row[acc_col(j, lane)];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = c0 + c.abase + wa + acc_row(i, r, lane);
         if (v < a.V) {
           float* row = a.dW + (size_t)v * a.H + c.bbase + wb;
 #pragma unroll
-          for (int j = 0; j < kBlkB; ++j) row[acc_col(j, lane)] = acc.c[i][j][r];
+          for (int j = 0; j < kBlkB; ++j)
+            row[acc_col(j, lane)] = kAccum ? old[r][j] + acc.c[i][j][r] : acc.c[i][j][r];
         }
       }
+      // one block at a time: keeps the live ranges short
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   if constexpr (kClaimed)
@@ -404,9 +436,10 @@ __global__ __launch_bounds__(kThreads) void dh_chunk_kernel(BwdArgs a, int c0) {
   dh_chunk_tiles<kFirst, false>(sm, a, c0);
 }
 
+template <bool kAccum>
 __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
   __shared__ RingSmem sm;
-  dw_chunk_tiles<false>(sm, a, c0);
+  dw_chunk_tiles<false, kAccum>(sm, a, c0);
 }
 
 // Both GEMMs of a chunk in one launch: each work-group first takes its dL/dh tiles in the
@@ -415,11 +448,11 @@ __global__ __launch_bounds__(kThreads) void dw_chunk_kernel(BwdArgs a, int c0) {
 // last round of dL/dh with dL/dW tiles.  The two are independent (both read Gv; dL/dh writes
 // dhp, dL/dW writes dW), and which work-group computes a tile changes no result: the
 // separate launches give the same bits.
-template <bool kFirst>
+template <bool kFirst, bool kAccum>
 __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, int c0) {
   __shared__ RingSmem sm;
   dh_chunk_tiles<kFirst, true>(sm, a, c0);
-  dw_chunk_tiles<true>(sm, a, c0);
+  dw_chunk_tiles<true, kAccum>(sm, a, c0);
 }
 
 }  // namespace
@@ -431,56 +464,63 @@ hipError_t launch_zero(float* p, size_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream) {
-  hipError_t e = launch_zero(a.dh, (size_t)a.N * a.H, stream);
-  if (e != hipSuccess) return e;
+hipError_t launch_bwd_transpose(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(transpose_h_kernel, dim3(a.Npad / 64, a.H / 256), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-// The combined launch for batches of at most this many tokens.  There the GEMMs have few
-// tiles per chunk (at 2053 active tokens, 576 dL/dh tiles: 2.25 rounds of 256 work-groups)
-// and the combined launch made the backward 6% faster; at 16384 tokens (9831 active) it was
-// ~1% slower than two launches: the chip is at its power limit there, and dL/dW tiles started
-// at staggered times share fewer L2 panels.  A scheduling choice only: the bits are the same.
+// The combined launch for token blocks of at most this many tokens.  There the GEMMs have few tiles per chunk (at 2053 active
+// tokens, 576 dL/dh tiles: 2.25 rounds of 256 work-groups) and the combined launch made the
+// backward 6% faster; with all of 9831 active tokens in one pass it was ~1% slower than two
+// launches: the chip is at its power limit there, and dL/dW tiles started at staggered times
+// share fewer L2 panels.  A scheduling choice only: the bits are the same.
 constexpr int64_t kCombinedMaxTokens = 4096;
 
-static hipError_t launch_grad_chunk(const BwdArgs& a, int c0, int grid, hipStream_t stream) {
-  if (a.N <= kCombinedMaxTokens) {
+template <bool kFirst, bool kAccum>
+static void launch_two(const BwdArgs& a, int c0, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(dh_chunk_kernel<kFirst>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  hipLaunchKernelGGL(dw_chunk_kernel<kAccum>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+}
+
+static hipError_t launch_grad_chunk(const BwdArgs& a, int c0, int grid, bool accum_dw,
+                                    hipStream_t stream) {
+  const bool first = c0 == 0;
+  if (a.Npad <= kCombinedMaxTokens) {
     hipError_t e = launch_zero(reinterpret_cast<float*>(a.sched), 8, stream);  // claim counters
     if (e != hipSuccess) return e;
-    if (c0 == 0)
-      hipLaunchKernelGGL(grad_chunk_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-    else
-      hipLaunchKernelGGL(grad_chunk_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+    auto k = first ? (accum_dw ? grad_chunk_kernel<true, true> : grad_chunk_kernel<true, false>)
+                   : (accum_dw ? grad_chunk_kernel<false, true> : grad_chunk_kernel<false, false>);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+  } else if (first) {
+    if (accum_dw) launch_two<true, true>(a, c0, grid, stream);
+    else launch_two<true, false>(a, c0, grid, stream);
   } else {
-    if (c0 == 0)
-      hipLaunchKernelGGL(dh_chunk_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-    else
-      hipLaunchKernelGGL(dh_chunk_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-    hipLaunchKernelGGL(dw_chunk_kernel, dim3(grid), dim3(kThreads), 0, stream, a, c0);
+    if (accum_dw) launch_two<false, true>(a, c0, grid, stream);
+    else launch_two<false, false>(a, c0, grid, stream);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t stream) {
+hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, bool accum_dw,
+                            hipStream_t stream) {
   const int c0 = chunk * kBwdChunk;
   if (a.ent_coef)
     hipLaunchKernelGGL(dlogits_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
   else
     hipLaunchKernelGGL(dlogits_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a, c0);
-  return launch_grad_chunk(a, c0, grid, stream);
+  return launch_grad_chunk(a, c0, grid, accum_dw, stream);
 }
 
-hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, hipStream_t stream) {
+hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, bool accum_dw,
+                                  hipStream_t stream) {
   const int c0 = chunk * kBwdChunk;
-  return launch_grad_chunk(a, c0, grid, stream);
+  return launch_grad_chunk(a, c0, grid, accum_dw, stream);
 }
 
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {
   const int kc0 = ((a.V < kBwdChunk ? a.V : kBwdChunk) + 63) / 64 * 64;  // first chunk's K extent
   switch ((kc0 + kDhSplitK - 1) / kDhSplitK) {
-    case 1: hipLaunchKernelGGL(dh_finish_kernel<1>, dim3(2048), dim3(256), 0, stream, a); break;
+    case 1: break;  // one piece: dh holds the result already
     case 2: hipLaunchKernelGGL(dh_finish_kernel<2>, dim3(2048), dim3(256), 0, stream, a); break;
     case 3: hipLaunchKernelGGL(dh_finish_kernel<3>, dim3(2048), dim3(256), 0, stream, a); break;
     default: hipLaunchKernelGGL(dh_finish_kernel<4>, dim3(2048), dim3(256), 0, stream, a); break;

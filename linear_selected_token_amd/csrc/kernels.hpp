@@ -10,6 +10,9 @@ constexpr int kVocabPartial = 128;  // vocabulary entries per partial-statistics
 constexpr int kBwdChunk = 65536;    // vocabulary entries per backward chunk (build constant)
 constexpr int kDhSplitK = 16384;    // dL/dh sums each 16384-entry piece of a chunk apart
 constexpr int kDhPieces = kBwdChunk / kDhSplitK;  // pieces of a full chunk (4)
+// The backward (and the KL paths) take the active tokens in blocks of at most a capacity the
+// host derives from H (a multiple of 256, at most 65536), in compacted order: its buffers hold
+// one block, so the workspace does not grow past that many tokens.
 // Row pitch (entries) of the token-major chunk buffers: the chunk plus 128 bytes, so that the
 // rows a wave writes at once (32 tokens) do not all start at the same 64 KiB-aligned offset.
 constexpr int kGvPitch = kBwdChunk + 64;  // bf16 dL/dz
@@ -25,7 +28,21 @@ struct CompactArgs {
   int N;
   float* entropy = nullptr;  // may be null: 0 at inactive tokens
   float* extra = nullptr;    // may be null: 0 at inactive tokens
+  // Token blocks of at most block_cap compacted indices (block_cap a multiple of 256), for
+  // nblk blocks (the host's bound, at most 1024):
+  //   block_count [nblk]     fixed blocks b * block_cap ...: active tokens of each (may be null)
+  //   block_desc  [nblk][2]  balanced blocks (count, first compacted index): the active tokens
+  //                          cut into ceil(Na / block_cap) blocks of one size, a multiple of 256
+  //                          but for the last (may be null)
+  int32_t* block_count = nullptr;
+  int32_t* block_desc = nullptr;
+  int nblk = 0;
+  int block_cap = 0;
 };
+
+// Copies block b of the balanced partition: bidx[0 .. count) = idx[first ..], *bn = count.
+hipError_t launch_select_block(const int32_t* idx, const int32_t* desc, int b, int cap,
+                               int32_t* bidx, int32_t* bn, hipStream_t stream);
 
 struct FwdTileArgs {
   const void* h;
@@ -85,8 +102,11 @@ struct BwdArgs {
   float* dW;              // [V, H]
   uint16_t* hT;           // [H, Npad]   compacted h, transposed, zero past Na
   uint16_t* Gv;           // [Npad, kGvPitch] dL/dz of the chunk, token-major
-  float* dhp[kDhPieces];  // [Npad, H] each: dL/dh from piece q of every chunk, compacted rows
+  float* dhp[kDhPieces];  // [Npad, H] each for q >= 1: dL/dh from piece q of every chunk,
+                          // compacted rows; piece 0 accumulates in place in dh's own rows
   int* sched;             // [8] tile-claim counters of the dL/dW section (zeroed per launch)
+  // A token block: idx and n_active hold the block's compacted indices and its count (at most
+  // Npad), so every kernel sees the block as a batch of its own.
   // entropy bonus (both null without it): L gains -sum_t mask_t c_t H_t
   const float* ent_coef = nullptr;  // [N] c_t
   const float* entropy = nullptr;   // [N] H_t from the entropy forward
@@ -100,10 +120,13 @@ hipError_t launch_logits_logp(const LogitsArgs& a, bool bf16, hipStream_t stream
 
 // Backward phases.
 hipError_t launch_zero(float* p, size_t n, hipStream_t stream);
-hipError_t launch_bwd_prepare(const BwdArgs& a, hipStream_t stream);          // dh = 0, hT
-hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, hipStream_t stream);
+hipError_t launch_bwd_transpose(const BwdArgs& a, hipStream_t stream);  // hT of the block
+// accum_dw: add the block's dL/dW to what earlier blocks stored (the first block stores)
+hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, bool accum_dw,
+                            hipStream_t stream);
 // dL/dh and dL/dW of one chunk from a Gv written elsewhere
-hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, hipStream_t stream);
+hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, bool accum_dw,
+                                  hipStream_t stream);
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dh[idx] = sum of pieces
 
 }  // namespace rlk

@@ -105,26 +105,59 @@ inline DiagLayout diag_layout(int64_t N) {
 constexpr int64_t kBwdChunkEntries = 65536;
 constexpr int kBwdDhPieces = 4;  // dL/dh pieces of a full chunk (16384 entries each)
 
-inline int64_t bwd_npad(int64_t N) { return ((N > 0 ? N : 1) + 255) / 256 * 256; }
+// The backward takes the active tokens in blocks (compacted order) and its buffers hold one
+// block: per token of capacity, a row of the bf16 dL/dz chunk, three fp32 dL/dh piece rows
+// (the first piece accumulates in dh itself) and a bf16 column of the transposed h.  The
+// capacity is the largest multiple of 256 tokens whose buffers fit this budget (at least 256):
+// 5120 tokens at H = 4096, 4096 at H = 7168.
+constexpr size_t kBwdBlockBudget = 1000000000;  // bytes
 
-// Workspace layout of the backward: idx[N] | n_active | sched[8] | hT[H, Npad] | Gv[Npad, chunk] (bf16)
-// | dhp[4][Npad, H] (fp32).
+inline size_t bwd_bytes_per_token(int64_t H) {
+  return 2 * (size_t)(kBwdChunkEntries + 64) + 4 * (kBwdDhPieces - 1) * (size_t)H + 2 * (size_t)H;
+}
+
+inline int64_t bwd_token_cap(int64_t H) {
+  const int64_t c = (int64_t)(kBwdBlockBudget / bwd_bytes_per_token(H > 0 ? H : 1)) / 256 * 256;
+  return c < 256 ? 256 : c;
+}
+
+// Token blocks for N tokens (an upper bound: it assumes every token is active; blocks past the
+// active tokens do nothing).  At most 586 for the shapes check_shape accepts (N <= 2^22 and
+// h <= 2^31 bytes bound N by the capacity's H).
+inline int bwd_blocks(int64_t N, int64_t H) {
+  const int64_t cap = bwd_token_cap(H);
+  return (int)(((N > 0 ? N : 1) + cap - 1) / cap);
+}
+
+// Token capacity of the block buffers: min(N, capacity) rounded up to the 256-token tile.
+inline int64_t bwd_npad(int64_t N, int64_t H) {
+  const int64_t cap = bwd_token_cap(H);
+  const int64_t n = N <= 0 ? 1 : (N < cap ? N : cap);
+  return (n + 255) / 256 * 256;
+}
+
+// Workspace layout of the backward: idx[N] | n_active | block_desc[blocks][2] | bidx[Npad] |
+// bn | sched[8] | hT[H, Npad] | Gv[Npad, chunk] (bf16) | dhp[1..3][Npad, H] (fp32).
 struct BwdLayout {
-  size_t idx, n_active, sched, hT, Gv, dhp[kBwdDhPieces], total;
+  size_t idx, n_active, block_desc, bidx, bn, sched, hT, Gv, dhp[kBwdDhPieces], total;
 };
 
 inline BwdLayout bwd_layout(int64_t N, int64_t H) {
   BwdLayout L;
   const size_t n = (size_t)(N > 0 ? N : 1);
-  const size_t np = (size_t)bwd_npad(N);
+  const size_t np = (size_t)bwd_npad(N, H);
   const size_t c = (size_t)kBwdChunkEntries;
   size_t o = 0;
-  L.idx = o;      o = align_up(o + 4 * n, 256);
-  L.n_active = o; o = align_up(o + 4, 256);
-  L.sched = o;    o = align_up(o + 4 * 8, 256);
-  L.hT = o;       o = align_up(o + 2 * (size_t)H * np, 256);
-  L.Gv = o;       o = align_up(o + 2 * np * (c + 64), 256);  // rows of kGvPitch entries
-  for (int q = 0; q < kBwdDhPieces; ++q) {
+  L.idx = o;        o = align_up(o + 4 * n, 256);
+  L.n_active = o;   o = align_up(o + 4, 256);
+  L.block_desc = o; o = align_up(o + 8 * (size_t)bwd_blocks(N, H), 256);
+  L.bidx = o;       o = align_up(o + 4 * np, 256);
+  L.bn = o;         o = align_up(o + 4, 256);
+  L.sched = o;      o = align_up(o + 4 * 8, 256);
+  L.hT = o;         o = align_up(o + 2 * (size_t)H * np, 256);
+  L.Gv = o;         o = align_up(o + 2 * np * (c + 64), 256);  // rows of kGvPitch entries
+  L.dhp[0] = 0;     // piece 0 accumulates in dh's rows
+  for (int q = 1; q < kBwdDhPieces; ++q) {
     L.dhp[q] = o;
     o = align_up(o + 4 * np * (size_t)H, 256);
   }
@@ -200,43 +233,45 @@ inline rlk_status_t check_bwd(const void* h, const void* W, const int32_t* targe
   if (N == 0) return RLK_SUCCESS;  // dW is still zeroed by the caller-visible contract
   if (!h || !W || !targets || !mask || !adv || !lse || !dh || !ws) return RLK_ERROR_INVALID_VALUE;
   if (!aligned(h, 16) || !aligned(W, 16) || !aligned(targets, 4) || !aligned(adv, 4) ||
-      !aligned(lse, 4) || !aligned(dh, 4) || !aligned(dW, 4) || !aligned(ws, 256))
+      !aligned(lse, 4) || !aligned(dh, 16) || !aligned(dW, 4) || !aligned(ws, 256))
     return RLK_ERROR_UNSUPPORTED;
   if (ws_bytes < bwd_layout(N, H).total) return RLK_ERROR_WORKSPACE;
   return RLK_SUCCESS;
 }
 
-// Full-vocabulary KL: one chunk of each head's x, [Npad][chunk] fp32.
-inline size_t kl_chunk_bytes(int64_t N) {
-  return align_up(4 * (size_t)bwd_npad(N) * (size_t)(kBwdChunkEntries + 32), 256);  // kXPitch
+// Full-vocabulary KL: one chunk of each head's x for one token block, [Npad][chunk] fp32
+// (the KL paths take the active tokens in the backward's blocks, sized for the student's H).
+inline size_t kl_chunk_bytes(int64_t N, int64_t H) {
+  return align_up(4 * (size_t)bwd_npad(N, H) * (size_t)(kBwdChunkEntries + 32), 256);  // kXPitch
 }
 
 struct KlLayout {
-  size_t idx, n_active, tmax, tsum, smax, ssum, wf, wr, xs, xt, total;
+  size_t idx, n_active, block_count, tmax, tsum, smax, ssum, wf, wr, xs, xt, total;
 };
 
-inline KlLayout kl_fwd_layout(int64_t N, int64_t V) {
+inline KlLayout kl_fwd_layout(int64_t N, int64_t H, int64_t V) {
   KlLayout L;
   const size_t n = (size_t)(N > 0 ? N : 1);
   const size_t jn = 4 * n * (size_t)num_partials(V);
   size_t o = 0;
   L.idx = o;      o = align_up(o + 4 * n, 256);
   L.n_active = o; o = align_up(o + 4, 256);
+  L.block_count = o; o = align_up(o + 4 * (size_t)bwd_blocks(N, H), 256);
   L.tmax = o;     o = align_up(o + jn, 256);
   L.tsum = o;     o = align_up(o + jn, 256);
   L.smax = o;     o = align_up(o + jn, 256);
   L.ssum = o;     o = align_up(o + jn, 256);
   L.wf = o;       o = align_up(o + jn, 256);
   L.wr = o;       o = align_up(o + jn, 256);
-  L.xs = o;       o += kl_chunk_bytes(N);
-  L.xt = o;       o += kl_chunk_bytes(N);
+  L.xs = o;       o += kl_chunk_bytes(N, H);
+  L.xt = o;       o += kl_chunk_bytes(N, H);
   L.total = o;
   return L;
 }
 
 // The backward's workspace, then the two chunk buffers.
 inline size_t kl_bwd_bytes(int64_t N, int64_t H) {
-  return bwd_layout(N, H).total + 2 * kl_chunk_bytes(N);
+  return bwd_layout(N, H).total + 2 * kl_chunk_bytes(N, H);
 }
 
 inline rlk_status_t check_kl(const void* hs, const void* Ws, const void* ht, const void* Wt,

@@ -8,6 +8,7 @@
 // the pointers below are plain numbers with the wanted alignment.
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstdio>
 #include <limits>
 #include <vector>
@@ -133,17 +134,38 @@ static void test_layouts() {
   for (int64_t N : {int64_t(1), int64_t(300), int64_t(4096), int64_t(16384), kMaxTokens})
     for (int64_t H : {int64_t(256), int64_t(4096), int64_t(7168), kMaxHidden}) {
       const BwdLayout L = bwd_layout(N, H);
-      const size_t np = (size_t)bwd_npad(N);
-      std::vector<size_t> off = {L.idx, L.n_active, L.sched, L.hT, L.Gv};
-      std::vector<size_t> sz = {4 * (size_t)N, 4, 32, 2 * (size_t)H * np,
-                                2 * np * (size_t)(kBwdChunkEntries + 64)};
-      for (int q = 0; q < kBwdDhPieces; ++q) {
+      const size_t np = (size_t)bwd_npad(N, H);
+      const int64_t cap = bwd_token_cap(H);
+      std::vector<size_t> off = {L.idx, L.n_active, L.block_desc, L.bidx, L.bn, L.sched, L.hT, L.Gv};
+      std::vector<size_t> sz = {4 * (size_t)N, 4, 8 * (size_t)bwd_blocks(N, H), 4 * np, 4, 32,
+                                2 * (size_t)H * np, 2 * np * (size_t)(kBwdChunkEntries + 64)};
+      for (int q = 1; q < kBwdDhPieces; ++q) {
         off.push_back(L.dhp[q]);
         sz.push_back(4 * np * (size_t)H);
       }
       expect_layout(off, sz, L.total);
-      EXPECT(np % 256 == 0 && np >= (size_t)N);
+      // the block buffers hold min(N, capacity) rows, rounded up to the 256-token tile, and the
+      // capacity's buffers fit the budget
+      EXPECT(cap % 256 == 0 && cap >= 256);
+      EXPECT((size_t)cap * bwd_bytes_per_token(H) <= kBwdBlockBudget || cap == 256);
+      EXPECT((size_t)(cap + 256) * bwd_bytes_per_token(H) > kBwdBlockBudget);
+      EXPECT(np % 256 == 0 && np >= (size_t)(N < cap ? N : cap) && np <= (size_t)cap);
+      EXPECT((int64_t)bwd_blocks(N, H) * cap >= N && (int64_t)(bwd_blocks(N, H) - 1) * cap < N);
+      // the compaction writes the block descriptors with one thread each: at most 1024 blocks
+      // for every shape the checks accept
+      if (check_shape(N, H, 151936, RLK_BF16) == RLK_SUCCESS) EXPECT(bwd_blocks(N, H) <= 1024);
+      // the block buffers are all the workspace but for the index and the block descriptors
+      EXPECT(L.total - L.hT <= (size_t)kBwdBlockBudget + 8 * 256);
     }
+  EXPECT(bwd_token_cap(4096) == 5120 && bwd_token_cap(7168) == 4096);
+  int max_blocks = 0;
+  for (int64_t H = 64; H <= kMaxHidden; H += 64) {
+    const int64_t n = std::min<int64_t>(kMaxTokens, kMaxHiddenStateBytes / (2 * H));
+    if (check_shape(n, H, 151936, RLK_BF16) == RLK_SUCCESS)
+      max_blocks = std::max(max_blocks, bwd_blocks(n, H));
+  }
+  EXPECT(max_blocks > 1 && max_blocks <= 1024);
+  EXPECT(bwd_blocks(0, 4096) == 1 && bwd_blocks(5120, 4096) == 1 && bwd_blocks(5121, 4096) == 2);
   for (int64_t N : {int64_t(0), int64_t(1), int64_t(1023), int64_t(1024), int64_t(1) << 20,
                     kMaxTokens}) {
     const DiagLayout D = diag_layout(N);
@@ -154,10 +176,12 @@ static void test_layouts() {
     expect_layout({G.idx, G.n_active}, {4 * n, 4}, G.total);
     EXPECT(loss_workspace(N) >= 32 * nb && loss_workspace(N) % 256 == 0);
     for (int64_t V : {int64_t(1), int64_t(151936), kMaxVocab}) {
-      const KlLayout K = kl_fwd_layout(N, V);
-      const size_t jn = 4 * n * (size_t)num_partials(V), c = kl_chunk_bytes(N);
-      expect_layout({K.idx, K.n_active, K.tmax, K.tsum, K.smax, K.ssum, K.wf, K.wr, K.xs, K.xt},
-                    {4 * n, 4, jn, jn, jn, jn, jn, jn, c, c}, K.total);
+      const KlLayout K = kl_fwd_layout(N, 4096, V);
+      const size_t jn = 4 * n * (size_t)num_partials(V), c = kl_chunk_bytes(N, 4096);
+      expect_layout({K.idx, K.n_active, K.block_count, K.tmax, K.tsum, K.smax, K.ssum, K.wf,
+                     K.wr, K.xs, K.xt},
+                    {4 * n, 4, 4 * (size_t)bwd_blocks(N, 4096), jn, jn, jn, jn, jn, jn, c, c},
+                    K.total);
     }
   }
 }
@@ -231,6 +255,8 @@ static void test_bwd() {
   EXPECT(call(300, 4096, RLK_BF16, 0, A, A, ws) == RLK_ERROR_INVALID_VALUE);
   EXPECT(call(300, 4096, RLK_BF16, A, A, A, ws, 0) == RLK_ERROR_INVALID_VALUE);
   EXPECT(call(300, 4096, RLK_BF16, ODD, A, A, ws) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(300, 4096, RLK_BF16, A + 4, A, A, ws) == RLK_ERROR_UNSUPPORTED);  // dh: 16 B
+  EXPECT(call(300, 4096, RLK_BF16, A + 16, A + 4, A, ws) == RLK_SUCCESS);     // dW: 4 B
   EXPECT(call(300, 4096, RLK_BF16, A, A, A + 64, ws) == RLK_ERROR_UNSUPPORTED);
 }
 

@@ -95,6 +95,58 @@ def test_schedules_agree_across_4096_tokens(H):
     assert torch.equal(dW1.view(torch.int32), dW2.view(torch.int32))
 
 
+def _token_cap(H):
+    """Token capacity of the backward's block buffers, by the rule the build states: the largest
+    multiple of 256 tokens whose buffers (131200 + 14 H bytes per token) fit 1e9 bytes."""
+    import re
+    import linear_selected_token_amd as rlk
+    m = re.search(r"multiple of 256 tokens whose buffers \((\d+) \+ (\d+) H bytes per token\) "
+                  r"fit (\d+) bytes", rlk.build_info())
+    assert m, rlk.build_info()
+    a, b, budget = (int(x) for x in m.groups())
+    return budget // (a + b * H) // 256 * 256
+
+
+# ~60% active of 22000 tokens at H = 256 (7168-token blocks): two equal blocks of the backward
+# and two more that hold no active token
+MULTI = wl.scaled_spec(3, N=22000, H=256, V=3000, n_seq=60, len_lo=128, len_hi=512, seed=141,
+                       targets="uniform", backward=True)
+
+
+def test_token_blocks_full():
+    # every active dL/dh row and every dL/dW row against the oracle when the active tokens
+    # span more than one token block of the backward, with an empty last block
+    w = wl.make(MULTI)
+    cap = _token_cap(w.H)
+    flush(f"  {w.n_active} active of {w.N}: token blocks of at most {cap}")
+    assert cap < w.n_active < 2 * cap and w.N > 3 * cap
+    _full_compare(w)
+
+
+def test_token_blocks_dh_invariance_and_dw():
+    # a token's dL/dh row keeps its bits whichever token block it falls in (alone, shuffled,
+    # padded, all tokens active: 22000 active, four blocks); dL/dW is deterministic and does not
+    # depend on padding or inactive rows (they never enter the compacted order)
+    fam = wl.Family(MULTI)
+    base = fam.batch()
+    _, _, dh, dW = run_bwd(base)
+    dh = dh.cpu().numpy()
+    ref = {k: dh[i] for i, k in enumerate(base.key()) if base.mask[i]}
+    for w in (fam.alone(17), fam.shuffled(7), fam.padded(8), fam.all_active()):
+        _, _, dh2, _ = run_bwd(w)
+        dh2 = dh2.cpu().numpy()
+        n = 0
+        for i, k in enumerate(w.key()):
+            if k[0] >= 0 and w.mask[i] and k in ref:
+                assert np.array_equal(bits(dh2[i]), bits(ref[k])), k
+                n += 1
+        flush(f"  {w.N} tokens, {w.n_active} active: {n} dh rows bit-identical")
+    _, _, _, dW2 = run_bwd(base)
+    assert torch.equal(dW.view(torch.int32), dW2.view(torch.int32))
+    _, _, _, dW3 = run_bwd(fam.padded(9))
+    assert torch.equal(dW.view(torch.int32), dW3.view(torch.int32))
+
+
 def test_all_masked_backward():
     import linear_selected_token_amd as rlk
     w = wl.make(SMALL)

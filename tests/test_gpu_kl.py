@@ -211,6 +211,26 @@ def test_bwd_qwen_head_sampled():
     assert_rows("dW (sampled rows)", dW[vr], odW, vr)
 
 
+def test_token_blocks_forward_and_backward():
+    # the KL paths take the active tokens in the backward's token blocks (7168 tokens at H = 256):
+    # 8437 active tokens of 9000 (two blocks), both directions against the oracle
+    w = wl.make(wl.scaled_spec(5, N=9000, H=256, V=2000, n_seq=18, len_lo=400, len_hi=600,
+                               seed=161, prompt="none", T=0.8))
+    w.mask[::16] = 0
+    ht, Wt = _teacher(w, 128, 162)
+    _check_fwd(w, ht, Wt)
+    c = np.random.default_rng(164).uniform(0.5, 1.5, w.N).astype(np.float32)
+    for reverse in (False, True):
+        dh, dW = _bwd(w, ht, Wt, reverse, c)
+        odh, odW = od.kl_grads(*(wl.as_f64(x) for x in (w.h, w.W, ht, Wt)), w.mask, w.T, c,
+                               reverse)
+        act = np.nonzero(w.mask)[0]
+        flush(f"  KL bwd over token blocks, reverse={reverse}, {act.size} active")
+        assert_rows("dh (every active row)", dh[act], odh[act], act)
+        assert_rows("dW (every vocabulary row)", dW, odW)
+        assert not dh[w.mask == 0].any()
+
+
 def test_empty_and_all_masked():
     import linear_selected_token_amd as rlk
     w = wl.make(SMALL)
