@@ -87,7 +87,10 @@ const char* rlk_build_info(void);
 int64_t rlk_num_vocab_partials(int64_t V);
 
 /* Workspace bytes needed by rlk_linear_logp_fwd / rlk_linear_logp_bwd for N tokens
- * (an upper bound: it assumes every token is active).  Host-only, no device work. */
+ * (an upper bound: it assumes every token is active).  Host-only, no device work.
+ * The forward's grows with N (8 bytes per token and 128-entry vocabulary column).  The
+ * backward's stops growing past one token block (see rlk_linear_logp_bwd): about 1e9 bytes at
+ * most, plus 4 bytes of index per token. */
 rlk_status_t rlk_linear_logp_fwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
                                                 size_t* bytes);
 rlk_status_t rlk_linear_logp_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
@@ -177,17 +180,24 @@ rlk_status_t rlk_logp_from_logits(const void* logits, int64_t ld, const int32_t*
                                   float temperature, float* logp, float* lse, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
-/* Backward of L = -sum_t mask_t * adv_t * logp_t (bf16 only).
+/* Backward of L = -sum_t mask_t * adv_t * logp_t (bf16 only, H a multiple of 256).
  *   h, W, targets, mask, N, H, V, dtype, temperature: exactly as passed to the forward
  *   adv      [N]    float     per-token advantage (the upstream gradient is -adv_t at
  *                             active tokens; pass adv = -dL/dlogp for another loss)
  *   lse      [N]    float     the forward's lse output for the same inputs
- *   dh       [N,H]  float     out, overwritten: dL/dh; rows of inactive tokens are 0
+ *   dh       [N,H]  float     out, overwritten: dL/dh; rows of inactive tokens are 0.
+ *                             16-byte aligned (it also serves as one of the partial sums)
  *   dW       [V,H]  float     out, overwritten: dL/dW
  *   workspace: at least rlk_linear_logp_bwd_workspace_size bytes.
  * The vocabulary is walked in fixed chunks; per chunk the logits are recomputed on MFMA,
- * turned into dL/dz (rounded to bf16), and multiplied into dh (accumulated in fp32 in
- * chunk order) and into the chunk's rows of dW. */
+ * turned into dL/dz (rounded to bf16), and multiplied into dh (accumulated in fp32 in a fixed
+ * order of vocabulary pieces) and into the chunk's rows of dW.  The active tokens are taken in
+ * blocks of equal size (the last shorter), at most the largest multiple of 256 tokens whose
+ * buffers (131200 + 14 H bytes per token) fit 1e9 bytes: 5120 tokens at H = 4096, 4096 at
+ * H = 7168.  The workspace holds one block, so it does not grow with N past that.  A token's
+ * dL/dh row does not depend on the block it falls in (bit-identical in any batch); dL/dW is
+ * the sum of the blocks' sums in ascending block order (deterministic, and independent of
+ * padding and inactive rows). */
 rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* targets,
                                  const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
                                  float temperature, const float* adv, const float* lse,
@@ -223,14 +233,15 @@ rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int
  *   kl_fwd[t] = sum_v p_t (log p_t - log p_s),  kl_rev[t] = sum_v p_s (log p_s - log p_t)
  * at active tokens, 0 elsewhere (both clamped at 0 against rounding).  The vocabulary is walked
  * in chunks of 65536 entries: per chunk each head's tile GEMM writes its column statistics
- * and its logits of that chunk only (fp32, [N rounded up to 256] x 65536 in the workspace),
- * a streaming kernel pairs the two entry by entry, and a fixed-order merge gives the results.
+ * and its logits of that chunk only (fp32, one token block of rlk_linear_logp_bwd's size for
+ * the student's H, x 65536 entries, in the workspace), a streaming kernel pairs the two entry
+ * by entry, and a fixed-order merge gives the results.
  * Batch-invariant like logp.  H_s and H_t: multiples of 64; each h at most 2^31 - 1 bytes.
  *   lse_s, lse_t [N] float     out (may be NULL): each head's log-sum-exp, which the backward
  *                              takes back
  *   workspace: rlk_linear_kl_fwd_workspace_size bytes: six float arrays of ceil(V/128) x N
  *              (both heads' column statistics and the two cross terms) and two chunk buffers of
- *              65568 floats per token, N rounded up to 256 (9.06 GB in all at N = 16384,
+ *              65568 floats per token of one block (3.15 GB in all at N = 16384, H_s = 4096,
  *              V = 151936). */
 rlk_status_t rlk_linear_kl_fwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
                                               int dtype, size_t* bytes);
@@ -246,7 +257,7 @@ rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t
  * are recomputed on MFMA, dL/dz is formed in a streaming kernel and rounded to bf16, and the
  * chunk's dL/dh_s and dL/dW_s follow as in rlk_linear_logp_bwd.
  *   coef [N] float; lse_s, lse_t [N] and (reverse only) kl_rev [N] from rlk_linear_kl_fwd
- *   dh_s [N,H_s], dW_s [V,H_s] float   out, overwritten
+ *   dh_s [N,H_s], dW_s [V,H_s] float   out, overwritten (dh_s 16-byte aligned)
  *   workspace: rlk_linear_kl_bwd_workspace_size bytes: rlk_linear_logp_bwd's workspace plus the
  *              two chunk buffers of the forward. */
 rlk_status_t rlk_linear_kl_bwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,

@@ -485,7 +485,10 @@ static void launch_two(const BwdArgs& a, int c0, int grid, hipStream_t stream) {
 static hipError_t launch_grad_chunk(const BwdArgs& a, int c0, int grid, bool accum_dw,
                                     hipStream_t stream) {
   const bool first = c0 == 0;
-  if (a.Npad <= kCombinedMaxTokens) {
+  // The ragged last chunk (20864 entries of the Qwen3-8B vocabulary) takes the combined launch
+  // at any block size: its dL/dh pieces have unequal K (16384 and 4480 entries), and the claimed
+  // dL/dW tiles fill the work-groups that drew short pieces (0.3 ms per step at 9831 tokens).
+  if (a.Npad <= kCombinedMaxTokens || a.V - c0 < kBwdChunk) {
     hipError_t e = launch_zero(reinterpret_cast<float*>(a.sched), 8, stream);  // claim counters
     if (e != hipSuccess) return e;
     auto k = first ? (accum_dw ? grad_chunk_kernel<true, true> : grad_chunk_kernel<true, false>)
