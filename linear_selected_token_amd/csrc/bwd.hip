@@ -23,8 +23,10 @@
 //                is 256 hidden columns x 256 tokens.  Piece q is added to dhp[q] (compacted
 //                rows), in chunk order; the pieces are independent tiles, so a chunk fills the
 //                machine even when few tokens are active;
-//   dw_chunk     dW[chunk rows] = Gv^T hT^T  (K = the active tokens in ascending order; Gv
-//                is read as a K-strided panel).
+//   dw_chunk     dW[chunk rows]^T = hT Gv  (K = the active tokens in ascending order; hT is
+//                the first operand, Gv the second, read as a K-strided panel, so a lane's four
+//                consecutive accumulator rows are four consecutive hidden columns of one dW row,
+//                written 16 bytes at a time).
 // dh_chunk and dw_chunk run as the two sections of one launch (grad_chunk_kernel): the
 // dL/dW tiles are claimed at run time, so they fill the last round of dL/dh tiles.
 // The active tokens are taken in blocks (compacted order, at most the buffers' capacity, all of
@@ -362,7 +364,7 @@ __device__ __forceinline__ void dw_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
   const int vc = min(kBwdChunk, a.V - c0);
   const int nVocTiles = (vc + kTile - 1) / kTile;
   const int nHTiles = a.H / kTile;
-  const int band = nHTiles < 8 ? nHTiles : 8;
+  const int band = nVocTiles < 8 ? nVocTiles : 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const size_t row_bytes = (size_t)a.Npad * 2;         // hT rows
@@ -371,63 +373,73 @@ __device__ __forceinline__ void dw_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
   const int wa = wave_a0(wave);
   const int wb = wave_b0(wave);
 
+  // A = hT rows of hidden columns abase .. (K = the block's tokens, contiguous), B = the chunk's
+  // dL/dz columns bbase .. read K-strided from the token-major Gv (a transposing panel).
   auto setup = [&](int u, TileSrc& src, RowColCtx& c) {
-    int vt, ht;
-    tile_coords(u, nVocTiles, nHTiles, band, vt, ht);
-    c.abase = vt * kTile;  // within the chunk
-    c.bbase = ht * kTile;
+    int ht, vt;
+    tile_coords(u, nHTiles, nVocTiles, band, ht, vt);
+    c.abase = ht * kTile;
+    c.bbase = vt * kTile;  // within the chunk
     c.piece = 0;
     src.nk = nk;
-    src.a_kstep = 64 * g_pitch;  // 64 token rows of Gv per stage
-    src.b_kstep = kKBytes;
-    src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + 2 * (size_t)c.abase);
-    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.hT) + (size_t)c.bbase * row_bytes);
-    src.a_bytes = operand_bytes((size_t)a.Npad * g_pitch - 2 * (size_t)c.abase);
-    src.b_bytes = operand_bytes((size_t)(a.H - c.bbase) * row_bytes);
+    src.a_kstep = kKBytes;
+    src.b_kstep = 64 * g_pitch;  // 64 token rows of Gv per stage
+    src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.hT) + (size_t)c.abase * row_bytes);
+    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + 2 * (size_t)c.bbase);
+    src.a_bytes = operand_bytes((size_t)(a.H - c.abase) * row_bytes);
+    src.b_bytes = operand_bytes((size_t)a.Npad * g_pitch - 2 * (size_t)c.bbase);
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
-      const int r = dma_row(q, wave, lane);
-      const int ch = dma_chunk(q, wave, lane);
-      src.ao[q] = (uint32_t)(tdma_row(q, wave, lane) * g_pitch) + 16 * tdma_chunk(q, wave, lane);
-      src.bo[q] = (uint32_t)((size_t)r * row_bytes) + 16 * ch;
+      src.ao[q] = (uint32_t)((size_t)dma_row(q, wave, lane) * row_bytes) + 16 * dma_chunk(q, wave, lane);
+      src.bo[q] = (uint32_t)(tdma_row(q, wave, lane) * g_pitch) + 16 * tdma_chunk(q, wave, lane);
     }
   };
 
-  // A later block adds to the stored rows: per 32-row block of the tile, all 32 of the lane's
-  // old values are loaded before any is added and stored back, so the loads are in flight
-  // together instead of one load-add-store chain after another.
+  // Accumulator rows are hidden columns, columns are vocabulary rows: a lane holds 4
+  // consecutive hidden columns of its vocabulary row per register group and writes them 16 bytes
+  // at a time (dW rows start 16-byte aligned: H % 256 == 0; the whole-row offset keeps dW's own
+  // alignment, which is checked).  A later block adds to the stored rows, its old values loaded
+  // (per vocabulary column of the wave) before any is added and stored back.
   auto epilogue = [&](const RowColCtx& c, Acc& acc) {
 #pragma unroll
-    for (int i = 0; i < kBlkA; ++i) {
-      float old[16][kBlkB];
-      if constexpr (kAccum) {
+    for (int j = 0; j < kBlkB; ++j) {
+      const int v = c0 + c.bbase + wb + acc_col(j, lane);
+      if (v < a.V) {
+        float* row = a.dW + (size_t)v * a.H + c.abase + wa;
+        f32x4 old[kBlkA][4];
+        if constexpr (kAccum) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = c0 + c.abase + wa + acc_row(i, r, lane);
-          const float* row = a.dW + (size_t)(v < a.V ? v : a.V - 1) * a.H + c.bbase + wb;
+          for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
-          for (int j = 0; j < kBlkB; ++j) old[r][j] = row[acc_col(j, lane)];
+            for (int g = 0; g < 4; ++g)
+              old[i][g] = *reinterpret_cast<const f32x4*>(row + acc_row(i, 4 * g, lane));
         }
-      }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = c0 + c.abase + wa + acc_row(i, r, lane);
-        if (v < a.V) {
-          float* row = a.dW + (size_t)v * a.H + c.bbase + wb;
+        for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
-          for (int j = 0; j < kBlkB; ++j)
-            row[acc_col(j, lane)] = kAccum ? old[r][j] + acc.c[i][j][r] : acc.c[i][j][r];
-        }
+          for (int g = 0; g < 4; ++g) {
+            f32x4 x;
+            x.x = acc.c[i][j][4 * g + 0];
+            x.y = acc.c[i][j][4 * g + 1];
+            x.z = acc.c[i][j][4 * g + 2];
+            x.w = acc.c[i][j][4 * g + 3];
+            if constexpr (kAccum) {
+              x.x += old[i][g].x;
+              x.y += old[i][g].y;
+              x.z += old[i][g].z;
+              x.w += old[i][g].w;
+            }
+            *reinterpret_cast<f32x4*>(row + acc_row(i, 4 * g, lane)) = x;
+          }
       }
-      // one block at a time: keeps the live ranges short
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   if constexpr (kClaimed)
-    claimed_tiles<true, RowColCtx, true, false>(sm, nVocTiles * nHTiles, a.sched, setup, epilogue);
+    claimed_tiles<true, RowColCtx, false, true>(sm, nVocTiles * nHTiles, a.sched, setup, epilogue);
   else
-    persistent_tiles<true, RowColCtx, true, false>(sm, nVocTiles * nHTiles, setup, epilogue);
+    persistent_tiles<true, RowColCtx, false, true>(sm, nVocTiles * nHTiles, setup, epilogue);
 }
 
 template <bool kFirst>
