@@ -430,7 +430,7 @@ def bench_kl(args, w):
 
     def step():
         _, kr, ls, lt = fwd()
-        rlk.rlk_linear_kl_bwd(h, W, ht, Wt, mask, T, False, coef, ls, lt, kr, workspace=ws_b)
+        rlk.rlk_linear_kl_bwd(h, W, ht, Wt, mask, T, coef, None, ls, lt, kr, workspace=ws_b)
 
     ms = timed(step)
     fwd_ms = timed(fwd)

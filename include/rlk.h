@@ -251,12 +251,14 @@ rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t
                                float* kl_fwd, float* kl_rev, float* lse_s, float* lse_t,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward of L = sum_t mask_t coef_t KL[t] into the student (bf16, H_s a multiple of 256); the
- * teacher is frozen.  reverse = 0: KL = kl_fwd, dL/dz_s = coef (p_s - p_t); reverse != 0:
- * KL = kl_rev, dL/dz_s = coef p_s (log p_s - log p_t - kl_rev).  Per chunk both heads' logits
- * are recomputed on MFMA, dL/dz is formed in a streaming kernel and rounded to bf16, and the
- * chunk's dL/dh_s and dL/dW_s follow as in rlk_linear_logp_bwd.
- *   coef [N] float; lse_s, lse_t [N] and (reverse only) kl_rev [N] from rlk_linear_kl_fwd
+/* Backward of L = sum_t mask_t (coef_fwd_t kl_fwd[t] + coef_rev_t kl_rev[t]) into the student
+ * (bf16, H_s a multiple of 256); the teacher is frozen.  Per chunk both heads' logits are
+ * recomputed on MFMA, dL/dz_s = (coef_fwd (p_s - p_t) + coef_rev p_s (log p_s - log p_t -
+ * kl_rev)) / T is formed in a streaming kernel and rounded to bf16, and the chunk's dL/dh_s and
+ * dL/dW_s follow as in rlk_linear_logp_bwd.
+ *   coef_fwd, coef_rev [N] float   dL/dkl_fwd and dL/dkl_rev per token; either may be NULL (that
+ *                                  term is absent), not both
+ *   lse_s, lse_t [N] and (with coef_rev) kl_rev [N]: from rlk_linear_kl_fwd
  *   dh_s [N,H_s], dW_s [V,H_s] float   out, overwritten (dh_s 16-byte aligned)
  *   workspace: rlk_linear_kl_bwd_workspace_size bytes: rlk_linear_logp_bwd's workspace plus the
  *              two chunk buffers of the forward. */
@@ -265,7 +267,7 @@ rlk_status_t rlk_linear_kl_bwd_workspace_size(int64_t N, int64_t H_s, int64_t H_
 rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t,
                                const void* W_t, const uint8_t* mask, int64_t N, int64_t H_s,
                                int64_t H_t, int64_t V, int dtype, float temperature,
-                               int reverse, const float* coef, const float* lse_s,
+                               const float* coef_fwd, const float* coef_rev, const float* lse_s,
                                const float* lse_t, const float* kl_rev, float* dh_s,
                                float* dW_s, void* workspace, size_t workspace_bytes,
                                void* stream);

@@ -55,7 +55,7 @@ SIGNATURES = {
                                  _p, _p, _sz, _p]),
     "rlk_linear_kl_bwd_workspace_size": (_int, [_i64, _i64, _i64, _i64, _int,
                                                 ctypes.POINTER(_sz)]),
-    "rlk_linear_kl_bwd": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _f, _int, _p,
+    "rlk_linear_kl_bwd": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _f, _p, _p,
                                  _p, _p, _p, _p, _p, _p, _sz, _p]),
     "rlk_ratio_kl_loss_workspace_size": (_int, [_i64, ctypes.POINTER(_sz)]),
     "rlk_ratio_kl_loss": (_int, [_p, _p, _p, _p, _p, _i64, _f, _f, _f, _f, _p, _p, _p, _p, _p,

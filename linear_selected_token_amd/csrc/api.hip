@@ -537,7 +537,7 @@ rlk_status_t rlk_linear_kl_bwd_workspace_size(int64_t N, int64_t H_s, int64_t H_
 rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t,
                                const void* W_t, const uint8_t* mask, int64_t N, int64_t H_s,
                                int64_t H_t, int64_t V, int dtype, float temperature,
-                               int reverse, const float* coef, const float* lse_s,
+                               const float* coef_fwd, const float* coef_rev, const float* lse_s,
                                const float* lse_t, const float* kl_rev, float* dh_s,
                                float* dW_s, void* workspace, size_t workspace_bytes,
                                void* stream) {
@@ -549,8 +549,10 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
   if (!aligned(dW_s, 4)) return RLK_ERROR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (N == 0) return dev_status(launch_zero(dW_s, (size_t)V * (size_t)H_s, st));
-  if (!coef || !lse_s || !lse_t || !dh_s || (reverse && !kl_rev)) return RLK_ERROR_INVALID_VALUE;
-  if (!aligned(coef, 4) || !aligned(lse_s, 4) || !aligned(lse_t, 4) || !aligned(kl_rev, 4) ||
+  if ((!coef_fwd && !coef_rev) || !lse_s || !lse_t || !dh_s || (coef_rev && !kl_rev))
+    return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(coef_fwd, 4) || !aligned(coef_rev, 4) || !aligned(lse_s, 4) || !aligned(lse_t, 4) ||
+      !aligned(kl_rev, 4) ||
       !aligned(dh_s, 16))
     return RLK_ERROR_UNSUPPORTED;
   if (workspace_bytes < kl_bwd_bytes(N, H_s)) return RLK_ERROR_WORKSPACE;
@@ -593,7 +595,8 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
   k.lse_s_in = lse_s;
   k.lse_t_in = lse_t;
   k.kl_rev_in = kl_rev;
-  k.coef = coef;
+  k.coef_f = coef_fwd;
+  k.coef_r = coef_rev;
   k.Gv = a.Gv;
   const int nblk = bwd_blocks(N, H_s);
   CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
@@ -625,7 +628,7 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
                     nullptr, xs};
       e = launch_fwd_tiles(u, true, grid, st, kFwdStoreX);
       if (e != hipSuccess) return RLK_ERROR_DEVICE;
-      e = launch_kl_grad(k, (int)c0, a.Npad, reverse != 0, st);
+      e = launch_kl_grad(k, (int)c0, a.Npad, st);
       if (e != hipSuccess) return RLK_ERROR_DEVICE;
       e = launch_bwd_chunk_gemms(a, ch, grid, b > 0, st);
       if (e != hipSuccess) return RLK_ERROR_DEVICE;

@@ -66,8 +66,9 @@ struct KlArgs {
   // backward
   const float* lse_s_in;
   const float* lse_t_in;
-  const float* kl_rev_in;  // reverse KL only
-  const float* coef;       // [N] c_t
+  const float* kl_rev_in;  // with coef_r only
+  const float* coef_f;     // [N] dL/dKL_fwd per token, or null
+  const float* coef_r;     // [N] dL/dKL_rev per token, or null (not both null)
   uint16_t* Gv;            // [Npad][kGvPitch]
 };
 
@@ -75,6 +76,6 @@ hipError_t launch_ratio_kl_loss(const LossArgs& a, double* sums, hipStream_t str
 hipError_t launch_dlogp_diagnostics(const DiagArgs& a, hipStream_t stream);
 hipError_t launch_kl_cross(const KlArgs& a, int c0, int rows, hipStream_t stream);
 hipError_t launch_kl_merge(const KlArgs& a, hipStream_t stream);
-hipError_t launch_kl_grad(const KlArgs& a, int c0, int rows, bool reverse, hipStream_t stream);
+hipError_t launch_kl_grad(const KlArgs& a, int c0, int rows, hipStream_t stream);
 
 }  // namespace rlk

@@ -16,10 +16,9 @@
 //                 KL_fwd = ln2 (A_f / S_t - (M_t + log2 S_t) + (M_s + log2 S_s))
 //                 KL_rev = ln2 (A_r / S_s - (M_s + log2 S_s) + (M_t + log2 S_t))
 //               with A_f = sum_j 2^(m_t,j - M_t) wf_j and A_r likewise.
-//   kl_grad     the backward's dL/dz of one chunk for L = sum_t c_t KL_t, rounded to bf16 in
-//               the token-major layout the dL/dh and dL/dW GEMMs read (Gv):
-//                 forward KL: (c_t / T)(p_s - p_t)
-//                 reverse KL: (c_t / T) p_s (ln p_s - ln p_t - KL_rev)
+//   kl_grad     the backward's dL/dz of one chunk for L = sum_t (f_t KL_fwd,t + r_t KL_rev,t),
+//               rounded to bf16 in the token-major layout the dL/dh and dL/dW GEMMs read (Gv):
+//                 (f_t / T)(p_s - p_t) + (r_t / T) p_s (ln p_s - ln p_t - KL_rev)
 //
 // Every reduction is a fixed in-lane order followed by a fixed xor tree, and the columns
 // are merged in one fixed order, so a token's results depend only on its own rows.
@@ -187,7 +186,8 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 // exit); each thread forms 4 consecutive entries per step, two steps at a time (both steps'
 // non-temporal loads issued first).  Rows past the active count and
 // entries past the vocabulary are written as 0, since the GEMMs that follow read them.
-template <bool kReverse>
+// kF / kR: the forward / reverse KL term is present (coef_f / coef_r given).
+template <bool kF, bool kR>
 __global__ __launch_bounds__(256) void kl_grad_kernel(KlArgs a, int c0) {
   const int Na = *a.n_active;
   const int i = blockIdx.x;
@@ -196,13 +196,16 @@ __global__ __launch_bounds__(256) void kl_grad_kernel(KlArgs a, int c0) {
   const int vc = min(kBwdChunk, a.V - c0);
   const int vt = (vc + 255) / 256 * 256;  // entries the tiles of the chunk cover
   const bool act = i < Na;
-  float lse2s = 0.f, lse2t = 0.f, cs = 0.f, klr = 0.f;
+  float lse2s = 0.f, lse2t = 0.f, cf = 0.f, cr = 0.f, klr = 0.f;
   if (act) {
     const int t = a.idx[i];
     lse2s = a.lse_s_in[t] * kLog2e;
     lse2t = a.lse_t_in[t] * kLog2e;
-    cs = a.coef[t] * a.inv_t;
-    if constexpr (kReverse) klr = a.kl_rev_in[t];
+    if constexpr (kF) cf = a.coef_f[t] * a.inv_t;
+    if constexpr (kR) {
+      cr = a.coef_r[t] * a.inv_t;
+      klr = a.kl_rev_in[t];
+    }
   }
   const float* xs_row = a.xs + (size_t)i * kXPitch;
   const float* xt_row = a.xt + (size_t)i * kXPitch;
@@ -218,10 +221,10 @@ __global__ __launch_bounds__(256) void kl_grad_kernel(KlArgs a, int c0) {
           const float ls = s4[e] - lse2s;  // log2 p_s
           const float lt = t4[e] - lse2t;
           const float ps = __builtin_amdgcn_exp2f(ls);
-          if constexpr (kReverse)
-            G[e] = cs * ps * __builtin_fmaf(ls - lt, kLn2, -klr);
-          else
-            G[e] = cs * (ps - __builtin_amdgcn_exp2f(lt));
+          float g = 0.f;
+          if constexpr (kF) g = cf * (ps - __builtin_amdgcn_exp2f(lt));
+          if constexpr (kR) g = __builtin_fmaf(cr * ps, __builtin_fmaf(ls - lt, kLn2, -klr), g);
+          G[e] = g;
         }
       }
     }
@@ -256,12 +259,14 @@ hipError_t launch_kl_merge(const KlArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_kl_grad(const KlArgs& a, int c0, int rows, bool reverse, hipStream_t stream) {
+hipError_t launch_kl_grad(const KlArgs& a, int c0, int rows, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  if (reverse)
-    hipLaunchKernelGGL(kl_grad_kernel<true>, dim3(rows), dim3(256), 0, stream, a, c0);
+  if (a.coef_f && a.coef_r)
+    hipLaunchKernelGGL((kl_grad_kernel<true, true>), dim3(rows), dim3(256), 0, stream, a, c0);
+  else if (a.coef_r)
+    hipLaunchKernelGGL((kl_grad_kernel<false, true>), dim3(rows), dim3(256), 0, stream, a, c0);
   else
-    hipLaunchKernelGGL(kl_grad_kernel<false>, dim3(rows), dim3(256), 0, stream, a, c0);
+    hipLaunchKernelGGL((kl_grad_kernel<true, false>), dim3(rows), dim3(256), 0, stream, a, c0);
   return hipGetLastError();
 }
 

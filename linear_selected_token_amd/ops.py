@@ -471,11 +471,13 @@ def rlk_linear_kl_fwd(h_s, W_s, h_t, W_t, mask, temperature: float,
     return tuple(outs)
 
 
-def rlk_linear_kl_bwd(h_s, W_s, h_t, W_t, mask, temperature: float, reverse: bool,
-                      coef: torch.Tensor, lse_s: torch.Tensor, lse_t: torch.Tensor,
+def rlk_linear_kl_bwd(h_s, W_s, h_t, W_t, mask, temperature: float,
+                      coef_fwd: Optional[torch.Tensor], coef_rev: Optional[torch.Tensor],
+                      lse_s: torch.Tensor, lse_t: torch.Tensor,
                       kl_rev: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None):
-    """Gradients of L = sum_t mask_t coef_t KL[t] into the student; returns (dh_s, dW_s)."""
+    """Gradients of L = sum_t mask_t (coef_fwd_t KL_fwd[t] + coef_rev_t KL_rev[t]) into the
+    student (either coefficient may be None, not both); returns (dh_s, dW_s)."""
     mask = _mask_u8(mask)
     _check_kl(h_s, W_s, h_t, W_t, mask)
     N, Hs = h_s.shape
@@ -483,9 +485,17 @@ def rlk_linear_kl_bwd(h_s, W_s, h_t, W_t, mask, temperature: float, reverse: boo
     V = W_s.shape[0]
     dt = _dtype_code(h_s)
     dev = h_s.device
-    for name, t in (("coef", coef), ("lse_s", lse_s), ("lse_t", lse_t)) + (
-            (("kl_rev", kl_rev),) if reverse else ()):
-        _vec(name, t, N)
+    if coef_fwd is None and coef_rev is None:
+        raise ValueError("coef_fwd and coef_rev cannot both be None")
+    for name, t in (("coef_fwd", coef_fwd), ("coef_rev", coef_rev)):
+        if t is not None:
+            _vec(name, t, N)
+    _vec("lse_s", lse_s, N)
+    _vec("lse_t", lse_t, N)
+    if coef_rev is not None:
+        if kl_rev is None:
+            raise ValueError("kl_rev is required with coef_rev")
+        _vec("kl_rev", kl_rev, N)
     dh = torch.empty((N, Hs), dtype=torch.float32, device=dev)
     dW = torch.empty((V, Hs), dtype=torch.float32, device=dev)
     nb = ctypes.c_size_t(0)
@@ -493,9 +503,9 @@ def rlk_linear_kl_bwd(h_s, W_s, h_t, W_t, mask, temperature: float, reverse: boo
             "rlk_linear_kl_bwd_workspace_size")
     ws = _workspace(int(nb.value), dev, workspace)
     L.check(L.lib().rlk_linear_kl_bwd(_vp(h_s), _vp(W_s), _vp(h_t), _vp(W_t), _vp(mask), N, Hs,
-                                      Ht, V, dt, float(temperature), int(bool(reverse)),
-                                      _vp(coef), _vp(lse_s), _vp(lse_t), _vp(kl_rev), _vp(dh),
-                                      _vp(dW), _vp(ws), ws.numel() * ws.element_size(),
+                                      Ht, V, dt, float(temperature), _vp(coef_fwd),
+                                      _vp(coef_rev), _vp(lse_s), _vp(lse_t), _vp(kl_rev),
+                                      _vp(dh), _vp(dW), _vp(ws), ws.numel() * ws.element_size(),
                                       _stream(dev)),
             "rlk_linear_kl_bwd")
     return dh, dW
@@ -503,8 +513,8 @@ def rlk_linear_kl_bwd(h_s, W_s, h_t, W_t, mask, temperature: float, reverse: boo
 
 class LinearKL(torch.autograd.Function):
     """(kl_fwd, kl_rev) = linear_kl(h_s, W_s, h_t, W_t, mask, T); gradients reach the student
-    only, through rlk_linear_kl_bwd with coef = dL/dKL (once per direction that receives a
-    gradient, the two results added)."""
+    only, through one rlk_linear_kl_bwd call with coef_fwd = dL/dkl_fwd and coef_rev =
+    dL/dkl_rev (None for a direction that receives no gradient)."""
 
     @staticmethod
     def forward(ctx, h_s, W_s, h_t, W_t, mask, temperature):
@@ -516,17 +526,11 @@ class LinearKL(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_fwd, grad_rev):
         h_s, W_s, h_t, W_t, mask, ls, lt, kr = ctx.saved_tensors
-        dh = dW = None
-        for g, reverse in ((grad_fwd, False), (grad_rev, True)):
-            if g is None:
-                continue
-            a, b = rlk_linear_kl_bwd(h_s, W_s, h_t, W_t, mask, ctx.temperature, reverse,
-                                     g.to(torch.float32).contiguous(), ls, lt, kr)
-            dh = a if dh is None else dh + a
-            dW = b if dW is None else dW + b
-        if dh is None:
-            dh, dW = torch.zeros_like(h_s, dtype=torch.float32), torch.zeros_like(W_s,
-                                                                               dtype=torch.float32)
+        if grad_fwd is None and grad_rev is None:
+            return None, None, None, None, None, None
+        cf = None if grad_fwd is None else grad_fwd.to(torch.float32).contiguous()
+        cr = None if grad_rev is None else grad_rev.to(torch.float32).contiguous()
+        dh, dW = rlk_linear_kl_bwd(h_s, W_s, h_t, W_t, mask, ctx.temperature, cf, cr, ls, lt, kr)
         return dh.to(h_s.dtype), dW.to(W_s.dtype), None, None, None, None
 
 

@@ -324,14 +324,17 @@ def test_kl_argument_errors(L):
     st2, b2 = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 32768, 4096, 2048, 151936, 0)
     assert st2 == 0 and b2 - b < 6 * 4 * 16384 * 1188 + 16384 * 8
 
-    def bwd(Hs=256, dt=0, rev=0, kr=FAKE, coef=FAKE, wsb=1 << 40):
-        return lib.rlk_linear_kl_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 8, Hs, 64, 1000, dt, 1.0, rev,
-                                     coef, FAKE, FAKE, kr, FAKE, FAKE, FAKE, wsb, None)
+    def bwd(Hs=256, dt=0, cf=FAKE, cr=None, kr=FAKE, wsb=1 << 40, dh=FAKE):
+        return lib.rlk_linear_kl_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 8, Hs, 64, 1000, dt, 1.0, cf, cr,
+                                     FAKE, FAKE, kr, dh, FAKE, FAKE, wsb, None)
 
     assert bwd(Hs=64) == E.RLK_ERROR_UNSUPPORTED
     assert bwd(dt=1) == E.RLK_ERROR_UNSUPPORTED
-    assert bwd(coef=None) == E.RLK_ERROR_INVALID_VALUE
-    assert bwd(rev=1, kr=None) == E.RLK_ERROR_INVALID_VALUE
+    assert bwd(cf=None) == E.RLK_ERROR_INVALID_VALUE            # no coefficient at all
+    assert bwd(cf=None, cr=FAKE, kr=None) == E.RLK_ERROR_INVALID_VALUE  # reverse needs kl_rev
+    assert bwd(cr=FAKE + 2) == E.RLK_ERROR_UNSUPPORTED
+    assert bwd(dh=FAKE + 4) == E.RLK_ERROR_UNSUPPORTED          # dh_s: 16 bytes
     assert bwd(wsb=1000) == E.RLK_ERROR_WORKSPACE
+    assert bwd(cf=None, cr=FAKE, wsb=1000) == E.RLK_ERROR_WORKSPACE
     assert _ws(lib, "rlk_linear_kl_bwd_workspace_size", 8, 64, 64, 1000, 0)[0] == \
         E.RLK_ERROR_UNSUPPORTED

@@ -149,7 +149,9 @@ def _bwd(w, ht, Wt, reverse, coef):
     import linear_selected_token_amd as rlk
     d = [_dev(x) for x in (w.h, w.W, ht, Wt, w.mask)]
     kf, kr, ls, lt = rlk.rlk_linear_kl_fwd(*d, w.T)
-    dh, dW = rlk.rlk_linear_kl_bwd(*d, w.T, reverse, _dev(coef), ls, lt, kr)
+    c = _dev(coef)
+    dh, dW = rlk.rlk_linear_kl_bwd(*d, w.T, None if reverse else c, c if reverse else None, ls,
+                                   lt, kr)
     torch.cuda.synchronize()
     return dh.cpu().numpy(), dW.cpu().numpy()
 
@@ -241,7 +243,7 @@ def test_empty_and_all_masked():
     assert not any(o.any() for o in outs)
     d = [_dev(x) for x in (w.h, w.W, ht, Wt)]
     z = torch.zeros(w.N, dtype=torch.float32, device=d[0].device)
-    dh, dW = rlk.rlk_linear_kl_bwd(*d, _dev(m0), w.T, False, z + 1, z, z)
+    dh, dW = rlk.rlk_linear_kl_bwd(*d, _dev(m0), w.T, z + 1, z + 1, z, z, z)
     torch.cuda.synchronize()
     assert not dh.any() and not dW.any()
     # no tokens at all
@@ -250,7 +252,7 @@ def test_empty_and_all_masked():
     out0 = rlk.rlk_linear_kl_fwd(e[0], e[1], e[2], e[3], em, 1.0)
     assert all(o.numel() == 0 for o in out0)
     z0 = torch.zeros(0, dtype=torch.float32, device=d[0].device)
-    dh0, dW0 = rlk.rlk_linear_kl_bwd(e[0], e[1], e[2], e[3], em, 1.0, True, z0, z0, z0, z0)
+    dh0, dW0 = rlk.rlk_linear_kl_bwd(e[0], e[1], e[2], e[3], em, 1.0, None, z0, z0, z0, z0)
     torch.cuda.synchronize()
     assert dh0.numel() == 0 and not dW0.any()
 
@@ -269,11 +271,18 @@ def test_autograd_matches_direct_calls():
     cf, cr = cf.to(hs.device), cr.to(hs.device)
     ((cf * kf).sum() + (cr * kr).sum()).backward()
     _, kr0, ls, lt = rlk.rlk_linear_kl_fwd(*d, w.T)
-    a1, b1 = rlk.rlk_linear_kl_bwd(*d, w.T, False, cf, ls, lt, kr0)
-    a2, b2 = rlk.rlk_linear_kl_bwd(*d, w.T, True, cr, ls, lt, kr0)
+    a, b = rlk.rlk_linear_kl_bwd(*d, w.T, cf, cr, ls, lt, kr0)
     torch.cuda.synchronize()
-    assert torch.equal(hs.grad, (a1 + a2).to(torch.bfloat16))
-    assert torch.equal(Ws.grad, (b1 + b2).to(torch.bfloat16))
+    assert torch.equal(hs.grad, a.to(torch.bfloat16))
+    assert torch.equal(Ws.grad, b.to(torch.bfloat16))
+    # against the oracle: the two directions' gradients add
+    hs64, Ws64, ht64, Wt64 = (wl.as_f64(x) for x in (w.h, w.W, ht, Wt))
+    f1 = od.kl_grads(hs64, Ws64, ht64, Wt64, w.mask, w.T, cf.cpu().numpy(), False)
+    f2 = od.kl_grads(hs64, Ws64, ht64, Wt64, w.mask, w.T, cr.cpu().numpy(), True)
+    act = np.nonzero(w.mask)[0]
+    assert_rows("dh (both directions, every active row)", a.cpu().numpy()[act],
+                (f1[0] + f2[0])[act], act)
+    assert_rows("dW (both directions, every vocabulary row)", b.cpu().numpy(), f1[1] + f2[1])
 
 
 @pytest.mark.parametrize("V", [1, 2, 129])
