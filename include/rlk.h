@@ -193,7 +193,7 @@ rlk_status_t rlk_logp_from_logits(const void* logits, int64_t ld, const int32_t*
  * turned into dL/dz (rounded to bf16), and multiplied into dh (accumulated in fp32 in a fixed
  * order of vocabulary pieces) and into the chunk's rows of dW.  The active tokens are taken in
  * blocks of equal size (the last shorter), at most the largest multiple of 256 tokens whose
- * buffers (131200 + 14 H bytes per token) fit 1e9 bytes: 5120 tokens at H = 4096, 4096 at
+ * buffers (65664 + 6 H bytes per token) fit 1e9 bytes: 11008 tokens at H = 4096, 8960 at
  * H = 7168.  The workspace holds one block, so it does not grow with N past that.  A token's
  * dL/dh row does not depend on the block it falls in (bit-identical in any batch); dL/dW is
  * the sum of the blocks' sums in ascending block order (deterministic, and independent of
@@ -232,16 +232,16 @@ rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int
  *   z_s = h_s W_s^T / T, z_t = h_t W_t^T / T, p = softmax(z)
  *   kl_fwd[t] = sum_v p_t (log p_t - log p_s),  kl_rev[t] = sum_v p_s (log p_s - log p_t)
  * at active tokens, 0 elsewhere (both clamped at 0 against rounding).  The vocabulary is walked
- * in chunks of 65536 entries: per chunk each head's tile GEMM writes its column statistics
+ * in chunks of 32768 entries: per chunk each head's tile GEMM writes its column statistics
  * and its logits of that chunk only (fp32, one token block of rlk_linear_logp_bwd's size for
- * the student's H, x 65536 entries, in the workspace), a streaming kernel pairs the two entry
+ * the student's H, x 32768 entries, in the workspace), a streaming kernel pairs the two entry
  * by entry, and a fixed-order merge gives the results.
  * Batch-invariant like logp.  H_s and H_t: multiples of 64; each h at most 2^31 - 1 bytes.
  *   lse_s, lse_t [N] float     out (may be NULL): each head's log-sum-exp, which the backward
  *                              takes back
  *   workspace: rlk_linear_kl_fwd_workspace_size bytes: six float arrays of ceil(V/128) x N
  *              (both heads' column statistics and the two cross terms) and two chunk buffers of
- *              65568 floats per token of one block (3.15 GB in all at N = 16384, H_s = 4096,
+ *              32800 floats per token of one block (3.36 GB in all at N = 16384, H_s = 4096,
  *              V = 151936). */
 rlk_status_t rlk_linear_kl_fwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
                                               int dtype, size_t* bytes);

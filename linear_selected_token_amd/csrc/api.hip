@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cstdio>
+#include <string>
 
 #include "aux_kernels.hpp"
 #include "kernels.hpp"
@@ -73,14 +74,21 @@ T* carve(void* ws, size_t off) {
 }
 
 const char* build_info_string() {
-  static const char* s =
-      "rlk linear_logp | arch gfx950 | compiler " __clang_version__
-      " | tile 256x256, K stage 128 B, 8 wave64 x 128x64, mfma 32x32x16 bf16 / 32x32x2 f32"
-      " | vocab partial 128 | merge 8 strided slices + fixed tree"
-      " | bwd chunk 65536, dh split at 16384 (four pieces per chunk)"
-      " | bwd token blocks: equal blocks of at most the largest multiple of 256 tokens whose"
-      " buffers (131200 + 14 H bytes per token) fit 1000000000 bytes";
-  return s;
+  // written once (thread-safe static initialisation), from the build's constants
+  static const std::string s = [] {
+    char buf[768];
+    snprintf(buf, sizeof buf,
+             "rlk linear_logp | arch gfx950 | compiler " __clang_version__
+             " | tile 256x256, K stage 128 B, 8 wave64 x 128x64, mfma 32x32x16 bf16 / 32x32x2 f32"
+             " | vocab partial 128 | merge 8 strided slices + fixed tree"
+             " | bwd chunk %d, dh split at %d"
+             " | bwd token blocks: equal blocks of at most the largest multiple of 256 tokens whose"
+             " buffers (%zu + %zu H bytes per token) fit %zu bytes",
+             kBwdChunk, kDhSplitK, bwd_bytes_per_token(0), (bwd_bytes_per_token(1 << 10) - bwd_bytes_per_token(0)) >> 10,
+             kBwdBlockBudget);
+    return std::string(buf);
+  }();
+  return s.c_str();
 }
 
 // The backward behind rlk_linear_logp_bwd and rlk_linear_logp_bwd_entropy (ent_coef and

@@ -17,7 +17,7 @@
 //   dlogits      the forward tile GEMM again, epilogue G = (g_t / T)(delta - p) rounded to
 //                bf16 and stored token-major (Gv);
 //   dh_chunk     (Gv W[chunk])^T = W[chunk]^T Gv^T in K pieces of kDhSplitK entries
-//                (fp32 accumulation; four per full chunk): W is the first operand, read as
+//                (fp32 accumulation; two per full chunk): W is the first operand, read as
 //                a K-strided panel on the three-stage ring (rows past V as zeros), so the
 //                operand that streams from memory is the one loaded two stages ahead; a tile
 //                is 256 hidden columns x 256 tokens.  Piece q is added to dhp[q] (compacted
@@ -295,11 +295,10 @@ __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
   // branch: chosen inside it (a nested select under a divergent mask), this compiler sent
   // piece 3's stores of half the lanes to piece 1's buffer.
   auto epilogue = [&](const RowColCtx& c, Acc& acc) {
-    static_assert(kDhPieces == 4, "piece buffers");
-    float* const base = c.piece == 0   ? a.dh
-                        : c.piece == 1 ? a.dhp[1]
-                        : c.piece == 2 ? a.dhp[2]
-                                       : a.dhp[3];
+    static_assert(kDhPieces >= 1 && kDhPieces <= 4, "piece buffers");
+    float* base = a.dh;
+#pragma unroll
+    for (int q = 1; q < kDhPieces; ++q) base = c.piece == q ? a.dhp[q] : base;
     const bool in_dh = c.piece == 0;
 #pragma unroll
     for (int j = 0; j < kBlkB; ++j) {
@@ -534,11 +533,15 @@ hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, bool ac
 
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {
   const int kc0 = ((a.V < kBwdChunk ? a.V : kBwdChunk) + 63) / 64 * 64;  // first chunk's K extent
-  switch ((kc0 + kDhSplitK - 1) / kDhSplitK) {
-    case 1: break;  // one piece: dh holds the result already
-    case 2: hipLaunchKernelGGL(dh_finish_kernel<2>, dim3(2048), dim3(256), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(dh_finish_kernel<3>, dim3(2048), dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL(dh_finish_kernel<4>, dim3(2048), dim3(256), 0, stream, a); break;
+  const int pieces = (kc0 + kDhSplitK - 1) / kDhSplitK;
+  // one piece: dh holds the result already
+  if (pieces == 2)
+    hipLaunchKernelGGL(dh_finish_kernel<2>, dim3(2048), dim3(256), 0, stream, a);
+  if constexpr (kDhPieces >= 3) {
+    if (pieces == 3) hipLaunchKernelGGL(dh_finish_kernel<3>, dim3(2048), dim3(256), 0, stream, a);
+  }
+  if constexpr (kDhPieces >= 4) {
+    if (pieces >= 4) hipLaunchKernelGGL(dh_finish_kernel<4>, dim3(2048), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }

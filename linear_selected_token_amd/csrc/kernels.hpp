@@ -7,9 +7,13 @@
 namespace rlk {
 
 constexpr int kVocabPartial = 128;  // vocabulary entries per partial-statistics column
-constexpr int kBwdChunk = 65536;    // vocabulary entries per backward chunk (build constant)
-constexpr int kDhSplitK = 16384;    // dL/dh sums each 16384-entry piece of a chunk apart
-constexpr int kDhPieces = kBwdChunk / kDhSplitK;  // pieces of a full chunk (4)
+// Vocabulary entries per backward chunk, and per dL/dh piece of a chunk (build constants; a
+// token's dL/dh bits depend on them, never on N).
+#define RLK_BWD_CHUNK 32768
+#define RLK_DH_SPLIT 16384
+constexpr int kBwdChunk = RLK_BWD_CHUNK;  // vocabulary entries per backward chunk
+constexpr int kDhSplitK = RLK_DH_SPLIT;   // dL/dh sums each piece of a chunk apart
+constexpr int kDhPieces = kBwdChunk / kDhSplitK;  // pieces of a full chunk
 // The backward (and the KL paths) take the active tokens in blocks of at most a capacity the
 // host derives from H (a multiple of 256, at most 65536), in compacted order: its buffers hold
 // one block, so the workspace does not grow past that many tokens.

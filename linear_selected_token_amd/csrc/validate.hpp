@@ -102,14 +102,15 @@ inline DiagLayout diag_layout(int64_t N) {
   return L;
 }
 
-constexpr int64_t kBwdChunkEntries = 65536;
-constexpr int kBwdDhPieces = 4;  // dL/dh pieces of a full chunk (16384 entries each)
+constexpr int64_t kBwdChunkEntries = 32768;
+constexpr int kBwdDhPieces = 2;  // dL/dh pieces of a full chunk (16384 entries each): the first
+                                 // accumulates in dh, the other in the workspace
 
 // The backward takes the active tokens in blocks (compacted order) and its buffers hold one
 // block: per token of capacity, a row of the bf16 dL/dz chunk, three fp32 dL/dh piece rows
 // (the first piece accumulates in dh itself) and a bf16 column of the transposed h.  The
 // capacity is the largest multiple of 256 tokens whose buffers fit this budget (at least 256):
-// 5120 tokens at H = 4096, 4096 at H = 7168.
+// 11008 tokens at H = 4096, 8960 at H = 7168.
 constexpr size_t kBwdBlockBudget = 1000000000;  // bytes
 
 inline size_t bwd_bytes_per_token(int64_t H) {
@@ -137,7 +138,7 @@ inline int64_t bwd_npad(int64_t N, int64_t H) {
 }
 
 // Workspace layout of the backward: idx[N] | n_active | block_desc[blocks][2] | bidx[Npad] |
-// bn | sched[8] | hT[H, Npad] | Gv[Npad, chunk] (bf16) | dhp[1..3][Npad, H] (fp32).
+// bn | sched[8] | hT[H, Npad] | Gv[Npad, chunk] (bf16) | dhp[1 ..][Npad, H] (fp32).
 struct BwdLayout {
   size_t idx, n_active, block_desc, bidx, bn, sched, hT, Gv, dhp[kBwdDhPieces], total;
 };

@@ -157,7 +157,7 @@ static void test_layouts() {
       // the block buffers are all the workspace but for the index and the block descriptors
       EXPECT(L.total - L.hT <= (size_t)kBwdBlockBudget + 8 * 256);
     }
-  EXPECT(bwd_token_cap(4096) == 5120 && bwd_token_cap(7168) == 4096);
+  EXPECT(bwd_token_cap(4096) == 11008 && bwd_token_cap(7168) == 8960);
   int max_blocks = 0;
   for (int64_t H = 64; H <= kMaxHidden; H += 64) {
     const int64_t n = std::min<int64_t>(kMaxTokens, kMaxHiddenStateBytes / (2 * H));
@@ -165,7 +165,8 @@ static void test_layouts() {
       max_blocks = std::max(max_blocks, bwd_blocks(n, H));
   }
   EXPECT(max_blocks > 1 && max_blocks <= 1024);
-  EXPECT(bwd_blocks(0, 4096) == 1 && bwd_blocks(5120, 4096) == 1 && bwd_blocks(5121, 4096) == 2);
+  EXPECT(bwd_blocks(0, 4096) == 1 && bwd_blocks(11008, 4096) == 1 &&
+         bwd_blocks(11009, 4096) == 2);
   for (int64_t N : {int64_t(0), int64_t(1), int64_t(1023), int64_t(1024), int64_t(1) << 20,
                     kMaxTokens}) {
     const DiagLayout D = diag_layout(N);

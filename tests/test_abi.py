@@ -80,7 +80,7 @@ def test_workspace_queries(L):
     assert st == 0 and b < a
     st, c = _ws(lib, "rlk_linear_logp_bwd_workspace_size", 4096, 4096, 151936, L.RLK_BF16)
     assert st == 0 and c > 0
-    # the backward's buffers hold one token block (5120 tokens at H = 4096): past it only the
+    # the backward's buffers hold one token block (11008 tokens at H = 4096): past it only the
     # index grows, and the Qwen3-8B head's backward needs under 1 GB at 16384 tokens (its
     # active tokens' bf16 logits alone would take ~3 GB)
     st, d = _ws(lib, "rlk_linear_logp_bwd_workspace_size", 16384, 4096, 151936, L.RLK_BF16)
@@ -313,13 +313,13 @@ def test_kl_argument_errors(L):
     assert fwd(T=0.0) == E.RLK_ERROR_INVALID_VALUE
     assert fwd(wsb=1000) == E.RLK_ERROR_WORKSPACE
     st, b = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 16384, 4096, 2048, 151936, 0)
-    # six [J][N] statistics plus two fp32 chunks of one token block (5120 tokens at the
+    # six [J][N] statistics plus two fp32 chunks of one token block (11008 tokens at the
     # student's H = 4096) x (chunk entries)
     import re
     info = lib.rlk_build_info().decode()
     chunk = int(re.search(r"bwd chunk (\d+)", info).group(1))
-    assert st == 0 and b >= 6 * 4 * 16384 * 1187 + 2 * 4 * 5120 * chunk
-    assert b < 6 * 4 * 16384 * 1188 + 2 * 4 * 5120 * (chunk + 64) + (1 << 20)
+    assert st == 0 and b >= 6 * 4 * 16384 * 1187 + 2 * 4 * 11008 * chunk
+    assert b < 6 * 4 * 16384 * 1188 + 2 * 4 * 11008 * (chunk + 64) + (1 << 20)
     # past one token block only the [J][N] statistics grow with N
     st2, b2 = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 32768, 4096, 2048, 151936, 0)
     assert st2 == 0 and b2 - b < 6 * 4 * 16384 * 1188 + 16384 * 8

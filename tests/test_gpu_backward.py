@@ -107,9 +107,9 @@ def _token_cap(H):
     return budget // (a + b * H) // 256 * 256
 
 
-# ~60% active of 22000 tokens at H = 256 (7168-token blocks): two equal blocks of the backward
-# and two more that hold no active token
-MULTI = wl.scaled_spec(3, N=22000, H=256, V=3000, n_seq=60, len_lo=128, len_hi=512, seed=141,
+# ~60% active of 40000 tokens at H = 256 (blocks of at most 14848 tokens): two equal blocks of
+# the backward and a third that holds no active token
+MULTI = wl.scaled_spec(3, N=40000, H=256, V=3000, n_seq=110, len_lo=128, len_hi=512, seed=141,
                        targets="uniform", backward=True)
 
 
@@ -119,13 +119,13 @@ def test_token_blocks_full():
     w = wl.make(MULTI)
     cap = _token_cap(w.H)
     flush(f"  {w.n_active} active of {w.N}: token blocks of at most {cap}")
-    assert cap < w.n_active < 2 * cap and w.N > 3 * cap
+    assert cap < w.n_active < 2 * cap and w.N > 2 * cap
     _full_compare(w)
 
 
 def test_token_blocks_dh_invariance_and_dw():
     # a token's dL/dh row keeps its bits whichever token block it falls in (alone, shuffled,
-    # padded, all tokens active: 22000 active, four blocks); dL/dW is deterministic and does not
+    # padded, all tokens active: 40000 active, three blocks); dL/dW is deterministic and does not
     # depend on padding or inactive rows (they never enter the compacted order)
     fam = wl.Family(MULTI)
     base = fam.batch()
@@ -193,7 +193,7 @@ def test_autograd_matches_direct_call():
 
 def _edge_vocab_rows(V, r, n_random):
     """dL/dW rows on the boundaries the backward cuts the vocabulary at: every dL/dh piece
-    and chunk (multiples of 16384 and 65536, two rows each side), a spread of the 256-entry
+    and chunk (multiples of 16384 and of the chunk size, two rows each side), a spread of the 256-entry
     tile boundaries, the ragged tail, plus random rows."""
     _, split = _chunking()
     piece = edge_rows(V, split, 2)
