@@ -287,13 +287,13 @@ __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
 
   // Accumulator rows are hidden columns, columns are tokens: a lane holds 4 consecutive
   // hidden columns per register group, added into its token's row 16 bytes at a time.  Piece
-  // 0 accumulates in dh's own row of the token (idx[m]); pieces 1-3 in the token's compacted
-  // row of dhp[piece].  Every row starts 16-byte aligned: dh and the 256-byte aligned dhp
+  // 0 accumulates in dh's own row of the token (idx[m]); every later piece in the token's
+  // compacted row of dhp[piece].  Every row starts 16-byte aligned: dh and the 256-byte aligned dhp
   // buffers are 16-byte aligned and H % 256 == 0.
   //
   // The piece's buffer is chosen once per tile, in wave-uniform code before the per-lane
-  // branch: chosen inside it (a nested select under a divergent mask), this compiler sent
-  // piece 3's stores of half the lanes to piece 1's buffer.
+  // branch: chosen inside it (a nested select under a divergent mask, with four pieces), this
+  // compiler sent piece 3's stores of half the lanes to piece 1's buffer.
   auto epilogue = [&](const RowColCtx& c, Acc& acc) {
     static_assert(kDhPieces >= 1 && kDhPieces <= 4, "piece buffers");
     float* base = a.dh;
@@ -325,7 +325,7 @@ __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
   persistent_tiles<true, RowColCtx, true, false, kSpread>(sm, per_piece * npiece, setup, epilogue);
 }
 
-// dh[idx[m]] = ((dh[idx[m]] + dhp[1][m]) + dhp[2][m]) + dhp[3][m] over the kP pieces the first
+// dh[idx[m]] = (dh[idx[m]] + dhp[1][m]) + ... + dhp[kP-1][m] over the kP pieces the first
 // chunk has (every later chunk has at most as many, and adds to them; the others were never
 // written), piece 0 being the sum dh[idx[m]] already holds.  A work-group walks rows
 // m = blockIdx.x, blockIdx.x + gridDim.x, ...; its threads take 4 consecutive entries at a time.
