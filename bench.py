@@ -2,16 +2,20 @@
 
 One step is one pass of the whole path over one batch: active-row compaction, the vocab
 tile kernel with its fused softmax-statistics epilogue, the fixed-order merge (the
-forward), then the chunked backward of L = -sum_t mask_t adv_t logp_t.  The default
-workload is the Qwen3-8B LM-head shape with N=16384 tokens in 64 packed sequences (~60%
-active), T=0.7 and targets sampled from the oracle softmax (stored under tests/golden),
-with per-sequence advantages ~N(0,1) for the backward.  Inputs are seeded synthetic data,
-resident in HBM before the timed region.
+forward), then the chunked backward of L = -sum_t mask_t adv_t logp_t.  The headline step
+is rlk_linear_logp_fwd_bwd, which does all of it in one call: each token block's forward
+keeps its logits (16-bit codes, relative to the column maximum) in the workspace, so the backward
+forms dL/dz from them instead of running the logits GEMM again.  The same step as two calls
+(rlk_linear_logp_fwd, then rlk_linear_logp_bwd, which recomputes the logits) is timed beside
+it.  The default workload is the Qwen3-8B LM-head shape with N=16384 tokens in 64 packed
+sequences (~60% active), T=0.7 and targets sampled from the oracle softmax (stored under
+tests/golden), with per-sequence advantages ~N(0,1) for the backward.  Inputs are seeded
+synthetic data, resident in HBM before the timed region.
 
 Prints one JSON line.  `value` is active tokens per second for the whole step; the
-forward alone, the backward alone, and the roofline of the dominant kernel (the forward
-tile kernel, timed with HIP events on the stream it runs on) are reported beside it, and
-the float64 CPU oracle is timed on a bounded sample of the same workload.
+forward alone, the two-call step, and the roofline of the forward tile kernel (the GEMM
+kernel of both forms, timed with HIP events on the stream it runs on) are reported beside
+it, and the float64 CPU oracle is timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -57,7 +61,8 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     p.add_argument("--mode", default="fwdbwd",
                    choices=["fwd", "fwdbwd", "entropy", "ppo", "kl", "logits", "gemm-reference"],
-                   help="fwdbwd: the fused forward and backward (the headline); fwd: forward "
+                   help="fwdbwd: forward and backward (the headline: one fused call, and the "
+                        "two calls beside it); fwd: forward "
                         "only; entropy: a step with an entropy bonus (the entropy forward and "
                         "its backward); ppo: forward, clipped policy-gradient loss with a KL "
                         "penalty, backward, plus the dlogp diagnostics; kl: full-vocabulary KL "
@@ -530,28 +535,33 @@ def main():
         return
     m = measure(w, dev, args.steps, args.warmup, args.mode == "fwdbwd")
     N, H, V, T, Na = w.N, w.H, w.V, w.T, w.n_active
+    head = m["fused"] if "fused" in m else m
     out = {
         "metric": METRIC,
-        "value": round(Na / (m["ms"] * 1e-3), 1),
+        "value": round(Na / (head["ms"] * 1e-3), 1),
         "unit": "active tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(m["ms"], 4),
-        "step_ms_median": m["step_ms_median"],
-        "step_ms_min": m["step_ms_min"],
+        "ms_per_step": round(head["ms"], 4),
+        "step_ms_median": head["step_ms_median"],
+        "step_ms_min": head["step_ms_min"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic: seeded h~N(0,1), W~N(0,1/H) rounded to bf16, packed "
                 "prompt/response sequences",
         "config": {"workload": args.workload, "mode": args.mode, "N": N, "H": H, "V": V,
                    "T": T, "n_active": Na, "parallelism": "none (1 GPU)"},
-        "timed": "rlk_linear_logp_fwd then rlk_linear_logp_bwd per step, on the current stream",
+        "timed": ("rlk_linear_logp_fwd_bwd per step (forward and backward in one call), on the "
+                  "current stream" if "fused" in m else
+                  "rlk_linear_logp_fwd per step, on the current stream"),
         "fwd": m["fwd"],
         "roofline": m["roofline"],
     }
-    for k in ("bwd", "fwd_bwd_tflops_executed", "fwd_bwd_tflops_no_recompute_basis",
-              "fwd_bwd_mfma_frac", "workspace_bytes"):
-        if k in m:
-            out[k] = m[k]
+    if "fused" in m:
+        out["fwd_bwd_tflops_executed"] = m["fused"]["tflops_executed"]
+        out["fwd_bwd_mfma_frac"] = m["fused"]["mfma_frac"]
+        out["two_calls"] = m["two_calls"]
+    if "workspace_bytes" in m:
+        out["workspace_bytes"] = m["workspace_bytes"]
     logp = m.pop("_logp")
     del m
     if args.cpu_baseline_seconds > 0:
@@ -571,9 +581,11 @@ def measure(w, dev, steps, warmup, do_bwd):
 
     A step is rlk_linear_logp_fwd (compaction, tile kernel, merge) and, if do_bwd,
     rlk_linear_logp_bwd, enqueued on the current stream; HIP events bracket the forward and
-    the backward of every step and the whole timed region.  The tile kernel alone is timed in
-    a second loop that calls the forward's three stages as separate entry points, with events
-    on the stream the tile kernel runs on (the roofline's launch duration)."""
+    the backward of every step and the whole timed region.  With do_bwd the fused call
+    rlk_linear_logp_fwd_bwd is timed the same way in a loop of its own (its logp must carry
+    the forward's bits).  The tile kernel alone is timed in a further loop that calls the
+    forward's three stages as separate entry points, with events on the stream the tile
+    kernel runs on (the roofline's launch duration)."""
     import torch
     import linear_selected_token_amd as rlk
     N, H, V, T, Na = w.N, w.H, w.V, w.T, w.n_active
@@ -638,6 +650,40 @@ def measure(w, dev, steps, warmup, do_bwd):
     torch.cuda.synchronize()
     tile_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in tevs]))
     assert torch.equal(bufs.logp[:N], res["logp"]), "stage calls and rlk_linear_logp_fwd differ"
+    del bufs
+
+    fused = None
+    if do_bwd:
+        # the fused call: forward and backward in one, no second logits GEMM
+        del bws
+        xws = torch.empty(rlk.fwd_bwd_workspace_bytes(N, H, V, dt), dtype=torch.uint8,
+                          device=dev)
+        ws_bytes["fwd_bwd"] = xws.numel()
+
+        def fstep(ev):
+            ev[0].record()
+            logp, _, _, _ = rlk.rlk_linear_logp_fwd_bwd(h, W, targets, mask, T, adv,
+                                                        workspace=xws, dh=dh, dW=dW)
+            ev[1].record()
+            res["flogp"] = logp
+
+        for _ in range(warmup):
+            fstep(events(2))
+        torch.cuda.synchronize()
+        fevs = [events(2) for _ in range(steps)]
+        f0, f1 = events(2)
+        torch.cuda.synchronize()
+        f0.record()
+        for ev in fevs:
+            fstep(ev)
+        f1.record()
+        torch.cuda.synchronize()
+        fms = f0.elapsed_time(f1) / steps
+        fstep_ms = [e[0].elapsed_time(e[1]) for e in fevs]
+        assert torch.equal(res["flogp"], res["logp"]), "fused and two-call logp differ"
+        del xws
+        fused = {"ms": fms, "step_ms_median": round(float(np.median(fstep_ms)), 4),
+                 "step_ms_min": round(float(np.min(fstep_ms)), 4)}
 
     bf16 = w.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
@@ -658,14 +704,20 @@ def measure(w, dev, steps, warmup, do_bwd):
                  "mfma_frac": round(fwd_flop / (fwd_ms * 1e-3) / 1e12 / peak, 4)},
          "roofline": roofline, "workspace_bytes": ws_bytes, "_logp": res["logp"]}
     if do_bwd:
-        m["bwd"] = {"ms": round(bwd_ms, 4),
-                    "tflops_executed": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
-                    "mfma_frac": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / peak, 4)}
-        m["fwd_bwd_tflops_executed"] = round((fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12, 2)
-        m["fwd_bwd_mfma_frac"] = round((fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12 / peak, 4)
-        # without the recompute the step would need 6 H V flops per active token
-        m["fwd_bwd_tflops_no_recompute_basis"] = round(
-            6.0 * Na * H * V / (ms * 1e-3) / 1e12, 2)
+        # the two calls: 8 H V flops per active token (the backward runs the logits GEMM again)
+        m["two_calls"] = {
+            "ms": round(ms, 4), "active_tokens_per_s": round(Na / (ms * 1e-3), 1),
+            "step_ms_median": m["step_ms_median"], "step_ms_min": m["step_ms_min"],
+            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "bwd_tflops_executed": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
+            "bwd_mfma_frac": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / peak, 4),
+            "tflops_executed": round((fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round((fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12 / peak, 4)}
+        # the fused call: 6 H V flops per active token (forward, dL/dh, dL/dW)
+        fflop = 6.0 * Na * H * V
+        fused["tflops_executed"] = round(fflop / (fused["ms"] * 1e-3) / 1e12, 2)
+        fused["mfma_frac"] = round(fflop / (fused["ms"] * 1e-3) / 1e12 / peak, 4)
+        m["fused"] = fused
     return m
 
 
@@ -703,10 +755,13 @@ def bench_configs(args, dev):
                "tile_kernel_frac": m["roofline"]["frac"], "peak_tflops": m["roofline"]["peak"],
                "workspace_bytes": m["workspace_bytes"]}
         if do_bwd:
-            rec.update({"fwd_bwd_ms": round(m["ms"], 4),
-                        "fwd_bwd_active_tokens_per_s": round(Na / (m["ms"] * 1e-3), 1),
-                        "bwd_ms": m["bwd"]["ms"], "bwd_mfma_frac": m["bwd"]["mfma_frac"],
-                        "fwd_bwd_mfma_frac": m["fwd_bwd_mfma_frac"]})
+            f = m["fused"]
+            rec.update({"fwd_bwd_ms": round(f["ms"], 4),
+                        "fwd_bwd_active_tokens_per_s": round(Na / (f["ms"] * 1e-3), 1),
+                        "fwd_bwd_mfma_frac": f["mfma_frac"],
+                        "two_calls": {k: m["two_calls"][k] for k in
+                                      ("ms", "active_tokens_per_s", "bwd_ms", "bwd_mfma_frac",
+                                       "mfma_frac")}})
         logp = m.pop("_logp").cpu().numpy()
         del m
         torch.cuda.empty_cache()

@@ -204,6 +204,38 @@ rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* ta
                                  float* dh, float* dW, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* Forward and backward in one call (bf16 only, H a multiple of 256): logp and lse as
+ * rlk_linear_logp_fwd returns them (the same bits), and dL/dh, dL/dW of
+ * L = -sum_t mask_t * adv_t * logp_t as rlk_linear_logp_bwd defines them, for a loss whose
+ * upstream gradient is known before the forward (RL-Kernel Roadmap (2026), P0.2: fused linear
+ * log-prob with a fused backward).  Instead of recomputing the logits for the backward, each
+ * token block's forward keeps d = x - m (x = z log2 e / T, m the maximum over the token's
+ * 128-entry vocabulary column, so d <= 0) of every entry as a 16-bit code, round(-d 2^9)
+ * clamped to 65535, and turns it into dL/dz once lse is known: three GEMMs per step instead of
+ * four.  The code moves each p by at most 2^-10 ln 2 relative, whatever d is (entries with
+ * d <= -128 have p < 2^-128); dL/dz is rounded to bf16 as in the two-call path, whose dh and
+ * dW differ from these only by such rounding.
+ *   h, W, targets, mask, N, H, V, dtype, temperature, adv: as for rlk_linear_logp_bwd
+ *   logp [N] float  out: as rlk_linear_logp_fwd
+ *   lse  [N] float  out (required: the gradient pass reads it back)
+ *   dh   [N,H] float out, overwritten: dL/dh (inactive rows 0), 16-byte aligned
+ *   dW   [V,H] float out, overwritten: dL/dW
+ *   workspace: at least rlk_linear_logp_fwd_bwd_workspace_size bytes.  The active tokens are
+ *   taken in blocks of equal size (the last shorter) of at most the largest multiple of 256
+ *   tokens whose buffers fit 1e9 bytes: per token a row of roundup(V, 256) + 64 two-byte
+ *   entries, the column statistics (8 bytes per 128 entries) and 6 H + 12 bytes, i.e. 2816
+ *   tokens at H = 4096, V = 151936 (0.96 GB), so the workspace does not grow past one block.
+ * A token's logp, lse and dL/dh row are the same bits in any batch, whatever block it falls in;
+ * dL/dW is the sum of the blocks' sums in ascending block order.  Returns
+ * RLK_ERROR_UNSUPPORTED when N would need more than 1024 blocks. */
+rlk_status_t rlk_linear_logp_fwd_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
+                                                    size_t* bytes);
+rlk_status_t rlk_linear_logp_fwd_bwd(const void* h, const void* W, const int32_t* targets,
+                                     const uint8_t* mask, int64_t N, int64_t H, int64_t V,
+                                     int dtype, float temperature, const float* adv, float* logp,
+                                     float* lse, float* dh, float* dW, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* Backward of the policy-gradient loss with an entropy bonus (bf16 only),
  *   L = -sum_t mask_t (adv_t logp_t + c_t H_t)
  * with H_t the entropy of softmax(z[t,:]) (RL-Kernel Roadmap (2026), "operator backlog":

@@ -12,12 +12,15 @@ from .ops import (  # noqa: E402,F401
     LinearKL,
     LinearLogp,
     LinearLogpEntropy,
+    LinearLogpPGLoss,
     bwd_workspace_bytes,
+    fwd_bwd_workspace_bytes,
     fwd_entropy_workspace_bytes,
     fwd_workspace_bytes,
     linear_kl,
     linear_logp,
     linear_logp_entropy,
+    linear_logp_pg_loss,
     logits_workspace_bytes,
     num_vocab_partials,
     rlk_compact_active,
@@ -27,6 +30,7 @@ from .ops import (  # noqa: E402,F401
     rlk_linear_logp_bwd,
     rlk_linear_logp_bwd_entropy,
     rlk_linear_logp_fwd,
+    rlk_linear_logp_fwd_bwd,
     rlk_linear_logp_fwd_entropy,
     rlk_linear_logp_fwd_noalloc,
     rlk_linear_logp_merge,

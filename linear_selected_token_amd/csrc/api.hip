@@ -163,6 +163,100 @@ rlk_status_t run_bwd(const void* h, const void* W, const int32_t* targets, const
 }
 
 
+// The fused forward + backward behind rlk_linear_logp_fwd_bwd.  Per token block: the forward
+// tile kernel with the statistics and the 16-bit code of every entry's d stored, the merge (logp and lse
+// of the block's tokens, the same bits as rlk_linear_logp_fwd), d turned into dL/dz in place,
+// then the backward's dL/dh and dL/dW GEMMs over the vocabulary chunks, reading dL/dz from the
+// block's rows.  No GEMM is run twice.
+rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, const uint8_t* mask,
+                       int64_t N, int64_t H, int64_t V, int dtype, float temperature,
+                       const float* adv, float* logp, float* lse, float* dh, float* dW,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  rlk_status_t s = check_fused(h, W, targets, mask, N, H, V, dtype, temperature, adv, logp, lse,
+                               dh, dW, workspace, workspace_bytes);
+  if (s != RLK_SUCCESS) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (N == 0) return dev_status(launch_zero(dW, (size_t)V * (size_t)H, st));
+  int grid = 0;
+  if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
+  const FusedLayout L = fused_layout(N, H, V);
+  const int np = (int)fused_npad(N, H, V);
+  const int cap = (int)fused_token_cap(H, V);
+  const int nblk = fused_blocks(N, H, V);
+  const float inv_t = (float)(1.0 / (double)temperature);
+  int32_t* idx = carve<int32_t>(workspace, L.idx);
+  int32_t* na = carve<int32_t>(workspace, L.n_active);
+  int32_t* desc = carve<int32_t>(workspace, L.block_desc);
+  int32_t* bidx = carve<int32_t>(workspace, L.bidx);
+  int32_t* bn = carve<int32_t>(workspace, L.bn);
+  float* zy = carve<float>(workspace, L.target_logit);
+  float* pm = carve<float>(workspace, L.part_max);
+  float* ps = carve<float>(workspace, L.part_sum);
+  uint16_t* X = carve<uint16_t>(workspace, L.X);
+
+  FwdTileArgs f{h, W, targets, bidx, bn, (int)N, (int)H, (int)V, inv_t, pm, ps, zy, 0};
+  f.pstride = np;
+  f.dbuf = X;
+  f.d_pitch = (int)fused_pitch(V);
+  MergeArgs m{pm, ps, zy, bidx, bn, np, (int)V, logp, lse};  // N = np: the partials' stride
+  DzArgs z{X, (int)fused_pitch(V), pm, np, bidx, bn, targets, adv, lse, (int)V, inv_t};
+  BwdArgs a{};
+  a.h = h;
+  a.W = W;
+  a.targets = targets;
+  a.adv = adv;
+  a.lse = lse;
+  a.idx = bidx;
+  a.n_active = bn;
+  a.N = (int)N;
+  a.H = (int)H;
+  a.V = (int)V;
+  a.Npad = np;
+  a.inv_t = inv_t;
+  a.dh = dh;
+  a.dW = dW;
+  a.hT = carve<uint16_t>(workspace, L.hT);
+  a.Gv = X;
+  a.gv_pitch = (int)fused_pitch(V);
+  a.gv_full = true;
+  a.dhp[0] = nullptr;  // piece 0 accumulates in dh's rows
+  for (int q = 1; q < kDhPieces; ++q) a.dhp[q] = carve<float>(workspace, L.dhp[q]);
+  a.sched = carve<int>(workspace, L.sched);
+
+  // logp and lse are zeroed at every token (the merge writes the active ones)
+  CompactArgs c{mask, idx, na, nullptr, logp, lse, (int)N};
+  c.block_desc = desc;
+  c.nblk = nblk;
+  c.block_cap = cap;
+  hipError_t e = launch_compact(c, st);
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  e = launch_zero(dh, (size_t)N * (size_t)H, st);  // inactive rows stay 0
+  if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  const int nchunks = (int)((V + kBwdChunk - 1) / kBwdChunk);
+  for (int b = 0; b < nblk; ++b) {
+    e = launch_select_block(idx, desc, b, np, bidx, bn, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    // a target outside [0, V) is never captured: its logp stays NaN, as in the forward
+    e = launch_fill(zy, (size_t)np, NAN, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    e = launch_fwd_tiles(f, true, grid, st, kFwdStoreD);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    e = launch_fwd_merge(m, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    e = launch_dz_from_d(z, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    e = launch_bwd_transpose(a, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    for (int ch = 0; ch < nchunks; ++ch) {
+      e = launch_bwd_chunk_gemms(a, ch, grid, b > 0, st);
+      if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    }
+    e = launch_bwd_finish(a, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+  }
+  return RLK_SUCCESS;
+}
+
 }  // namespace
 }  // namespace rlk
 
@@ -666,6 +760,26 @@ rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int
   if (!aligned(ent_coef, 4) || !aligned(entropy, 4)) return RLK_ERROR_UNSUPPORTED;
   return run_bwd(h, W, targets, mask, N, H, V, dtype, temperature, adv, lse, ent_coef, entropy,
                  dh, dW, workspace, workspace_bytes, stream);
+}
+
+rlk_status_t rlk_linear_logp_fwd_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
+                                                    size_t* bytes) {
+  if (!bytes) return RLK_ERROR_INVALID_VALUE;
+  rlk_status_t s = check_shape(N, H, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  if (dtype != RLK_BF16 || H % 256 != 0 || fused_blocks(N, H, V) > 1024)
+    return RLK_ERROR_UNSUPPORTED;
+  *bytes = fused_layout(N, H, V).total;
+  return RLK_SUCCESS;
+}
+
+rlk_status_t rlk_linear_logp_fwd_bwd(const void* h, const void* W, const int32_t* targets,
+                                     const uint8_t* mask, int64_t N, int64_t H, int64_t V,
+                                     int dtype, float temperature, const float* adv, float* logp,
+                                     float* lse, float* dh, float* dW, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return run_fused(h, W, targets, mask, N, H, V, dtype, temperature, adv, logp, lse, dh, dW,
+                   workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -93,6 +93,59 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, size_t n) {
     p[e] = 0.f;
 }
 
+__global__ __launch_bounds__(256) void fill_kernel(float* p, size_t n, float value) {
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256)
+    p[e] = value;
+}
+
+// ---------------------------------------------------------------- dL/dz from the stored d
+
+// Row m of X holds, for the block's compacted token m, the code c = round(-d 2^9) of every
+// entry's d = x - m_col (log2 units, x = z log2 e / T, m_col the maximum of x over the entry's
+// 128-entry column, part_max).  With lse in log2 units, log2 p = d + (m_col - lse2), so
+//   G[m][v] = (-adv_t / T) (delta(v, y_t) - 2^(-c 2^-9 + m_col - lse2))
+// is the dL/dz the dlogits epilogue forms from the recomputed logit, here from the code instead
+// (it moves log2 p by at most 2^-10: a relative error of at most 2^-10 ln 2 in p, for every
+// entry; the bf16 rounding of G that follows is up to 2^-9).  Rows of padded token columns
+// (Na <= m < the block's 256-token tiles) and the entries past the vocabulary become 0, so the
+// GEMMs that read X as dL/dz add nothing for them.  Each thread converts 8 consecutive entries
+// (16 bytes in, 16 bytes out, in place); a work-group takes 2048 entries of one row; the grid
+// walks (row, segment) pairs.
+__global__ __launch_bounds__(256) void dz_from_d_kernel(DzArgs a) {
+  const int Na = *a.n_active;
+  const int rows = (Na + kTile - 1) / kTile * kTile;
+  const int vr = (a.V + kTile - 1) / kTile * kTile;  // columns the GEMMs may read
+  const int nseg = (vr + 2047) / 2048;
+  const int64_t total = (int64_t)rows * nseg;
+  for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
+    const int m = (int)(u / nseg);
+    const int v0 = (int)(u - (int64_t)m * nseg) * 2048 + 8 * (int)threadIdx.x;
+    if (v0 >= vr) continue;
+    u32x4* p = reinterpret_cast<u32x4*>(a.X + (size_t)m * a.pitch + v0);
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (m < Na && v0 < a.V) {  // (the quadrant holding v0 was stored: its d entries are set)
+      const int t = a.idx[m];
+      const float gs = -a.adv[t] * a.inv_t;
+      const int y = a.targets[t];
+      const float off = a.part_max[(size_t)(v0 / kVocabPartial) * a.pstride + m] - a.lse[t] * kLog2e;
+      const u32x4 cw = *p;
+      float G[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int v = v0 + e;
+        const uint32_t c = (cw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf((float)c, -1.f / 512.f, off));
+        G[e] = v < a.V ? gs * ((v == y ? 1.f : 0.f) - pv) : 0.f;
+      }
+      out.x = pack_bf16(G[0], G[1]);
+      out.y = pack_bf16(G[2], G[3]);
+      out.z = pack_bf16(G[4], G[5]);
+      out.w = pack_bf16(G[6], G[7]);
+    }
+    *p = out;
+  }
+}
+
 // ---------------------------------------------------------------- dlogits of one chunk
 
 struct DlogitsCtx {
@@ -221,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
           q.z = s0[1];
           q.w = s1[1];
           const int vl = c.vbase - c0 + wv + 32 * i + 16 * h + 8 * (lane >> 5);  // first of 8
-          *reinterpret_cast<u32x4*>(a.Gv + (size_t)ti * kGvPitch + vl) = q;
+          *reinterpret_cast<u32x4*>(a.Gv + (size_t)ti * a.gv_pitch + vl) = q;
         }
         // one block at a time: keeps the live ranges short (no spills)
         __builtin_amdgcn_sched_barrier(0);
@@ -254,7 +307,8 @@ __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
   const int band = nTokTiles < 8 ? nTokTiles : 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const size_t g_row = (size_t)kGvPitch * 2;   // bytes per Gv row (one token)
+  const size_t g_row = (size_t)a.gv_pitch * 2;  // bytes per Gv row (one token)
+  const size_t gcol = a.gv_full ? (size_t)c0 : 0;  // the chunk's first column in a Gv row
   const uint32_t w_pitch = (uint32_t)a.H * 2;  // bytes per W row
   const int wa = wave_a0(wave);
   const int wb = wave_b0(wave);
@@ -275,9 +329,10 @@ __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
     // W rows c0 + k0 ... of this tile's 256 columns; rows past V read as zeros
     const size_t v0 = (size_t)c0 + k0;
     src.a = uniform_ptr(static_cast<const uint8_t*>(a.W) + v0 * w_pitch + 2 * (size_t)c.abase);
-    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)c.bbase * g_row + 2 * k0);
+    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)c.bbase * g_row +
+                        2 * (gcol + k0));
     src.a_bytes = operand_bytes(((size_t)a.V - v0) * w_pitch - 2 * (size_t)c.abase);
-    src.b_bytes = operand_bytes((size_t)(a.Npad - c.bbase) * g_row - 2 * k0);
+    src.b_bytes = operand_bytes((size_t)(a.Npad - c.bbase) * g_row - 2 * (gcol + k0));
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       src.ao[q] = (uint32_t)(tdma_row(q, wave, lane) * w_pitch) + 16 * tdma_chunk(q, wave, lane);
@@ -367,7 +422,8 @@ __device__ __forceinline__ void dw_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const size_t row_bytes = (size_t)a.Npad * 2;         // hT rows
-  const uint32_t g_pitch = (uint32_t)kGvPitch * 2;   // Gv rows (one token each)
+  const uint32_t g_pitch = (uint32_t)a.gv_pitch * 2;  // Gv rows (one token each)
+  const size_t gcol = a.gv_full ? (size_t)c0 : 0;      // the chunk's first column in a Gv row
   const int nk = ((Na + 63) & ~63) * 2 / kKBytes;
   const int wa = wave_a0(wave);
   const int wb = wave_b0(wave);
@@ -384,9 +440,9 @@ __device__ __forceinline__ void dw_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
     src.a_kstep = kKBytes;
     src.b_kstep = 64 * g_pitch;  // 64 token rows of Gv per stage
     src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.hT) + (size_t)c.abase * row_bytes);
-    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + 2 * (size_t)c.bbase);
+    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + 2 * (gcol + c.bbase));
     src.a_bytes = operand_bytes((size_t)(a.H - c.abase) * row_bytes);
-    src.b_bytes = operand_bytes((size_t)a.Npad * g_pitch - 2 * (size_t)c.bbase);
+    src.b_bytes = operand_bytes((size_t)a.Npad * g_pitch - 2 * (gcol + c.bbase));
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
       src.ao[q] = (uint32_t)((size_t)dma_row(q, wave, lane) * row_bytes) + 16 * dma_chunk(q, wave, lane);
@@ -472,6 +528,18 @@ hipError_t launch_zero(float* p, size_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int zb = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
   hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(float* p, size_t n, float value, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int zb = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  hipLaunchKernelGGL(fill_kernel, dim3(zb), dim3(256), 0, stream, p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_dz_from_d(const DzArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(dz_from_d_kernel, dim3(4096), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -26,6 +26,16 @@ namespace rlk {
 
 namespace {
 
+// The 16-bit code of an exponent d <= 0 (log2 units): round(-d 2^9), clamped to [0, 65535]
+// (-inf gives 65535; a rounding residual just above 0 gives 0).  Two codes per word, the first
+// in the low half.
+__device__ __forceinline__ uint32_t dcode(float d) {
+  return (uint32_t)__builtin_rintf(fminf(fmaxf(-d * 512.f, 0.f), 65535.f));
+}
+__device__ __forceinline__ uint32_t pack_dcode(float lo, float hi) {
+  return dcode(lo) | (dcode(hi) << 16);
+}
+
 struct FwdCtx {
   int vq;      // first vocabulary entry of this wave's quadrant
   int tok[kBlkB];  // compacted token index of each of this lane's token columns
@@ -43,6 +53,15 @@ struct FwdCtx {
 //                chunk per launch, as a shard); the column statistics are written only when
 //                part_max is given.  No target.  The full-vocabulary KL between two heads
 //                pairs their x entry by entry from two such buffers.
+//   kFwdStoreD   the plain statistics and target, and d = x - max of every entry of the tile
+//                (the exponent the column sum adds up, <= 0) into dbuf as a 16-bit code,
+//                round(-d 2^9) clamped to [0, 65535]: steps of 2^-9 over (-128, 0], so the
+//                p = 2^(d + max - lse) it gives back carries at most 2^-10 ln 2 relative error
+//                whatever d is (entries with d <= -128 have p < 2^-128).  Token-major rows of
+//                d_pitch codes, entry v of the vocabulary at column v, one row per compacted
+//                token of the launch (padded token columns included).  The fused forward +
+//                backward turns these rows into dL/dz once lse is known, in place of a second
+//                pass of the GEMM.
 template <bool kBF16, int kMode>
 __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
   constexpr bool kEnt = kMode == kFwdEntropy;
@@ -59,6 +78,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
   const float c2 = a.inv_t * kLog2e;
   const int wv = wave_a0(wave);  // vocabulary offset of the wave sub-tile
   const int wt = wave_b0(wave);  // token offset of the wave sub-tile
+  const size_t pst = a.pstride > 0 ? (size_t)a.pstride : (size_t)a.N;  // partial column stride
 
   auto setup = [&](int u, TileSrc& src, FwdCtx& c) {
     int vt, tt;
@@ -185,13 +205,48 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
             }
         }
       }
+      if constexpr (kMode == kFwdStoreD) {
+        // codes of the wave's 128 entries for this token column, 16 bytes per lane: per 32-entry
+        // block, v_permlane32_swap on the packed groups (2h, 2h + 1) hands lane l entries
+        // 16 h + 0..7 and lane l + 32 entries 16 h + 8..15 of the same token (as for dL/dz).
+        // Rows of padded token columns (ti >= Na, still inside the block's rows) are written
+        // too and never read as d.
+        uint16_t* drow = a.dbuf + (size_t)ti * a.d_pitch + vq;
+#pragma unroll
+        for (int i = 0; i < kBlkA; ++i) {
+          u32x2 pk[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float d0 = __builtin_fmaf(acc.c[i][j][4 * g + 0], c2, -mx);
+            const float d1 = __builtin_fmaf(acc.c[i][j][4 * g + 1], c2, -mx);
+            const float d2 = __builtin_fmaf(acc.c[i][j][4 * g + 2], c2, -mx);
+            const float d3 = __builtin_fmaf(acc.c[i][j][4 * g + 3], c2, -mx);
+            pk[g][0] = pack_dcode(d0, d1);
+            pk[g][1] = pack_dcode(d2, d3);
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const auto s0 =
+                __builtin_amdgcn_permlane32_swap(pk[2 * h][0], pk[2 * h + 1][0], false, false);
+            const auto s1 =
+                __builtin_amdgcn_permlane32_swap(pk[2 * h][1], pk[2 * h + 1][1], false, false);
+            u32x4 q;
+            q.x = s0[0];
+            q.y = s1[0];
+            q.z = s0[1];
+            q.w = s1[1];
+            *reinterpret_cast<u32x4*>(drow + 32 * i + 16 * h + 8 * (lane >> 5)) = q;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       if (ti < Na) {
         if (lane < 32) {
           if (kMode != kFwdStoreX || a.part_max) {
-            a.part_max[(size_t)col * a.N + ti] = mx;
-            a.part_sum[(size_t)col * a.N + ti] = s;
+            a.part_max[col * pst + ti] = mx;
+            a.part_sum[col * pst + ti] = s;
           }
-          if constexpr (kEnt) a.part_w[(size_t)col * a.N + ti] = w;
+          if constexpr (kEnt) a.part_w[col * pst + ti] = w;
         }
         if (hit) a.target_logit[ti] = zsel * a.inv_t;
       }
@@ -304,6 +359,11 @@ hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream
     case kFwdPlain: launch_mode<kFwdPlain>(a, bf16, grid, stream); break;
     case kFwdEntropy: launch_mode<kFwdEntropy>(a, bf16, grid, stream); break;
     case kFwdStoreX: launch_mode<kFwdStoreX>(a, bf16, grid, stream); break;
+    case kFwdStoreD:
+      if (!bf16) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((fwd_tiles_kernel<true, kFwdStoreD>), dim3(grid), dim3(kThreads), 0,
+                         stream, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

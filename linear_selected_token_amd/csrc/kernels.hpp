@@ -62,9 +62,12 @@ struct FwdTileArgs {
   int vstart;  // global vocabulary index of W row 0 (a multiple of kVocabPartial)
   float* part_w = nullptr;  // [J][N] entropy statistic per column (kFwdEntropy)
   float* xbuf = nullptr;    // [Npad][kXPitch] x = z log2 e of one vocabulary chunk (kFwdStoreX)
+  int pstride = 0;          // column stride of part_max / part_sum / part_w (0: N)
+  uint16_t* dbuf = nullptr; // [rows][d_pitch] 16-bit code of d = x - column max (kFwdStoreD)
+  int d_pitch = 0;          // entries per dbuf row
 };
 
-enum FwdMode { kFwdPlain = 0, kFwdEntropy = 1, kFwdStoreX = 2 };
+enum FwdMode { kFwdPlain = 0, kFwdEntropy = 1, kFwdStoreX = 2, kFwdStoreD = 3 };
 
 struct MergeArgs {
   const float* part_max;
@@ -105,7 +108,7 @@ struct BwdArgs {
   float* dh;              // [N, H]
   float* dW;              // [V, H]
   uint16_t* hT;           // [H, Npad]   compacted h, transposed, zero past Na
-  uint16_t* Gv;           // [Npad, kGvPitch] dL/dz of the chunk, token-major
+  uint16_t* Gv;           // [Npad, gv_pitch] dL/dz of the chunk, token-major
   float* dhp[kDhPieces];  // [Npad, H] each for q >= 1: dL/dh from piece q of every chunk,
                           // compacted rows; piece 0 accumulates in place in dh's own rows
   int* sched;             // [8] tile-claim counters of the dL/dW section (zeroed per launch)
@@ -114,6 +117,26 @@ struct BwdArgs {
   // entropy bonus (both null without it): L gains -sum_t mask_t c_t H_t
   const float* ent_coef = nullptr;  // [N] c_t
   const float* entropy = nullptr;   // [N] H_t from the entropy forward
+  int gv_pitch = kGvPitch;  // entries per Gv row
+  // false: a Gv row holds one chunk (entry v - c0 of the chunk at c0); true: the whole
+  // vocabulary (entry v), so the chunk at c0 starts at column c0 of every row
+  bool gv_full = false;
+};
+
+// dL/dz of a token block from its stored d (fwd tiles in kFwdStoreD), in place: the 16-bit
+// codes of X become bf16 dL/dz, with zeros in the padded rows and past the vocabulary.
+struct DzArgs {
+  uint16_t* X;             // [rows][pitch]
+  int pitch;               // entries per row
+  const float* part_max;   // [J][pstride] column maxima (log2 units) of the block's tokens
+  int pstride;
+  const int32_t* idx;      // the block's compacted indices (positions in [0, N))
+  const int32_t* n_active; // the block's token count
+  const int32_t* targets;  // [N]
+  const float* adv;        // [N]
+  const float* lse;        // [N] natural-log lse, written by the merge
+  int V;
+  float inv_t;
 };
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
@@ -132,5 +155,7 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, bool accum_dw
 hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, bool accum_dw,
                                   hipStream_t stream);
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dh[idx] = sum of pieces
+hipError_t launch_fill(float* p, size_t n, float value, hipStream_t stream);
+hipError_t launch_dz_from_d(const DzArgs& a, hipStream_t stream);
 
 }  // namespace rlk

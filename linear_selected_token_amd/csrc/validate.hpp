@@ -166,6 +166,70 @@ inline BwdLayout bwd_layout(int64_t N, int64_t H) {
   return L;
 }
 
+// The fused forward + backward keeps, per token of a block, the 16-bit d code of every vocabulary
+// entry (one row of roundup(V, 256) + 64 entries, turned into bf16 dL/dz in place), the
+// block's column statistics (max and sum per 128-entry column), its target logit, a bf16 column
+// of the transposed h and the fp32 dL/dh piece rows past the first.  Blocks hold the largest
+// multiple of 256 tokens whose buffers fit the backward's budget (at least 256): 2816 tokens
+// for H = 4096, V = 151936.
+inline int64_t fused_pitch(int64_t V) { return (V + 255) / 256 * 256 + 64; }
+
+inline size_t fused_bytes_per_token(int64_t H, int64_t V) {
+  return 2 * (size_t)fused_pitch(V) + 8 * (size_t)num_partials(V) + 4 +
+         4 * (kBwdDhPieces - 1) * (size_t)H + 2 * (size_t)H + 8;
+}
+
+inline int64_t fused_token_cap(int64_t H, int64_t V) {
+  const int64_t c = (int64_t)(kBwdBlockBudget / fused_bytes_per_token(H > 0 ? H : 1, V > 0 ? V : 1)) /
+                    256 * 256;
+  return c < 256 ? 256 : (c > kMaxTokens ? kMaxTokens : c);
+}
+
+inline int fused_blocks(int64_t N, int64_t H, int64_t V) {
+  const int64_t cap = fused_token_cap(H, V);
+  return (int)(((N > 0 ? N : 1) + cap - 1) / cap);
+}
+
+inline int64_t fused_npad(int64_t N, int64_t H, int64_t V) {
+  const int64_t cap = fused_token_cap(H, V);
+  const int64_t n = N <= 0 ? 1 : (N < cap ? N : cap);
+  return (n + 255) / 256 * 256;
+}
+
+// Workspace layout of the fused forward + backward: idx[N] | n_active | block_desc[blocks][2] |
+// bidx[Npad] | bn | sched[8] | target_logit[Npad] | part_max[J][Npad] | part_sum[J][Npad] |
+// hT[H, Npad] | X[Npad, pitch] (d codes, then bf16 dL/dz) | dhp[1 ..][Npad, H] (fp32).
+struct FusedLayout {
+  size_t idx, n_active, block_desc, bidx, bn, sched, target_logit, part_max, part_sum, hT, X,
+      dhp[kBwdDhPieces], total;
+};
+
+inline FusedLayout fused_layout(int64_t N, int64_t H, int64_t V) {
+  FusedLayout L;
+  const size_t n = (size_t)(N > 0 ? N : 1);
+  const size_t np = (size_t)fused_npad(N, H, V);
+  const size_t jn = 4 * np * (size_t)num_partials(V);
+  size_t o = 0;
+  L.idx = o;          o = align_up(o + 4 * n, 256);
+  L.n_active = o;     o = align_up(o + 4, 256);
+  L.block_desc = o;   o = align_up(o + 8 * (size_t)fused_blocks(N, H, V), 256);
+  L.bidx = o;         o = align_up(o + 4 * np, 256);
+  L.bn = o;           o = align_up(o + 4, 256);
+  L.sched = o;        o = align_up(o + 4 * 8, 256);
+  L.target_logit = o; o = align_up(o + 4 * np, 256);
+  L.part_max = o;     o = align_up(o + jn, 256);
+  L.part_sum = o;     o = align_up(o + jn, 256);
+  L.hT = o;           o = align_up(o + 2 * (size_t)H * np, 256);
+  L.X = o;            o = align_up(o + 2 * np * (size_t)fused_pitch(V), 256);
+  L.dhp[0] = 0;       // piece 0 accumulates in dh's rows
+  for (int q = 1; q < kBwdDhPieces; ++q) {
+    L.dhp[q] = o;
+    o = align_up(o + 4 * np * (size_t)H, 256);
+  }
+  L.total = o;
+  return L;
+}
+
 // Workspace of the log-prob from existing logits: idx[N] | n_active.
 struct LogitsLayout {
   size_t idx, n_active, total;
@@ -237,6 +301,29 @@ inline rlk_status_t check_bwd(const void* h, const void* W, const int32_t* targe
       !aligned(lse, 4) || !aligned(dh, 16) || !aligned(dW, 4) || !aligned(ws, 256))
     return RLK_ERROR_UNSUPPORTED;
   if (ws_bytes < bwd_layout(N, H).total) return RLK_ERROR_WORKSPACE;
+  return RLK_SUCCESS;
+}
+
+inline rlk_status_t check_fused(const void* h, const void* W, const int32_t* targets,
+                                const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
+                                float T, const float* adv, const float* logp, const float* lse,
+                                const float* dh, const float* dW, const void* ws,
+                                size_t ws_bytes) {
+  rlk_status_t s = check_shape(N, H, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  s = check_temperature(T);
+  if (s != RLK_SUCCESS) return s;
+  if (dtype != RLK_BF16 || H % 256 != 0) return RLK_ERROR_UNSUPPORTED;
+  if (fused_blocks(N, H, V) > 1024) return RLK_ERROR_UNSUPPORTED;  // the compaction's bound
+  if (!dW) return RLK_ERROR_INVALID_VALUE;
+  if (N == 0) return RLK_SUCCESS;
+  if (!h || !W || !targets || !mask || !adv || !logp || !lse || !dh || !ws)
+    return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(targets, 4) || !aligned(adv, 4) ||
+      !aligned(logp, 4) || !aligned(lse, 4) || !aligned(dh, 16) || !aligned(dW, 4) ||
+      !aligned(ws, 256))
+    return RLK_ERROR_UNSUPPORTED;
+  if (ws_bytes < fused_layout(N, H, V).total) return RLK_ERROR_WORKSPACE;
   return RLK_SUCCESS;
 }
 

@@ -252,6 +252,42 @@ def rlk_linear_logp_bwd_entropy(h: torch.Tensor, W: torch.Tensor, targets: torch
     return dh, dW
 
 
+def fwd_bwd_workspace_bytes(N: int, H: int, V: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_linear_logp_fwd_bwd_workspace_size(N, H, V, dtype, ctypes.byref(out)),
+            "rlk_linear_logp_fwd_bwd_workspace_size")
+    return int(out.value)
+
+
+def rlk_linear_logp_fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                            mask: torch.Tensor, temperature: float, adv: torch.Tensor,
+                            workspace: Optional[torch.Tensor] = None,
+                            dh: Optional[torch.Tensor] = None, dW: Optional[torch.Tensor] = None,
+                            ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Forward and gradients of L = -sum_t mask_t adv_t logp_t in one call; returns
+    (logp [N], lse [N], dh [N,H], dW [V,H]), all float32."""
+    mask = _mask_u8(mask)
+    _check(h, W, targets, mask)
+    N, H = h.shape
+    V = W.shape[0]
+    dt = _dtype_code(h)
+    if not adv.is_cuda or adv.dtype != torch.float32 or adv.shape != (N,) or not adv.is_contiguous():
+        raise ValueError("adv must be a contiguous float32 GPU tensor [N]")
+    logp = torch.empty(N, dtype=torch.float32, device=h.device)
+    lse = torch.empty(N, dtype=torch.float32, device=h.device)
+    if dh is None:
+        dh = torch.empty((N, H), dtype=torch.float32, device=h.device)
+    if dW is None:
+        dW = torch.empty((V, H), dtype=torch.float32, device=h.device)
+    ws = _workspace(fwd_bwd_workspace_bytes(N, H, V, dt), h.device, workspace)
+    L.check(L.lib().rlk_linear_logp_fwd_bwd(_vp(h), _vp(W), _vp(targets), _vp(mask), N, H, V, dt,
+                                            float(temperature), _vp(adv), _vp(logp), _vp(lse),
+                                            _vp(dh), _vp(dW), _vp(ws),
+                                            ws.numel() * ws.element_size(), _stream(h.device)),
+            "rlk_linear_logp_fwd_bwd")
+    return logp, lse, dh, dW
+
+
 # ---- building blocks of the forward
 
 def rlk_compact_active(mask: torch.Tensor, idx: torch.Tensor, n_active: torch.Tensor,
@@ -363,6 +399,35 @@ class LinearLogpEntropy(torch.autograd.Function):
 def linear_logp_entropy(h, W, targets, mask, temperature):
     """Differentiable selected-token log-prob and entropy, each [N] (float32)."""
     return LinearLogpEntropy.apply(h, W, targets, mask, temperature)
+
+
+class LinearLogpPGLoss(torch.autograd.Function):
+    """loss = -sum_t mask_t adv_t logp_t with its gradients computed in the forward
+    (rlk_linear_logp_fwd_bwd); the backward scales them by the incoming scalar gradient."""
+
+    @staticmethod
+    def forward(ctx, h, W, targets, mask, temperature, adv):
+        adv32 = adv.to(torch.float32).contiguous()
+        logp, _, dh, dW = rlk_linear_logp_fwd_bwd(h, W, targets, mask, temperature, adv32)
+        m = _mask_u8(mask).to(torch.float32)
+        loss = -(m * adv32 * torch.nan_to_num(logp)).sum()
+        ctx.save_for_backward(dh, dW)
+        ctx.dtypes = (h.dtype, W.dtype)
+        ctx.mark_non_differentiable(logp)
+        return loss, logp
+
+    @staticmethod
+    def backward(ctx, grad_loss, grad_logp):
+        dh, dW = ctx.saved_tensors
+        g = grad_loss.to(torch.float32)
+        return (dh * g).to(ctx.dtypes[0]), (dW * g).to(ctx.dtypes[1]), None, None, None, None
+
+
+def linear_logp_pg_loss(h, W, targets, mask, temperature, adv):
+    """(loss, logp): the policy-gradient loss -sum mask * adv * logp as a differentiable
+    scalar (gradients into h and W, formed in the forward in one fused call), and the
+    selected-token log-prob [N] (float32, not differentiable)."""
+    return LinearLogpPGLoss.apply(h, W, targets, mask, temperature, adv)
 
 
 # ---- loss fragments on the log-prob

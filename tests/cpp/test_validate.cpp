@@ -187,6 +187,61 @@ static void test_layouts() {
   }
 }
 
+// The fused forward + backward: one token block's rows of fp16 d / bf16 dL/dz (every row starts
+// 16-byte aligned and holds every column a GEMM reads), its column statistics, hT and the dL/dh
+// piece rows within the budget; at most 1024 blocks wherever the checks accept the call.
+static void test_fused() {
+  EXPECT(fused_token_cap(4096, 151936) == 2816 && fused_token_cap(7168, 129280) == 3072);
+  EXPECT(fused_blocks(16384, 4096, 151936) == 6 && fused_blocks(2816, 4096, 151936) == 1 &&
+         fused_blocks(2817, 4096, 151936) == 2);
+  for (int64_t V : {int64_t(1), int64_t(257), int64_t(1000), int64_t(151936), kMaxVocab}) {
+    EXPECT(fused_pitch(V) >= (V + 255) / 256 * 256 && (fused_pitch(V) * 2) % 16 == 0);
+    for (int64_t H : {int64_t(256), int64_t(4096), int64_t(7168), kMaxHidden})
+      for (int64_t N : {int64_t(1), int64_t(300), int64_t(4096), int64_t(16384), kMaxTokens}) {
+        const FusedLayout L = fused_layout(N, H, V);
+        const size_t np = (size_t)fused_npad(N, H, V);
+        const int64_t cap = fused_token_cap(H, V);
+        const size_t jn = 4 * np * (size_t)num_partials(V);
+        std::vector<size_t> off = {L.idx, L.n_active, L.block_desc, L.bidx, L.bn, L.sched,
+                                   L.target_logit, L.part_max, L.part_sum, L.hT, L.X};
+        std::vector<size_t> sz = {4 * (size_t)N, 4, 8 * (size_t)fused_blocks(N, H, V), 4 * np, 4,
+                                  32, 4 * np, jn, jn, 2 * (size_t)H * np,
+                                  2 * np * (size_t)fused_pitch(V)};
+        for (int q = 1; q < kBwdDhPieces; ++q) {
+          off.push_back(L.dhp[q]);
+          sz.push_back(4 * np * (size_t)H);
+        }
+        expect_layout(off, sz, L.total);
+        EXPECT(cap % 256 == 0 && cap >= 256);
+        EXPECT((size_t)cap * fused_bytes_per_token(H, V) <= kBwdBlockBudget || cap == 256 ||
+               cap == kMaxTokens);
+        EXPECT(np % 256 == 0 && np >= (size_t)(N < cap ? N : cap) && np <= (size_t)cap);
+        EXPECT((int64_t)fused_blocks(N, H, V) * cap >= N);
+        const rlk_status_t s = check_fused(P(A), P(A), PT<const int32_t>(A), PT<const uint8_t>(A),
+                                           N, H, V, RLK_BF16, 1.f, PT<const float>(A),
+                                           PT<float>(A), PT<float>(A), PT<float>(A),
+                                           PT<float>(A), P(A), L.total);
+        if (s == RLK_SUCCESS) EXPECT(fused_blocks(N, H, V) <= 1024);
+        if (fused_blocks(N, H, V) > 1024) EXPECT(s == RLK_ERROR_UNSUPPORTED);
+      }
+  }
+  const size_t ws = fused_layout(16384, 4096, 151936).total;
+  EXPECT(ws <= (size_t)kBwdBlockBudget);
+  auto call = [&](uintptr_t lp, uintptr_t ls, uintptr_t dh, int dt, int64_t H, size_t bytes) {
+    return check_fused(P(A), P(A), PT<const int32_t>(A), PT<const uint8_t>(A), 16384, H, 151936,
+                       dt, 0.7f, PT<const float>(A), PT<float>(lp), PT<float>(ls), PT<float>(dh),
+                       PT<float>(A), P(A), bytes);
+  };
+  EXPECT(call(A, A, A, RLK_BF16, 4096, ws) == RLK_SUCCESS);
+  EXPECT(call(A, A, A, RLK_BF16, 4096, ws - 1) == RLK_ERROR_WORKSPACE);
+  EXPECT(call(0, A, A, RLK_BF16, 4096, ws) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(call(A, 0, A, RLK_BF16, 4096, ws) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(call(A, A, 0, RLK_BF16, 4096, ws) == RLK_ERROR_INVALID_VALUE);
+  EXPECT(call(A, A, A + 4, RLK_BF16, 4096, ws) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(A, A, A, RLK_FP32, 4096, ws) == RLK_ERROR_UNSUPPORTED);
+  EXPECT(call(A, A, A, RLK_BF16, 4160, ws) == RLK_ERROR_UNSUPPORTED);
+}
+
 static void test_fwd() {
   const size_t ws = fwd_layout(1000, 151936).total;
   auto call = [&](const void* h, const void* W, uintptr_t tg, uintptr_t mk, int64_t N, int64_t H,
@@ -298,6 +353,7 @@ int main() {
   test_layouts();
   test_fwd();
   test_bwd();
+  test_fused();
   test_logits();
   test_kl();
   std::printf("validate: %d checks, %d failed\n", g_checks, g_fail);

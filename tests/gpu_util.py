@@ -82,13 +82,16 @@ def assert_rows(name, got, ref, row_ids=None, gate=GRAD_REL_L2):
 
 def assert_tiles(name, got, ref, tile=256, gate=GRAD_REL_L2):
     """Gate every tile x tile block of a 2-D gradient on its own rel-L2 (the kernels' output
-    tiles are 256 x 256); prints the worst block."""
+    tiles are 256 x 256); a block whose reference is exactly zero gets the absolute norm of the
+    computed block, as rows do in row_rel_l2.  Prints the worst block."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     worst, at = 0.0, (0, 0)
     for r0 in range(0, ref.shape[0], tile):
         for c0 in range(0, ref.shape[1], tile):
-            e = rel_l2(got[r0:r0 + tile, c0:c0 + tile], ref[r0:r0 + tile, c0:c0 + tile])
+            g = got[r0:r0 + tile, c0:c0 + tile]
+            rb = ref[r0:r0 + tile, c0:c0 + tile]
+            e = rel_l2(g, rb) if rb.any() else float(np.linalg.norm(g))
             if e > worst:
                 worst, at = e, (r0, c0)
     flush(f"  {name}: worst {tile}x{tile} block at {at} relL2 {worst:.3e}")

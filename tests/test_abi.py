@@ -153,6 +153,47 @@ def test_backward_argument_errors(L):
     assert bwd(wsb=10) == E.RLK_ERROR_WORKSPACE
 
 
+def test_fused_workspace_and_argument_errors(L):
+    lib = L.lib()
+    E = L
+    # the fused call's buffers hold one token block (2816 tokens at H = 4096, V = 151936: a
+    # row of 152128 two-byte entries per token is most of it); past it only the index grows
+    st, a = _ws(lib, "rlk_linear_logp_fwd_bwd_workspace_size", 16384, 4096, 151936, L.RLK_BF16)
+    assert st == 0 and a <= 1_000_000_000
+    st, b = _ws(lib, "rlk_linear_logp_fwd_bwd_workspace_size", 2816, 4096, 151936, L.RLK_BF16)
+    assert st == 0 and 0 <= a - b <= 4 * (16384 - 2816) + 1024
+    st, c = _ws(lib, "rlk_linear_logp_fwd_bwd_workspace_size", 2816, 4096, 151936, L.RLK_BF16)
+    assert c >= 2816 * (2 * 152128 + 8 * 1187 + 6 * 4096)
+    st, d = _ws(lib, "rlk_linear_logp_fwd_bwd_workspace_size", 600, 512, 3000, L.RLK_BF16)
+    assert st == 0 and d < b
+    assert _ws(lib, "rlk_linear_logp_fwd_bwd_workspace_size", 64, 4096, 151936,
+               L.RLK_FP32)[0] == E.RLK_ERROR_UNSUPPORTED
+    assert _ws(lib, "rlk_linear_logp_fwd_bwd_workspace_size", 64, 320, 1000,
+               L.RLK_BF16)[0] == E.RLK_ERROR_UNSUPPORTED
+    # a vocabulary of 2^22 entries leaves room for 256 tokens per block: 2^22 tokens would need
+    # more than 1024 blocks
+    assert _ws(lib, "rlk_linear_logp_fwd_bwd_workspace_size", (1 << 22) - 256, 256, 1 << 22,
+               L.RLK_BF16)[0] == E.RLK_ERROR_UNSUPPORTED
+
+    def fused(h=FAKE, adv=FAKE, lp=FAKE, lse=FAKE, dh=FAKE, dW=FAKE, N=8, H=256, dt=0, T=1.0,
+              wsb=1 << 30):
+        return lib.rlk_linear_logp_fwd_bwd(h, FAKE, FAKE, FAKE, N, H, 100, dt, T, adv, lp, lse,
+                                           dh, dW, FAKE, wsb, None)
+
+    assert fused(h=None) == E.RLK_ERROR_INVALID_VALUE
+    assert fused(adv=None) == E.RLK_ERROR_INVALID_VALUE
+    assert fused(lp=None) == E.RLK_ERROR_INVALID_VALUE
+    assert fused(lse=None) == E.RLK_ERROR_INVALID_VALUE
+    assert fused(dh=None) == E.RLK_ERROR_INVALID_VALUE
+    assert fused(dW=None) == E.RLK_ERROR_INVALID_VALUE
+    assert fused(T=float("nan")) == E.RLK_ERROR_INVALID_VALUE
+    assert fused(dt=1) == E.RLK_ERROR_UNSUPPORTED
+    assert fused(H=192) == E.RLK_ERROR_UNSUPPORTED
+    assert fused(dh=FAKE + 4) == E.RLK_ERROR_UNSUPPORTED  # dh holds 16-byte vectors
+    assert fused(lse=FAKE + 2) == E.RLK_ERROR_UNSUPPORTED
+    assert fused(wsb=10) == E.RLK_ERROR_WORKSPACE
+
+
 def test_building_block_argument_errors(L):
     lib = L.lib()
     E = L

@@ -1,0 +1,240 @@
+"""Parity of the fused forward + backward (rlk_linear_logp_fwd_bwd) against the float64 oracle
+(needs an MI355X).
+
+logp and lse are the forward's own bits; dL/dh and dL/dW of L = -sum_t mask_t adv_t logp_t are
+gated per row at rel-L2 <= 1e-2 like the two-call backward.  The fused call forms dL/dz from the
+forward's d = x - (column max), kept as a 16-bit code in steps of 2^-9, instead of recomputing
+the logits, so its gradients differ from the two-call backward's by that rounding only; a
+token's dL/dh row is still bit-identical across batch layouts and token blocks."""
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import (MAX_ABS_DLOGP, assert_rows, assert_tiles, bits, device, edge_rows, flush,
+                      oracle_inputs, rel_l2, run_fwd, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fused(w, d=None):
+    import linear_selected_token_amd as rlk
+    d = d or upload(w)
+    logp, lse, dh, dW = rlk.rlk_linear_logp_fwd_bwd(d["h"], d["W"], d["targets"], d["mask"], w.T,
+                                                    d["adv"])
+    torch.cuda.synchronize()
+    return logp, lse, dh, dW
+
+
+def _chunking():
+    import linear_selected_token_amd as rlk
+    m = re.search(r"bwd chunk (\d+), dh split at (\d+)", rlk.build_info())
+    assert m, rlk.build_info()
+    return int(m.group(1)), int(m.group(2))
+
+
+def _fused_cap(H, V):
+    """Token capacity of the fused call's block buffers, by the rule include/rlk.h states: the
+    largest multiple of 256 tokens whose buffers (a row of roundup(V, 256) + 64 two-byte
+    entries, 8 bytes per 128-entry column, 6 H + 12 bytes) fit 1e9 bytes."""
+    pitch = (V + 255) // 256 * 256 + 64
+    per = 2 * pitch + 8 * ((V + 127) // 128) + 6 * H + 12
+    return max(256, 10**9 // per // 256 * 256)
+
+
+def _same_forward(w, d, logp, lse):
+    """logp and lse of the fused call carry the forward's bits at every token."""
+    flogp, flse = run_fwd(w, d)
+    assert np.array_equal(bits(logp.cpu().numpy()), bits(flogp))
+    assert np.array_equal(bits(lse.cpu().numpy()), bits(flse))
+
+
+def _full_compare(w):
+    d = upload(w)
+    logp, lse, dh, dW = run_fused(w, d)
+    _same_forward(w, d, logp, lse)
+    dh = dh.cpu().numpy()
+    dW = dW.cpu().numpy()
+    h64, W64 = oracle_inputs(w)
+    odh, odW = oracle.linear_logp_grads(h64, W64, w.targets, w.mask, w.T, w.adv)
+    act = np.nonzero(w.mask)[0]
+    flush(f"  {w.spec.name} N={w.N} H={w.H} V={w.V} active={act.size}")
+    assert_rows("fused dh (every active row)", dh[act], odh[act], act)
+    assert_rows("fused dW (every vocabulary row)", dW, odW)
+    assert_tiles("fused dW", dW, odW)
+    assert not dh[w.mask == 0].any()
+    return dh, dW
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_small_full(T):
+    _full_compare(wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64,
+                                         len_hi=300, seed=95, T=T)))
+
+
+def test_two_chunks_ragged():
+    # two backward chunks read from one stored row: the second chunk starts at column chunk of
+    # every row, with entries past the dL/dh split point and a ragged tail
+    chunk, split = _chunking()
+    _full_compare(wl.make(wl.scaled_spec(5, N=300, H=256, V=chunk + split + 300, n_seq=2,
+                                         len_lo=100, len_hi=200, seed=96)))
+
+
+@pytest.mark.parametrize("V", [1, 129, 255, 257])
+def test_tiny_vocabularies(V):
+    # one tile or a few entries past one: the stored rows end inside the first vocabulary tile
+    _full_compare(wl.make(wl.scaled_spec(5, N=300, H=256, V=V, n_seq=2, len_lo=100,
+                                         len_hi=200, seed=98)))
+
+
+@pytest.mark.parametrize("scale", [4.0, 24.0])
+def test_peaked_softmax(scale):
+    # h scaled up: most of each token's probability sits on a few entries, where the stored d
+    # (distance to the column maximum) is small; the rest of the row spans tens of log2 units
+    w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
+                               seed=100, T=0.7))
+    w.h = wl.bf16_bits(wl.bf16_to_f32(w.h) * np.float32(scale))
+    _full_compare(w)
+
+
+def test_agrees_with_two_call_backward():
+    # the same gradients as rlk_linear_logp_fwd + rlk_linear_logp_bwd up to the rounding of d
+    from gpu_util import run_bwd
+    w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
+                               seed=99, T=0.7))
+    d = upload(w)
+    _, _, dh1, dW1 = run_bwd(w, d)
+    _, _, dh2, dW2 = run_fused(w, d)
+    eh = rel_l2(dh2.cpu().numpy(), dh1.cpu().numpy())
+    ew = rel_l2(dW2.cpu().numpy(), dW1.cpu().numpy())
+    flush(f"  fused vs two-call: dh relL2 {eh:.3e}, dW relL2 {ew:.3e}")
+    assert eh <= 5e-3 and ew <= 5e-3
+
+
+def test_all_masked():
+    import linear_selected_token_amd as rlk
+    w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
+                               seed=95))
+    d = upload(w)
+    d["mask"].zero_()
+    logp, lse, dh, dW = rlk.rlk_linear_logp_fwd_bwd(d["h"], d["W"], d["targets"], d["mask"], 1.0,
+                                                    d["adv"])
+    torch.cuda.synchronize()
+    assert not logp.any() and not lse.any() and not dh.any() and not dW.any()
+
+
+def test_invariance_and_determinism():
+    fam = wl.Family(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
+                                   seed=95))
+    base = fam.batch()
+    logp, lse, dh, dW = run_fused(base)
+    dh = dh.cpu().numpy()
+    logp = logp.cpu().numpy()
+    ref = {k: (dh[i], logp[i]) for i, k in enumerate(base.key()) if base.mask[i]}
+    for w in (fam.alone(1), fam.shuffled(7), fam.padded(8)):
+        lp2, _, dh2, _ = run_fused(w)
+        dh2 = dh2.cpu().numpy()
+        lp2 = lp2.cpu().numpy()
+        for i, k in enumerate(w.key()):
+            if k[0] >= 0 and w.mask[i]:
+                assert np.array_equal(bits(dh2[i]), bits(ref[k][0])), k
+                assert np.array_equal(bits(lp2[i]), bits(ref[k][1])), k
+    _, _, _, dW2 = run_fused(base)
+    assert np.array_equal(bits(dW.cpu().numpy()), bits(dW2.cpu().numpy()))
+    _, _, _, dW3 = run_fused(fam.padded(9))
+    assert np.array_equal(bits(dW.cpu().numpy()), bits(dW3.cpu().numpy()))
+
+
+# The full Qwen3-8B vocabulary at H = 256: blocks of at most 3072 tokens, so ~60% active of
+# 8000 tokens take two blocks; sampled rows against the oracle
+BLOCKS = wl.scaled_spec(3, N=8000, H=256, n_seq=24, len_lo=128, len_hi=512, seed=161,
+                        targets="uniform", backward=True)
+
+
+def _sampled_compare(w, logp, lse, dh, dW, seed, n_tok=24, n_voc=24):
+    h64, W64 = oracle_inputs(w)
+    act = np.nonzero(w.mask)[0]
+    r = np.random.default_rng(seed)
+    flush(f"  oracle logp and lse over all {act.size} active tokens")
+    ologp, olse = oracle.linear_logp(h64, W64, w.targets, w.mask, w.T)
+    dl = np.abs(logp.cpu().numpy()[act].astype(np.float64) - ologp[act]).max()
+    ds = np.abs(lse.cpu().numpy()[act].astype(np.float64) - olse[act]).max()
+    flush(f"  max|dlogp|={dl:.3e} max|dlse|={ds:.3e}")
+    assert dl <= MAX_ABS_DLOGP and ds <= MAX_ABS_DLOGP
+    ci = edge_rows(act.size, 256, 1)
+    rows = np.unique(np.concatenate([act[ci], r.choice(act, n_tok, replace=False)]))
+    odh = oracle.grad_h_rows(h64, W64, w.targets, w.mask, w.T, w.adv, rows)
+    assert_rows("fused dh (sampled rows)",
+                dh[torch.from_numpy(rows).to(dh.device)].cpu().numpy(), odh, rows)
+    _, split = _chunking()
+    vr = np.unique(np.concatenate([w.targets[act[:8]], edge_rows(w.V, split, 2),
+                                   [w.V - 2, w.V - 1], r.integers(0, w.V, n_voc)]))
+    odW = oracle.grad_W_rows(h64, W64, w.targets, w.mask, w.T, w.adv, vr, lse=olse)
+    assert_rows("fused dW (sampled rows)",
+                dW[torch.from_numpy(vr).to(dW.device)].cpu().numpy(), odW, vr)
+
+
+def test_token_blocks_sampled():
+    w = wl.make(BLOCKS)
+    cap = _fused_cap(w.H, w.V)
+    flush(f"  {w.n_active} active of {w.N}: fused blocks of at most {cap}")
+    assert cap < w.n_active < 2 * cap
+    d = upload(w)
+    logp, lse, dh, dW = run_fused(w, d)
+    _same_forward(w, d, logp, lse)
+    assert not dh[torch.from_numpy(w.mask == 0).to(dh.device)].any()
+    _sampled_compare(w, logp, lse, dh, dW, 162)
+
+
+def test_token_blocks_dh_invariance():
+    # a token's logp and dL/dh row keep their bits whichever block it falls in
+    fam = wl.Family(BLOCKS)
+    base = fam.batch()
+    logp, _, dh, _ = run_fused(base)
+    dh = dh.cpu().numpy()
+    logp = logp.cpu().numpy()
+    ref = {k: (dh[i], logp[i]) for i, k in enumerate(base.key()) if base.mask[i]}
+    for w in (fam.alone(5), fam.shuffled(3), fam.all_active()):
+        lp2, _, dh2, _ = run_fused(w)
+        dh2 = dh2.cpu().numpy()
+        lp2 = lp2.cpu().numpy()
+        n = 0
+        for i, k in enumerate(w.key()):
+            if k[0] >= 0 and w.mask[i] and k in ref:
+                assert np.array_equal(bits(dh2[i]), bits(ref[k][0])), k
+                assert np.array_equal(bits(lp2[i]), bits(ref[k][1])), k
+                n += 1
+        flush(f"  {w.N} tokens, {w.n_active} active: {n} rows bit-identical")
+
+
+def test_config5_full_size_sampled():
+    flush("config 5 fused: generating inputs")
+    w = wl.make(5)
+    d = upload(w)
+    logp, lse, dh, dW = run_fused(w, d)
+    _same_forward(w, d, logp, lse)
+    _sampled_compare(w, logp, lse, dh, dW, 163)
+    colsum = dW.double().sum(0).abs().max().item()
+    scale = dW.double().abs().sum(0).max().item()
+    flush(f"  config5 fused |sum_v dW_v|max={colsum:.3e} (column abs-sum {scale:.3e})")
+    assert colsum <= 1e-3 * scale
+
+
+def test_autograd_loss():
+    import linear_selected_token_amd as rlk
+    w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
+                               seed=95))
+    d = upload(w)
+    h = d["h"].clone().requires_grad_(True)
+    W = d["W"].clone().requires_grad_(True)
+    loss, lp = rlk.linear_logp_pg_loss(h, W, d["targets"], d["mask"], w.T, d["adv"])
+    (2.0 * loss).backward()
+    logp, _, dh, dW = run_fused(w, d)
+    assert torch.equal(lp, logp)
+    assert torch.equal(h.grad, (2.0 * dh).to(torch.bfloat16))
+    assert torch.equal(W.grad, (2.0 * dW).to(torch.bfloat16))
+    ref = -(d["mask"].float() * d["adv"] * logp).sum()
+    assert torch.equal(loss.detach(), ref)
