@@ -26,14 +26,15 @@ namespace rlk {
 
 namespace {
 
-// The 16-bit code of an exponent d <= 0 (log2 units): round(-d 2^9), clamped to [0, 65535]
-// (-inf gives 65535; a rounding residual just above 0 gives 0).  Two codes per word, the first
-// in the low half.
-__device__ __forceinline__ uint32_t dcode(float d) {
-  return (uint32_t)__builtin_rintf(fminf(fmaxf(-d * 512.f, 0.f), 65535.f));
-}
-__device__ __forceinline__ uint32_t pack_dcode(float lo, float hi) {
-  return dcode(lo) | (dcode(hi) << 16);
+// The 16-bit codes of two entries' exponents d = acc c2 - mx <= 0 (log2 units): -d 2^9 rounded
+// half up and clamped to [0, 65535], as one fma per entry with k1 = -c2 2^9 and
+// k2 = mx 2^9 + 1/2, then truncation (a -inf entry past the vocabulary gives 65535; the
+// column maximum's own rounding residual gives 0).  Two codes per word, the first in the low
+// half.
+__device__ __forceinline__ uint32_t pack_dcode(float acc_lo, float acc_hi, float k1, float k2) {
+  const float lo = __builtin_amdgcn_fmed3f(__builtin_fmaf(acc_lo, k1, k2), 0.f, 65535.f);
+  const float hi = __builtin_amdgcn_fmed3f(__builtin_fmaf(acc_hi, k1, k2), 0.f, 65535.f);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_u16((uint32_t)lo, (uint32_t)hi));
 }
 
 struct FwdCtx {
@@ -55,7 +56,7 @@ struct FwdCtx {
 //                pairs their x entry by entry from two such buffers.
 //   kFwdStoreD   the plain statistics and target, and d = x - max of every entry of the tile
 //                (the exponent the column sum adds up, <= 0) into dbuf as a 16-bit code,
-//                round(-d 2^9) clamped to [0, 65535]: steps of 2^-9 over (-128, 0], so the
+//                -d 2^9 rounded and clamped to [0, 65535]: steps of 2^-9 over (-128, 0], so the
 //                p = 2^(d + max - lse) it gives back carries at most 2^-10 ln 2 relative error
 //                whatever d is (entries with d <= -128 have p < 2^-128).  Token-major rows of
 //                d_pitch codes, entry v of the vocabulary at column v, one row per compacted
@@ -212,17 +213,15 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
         // Rows of padded token columns (ti >= Na, still inside the block's rows) are written
         // too and never read as d.
         uint16_t* drow = a.dbuf + (size_t)ti * a.d_pitch + vq;
+        const float k1 = -c2 * 512.f;
+        const float k2 = __builtin_fmaf(mx, 512.f, 0.5f);
 #pragma unroll
         for (int i = 0; i < kBlkA; ++i) {
           u32x2 pk[4];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const float d0 = __builtin_fmaf(acc.c[i][j][4 * g + 0], c2, -mx);
-            const float d1 = __builtin_fmaf(acc.c[i][j][4 * g + 1], c2, -mx);
-            const float d2 = __builtin_fmaf(acc.c[i][j][4 * g + 2], c2, -mx);
-            const float d3 = __builtin_fmaf(acc.c[i][j][4 * g + 3], c2, -mx);
-            pk[g][0] = pack_dcode(d0, d1);
-            pk[g][1] = pack_dcode(d2, d3);
+            pk[g][0] = pack_dcode(acc.c[i][j][4 * g + 0], acc.c[i][j][4 * g + 1], k1, k2);
+            pk[g][1] = pack_dcode(acc.c[i][j][4 * g + 2], acc.c[i][j][4 * g + 3], k1, k2);
           }
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
