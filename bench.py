@@ -559,6 +559,9 @@ def main():
     if "fused" in m:
         out["fwd_bwd_tflops_executed"] = m["fused"]["tflops_executed"]
         out["fwd_bwd_mfma_frac"] = m["fused"]["mfma_frac"]
+        if "one_block" in m["fused"]:
+            # not the headline: the default workspace (under 1e9 bytes) is
+            out["fused_one_block_workspace"] = m["fused"]["one_block"]
         out["two_calls"] = m["two_calls"]
     if "workspace_bytes" in m:
         out["workspace_bytes"] = m["workspace_bytes"]
@@ -684,6 +687,25 @@ def measure(w, dev, steps, warmup, do_bwd):
         del xws
         fused = {"ms": fms, "step_ms_median": round(float(np.median(fstep_ms)), 4),
                  "step_ms_min": round(float(np.min(fstep_ms)), 4)}
+        # the same call with a workspace that holds every active token in one block
+        nb = rlk.fwd_bwd_workspace_bytes_for_block(N, H, V, dt, Na)
+        if nb > ws_bytes["fwd_bwd"]:
+            xws = torch.empty(nb, dtype=torch.uint8, device=dev)
+            for _ in range(warmup):
+                fstep(events(2))
+            torch.cuda.synchronize()
+            f0, f1 = events(2)
+            f0.record()
+            for ev in fevs:
+                fstep(ev)
+            f1.record()
+            torch.cuda.synchronize()
+            assert torch.equal(res["flogp"], res["logp"]), "one-block and two-call logp differ"
+            oms = f0.elapsed_time(f1) / steps
+            fused["one_block"] = {"ms": round(oms, 4),
+                                  "active_tokens_per_s": round(Na / (oms * 1e-3), 1),
+                                  "workspace_bytes": nb}
+            del xws
 
     bf16 = w.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
@@ -759,6 +781,7 @@ def bench_configs(args, dev):
             rec.update({"fwd_bwd_ms": round(f["ms"], 4),
                         "fwd_bwd_active_tokens_per_s": round(Na / (f["ms"] * 1e-3), 1),
                         "fwd_bwd_mfma_frac": f["mfma_frac"],
+                        "fused_one_block_workspace": f.get("one_block"),
                         "two_calls": {k: m["two_calls"][k] for k in
                                       ("ms", "active_tokens_per_s", "bwd_ms", "bwd_mfma_frac",
                                        "mfma_frac")}})

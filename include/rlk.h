@@ -230,6 +230,16 @@ rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* ta
  * RLK_ERROR_UNSUPPORTED when N would need more than 1024 blocks. */
 rlk_status_t rlk_linear_logp_fwd_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
                                                     size_t* bytes);
+/* A workspace larger than rlk_linear_logp_fwd_bwd_workspace_size buys larger token blocks: the
+ * call takes blocks of the largest multiple of 256 tokens (past the budget's) whose buffers fit
+ * workspace_bytes, at most one block for all N tokens.  This query gives the bytes for blocks
+ * of at least block_tokens tokens (rounded up to 256; block_tokens >= N: one block), e.g.
+ * 3.38 GB for blocks of 9984 tokens at N = 16384, H = 4096, V = 151936 (one block for up to
+ * 9984 active tokens).  logp, lse and dL/dh do not depend on the block size; dL/dW sums the
+ * blocks in ascending order, so its rounding does. */
+rlk_status_t rlk_linear_logp_fwd_bwd_workspace_size_for_block(int64_t N, int64_t H, int64_t V,
+                                                              int dtype, int64_t block_tokens,
+                                                              size_t* bytes);
 rlk_status_t rlk_linear_logp_fwd_bwd(const void* h, const void* W, const int32_t* targets,
                                      const uint8_t* mask, int64_t N, int64_t H, int64_t V,
                                      int dtype, float temperature, const float* adv, float* logp,

@@ -15,6 +15,7 @@ from .ops import (  # noqa: E402,F401
     LinearLogpPGLoss,
     bwd_workspace_bytes,
     fwd_bwd_workspace_bytes,
+    fwd_bwd_workspace_bytes_for_block,
     fwd_entropy_workspace_bytes,
     fwd_workspace_bytes,
     linear_kl,

@@ -179,10 +179,12 @@ rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, con
   if (N == 0) return dev_status(launch_zero(dW, (size_t)V * (size_t)H, st));
   int grid = 0;
   if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
-  const FusedLayout L = fused_layout(N, H, V);
-  const int np = (int)fused_npad(N, H, V);
-  const int cap = (int)fused_token_cap(H, V);
-  const int nblk = fused_blocks(N, H, V);
+  // the budget's block capacity, or a larger one that the given workspace holds
+  const int64_t cap64 = fused_cap_for_workspace(N, H, V, workspace_bytes);
+  const FusedLayout L = fused_layout_cap(N, H, V, cap64);
+  const int np = (int)fused_npad_cap(N, cap64);
+  const int cap = (int)cap64;
+  const int nblk = fused_blocks_cap(N, cap64);
   const float inv_t = (float)(1.0 / (double)temperature);
   int32_t* idx = carve<int32_t>(workspace, L.idx);
   int32_t* na = carve<int32_t>(workspace, L.n_active);
@@ -770,6 +772,21 @@ rlk_status_t rlk_linear_logp_fwd_bwd_workspace_size(int64_t N, int64_t H, int64_
   if (dtype != RLK_BF16 || H % 256 != 0 || fused_blocks(N, H, V) > 1024)
     return RLK_ERROR_UNSUPPORTED;
   *bytes = fused_layout(N, H, V).total;
+  return RLK_SUCCESS;
+}
+
+rlk_status_t rlk_linear_logp_fwd_bwd_workspace_size_for_block(int64_t N, int64_t H, int64_t V,
+                                                              int dtype, int64_t block_tokens,
+                                                              size_t* bytes) {
+  if (!bytes || block_tokens < 0) return RLK_ERROR_INVALID_VALUE;
+  rlk_status_t s = check_shape(N, H, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  if (dtype != RLK_BF16 || H % 256 != 0 || fused_blocks(N, H, V) > 1024)
+    return RLK_ERROR_UNSUPPORTED;
+  const int64_t n = N > 0 ? N : 1;
+  const int64_t want = ((block_tokens < n ? block_tokens : n) + 255) / 256 * 256;
+  const int64_t c0 = fused_token_cap(H, V);
+  *bytes = fused_layout_cap(N, H, V, want > c0 ? want : c0).total;
   return RLK_SUCCESS;
 }
 

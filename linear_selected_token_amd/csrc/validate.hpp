@@ -185,15 +185,22 @@ inline int64_t fused_token_cap(int64_t H, int64_t V) {
   return c < 256 ? 256 : (c > kMaxTokens ? kMaxTokens : c);
 }
 
-inline int fused_blocks(int64_t N, int64_t H, int64_t V) {
-  const int64_t cap = fused_token_cap(H, V);
+// Blocks of at most cap tokens (a multiple of 256) for N tokens, and the block buffers' rows.
+inline int fused_blocks_cap(int64_t N, int64_t cap) {
   return (int)(((N > 0 ? N : 1) + cap - 1) / cap);
 }
 
-inline int64_t fused_npad(int64_t N, int64_t H, int64_t V) {
-  const int64_t cap = fused_token_cap(H, V);
+inline int64_t fused_npad_cap(int64_t N, int64_t cap) {
   const int64_t n = N <= 0 ? 1 : (N < cap ? N : cap);
   return (n + 255) / 256 * 256;
+}
+
+inline int fused_blocks(int64_t N, int64_t H, int64_t V) {
+  return fused_blocks_cap(N, fused_token_cap(H, V));
+}
+
+inline int64_t fused_npad(int64_t N, int64_t H, int64_t V) {
+  return fused_npad_cap(N, fused_token_cap(H, V));
 }
 
 // Workspace layout of the fused forward + backward: idx[N] | n_active | block_desc[blocks][2] |
@@ -204,15 +211,16 @@ struct FusedLayout {
       dhp[kBwdDhPieces], total;
 };
 
-inline FusedLayout fused_layout(int64_t N, int64_t H, int64_t V) {
+// The layout for blocks of at most cap tokens (fused_layout: the budget's capacity).
+inline FusedLayout fused_layout_cap(int64_t N, int64_t H, int64_t V, int64_t cap) {
   FusedLayout L;
   const size_t n = (size_t)(N > 0 ? N : 1);
-  const size_t np = (size_t)fused_npad(N, H, V);
+  const size_t np = (size_t)fused_npad_cap(N, cap);
   const size_t jn = 4 * np * (size_t)num_partials(V);
   size_t o = 0;
   L.idx = o;          o = align_up(o + 4 * n, 256);
   L.n_active = o;     o = align_up(o + 4, 256);
-  L.block_desc = o;   o = align_up(o + 8 * (size_t)fused_blocks(N, H, V), 256);
+  L.block_desc = o;   o = align_up(o + 8 * (size_t)fused_blocks_cap(N, cap), 256);
   L.bidx = o;         o = align_up(o + 4 * np, 256);
   L.bn = o;           o = align_up(o + 4, 256);
   L.sched = o;        o = align_up(o + 4 * 8, 256);
@@ -228,6 +236,26 @@ inline FusedLayout fused_layout(int64_t N, int64_t H, int64_t V) {
   }
   L.total = o;
   return L;
+}
+
+inline FusedLayout fused_layout(int64_t N, int64_t H, int64_t V) {
+  return fused_layout_cap(N, H, V, fused_token_cap(H, V));
+}
+
+// The block capacity a workspace of ws_bytes allows: the budget's capacity, or the largest
+// multiple of 256 tokens past it whose layout still fits ws_bytes (at most N rounded up to 256:
+// one block).  A larger workspace only buys fewer, larger blocks.
+inline int64_t fused_cap_for_workspace(int64_t N, int64_t H, int64_t V, size_t ws_bytes) {
+  const int64_t c0 = fused_token_cap(H, V);
+  const int64_t top = ((N > 0 ? N : 1) + 255) / 256 * 256;
+  if (top <= c0 || fused_layout_cap(N, H, V, c0 + 256).total > ws_bytes) return c0;
+  int64_t lo = c0 + 256, hi = top;  // lo fits; find the largest fitting multiple of 256
+  while (lo < hi) {
+    const int64_t mid = (lo / 256 + (hi / 256 - lo / 256 + 1) / 2) * 256;
+    if (fused_layout_cap(N, H, V, mid).total <= ws_bytes) lo = mid;
+    else hi = mid - 256;
+  }
+  return lo;
 }
 
 // Workspace of the log-prob from existing logits: idx[N] | n_active.

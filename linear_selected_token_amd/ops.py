@@ -259,6 +259,17 @@ def fwd_bwd_workspace_bytes(N: int, H: int, V: int, dtype: int) -> int:
     return int(out.value)
 
 
+def fwd_bwd_workspace_bytes_for_block(N: int, H: int, V: int, dtype: int,
+                                      block_tokens: int) -> int:
+    """Workspace bytes with which rlk_linear_logp_fwd_bwd takes blocks of at least block_tokens
+    tokens (block_tokens >= N: one block)."""
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_linear_logp_fwd_bwd_workspace_size_for_block(N, H, V, dtype, block_tokens,
+                                                                     ctypes.byref(out)),
+            "rlk_linear_logp_fwd_bwd_workspace_size_for_block")
+    return int(out.value)
+
+
 def rlk_linear_logp_fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                             mask: torch.Tensor, temperature: float, adv: torch.Tensor,
                             workspace: Optional[torch.Tensor] = None,

@@ -227,6 +227,18 @@ static void test_fused() {
   }
   const size_t ws = fused_layout(16384, 4096, 151936).total;
   EXPECT(ws <= (size_t)kBwdBlockBudget);
+  // a larger workspace gives the largest capacity (a multiple of 256 past the budget's, at most
+  // one block) whose layout fits it
+  for (int64_t N : {int64_t(300), int64_t(9831), int64_t(16384), int64_t(100000)}) {
+    const int64_t c0 = fused_token_cap(4096, 151936), top = (N + 255) / 256 * 256;
+    EXPECT(fused_cap_for_workspace(N, 4096, 151936, fused_layout(N, 4096, 151936).total) == c0);
+    EXPECT(fused_cap_for_workspace(N, 4096, 151936, size_t(1) << 62) == (top > c0 ? top : c0));
+    for (int64_t c = c0 + 256; c <= top && c <= c0 + 256 * 40; c += 256) {
+      const size_t t = fused_layout_cap(N, 4096, 151936, c).total;
+      EXPECT(fused_cap_for_workspace(N, 4096, 151936, t) == c);
+      EXPECT(fused_cap_for_workspace(N, 4096, 151936, t - 1) == c - 256);
+    }
+  }
   auto call = [&](uintptr_t lp, uintptr_t ls, uintptr_t dh, int dt, int64_t H, size_t bytes) {
     return check_fused(P(A), P(A), PT<const int32_t>(A), PT<const uint8_t>(A), 16384, H, 151936,
                        dt, 0.7f, PT<const float>(A), PT<float>(lp), PT<float>(ls), PT<float>(dh),

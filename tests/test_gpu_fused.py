@@ -210,6 +210,30 @@ def test_token_blocks_dh_invariance():
         flush(f"  {w.N} tokens, {w.n_active} active: {n} rows bit-identical")
 
 
+def test_larger_workspace_one_block():
+    # a workspace sized for one block of every active token: logp, lse and each dL/dh row keep
+    # their bits; dL/dW (one block's sum instead of two) agrees with the oracle and, to rounding,
+    # with the two-block result
+    import linear_selected_token_amd as rlk
+    w = wl.make(BLOCKS)
+    d = upload(w)
+    lp1, ls1, dh1, dW1 = run_fused(w, d)
+    nb = rlk.fwd_bwd_workspace_bytes_for_block(w.N, w.H, w.V, 0, w.n_active)
+    assert nb > rlk.fwd_bwd_workspace_bytes(w.N, w.H, w.V, 0)
+    ws = torch.empty(nb, dtype=torch.uint8, device=d["h"].device)
+    lp2, ls2, dh2, dW2 = rlk.rlk_linear_logp_fwd_bwd(d["h"], d["W"], d["targets"], d["mask"], w.T,
+                                                     d["adv"], workspace=ws)
+    torch.cuda.synchronize()
+    flush(f"  {w.n_active} active: one block with {nb / 1e9:.2f} GB against two")
+    assert torch.equal(lp1.view(torch.int32), lp2.view(torch.int32))
+    assert torch.equal(ls1.view(torch.int32), ls2.view(torch.int32))
+    assert torch.equal(dh1.view(torch.int32), dh2.view(torch.int32))
+    e = rel_l2(dW2.cpu().numpy(), dW1.cpu().numpy())
+    flush(f"  dW one block vs two: relL2 {e:.3e}")
+    assert e <= 1e-5
+    _sampled_compare(w, lp2, ls2, dh2, dW2, 164, n_tok=8)
+
+
 def test_config5_full_size_sampled():
     flush("config 5 fused: generating inputs")
     w = wl.make(5)
