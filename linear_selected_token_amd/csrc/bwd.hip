@@ -108,41 +108,63 @@ __global__ __launch_bounds__(256) void fill_kernel(float* p, size_t n, float val
 // (it moves log2 p by at most 2^-10: a relative error of at most 2^-10 ln 2 in p, for every
 // entry; the bf16 rounding of G that follows is up to 2^-9).  Rows of padded token columns
 // (Na <= m < the block's 256-token tiles) and the entries past the vocabulary become 0, so the
-// GEMMs that read X as dL/dz add nothing for them.  Each thread converts 8 consecutive entries
-// (16 bytes in, 16 bytes out, in place); a work-group takes 2048 entries of one row; the grid
-// walks (row, segment) pairs.
+// GEMMs that read X as dL/dz add nothing for them.  A work-group takes 8192 entries of one row
+// (the grid walks (row, segment) pairs): each thread converts four groups of 8 consecutive
+// entries, 2048 entries apart, in place, with all four 16-byte loads issued before any result
+// is formed.
 __global__ __launch_bounds__(256) void dz_from_d_kernel(DzArgs a) {
+  constexpr int kU = 4;                  // 16-byte groups per thread per segment
+  constexpr int kSeg = 8 * 256 * kU;     // entries per segment (8192)
   const int Na = *a.n_active;
   const int rows = (Na + kTile - 1) / kTile * kTile;
   const int vr = (a.V + kTile - 1) / kTile * kTile;  // columns the GEMMs may read
-  const int nseg = (vr + 2047) / 2048;
+  const int nseg = (vr + kSeg - 1) / kSeg;
   const int64_t total = (int64_t)rows * nseg;
   for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
     const int m = (int)(u / nseg);
-    const int v0 = (int)(u - (int64_t)m * nseg) * 2048 + 8 * (int)threadIdx.x;
-    if (v0 >= vr) continue;
-    u32x4* p = reinterpret_cast<u32x4*>(a.X + (size_t)m * a.pitch + v0);
-    u32x4 out = {0u, 0u, 0u, 0u};
-    if (m < Na && v0 < a.V) {  // (the quadrant holding v0 was stored: its d entries are set)
-      const int t = a.idx[m];
-      const float gs = -a.adv[t] * a.inv_t;
-      const int y = a.targets[t];
-      const float off = a.part_max[(size_t)(v0 / kVocabPartial) * a.pstride + m] - a.lse[t] * kLog2e;
-      const u32x4 cw = *p;
+    const int s0 = (int)(u - (int64_t)m * nseg) * kSeg + 8 * (int)threadIdx.x;
+    uint16_t* row = a.X + (size_t)m * a.pitch;
+    if (m >= Na) {  // a padded row of the block's last token tile: zeros
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const int v0 = s0 + 2048 * k;
+        if (v0 < vr) *reinterpret_cast<u32x4*>(row + v0) = u32x4{0u, 0u, 0u, 0u};
+      }
+      continue;
+    }
+    const int t = a.idx[m];
+    const float gs = -a.adv[t] * a.inv_t;
+    const int y = a.targets[t];
+    const float lse2 = a.lse[t] * kLog2e;
+    // group k: entries v0 .. v0 + 7 (inside one 128-entry column), loaded before any is used
+    u32x4 cw[kU];
+    float off[kU];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const int v0 = s0 + 2048 * k;
+      const bool in = v0 < a.V;  // (the quadrant holding v0 was stored: its entries are set)
+      cw[k] = in ? *reinterpret_cast<const u32x4*>(row + v0) : u32x4{0u, 0u, 0u, 0u};
+      off[k] = in ? a.part_max[(size_t)(v0 / kVocabPartial) * a.pstride + m] - lse2 : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const int v0 = s0 + 2048 * k;
+      if (v0 >= vr) continue;
       float G[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int v = v0 + e;
-        const uint32_t c = (cw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf((float)c, -1.f / 512.f, off));
+        const uint32_t c = (cw[k][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf((float)c, -1.f / 512.f, off[k]));
         G[e] = v < a.V ? gs * ((v == y ? 1.f : 0.f) - pv) : 0.f;
       }
+      u32x4 out;
       out.x = pack_bf16(G[0], G[1]);
       out.y = pack_bf16(G[2], G[3]);
       out.z = pack_bf16(G[4], G[5]);
       out.w = pack_bf16(G[6], G[7]);
+      *reinterpret_cast<u32x4*>(row + v0) = out;
     }
-    *p = out;
   }
 }
 
