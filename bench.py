@@ -559,6 +559,8 @@ def main():
     if "fused" in m:
         out["fwd_bwd_tflops_executed"] = m["fused"]["tflops_executed"]
         out["fwd_bwd_mfma_frac"] = m["fused"]["mfma_frac"]
+        out["fwd_bwd_frac_over_8NaHV"] = m["fused"]["frac_over_8NaHV"]
+        out["bwd_added_ms"] = m["fused"]["bwd_added_ms"]
         if "one_block" in m["fused"]:
             # not the headline: the default workspace (under 1e9 bytes) is
             out["fused_one_block_workspace"] = m["fused"]["one_block"]
@@ -739,6 +741,11 @@ def measure(w, dev, steps, warmup, do_bwd):
         fflop = 6.0 * Na * H * V
         fused["tflops_executed"] = round(fflop / (fused["ms"] * 1e-3) / 1e12, 2)
         fused["mfma_frac"] = round(fflop / (fused["ms"] * 1e-3) / 1e12 / peak, 4)
+        # the same job counted as the recompute formulation's 8 H V flops per active token (what
+        # the two calls execute): a rate for comparing the two forms, not flops executed here
+        fused["frac_over_8NaHV"] = round(fwd_flop * 4 / (fused["ms"] * 1e-3) / 1e12 / peak, 4)
+        # what the backward adds to a forward alone (fused step minus the forward call)
+        fused["bwd_added_ms"] = round(fused["ms"] - fwd_ms, 4)
         m["fused"] = fused
     return m
 
@@ -781,6 +788,8 @@ def bench_configs(args, dev):
             rec.update({"fwd_bwd_ms": round(f["ms"], 4),
                         "fwd_bwd_active_tokens_per_s": round(Na / (f["ms"] * 1e-3), 1),
                         "fwd_bwd_mfma_frac": f["mfma_frac"],
+                        "fwd_bwd_frac_over_8NaHV": f["frac_over_8NaHV"],
+                        "bwd_added_ms": f["bwd_added_ms"],
                         "fused_one_block_workspace": f.get("one_block"),
                         "two_calls": {k: m["two_calls"][k] for k in
                                       ("ms", "active_tokens_per_s", "bwd_ms", "bwd_mfma_frac",

@@ -273,18 +273,21 @@ rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int
  *   h_t [N,H_t], W_t [V,H_t]   teacher (the same dtype, vocabulary and temperature)
  *   z_s = h_s W_s^T / T, z_t = h_t W_t^T / T, p = softmax(z)
  *   kl_fwd[t] = sum_v p_t (log p_t - log p_s),  kl_rev[t] = sum_v p_s (log p_s - log p_t)
- * at active tokens, 0 elsewhere (both clamped at 0 against rounding).  The vocabulary is walked
- * in chunks of 32768 entries: per chunk each head's tile GEMM writes its column statistics
- * and its logits of that chunk only (fp32, one token block of rlk_linear_logp_bwd's size for
- * the student's H, x 32768 entries, in the workspace), a streaming kernel pairs the two entry
- * by entry, and a fixed-order merge gives the results.
+ * at active tokens, 0 elsewhere (both clamped at 0 against rounding).  The active tokens are
+ * taken in blocks (compacted order) of at most the largest multiple of 256 tokens whose rows
+ * fit 1e9 bytes (8 (32768 + 32) + 24 ceil(V/128) bytes per token: 3328 tokens at V = 151936).
+ * Per block the vocabulary is walked in chunks of 32768 entries: per chunk each head's tile
+ * GEMM writes its column statistics and its logits of that chunk only (fp32, the block's rows x
+ * 32768 entries, in the workspace), a streaming kernel pairs the two entry by entry, and after
+ * the block's last chunk a fixed-order merge gives its tokens' results.
  * Batch-invariant like logp.  H_s and H_t: multiples of 64; each h at most 2^31 - 1 bytes.
+ * RLK_ERROR_UNSUPPORTED when N would need more than 1024 blocks.
  *   lse_s, lse_t [N] float     out (may be NULL): each head's log-sum-exp, which the backward
  *                              takes back
- *   workspace: rlk_linear_kl_fwd_workspace_size bytes: six float arrays of ceil(V/128) x N
- *              (both heads' column statistics and the two cross terms) and two chunk buffers of
- *              32800 floats per token of one block (3.36 GB in all at N = 16384, H_s = 4096,
- *              V = 151936). */
+ *   workspace: rlk_linear_kl_fwd_workspace_size bytes: six float arrays of ceil(V/128) x one
+ *              block's rows (both heads' column statistics and the two cross terms) and two
+ *              chunk buffers of 32800 floats per row (0.97 GB at N = 16384, V = 151936; past
+ *              one block only the 4-byte index per token grows). */
 rlk_status_t rlk_linear_kl_fwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
                                               int dtype, size_t* bytes);
 rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t,

@@ -540,7 +540,8 @@ rlk_status_t rlk_linear_kl_fwd_workspace_size(int64_t N, int64_t H_s, int64_t H_
   rlk_status_t s = check_shape(N, H_s, V, dtype);
   if (s == RLK_SUCCESS) s = check_shape(N, H_t, V, dtype);
   if (s != RLK_SUCCESS) return s;
-  *bytes = kl_fwd_layout(N, H_s, V).total;
+  if (kl_fwd_blocks(N, V) > 1024) return RLK_ERROR_UNSUPPORTED;  // the compaction's bound
+  *bytes = kl_fwd_layout(N, V).total;
   return RLK_SUCCESS;
 }
 
@@ -555,14 +556,16 @@ rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t
   if (!kl_fwd || !kl_rev) return RLK_ERROR_INVALID_VALUE;
   if (!aligned(kl_fwd, 4) || !aligned(kl_rev, 4) || !aligned(lse_s, 4) || !aligned(lse_t, 4))
     return RLK_ERROR_UNSUPPORTED;
-  if (workspace_bytes < kl_fwd_layout(N, H_s, V).total) return RLK_ERROR_WORKSPACE;
-  const KlLayout L = kl_fwd_layout(N, H_s, V);
+  if (kl_fwd_blocks(N, V) > 1024) return RLK_ERROR_UNSUPPORTED;
+  if (workspace_bytes < kl_fwd_layout(N, V).total) return RLK_ERROR_WORKSPACE;
+  const KlLayout L = kl_fwd_layout(N, V);
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* idx = carve<int32_t>(workspace, L.idx);
   int32_t* na = carve<int32_t>(workspace, L.n_active);
   int32_t* counts = carve<int32_t>(workspace, L.block_count);
-  const int nblk = bwd_blocks(N, H_s);
-  const int cap = (int)bwd_token_cap(H_s);
+  const int nblk = kl_fwd_blocks(N, V);
+  const int cap = (int)kl_fwd_token_cap(V);
+  const int np = (int)kl_fwd_npad(N, V);
   CompactArgs c{mask, idx, na, nullptr, kl_fwd, lse_s, (int)N, kl_rev, lse_t};
   c.block_count = counts;
   c.nblk = nblk;
@@ -576,7 +579,7 @@ rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t
   KlArgs k{};
   k.idx = idx;
   k.n_active = na;
-  k.N = (int)N;
+  k.N = np;  // the row stride of the block's statistics
   k.V = (int)V;
   k.inv_t = inv_t;
   k.xs = carve<float>(workspace, L.xs);
@@ -591,40 +594,38 @@ rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t
   k.kl_rev = kl_rev;
   k.lse_s = lse_s;
   k.lse_t = lse_t;
-  // Per token block (the chunk buffers hold one block's rows): per chunk, both heads' column
-  // statistics and x, then the cross terms.  The [J][N] arrays are addressed from the block's
-  // first compacted index, so each block writes its own columns of them.
+  // Per token block (the fixed partition: compacted indices b * cap ..; the buffers hold one
+  // block's rows): per chunk, both heads' column statistics and x, then the cross terms; then
+  // the block's merge writes its tokens' results.
   for (int b = 0; b < nblk; ++b) {
     const size_t t0 = (size_t)b * cap;
-    const int rows = (int)(N - (int64_t)t0 < cap ? N - (int64_t)t0 : cap);
+    const int rows = (int)(N - (int64_t)t0 < np ? N - (int64_t)t0 : np);
     KlArgs kb = k;
     kb.idx = idx + t0;
     kb.n_active = counts + b;
-    kb.s_max = k.s_max + t0;
-    kb.s_sum = k.s_sum + t0;
-    kb.t_max = k.t_max + t0;
-    kb.t_sum = k.t_sum + t0;
-    kb.wf = k.wf + t0;
-    kb.wr = k.wr + t0;
     for (int64_t c0 = 0; c0 < V; c0 += kBwdChunk) {
       const int vc = (int)(V - c0 < kBwdChunk ? V - c0 : kBwdChunk);
       FwdTileArgs t{h_t, static_cast<const uint8_t*>(W_t) + (size_t)c0 * H_t * es, nullptr,
                     kb.idx, kb.n_active, (int)N, (int)H_t, vc, inv_t,
                     const_cast<float*>(kb.t_max), const_cast<float*>(kb.t_sum), nullptr, (int)c0,
                     nullptr, const_cast<float*>(k.xt)};
+      t.pstride = np;
       e = launch_fwd_tiles(t, dtype == RLK_BF16, grid, st, kFwdStoreX);
       if (e != hipSuccess) return RLK_ERROR_DEVICE;
       FwdTileArgs u{h_s, static_cast<const uint8_t*>(W_s) + (size_t)c0 * H_s * es, nullptr,
                     kb.idx, kb.n_active, (int)N, (int)H_s, vc, inv_t,
                     const_cast<float*>(kb.s_max), const_cast<float*>(kb.s_sum), nullptr, (int)c0,
                     nullptr, const_cast<float*>(k.xs)};
+      u.pstride = np;
       e = launch_fwd_tiles(u, dtype == RLK_BF16, grid, st, kFwdStoreX);
       if (e != hipSuccess) return RLK_ERROR_DEVICE;
       e = launch_kl_cross(kb, (int)c0, rows, st);
       if (e != hipSuccess) return RLK_ERROR_DEVICE;
     }
+    e = launch_kl_merge(kb, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
   }
-  return dev_status(launch_kl_merge(k, st));
+  return RLK_SUCCESS;
 }
 
 rlk_status_t rlk_linear_kl_bwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,

@@ -355,32 +355,61 @@ inline rlk_status_t check_fused(const void* h, const void* W, const int32_t* tar
   return RLK_SUCCESS;
 }
 
-// Full-vocabulary KL: one chunk of each head's x for one token block, [Npad][chunk] fp32
-// (the KL paths take the active tokens in the backward's blocks, sized for the student's H).
-inline size_t kl_chunk_bytes(int64_t N, int64_t H) {
-  return align_up(4 * (size_t)bwd_npad(N, H) * (size_t)(kBwdChunkEntries + 32), 256);  // kXPitch
+// Full-vocabulary KL: one chunk of each head's x for np token rows, [np][chunk + 32] fp32.
+inline size_t kl_chunk_bytes_rows(int64_t np) {
+  return align_up(4 * (size_t)np * (size_t)(kBwdChunkEntries + 32), 256);  // kXPitch
+}
+
+// The KL backward takes the active tokens in the backward's blocks (the student's H sets them).
+inline size_t kl_chunk_bytes(int64_t N, int64_t H) { return kl_chunk_bytes_rows(bwd_npad(N, H)); }
+
+// The KL forward takes the active tokens in blocks of its own: per token of capacity, a row of
+// each head's fp32 x chunk and a row of the six column-statistics arrays (both heads' maxima
+// and sums, both cross terms), 8 (chunk + 32) + 24 ceil(V / 128) bytes.  The capacity is the
+// largest multiple of 256 tokens whose rows fit the backward's budget (at least 256): 3328
+// tokens at V = 151936, so the forward's workspace stays under 1e9 bytes at any N.
+inline size_t kl_fwd_bytes_per_token(int64_t V) {
+  return 8 * (size_t)(kBwdChunkEntries + 32) + 24 * (size_t)num_partials(V);
+}
+
+inline int64_t kl_fwd_token_cap(int64_t V) {
+  const int64_t c = (int64_t)(kBwdBlockBudget / kl_fwd_bytes_per_token(V > 0 ? V : 1)) / 256 * 256;
+  return c < 256 ? 256 : (c > kMaxTokens ? kMaxTokens : c);
+}
+
+inline int kl_fwd_blocks(int64_t N, int64_t V) {
+  const int64_t cap = kl_fwd_token_cap(V);
+  return (int)(((N > 0 ? N : 1) + cap - 1) / cap);
+}
+
+inline int64_t kl_fwd_npad(int64_t N, int64_t V) {
+  const int64_t cap = kl_fwd_token_cap(V);
+  const int64_t n = N <= 0 ? 1 : (N < cap ? N : cap);
+  return (n + 255) / 256 * 256;
 }
 
 struct KlLayout {
   size_t idx, n_active, block_count, tmax, tsum, smax, ssum, wf, wr, xs, xt, total;
 };
 
-inline KlLayout kl_fwd_layout(int64_t N, int64_t H, int64_t V) {
+// idx[N] | n_active | block_count[blocks] | six [J][Npad] statistics | xs, xt [Npad][chunk + 32]
+inline KlLayout kl_fwd_layout(int64_t N, int64_t V) {
   KlLayout L;
   const size_t n = (size_t)(N > 0 ? N : 1);
-  const size_t jn = 4 * n * (size_t)num_partials(V);
+  const int64_t np = kl_fwd_npad(N, V);
+  const size_t jn = 4 * (size_t)np * (size_t)num_partials(V);
   size_t o = 0;
   L.idx = o;      o = align_up(o + 4 * n, 256);
   L.n_active = o; o = align_up(o + 4, 256);
-  L.block_count = o; o = align_up(o + 4 * (size_t)bwd_blocks(N, H), 256);
+  L.block_count = o; o = align_up(o + 4 * (size_t)kl_fwd_blocks(N, V), 256);
   L.tmax = o;     o = align_up(o + jn, 256);
   L.tsum = o;     o = align_up(o + jn, 256);
   L.smax = o;     o = align_up(o + jn, 256);
   L.ssum = o;     o = align_up(o + jn, 256);
   L.wf = o;       o = align_up(o + jn, 256);
   L.wr = o;       o = align_up(o + jn, 256);
-  L.xs = o;       o += kl_chunk_bytes(N, H);
-  L.xt = o;       o += kl_chunk_bytes(N, H);
+  L.xs = o;       o += kl_chunk_bytes_rows(np);
+  L.xt = o;       o += kl_chunk_bytes_rows(np);
   L.total = o;
   return L;
 }

@@ -158,6 +158,8 @@ static void test_layouts() {
       EXPECT(L.total - L.hT <= (size_t)kBwdBlockBudget + 8 * 256);
     }
   EXPECT(bwd_token_cap(4096) == 11008 && bwd_token_cap(7168) == 8960);
+  EXPECT(kl_fwd_token_cap(151936) == 3328 && kl_fwd_blocks(16384, 151936) == 5);
+  EXPECT(kl_fwd_layout(16384, 151936).total <= (size_t)kBwdBlockBudget);
   int max_blocks = 0;
   for (int64_t H = 64; H <= kMaxHidden; H += 64) {
     const int64_t n = std::min<int64_t>(kMaxTokens, kMaxHiddenStateBytes / (2 * H));
@@ -177,12 +179,17 @@ static void test_layouts() {
     expect_layout({G.idx, G.n_active}, {4 * n, 4}, G.total);
     EXPECT(loss_workspace(N) >= 32 * nb && loss_workspace(N) % 256 == 0);
     for (int64_t V : {int64_t(1), int64_t(151936), kMaxVocab}) {
-      const KlLayout K = kl_fwd_layout(N, 4096, V);
-      const size_t jn = 4 * n * (size_t)num_partials(V), c = kl_chunk_bytes(N, 4096);
+      const KlLayout K = kl_fwd_layout(N, V);
+      const int64_t np = kl_fwd_npad(N, V), cap = kl_fwd_token_cap(V);
+      const size_t jn = 4 * (size_t)np * (size_t)num_partials(V), c = kl_chunk_bytes_rows(np);
       expect_layout({K.idx, K.n_active, K.block_count, K.tmax, K.tsum, K.smax, K.ssum, K.wf,
                      K.wr, K.xs, K.xt},
-                    {4 * n, 4, 4 * (size_t)bwd_blocks(N, 4096), jn, jn, jn, jn, jn, jn, c, c},
+                    {4 * n, 4, 4 * (size_t)kl_fwd_blocks(N, V), jn, jn, jn, jn, jn, jn, c, c},
                     K.total);
+      // the KL forward's buffers hold one block of its own capacity, within the budget
+      EXPECT(cap % 256 == 0 && cap >= 256 && np <= cap && np % 256 == 0);
+      EXPECT((size_t)cap * kl_fwd_bytes_per_token(V) <= kBwdBlockBudget || cap == 256);
+      EXPECT(K.total - K.tmax <= (size_t)kBwdBlockBudget + 8 * 256 || cap == 256);
     }
   }
 }

@@ -365,16 +365,20 @@ def test_kl_argument_errors(L):
     assert fwd(T=0.0) == E.RLK_ERROR_INVALID_VALUE
     assert fwd(wsb=1000) == E.RLK_ERROR_WORKSPACE
     st, b = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 16384, 4096, 2048, 151936, 0)
-    # six [J][N] statistics plus two fp32 chunks of one token block (11008 tokens at the
-    # student's H = 4096) x (chunk entries)
+    # six [J][Npad] statistics and two fp32 chunks for one token block of the forward's own
+    # capacity (3328 tokens at V = 151936): under 1e9 bytes
     import re
     info = lib.rlk_build_info().decode()
     chunk = int(re.search(r"bwd chunk (\d+)", info).group(1))
-    assert st == 0 and b >= 6 * 4 * 16384 * 1187 + 2 * 4 * 11008 * chunk
-    assert b < 6 * 4 * 16384 * 1188 + 2 * 4 * 11008 * (chunk + 64) + (1 << 20)
-    # past one token block only the [J][N] statistics grow with N
+    assert st == 0 and b >= 6 * 4 * 3328 * 1187 + 2 * 4 * 3328 * chunk
+    assert b <= 1_000_000_000 + 4 * 16384 + 8192
+    # past one token block only the index grows with N
     st2, b2 = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 32768, 4096, 2048, 151936, 0)
-    assert st2 == 0 and b2 - b < 6 * 4 * 16384 * 1188 + 16384 * 8
+    assert st2 == 0 and b2 - b <= 4 * 16384 + 512
+    # a vocabulary of 2^22 entries leaves 256 tokens per block: 2^22 tokens would need more than
+    # 1024 blocks
+    assert _ws(lib, "rlk_linear_kl_fwd_workspace_size", (1 << 22) - 256, 256, 256, 1 << 22,
+               0)[0] == E.RLK_ERROR_UNSUPPORTED
 
     def bwd(Hs=256, dt=0, cf=FAKE, cr=None, kr=FAKE, wsb=1 << 40, dh=FAKE):
         return lib.rlk_linear_kl_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 8, Hs, 64, 1000, dt, 1.0, cf, cr,

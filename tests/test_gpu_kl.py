@@ -214,8 +214,9 @@ def test_bwd_qwen_head_sampled():
 
 
 def test_token_blocks_forward_and_backward():
-    # the KL paths take the active tokens in the backward's token blocks (at most 14848 tokens at
-    # H = 256): 18750 active tokens of 20000 (two blocks), both directions against the oracle
+    # 18750 active tokens of 20000: the KL forward's own blocks (3584 tokens at V = 2000, six
+    # blocks) and the backward's (14848 tokens at H = 256, two blocks), both directions against
+    # the oracle
     w = wl.make(wl.scaled_spec(5, N=20000, H=256, V=2000, n_seq=40, len_lo=400, len_hi=600,
                                seed=161, prompt="none", T=0.8))
     w.mask[::16] = 0
