@@ -324,8 +324,10 @@ def bench_entropy(args, w):
 def bench_ppo(args, w):
     """A PPO/GRPO-style step: the forward, the clipped policy-gradient loss with a KL penalty
     on the fresh log-prob (old and reference log-probs are seeded perturbations of it, made
-    before the timed region), and the backward driven by the loss's -dloss/dlogp; the loss
-    fragment and the dlogp diagnostics are also timed alone."""
+    before the timed region), and the backward driven by the loss's -dloss/dlogp.  The headline
+    runs it as one call (rlk_linear_ppo_fwd_bwd); the chain of three calls is timed beside it
+    (their per-token outputs must agree bit for bit), and the loss fragment and the dlogp
+    diagnostics alone."""
     import torch
     import linear_selected_token_amd as rlk
     dev = torch.device("cuda", 0)
@@ -356,16 +358,31 @@ def bench_ppo(args, w):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
+    res = {}
+
     def step():
         logp, lse = rlk.rlk_linear_logp_fwd(h, W, targets, mask, T, workspace=ws_f)
-        _, badv, _, _ = rlk.rlk_ratio_kl_loss(logp, old, ref, adv, mask, 0.2, 0.28, 0.01, scale)
+        loss, badv, _, _ = rlk.rlk_ratio_kl_loss(logp, old, ref, adv, mask, 0.2, 0.28, 0.01,
+                                                 scale)
         rlk.rlk_linear_logp_bwd(h, W, targets, mask, T, badv, lse, workspace=ws_b, dh=dh, dW=dW)
+        res["chain"] = (logp, loss, badv)
 
-    ms = timed(step)
+    chain_ms = timed(step)
+    del ws_b
+    ws_p = torch.empty(rlk.ppo_fwd_bwd_workspace_bytes(N, H, V, dt), dtype=torch.uint8, device=dev)
+
+    def fused_step():
+        out = rlk.rlk_linear_ppo_fwd_bwd(h, W, targets, mask, T, old, ref, adv, 0.2, 0.28, 0.01,
+                                         scale, workspace=ws_p, dh=dh, dW=dW)
+        res["fused"] = (out[0], out[2], out[3])
+
+    ms = timed(fused_step)
+    for a, b in zip(res["fused"], res["chain"]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), "fused and chained PPO differ"
     loss_ms = timed(lambda: rlk.rlk_ratio_kl_loss(logp0, old, ref, adv, mask, 0.2, 0.28, 0.01,
                                                   scale))
     diag_ms = timed(lambda: rlk.rlk_dlogp_diagnostics(logp0, old, mask, 0.2))
-    flop = 8.0 * Na * H * V
+    flop = 6.0 * Na * H * V
     tf = flop / (ms * 1e-3) / 1e12
     loss_bytes = N * (4 * 4 + 1 + 4 * 2) + 32 * ((N + 1023) // 1024)
     out = {
@@ -379,11 +396,17 @@ def bench_ppo(args, w):
         "config": {"workload": args.workload, "mode": "ppo", "N": N, "H": H, "V": V, "T": T,
                    "n_active": Na, "eps_lo": 0.2, "eps_hi": 0.28, "beta": 0.01,
                    "parallelism": "none (1 GPU)"},
+        "timed": "rlk_linear_ppo_fwd_bwd per step (forward, loss fragment per token block, "
+                 "gradients), on the current stream",
+        "chain_of_calls": {"ms": round(chain_ms, 4),
+                           "active_tokens_per_s": round(Na / (chain_ms * 1e-3), 1),
+                           "calls": "rlk_linear_logp_fwd, rlk_ratio_kl_loss, rlk_linear_logp_bwd"},
+        "workspace_bytes": ws_p.numel(),
         "loss_fragment": {"ms": round(loss_ms, 5), "bytes": loss_bytes,
                           "gbs": round(loss_bytes / (loss_ms * 1e-3) / 1e9, 1)},
         "diagnostics_ms": round(diag_ms, 5),
         "roofline": {"bound": "mfma", "kernel": "whole step (forward + loss fragment + "
-                     "backward)", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "backward; 6 Na H V flops)", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "algorithmic_flop_per_launch": flop,
                      "avg_launch_ms": round(ms, 4)},

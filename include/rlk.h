@@ -246,6 +246,34 @@ rlk_status_t rlk_linear_logp_fwd_bwd(const void* h, const void* W, const int32_t
                                      float* lse, float* dh, float* dW, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* rlk_linear_logp_fwd_bwd for the clipped policy-gradient loss with a KL penalty
+ * (rlk_ratio_kl_loss), whose gradient depends on the fresh logp: the loss fragment runs after
+ * each token block's merge and its -dloss/dlogp drives that block's gradient pass, so one call
+ * gives what rlk_linear_logp_fwd, rlk_ratio_kl_loss and rlk_linear_logp_bwd give in sequence
+ * (RL-Kernel integration roadmap for vime, "RL Loss Operators": ratio_kl / GRPO / PPO loss
+ * fragments fused with linear_logp).
+ *   h, W, targets, mask, N, H, V, dtype, temperature: as for rlk_linear_logp_fwd_bwd
+ *   old_logp, ref_logp, adv, eps_lo, eps_hi, beta, scale: as for rlk_ratio_kl_loss (ref_logp
+ *              may be NULL: no KL term)
+ *   logp, lse  out: the forward's bits
+ *   loss, bwd_adv, ratio, sums  out: the bits rlk_ratio_kl_loss gives for this logp (ratio and
+ *              sums may be NULL)
+ *   dh, dW     out: gradients of sum_t loss_t (dL/dlogp_t = -bwd_adv_t), as rlk_linear_logp_fwd_bwd
+ *              forms them
+ *   workspace: at least rlk_linear_ppo_fwd_bwd_workspace_size bytes, never NULL (the loss
+ *              fragment's partial sums, then the fused call's workspace; a larger one buys
+ *              larger token blocks as there). */
+rlk_status_t rlk_linear_ppo_fwd_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
+                                                   size_t* bytes);
+rlk_status_t rlk_linear_ppo_fwd_bwd(const void* h, const void* W, const int32_t* targets,
+                                    const uint8_t* mask, int64_t N, int64_t H, int64_t V,
+                                    int dtype, float temperature, const float* old_logp,
+                                    const float* ref_logp, const float* adv, float eps_lo,
+                                    float eps_hi, float beta, float scale, float* logp,
+                                    float* lse, float* loss, float* bwd_adv, float* ratio,
+                                    double* sums, float* dh, float* dW, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* Backward of the policy-gradient loss with an entropy bonus (bf16 only),
  *   L = -sum_t mask_t (adv_t logp_t + c_t H_t)
  * with H_t the entropy of softmax(z[t,:]) (RL-Kernel Roadmap (2026), "operator backlog":

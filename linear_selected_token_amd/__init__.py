@@ -24,6 +24,7 @@ from .ops import (  # noqa: E402,F401
     linear_logp_pg_loss,
     logits_workspace_bytes,
     num_vocab_partials,
+    ppo_fwd_bwd_workspace_bytes,
     rlk_compact_active,
     rlk_dlogp_diagnostics,
     rlk_linear_kl_bwd,
@@ -32,6 +33,7 @@ from .ops import (  # noqa: E402,F401
     rlk_linear_logp_bwd_entropy,
     rlk_linear_logp_fwd,
     rlk_linear_logp_fwd_bwd,
+    rlk_linear_ppo_fwd_bwd,
     rlk_linear_logp_fwd_entropy,
     rlk_linear_logp_fwd_noalloc,
     rlk_linear_logp_merge,

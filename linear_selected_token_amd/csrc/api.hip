@@ -168,15 +168,37 @@ rlk_status_t run_bwd(const void* h, const void* W, const int32_t* targets, const
 // of the block's tokens, the same bits as rlk_linear_logp_fwd), d turned into dL/dz in place,
 // then the backward's dL/dh and dL/dW GEMMs over the vocabulary chunks, reading dL/dz from the
 // block's rows.  No GEMM is run twice.
+//
+// With `loss` (rlk_linear_ppo_fwd_bwd) the upstream gradient comes from the clipped policy-
+// gradient loss on the fresh logp: after each block's merge the loss fragment runs over every
+// token (the block's tokens now have their final logp; the others are recomputed by their own
+// block) and its -dloss/dlogp takes the place of adv in the dz pass; a last run after the final
+// block gives every token's loss and ratio and the fixed-order sums.
+struct FusedLoss {
+  LossArgs args;  // logp, mask and N filled in here; part: the loss fragment's partial sums
+  double* sums;   // may be null
+};
+
 rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, const uint8_t* mask,
                        int64_t N, int64_t H, int64_t V, int dtype, float temperature,
                        const float* adv, float* logp, float* lse, float* dh, float* dW,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       FusedLoss* loss = nullptr) {
   rlk_status_t s = check_fused(h, W, targets, mask, N, H, V, dtype, temperature, adv, logp, lse,
                                dh, dW, workspace, workspace_bytes);
   if (s != RLK_SUCCESS) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (N == 0) return dev_status(launch_zero(dW, (size_t)V * (size_t)H, st));
+  if (loss) {
+    loss->args.logp = logp;
+    loss->args.mask = mask;
+    loss->args.N = (int)N;
+    adv = loss->args.bwd_adv;  // the dz pass reads -dloss/dlogp
+  }
+  if (N == 0) {
+    if (loss && launch_ratio_kl_loss(loss->args, loss->sums, st) != hipSuccess)
+      return RLK_ERROR_DEVICE;
+    return dev_status(launch_zero(dW, (size_t)V * (size_t)H, st));
+  }
   int grid = 0;
   if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
   // the budget's block capacity, or a larger one that the given workspace holds
@@ -245,6 +267,10 @@ rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, con
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
     e = launch_fwd_merge(m, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    if (loss) {
+      e = launch_ratio_kl_loss(loss->args, nullptr, st);
+      if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    }
     e = launch_dz_from_d(z, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
     e = launch_bwd_transpose(a, st);
@@ -256,6 +282,7 @@ rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, con
     e = launch_bwd_finish(a, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
   }
+  if (loss) return dev_status(launch_ratio_kl_loss(loss->args, loss->sums, st));
   return RLK_SUCCESS;
 }
 
@@ -798,6 +825,44 @@ rlk_status_t rlk_linear_logp_fwd_bwd(const void* h, const void* W, const int32_t
                                      size_t workspace_bytes, void* stream) {
   return run_fused(h, W, targets, mask, N, H, V, dtype, temperature, adv, logp, lse, dh, dW,
                    workspace, workspace_bytes, stream);
+}
+
+rlk_status_t rlk_linear_ppo_fwd_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
+                                                   size_t* bytes) {
+  if (!bytes) return RLK_ERROR_INVALID_VALUE;
+  size_t f = 0;
+  rlk_status_t s = rlk_linear_logp_fwd_bwd_workspace_size(N, H, V, dtype, &f);
+  if (s != RLK_SUCCESS) return s;
+  *bytes = loss_workspace(N) + f;
+  return RLK_SUCCESS;
+}
+
+rlk_status_t rlk_linear_ppo_fwd_bwd(const void* h, const void* W, const int32_t* targets,
+                                    const uint8_t* mask, int64_t N, int64_t H, int64_t V,
+                                    int dtype, float temperature, const float* old_logp,
+                                    const float* ref_logp, const float* adv, float eps_lo,
+                                    float eps_hi, float beta, float scale, float* logp,
+                                    float* lse, float* loss, float* bwd_adv, float* ratio,
+                                    double* sums, float* dh, float* dW, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  // the loss fragment's own checks (as rlk_ratio_kl_loss), then the fused call's
+  if (!(eps_lo >= 0.f && eps_lo < 1.f) || !(eps_hi >= 0.f && eps_hi <= 1e30f) ||
+      !(fabsf(beta) <= 1e30f) || !(fabsf(scale) <= 1e30f))
+    return RLK_ERROR_INVALID_VALUE;
+  if (N > 0 && (!old_logp || !adv || !loss || !bwd_adv)) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(old_logp, 4) || !aligned(ref_logp, 4) || !aligned(adv, 4) || !aligned(loss, 4) ||
+      !aligned(bwd_adv, 4) || !aligned(ratio, 4) || !aligned(sums, 8) || !aligned(workspace, 256))
+    return RLK_ERROR_UNSUPPORTED;
+  const size_t lw = loss_workspace(N > 0 ? N : 0);
+  if (!workspace) return RLK_ERROR_INVALID_VALUE;
+  if (workspace_bytes < lw) return RLK_ERROR_WORKSPACE;
+  FusedLoss fl;
+  fl.args = LossArgs{nullptr, old_logp, ref_logp, adv, nullptr, 0, eps_lo, eps_hi, beta, scale,
+                     loss, bwd_adv, ratio, static_cast<double*>(workspace)};
+  fl.sums = sums;
+  // adv is checked by the fused call as its upstream gradient; the loss replaces it there
+  return run_fused(h, W, targets, mask, N, H, V, dtype, temperature, adv, logp, lse, dh, dW,
+                   static_cast<uint8_t*>(workspace) + lw, workspace_bytes - lw, stream, &fl);
 }
 
 }  // extern "C"

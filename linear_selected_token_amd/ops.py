@@ -412,6 +412,50 @@ def linear_logp_entropy(h, W, targets, mask, temperature):
     return LinearLogpEntropy.apply(h, W, targets, mask, temperature)
 
 
+def ppo_fwd_bwd_workspace_bytes(N: int, H: int, V: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_linear_ppo_fwd_bwd_workspace_size(N, H, V, dtype, ctypes.byref(out)),
+            "rlk_linear_ppo_fwd_bwd_workspace_size")
+    return int(out.value)
+
+
+def rlk_linear_ppo_fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                           mask: torch.Tensor, temperature: float, old_logp: torch.Tensor,
+                           ref_logp: Optional[torch.Tensor], adv: torch.Tensor, eps_lo: float,
+                           eps_hi: float, beta: float, scale: float,
+                           workspace: Optional[torch.Tensor] = None,
+                           dh: Optional[torch.Tensor] = None, dW: Optional[torch.Tensor] = None):
+    """Forward, clipped policy-gradient loss with a KL penalty and its gradients in one call;
+    returns (logp, lse, loss, bwd_adv, ratio [N] float32, sums [4] float64, dh [N,H],
+    dW [V,H])."""
+    mask = _mask_u8(mask)
+    _check(h, W, targets, mask)
+    N, H = h.shape
+    V = W.shape[0]
+    dt = _dtype_code(h)
+    _vec("old_logp", old_logp, N)
+    _vec("adv", adv, N)
+    if ref_logp is not None:
+        _vec("ref_logp", ref_logp, N)
+    f32 = dict(dtype=torch.float32, device=h.device)
+    logp, lse, loss, badv, ratio = (torch.empty(N, **f32) for _ in range(5))
+    sums = torch.empty(4, dtype=torch.float64, device=h.device)
+    if dh is None:
+        dh = torch.empty((N, H), **f32)
+    if dW is None:
+        dW = torch.empty((V, H), **f32)
+    ws = _workspace(ppo_fwd_bwd_workspace_bytes(N, H, V, dt), h.device, workspace)
+    L.check(L.lib().rlk_linear_ppo_fwd_bwd(_vp(h), _vp(W), _vp(targets), _vp(mask), N, H, V, dt,
+                                           float(temperature), _vp(old_logp), _vp(ref_logp),
+                                           _vp(adv), float(eps_lo), float(eps_hi), float(beta),
+                                           float(scale), _vp(logp), _vp(lse), _vp(loss),
+                                           _vp(badv), _vp(ratio), _vp(sums), _vp(dh), _vp(dW),
+                                           _vp(ws), ws.numel() * ws.element_size(),
+                                           _stream(h.device)),
+            "rlk_linear_ppo_fwd_bwd")
+    return logp, lse, loss, badv, ratio, sums, dh, dW
+
+
 class LinearLogpPGLoss(torch.autograd.Function):
     """loss = -sum_t mask_t adv_t logp_t with its gradients computed in the forward
     (rlk_linear_logp_fwd_bwd); the backward scales them by the incoming scalar gradient."""

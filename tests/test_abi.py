@@ -205,6 +205,36 @@ def test_fused_workspace_and_argument_errors(L):
     assert fused(wsb=10) == E.RLK_ERROR_WORKSPACE
 
 
+def test_fused_ppo_argument_errors(L):
+    lib = L.lib()
+    E = L
+    st, a = _ws(lib, "rlk_linear_ppo_fwd_bwd_workspace_size", 16384, 4096, 151936, L.RLK_BF16)
+    st2, b = _ws(lib, "rlk_linear_logp_fwd_bwd_workspace_size", 16384, 4096, 151936, L.RLK_BF16)
+    assert st == 0 and st2 == 0 and b < a <= b + 1024
+
+    def ppo(old=FAKE, adv=FAKE, loss=FAKE, badv=FAKE, ratio=None, sums=None, eps_lo=0.2,
+            eps_hi=0.2, beta=0.0, scale=1.0, ws=FAKE, wsb=1 << 30, N=8, H=256, dt=0):
+        return lib.rlk_linear_ppo_fwd_bwd(FAKE, FAKE, FAKE, FAKE, N, H, 100, dt, 1.0, old, None,
+                                          adv, eps_lo, eps_hi, beta, scale, FAKE, FAKE, loss,
+                                          badv, ratio, sums, FAKE, FAKE, ws, wsb, None)
+
+    assert ppo(old=None) == E.RLK_ERROR_INVALID_VALUE
+    assert ppo(adv=None) == E.RLK_ERROR_INVALID_VALUE
+    assert ppo(loss=None) == E.RLK_ERROR_INVALID_VALUE
+    assert ppo(badv=None) == E.RLK_ERROR_INVALID_VALUE
+    assert ppo(ws=None) == E.RLK_ERROR_INVALID_VALUE
+    for lo in (-0.1, 1.0, float("nan")):
+        assert ppo(eps_lo=lo) == E.RLK_ERROR_INVALID_VALUE
+    assert ppo(eps_hi=-1.0) == E.RLK_ERROR_INVALID_VALUE
+    assert ppo(beta=float("inf")) == E.RLK_ERROR_INVALID_VALUE
+    assert ppo(ratio=FAKE + 2) == E.RLK_ERROR_UNSUPPORTED
+    assert ppo(sums=FAKE + 4) == E.RLK_ERROR_UNSUPPORTED
+    assert ppo(dt=1) == E.RLK_ERROR_UNSUPPORTED
+    assert ppo(H=192) == E.RLK_ERROR_UNSUPPORTED
+    assert ppo(wsb=10) == E.RLK_ERROR_WORKSPACE
+    assert ppo(wsb=1024) == E.RLK_ERROR_WORKSPACE  # the loss partials fit, the rest does not
+
+
 def test_building_block_argument_errors(L):
     lib = L.lib()
     E = L

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import oracle.rl_loss as orl
 import workloads as wl
 from gpu_util import (MAX_ABS_DLOGP, assert_rows, assert_tiles, bits, device, edge_rows, flush,
                       oracle_inputs, rel_l2, run_fwd, upload)
@@ -262,3 +263,97 @@ def test_autograd_loss():
     assert torch.equal(W.grad, (2.0 * dW).to(torch.bfloat16))
     ref = -(d["mask"].float() * d["adv"] * logp).sum()
     assert torch.equal(loss.detach(), ref)
+
+
+# ------------------------------------------------------------------ the fused PPO step
+
+def _ppo_inputs(w, d, seed):
+    """old and reference log-probs: the forward's logp plus seeded noise (tokens whose ratio
+    would sit within 1e-4 of a clip edge keep old = logp, so no decision is a rounding tie)."""
+    logp, _ = run_fwd(w, d)
+    r = np.random.default_rng(seed)
+    old = (logp + r.normal(0, 0.2, w.N)).astype(np.float32)
+    ref = (logp + r.normal(0, 0.2, w.N)).astype(np.float32)
+    ratio = np.exp(logp.astype(np.float64) - old)
+    near = (np.abs(ratio - 0.8) < 1e-4) | (np.abs(ratio - 1.2) < 1e-4)
+    old[near] = logp[near]
+    return old, ref
+
+
+def _ppo_chain(w, d, old_t, ref_t, scale):
+    """The same step through the separate calls: forward, loss fragment, backward."""
+    import linear_selected_token_amd as rlk
+    logp, lse = rlk.rlk_linear_logp_fwd(d["h"], d["W"], d["targets"], d["mask"], w.T)
+    loss, badv, ratio, sums = rlk.rlk_ratio_kl_loss(logp, old_t, ref_t, d["adv"], d["mask"], 0.2,
+                                                    0.2, 0.05, scale, want_ratio=True)
+    dh, dW = rlk.rlk_linear_logp_bwd(d["h"], d["W"], d["targets"], d["mask"], w.T, badv, lse)
+    torch.cuda.synchronize()
+    return logp, lse, loss, badv, ratio, sums, dh, dW
+
+
+def _check_ppo(w, seed, oracle_rows=None):
+    import linear_selected_token_amd as rlk
+    d = upload(w)
+    dev = d["h"].device
+    old, ref = _ppo_inputs(w, d, seed)
+    old_t, ref_t = torch.from_numpy(old).to(dev), torch.from_numpy(ref).to(dev)
+    scale = 1.0 / int(w.mask.sum())
+    chain = _ppo_chain(w, d, old_t, ref_t, scale)
+    fused = rlk.rlk_linear_ppo_fwd_bwd(d["h"], d["W"], d["targets"], d["mask"], w.T, old_t, ref_t,
+                                       d["adv"], 0.2, 0.2, 0.05, scale)
+    torch.cuda.synchronize()
+    # logp, lse, loss, -dloss/dlogp, ratio and the fixed-order sums: the chain's bits
+    for name, a, b in zip(("logp", "lse", "loss", "bwd_adv", "ratio", "sums"), fused[:6], chain[:6]):
+        ai = a.view(torch.int64) if a.dtype == torch.float64 else a.view(torch.int32)
+        bi = b.view(torch.int64) if b.dtype == torch.float64 else b.view(torch.int32)
+        assert torch.equal(ai, bi), name
+    act = np.nonzero(w.mask)[0]
+    eh = rel_l2(fused[6].cpu().numpy()[act], chain[6].cpu().numpy()[act])
+    ew = rel_l2(fused[7].cpu().numpy(), chain[7].cpu().numpy())
+    flush(f"  fused PPO vs the chain of calls: dh relL2 {eh:.3e}, dW relL2 {ew:.3e}")
+    assert eh <= 5e-3 and ew <= 5e-3
+    assert not fused[6][torch.from_numpy(w.mask == 0).to(dev)].any()
+    # against the oracle's chain rule on the oracle's own logp
+    h64, W64 = oracle_inputs(w)
+    olp, olse = oracle.linear_logp(h64, W64, w.targets, w.mask, w.T)
+    _, og, _, _, _ = orl.ratio_kl_loss(olp, old, ref, w.adv, w.mask, 0.2, 0.2, 0.05, scale)
+    dh, dW = fused[6].cpu().numpy(), fused[7].cpu().numpy()
+    if oracle_rows is None:
+        odh, odW = oracle.linear_logp_grads(h64, W64, w.targets, w.mask, w.T, -og)
+        assert_rows("fused PPO dh (every active row)", dh[act], odh[act], act)
+        assert_rows("fused PPO dW (every vocabulary row)", dW, odW)
+    else:
+        rows, vr = oracle_rows
+        odh = oracle.grad_h_rows(h64, W64, w.targets, w.mask, w.T, -og, rows)
+        assert_rows("fused PPO dh (sampled rows)", dh[rows], odh, rows)
+        odW = oracle.grad_W_rows(h64, W64, w.targets, w.mask, w.T, -og, vr, lse=olse)
+        assert_rows("fused PPO dW (sampled rows)", dW[vr], odW, vr)
+
+
+def test_ppo_fused_matches_chain_and_oracle():
+    _check_ppo(wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
+                                      seed=101, T=0.9)), 102)
+
+
+def test_ppo_fused_token_blocks():
+    # two token blocks over the Qwen3-8B vocabulary: each block's loss fragment sees its own
+    # tokens' final logp
+    w = wl.make(BLOCKS)
+    act = np.nonzero(w.mask)[0]
+    r = np.random.default_rng(171)
+    rows = np.unique(np.concatenate([act[edge_rows(act.size, 256, 1)], r.choice(act, 8, False)]))
+    vr = np.unique(np.concatenate([w.targets[act[:4]], r.integers(0, w.V, 12)]))
+    _check_ppo(w, 172, oracle_rows=(rows, vr))
+
+
+def test_ppo_fused_all_masked():
+    import linear_selected_token_amd as rlk
+    w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
+                               seed=95))
+    d = upload(w)
+    d["mask"].zero_()
+    z = torch.zeros(w.N, dtype=torch.float32, device=d["h"].device)
+    out = rlk.rlk_linear_ppo_fwd_bwd(d["h"], d["W"], d["targets"], d["mask"], 1.0, z, z, d["adv"],
+                                     0.2, 0.2, 0.05, 1.0)
+    torch.cuda.synchronize()
+    assert all(not t.any() for t in out)
