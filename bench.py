@@ -253,9 +253,12 @@ def bench_logits(args, w):
 
 def bench_entropy(args, w):
     """A training step with an entropy bonus: the forward that also returns each token's
-    entropy, then the backward of L = -sum_t mask_t (adv_t logp_t + c_t H_t) (c_t = 0.01),
-    timed whole on the caller's stream; the entropy forward alone and the plain forward are
-    timed beside it (the entropy's overhead)."""
+    entropy and the gradients of L = -sum_t mask_t (adv_t logp_t + c_t H_t) (c_t = 0.01), timed
+    whole on the caller's stream.  The headline is the fused call
+    (rlk_linear_logp_fwd_bwd_entropy); the two calls (the entropy forward, then the
+    entropy-bonus backward) are timed beside it, their logp and entropy checked bit for bit
+    against it, and so are the entropy forward alone and the plain forward (the entropy's
+    overhead)."""
     import torch
     import linear_selected_token_amd as rlk
     dev = torch.device("cuda", 0)
@@ -283,16 +286,31 @@ def bench_entropy(args, w):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
+    res = {}
+
     def step():
-        _, lse, ent = rlk.rlk_linear_logp_fwd_entropy(h, W, targets, mask, T, workspace=ws_e)
+        lp, lse, ent = rlk.rlk_linear_logp_fwd_entropy(h, W, targets, mask, T, workspace=ws_e)
         rlk.rlk_linear_logp_bwd_entropy(h, W, targets, mask, T, adv, coef, lse, ent,
                                         workspace=ws_b, dh=dh, dW=dW)
+        res["two"] = (lp, ent)
 
-    ms = timed(step)
+    two_ms = timed(step)
     fwd_ms = timed(lambda: rlk.rlk_linear_logp_fwd_entropy(h, W, targets, mask, T,
                                                            workspace=ws_e))
     plain_ms = timed(lambda: rlk.rlk_linear_logp_fwd(h, W, targets, mask, T, workspace=ws_p))
-    flop = 8.0 * Na * H * V   # forward + recompute + dL/dh + dL/dW, as executed
+    del ws_b
+    ws_f = torch.empty(rlk.fwd_bwd_entropy_workspace_bytes(N, H, V, dt), dtype=torch.uint8,
+                       device=dev)
+
+    def fused_step():
+        lp, _, ent, _, _ = rlk.rlk_linear_logp_fwd_bwd_entropy(h, W, targets, mask, T, adv, coef,
+                                                               workspace=ws_f, dh=dh, dW=dW)
+        res["fused"] = (lp, ent)
+
+    ms = timed(fused_step)
+    for a, b in zip(res["fused"], res["two"]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), "fused and two-call differ"
+    flop = 6.0 * Na * H * V   # forward, dL/dh, dL/dW, as executed by the fused call
     tf = flop / (ms * 1e-3) / 1e12
     out = {
         "metric": "active tokens/sec, fused linear logp fwd+bwd with an entropy bonus",
@@ -304,12 +322,17 @@ def bench_entropy(args, w):
                 "prompt/response sequences",
         "config": {"workload": args.workload, "mode": "entropy", "N": N, "H": H, "V": V,
                    "T": T, "n_active": Na, "ent_coef": 0.01, "parallelism": "none (1 GPU)"},
+        "timed": "rlk_linear_logp_fwd_bwd_entropy per step, on the current stream",
+        "two_calls": {"ms": round(two_ms, 4), "active_tokens_per_s": round(Na / (two_ms * 1e-3), 1),
+                      "calls": "rlk_linear_logp_fwd_entropy, rlk_linear_logp_bwd_entropy"},
+        "workspace_bytes": ws_f.numel(),
         "fwd_entropy_ms": round(fwd_ms, 4),
         "plain_fwd_ms": round(plain_ms, 4),
         "entropy_fwd_overhead_frac": round(fwd_ms / plain_ms - 1.0, 4),
         # the whole step's executed flops over its time: a lower bound of every kernel's rate
-        "roofline": {"bound": "mfma", "kernel": "whole step (entropy forward + entropy-bonus "
-                     "backward)", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": "whole step (fused entropy forward + "
+                     "entropy-bonus gradients; 6 Na H V flops)", "achieved": round(tf, 2),
+                     "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "algorithmic_flop_per_launch": flop,
                      "avg_launch_ms": round(ms, 4)},

@@ -246,6 +246,26 @@ rlk_status_t rlk_linear_logp_fwd_bwd(const void* h, const void* W, const int32_t
                                      float* lse, float* dh, float* dW, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* rlk_linear_logp_fwd_bwd with an entropy bonus: logp, lse and entropy as
+ * rlk_linear_logp_fwd_entropy returns them (the same bits), and the gradients of
+ * L = -sum_t mask_t (adv_t logp_t + c_t H_t) as rlk_linear_logp_bwd_entropy defines them, formed
+ * from the forward's stored logit codes (the entropy's statistic rides along in the forward;
+ * the dz pass adds c_t p (ln p + H_t) / T).
+ *   ent_coef [N] float  c_t;   entropy [N] float  out
+ *   the rest as for rlk_linear_logp_fwd_bwd; the workspace (and so the token blocks) holds one
+ *   more statistic per 128 vocabulary entries: rlk_linear_logp_fwd_bwd_entropy_workspace_size
+ *   bytes at least (still 2816 tokens per block at H = 4096, V = 151936). */
+rlk_status_t rlk_linear_logp_fwd_bwd_entropy_workspace_size(int64_t N, int64_t H, int64_t V,
+                                                            int dtype, size_t* bytes);
+rlk_status_t rlk_linear_logp_fwd_bwd_entropy(const void* h, const void* W,
+                                             const int32_t* targets, const uint8_t* mask,
+                                             int64_t N, int64_t H, int64_t V, int dtype,
+                                             float temperature, const float* adv,
+                                             const float* ent_coef, float* logp, float* lse,
+                                             float* entropy, float* dh, float* dW,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream);
+
 /* rlk_linear_logp_fwd_bwd for the clipped policy-gradient loss with a KL penalty
  * (rlk_ratio_kl_loss), whose gradient depends on the fresh logp: the loss fragment runs after
  * each token block's merge and its -dloss/dlogp drives that block's gradient pass, so one call

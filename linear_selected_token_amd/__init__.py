@@ -16,6 +16,7 @@ from .ops import (  # noqa: E402,F401
     bwd_workspace_bytes,
     fwd_bwd_workspace_bytes,
     fwd_bwd_workspace_bytes_for_block,
+    fwd_bwd_entropy_workspace_bytes,
     fwd_entropy_workspace_bytes,
     fwd_workspace_bytes,
     linear_kl,
@@ -33,6 +34,7 @@ from .ops import (  # noqa: E402,F401
     rlk_linear_logp_bwd_entropy,
     rlk_linear_logp_fwd,
     rlk_linear_logp_fwd_bwd,
+    rlk_linear_logp_fwd_bwd_entropy,
     rlk_linear_ppo_fwd_bwd,
     rlk_linear_logp_fwd_entropy,
     rlk_linear_logp_fwd_noalloc,

@@ -49,6 +49,10 @@ SIGNATURES = {
                                                                 ctypes.POINTER(_sz)]),
     "rlk_linear_logp_fwd_bwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p, _p,
                                        _p, _p, _p, _sz, _p]),
+    "rlk_linear_logp_fwd_bwd_entropy_workspace_size": (_int, [_i64, _i64, _i64, _int,
+                                                              ctypes.POINTER(_sz)]),
+    "rlk_linear_logp_fwd_bwd_entropy": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p,
+                                               _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "rlk_linear_ppo_fwd_bwd_workspace_size": (_int, [_i64, _i64, _i64, _int,
                                                      ctypes.POINTER(_sz)]),
     "rlk_linear_ppo_fwd_bwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _f, _p, _p, _p,

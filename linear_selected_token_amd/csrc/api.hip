@@ -179,13 +179,18 @@ struct FusedLoss {
   double* sums;   // may be null
 };
 
+// With `ent_coef` (rlk_linear_logp_fwd_bwd_entropy) the forward also keeps the entropy
+// statistic, the merge writes each token's entropy, and the dz pass adds the entropy bonus's
+// term.
 rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, const uint8_t* mask,
                        int64_t N, int64_t H, int64_t V, int dtype, float temperature,
                        const float* adv, float* logp, float* lse, float* dh, float* dW,
                        void* workspace, size_t workspace_bytes, void* stream,
-                       FusedLoss* loss = nullptr) {
+                       FusedLoss* loss = nullptr, const float* ent_coef = nullptr,
+                       float* entropy = nullptr) {
+  const bool ent = ent_coef != nullptr;
   rlk_status_t s = check_fused(h, W, targets, mask, N, H, V, dtype, temperature, adv, logp, lse,
-                               dh, dW, workspace, workspace_bytes);
+                               dh, dW, workspace, workspace_bytes, ent);
   if (s != RLK_SUCCESS) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (loss) {
@@ -202,8 +207,8 @@ rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, con
   int grid = 0;
   if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
   // the budget's block capacity, or a larger one that the given workspace holds
-  const int64_t cap64 = fused_cap_for_workspace(N, H, V, workspace_bytes);
-  const FusedLayout L = fused_layout_cap(N, H, V, cap64);
+  const int64_t cap64 = fused_cap_for_workspace(N, H, V, workspace_bytes, ent);
+  const FusedLayout L = fused_layout_cap(N, H, V, cap64, ent);
   const int np = (int)fused_npad_cap(N, cap64);
   const int cap = (int)cap64;
   const int nblk = fused_blocks_cap(N, cap64);
@@ -224,6 +229,14 @@ rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, con
   f.d_pitch = (int)fused_pitch(V);
   MergeArgs m{pm, ps, zy, bidx, bn, np, (int)V, logp, lse};  // N = np: the partials' stride
   DzArgs z{X, (int)fused_pitch(V), pm, np, bidx, bn, targets, adv, lse, (int)V, inv_t};
+  if (ent) {
+    float* pw = carve<float>(workspace, L.part_w);
+    f.part_w = pw;
+    m.part_w = pw;
+    m.entropy = entropy;
+    z.ent_coef = ent_coef;
+    z.entropy = entropy;
+  }
   BwdArgs a{};
   a.h = h;
   a.W = W;
@@ -247,8 +260,8 @@ rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, con
   for (int q = 1; q < kDhPieces; ++q) a.dhp[q] = carve<float>(workspace, L.dhp[q]);
   a.sched = carve<int>(workspace, L.sched);
 
-  // logp and lse are zeroed at every token (the merge writes the active ones)
-  CompactArgs c{mask, idx, na, nullptr, logp, lse, (int)N};
+  // logp, lse (and the entropy) are zeroed at every token (the merge writes the active ones)
+  CompactArgs c{mask, idx, na, nullptr, logp, lse, (int)N, entropy};
   c.block_desc = desc;
   c.nblk = nblk;
   c.block_cap = cap;
@@ -263,7 +276,7 @@ rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, con
     // a target outside [0, V) is never captured: its logp stays NaN, as in the forward
     e = launch_fill(zy, (size_t)np, NAN, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
-    e = launch_fwd_tiles(f, true, grid, st, kFwdStoreD);
+    e = launch_fwd_tiles(f, true, grid, st, ent ? kFwdStoreDEnt : kFwdStoreD);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
     e = launch_fwd_merge(m, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
@@ -825,6 +838,33 @@ rlk_status_t rlk_linear_logp_fwd_bwd(const void* h, const void* W, const int32_t
                                      size_t workspace_bytes, void* stream) {
   return run_fused(h, W, targets, mask, N, H, V, dtype, temperature, adv, logp, lse, dh, dW,
                    workspace, workspace_bytes, stream);
+}
+
+rlk_status_t rlk_linear_logp_fwd_bwd_entropy_workspace_size(int64_t N, int64_t H, int64_t V,
+                                                            int dtype, size_t* bytes) {
+  if (!bytes) return RLK_ERROR_INVALID_VALUE;
+  rlk_status_t s = check_shape(N, H, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  if (dtype != RLK_BF16 || H % 256 != 0 || fused_blocks(N, H, V, true) > 1024)
+    return RLK_ERROR_UNSUPPORTED;
+  *bytes = fused_layout(N, H, V, true).total;
+  return RLK_SUCCESS;
+}
+
+rlk_status_t rlk_linear_logp_fwd_bwd_entropy(const void* h, const void* W,
+                                             const int32_t* targets, const uint8_t* mask,
+                                             int64_t N, int64_t H, int64_t V, int dtype,
+                                             float temperature, const float* adv,
+                                             const float* ent_coef, float* logp, float* lse,
+                                             float* entropy, float* dh, float* dW,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (N > 0 && (!ent_coef || !entropy)) return RLK_ERROR_INVALID_VALUE;
+  if (!aligned(ent_coef, 4) || !aligned(entropy, 4)) return RLK_ERROR_UNSUPPORTED;
+  // (N == 0: only dL/dW is written; ent_coef selects the layout, so a stand-in is passed)
+  const float* ec = ent_coef ? ent_coef : reinterpret_cast<const float*>(uintptr_t(256));
+  return run_fused(h, W, targets, mask, N, H, V, dtype, temperature, adv, logp, lse, dh, dW,
+                   workspace, workspace_bytes, stream, nullptr, ec, entropy);
 }
 
 rlk_status_t rlk_linear_ppo_fwd_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,

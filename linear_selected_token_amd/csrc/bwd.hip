@@ -106,12 +106,14 @@ __global__ __launch_bounds__(256) void fill_kernel(float* p, size_t n, float val
 //   G[m][v] = (-adv_t / T) (delta(v, y_t) - 2^(-c 2^-9 + m_col - lse2))
 // is the dL/dz the dlogits epilogue forms from the recomputed logit, here from the code instead
 // (it moves log2 p by at most 2^-10: a relative error of at most 2^-10 ln 2 in p, for every
-// entry; the bf16 rounding of G that follows is up to 2^-9).  Rows of padded token columns
+// entry; the bf16 rounding of G that follows is up to 2^-9).  With an entropy bonus G gains
+// (c_t / T) p (ln p + H_t), as in the dlogits epilogue.  Rows of padded token columns
 // (Na <= m < the block's 256-token tiles) and the entries past the vocabulary become 0, so the
 // GEMMs that read X as dL/dz add nothing for them.  A work-group takes 8192 entries of one row
 // (the grid walks (row, segment) pairs): each thread converts four groups of 8 consecutive
 // entries, 2048 entries apart, in place, with all four 16-byte loads issued before any result
 // is formed.
+template <bool kEnt>
 __global__ __launch_bounds__(256) void dz_from_d_kernel(DzArgs a) {
   constexpr int kU = 4;                  // 16-byte groups per thread per segment
   constexpr int kSeg = 8 * 256 * kU;     // entries per segment (8192)
@@ -136,6 +138,8 @@ __global__ __launch_bounds__(256) void dz_from_d_kernel(DzArgs a) {
     const float gs = -a.adv[t] * a.inv_t;
     const int y = a.targets[t];
     const float lse2 = a.lse[t] * kLog2e;
+    const float bs = kEnt ? a.ent_coef[t] * a.inv_t : 0.f;
+    const float hn = kEnt ? a.entropy[t] : 0.f;
     // group k: entries v0 .. v0 + 7 (inside one 128-entry column), loaded before any is used
     u32x4 cw[kU];
     float off[kU];
@@ -155,8 +159,14 @@ __global__ __launch_bounds__(256) void dz_from_d_kernel(DzArgs a) {
       for (int e = 0; e < 8; ++e) {
         const int v = v0 + e;
         const uint32_t c = (cw[k][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf((float)c, -1.f / 512.f, off[k]));
-        G[e] = v < a.V ? gs * ((v == y ? 1.f : 0.f) - pv) : 0.f;
+        const float xl = __builtin_fmaf((float)c, -1.f / 512.f, off[k]);  // log2 p
+        const float pv = __builtin_amdgcn_exp2f(xl);
+        float g = gs * ((v == y ? 1.f : 0.f) - pv);
+        if constexpr (kEnt) {
+          // log p, clamped where p is 0 (underflow) so that 0 * log p = 0
+          g = __builtin_fmaf(bs * pv, fmaxf(xl, -126.f) * kLn2 + hn, g);
+        }
+        G[e] = v < a.V ? g : 0.f;
       }
       u32x4 out;
       out.x = pack_bf16(G[0], G[1]);
@@ -561,7 +571,10 @@ hipError_t launch_fill(float* p, size_t n, float value, hipStream_t stream) {
 }
 
 hipError_t launch_dz_from_d(const DzArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(dz_from_d_kernel, dim3(4096), dim3(256), 0, stream, a);
+  if (a.ent_coef)
+    hipLaunchKernelGGL(dz_from_d_kernel<true>, dim3(4096), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(dz_from_d_kernel<false>, dim3(4096), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

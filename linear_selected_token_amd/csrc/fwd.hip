@@ -63,9 +63,12 @@ struct FwdCtx {
 //                token of the launch (padded token columns included).  The fused forward +
 //                backward turns these rows into dL/dz once lse is known, in place of a second
 //                pass of the GEMM.
+//   kFwdStoreDEnt kFwdStoreD plus the entropy statistic of kFwdEntropy (the fused call with an
+//                entropy bonus).
 template <bool kBF16, int kMode>
 __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
-  constexpr bool kEnt = kMode == kFwdEntropy;
+  constexpr bool kEnt = kMode == kFwdEntropy || kMode == kFwdStoreDEnt;
+  constexpr bool kStoreD = kMode == kFwdStoreD || kMode == kFwdStoreDEnt;
   constexpr bool kNoTarget = kMode == kFwdStoreX;
   __shared__ RingSmem sm;
   const int Na = *a.n_active;
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
             }
         }
       }
-      if constexpr (kMode == kFwdStoreD) {
+      if constexpr (kStoreD) {
         // codes of the wave's 128 entries for this token column, 16 bytes per lane: per 32-entry
         // block, v_permlane32_swap on the packed groups (2h, 2h + 1) hands lane l entries
         // 16 h + 0..7 and lane l + 32 entries 16 h + 8..15 of the same token (as for dL/dz).
@@ -361,6 +364,11 @@ hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream
     case kFwdStoreD:
       if (!bf16) return hipErrorInvalidValue;
       hipLaunchKernelGGL((fwd_tiles_kernel<true, kFwdStoreD>), dim3(grid), dim3(kThreads), 0,
+                         stream, a);
+      break;
+    case kFwdStoreDEnt:
+      if (!bf16) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((fwd_tiles_kernel<true, kFwdStoreDEnt>), dim3(grid), dim3(kThreads), 0,
                          stream, a);
       break;
     default: return hipErrorInvalidValue;

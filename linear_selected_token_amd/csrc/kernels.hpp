@@ -67,7 +67,7 @@ struct FwdTileArgs {
   int d_pitch = 0;          // entries per dbuf row
 };
 
-enum FwdMode { kFwdPlain = 0, kFwdEntropy = 1, kFwdStoreX = 2, kFwdStoreD = 3 };
+enum FwdMode { kFwdPlain = 0, kFwdEntropy = 1, kFwdStoreX = 2, kFwdStoreD = 3, kFwdStoreDEnt = 4 };
 
 struct MergeArgs {
   const float* part_max;
@@ -137,6 +137,9 @@ struct DzArgs {
   const float* lse;        // [N] natural-log lse, written by the merge
   int V;
   float inv_t;
+  // entropy bonus (both null without it): dL/dz gains c_t p (ln p + H_t)
+  const float* ent_coef = nullptr;  // [N] c_t
+  const float* entropy = nullptr;   // [N] H_t, written by the merge
 };
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);

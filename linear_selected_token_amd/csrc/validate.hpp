@@ -174,14 +174,16 @@ inline BwdLayout bwd_layout(int64_t N, int64_t H) {
 // for H = 4096, V = 151936.
 inline int64_t fused_pitch(int64_t V) { return (V + 255) / 256 * 256 + 64; }
 
-inline size_t fused_bytes_per_token(int64_t H, int64_t V) {
-  return 2 * (size_t)fused_pitch(V) + 8 * (size_t)num_partials(V) + 4 +
+// ent: with an entropy bonus, a third statistic per column (4 bytes per 128 entries more).
+inline size_t fused_bytes_per_token(int64_t H, int64_t V, bool ent = false) {
+  return 2 * (size_t)fused_pitch(V) + (ent ? 12 : 8) * (size_t)num_partials(V) + 4 +
          4 * (kBwdDhPieces - 1) * (size_t)H + 2 * (size_t)H + 8;
 }
 
-inline int64_t fused_token_cap(int64_t H, int64_t V) {
-  const int64_t c = (int64_t)(kBwdBlockBudget / fused_bytes_per_token(H > 0 ? H : 1, V > 0 ? V : 1)) /
-                    256 * 256;
+inline int64_t fused_token_cap(int64_t H, int64_t V, bool ent = false) {
+  const int64_t c =
+      (int64_t)(kBwdBlockBudget / fused_bytes_per_token(H > 0 ? H : 1, V > 0 ? V : 1, ent)) /
+      256 * 256;
   return c < 256 ? 256 : (c > kMaxTokens ? kMaxTokens : c);
 }
 
@@ -195,24 +197,26 @@ inline int64_t fused_npad_cap(int64_t N, int64_t cap) {
   return (n + 255) / 256 * 256;
 }
 
-inline int fused_blocks(int64_t N, int64_t H, int64_t V) {
-  return fused_blocks_cap(N, fused_token_cap(H, V));
+inline int fused_blocks(int64_t N, int64_t H, int64_t V, bool ent = false) {
+  return fused_blocks_cap(N, fused_token_cap(H, V, ent));
 }
 
-inline int64_t fused_npad(int64_t N, int64_t H, int64_t V) {
-  return fused_npad_cap(N, fused_token_cap(H, V));
+inline int64_t fused_npad(int64_t N, int64_t H, int64_t V, bool ent = false) {
+  return fused_npad_cap(N, fused_token_cap(H, V, ent));
 }
 
 // Workspace layout of the fused forward + backward: idx[N] | n_active | block_desc[blocks][2] |
 // bidx[Npad] | bn | sched[8] | target_logit[Npad] | part_max[J][Npad] | part_sum[J][Npad] |
 // hT[H, Npad] | X[Npad, pitch] (d codes, then bf16 dL/dz) | dhp[1 ..][Npad, H] (fp32).
 struct FusedLayout {
-  size_t idx, n_active, block_desc, bidx, bn, sched, target_logit, part_max, part_sum, hT, X,
-      dhp[kBwdDhPieces], total;
+  size_t idx, n_active, block_desc, bidx, bn, sched, target_logit, part_max, part_sum, part_w,
+      hT, X, dhp[kBwdDhPieces], total;
 };
 
-// The layout for blocks of at most cap tokens (fused_layout: the budget's capacity).
-inline FusedLayout fused_layout_cap(int64_t N, int64_t H, int64_t V, int64_t cap) {
+// The layout for blocks of at most cap tokens (fused_layout: the budget's capacity); ent adds
+// the entropy statistic part_w[J][Npad] (else its size is 0).
+inline FusedLayout fused_layout_cap(int64_t N, int64_t H, int64_t V, int64_t cap,
+                                    bool ent = false) {
   FusedLayout L;
   const size_t n = (size_t)(N > 0 ? N : 1);
   const size_t np = (size_t)fused_npad_cap(N, cap);
@@ -227,6 +231,7 @@ inline FusedLayout fused_layout_cap(int64_t N, int64_t H, int64_t V, int64_t cap
   L.target_logit = o; o = align_up(o + 4 * np, 256);
   L.part_max = o;     o = align_up(o + jn, 256);
   L.part_sum = o;     o = align_up(o + jn, 256);
+  L.part_w = o;       if (ent) o = align_up(o + jn, 256);
   L.hT = o;           o = align_up(o + 2 * (size_t)H * np, 256);
   L.X = o;            o = align_up(o + 2 * np * (size_t)fused_pitch(V), 256);
   L.dhp[0] = 0;       // piece 0 accumulates in dh's rows
@@ -238,21 +243,22 @@ inline FusedLayout fused_layout_cap(int64_t N, int64_t H, int64_t V, int64_t cap
   return L;
 }
 
-inline FusedLayout fused_layout(int64_t N, int64_t H, int64_t V) {
-  return fused_layout_cap(N, H, V, fused_token_cap(H, V));
+inline FusedLayout fused_layout(int64_t N, int64_t H, int64_t V, bool ent = false) {
+  return fused_layout_cap(N, H, V, fused_token_cap(H, V, ent), ent);
 }
 
 // The block capacity a workspace of ws_bytes allows: the budget's capacity, or the largest
 // multiple of 256 tokens past it whose layout still fits ws_bytes (at most N rounded up to 256:
 // one block).  A larger workspace only buys fewer, larger blocks.
-inline int64_t fused_cap_for_workspace(int64_t N, int64_t H, int64_t V, size_t ws_bytes) {
-  const int64_t c0 = fused_token_cap(H, V);
+inline int64_t fused_cap_for_workspace(int64_t N, int64_t H, int64_t V, size_t ws_bytes,
+                                       bool ent = false) {
+  const int64_t c0 = fused_token_cap(H, V, ent);
   const int64_t top = ((N > 0 ? N : 1) + 255) / 256 * 256;
-  if (top <= c0 || fused_layout_cap(N, H, V, c0 + 256).total > ws_bytes) return c0;
+  if (top <= c0 || fused_layout_cap(N, H, V, c0 + 256, ent).total > ws_bytes) return c0;
   int64_t lo = c0 + 256, hi = top;  // lo fits; find the largest fitting multiple of 256
   while (lo < hi) {
     const int64_t mid = (lo / 256 + (hi / 256 - lo / 256 + 1) / 2) * 256;
-    if (fused_layout_cap(N, H, V, mid).total <= ws_bytes) lo = mid;
+    if (fused_layout_cap(N, H, V, mid, ent).total <= ws_bytes) lo = mid;
     else hi = mid - 256;
   }
   return lo;
@@ -336,13 +342,13 @@ inline rlk_status_t check_fused(const void* h, const void* W, const int32_t* tar
                                 const uint8_t* mask, int64_t N, int64_t H, int64_t V, int dtype,
                                 float T, const float* adv, const float* logp, const float* lse,
                                 const float* dh, const float* dW, const void* ws,
-                                size_t ws_bytes) {
+                                size_t ws_bytes, bool ent = false) {
   rlk_status_t s = check_shape(N, H, V, dtype);
   if (s != RLK_SUCCESS) return s;
   s = check_temperature(T);
   if (s != RLK_SUCCESS) return s;
   if (dtype != RLK_BF16 || H % 256 != 0) return RLK_ERROR_UNSUPPORTED;
-  if (fused_blocks(N, H, V) > 1024) return RLK_ERROR_UNSUPPORTED;  // the compaction's bound
+  if (fused_blocks(N, H, V, ent) > 1024) return RLK_ERROR_UNSUPPORTED;  // the compaction's bound
   if (!dW) return RLK_ERROR_INVALID_VALUE;
   if (N == 0) return RLK_SUCCESS;
   if (!h || !W || !targets || !mask || !adv || !logp || !lse || !dh || !ws)
@@ -351,7 +357,7 @@ inline rlk_status_t check_fused(const void* h, const void* W, const int32_t* tar
       !aligned(logp, 4) || !aligned(lse, 4) || !aligned(dh, 16) || !aligned(dW, 4) ||
       !aligned(ws, 256))
     return RLK_ERROR_UNSUPPORTED;
-  if (ws_bytes < fused_layout(N, H, V).total) return RLK_ERROR_WORKSPACE;
+  if (ws_bytes < fused_layout(N, H, V, ent).total) return RLK_ERROR_WORKSPACE;
   return RLK_SUCCESS;
 }
 

@@ -412,6 +412,46 @@ def linear_logp_entropy(h, W, targets, mask, temperature):
     return LinearLogpEntropy.apply(h, W, targets, mask, temperature)
 
 
+def fwd_bwd_entropy_workspace_bytes(N: int, H: int, V: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().rlk_linear_logp_fwd_bwd_entropy_workspace_size(N, H, V, dtype,
+                                                                   ctypes.byref(out)),
+            "rlk_linear_logp_fwd_bwd_entropy_workspace_size")
+    return int(out.value)
+
+
+def rlk_linear_logp_fwd_bwd_entropy(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                                    mask: torch.Tensor, temperature: float, adv: torch.Tensor,
+                                    ent_coef: torch.Tensor,
+                                    workspace: Optional[torch.Tensor] = None,
+                                    dh: Optional[torch.Tensor] = None,
+                                    dW: Optional[torch.Tensor] = None):
+    """Forward with the entropy and gradients of L = -sum mask (adv logp + c H) in one call;
+    returns (logp, lse, entropy [N], dh [N,H], dW [V,H]), all float32."""
+    mask = _mask_u8(mask)
+    _check(h, W, targets, mask)
+    N, H = h.shape
+    V = W.shape[0]
+    dt = _dtype_code(h)
+    _vec("adv", adv, N)
+    _vec("ent_coef", ent_coef, N)
+    f32 = dict(dtype=torch.float32, device=h.device)
+    logp, lse, ent = (torch.empty(N, **f32) for _ in range(3))
+    if dh is None:
+        dh = torch.empty((N, H), **f32)
+    if dW is None:
+        dW = torch.empty((V, H), **f32)
+    ws = _workspace(fwd_bwd_entropy_workspace_bytes(N, H, V, dt), h.device, workspace)
+    L.check(L.lib().rlk_linear_logp_fwd_bwd_entropy(_vp(h), _vp(W), _vp(targets), _vp(mask), N, H,
+                                                    V, dt, float(temperature), _vp(adv),
+                                                    _vp(ent_coef), _vp(logp), _vp(lse), _vp(ent),
+                                                    _vp(dh), _vp(dW), _vp(ws),
+                                                    ws.numel() * ws.element_size(),
+                                                    _stream(h.device)),
+            "rlk_linear_logp_fwd_bwd_entropy")
+    return logp, lse, ent, dh, dW
+
+
 def ppo_fwd_bwd_workspace_bytes(N: int, H: int, V: int, dtype: int) -> int:
     out = ctypes.c_size_t(0)
     L.check(L.lib().rlk_linear_ppo_fwd_bwd_workspace_size(N, H, V, dtype, ctypes.byref(out)),

@@ -357,3 +357,63 @@ def test_ppo_fused_all_masked():
                                      0.2, 0.2, 0.05, 1.0)
     torch.cuda.synchronize()
     assert all(not t.any() for t in out)
+
+
+# ------------------------------------------------------------------ the fused entropy bonus
+
+def _check_entropy(w, seed, oracle_rows=None):
+    import linear_selected_token_amd as rlk
+    d = upload(w)
+    dev = d["h"].device
+    c = np.random.default_rng(seed).uniform(0.0, 0.5, w.N).astype(np.float32)
+    ct = torch.from_numpy(c).to(dev)
+    lp1, ls1, en1 = rlk.rlk_linear_logp_fwd_entropy(d["h"], d["W"], d["targets"], d["mask"], w.T)
+    dh1, dW1 = rlk.rlk_linear_logp_bwd_entropy(d["h"], d["W"], d["targets"], d["mask"], w.T,
+                                               d["adv"], ct, ls1, en1)
+    lp2, ls2, en2, dh2, dW2 = rlk.rlk_linear_logp_fwd_bwd_entropy(d["h"], d["W"], d["targets"],
+                                                                  d["mask"], w.T, d["adv"], ct)
+    torch.cuda.synchronize()
+    for name, a, b in (("logp", lp2, lp1), ("lse", ls2, ls1), ("entropy", en2, en1)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
+    act = np.nonzero(w.mask)[0]
+    eh = rel_l2(dh2.cpu().numpy()[act], dh1.cpu().numpy()[act])
+    ew = rel_l2(dW2.cpu().numpy(), dW1.cpu().numpy())
+    flush(f"  fused entropy bonus vs the two calls: dh relL2 {eh:.3e}, dW relL2 {ew:.3e}")
+    assert eh <= 5e-3 and ew <= 5e-3
+    h64, W64 = oracle_inputs(w)
+    dh, dW = dh2.cpu().numpy(), dW2.cpu().numpy()
+    if oracle_rows is None:
+        odh, odW = oracle.linear_logp_entropy_grads(h64, W64, w.targets, w.mask, w.T, w.adv, c)
+        assert_rows("fused entropy dh (every active row)", dh[act], odh[act], act)
+        assert_rows("fused entropy dW (every vocabulary row)", dW, odW)
+    else:
+        rows, vr = oracle_rows
+        odh = oracle.grad_h_rows(h64, W64, w.targets, w.mask, w.T, w.adv, rows, ent_coef=c)
+        assert_rows("fused entropy dh (sampled rows)", dh[rows], odh, rows)
+        _, olse = oracle.linear_logp(h64, W64, w.targets, w.mask, w.T)
+        odW = oracle.grad_W_rows(h64, W64, w.targets, w.mask, w.T, w.adv, vr, lse=olse,
+                                 ent_coef=c)
+        assert_rows("fused entropy dW (sampled rows)", dW[vr], odW, vr)
+
+
+def test_entropy_bonus_fused():
+    _check_entropy(wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64,
+                                          len_hi=300, seed=103, T=0.8)), 104)
+
+
+def test_entropy_bonus_fused_peaked():
+    # h x 8: peaked softmaxes, where p ln p of the tail entries is tiny but their codes are far
+    # from 0
+    w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
+                               seed=105, T=0.8))
+    w.h = wl.bf16_bits(wl.bf16_to_f32(w.h) * np.float32(8.0))
+    _check_entropy(w, 106)
+
+
+def test_entropy_bonus_fused_token_blocks():
+    w = wl.make(BLOCKS)
+    act = np.nonzero(w.mask)[0]
+    r = np.random.default_rng(173)
+    rows = np.unique(np.concatenate([act[edge_rows(act.size, 256, 1)], r.choice(act, 6, False)]))
+    vr = np.unique(np.concatenate([w.targets[act[:4]], r.integers(0, w.V, 10)]))
+    _check_entropy(w, 174, oracle_rows=(rows, vr))
