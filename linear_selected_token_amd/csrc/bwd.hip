@@ -16,11 +16,10 @@
 // The vocabulary is walked in chunks of kBwdChunk entries, in ascending order.  Per chunk:
 //   dlogits      the forward tile GEMM again, epilogue G = (g_t / T)(delta - p) rounded to
 //                bf16 and stored token-major (Gv);
-//   dh_chunk     (Gv W[chunk])^T = W[chunk]^T Gv^T in K pieces of kDhSplitK entries
-//                (fp32 accumulation; two per full chunk): W is the first operand, read as
-//                a K-strided panel on the three-stage ring (rows past V as zeros), so the
-//                operand that streams from memory is the one loaded two stages ahead; a tile
-//                is 256 hidden columns x 256 tokens.  Piece q is added to dhp[q] (compacted
+//   dh_chunk     Gv W[chunk] in K pieces of kDhSplitK entries (fp32 accumulation; two per
+//                full chunk): Gv is the first operand, W the second, read as a K-strided
+//                panel (rows past V as zeros); a tile is 256 tokens x 256 hidden
+//                columns.  Piece q is added to dhp[q] (compacted
 //                rows), in chunk order; the pieces are independent tiles, so a chunk fills the
 //                machine even when few tokens are active;
 //   dw_chunk     dW[chunk rows]^T = hT Gv  (K = the active tokens in ascending order; hT is
@@ -324,6 +323,43 @@ struct RowColCtx {
   int piece;         // dh_chunk: which K piece of the chunk (into dhp[piece])
 };
 
+// Exchange of a value with the lane one (dpp_xor1) or two (dpp_xor2) positions away in the
+// same group of four lanes (DPP quad permutations [1, 0, 3, 2] and [2, 3, 0, 1]).
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+}
+
+// 4 x 4 transpose within each group of four lanes: if lane c of the group holds element e of
+// v = M[e][c], it returns M[c][0 .. 3].  Two exchanges: the first swaps the roles of lane
+// bit 0 and element bit 0, the second those of lane bit 1 and element bit 1; each lane sends
+// the elements it replaces.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 v, int lane) {
+  const bool c0 = (lane & 1) != 0;
+  const bool c1 = (lane & 2) != 0;
+  float s0 = c0 ? v.x : v.y;
+  float s1 = c0 ? v.z : v.w;
+  s0 = dpp_xor1(s0);
+  s1 = dpp_xor1(s1);
+  v.x = c0 ? s0 : v.x;
+  v.y = c0 ? v.y : s0;
+  v.z = c0 ? s1 : v.z;
+  v.w = c0 ? v.w : s1;
+  float t0 = c1 ? v.x : v.z;
+  float t1 = c1 ? v.y : v.w;
+  t0 = dpp_xor2(t0);
+  t1 = dpp_xor2(t1);
+  v.x = c1 ? t0 : v.x;
+  v.y = c1 ? t1 : v.y;
+  v.z = c1 ? v.z : t0;
+  v.w = c1 ? v.w : t1;
+  return v;
+}
+
 // kFirst: the first chunk, whose tiles store their sums (later chunks add to them).
 // kSpread: a last, partial round of tiles is dealt out across the XCDs (for the combined
 // launch, whose work-groups go on to claim dL/dW tiles from their XCD's counter).
@@ -336,7 +372,7 @@ __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nHTiles = a.H / kTile;
   const int per_piece = nTokTiles * nHTiles;
-  const int band = nTokTiles < 8 ? nTokTiles : 8;
+  const int band = nHTiles < 8 ? nHTiles : 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const size_t g_row = (size_t)a.gv_pitch * 2;  // bytes per Gv row (one token)
@@ -345,38 +381,42 @@ __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
   const int wa = wave_a0(wave);
   const int wb = wave_b0(wave);
 
-  // A = W[c0 + k0 ..][hidden columns abase ..] (K-strided), B = Gv rows of tokens bbase ..
+  // A = Gv rows of tokens abase .. (K = the piece's vocabulary entries, contiguous), B =
+  // W[c0 + k0 ..][hidden columns bbase ..] read K-strided (a transposing panel, rows past V as
+  // zeros).  W is the operand with the transposing reads, so each wave reads it for its 64
+  // hidden columns (two 32-column blocks) rather than 128.
   auto setup = [&](int u, TileSrc& src, RowColCtx& c) {
     const int piece = u / per_piece;
-    int ht, tt;
-    tile_coords(u - piece * per_piece, nHTiles, nTokTiles, band, ht, tt);
-    c.abase = ht * kTile;
-    c.bbase = tt * kTile;
+    int tt, ht;
+    tile_coords(u - piece * per_piece, nTokTiles, nHTiles, band, tt, ht);
+    c.abase = tt * kTile;
+    c.bbase = ht * kTile;
     c.piece = piece;
     const int k0 = piece * kDhSplitK;  // K entries [k0, k1) of this piece
     const int k1 = min(kc, k0 + kDhSplitK);
     src.nk = (k1 - k0) * 2 / kKBytes;
-    src.a_kstep = 64 * w_pitch;  // 64 W rows per stage
-    src.b_kstep = kKBytes;
-    // W rows c0 + k0 ... of this tile's 256 columns; rows past V read as zeros
+    src.a_kstep = kKBytes;
+    src.b_kstep = 64 * w_pitch;  // 64 W rows per stage
     const size_t v0 = (size_t)c0 + k0;
-    src.a = uniform_ptr(static_cast<const uint8_t*>(a.W) + v0 * w_pitch + 2 * (size_t)c.abase);
-    src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)c.bbase * g_row +
+    src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(a.Gv) + (size_t)c.abase * g_row +
                         2 * (gcol + k0));
-    src.a_bytes = operand_bytes(((size_t)a.V - v0) * w_pitch - 2 * (size_t)c.abase);
-    src.b_bytes = operand_bytes((size_t)(a.Npad - c.bbase) * g_row - 2 * (gcol + k0));
+    src.b = uniform_ptr(static_cast<const uint8_t*>(a.W) + v0 * w_pitch + 2 * (size_t)c.bbase);
+    src.a_bytes = operand_bytes((size_t)(a.Npad - c.abase) * g_row - 2 * (gcol + k0));
+    src.b_bytes = operand_bytes(((size_t)a.V - v0) * w_pitch - 2 * (size_t)c.bbase);
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q) {
-      src.ao[q] = (uint32_t)(tdma_row(q, wave, lane) * w_pitch) + 16 * tdma_chunk(q, wave, lane);
-      src.bo[q] = (uint32_t)(dma_row(q, wave, lane) * g_row) + 16 * dma_chunk(q, wave, lane);
+      src.ao[q] = (uint32_t)(dma_row(q, wave, lane) * g_row) + 16 * dma_chunk(q, wave, lane);
+      src.bo[q] = (uint32_t)(tdma_row(q, wave, lane) * w_pitch) + 16 * tdma_chunk(q, wave, lane);
     }
   };
 
-  // Accumulator rows are hidden columns, columns are tokens: a lane holds 4 consecutive
-  // hidden columns per register group, added into its token's row 16 bytes at a time.  Piece
-  // 0 accumulates in dh's own row of the token (idx[m]); every later piece in the token's
-  // compacted row of dhp[piece].  Every row starts 16-byte aligned: dh and the 256-byte aligned dhp
-  // buffers are 16-byte aligned and H % 256 == 0.
+  // Accumulator rows are tokens, columns hidden entries.  Register group g of block (i, j)
+  // holds four consecutive token rows of the lane's hidden column; a transpose within each
+  // group of four lanes gives lane e of the group token row e of that group and the group's
+  // four consecutive hidden columns, added into the token's row 16 bytes at a time.  Piece 0
+  // accumulates in dh's own row of the token (idx[m]); every later piece in the token's
+  // compacted row of dhp[piece].  Every row starts 16-byte aligned: dh and the 256-byte
+  // aligned dhp buffers are 16-byte aligned and H % 256 == 0.
   //
   // The piece's buffer is chosen once per tile, in wave-uniform code before the per-lane
   // branch: chosen inside it (a nested select under a divergent mask, with four pieces), this
@@ -387,29 +427,40 @@ __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
 #pragma unroll
     for (int q = 1; q < kDhPieces; ++q) base = c.piece == q ? a.dhp[q] : base;
     const bool in_dh = c.piece == 0;
+    const int col = c.bbase + wb + 4 * ((lane & 31) >> 2);
 #pragma unroll
-    for (int j = 0; j < kBlkB; ++j) {
-      const int m = c.bbase + wb + acc_col(j, lane);
-      if (m < Na) {
-        const size_t r = in_dh ? (size_t)a.idx[m] : (size_t)m;
-        float* row = base + r * a.H + c.abase + wa;
+    for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
-        for (int i = 0; i < kBlkA; ++i)
+      for (int g = 0; g < 4; ++g) {
+        f32x4 t[kBlkB];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4* p = reinterpret_cast<f32x4*>(row + acc_row(i, 4 * g, lane));
+        for (int j = 0; j < kBlkB; ++j) {
+          f32x4 v;
+          v.x = acc.c[i][j][4 * g + 0];
+          v.y = acc.c[i][j][4 * g + 1];
+          v.z = acc.c[i][j][4 * g + 2];
+          v.w = acc.c[i][j][4 * g + 3];
+          t[j] = quad_transpose(v, lane);
+        }
+        const int m = c.abase + wa + acc_row(i, 4 * g + (lane & 3), lane);
+        if (m < Na) {
+          const size_t r = in_dh ? (size_t)a.idx[m] : (size_t)m;
+          float* row = base + r * a.H + col;
+#pragma unroll
+          for (int j = 0; j < kBlkB; ++j) {
+            f32x4* p = reinterpret_cast<f32x4*>(row + 32 * j);
             f32x4 v = kFirst ? f32x4{0.f, 0.f, 0.f, 0.f} : *p;
-            v.x += acc.c[i][j][4 * g + 0];
-            v.y += acc.c[i][j][4 * g + 1];
-            v.z += acc.c[i][j][4 * g + 2];
-            v.w += acc.c[i][j][4 * g + 3];
+            v.x += t[j].x;
+            v.y += t[j].y;
+            v.z += t[j].z;
+            v.w += t[j].w;
             *p = v;
           }
+        }
       }
-    }
   };
 
-  persistent_tiles<true, RowColCtx, true, false, kSpread>(sm, per_piece * npiece, setup, epilogue);
+  persistent_tiles<true, RowColCtx, false, true, kSpread>(sm, per_piece * npiece, setup, epilogue);
 }
 
 // dh[idx[m]] = (dh[idx[m]] + dhp[1][m]) + ... + dhp[kP-1][m] over the kP pieces the first
