@@ -498,8 +498,9 @@ def bench_kl(args, w):
                    "T": T, "n_active": Na, "parallelism": "none (1 GPU)"},
         "fwd_ms": round(fwd_ms, 4),
         "fwd_tflops": round(4.0 * Na * H * V / (fwd_ms * 1e-3) / 1e12, 2),
-        "roofline": {"bound": "mfma", "kernel": "whole step (both heads' tile GEMMs per chunk, "
-                     "cross/grad streams, dL/dh, dL/dW)", "achieved": round(tf, 2),
+        "workspace_bytes": {"fwd": int(ws_f.numel()), "bwd": int(ws_b.numel())},
+        "roofline": {"bound": "mfma", "kernel": "whole step (the two-head tile kernel over the "
+                     "vocabulary, again per chunk for dL/dz, dL/dh, dL/dW)", "achieved": round(tf, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "algorithmic_flop_per_launch": flop, "avg_launch_ms": round(ms, 4)},

@@ -321,23 +321,29 @@ rlk_status_t rlk_linear_logp_bwd_entropy(const void* h, const void* W, const int
  *   h_t [N,H_t], W_t [V,H_t]   teacher (the same dtype, vocabulary and temperature)
  *   z_s = h_s W_s^T / T, z_t = h_t W_t^T / T, p = softmax(z)
  *   kl_fwd[t] = sum_v p_t (log p_t - log p_s),  kl_rev[t] = sum_v p_s (log p_s - log p_t)
- * at active tokens, 0 elsewhere (both clamped at 0 against rounding).  The active tokens are
- * taken in blocks (compacted order) of at most the largest multiple of 256 tokens whose rows
- * fit 1e9 bytes (8 (32768 + 32) + 24 ceil(V/128) bytes per token: 3328 tokens at V = 151936).
- * Per block the vocabulary is walked in chunks of 32768 entries: per chunk each head's tile
- * GEMM writes its column statistics and its logits of that chunk only (fp32, the block's rows x
- * 32768 entries, in the workspace), a streaming kernel pairs the two entry by entry, and after
- * the block's last chunk a fixed-order merge gives its tokens' results.
- * Batch-invariant like logp.  H_s and H_t: multiples of 64; each h at most 2^31 - 1 bytes.
- * RLK_ERROR_UNSUPPORTED when N would need more than 1024 blocks.
+ * at active tokens, 0 elsewhere (both clamped at 0 against rounding).  One tile kernel forms
+ * both heads' logits for each 256 x 256 (vocabulary x token) tile, the teacher's first (its
+ * fp32 tile waits in a per-work-group scratch slot, never as logits in memory), and pairs them
+ * in the student's epilogue into per-column statistics: each head's maximum and sum and the two
+ * cross terms; a fixed-order merge per token gives the results.  The active tokens are taken
+ * in blocks (compacted order) of the largest multiple of 256 tokens whose statistics fit the
+ * workspace given (at most 1024 blocks).  Batch-invariant like logp.  H_s and H_t: multiples
+ * of 64; each h at most 2^31 - 1 bytes.
  *   lse_s, lse_t [N] float     out (may be NULL): each head's log-sum-exp, which the backward
  *                              takes back
- *   workspace: rlk_linear_kl_fwd_workspace_size bytes: six float arrays of ceil(V/128) x one
- *              block's rows (both heads' column statistics and the two cross terms) and two
- *              chunk buffers of 32800 floats per row (0.97 GB at N = 16384, V = 151936; past
- *              one block only the 4-byte index per token grows). */
+ *   workspace: rlk_linear_kl_fwd_workspace_size bytes (blocks of the largest multiple of 256
+ *              tokens whose six float statistics of ceil(V/128) per token fit 1e9 bytes beside
+ *              the 64 MiB scratch: 32512 tokens at V = 151936, so 0.53 GB at N = 16384; past one
+ *              block only the 4-byte index per token grows), or
+ *              rlk_linear_kl_fwd_workspace_size_for_block bytes for blocks of block_tokens (a
+ *              positive multiple of 256): a smaller workspace trades memory for more launches.
+ *              RLK_ERROR_WORKSPACE when not even 256-token blocks (within 1024 blocks) fit;
+ *              the size queries return RLK_ERROR_UNSUPPORTED past 1024 blocks. */
 rlk_status_t rlk_linear_kl_fwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
                                               int dtype, size_t* bytes);
+rlk_status_t rlk_linear_kl_fwd_workspace_size_for_block(int64_t N, int64_t H_s, int64_t H_t,
+                                                        int64_t V, int dtype,
+                                                        int64_t block_tokens, size_t* bytes);
 rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t,
                                const void* W_t, const uint8_t* mask, int64_t N, int64_t H_s,
                                int64_t H_t, int64_t V, int dtype, float temperature,
@@ -345,16 +351,18 @@ rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward of L = sum_t mask_t (coef_fwd_t kl_fwd[t] + coef_rev_t kl_rev[t]) into the student
- * (bf16, H_s a multiple of 256); the teacher is frozen.  Per chunk both heads' logits are
- * recomputed on MFMA, dL/dz_s = (coef_fwd (p_s - p_t) + coef_rev p_s (log p_s - log p_t -
- * kl_rev)) / T is formed in a streaming kernel and rounded to bf16, and the chunk's dL/dh_s and
- * dL/dW_s follow as in rlk_linear_logp_bwd.
+ * (bf16, H_s a multiple of 256); the teacher is frozen.  Per vocabulary chunk of 32768 entries,
+ * the forward's tile kernel forms both heads' logits again and its epilogue writes
+ * dL/dz_s = (coef_fwd (p_s - p_t) + coef_rev p_s (log p_s - log p_t - kl_rev)) / T, rounded to
+ * bf16; the chunk's dL/dh_s and dL/dW_s follow as in rlk_linear_logp_bwd, over token blocks of
+ * the largest multiple of 256 tokens whose buffers fit 1e9 bytes beside the scratch (10240 at
+ * H_s = 4096).
  *   coef_fwd, coef_rev [N] float   dL/dkl_fwd and dL/dkl_rev per token; either may be NULL (that
  *                                  term is absent), not both
  *   lse_s, lse_t [N] and (with coef_rev) kl_rev [N]: from rlk_linear_kl_fwd
  *   dh_s [N,H_s], dW_s [V,H_s] float   out, overwritten (dh_s 16-byte aligned)
- *   workspace: rlk_linear_kl_bwd_workspace_size bytes: rlk_linear_logp_bwd's workspace plus the
- *              two chunk buffers of the forward. */
+ *   workspace: rlk_linear_kl_bwd_workspace_size bytes: the backward's buffers for one block and
+ *              the 64 MiB scratch (within 1e9 bytes but for the 4-byte index per token). */
 rlk_status_t rlk_linear_kl_bwd_workspace_size(int64_t N, int64_t H_s, int64_t H_t, int64_t V,
                                               int dtype, size_t* bytes);
 rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t,

@@ -19,6 +19,7 @@ from .ops import (  # noqa: E402,F401
     fwd_bwd_entropy_workspace_bytes,
     fwd_entropy_workspace_bytes,
     fwd_workspace_bytes,
+    kl_fwd_workspace_bytes,
     linear_kl,
     linear_logp,
     linear_logp_entropy,

@@ -66,6 +66,8 @@ SIGNATURES = {
     "rlk_linear_logp_merge": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p]),
     "rlk_linear_kl_fwd_workspace_size": (_int, [_i64, _i64, _i64, _i64, _int,
                                                 ctypes.POINTER(_sz)]),
+    "rlk_linear_kl_fwd_workspace_size_for_block": (_int, [_i64, _i64, _i64, _i64, _int, _i64,
+                                                          ctypes.POINTER(_sz)]),
     "rlk_linear_kl_fwd": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _f, _p, _p, _p,
                                  _p, _p, _sz, _p]),
     "rlk_linear_kl_bwd_workspace_size": (_int, [_i64, _i64, _i64, _i64, _int,

@@ -15,6 +15,8 @@
 
 static_assert(rlk::kBwdChunkEntries == rlk::kBwdChunk && rlk::kBwdDhPieces == rlk::kDhPieces,
               "host workspace layout and device chunking agree");
+static_assert(rlk::kKlScratchBytes == (size_t)rlk::kKlSlots * rlk::kKlSlotFloats * 4,
+              "the KL scratch size the host carves is the one the tile kernel addresses");
 
 namespace rlk {
 namespace {
@@ -585,6 +587,21 @@ rlk_status_t rlk_linear_kl_fwd_workspace_size(int64_t N, int64_t H_s, int64_t H_
   return RLK_SUCCESS;
 }
 
+rlk_status_t rlk_linear_kl_fwd_workspace_size_for_block(int64_t N, int64_t H_s, int64_t H_t,
+                                                        int64_t V, int dtype,
+                                                        int64_t block_tokens, size_t* bytes) {
+  if (!bytes) return RLK_ERROR_INVALID_VALUE;
+  rlk_status_t s = check_shape(N, H_s, V, dtype);
+  if (s == RLK_SUCCESS) s = check_shape(N, H_t, V, dtype);
+  if (s != RLK_SUCCESS) return s;
+  if (block_tokens <= 0 || block_tokens % 256 != 0) return RLK_ERROR_INVALID_VALUE;
+  const int64_t top = ((N > 0 ? N : 1) + 255) / 256 * 256;
+  const int64_t cap = block_tokens < top ? block_tokens : top;
+  if (bwd_blocks_cap(N, cap) > 1024) return RLK_ERROR_UNSUPPORTED;
+  *bytes = kl_fwd_layout_cap(N, V, cap).total;
+  return RLK_SUCCESS;
+}
+
 rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t,
                                const void* W_t, const uint8_t* mask, int64_t N, int64_t H_s,
                                int64_t H_t, int64_t V, int dtype, float temperature,
@@ -596,16 +613,17 @@ rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t
   if (!kl_fwd || !kl_rev) return RLK_ERROR_INVALID_VALUE;
   if (!aligned(kl_fwd, 4) || !aligned(kl_rev, 4) || !aligned(lse_s, 4) || !aligned(lse_t, 4))
     return RLK_ERROR_UNSUPPORTED;
-  if (kl_fwd_blocks(N, V) > 1024) return RLK_ERROR_UNSUPPORTED;
-  if (workspace_bytes < kl_fwd_layout(N, V).total) return RLK_ERROR_WORKSPACE;
-  const KlLayout L = kl_fwd_layout(N, V);
+  // the block capacity is the largest the workspace holds (at most 1024 blocks)
+  const int64_t cap64 = kl_fwd_cap_for_workspace(N, V, workspace_bytes);
+  if (cap64 == 0) return RLK_ERROR_WORKSPACE;
+  const KlLayout L = kl_fwd_layout_cap(N, V, cap64);
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* idx = carve<int32_t>(workspace, L.idx);
   int32_t* na = carve<int32_t>(workspace, L.n_active);
   int32_t* counts = carve<int32_t>(workspace, L.block_count);
-  const int nblk = kl_fwd_blocks(N, V);
-  const int cap = (int)kl_fwd_token_cap(V);
-  const int np = (int)kl_fwd_npad(N, V);
+  const int nblk = bwd_blocks_cap(N, cap64);
+  const int cap = (int)cap64;
+  const int np = (int)bwd_npad_cap(N, cap64);
   CompactArgs c{mask, idx, na, nullptr, kl_fwd, lse_s, (int)N, kl_rev, lse_t};
   c.block_count = counts;
   c.nblk = nblk;
@@ -614,55 +632,48 @@ rlk_status_t rlk_linear_kl_fwd(const void* h_s, const void* W_s, const void* h_t
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
   int grid = 0;
   if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
-  const float inv_t = (float)(1.0 / (double)temperature);
-  const size_t es = dtype == RLK_BF16 ? 2 : 4;
+  KlTileArgs t{};
+  t.h_s = h_s;
+  t.W_s = W_s;
+  t.h_t = h_t;
+  t.W_t = W_t;
+  t.N = (int)N;
+  t.H_s = (int)H_s;
+  t.H_t = (int)H_t;
+  t.V = (int)V;
+  t.vstart = 0;
+  t.inv_t = (float)(1.0 / (double)temperature);
+  t.scratch = carve<float>(workspace, L.scratch);
+  t.t_max = carve<float>(workspace, L.tmax);
+  t.t_sum = carve<float>(workspace, L.tsum);
+  t.s_max = carve<float>(workspace, L.smax);
+  t.s_sum = carve<float>(workspace, L.ssum);
+  t.wf = carve<float>(workspace, L.wf);
+  t.wr = carve<float>(workspace, L.wr);
+  t.pstride = np;
   KlArgs k{};
-  k.idx = idx;
-  k.n_active = na;
   k.N = np;  // the row stride of the block's statistics
   k.V = (int)V;
-  k.inv_t = inv_t;
-  k.xs = carve<float>(workspace, L.xs);
-  k.xt = carve<float>(workspace, L.xt);
-  k.s_max = carve<float>(workspace, L.smax);
-  k.s_sum = carve<float>(workspace, L.ssum);
-  k.t_max = carve<float>(workspace, L.tmax);
-  k.t_sum = carve<float>(workspace, L.tsum);
-  k.wf = carve<float>(workspace, L.wf);
-  k.wr = carve<float>(workspace, L.wr);
+  k.t_max = t.t_max;
+  k.t_sum = t.t_sum;
+  k.s_max = t.s_max;
+  k.s_sum = t.s_sum;
+  k.wf = t.wf;
+  k.wr = t.wr;
   k.kl_fwd = kl_fwd;
   k.kl_rev = kl_rev;
   k.lse_s = lse_s;
   k.lse_t = lse_t;
-  // Per token block (the fixed partition: compacted indices b * cap ..; the buffers hold one
-  // block's rows): per chunk, both heads' column statistics and x, then the cross terms; then
-  // the block's merge writes its tokens' results.
+  // Per token block (the fixed partition: compacted indices b * cap ..; the statistics hold
+  // one block's rows): both heads over the whole vocabulary in one launch, then the block's
+  // merge writes its tokens' results.
   for (int b = 0; b < nblk; ++b) {
     const size_t t0 = (size_t)b * cap;
-    const int rows = (int)(N - (int64_t)t0 < np ? N - (int64_t)t0 : np);
-    KlArgs kb = k;
-    kb.idx = idx + t0;
-    kb.n_active = counts + b;
-    for (int64_t c0 = 0; c0 < V; c0 += kBwdChunk) {
-      const int vc = (int)(V - c0 < kBwdChunk ? V - c0 : kBwdChunk);
-      FwdTileArgs t{h_t, static_cast<const uint8_t*>(W_t) + (size_t)c0 * H_t * es, nullptr,
-                    kb.idx, kb.n_active, (int)N, (int)H_t, vc, inv_t,
-                    const_cast<float*>(kb.t_max), const_cast<float*>(kb.t_sum), nullptr, (int)c0,
-                    nullptr, const_cast<float*>(k.xt)};
-      t.pstride = np;
-      e = launch_fwd_tiles(t, dtype == RLK_BF16, grid, st, kFwdStoreX);
-      if (e != hipSuccess) return RLK_ERROR_DEVICE;
-      FwdTileArgs u{h_s, static_cast<const uint8_t*>(W_s) + (size_t)c0 * H_s * es, nullptr,
-                    kb.idx, kb.n_active, (int)N, (int)H_s, vc, inv_t,
-                    const_cast<float*>(kb.s_max), const_cast<float*>(kb.s_sum), nullptr, (int)c0,
-                    nullptr, const_cast<float*>(k.xs)};
-      u.pstride = np;
-      e = launch_fwd_tiles(u, dtype == RLK_BF16, grid, st, kFwdStoreX);
-      if (e != hipSuccess) return RLK_ERROR_DEVICE;
-      e = launch_kl_cross(kb, (int)c0, rows, st);
-      if (e != hipSuccess) return RLK_ERROR_DEVICE;
-    }
-    e = launch_kl_merge(kb, st);
+    t.idx = k.idx = idx + t0;
+    t.n_active = k.n_active = counts + b;
+    e = launch_kl_tiles(t, dtype == RLK_BF16, false, grid, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    e = launch_kl_merge(k, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
   }
   return RLK_SUCCESS;
@@ -703,7 +714,8 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
   if (workspace_bytes < kl_bwd_bytes(N, H_s)) return RLK_ERROR_WORKSPACE;
   int grid = 0;
   if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
-  const BwdLayout L = bwd_layout(N, H_s);
+  const BwdLayout L = kl_bwd_layout(N, H_s);
+  const int64_t cap = kl_bwd_token_cap(H_s);
   const float inv_t = (float)(1.0 / (double)temperature);
   int32_t* idx = carve<int32_t>(workspace, L.idx);
   int32_t* na = carve<int32_t>(workspace, L.n_active);
@@ -716,7 +728,7 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
   a.N = (int)N;
   a.H = (int)H_s;
   a.V = (int)V;
-  a.Npad = (int)bwd_npad(N, H_s);
+  a.Npad = (int)bwd_npad_cap(N, cap);
   a.inv_t = inv_t;
   a.dh = dh_s;
   a.dW = dW_s;
@@ -727,27 +739,28 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
   a.sched = carve<int>(workspace, L.sched);
   a.idx = bidx;
   a.n_active = bn;
-  float* xs = carve<float>(workspace, L.total);
-  float* xt = carve<float>(workspace, L.total + kl_chunk_bytes(N, H_s));
-  KlArgs k{};
-  k.idx = bidx;
-  k.n_active = bn;
-  k.N = (int)N;
-  k.V = (int)V;
-  k.inv_t = inv_t;
-  k.xs = xs;
-  k.xt = xt;
-  k.lse_s_in = lse_s;
-  k.lse_t_in = lse_t;
-  k.kl_rev_in = kl_rev;
-  k.coef_f = coef_fwd;
-  k.coef_r = coef_rev;
-  k.Gv = a.Gv;
-  const int nblk = bwd_blocks(N, H_s);
+  KlTileArgs t{};
+  t.h_s = h_s;
+  t.h_t = h_t;
+  t.idx = bidx;
+  t.n_active = bn;
+  t.N = (int)N;
+  t.H_s = (int)H_s;
+  t.H_t = (int)H_t;
+  t.inv_t = inv_t;
+  t.scratch = carve<float>(workspace, L.total);
+  t.lse_s = lse_s;
+  t.lse_t = lse_t;
+  t.kl_rev = kl_rev;
+  t.coef_f = coef_fwd;
+  t.coef_r = coef_rev;
+  t.Gv = a.Gv;
+  t.gv_pitch = kGvPitch;
+  const int nblk = bwd_blocks_cap(N, cap);
   CompactArgs c{mask, idx, na, nullptr, nullptr, nullptr, (int)N};
   c.block_desc = desc;
   c.nblk = nblk;
-  c.block_cap = (int)bwd_token_cap(H_s);
+  c.block_cap = (int)cap;
   hipError_t e = launch_compact(c, st);
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
   e = launch_zero(dh_s, (size_t)N * (size_t)H_s, st);  // inactive rows stay 0
@@ -761,19 +774,12 @@ rlk_status_t rlk_linear_kl_bwd(const void* h_s, const void* W_s, const void* h_t
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
     for (int ch = 0; ch < nchunks; ++ch) {
       const int64_t c0 = (int64_t)ch * kBwdChunk;
-      const int vc = (int)(V - c0 < kBwdChunk ? V - c0 : kBwdChunk);
-      // both heads' x of the chunk (no statistics), then dL/dz of the chunk into Gv
-      FwdTileArgs t{h_t, static_cast<const uint8_t*>(W_t) + (size_t)c0 * H_t * 2, nullptr, a.idx,
-                    a.n_active, (int)N, (int)H_t, vc, inv_t, nullptr, nullptr, nullptr, (int)c0,
-                    nullptr, xt};
-      e = launch_fwd_tiles(t, true, grid, st, kFwdStoreX);
-      if (e != hipSuccess) return RLK_ERROR_DEVICE;
-      FwdTileArgs u{h_s, static_cast<const uint8_t*>(W_s) + (size_t)c0 * H_s * 2, nullptr, a.idx,
-                    a.n_active, (int)N, (int)H_s, vc, inv_t, nullptr, nullptr, nullptr, (int)c0,
-                    nullptr, xs};
-      e = launch_fwd_tiles(u, true, grid, st, kFwdStoreX);
-      if (e != hipSuccess) return RLK_ERROR_DEVICE;
-      e = launch_kl_grad(k, (int)c0, a.Npad, st);
+      // dL/dz of the chunk from both heads' tiles, then its dL/dh and dL/dW
+      t.W_s = static_cast<const uint8_t*>(W_s) + (size_t)c0 * H_s * 2;
+      t.W_t = static_cast<const uint8_t*>(W_t) + (size_t)c0 * H_t * 2;
+      t.V = (int)(V - c0 < kBwdChunk ? V - c0 : kBwdChunk);
+      t.vstart = (int)c0;
+      e = launch_kl_tiles(t, true, true, grid, st);
       if (e != hipSuccess) return RLK_ERROR_DEVICE;
       e = launch_bwd_chunk_gemms(a, ch, grid, b > 0, st);
       if (e != hipSuccess) return RLK_ERROR_DEVICE;

@@ -46,36 +46,66 @@ struct DiagArgs {
 };
 
 // Full-vocabulary KL between a student (s) and a teacher (t) head.
+//
+// The tile kernel runs both heads' GEMMs on the same 256 x 256 (vocabulary x token) tile, the
+// teacher's first; the teacher's fp32 accumulators wait in the work-group's scratch slot
+// (kKlSlotFloats floats, written and read back by the same lanes) while the student's are
+// formed, and the student's epilogue pairs the two entry by entry.
+constexpr int kKlSlots = 256;                     // scratch slots: the launch's grid is at most this
+constexpr int kKlSlotFloats = 8 * 128 * 64;       // per work-group: 8 waves x 128 accumulators x 64 lanes
+
+struct KlTileArgs {
+  const void* h_s;  // [N][H_s] student hidden states (bf16 or fp32)
+  const void* W_s;  // the launch's first vocabulary row of the student head, [V][H_s]
+  const void* h_t;  // teacher
+  const void* W_t;
+  const int32_t* idx;       // the block's compacted token indices
+  const int32_t* n_active;  // the block's token count
+  int N, H_s, H_t;
+  int V;       // vocabulary entries of the launch (rows of W_s and W_t from their bases)
+  int vstart;  // global index of the launch's first entry (a multiple of 256)
+  float inv_t;
+  float* scratch;  // [kKlSlots][kKlSlotFloats]
+  // forward: per token of the block and 128-entry column, [J][pstride]: each head's column
+  // maximum (log2 units) and sum, and the two cross terms
+  float* t_max;
+  float* t_sum;
+  float* s_max;
+  float* s_sum;
+  float* wf;
+  float* wr;
+  int pstride;
+  // backward: dL/dz of the launch's entries for the block's tokens, bf16, [rows][gv_pitch]
+  const float* lse_s;   // [N] natural-log lse of each head, from the forward
+  const float* lse_t;
+  const float* kl_rev;  // [N] with coef_r only
+  const float* coef_f;  // [N] dL/dKL_fwd per token, or null
+  const float* coef_r;  // [N] dL/dKL_rev per token, or null (not both null)
+  uint16_t* Gv;
+  int gv_pitch;
+};
+
+// The per-token merge of the block's column statistics.
 struct KlArgs {
   const int32_t* idx;
   const int32_t* n_active;
-  int N, V;
-  float inv_t;
-  const float* xs;     // [Npad][kXPitch] student x of the current chunk
-  const float* xt;     // teacher
+  int N, V;            // N: the statistics' column stride
   const float* s_max;  // [J][N] column statistics
   const float* s_sum;
   const float* t_max;
   const float* t_sum;
-  float* wf;           // [J][N] forward-KL cross term per column
-  float* wr;           // reverse
+  const float* wf;     // [J][N] forward-KL cross term per column
+  const float* wr;     // reverse
   float* kl_fwd;       // [N] outputs of the merge
   float* kl_rev;
   float* lse_s;        // may be null
   float* lse_t;        // may be null
-  // backward
-  const float* lse_s_in;
-  const float* lse_t_in;
-  const float* kl_rev_in;  // with coef_r only
-  const float* coef_f;     // [N] dL/dKL_fwd per token, or null
-  const float* coef_r;     // [N] dL/dKL_rev per token, or null (not both null)
-  uint16_t* Gv;            // [Npad][kGvPitch]
 };
 
 hipError_t launch_ratio_kl_loss(const LossArgs& a, double* sums, hipStream_t stream);
 hipError_t launch_dlogp_diagnostics(const DiagArgs& a, hipStream_t stream);
-hipError_t launch_kl_cross(const KlArgs& a, int c0, int rows, hipStream_t stream);
+// mode: false the forward statistics, true the backward's dL/dz; grid at most kKlSlots
+hipError_t launch_kl_tiles(const KlTileArgs& a, bool bf16, bool grad, int grid, hipStream_t stream);
 hipError_t launch_kl_merge(const KlArgs& a, hipStream_t stream);
-hipError_t launch_kl_grad(const KlArgs& a, int c0, int rows, hipStream_t stream);
 
 }  // namespace rlk

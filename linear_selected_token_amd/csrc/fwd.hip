@@ -49,11 +49,6 @@ struct FwdCtx {
 //                and e_v = 2^d_v; the clamp only touches terms whose e_v is 0 (entries past
 //                the vocabulary, or underflowed), so the column's sum_v e_v x_v is
 //                part_w + max * part_sum.
-//   kFwdStoreX   also stores x = z log2 e of every entry of the tile into xbuf, token-major
-//                with kBwdChunk entries per compacted token (the vocabulary is walked one
-//                chunk per launch, as a shard); the column statistics are written only when
-//                part_max is given.  No target.  The full-vocabulary KL between two heads
-//                pairs their x entry by entry from two such buffers.
 //   kFwdStoreD   the plain statistics and target, and d = x - max of every entry of the tile
 //                (the exponent the column sum adds up, <= 0) into dbuf as a 16-bit code,
 //                -d 2^9 rounded and clamped to [0, 65535]: steps of 2^-9 over (-128, 0], so the
@@ -69,7 +64,6 @@ template <bool kBF16, int kMode>
 __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
   constexpr bool kEnt = kMode == kFwdEntropy || kMode == kFwdStoreDEnt;
   constexpr bool kStoreD = kMode == kFwdStoreD || kMode == kFwdStoreDEnt;
-  constexpr bool kNoTarget = kMode == kFwdStoreX;
   __shared__ RingSmem sm;
   const int Na = *a.n_active;
   const int nTokTiles = (Na + kTile - 1) / kTile;
@@ -109,12 +103,8 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
     for (int j = 0; j < kBlkB; ++j) {
       c.tok[j] = tbase + wt + acc_col(j, lane);
       // target as a row of this W (out of range or in another vocabulary shard: none)
-      if constexpr (kNoTarget) {
-        c.tgt[j] = -1;
-      } else {
-        const int y = c.tok[j] < Na ? a.targets[a.idx[c.tok[j]]] - a.vstart : -1;
-        c.tgt[j] = (y >= 0 && y < a.V) ? y : -1;
-      }
+      const int y = c.tok[j] < Na ? a.targets[a.idx[c.tok[j]]] - a.vstart : -1;
+      c.tgt[j] = (y >= 0 && y < a.V) ? y : -1;
     }
   };
 
@@ -192,23 +182,6 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
         w = w + __shfl_xor(w, 32);
       }
       const int ti = c.tok[j];
-      if constexpr (kMode == kFwdStoreX) {
-        // x of every entry (tail entries hold -inf), four consecutive entries per store
-        if (ti < Na) {
-          float* xrow = a.xbuf + (size_t)ti * kXPitch + vq;
-#pragma unroll
-          for (int i = 0; i < kBlkA; ++i)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              f32x4 x;
-              x.x = acc.c[i][j][4 * g + 0] * c2;
-              x.y = acc.c[i][j][4 * g + 1] * c2;
-              x.z = acc.c[i][j][4 * g + 2] * c2;
-              x.w = acc.c[i][j][4 * g + 3] * c2;
-              *reinterpret_cast<f32x4*>(xrow + acc_row(i, 4 * g, lane)) = x;
-            }
-        }
-      }
       if constexpr (kStoreD) {
         // codes of the wave's 128 entries for this token column, 16 bytes per lane: per 32-entry
         // block, v_permlane32_swap on the packed groups (2h, 2h + 1) hands lane l entries
@@ -244,10 +217,8 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
       }
       if (ti < Na) {
         if (lane < 32) {
-          if (kMode != kFwdStoreX || a.part_max) {
-            a.part_max[col * pst + ti] = mx;
-            a.part_sum[col * pst + ti] = s;
-          }
+          a.part_max[col * pst + ti] = mx;
+          a.part_sum[col * pst + ti] = s;
           if constexpr (kEnt) a.part_w[col * pst + ti] = w;
         }
         if (hit) a.target_logit[ti] = zsel * a.inv_t;
@@ -360,7 +331,6 @@ hipError_t launch_fwd_tiles(const FwdTileArgs& a, bool bf16, int grid, hipStream
   switch (mode) {
     case kFwdPlain: launch_mode<kFwdPlain>(a, bf16, grid, stream); break;
     case kFwdEntropy: launch_mode<kFwdEntropy>(a, bf16, grid, stream); break;
-    case kFwdStoreX: launch_mode<kFwdStoreX>(a, bf16, grid, stream); break;
     case kFwdStoreD:
       if (!bf16) return hipErrorInvalidValue;
       hipLaunchKernelGGL((fwd_tiles_kernel<true, kFwdStoreD>), dim3(grid), dim3(kThreads), 0,

@@ -20,7 +20,6 @@ constexpr int kDhPieces = kBwdChunk / kDhSplitK;  // pieces of a full chunk
 // Row pitch (entries) of the token-major chunk buffers: the chunk plus 128 bytes, so that the
 // rows a wave writes at once (32 tokens) do not all start at the same 64 KiB-aligned offset.
 constexpr int kGvPitch = kBwdChunk + 64;  // bf16 dL/dz
-constexpr int kXPitch = kBwdChunk + 32;   // fp32 x of the KL path
 
 struct CompactArgs {
   const uint8_t* mask;
@@ -61,13 +60,12 @@ struct FwdTileArgs {
   float* target_logit;
   int vstart;  // global vocabulary index of W row 0 (a multiple of kVocabPartial)
   float* part_w = nullptr;  // [J][N] entropy statistic per column (kFwdEntropy)
-  float* xbuf = nullptr;    // [Npad][kXPitch] x = z log2 e of one vocabulary chunk (kFwdStoreX)
   int pstride = 0;          // column stride of part_max / part_sum / part_w (0: N)
   uint16_t* dbuf = nullptr; // [rows][d_pitch] 16-bit code of d = x - column max (kFwdStoreD)
   int d_pitch = 0;          // entries per dbuf row
 };
 
-enum FwdMode { kFwdPlain = 0, kFwdEntropy = 1, kFwdStoreX = 2, kFwdStoreD = 3, kFwdStoreDEnt = 4 };
+enum FwdMode { kFwdPlain = 0, kFwdEntropy = 1, kFwdStoreD = 3, kFwdStoreDEnt = 4 };
 
 struct MergeArgs {
   const float* part_max;

@@ -2,94 +2,294 @@
 // operator backlog: chunked full-vocabulary / distillation KL fused with the LM head,
 // forward and reverse).
 //
-// The vocabulary is walked in chunks of kBwdChunk entries.  Per chunk, each head's tile
-// kernel (fwd_tiles_kernel in its kFwdStoreX mode, run as a vocabulary shard) writes its
-// column statistics and x = z log2 e of the chunk, token-major, into a chunk buffer; the
-// kernels below pair the two buffers entry by entry.  At most one chunk of each head's
-// logits exists at a time.
-//
-//   kl_cross    per token and 128-entry column:
-//                 wf = sum_v 2^(x_t - m_t) (x_t - x_s)   (forward KL's cross term)
-//                 wr = sum_v 2^(x_s - m_s) (x_s - x_t)   (reverse KL's)
-//               with m_t, m_s the columns' maxima.
+//   kl_tiles    persistent grid over (vocabulary tile x token tile) pairs.  Per tile, the
+//               teacher's z_t = W_t h_t^T and then the student's z_s = W_s h_s^T, each on
+//               MFMA with fp32 accumulation over its whole hidden dimension in one fixed K
+//               order (the forward tile kernel's loop).  The teacher's accumulators wait in
+//               the work-group's scratch slot while the student's are formed; the student's
+//               epilogue pairs the two entry by entry, in log2 units x = z log2 e:
+//                 forward: per token and 128-entry column, both heads' column maximum m and
+//                   sum of 2^(x - m), and the cross terms
+//                     wf = sum_v 2^(x_t - m_t) (x_t - x_s)   (forward KL)
+//                     wr = sum_v 2^(x_s - m_s) (x_s - x_t)   (reverse KL)
+//                 backward: for L = sum_t (f_t KL_fwd,t + r_t KL_rev,t), the student's
+//                     dL/dz = (f_t / T)(p_s - p_t) + (r_t / T) p_s (ln p_s - ln p_t - KL_rev)
+//                   rounded to bf16 in the token-major layout the dL/dh and dL/dW GEMMs read.
+//               No logits of either head reach memory.
 //   kl_merge    per token, in the forward merge's fixed association: both heads' M and S,
 //                 KL_fwd = ln2 (A_f / S_t - (M_t + log2 S_t) + (M_s + log2 S_s))
 //                 KL_rev = ln2 (A_r / S_s - (M_s + log2 S_s) + (M_t + log2 S_t))
 //               with A_f = sum_j 2^(m_t,j - M_t) wf_j and A_r likewise.
-//   kl_grad     the backward's dL/dz of one chunk for L = sum_t (f_t KL_fwd,t + r_t KL_rev,t),
-//               rounded to bf16 in the token-major layout the dL/dh and dL/dW GEMMs read (Gv):
-//                 (f_t / T)(p_s - p_t) + (r_t / T) p_s (ln p_s - ln p_t - KL_rev)
 //
 // Every reduction is a fixed in-lane order followed by a fixed xor tree, and the columns
 // are merged in one fixed order, so a token's results depend only on its own rows.
 #include "common.hpp"
 #include "aux_kernels.hpp"
 #include "kernels.hpp"
+#include "mainloop.hpp"
 
 namespace rlk {
 
 namespace {
 
-// One work-group of 4 waves per compacted token row; each 32-lane half of a wave takes one
-// 128-entry column (4 entries per lane), so a wave step covers 2 columns.  A half takes its
-// columns two at a time (both columns' loads issued before either is reduced); the chunk
-// buffers are read once, with non-temporal loads.
-__global__ __launch_bounds__(256) void kl_cross_kernel(KlArgs a, int c0) {
+// Two floats to packed bf16, round to nearest even.
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+struct KlCtx {
+  int vbase, tbase;  // first vocabulary entry (of the launch) and first compacted token
+  int tok[kBlkB];    // this lane's token columns (compacted index within the block)
+};
+
+// kGrad: the backward's dL/dz (kF / kR: the forward / reverse term is present); otherwise
+// the forward's column statistics.
+template <bool kBF16, bool kGrad, bool kF, bool kR>
+__global__ __launch_bounds__(kThreads) void kl_tiles_kernel(KlTileArgs a) {
+  __shared__ RingSmem sm;
   const int Na = *a.n_active;
-  const int i = blockIdx.x;
-  if (i >= Na) return;
-  const int vc = min(kBwdChunk, a.V - c0);
-  const int ncol = (vc + 127) / 128;
+  const int nTokTiles = (Na + kTile - 1) / kTile;
+  const int nVocTiles = (a.V + kTile - 1) / kTile;
+  const int n_tiles = nTokTiles * nVocTiles;
+  const int band = nTokTiles < 8 ? nTokTiles : 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
-  const float* xs_row = a.xs + (size_t)i * kXPitch;
-  const float* xt_row = a.xt + (size_t)i * kXPitch;
-  auto ld = [&](const float* r, int v0) __attribute__((always_inline)) {
-    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + v0));
-  };
-  auto col_terms = [&](int jc, const f32x4& xs, const f32x4& xt, float ms,
-                       float mt) __attribute__((always_inline)) {
-    const int col = c0 / 128 + jc;
-    const int v0 = jc * 128 + 4 * l32;
-    const float s4[4] = {xs.x, xs.y, xs.z, xs.w};
-    const float t4[4] = {xt.x, xt.y, xt.z, xt.w};
-    float wf = 0.f, wr = 0.f;
+  const size_t es = kBF16 ? 2 : 4;
+  const size_t rb_t = (size_t)a.H_t * es;
+  const size_t rb_s = (size_t)a.H_s * es;
+  const float c2 = a.inv_t * kLog2e;
+  const int wv = wave_a0(wave);  // vocabulary offset of the wave sub-tile
+  const int wt = wave_b0(wave);  // token offset of the wave sub-tile
+  const int half4 = 4 * (lane >> 5);
+  // this lane's 32 vectors in the work-group's slot: vector e at slot[64 e]
+  f32x4* slot = reinterpret_cast<f32x4*>(a.scratch) +
+                ((size_t)blockIdx.x * kWaves + wave) * (kBlkA * kBlkB * 4 * 64) + lane;
+
+  // load sources of one head's GEMM for the tile at (vbase, tbase): rows of W past the launch's
+  // vocabulary repeat its last row (the epilogue drops them), token rows past the block repeat
+  // its last token (their columns are dropped or zeroed)
+  auto head_src = [&](const void* W, const void* h, size_t rb, const KlCtx& c, TileSrc& src) {
+    src.nk = (int)(rb / kKBytes);
+    src.a_kstep = src.b_kstep = kKBytes;
+    src.a = uniform_ptr(static_cast<const uint8_t*>(W) + (size_t)c.vbase * rb);
+    src.b = uniform_ptr(h);
+    src.a_bytes = operand_bytes((size_t)(a.V - c.vbase) * rb);
+    src.b_bytes = operand_bytes((size_t)a.N * rb);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (v0 + e < vc) {  // entries past the vocabulary hold -inf in both buffers
-        const float d = t4[e] - s4[e];
-        wf = __builtin_fmaf(__builtin_amdgcn_exp2f(t4[e] - mt), d, wf);
-        wr = __builtin_fmaf(__builtin_amdgcn_exp2f(s4[e] - ms), -d, wr);
+    for (int q = 0; q < kDmaPerWave; ++q) {
+      const int r = dma_row(q, wave, lane);
+      const int ch = dma_chunk(q, wave, lane);
+      const int v = min(c.vbase + r, a.V - 1);
+      const int t = a.idx[min(c.tbase + r, Na - 1)];
+      src.ao[q] = (uint32_t)((size_t)(v - c.vbase) * rb) + 16 * ch;
+      src.bo[q] = (uint32_t)((size_t)t * rb) + 16 * ch;
+    }
+  };
+  auto setup = [&](int u, KlCtx& c) {
+    int vt, tt;
+    tile_coords(u, nVocTiles, nTokTiles, band, vt, tt);
+    c.vbase = vt * kTile;
+    c.tbase = tt * kTile;
+#pragma unroll
+    for (int j = 0; j < kBlkB; ++j) c.tok[j] = c.tbase + wt + acc_col(j, lane);
+  };
+
+  // The teacher's accumulators of block (i, j), group g, go to vector 4 (i kBlkB + j) + g; for
+  // the forward, each token column's maximum over the wave's vocabulary rows (log2 units; rows
+  // past the vocabulary left out) is taken on the way.
+  auto stash = [&](const KlCtx& c, const Acc& acc, float (&mt)[kBlkB]) {
+    const int lim = a.V - c.vbase - wv - half4;  // row offsets >= lim are past the vocabulary
+    const bool tail = c.vbase + wv + kWaveA > a.V;  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < kBlkB; ++j) {
+      float am = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kBlkA; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+          v.x = acc.c[i][j][4 * g + 0];
+          v.y = acc.c[i][j][4 * g + 1];
+          v.z = acc.c[i][j][4 * g + 2];
+          v.w = acc.c[i][j][4 * g + 3];
+          slot[64 * ((i * kBlkB + j) * 4 + g)] = v;
+          if constexpr (!kGrad) {
+            if (tail) {
+              const int o = 32 * i + 8 * g;
+              v.x = o + 0 < lim ? v.x : -INFINITY;
+              v.y = o + 1 < lim ? v.y : -INFINITY;
+              v.z = o + 2 < lim ? v.z : -INFINITY;
+              v.w = o + 3 < lim ? v.w : -INFINITY;
+            }
+            am = fmaxf(fmaxf(am, v.x), fmaxf(v.y, fmaxf(v.z, v.w)));
+          }
+        }
+      if constexpr (!kGrad) mt[j] = fmaxf(am, __shfl_xor(am, 32)) * c2;
+    }
+  };
+
+  // The teacher's accumulators of block (i, j), as the student's are laid out.
+  auto unstash = [&](int i, int j, float (&tv)[16]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = slot[64 * ((i * kBlkB + j) * 4 + g)];
+      tv[4 * g + 0] = v.x;
+      tv[4 * g + 1] = v.y;
+      tv[4 * g + 2] = v.z;
+      tv[4 * g + 3] = v.w;
+    }
+  };
+
+  // Per token column j of the student's accumulators in acc.  Entry (i, r) is vocabulary row
+  // vq + acc_row(i, r, lane), at row offset 32 i + 8 (r >> 2) + (r & 3) from this lane's first.
+  // The teacher's blocks are read back one ahead of the one in use.
+  auto epilogue = [&](const KlCtx& c, Acc& acc, const float (&mt)[kBlkB]) {
+    const int vq = c.vbase + wv;
+    if (vq >= a.V) return;  // quadrant entirely past the vocabulary
+    const bool tail = vq + kWaveA > a.V;  // wave-uniform
+    const int lim = a.V - vq - half4;
+    float tv[2][16];
+    unstash(0, 0, tv[0]);
+#pragma unroll
+    for (int j = 0; j < kBlkB; ++j) {
+      const int ti = c.tok[j];
+      if constexpr (!kGrad) {
+        // entries past the vocabulary: -inf in the student's maximum, no term in the sums
+        float am = -INFINITY;
+        if (tail) {
+#pragma unroll
+          for (int i = 0; i < kBlkA; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * i + 8 * (r >> 2) + (r & 3) >= lim) acc.c[i][j][r] = -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < kBlkA; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2)
+            am = fmaxf(am, fmaxf(acc.c[i][j][r], acc.c[i][j][r + 1]));
+        const float ms = fmaxf(am, __shfl_xor(am, 32)) * c2;
+        // wf and wr are summed in accumulator units: wf = c2 sum et (t - s), wr = c2 sum es (s - t)
+        float st = 0.f, ss = 0.f, wf = 0.f, wr = 0.f;
+#pragma unroll
+        for (int i = 0; i < kBlkA; ++i) {
+          const int cb = (j * kBlkA + i) & 1;
+          if (j * kBlkA + i + 1 < kBlkA * kBlkB)
+            unstash((i + 1) % kBlkA, j + (i + 1) / kBlkA, tv[cb ^ 1]);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float t = tv[cb][r];
+            const float s_ = acc.c[i][j][r];  // -inf past the vocabulary
+            const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(t, c2, -mt[j]));
+            const float e_s = __builtin_amdgcn_exp2f(__builtin_fmaf(s_, c2, -ms));
+            float d = t - s_;
+            if (tail) d = 32 * i + 8 * (r >> 2) + (r & 3) < lim ? d : 0.f;
+            st += tail && !(32 * i + 8 * (r >> 2) + (r & 3) < lim) ? 0.f : et;
+            ss += e_s;
+            wf = __builtin_fmaf(et, d, wf);
+            wr = __builtin_fmaf(e_s, -d, wr);
+          }
+        }
+        float o[4] = {st, ss, wf * c2, wr * c2};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] += __shfl_xor(o[q], 32);
+        if (ti < Na && lane < 32) {
+          const size_t at = (size_t)((a.vstart + vq) / kVocabPartial) * a.pstride + ti;
+          a.t_max[at] = mt[j];
+          a.t_sum[at] = o[0];
+          a.s_max[at] = ms;
+          a.s_sum[at] = o[1];
+          a.wf[at] = o[2];
+          a.wr[at] = o[3];
+        }
+      } else {
+        // dL/dz of every entry, 0 past the vocabulary and in padded token columns; stored as
+        // the backward's logits pass stores it (per 32-entry block, v_permlane32_swap hands
+        // lane l entries 16 h + 0..7 and lane l + 32 entries 16 h + 8..15 of the same token)
+        const bool act = ti < Na;
+        const int t = act ? a.idx[ti] : 0;
+        const float lse2s = act ? a.lse_s[t] * kLog2e : 0.f;
+        const float lse2t = act ? a.lse_t[t] * kLog2e : 0.f;
+        const float cf = (kF && act) ? a.coef_f[t] * a.inv_t : 0.f;
+        const float cr = (kR && act) ? a.coef_r[t] * a.inv_t : 0.f;
+        const float klr = (kR && act) ? a.kl_rev[t] : 0.f;
+        const int lj = act ? lim : 0;  // entries at row offset >= lj are 0
+        const bool zero_some = tail || !act;
+#pragma unroll
+        for (int i = 0; i < kBlkA; ++i) {
+          const int cb = (j * kBlkA + i) & 1;
+          if (j * kBlkA + i + 1 < kBlkA * kBlkB)
+            unstash((i + 1) % kBlkA, j + (i + 1) / kBlkA, tv[cb ^ 1]);
+          u32x2 pk[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float G[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              const float ls = __builtin_fmaf(acc.c[i][j][r], c2, -lse2s);  // log2 p_s
+              const float lt = __builtin_fmaf(tv[cb][r], c2, -lse2t);
+              const float ps = __builtin_amdgcn_exp2f(ls);
+              float gv = 0.f;
+              if constexpr (kF) gv = cf * (ps - __builtin_amdgcn_exp2f(lt));
+              if constexpr (kR) gv = __builtin_fmaf(cr * ps, __builtin_fmaf(ls - lt, kLn2, -klr), gv);
+              if (zero_some) gv = (32 * i + 8 * g + e < lj) ? gv : 0.f;
+              G[e] = gv;
+            }
+            pk[g][0] = pack2(G[0], G[1]);
+            pk[g][1] = pack2(G[2], G[3]);
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const auto s0 =
+                __builtin_amdgcn_permlane32_swap(pk[2 * h][0], pk[2 * h + 1][0], false, false);
+            const auto s1 =
+                __builtin_amdgcn_permlane32_swap(pk[2 * h][1], pk[2 * h + 1][1], false, false);
+            u32x4 q;
+            q.x = s0[0];
+            q.y = s1[0];
+            q.z = s0[1];
+            q.w = s1[1];
+            const int vl = vq + 32 * i + 16 * h + 8 * (lane >> 5);  // first of 8
+            *reinterpret_cast<u32x4*>(a.Gv + (size_t)ti * a.gv_pitch + vl) = q;
+          }
+        }
       }
     }
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) {
-      wf += __shfl_xor(wf, o);
-      wr += __shfl_xor(wr, o);
-    }
-    if (l32 == 0) {
-      a.wf[(size_t)col * a.N + i] = wf;
-      a.wr[(size_t)col * a.N + i] = wr;
-    }
   };
-  for (int jc = 2 * wave + half; jc < ncol; jc += 16) {
-    const bool two = jc + 8 < ncol;
-    const int colA = c0 / 128 + jc, colB = colA + 8;
-    const f32x4 xsA = ld(xs_row, jc * 128 + 4 * l32), xtA = ld(xt_row, jc * 128 + 4 * l32);
-    f32x4 xsB = {0.f, 0.f, 0.f, 0.f}, xtB = {0.f, 0.f, 0.f, 0.f};
-    float msB = 0.f, mtB = 0.f;
-    if (two) {
-      xsB = ld(xs_row, (jc + 8) * 128 + 4 * l32);
-      xtB = ld(xt_row, (jc + 8) * 128 + 4 * l32);
-      msB = a.s_max[(size_t)colB * a.N + i];
-      mtB = a.t_max[(size_t)colB * a.N + i];
+
+  // The persistent walk (the tile driver of the forward kernel, with two GEMMs per tile): the
+  // student's first loads go out before the teacher's accumulators are stashed, the next tile's
+  // teacher loads before the epilogue.
+  int round = 0;
+  int u = virtual_tile(round, blockIdx.x, gridDim.x);
+  if (u >= n_tiles) return;
+  TileSrc src;
+  KlCtx ctx;
+  setup(u, ctx);
+  head_src(a.W_t, a.h_t, rb_t, ctx, src);
+  ring_prologue(sm, src, src.nk);
+  while (true) {
+    Acc acc;
+    zero_acc(acc);
+    ring_mainloop<kBF16, false, false>(sm, src, src.nk, acc);  // teacher
+    head_src(a.W_s, a.h_s, rb_s, ctx, src);
+    ring_prologue(sm, src, src.nk);
+    float mt[kBlkB];
+    stash(ctx, acc, mt);
+    zero_acc(acc);
+    ring_mainloop<kBF16, false, false>(sm, src, src.nk, acc);  // student
+    const int un = virtual_tile(++round, blockIdx.x, gridDim.x);
+    const bool more = un < n_tiles;
+    const KlCtx cur = ctx;
+    if (more) {
+      setup(un, ctx);
+      head_src(a.W_t, a.h_t, rb_t, ctx, src);
+      ring_prologue(sm, src, src.nk);
     }
-    const float msA = a.s_max[(size_t)colA * a.N + i];
-    const float mtA = a.t_max[(size_t)colA * a.N + i];
-    col_terms(jc, xsA, xtA, msA, mtA);
-    if (two) col_terms(jc + 8, xsB, xtB, msB, mtB);
+    epilogue(cur, acc, mt);
+    if (!more) break;
   }
 }
 
@@ -176,97 +376,35 @@ __global__ __launch_bounds__(256) void kl_merge_kernel(KlArgs a) {
   }
 }
 
-// Two floats to packed bf16, round to nearest even.
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// One work-group per row of Gv (rows up to the active count rounded to the tile, the rest
-// exit); each thread forms 4 consecutive entries per step, two steps at a time (both steps'
-// non-temporal loads issued first).  Rows past the active count and
-// entries past the vocabulary are written as 0, since the GEMMs that follow read them.
-// kF / kR: the forward / reverse KL term is present (coef_f / coef_r given).
-template <bool kF, bool kR>
-__global__ __launch_bounds__(256) void kl_grad_kernel(KlArgs a, int c0) {
-  const int Na = *a.n_active;
-  const int i = blockIdx.x;
-  const int rows = (Na + 255) / 256 * 256;
-  if (i >= rows) return;
-  const int vc = min(kBwdChunk, a.V - c0);
-  const int vt = (vc + 255) / 256 * 256;  // entries the tiles of the chunk cover
-  const bool act = i < Na;
-  float lse2s = 0.f, lse2t = 0.f, cf = 0.f, cr = 0.f, klr = 0.f;
-  if (act) {
-    const int t = a.idx[i];
-    lse2s = a.lse_s_in[t] * kLog2e;
-    lse2t = a.lse_t_in[t] * kLog2e;
-    if constexpr (kF) cf = a.coef_f[t] * a.inv_t;
-    if constexpr (kR) {
-      cr = a.coef_r[t] * a.inv_t;
-      klr = a.kl_rev_in[t];
-    }
-  }
-  const float* xs_row = a.xs + (size_t)i * kXPitch;
-  const float* xt_row = a.xt + (size_t)i * kXPitch;
-  uint16_t* g_row = a.Gv + (size_t)i * kGvPitch;
-  auto grad4 = [&](int v0, const f32x4& xs, const f32x4& xt) __attribute__((always_inline)) {
-    float G[4] = {0.f, 0.f, 0.f, 0.f};
-    if (act && v0 < vc) {
-      const float s4[4] = {xs.x, xs.y, xs.z, xs.w};
-      const float t4[4] = {xt.x, xt.y, xt.z, xt.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (v0 + e < vc) {
-          const float ls = s4[e] - lse2s;  // log2 p_s
-          const float lt = t4[e] - lse2t;
-          const float ps = __builtin_amdgcn_exp2f(ls);
-          float g = 0.f;
-          if constexpr (kF) g = cf * (ps - __builtin_amdgcn_exp2f(lt));
-          if constexpr (kR) g = __builtin_fmaf(cr * ps, __builtin_fmaf(ls - lt, kLn2, -klr), g);
-          G[e] = g;
-        }
-      }
-    }
-    u32x2 pk;
-    pk[0] = pack2(G[0], G[1]);
-    pk[1] = pack2(G[2], G[3]);
-    *reinterpret_cast<u32x2*>(g_row + v0) = pk;
-  };
-  auto ld = [&](const float* r, int v0) __attribute__((always_inline)) {
-    return (act && v0 < vc) ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + v0))
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
-  };
-  for (int v0 = 4 * threadIdx.x; v0 < vt; v0 += 2048) {
-    const int v1 = v0 + 1024;
-    const f32x4 xs0 = ld(xs_row, v0), xt0 = ld(xt_row, v0);
-    const f32x4 xs1 = ld(xs_row, v1), xt1 = ld(xt_row, v1);
-    grad4(v0, xs0, xt0);
-    if (v1 < vt) grad4(v1, xs1, xt1);
-  }
-}
-
 }  // namespace
 
-hipError_t launch_kl_cross(const KlArgs& a, int c0, int rows, hipStream_t stream) {
-  if (rows > 0) hipLaunchKernelGGL(kl_cross_kernel, dim3(rows), dim3(256), 0, stream, a, c0);
+hipError_t launch_kl_tiles(const KlTileArgs& a, bool bf16, bool grad, int grid, hipStream_t stream) {
+  if (grid > kKlSlots) grid = kKlSlots;
+  if (!grad) {
+    if (bf16)
+      hipLaunchKernelGGL((kl_tiles_kernel<true, false, false, false>), dim3(grid), dim3(kThreads), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((kl_tiles_kernel<false, false, false, false>), dim3(grid), dim3(kThreads), 0,
+                         stream, a);
+  } else if (!bf16) {
+    return hipErrorInvalidValue;  // the backward is bf16 only
+  } else if (a.coef_f && a.coef_r) {
+    hipLaunchKernelGGL((kl_tiles_kernel<true, true, true, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, a);
+  } else if (a.coef_r) {
+    hipLaunchKernelGGL((kl_tiles_kernel<true, true, false, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((kl_tiles_kernel<true, true, true, false>), dim3(grid), dim3(kThreads), 0,
+                       stream, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_kl_merge(const KlArgs& a, hipStream_t stream) {
   const int blocks = (a.N + 31) / 32;
   if (blocks > 0) hipLaunchKernelGGL(kl_merge_kernel, dim3(blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_kl_grad(const KlArgs& a, int c0, int rows, hipStream_t stream) {
-  if (rows <= 0) return hipSuccess;
-  if (a.coef_f && a.coef_r)
-    hipLaunchKernelGGL((kl_grad_kernel<true, true>), dim3(rows), dim3(256), 0, stream, a, c0);
-  else if (a.coef_r)
-    hipLaunchKernelGGL((kl_grad_kernel<false, true>), dim3(rows), dim3(256), 0, stream, a, c0);
-  else
-    hipLaunchKernelGGL((kl_grad_kernel<true, false>), dim3(rows), dim3(256), 0, stream, a, c0);
   return hipGetLastError();
 }
 

@@ -122,20 +122,22 @@ inline int64_t bwd_token_cap(int64_t H) {
   return c < 256 ? 256 : c;
 }
 
-// Token blocks for N tokens (an upper bound: it assumes every token is active; blocks past the
-// active tokens do nothing).  At most 586 for the shapes check_shape accepts (N <= 2^22 and
-// h <= 2^31 bytes bound N by the capacity's H).
-inline int bwd_blocks(int64_t N, int64_t H) {
-  const int64_t cap = bwd_token_cap(H);
+// Token blocks of at most cap tokens (a multiple of 256) for N tokens (an upper bound: it
+// assumes every token is active; blocks past the active tokens do nothing), and the block
+// buffers' rows: min(N, cap) rounded up to the 256-token tile.
+inline int bwd_blocks_cap(int64_t N, int64_t cap) {
   return (int)(((N > 0 ? N : 1) + cap - 1) / cap);
 }
 
-// Token capacity of the block buffers: min(N, capacity) rounded up to the 256-token tile.
-inline int64_t bwd_npad(int64_t N, int64_t H) {
-  const int64_t cap = bwd_token_cap(H);
+inline int64_t bwd_npad_cap(int64_t N, int64_t cap) {
   const int64_t n = N <= 0 ? 1 : (N < cap ? N : cap);
   return (n + 255) / 256 * 256;
 }
+
+// At most 586 blocks of the backward's capacity for the shapes check_shape accepts (N <= 2^22
+// and h <= 2^31 bytes bound N by the capacity's H).
+inline int bwd_blocks(int64_t N, int64_t H) { return bwd_blocks_cap(N, bwd_token_cap(H)); }
+inline int64_t bwd_npad(int64_t N, int64_t H) { return bwd_npad_cap(N, bwd_token_cap(H)); }
 
 // Workspace layout of the backward: idx[N] | n_active | block_desc[blocks][2] | bidx[Npad] |
 // bn | sched[8] | hT[H, Npad] | Gv[Npad, chunk] (bf16) | dhp[1 ..][Npad, H] (fp32).
@@ -143,15 +145,15 @@ struct BwdLayout {
   size_t idx, n_active, block_desc, bidx, bn, sched, hT, Gv, dhp[kBwdDhPieces], total;
 };
 
-inline BwdLayout bwd_layout(int64_t N, int64_t H) {
+inline BwdLayout bwd_layout_cap(int64_t N, int64_t H, int64_t cap) {
   BwdLayout L;
   const size_t n = (size_t)(N > 0 ? N : 1);
-  const size_t np = (size_t)bwd_npad(N, H);
+  const size_t np = (size_t)bwd_npad_cap(N, cap);
   const size_t c = (size_t)kBwdChunkEntries;
   size_t o = 0;
   L.idx = o;        o = align_up(o + 4 * n, 256);
   L.n_active = o;   o = align_up(o + 4, 256);
-  L.block_desc = o; o = align_up(o + 8 * (size_t)bwd_blocks(N, H), 256);
+  L.block_desc = o; o = align_up(o + 8 * (size_t)bwd_blocks_cap(N, cap), 256);
   L.bidx = o;       o = align_up(o + 4 * np, 256);
   L.bn = o;         o = align_up(o + 4, 256);
   L.sched = o;      o = align_up(o + 4 * 8, 256);
@@ -165,6 +167,8 @@ inline BwdLayout bwd_layout(int64_t N, int64_t H) {
   L.total = o;
   return L;
 }
+
+inline BwdLayout bwd_layout(int64_t N, int64_t H) { return bwd_layout_cap(N, H, bwd_token_cap(H)); }
 
 // The fused forward + backward keeps, per token of a block, the 16-bit d code of every vocabulary
 // entry (one row of roundup(V, 256) + 64 entries, turned into bf16 dL/dz in place), the
@@ -361,68 +365,82 @@ inline rlk_status_t check_fused(const void* h, const void* W, const int32_t* tar
   return RLK_SUCCESS;
 }
 
-// Full-vocabulary KL: one chunk of each head's x for np token rows, [np][chunk + 32] fp32.
-inline size_t kl_chunk_bytes_rows(int64_t np) {
-  return align_up(4 * (size_t)np * (size_t)(kBwdChunkEntries + 32), 256);  // kXPitch
-}
-
-// The KL backward takes the active tokens in the backward's blocks (the student's H sets them).
-inline size_t kl_chunk_bytes(int64_t N, int64_t H) { return kl_chunk_bytes_rows(bwd_npad(N, H)); }
+// Full-vocabulary KL.  The tile kernel keeps the teacher's accumulators of a tile in a scratch
+// slot per work-group while the student's are formed: 256 slots of 8 x 128 x 64 floats (the
+// launch's grid is at most 256 work-groups).
+constexpr size_t kKlScratchBytes = (size_t)256 * 8 * 128 * 64 * 4;  // 64 MiB
 
 // The KL forward takes the active tokens in blocks of its own: per token of capacity, a row of
-// each head's fp32 x chunk and a row of the six column-statistics arrays (both heads' maxima
-// and sums, both cross terms), 8 (chunk + 32) + 24 ceil(V / 128) bytes.  The capacity is the
-// largest multiple of 256 tokens whose rows fit the backward's budget (at least 256): 3328
-// tokens at V = 151936, so the forward's workspace stays under 1e9 bytes at any N.
-inline size_t kl_fwd_bytes_per_token(int64_t V) {
-  return 8 * (size_t)(kBwdChunkEntries + 32) + 24 * (size_t)num_partials(V);
-}
+// the six column-statistics arrays (both heads' maxima and sums, both cross terms), 24
+// ceil(V / 128) bytes.  The capacity is the largest multiple of 256 tokens whose rows fit the
+// backward's budget beside the scratch (at least 256): 32512 tokens at V = 151936.
+inline size_t kl_fwd_bytes_per_token(int64_t V) { return 24 * (size_t)num_partials(V); }
 
 inline int64_t kl_fwd_token_cap(int64_t V) {
-  const int64_t c = (int64_t)(kBwdBlockBudget / kl_fwd_bytes_per_token(V > 0 ? V : 1)) / 256 * 256;
+  const int64_t c = (int64_t)((kBwdBlockBudget - kKlScratchBytes) /
+                              kl_fwd_bytes_per_token(V > 0 ? V : 1)) / 256 * 256;
   return c < 256 ? 256 : (c > kMaxTokens ? kMaxTokens : c);
 }
 
-inline int kl_fwd_blocks(int64_t N, int64_t V) {
-  const int64_t cap = kl_fwd_token_cap(V);
-  return (int)(((N > 0 ? N : 1) + cap - 1) / cap);
-}
-
-inline int64_t kl_fwd_npad(int64_t N, int64_t V) {
-  const int64_t cap = kl_fwd_token_cap(V);
-  const int64_t n = N <= 0 ? 1 : (N < cap ? N : cap);
-  return (n + 255) / 256 * 256;
-}
+inline int kl_fwd_blocks(int64_t N, int64_t V) { return bwd_blocks_cap(N, kl_fwd_token_cap(V)); }
+inline int64_t kl_fwd_npad(int64_t N, int64_t V) { return bwd_npad_cap(N, kl_fwd_token_cap(V)); }
 
 struct KlLayout {
-  size_t idx, n_active, block_count, tmax, tsum, smax, ssum, wf, wr, xs, xt, total;
+  size_t idx, n_active, block_count, tmax, tsum, smax, ssum, wf, wr, scratch, total;
 };
 
-// idx[N] | n_active | block_count[blocks] | six [J][Npad] statistics | xs, xt [Npad][chunk + 32]
-inline KlLayout kl_fwd_layout(int64_t N, int64_t V) {
+// idx[N] | n_active | block_count[blocks] | six [J][Npad] statistics | scratch, for blocks of at
+// most cap tokens (a multiple of 256)
+inline KlLayout kl_fwd_layout_cap(int64_t N, int64_t V, int64_t cap) {
   KlLayout L;
   const size_t n = (size_t)(N > 0 ? N : 1);
-  const int64_t np = kl_fwd_npad(N, V);
+  const int64_t np = bwd_npad_cap(N, cap);
   const size_t jn = 4 * (size_t)np * (size_t)num_partials(V);
   size_t o = 0;
   L.idx = o;      o = align_up(o + 4 * n, 256);
   L.n_active = o; o = align_up(o + 4, 256);
-  L.block_count = o; o = align_up(o + 4 * (size_t)kl_fwd_blocks(N, V), 256);
+  L.block_count = o; o = align_up(o + 4 * (size_t)bwd_blocks_cap(N, cap), 256);
   L.tmax = o;     o = align_up(o + jn, 256);
   L.tsum = o;     o = align_up(o + jn, 256);
   L.smax = o;     o = align_up(o + jn, 256);
   L.ssum = o;     o = align_up(o + jn, 256);
   L.wf = o;       o = align_up(o + jn, 256);
   L.wr = o;       o = align_up(o + jn, 256);
-  L.xs = o;       o += kl_chunk_bytes_rows(np);
-  L.xt = o;       o += kl_chunk_bytes_rows(np);
+  L.scratch = o;  o += kKlScratchBytes;
   L.total = o;
   return L;
 }
 
-// The backward's workspace, then the two chunk buffers.
+inline KlLayout kl_fwd_layout(int64_t N, int64_t V) {
+  return kl_fwd_layout_cap(N, V, kl_fwd_token_cap(V));
+}
+
+// The block capacity a KL forward workspace of ws bytes gives: the largest multiple of 256
+// tokens, at most N rounded up to 256 and leaving at most 1024 blocks, whose layout fits; 0 if
+// none does.  The default workspace gives kl_fwd_token_cap(V) (or one block for fewer tokens).
+inline int64_t kl_fwd_cap_for_workspace(int64_t N, int64_t V, size_t ws) {
+  const int64_t n = N > 0 ? N : 1;
+  const int64_t top = (n + 255) / 256 * 256;
+  const int64_t low = (n + 1024 * 256 - 1) / (1024 * 256) * 256;  // ceil(n / 1024), to 256
+  for (int64_t cap = top; cap >= low; cap -= 256)
+    if (kl_fwd_layout_cap(N, V, cap).total <= ws) return cap;
+  return 0;
+}
+
+// The KL backward takes the active tokens in the backward's blocks, of a capacity whose
+// buffers fit the budget beside the scratch: 10240 tokens at H_s = 4096.
+inline int64_t kl_bwd_token_cap(int64_t H) {
+  const int64_t c = (int64_t)((kBwdBlockBudget - kKlScratchBytes) /
+                              bwd_bytes_per_token(H > 0 ? H : 1)) / 256 * 256;
+  return c < 256 ? 256 : c;
+}
+
+// The backward's layout for that capacity, then the scratch.
+inline BwdLayout kl_bwd_layout(int64_t N, int64_t H) {
+  return bwd_layout_cap(N, H, kl_bwd_token_cap(H));
+}
 inline size_t kl_bwd_bytes(int64_t N, int64_t H) {
-  return bwd_layout(N, H).total + 2 * kl_chunk_bytes(N, H);
+  return kl_bwd_layout(N, H).total + kKlScratchBytes;
 }
 
 inline rlk_status_t check_kl(const void* hs, const void* Ws, const void* ht, const void* Wt,

@@ -608,10 +608,28 @@ def _check_kl(h_s, W_s, h_t, W_t, mask):
         raise ValueError("mask must be [N]")
 
 
+def kl_fwd_workspace_bytes(N: int, H_s: int, H_t: int, V: int, dtype: int,
+                           block_tokens: Optional[int] = None) -> int:
+    """Workspace bytes of rlk_linear_kl_fwd: the default, or for token blocks of block_tokens (a
+    positive multiple of 256)."""
+    nb = ctypes.c_size_t(0)
+    if block_tokens is None:
+        L.check(L.lib().rlk_linear_kl_fwd_workspace_size(N, H_s, H_t, V, dtype, ctypes.byref(nb)),
+                "rlk_linear_kl_fwd_workspace_size")
+    else:
+        L.check(L.lib().rlk_linear_kl_fwd_workspace_size_for_block(N, H_s, H_t, V, dtype,
+                                                                   int(block_tokens),
+                                                                   ctypes.byref(nb)),
+                "rlk_linear_kl_fwd_workspace_size_for_block")
+    return int(nb.value)
+
+
 def rlk_linear_kl_fwd(h_s, W_s, h_t, W_t, mask, temperature: float,
-                      workspace: Optional[torch.Tensor] = None):
+                      workspace: Optional[torch.Tensor] = None,
+                      block_tokens: Optional[int] = None):
     """Forward and reverse full-vocabulary KL per token; returns (kl_fwd, kl_rev, lse_s, lse_t),
-    each [N] float32."""
+    each [N] float32.  block_tokens: token blocks of that many tokens (a multiple of 256), in a
+    workspace of that size, instead of the default's."""
     mask = _mask_u8(mask)
     _check_kl(h_s, W_s, h_t, W_t, mask)
     N, Hs = h_s.shape
@@ -620,13 +638,13 @@ def rlk_linear_kl_fwd(h_s, W_s, h_t, W_t, mask, temperature: float,
     dt = _dtype_code(h_s)
     dev = h_s.device
     outs = [torch.empty(N, dtype=torch.float32, device=dev) for _ in range(4)]
-    nb = ctypes.c_size_t(0)
-    L.check(L.lib().rlk_linear_kl_fwd_workspace_size(N, Hs, Ht, V, dt, ctypes.byref(nb)),
-            "rlk_linear_kl_fwd_workspace_size")
-    ws = _workspace(int(nb.value), dev, workspace)
+    nb = kl_fwd_workspace_bytes(N, Hs, Ht, V, dt, block_tokens)
+    ws = _workspace(nb, dev, workspace)
+    # the block size follows from the bytes passed: exactly the query's for block_tokens
+    wsb = nb if block_tokens is not None else ws.numel() * ws.element_size()
     L.check(L.lib().rlk_linear_kl_fwd(_vp(h_s), _vp(W_s), _vp(h_t), _vp(W_t), _vp(mask), N, Hs,
                                       Ht, V, dt, float(temperature), *(_vp(o) for o in outs),
-                                      _vp(ws), ws.numel() * ws.element_size(), _stream(dev)),
+                                      _vp(ws), wsb, _stream(dev)),
             "rlk_linear_kl_fwd")
     return tuple(outs)
 

@@ -158,8 +158,23 @@ static void test_layouts() {
       EXPECT(L.total - L.hT <= (size_t)kBwdBlockBudget + 8 * 256);
     }
   EXPECT(bwd_token_cap(4096) == 11008 && bwd_token_cap(7168) == 8960);
-  EXPECT(kl_fwd_token_cap(151936) == 3328 && kl_fwd_blocks(16384, 151936) == 5);
+  EXPECT(kl_fwd_token_cap(151936) == 32512 && kl_fwd_blocks(16384, 151936) == 1);
   EXPECT(kl_fwd_layout(16384, 151936).total <= (size_t)kBwdBlockBudget);
+  // the KL backward: the backward's buffers for blocks of its own capacity, then the scratch,
+  // within the budget but for the index and the block descriptors
+  EXPECT(kl_bwd_token_cap(4096) == 10240);
+  for (int64_t N : {int64_t(0), int64_t(1), int64_t(10240), int64_t(10241), int64_t(16384),
+                    kMaxTokens})
+    for (int64_t H : {int64_t(256), int64_t(4096), int64_t(7168), kMaxHidden}) {
+      const BwdLayout K = kl_bwd_layout(N, H);
+      const int64_t cap = kl_bwd_token_cap(H);
+      EXPECT(cap % 256 == 0 && cap >= 256 && cap <= bwd_token_cap(H));
+      EXPECT((size_t)cap * bwd_bytes_per_token(H) + kKlScratchBytes <= kBwdBlockBudget ||
+             cap == 256);
+      EXPECT(kl_bwd_bytes(N, H) == K.total + kKlScratchBytes && K.total % 256 == 0);
+      EXPECT(kl_bwd_bytes(N, H) - K.hT <= (size_t)kBwdBlockBudget + 8 * 256 || cap == 256);
+      EXPECT((int64_t)bwd_blocks_cap(N, cap) * cap >= N);
+    }
   int max_blocks = 0;
   for (int64_t H = 64; H <= kMaxHidden; H += 64) {
     const int64_t n = std::min<int64_t>(kMaxTokens, kMaxHiddenStateBytes / (2 * H));
@@ -181,14 +196,16 @@ static void test_layouts() {
     for (int64_t V : {int64_t(1), int64_t(151936), kMaxVocab}) {
       const KlLayout K = kl_fwd_layout(N, V);
       const int64_t np = kl_fwd_npad(N, V), cap = kl_fwd_token_cap(V);
-      const size_t jn = 4 * (size_t)np * (size_t)num_partials(V), c = kl_chunk_bytes_rows(np);
+      const size_t jn = 4 * (size_t)np * (size_t)num_partials(V);
       expect_layout({K.idx, K.n_active, K.block_count, K.tmax, K.tsum, K.smax, K.ssum, K.wf,
-                     K.wr, K.xs, K.xt},
-                    {4 * n, 4, 4 * (size_t)kl_fwd_blocks(N, V), jn, jn, jn, jn, jn, jn, c, c},
+                     K.wr, K.scratch},
+                    {4 * n, 4, 4 * (size_t)kl_fwd_blocks(N, V), jn, jn, jn, jn, jn, jn,
+                     kKlScratchBytes},
                     K.total);
       // the KL forward's buffers hold one block of its own capacity, within the budget
       EXPECT(cap % 256 == 0 && cap >= 256 && np <= cap && np % 256 == 0);
-      EXPECT((size_t)cap * kl_fwd_bytes_per_token(V) <= kBwdBlockBudget || cap == 256);
+      EXPECT((size_t)cap * kl_fwd_bytes_per_token(V) + kKlScratchBytes <= kBwdBlockBudget ||
+             cap == 256);
       EXPECT(K.total - K.tmax <= (size_t)kBwdBlockBudget + 8 * 256 || cap == 256);
     }
   }

@@ -395,16 +395,28 @@ def test_kl_argument_errors(L):
     assert fwd(T=0.0) == E.RLK_ERROR_INVALID_VALUE
     assert fwd(wsb=1000) == E.RLK_ERROR_WORKSPACE
     st, b = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 16384, 4096, 2048, 151936, 0)
-    # six [J][Npad] statistics and two fp32 chunks for one token block of the forward's own
-    # capacity (3328 tokens at V = 151936): under 1e9 bytes
-    import re
-    info = lib.rlk_build_info().decode()
-    chunk = int(re.search(r"bwd chunk (\d+)", info).group(1))
-    assert st == 0 and b >= 6 * 4 * 3328 * 1187 + 2 * 4 * 3328 * chunk
-    assert b <= 1_000_000_000 + 4 * 16384 + 8192
+    # six [J][Npad] statistics for one token block (all 16384 tokens fit the forward's own
+    # capacity of 32512 at V = 151936) and the 64 MiB scratch of the tile kernel: under 1e9 bytes
+    assert st == 0 and b >= 6 * 4 * 16384 * 1187 + (64 << 20)
+    assert b <= 1_000_000_000
     # past one token block only the index grows with N
-    st2, b2 = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 32768, 4096, 2048, 151936, 0)
-    assert st2 == 0 and b2 - b <= 4 * 16384 + 512
+    st1, b1 = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 65536, 4096, 2048, 151936, 0)
+    st2, b2 = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 131072, 4096, 2048, 151936, 0)
+    assert st1 == st2 == 0 and b1 <= 1_000_000_000 + 4 * 65536 + 8192
+    assert b2 - b1 <= 4 * 65536 + 512
+    # a workspace sized for 3584-token blocks (six at N = 20000, V = 2000) is smaller than the
+    # default's one block; block sizes are positive multiples of 256, at most 1024 blocks
+    sd = _ws(lib, "rlk_linear_kl_fwd_workspace_size", 20000, 256, 128, 2000, 0)
+    sb = _ws(lib, "rlk_linear_kl_fwd_workspace_size_for_block", 20000, 256, 128, 2000, 0, 3584)
+    assert sd[0] == sb[0] == 0 and sb[1] < sd[1]
+    assert sb[1] >= 6 * 4 * 3584 * 16 + (64 << 20)
+    for bad in (0, -256, 300):
+        assert _ws(lib, "rlk_linear_kl_fwd_workspace_size_for_block", 20000, 256, 128, 2000, 0,
+                   bad)[0] == E.RLK_ERROR_INVALID_VALUE
+    assert _ws(lib, "rlk_linear_kl_fwd_workspace_size_for_block", 1 << 20, 256, 256, 2000, 0,
+               256)[0] == E.RLK_ERROR_UNSUPPORTED
+    # a workspace below the smallest blocks' is refused before anything is launched
+    assert fwd(wsb=sb[1] // 4) == E.RLK_ERROR_WORKSPACE
     # a vocabulary of 2^22 entries leaves 256 tokens per block: 2^22 tokens would need more than
     # 1024 blocks
     assert _ws(lib, "rlk_linear_kl_fwd_workspace_size", (1 << 22) - 256, 256, 256, 1 << 22,
@@ -424,3 +436,9 @@ def test_kl_argument_errors(L):
     assert bwd(cf=None, cr=FAKE, wsb=1000) == E.RLK_ERROR_WORKSPACE
     assert _ws(lib, "rlk_linear_kl_bwd_workspace_size", 8, 64, 64, 1000, 0)[0] == \
         E.RLK_ERROR_UNSUPPORTED
+    # the backward's buffers for blocks of 10240 tokens (H_s = 4096) and the scratch: within
+    # 1e9 bytes but for the index, and no growth past one block but the index
+    st, b = _ws(lib, "rlk_linear_kl_bwd_workspace_size", 16384, 4096, 4096, 151936, 0)
+    assert st == 0 and b <= 1_000_000_000 + 4 * 16384 + 8192
+    st2, b2 = _ws(lib, "rlk_linear_kl_bwd_workspace_size", 65536, 4096, 4096, 151936, 0)
+    assert st2 == 0 and b2 - b <= 4 * (65536 - 16384) + 8 * 8 + 512

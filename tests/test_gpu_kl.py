@@ -37,10 +37,11 @@ def _dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
 
-def _fwd(w, ht, Wt, mask=None):
+def _fwd(w, ht, Wt, mask=None, block=None):
     import linear_selected_token_amd as rlk
     m = w.mask if mask is None else mask
-    out = rlk.rlk_linear_kl_fwd(_dev(w.h), _dev(w.W), _dev(ht), _dev(Wt), _dev(m), w.T)
+    out = rlk.rlk_linear_kl_fwd(_dev(w.h), _dev(w.W), _dev(ht), _dev(Wt), _dev(m), w.T,
+                                block_tokens=block)
     torch.cuda.synchronize()
     return [o.cpu().numpy() for o in out]
 
@@ -50,8 +51,8 @@ def _lse(h64, W64, T, rows):
     return oracle.logsumexp_rows(z)
 
 
-def _check_fwd(w, ht, Wt, rows=None, tol=MAX_ABS_DLOGP):
-    kf, kr, ls, lt = _fwd(w, ht, Wt)
+def _check_fwd(w, ht, Wt, rows=None, tol=MAX_ABS_DLOGP, block=None):
+    kf, kr, ls, lt = _fwd(w, ht, Wt, block=block)
     hs64, Ws64, ht64, Wt64 = (wl.as_f64(x) for x in (w.h, w.W, ht, Wt))
     act = w.mask.astype(bool)
     if rows is None:
@@ -214,14 +215,18 @@ def test_bwd_qwen_head_sampled():
 
 
 def test_token_blocks_forward_and_backward():
-    # 18750 active tokens of 20000: the KL forward's own blocks (3584 tokens at V = 2000, six
-    # blocks) and the backward's (14848 tokens at H = 256, two blocks), both directions against
-    # the oracle
+    # 18750 active tokens of 20000: the KL forward in blocks of 3584 tokens (six blocks, set by
+    # the workspace) and in its default one block, and the backward's own blocks (13824 tokens
+    # at H = 256 beside the scratch, two blocks), both directions against the oracle
     w = wl.make(wl.scaled_spec(5, N=20000, H=256, V=2000, n_seq=40, len_lo=400, len_hi=600,
                                seed=161, prompt="none", T=0.8))
     w.mask[::16] = 0
     ht, Wt = _teacher(w, 128, 162)
-    _check_fwd(w, ht, Wt)
+    kb = _check_fwd(w, ht, Wt, block=3584)
+    k1 = _fwd(w, ht, Wt)
+    mism = sum(int((bits(a) != bits(b)).sum()) for a, b in zip(kb, k1))
+    flush(f"  KL forward, six blocks against one: {mism} mismatches")
+    assert mism == 0
     c = np.random.default_rng(164).uniform(0.5, 1.5, w.N).astype(np.float32)
     for reverse in (False, True):
         dh, dW = _bwd(w, ht, Wt, reverse, c)
