@@ -159,6 +159,23 @@ static void test_layouts() {
     }
   EXPECT(bwd_token_cap(4096) == 11008 && bwd_token_cap(7168) == 8960);
   EXPECT(kl_fwd_token_cap(151936) == 32512 && kl_fwd_blocks(16384, 151936) == 1);
+  // the KL forward's block capacity follows from the workspace: the default workspace gives the
+  // default capacity (one block for fewer tokens), a workspace for any multiple of 256 that
+  // capacity, and too small a workspace none
+  for (int64_t N : {int64_t(1), int64_t(255), int64_t(20000), int64_t(65536), int64_t(1) << 20})
+    for (int64_t V : {int64_t(1), int64_t(2000), int64_t(151936)}) {
+      const int64_t top = (N + 255) / 256 * 256, cap = kl_fwd_token_cap(V);
+      if (bwd_blocks_cap(N, cap) <= 1024)
+        EXPECT(kl_fwd_cap_for_workspace(N, V, kl_fwd_layout(N, V).total) == std::min(cap, top));
+      for (int64_t b : {int64_t(256), int64_t(3584), int64_t(8192)}) {
+        if (b > top || bwd_blocks_cap(N, b) > 1024) continue;
+        EXPECT(kl_fwd_cap_for_workspace(N, V, kl_fwd_layout_cap(N, V, b).total) == b);
+        EXPECT(kl_fwd_cap_for_workspace(N, V, kl_fwd_layout_cap(N, V, b).total - 1) < b);
+      }
+      EXPECT(kl_fwd_cap_for_workspace(N, V, kKlScratchBytes) == 0);
+      EXPECT(kl_fwd_cap_for_workspace(N, V, (size_t)1 << 40) == top ||
+             bwd_blocks_cap(N, top) > 1024);
+    }
   EXPECT(kl_fwd_layout(16384, 151936).total <= (size_t)kBwdBlockBudget);
   // the KL backward: the backward's buffers for blocks of its own capacity, then the scratch,
   // within the budget but for the index and the block descriptors
