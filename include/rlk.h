@@ -220,23 +220,25 @@ rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* ta
  *   lse  [N] float  out (required: the gradient pass reads it back)
  *   dh   [N,H] float out, overwritten: dL/dh (inactive rows 0), 16-byte aligned
  *   dW   [V,H] float out, overwritten: dL/dW
- *   workspace: at least rlk_linear_logp_fwd_bwd_workspace_size bytes.  The active tokens are
- *   taken in blocks of equal size (the last shorter) of at most the largest multiple of 256
- *   tokens whose buffers fit 1e9 bytes: per token a row of roundup(V, 256) + 64 two-byte
- *   entries, the column statistics (8 bytes per 128 entries) and 6 H + 12 bytes, i.e. 2816
- *   tokens at H = 4096, V = 151936 (0.96 GB), so the workspace does not grow past one block.
+ *   workspace: rlk_linear_logp_fwd_bwd_workspace_size bytes by default.  The active tokens
+ *   are taken in blocks of equal size (the last shorter) of at most the largest multiple of 256
+ *   tokens whose buffers fit the workspace given: per token a row of roundup(V, 256) + 64
+ *   two-byte entries, the column statistics (8 bytes per 128 entries) and 6 H + 12 bytes.  The
+ *   default size is that of blocks which fit 1e9 bytes, 2816 tokens at H = 4096, V = 151936
+ *   (0.96 GB), so it does not grow past one block; RLK_ERROR_WORKSPACE when not even 256-token
+ *   blocks (at most 1024 of them) fit.
  * A token's logp, lse and dL/dh row are the same bits in any batch, whatever block it falls in;
- * dL/dW is the sum of the blocks' sums in ascending block order.  Returns
- * RLK_ERROR_UNSUPPORTED when N would need more than 1024 blocks. */
+ * dL/dW is the sum of the blocks' sums in ascending block order.  The size query returns
+ * RLK_ERROR_UNSUPPORTED when N would need more than 1024 blocks of the default size. */
 rlk_status_t rlk_linear_logp_fwd_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
                                                     size_t* bytes);
-/* A workspace larger than rlk_linear_logp_fwd_bwd_workspace_size buys larger token blocks: the
- * call takes blocks of the largest multiple of 256 tokens (past the budget's) whose buffers fit
- * workspace_bytes, at most one block for all N tokens.  This query gives the bytes for blocks
- * of at least block_tokens tokens (rounded up to 256; block_tokens >= N: one block), e.g.
+/* The workspace sets the block size: a larger one than rlk_linear_logp_fwd_bwd_workspace_size
+ * buys fewer, larger blocks (at most one for all N tokens), a smaller one trades speed for
+ * memory with more, smaller blocks.  This query gives the bytes for blocks of block_tokens
+ * tokens (rounded up to 256; 0: the default's blocks; block_tokens >= N: one block), e.g.
  * 3.38 GB for blocks of 9984 tokens at N = 16384, H = 4096, V = 151936 (one block for up to
- * 9984 active tokens).  logp, lse and dL/dh do not depend on the block size; dL/dW sums the
- * blocks in ascending order, so its rounding does. */
+ * 9984 active tokens), or RLK_ERROR_UNSUPPORTED past 1024 blocks.  logp, lse and dL/dh do not
+ * depend on the block size; dL/dW sums the blocks in ascending order, so its rounding does. */
 rlk_status_t rlk_linear_logp_fwd_bwd_workspace_size_for_block(int64_t N, int64_t H, int64_t V,
                                                               int dtype, int64_t block_tokens,
                                                               size_t* bytes);
@@ -254,7 +256,7 @@ rlk_status_t rlk_linear_logp_fwd_bwd(const void* h, const void* W, const int32_t
  *   ent_coef [N] float  c_t;   entropy [N] float  out
  *   the rest as for rlk_linear_logp_fwd_bwd; the workspace (and so the token blocks) holds one
  *   more statistic per 128 vocabulary entries: rlk_linear_logp_fwd_bwd_entropy_workspace_size
- *   bytes at least (still 2816 tokens per block at H = 4096, V = 151936). */
+ *   bytes by default (still 2816 tokens per block at H = 4096, V = 151936). */
 rlk_status_t rlk_linear_logp_fwd_bwd_entropy_workspace_size(int64_t N, int64_t H, int64_t V,
                                                             int dtype, size_t* bytes);
 rlk_status_t rlk_linear_logp_fwd_bwd_entropy(const void* h, const void* W,
@@ -280,9 +282,9 @@ rlk_status_t rlk_linear_logp_fwd_bwd_entropy(const void* h, const void* W,
  *              sums may be NULL)
  *   dh, dW     out: gradients of sum_t loss_t (dL/dlogp_t = -bwd_adv_t), as rlk_linear_logp_fwd_bwd
  *              forms them
- *   workspace: at least rlk_linear_ppo_fwd_bwd_workspace_size bytes, never NULL (the loss
- *              fragment's partial sums, then the fused call's workspace; a larger one buys
- *              larger token blocks as there). */
+ *   workspace: rlk_linear_ppo_fwd_bwd_workspace_size bytes by default, never NULL (the loss
+ *              fragment's partial sums, then the fused call's workspace, whose size sets the
+ *              token blocks as there). */
 rlk_status_t rlk_linear_ppo_fwd_bwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype,
                                                    size_t* bytes);
 rlk_status_t rlk_linear_ppo_fwd_bwd(const void* h, const void* W, const int32_t* targets,

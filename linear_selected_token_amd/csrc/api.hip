@@ -208,7 +208,7 @@ rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, con
   }
   int grid = 0;
   if (persistent_grid(&grid) != hipSuccess) return RLK_ERROR_DEVICE;
-  // the budget's block capacity, or a larger one that the given workspace holds
+  // the largest block capacity the given workspace holds (check_fused made sure one does)
   const int64_t cap64 = fused_cap_for_workspace(N, H, V, workspace_bytes, ent);
   const FusedLayout L = fused_layout_cap(N, H, V, cap64, ent);
   const int np = (int)fused_npad_cap(N, cap64);
@@ -831,9 +831,10 @@ rlk_status_t rlk_linear_logp_fwd_bwd_workspace_size_for_block(int64_t N, int64_t
   if (dtype != RLK_BF16 || H % 256 != 0 || fused_blocks(N, H, V) > 1024)
     return RLK_ERROR_UNSUPPORTED;
   const int64_t n = N > 0 ? N : 1;
+  if (block_tokens == 0) block_tokens = fused_token_cap(H, V);  // the default's blocks
   const int64_t want = ((block_tokens < n ? block_tokens : n) + 255) / 256 * 256;
-  const int64_t c0 = fused_token_cap(H, V);
-  *bytes = fused_layout_cap(N, H, V, want > c0 ? want : c0).total;
+  if (bwd_blocks_cap(N, want) > 1024) return RLK_ERROR_UNSUPPORTED;
+  *bytes = fused_layout_cap(N, H, V, want).total;
   return RLK_SUCCESS;
 }
 

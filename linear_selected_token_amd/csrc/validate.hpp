@@ -251,21 +251,18 @@ inline FusedLayout fused_layout(int64_t N, int64_t H, int64_t V, bool ent = fals
   return fused_layout_cap(N, H, V, fused_token_cap(H, V, ent), ent);
 }
 
-// The block capacity a workspace of ws_bytes allows: the budget's capacity, or the largest
-// multiple of 256 tokens past it whose layout still fits ws_bytes (at most N rounded up to 256:
-// one block).  A larger workspace only buys fewer, larger blocks.
+// The block capacity a workspace of ws_bytes allows: the largest multiple of 256 tokens, at most
+// N rounded up to 256 (one block) and leaving at most 1024 blocks, whose layout fits ws_bytes;
+// 0 if none does.  The budget's workspace gives the budget's capacity; a larger one buys fewer,
+// larger blocks, a smaller one more, smaller blocks.
 inline int64_t fused_cap_for_workspace(int64_t N, int64_t H, int64_t V, size_t ws_bytes,
                                        bool ent = false) {
-  const int64_t c0 = fused_token_cap(H, V, ent);
-  const int64_t top = ((N > 0 ? N : 1) + 255) / 256 * 256;
-  if (top <= c0 || fused_layout_cap(N, H, V, c0 + 256, ent).total > ws_bytes) return c0;
-  int64_t lo = c0 + 256, hi = top;  // lo fits; find the largest fitting multiple of 256
-  while (lo < hi) {
-    const int64_t mid = (lo / 256 + (hi / 256 - lo / 256 + 1) / 2) * 256;
-    if (fused_layout_cap(N, H, V, mid, ent).total <= ws_bytes) lo = mid;
-    else hi = mid - 256;
-  }
-  return lo;
+  const int64_t n = N > 0 ? N : 1;
+  const int64_t top = (n + 255) / 256 * 256;
+  const int64_t low = (n + 1024 * 256 - 1) / (1024 * 256) * 256;  // ceil(n / 1024), to 256
+  for (int64_t cap = top; cap >= low; cap -= 256)
+    if (fused_layout_cap(N, H, V, cap, ent).total <= ws_bytes) return cap;
+  return 0;
 }
 
 // Workspace of the log-prob from existing logits: idx[N] | n_active.
@@ -361,7 +358,7 @@ inline rlk_status_t check_fused(const void* h, const void* W, const int32_t* tar
       !aligned(logp, 4) || !aligned(lse, 4) || !aligned(dh, 16) || !aligned(dW, 4) ||
       !aligned(ws, 256))
     return RLK_ERROR_UNSUPPORTED;
-  if (ws_bytes < fused_layout(N, H, V, ent).total) return RLK_ERROR_WORKSPACE;
+  if (fused_cap_for_workspace(N, H, V, ws_bytes, ent) == 0) return RLK_ERROR_WORKSPACE;
   return RLK_SUCCESS;
 }
 

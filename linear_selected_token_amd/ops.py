@@ -81,6 +81,14 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+def _sized_workspace(default_bytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    """For calls whose token blocks follow the workspace's size: the caller's workspace as given
+    (the library refuses one too small for its smallest blocks), else one of the default size."""
+    if ws is not None:
+        return ws
+    return torch.empty(max(default_bytes, 256), dtype=torch.uint8, device=device)
+
+
 def rlk_linear_logp_fwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                         mask: torch.Tensor, temperature: float,
                         workspace: Optional[torch.Tensor] = None,
@@ -261,8 +269,8 @@ def fwd_bwd_workspace_bytes(N: int, H: int, V: int, dtype: int) -> int:
 
 def fwd_bwd_workspace_bytes_for_block(N: int, H: int, V: int, dtype: int,
                                       block_tokens: int) -> int:
-    """Workspace bytes with which rlk_linear_logp_fwd_bwd takes blocks of at least block_tokens
-    tokens (block_tokens >= N: one block)."""
+    """Workspace bytes with which rlk_linear_logp_fwd_bwd takes token blocks of block_tokens
+    tokens, rounded up to 256 (0: the default's blocks; N or more: one block)."""
     out = ctypes.c_size_t(0)
     L.check(L.lib().rlk_linear_logp_fwd_bwd_workspace_size_for_block(N, H, V, dtype, block_tokens,
                                                                      ctypes.byref(out)),
@@ -290,7 +298,7 @@ def rlk_linear_logp_fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Ten
         dh = torch.empty((N, H), dtype=torch.float32, device=h.device)
     if dW is None:
         dW = torch.empty((V, H), dtype=torch.float32, device=h.device)
-    ws = _workspace(fwd_bwd_workspace_bytes(N, H, V, dt), h.device, workspace)
+    ws = _sized_workspace(fwd_bwd_workspace_bytes(N, H, V, dt), h.device, workspace)
     L.check(L.lib().rlk_linear_logp_fwd_bwd(_vp(h), _vp(W), _vp(targets), _vp(mask), N, H, V, dt,
                                             float(temperature), _vp(adv), _vp(logp), _vp(lse),
                                             _vp(dh), _vp(dW), _vp(ws),
@@ -441,7 +449,7 @@ def rlk_linear_logp_fwd_bwd_entropy(h: torch.Tensor, W: torch.Tensor, targets: t
         dh = torch.empty((N, H), **f32)
     if dW is None:
         dW = torch.empty((V, H), **f32)
-    ws = _workspace(fwd_bwd_entropy_workspace_bytes(N, H, V, dt), h.device, workspace)
+    ws = _sized_workspace(fwd_bwd_entropy_workspace_bytes(N, H, V, dt), h.device, workspace)
     L.check(L.lib().rlk_linear_logp_fwd_bwd_entropy(_vp(h), _vp(W), _vp(targets), _vp(mask), N, H,
                                                     V, dt, float(temperature), _vp(adv),
                                                     _vp(ent_coef), _vp(logp), _vp(lse), _vp(ent),
@@ -484,7 +492,7 @@ def rlk_linear_ppo_fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tens
         dh = torch.empty((N, H), **f32)
     if dW is None:
         dW = torch.empty((V, H), **f32)
-    ws = _workspace(ppo_fwd_bwd_workspace_bytes(N, H, V, dt), h.device, workspace)
+    ws = _sized_workspace(ppo_fwd_bwd_workspace_bytes(N, H, V, dt), h.device, workspace)
     L.check(L.lib().rlk_linear_ppo_fwd_bwd(_vp(h), _vp(W), _vp(targets), _vp(mask), N, H, V, dt,
                                            float(temperature), _vp(old_logp), _vp(ref_logp),
                                            _vp(adv), float(eps_lo), float(eps_hi), float(beta),
@@ -639,7 +647,8 @@ def rlk_linear_kl_fwd(h_s, W_s, h_t, W_t, mask, temperature: float,
     dev = h_s.device
     outs = [torch.empty(N, dtype=torch.float32, device=dev) for _ in range(4)]
     nb = kl_fwd_workspace_bytes(N, Hs, Ht, V, dt, block_tokens)
-    ws = _workspace(nb, dev, workspace)
+    ws = _workspace(nb, dev, workspace) if block_tokens is not None else \
+        _sized_workspace(nb, dev, workspace)
     # the block size follows from the bytes passed: exactly the query's for block_tokens
     wsb = nb if block_tokens is not None else ws.numel() * ws.element_size()
     L.check(L.lib().rlk_linear_kl_fwd(_vp(h_s), _vp(W_s), _vp(h_t), _vp(W_t), _vp(mask), N, Hs,

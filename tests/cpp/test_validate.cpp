@@ -268,13 +268,15 @@ static void test_fused() {
   }
   const size_t ws = fused_layout(16384, 4096, 151936).total;
   EXPECT(ws <= (size_t)kBwdBlockBudget);
-  // a larger workspace gives the largest capacity (a multiple of 256 past the budget's, at most
-  // one block) whose layout fits it
+  // a workspace gives the largest capacity (a multiple of 256, at most one block) whose layout
+  // fits it: the budget's size the budget's capacity, a larger one more, a smaller one less,
+  // and below the 256-token blocks' size none
   for (int64_t N : {int64_t(300), int64_t(9831), int64_t(16384), int64_t(100000)}) {
     const int64_t c0 = fused_token_cap(4096, 151936), top = (N + 255) / 256 * 256;
-    EXPECT(fused_cap_for_workspace(N, 4096, 151936, fused_layout(N, 4096, 151936).total) == c0);
-    EXPECT(fused_cap_for_workspace(N, 4096, 151936, size_t(1) << 62) == (top > c0 ? top : c0));
-    for (int64_t c = c0 + 256; c <= top && c <= c0 + 256 * 40; c += 256) {
+    EXPECT(fused_cap_for_workspace(N, 4096, 151936, fused_layout(N, 4096, 151936).total) ==
+           std::min(c0, top));
+    EXPECT(fused_cap_for_workspace(N, 4096, 151936, size_t(1) << 62) == top);
+    for (int64_t c = 256; c <= top && c <= c0 + 256 * 40; c += 256) {
       const size_t t = fused_layout_cap(N, 4096, 151936, c).total;
       EXPECT(fused_cap_for_workspace(N, 4096, 151936, t) == c);
       EXPECT(fused_cap_for_workspace(N, 4096, 151936, t - 1) == c - 256);
@@ -286,7 +288,9 @@ static void test_fused() {
                        PT<float>(A), P(A), bytes);
   };
   EXPECT(call(A, A, A, RLK_BF16, 4096, ws) == RLK_SUCCESS);
-  EXPECT(call(A, A, A, RLK_BF16, 4096, ws - 1) == RLK_ERROR_WORKSPACE);
+  EXPECT(call(A, A, A, RLK_BF16, 4096, ws - 1) == RLK_SUCCESS);  // smaller blocks
+  EXPECT(call(A, A, A, RLK_BF16, 4096, fused_layout_cap(16384, 4096, 151936, 256).total - 1) ==
+         RLK_ERROR_WORKSPACE);
   EXPECT(call(0, A, A, RLK_BF16, 4096, ws) == RLK_ERROR_INVALID_VALUE);
   EXPECT(call(A, 0, A, RLK_BF16, 4096, ws) == RLK_ERROR_INVALID_VALUE);
   EXPECT(call(A, A, 0, RLK_BF16, 4096, ws) == RLK_ERROR_INVALID_VALUE);

@@ -175,13 +175,14 @@ def test_fused_workspace_and_argument_errors(L):
     assert _ws(lib, "rlk_linear_logp_fwd_bwd_workspace_size", (1 << 22) - 256, 256, 1 << 22,
                L.RLK_BF16)[0] == E.RLK_ERROR_UNSUPPORTED
 
-    # a larger workspace buys larger blocks: the size for blocks of block_tokens grows with it,
-    # equals the budget's size up to the budget's capacity and stops growing at one block
+    # the workspace sets the block size: the size for blocks of block_tokens grows with it (0:
+    # the budget's blocks), and stops growing at one block
     sizes = [_ws(lib, "rlk_linear_logp_fwd_bwd_workspace_size_for_block", 16384, 4096, 151936,
-                 L.RLK_BF16, bt) for bt in (0, 2816, 2817, 5000, 9831, 16384, 1 << 30)]
+                 L.RLK_BF16, bt) for bt in (0, 2816, 2817, 5000, 9831, 16384, 1 << 30, 256, 300)]
     assert all(st == 0 for st, _ in sizes)
     v = [x for _, x in sizes]
     assert v[0] == v[1] == a and a < v[2] <= v[3] < v[4] < v[5] == v[6]
+    assert v[7] < v[8] < a  # 256-token blocks, and 300 rounded up to 512
     assert v[4] >= 9984 * (2 * 152128 + 8 * 1187 + 6 * 4096)
     assert _ws(lib, "rlk_linear_logp_fwd_bwd_workspace_size_for_block", 16384, 4096, 151936,
                L.RLK_BF16, -1)[0] == E.RLK_ERROR_INVALID_VALUE

@@ -235,6 +235,38 @@ def test_larger_workspace_one_block():
     _sampled_compare(w, lp2, ls2, dh2, dW2, 164, n_tok=8)
 
 
+MANY = wl.scaled_spec(5, N=3200, H=256, V=1000, n_seq=8, len_lo=200, len_hi=600, seed=175, T=0.8)
+
+
+def test_many_small_blocks():
+    # a workspace for 256-token blocks (seven blocks here, against one by default): logp, lse and
+    # every dL/dh row keep their bits, dL/dW (a sum over the blocks) agrees with the one-block
+    # result to rounding and with the oracle row by row
+    import linear_selected_token_amd as rlk
+    w = wl.make(MANY)
+    d = upload(w)
+    lp1, ls1, dh1, dW1 = run_fused(w, d)
+    nb = rlk.fwd_bwd_workspace_bytes_for_block(w.N, w.H, w.V, 0, 256)
+    assert nb < rlk.fwd_bwd_workspace_bytes(w.N, w.H, w.V, 0)
+    ws = torch.empty(nb, dtype=torch.uint8, device=d["h"].device)
+    lp2, ls2, dh2, dW2 = rlk.rlk_linear_logp_fwd_bwd(d["h"], d["W"], d["targets"], d["mask"], w.T,
+                                                     d["adv"], workspace=ws)
+    torch.cuda.synchronize()
+    nblk = -(-w.n_active // 256)
+    flush(f"  {w.n_active} active: {nblk} blocks of 256 tokens in {nb / 1e6:.1f} MB against one")
+    assert nblk >= 7
+    assert torch.equal(lp1.view(torch.int32), lp2.view(torch.int32))
+    assert torch.equal(ls1.view(torch.int32), ls2.view(torch.int32))
+    assert torch.equal(dh1.view(torch.int32), dh2.view(torch.int32))
+    e = rel_l2(dW2.cpu().numpy(), dW1.cpu().numpy())
+    flush(f"  dW {nblk} blocks vs one: relL2 {e:.3e}")
+    assert e <= 1e-5
+    h64, W64 = oracle_inputs(w)
+    odh, odW = oracle.linear_logp_grads(h64, W64, w.targets, w.mask, w.T, w.adv)
+    assert_rows("fused dW over many blocks (every vocabulary row)", dW2.cpu().numpy(), odW)
+    assert_tiles("fused dW over many blocks", dW2.cpu().numpy(), odW)
+
+
 def test_config5_full_size_sampled():
     flush("config 5 fused: generating inputs")
     w = wl.make(5)
@@ -344,6 +376,35 @@ def test_ppo_fused_token_blocks():
     rows = np.unique(np.concatenate([act[edge_rows(act.size, 256, 1)], r.choice(act, 8, False)]))
     vr = np.unique(np.concatenate([w.targets[act[:4]], r.integers(0, w.V, 12)]))
     _check_ppo(w, 172, oracle_rows=(rows, vr))
+
+
+def test_ppo_fused_many_small_blocks():
+    # 256-token blocks: each block's loss fragment runs on its own tokens, so every per-token
+    # output and dL/dh row keeps the one-block call's bits; dL/dW agrees to rounding
+    import linear_selected_token_amd as rlk
+    w = wl.make(MANY)
+    d = upload(w)
+    dev = d["h"].device
+    old, ref = _ppo_inputs(w, d, 176)
+    old_t, ref_t = torch.from_numpy(old).to(dev), torch.from_numpy(ref).to(dev)
+    scale = 1.0 / int(w.mask.sum())
+    args = (d["h"], d["W"], d["targets"], d["mask"], w.T, old_t, ref_t, d["adv"], 0.2, 0.2, 0.05,
+            scale)
+    one = rlk.rlk_linear_ppo_fwd_bwd(*args)
+    loss_bytes = (rlk.ppo_fwd_bwd_workspace_bytes(w.N, w.H, w.V, 0) -
+                  rlk.fwd_bwd_workspace_bytes(w.N, w.H, w.V, 0))
+    nb = loss_bytes + rlk.fwd_bwd_workspace_bytes_for_block(w.N, w.H, w.V, 0, 256)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    many = rlk.rlk_linear_ppo_fwd_bwd(*args, workspace=ws)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("logp", "lse", "loss", "bwd_adv", "ratio", "sums", "dh"), many[:7],
+                          one[:7]):
+        ai = a.view(torch.int64) if a.dtype == torch.float64 else a.view(torch.int32)
+        bi = b.view(torch.int64) if b.dtype == torch.float64 else b.view(torch.int32)
+        assert torch.equal(ai, bi), name
+    e = rel_l2(many[7].cpu().numpy(), one[7].cpu().numpy())
+    flush(f"  fused PPO, 256-token blocks vs one block: dW relL2 {e:.3e}")
+    assert e <= 1e-5
 
 
 def test_ppo_fused_all_masked():
