@@ -68,7 +68,9 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
   const int Na = *a.n_active;
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nVocTiles = (a.V + kTile - 1) / kTile;
-  const int band = nTokTiles < 8 ? nTokTiles : 8;
+  // bands of 8 token tiles; up to 12 token tiles (a token block of the fused call) take one
+  // band, instead of a band of 8 and a narrow remainder band whose work-groups share few panels
+  const int band = nTokTiles <= 12 ? nTokTiles : 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const size_t row_bytes = (size_t)a.H * (kBF16 ? 2 : 4);
