@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(BwdArgs a, int c0) {
   const int vc = min(kBwdChunk, a.V - c0);  // vocabulary entries in this chunk
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nVocTiles = (vc + kTile - 1) / kTile;
-  const int band = nTokTiles < 8 ? nTokTiles : 8;
+  const int band = nTokTiles <= 12 ? nTokTiles : 8;  // as the forward tile kernel's order
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const size_t row_bytes = (size_t)a.H * 2;

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void kl_tiles_kernel(KlTileArgs a) {
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nVocTiles = (a.V + kTile - 1) / kTile;
   const int n_tiles = nTokTiles * nVocTiles;
-  const int band = nTokTiles < 8 ? nTokTiles : 8;
+  const int band = nTokTiles <= 12 ? nTokTiles : 8;  // as the forward tile kernel's order
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const size_t es = kBF16 ? 2 : 4;
