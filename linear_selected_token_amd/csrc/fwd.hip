@@ -18,6 +18,8 @@
 // statistics depend only on its own h row, the W tile and the fixed K order; the lane and
 // register order of every reduction is the same for every token position; the merge walks
 // the columns in the same fixed association for every token.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mainloop.hpp"
@@ -135,96 +137,103 @@ __global__ __launch_bounds__(kThreads) void fwd_tiles_kernel(FwdTileArgs a) {
       }
       // Column maximum in log2 units.  c2 > 0 and rounding is monotonic, so the maximum of
       // the scaled logits is the scaled maximum of the accumulators: take it on the raw
-      // values (entries past the vocabulary set to -inf in place), then form each exponent
-      // with one fma.
-      if (tail) {
+      // values (entries past the vocabulary read as -inf), then form each exponent with one
+      // fma.  The -inf is applied where a value is read, and only in the quadrant that holds
+      // the vocabulary's end: the body is instantiated with and without the mask (written
+      // into the accumulators in place, it made the store-code epilogues spill).
+      const int lim = a.V - vq - half4;  // local rows >= lim are past the vocabulary
+      auto column = [&](auto masked) __attribute__((always_inline)) {
+        auto val = [&](int i, int r) __attribute__((always_inline)) -> float {
+          const float x = acc.c[i][j][r];
+          if constexpr (decltype(masked)::value)
+            return 32 * i + 8 * (r >> 2) + (r & 3) >= lim ? -INFINITY : x;
+          else
+            return x;
+        };
+        float am = -INFINITY;
 #pragma unroll
         for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (vq + acc_row(i, r, lane) >= a.V) acc.c[i][j][r] = -INFINITY;
-      }
-      float am = -INFINITY;
+          for (int r = 0; r < 16; ++r) am = fmaxf(am, val(i, r));
+        am = fmaxf(am, __shfl_xor(am, 32));
+        const float mx = am * c2;
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+        float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
 #pragma unroll
-      for (int i = 0; i < kBlkA; ++i)
+        for (int i = 0; i < kBlkA; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) am = fmaxf(am, acc.c[i][j][r]);
-      am = fmaxf(am, __shfl_xor(am, 32));
-      const float mx = am * c2;
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-      float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
+          for (int r = 0; r < 16; r += 4) {
+            const float d0 = __builtin_fmaf(val(i, r + 0), c2, -mx);
+            const float d1 = __builtin_fmaf(val(i, r + 1), c2, -mx);
+            const float d2 = __builtin_fmaf(val(i, r + 2), c2, -mx);
+            const float d3 = __builtin_fmaf(val(i, r + 3), c2, -mx);
+            const float e0 = __builtin_amdgcn_exp2f(d0);
+            const float e1 = __builtin_amdgcn_exp2f(d1);
+            const float e2 = __builtin_amdgcn_exp2f(d2);
+            const float e3 = __builtin_amdgcn_exp2f(d3);
+            s0 += e0;
+            s1 += e1;
+            s2 += e2;
+            s3 += e3;
+            if constexpr (kEnt) {
+              w0 = __builtin_fmaf(e0, fmaxf(d0, -126.f), w0);
+              w1 = __builtin_fmaf(e1, fmaxf(d1, -126.f), w1);
+              w2 = __builtin_fmaf(e2, fmaxf(d2, -126.f), w2);
+              w3 = __builtin_fmaf(e3, fmaxf(d3, -126.f), w3);
+            }
+          }
+        float s = (s0 + s1) + (s2 + s3);
+        s = s + __shfl_xor(s, 32);
+        float w = 0.f;
+        if constexpr (kEnt) {
+          w = (w0 + w1) + (w2 + w3);
+          w = w + __shfl_xor(w, 32);
+        }
+        const int ti = c.tok[j];
+        if constexpr (kStoreD) {
+          // codes of the wave's 128 entries for this token column, 16 bytes per lane: per 32-entry
+          // block, v_permlane32_swap on the packed groups (2h, 2h + 1) hands lane l entries
+          // 16 h + 0..7 and lane l + 32 entries 16 h + 8..15 of the same token (as for dL/dz).
+          // Rows of padded token columns (ti >= Na, still inside the block's rows) are written
+          // too and never read as d.
+          uint16_t* drow = a.dbuf + (size_t)ti * a.d_pitch + vq;
+          const float k1 = -c2 * 512.f;
+          const float k2 = __builtin_fmaf(mx, 512.f, 0.5f);
 #pragma unroll
-      for (int i = 0; i < kBlkA; ++i)
+          for (int i = 0; i < kBlkA; ++i) {
+            u32x2 pk[4];
 #pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          const float d0 = __builtin_fmaf(acc.c[i][j][r + 0], c2, -mx);
-          const float d1 = __builtin_fmaf(acc.c[i][j][r + 1], c2, -mx);
-          const float d2 = __builtin_fmaf(acc.c[i][j][r + 2], c2, -mx);
-          const float d3 = __builtin_fmaf(acc.c[i][j][r + 3], c2, -mx);
-          const float e0 = __builtin_amdgcn_exp2f(d0);
-          const float e1 = __builtin_amdgcn_exp2f(d1);
-          const float e2 = __builtin_amdgcn_exp2f(d2);
-          const float e3 = __builtin_amdgcn_exp2f(d3);
-          s0 += e0;
-          s1 += e1;
-          s2 += e2;
-          s3 += e3;
-          if constexpr (kEnt) {
-            w0 = __builtin_fmaf(e0, fmaxf(d0, -126.f), w0);
-            w1 = __builtin_fmaf(e1, fmaxf(d1, -126.f), w1);
-            w2 = __builtin_fmaf(e2, fmaxf(d2, -126.f), w2);
-            w3 = __builtin_fmaf(e3, fmaxf(d3, -126.f), w3);
+            for (int g = 0; g < 4; ++g) {
+              pk[g][0] = pack_dcode(val(i, 4 * g + 0), val(i, 4 * g + 1), k1, k2);
+              pk[g][1] = pack_dcode(val(i, 4 * g + 2), val(i, 4 * g + 3), k1, k2);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const auto s0 =
+                  __builtin_amdgcn_permlane32_swap(pk[2 * h][0], pk[2 * h + 1][0], false, false);
+              const auto s1 =
+                  __builtin_amdgcn_permlane32_swap(pk[2 * h][1], pk[2 * h + 1][1], false, false);
+              u32x4 q;
+              q.x = s0[0];
+              q.y = s1[0];
+              q.z = s0[1];
+              q.w = s1[1];
+              *reinterpret_cast<u32x4*>(drow + 32 * i + 16 * h + 8 * (lane >> 5)) = q;
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
-      float s = (s0 + s1) + (s2 + s3);
-      s = s + __shfl_xor(s, 32);
-      float w = 0.f;
-      if constexpr (kEnt) {
-        w = (w0 + w1) + (w2 + w3);
-        w = w + __shfl_xor(w, 32);
-      }
-      const int ti = c.tok[j];
-      if constexpr (kStoreD) {
-        // codes of the wave's 128 entries for this token column, 16 bytes per lane: per 32-entry
-        // block, v_permlane32_swap on the packed groups (2h, 2h + 1) hands lane l entries
-        // 16 h + 0..7 and lane l + 32 entries 16 h + 8..15 of the same token (as for dL/dz).
-        // Rows of padded token columns (ti >= Na, still inside the block's rows) are written
-        // too and never read as d.
-        uint16_t* drow = a.dbuf + (size_t)ti * a.d_pitch + vq;
-        const float k1 = -c2 * 512.f;
-        const float k2 = __builtin_fmaf(mx, 512.f, 0.5f);
-#pragma unroll
-        for (int i = 0; i < kBlkA; ++i) {
-          u32x2 pk[4];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            pk[g][0] = pack_dcode(acc.c[i][j][4 * g + 0], acc.c[i][j][4 * g + 1], k1, k2);
-            pk[g][1] = pack_dcode(acc.c[i][j][4 * g + 2], acc.c[i][j][4 * g + 3], k1, k2);
+        if (ti < Na) {
+          if (lane < 32) {
+            a.part_max[col * pst + ti] = mx;
+            a.part_sum[col * pst + ti] = s;
+            if constexpr (kEnt) a.part_w[col * pst + ti] = w;
           }
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const auto s0 =
-                __builtin_amdgcn_permlane32_swap(pk[2 * h][0], pk[2 * h + 1][0], false, false);
-            const auto s1 =
-                __builtin_amdgcn_permlane32_swap(pk[2 * h][1], pk[2 * h + 1][1], false, false);
-            u32x4 q;
-            q.x = s0[0];
-            q.y = s1[0];
-            q.z = s0[1];
-            q.w = s1[1];
-            *reinterpret_cast<u32x4*>(drow + 32 * i + 16 * h + 8 * (lane >> 5)) = q;
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          if (hit) a.target_logit[ti] = zsel * a.inv_t;
         }
-      }
-      if (ti < Na) {
-        if (lane < 32) {
-          a.part_max[col * pst + ti] = mx;
-          a.part_sum[col * pst + ti] = s;
-          if constexpr (kEnt) a.part_w[col * pst + ti] = w;
-        }
-        if (hit) a.target_logit[ti] = zsel * a.inv_t;
-      }
+      };
+      if (tail) column(std::true_type{});
+      else column(std::false_type{});
     }
   };
 
