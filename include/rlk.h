@@ -214,7 +214,10 @@ rlk_status_t rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* ta
  * clamped to 65535, and turns it into dL/dz once lse is known: three GEMMs per step instead of
  * four.  The code moves each p by at most 2^-10 ln 2 relative, whatever d is (entries with
  * d <= -128 have p < 2^-128); dL/dz is rounded to bf16 as in the two-call path, whose dh and
- * dW differ from these only by such rounding.
+ * dW differ from these only by such rounding.  With every column's dL/dz in place, one launch
+ * per block runs both GEMMs over the whole vocabulary; dL/dh sums the two halves of the
+ * vocabulary apart and then adds them (the two-call path sums 16384-entry pieces of 32768-entry
+ * chunks), a split fixed by V alone.
  *   h, W, targets, mask, N, H, V, dtype, temperature, adv: as for rlk_linear_logp_bwd
  *   logp [N] float  out: as rlk_linear_logp_fwd
  *   lse  [N] float  out (required: the gradient pass reads it back)

@@ -271,7 +271,6 @@ rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, con
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
   e = launch_zero(dh, (size_t)N * (size_t)H, st);  // inactive rows stay 0
   if (e != hipSuccess) return RLK_ERROR_DEVICE;
-  const int nchunks = (int)((V + kBwdChunk - 1) / kBwdChunk);
   for (int b = 0; b < nblk; ++b) {
     e = launch_select_block(idx, desc, b, np, bidx, bn, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
@@ -290,11 +289,10 @@ rlk_status_t run_fused(const void* h, const void* W, const int32_t* targets, con
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
     e = launch_bwd_transpose(a, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
-    for (int ch = 0; ch < nchunks; ++ch) {
-      e = launch_bwd_chunk_gemms(a, ch, grid, b > 0, st);
-      if (e != hipSuccess) return RLK_ERROR_DEVICE;
-    }
-    e = launch_bwd_finish(a, st);
+    // dL/dz of every column is in place: both GEMMs of the whole vocabulary in one launch
+    e = launch_bwd_whole_gemms(a, grid, b > 0, st);
+    if (e != hipSuccess) return RLK_ERROR_DEVICE;
+    e = launch_bwd_finish_whole(a, st);
     if (e != hipSuccess) return RLK_ERROR_DEVICE;
   }
   if (loss) return dev_status(launch_ratio_kl_loss(loss->args, loss->sums, st));

@@ -28,6 +28,11 @@
 //                written 16 bytes at a time).
 // dh_chunk and dw_chunk run as the two sections of one launch (grad_chunk_kernel): the
 // dL/dW tiles are claimed at run time, so they fill the last round of dL/dh tiles.
+// The fused forward + backward has dL/dz of the whole vocabulary in place for a token block at
+// once, so there one launch per block covers every column (grad_whole_kernel): dL/dh in two
+// pieces, the two halves of the vocabulary (whole_dh_split), each tile summing its whole half,
+// and dL/dW over every vocabulary row; the finish then adds the second half to the first.  A
+// token's dL/dh is again a sum fixed by V alone (it differs in rounding from the chunked one).
 // The active tokens are taken in blocks (compacted order, at most the buffers' capacity, all of
 // one size but the last), each block a batch of its own for every kernel here (idx and
 // n_active hold the block's indices and count), so the buffers hold one block and the workspace
@@ -363,12 +368,16 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 v, int lane) {
 // kFirst: the first chunk, whose tiles store their sums (later chunks add to them).
 // kSpread: a last, partial round of tiles is dealt out across the XCDs (for the combined
 // launch, whose work-groups go on to claim dL/dW tiles from their XCD's counter).
-template <bool kFirst, bool kSpread>
+// kWhole: the whole vocabulary as one chunk (c0 = 0; Gv holds every column), split into the
+// pieces whole_dh_split gives; every piece stores its sum.
+template <bool kFirst, bool kSpread, bool kWhole = false>
 __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, int c0) {
+  static_assert(!kWhole || kFirst, "a whole-vocabulary piece is its token's only sum");
   const int Na = *a.n_active;
-  const int vc = min(kBwdChunk, a.V - c0);
+  const int vc = kWhole ? a.V : min(kBwdChunk, a.V - c0);
   const int kc = (vc + 63) & ~63;  // K extent (zero columns past V)
-  const int npiece = (kc + kDhSplitK - 1) / kDhSplitK;
+  const int split = kWhole ? whole_dh_split(a.V) : kDhSplitK;
+  const int npiece = (kc + split - 1) / split;
   const int nTokTiles = (Na + kTile - 1) / kTile;
   const int nHTiles = a.H / kTile;
   const int per_piece = nTokTiles * nHTiles;
@@ -392,8 +401,8 @@ __device__ __forceinline__ void dh_chunk_tiles(RingSmem& sm, const BwdArgs& a, i
     c.abase = tt * kTile;
     c.bbase = ht * kTile;
     c.piece = piece;
-    const int k0 = piece * kDhSplitK;  // K entries [k0, k1) of this piece
-    const int k1 = min(kc, k0 + kDhSplitK);
+    const int k0 = piece * split;  // K entries [k0, k1) of this piece
+    const int k1 = min(kc, k0 + split);
     src.nk = (k1 - k0) * 2 / kKBytes;
     src.a_kstep = kKBytes;
     src.b_kstep = 64 * w_pitch;  // 64 W rows per stage
@@ -494,11 +503,12 @@ __global__ __launch_bounds__(256) void dh_finish_kernel(BwdArgs a) {
 // order.  kAccum: a later token block, whose sums are added to the dL/dW rows the earlier blocks
 // stored (the first block stores, so dW is the blocks' sums in ascending block order); an empty
 // later block changes nothing and returns at once.
-template <bool kClaimed, bool kAccum>
+// kWhole: every vocabulary row (c0 = 0; Gv holds every column).
+template <bool kClaimed, bool kAccum, bool kWhole = false>
 __device__ __forceinline__ void dw_chunk_tiles(RingSmem& sm, const BwdArgs& a, int c0) {
   const int Na = *a.n_active;
   if (kAccum && Na == 0) return;
-  const int vc = min(kBwdChunk, a.V - c0);
+  const int vc = kWhole ? a.V : min(kBwdChunk, a.V - c0);
   const int nVocTiles = (vc + kTile - 1) / kTile;
   const int nHTiles = a.H / kTile;
   const int band = nVocTiles < 8 ? nVocTiles : 8;
@@ -605,6 +615,17 @@ __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, int c0)
   dw_chunk_tiles<true, kAccum>(sm, a, c0);
 }
 
+// The same for the whole vocabulary at once, when Gv holds every column (the fused forward +
+// backward): the dL/dh tiles of the whole-vocabulary pieces, then claimed dL/dW tiles of every
+// vocabulary row.  One launch per token block instead of one per chunk, so a block has one
+// partial last round instead of one per chunk.
+template <bool kAccum>
+__global__ __launch_bounds__(kThreads) void grad_whole_kernel(BwdArgs a) {
+  __shared__ RingSmem sm;
+  dh_chunk_tiles<true, true, true>(sm, a, 0);
+  dw_chunk_tiles<true, kAccum, true>(sm, a, 0);
+}
+
 }  // namespace
 
 hipError_t launch_zero(float* p, size_t n, hipStream_t stream) {
@@ -683,6 +704,25 @@ hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, bool ac
                                   hipStream_t stream) {
   const int c0 = chunk * kBwdChunk;
   return launch_grad_chunk(a, c0, grid, accum_dw, stream);
+}
+
+hipError_t launch_bwd_whole_gemms(const BwdArgs& a, int grid, bool accum_dw, hipStream_t stream) {
+  if (!a.gv_full) return hipErrorInvalidValue;
+  hipError_t e = launch_zero(reinterpret_cast<float*>(a.sched), 8, stream);  // claim counters
+  if (e != hipSuccess) return e;
+  if (accum_dw)
+    hipLaunchKernelGGL(grad_whole_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(grad_whole_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_finish_whole(const BwdArgs& a, hipStream_t stream) {
+  const int kc = (a.V + 63) / 64 * 64;
+  const int split = whole_dh_split(a.V);
+  if ((kc + split - 1) / split == 2)
+    hipLaunchKernelGGL(dh_finish_kernel<2>, dim3(2048), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {

@@ -14,6 +14,15 @@ constexpr int kVocabPartial = 128;  // vocabulary entries per partial-statistics
 constexpr int kBwdChunk = RLK_BWD_CHUNK;  // vocabulary entries per backward chunk
 constexpr int kDhSplitK = RLK_DH_SPLIT;   // dL/dh sums each piece of a chunk apart
 constexpr int kDhPieces = kBwdChunk / kDhSplitK;  // pieces of a full chunk
+// dL/dh pieces when one launch covers the whole vocabulary (the fused forward + backward, whose
+// dL/dz buffer holds every column): the K extent (V rounded up to 64) in two halves, each
+// rounded up to 64 entries (one piece when that covers it).  A rule of V alone, so a token's
+// dL/dh bits never depend on the batch; two pieces put the same K on a tile's critical path as
+// the chunked pieces (half the vocabulary).
+__host__ __device__ constexpr int whole_dh_split(int V) {
+  return (((V + 63) / 64 * 64) / 2 + 63) / 64 * 64;
+}
+static_assert(kDhPieces >= 2, "the whole-vocabulary split needs the second piece buffer");
 // The backward (and the KL paths) take the active tokens in blocks of at most a capacity the
 // host derives from H (a multiple of 256, at most 65536), in compacted order: its buffers hold
 // one block, so the workspace does not grow past that many tokens.
@@ -156,6 +165,10 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, int chunk, int grid, bool accum_dw
 hipError_t launch_bwd_chunk_gemms(const BwdArgs& a, int chunk, int grid, bool accum_dw,
                                   hipStream_t stream);
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dh[idx] = sum of pieces
+// With Gv holding every column (gv_full): dL/dh and dL/dW of the whole vocabulary in one launch,
+// dL/dh in the whole_dh_split pieces; then their sum into dh[idx].
+hipError_t launch_bwd_whole_gemms(const BwdArgs& a, int grid, bool accum_dw, hipStream_t stream);
+hipError_t launch_bwd_finish_whole(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fill(float* p, size_t n, float value, hipStream_t stream);
 hipError_t launch_dz_from_d(const DzArgs& a, hipStream_t stream);
 
