@@ -77,8 +77,9 @@ def test_small_full(T):
 
 
 def test_two_chunks_ragged():
-    # two backward chunks read from one stored row: the second chunk starts at column chunk of
-    # every row, with entries past the dL/dh split point and a ragged tail
+    # a vocabulary of two backward chunks of the two-call path plus a ragged tail; the fused
+    # call's dL/dh splits it into its two halves (the split at 24768 of 49472 columns, inside a
+    # 256-entry vocabulary tile) and its dL/dW tiles end in the ragged last tile
     chunk, split = _chunking()
     _full_compare(wl.make(wl.scaled_spec(5, N=300, H=256, V=chunk + split + 300, n_seq=2,
                                          len_lo=100, len_hi=200, seed=96)))
