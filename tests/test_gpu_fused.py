@@ -281,6 +281,18 @@ def test_config5_full_size_sampled():
     assert colsum <= 1e-3 * scale
 
 
+def test_large_hidden_head_fused_sampled():
+    # the large-hidden head (H = 7168, V = 129280) through the fused call: 28 hidden tiles per
+    # dL/dh row block, dL/dW tiles of every vocabulary row in the one whole-vocabulary launch
+    w = wl.make(wl.scaled_spec(4, N=512, n_seq=2, len_lo=200, len_hi=300, prompt="floor_half",
+                               seed=152, backward=True))
+    flush(f"  large-hidden head N={w.N} H={w.H} V={w.V}, {w.n_active} active")
+    d = upload(w)
+    logp, lse, dh, dW = run_fused(w, d)
+    _same_forward(w, d, logp, lse)
+    _sampled_compare(w, logp, lse, dh, dW, 153, n_tok=12, n_voc=16)
+
+
 def test_autograd_loss():
     import linear_selected_token_amd as rlk
     w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
