@@ -84,6 +84,8 @@ const char* build_info_string() {
              " | tile 256x256, K stage 128 B, 8 wave64 x 128x64, mfma 32x32x16 bf16 / 32x32x2 f32"
              " | vocab partial 128 | merge 8 strided slices + fixed tree"
              " | bwd chunk %d, dh split at %d"
+             " | fused fwd+bwd: one dh/dW launch per token block, dh in the two halves of V"
+             " (each rounded up to 64)"
              " | bwd token blocks: equal blocks of at most the largest multiple of 256 tokens whose"
              " buffers (%zu + %zu H bytes per token) fit %zu bytes",
              kBwdChunk, kDhSplitK, bwd_bytes_per_token(0), (bwd_bytes_per_token(1 << 10) - bwd_bytes_per_token(0)) >> 10,
