@@ -116,6 +116,40 @@ def test_agrees_with_two_call_backward():
     assert eh <= 5e-3 and ew <= 5e-3
 
 
+def test_out_of_range_targets_both_forms():
+    # an active token whose target is outside [0, V): logp NaN, lse unchanged, and dL/dz without
+    # the target term (-g_t p[t, v]) in the fused call and in the two calls alike.  Expected
+    # values: the oracle's gradients with those tokens' targets set to 0, minus the target
+    # term it then adds, g_t e_0, carried through dh_t = G_t W / T and dW_0 += G[t, 0] h_t / T.
+    from gpu_util import run_bwd
+    w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
+                               seed=191, T=0.7))
+    act = np.nonzero(w.mask)[0]
+    bad = np.array([int(act[3]), int(act[40])])
+    _, lse_ok, _, _ = run_fused(w)
+    w.targets[bad[0]] = w.V
+    w.targets[bad[1]] = -5
+    d = upload(w)
+    lp, lse, dh, dW = run_fused(w, d)
+    lp2, lse2, dh2, dW2 = run_bwd(w, d)
+    lp, lse, lp2 = lp.cpu().numpy(), lse.cpu().numpy(), lp2.cpu().numpy()
+    assert np.all(np.isnan(lp[bad])) and np.all(np.isnan(lp2[bad]))
+    assert np.array_equal(bits(lse), bits(lse_ok.cpu().numpy()))
+    keep = np.setdiff1d(act, bad)
+    assert not np.isnan(lp[keep]).any()
+    h64, W64 = oracle_inputs(w)
+    y0 = w.targets.copy()
+    y0[bad] = 0
+    odh, odW = oracle.linear_logp_grads(h64, W64, y0, w.mask, w.T, w.adv)
+    g = -w.adv[bad].astype(np.float64)
+    odh[bad] -= g[:, None] * W64[0][None, :] / w.T
+    odW[0] -= (g[:, None] * h64[bad]).sum(0) / w.T
+    for name, gh, gw in (("fused", dh, dW), ("two calls", dh2, dW2)):
+        gh = gh.cpu().numpy()
+        assert_rows(f"{name} dh (active rows, two without a target)", gh[act], odh[act], act)
+        assert_rows(f"{name} dW (every vocabulary row)", gw.cpu().numpy(), odW)
+
+
 def test_all_masked():
     import linear_selected_token_amd as rlk
     w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
