@@ -150,6 +150,27 @@ def test_out_of_range_targets_both_forms():
         assert_rows(f"{name} dW (every vocabulary row)", gw.cpu().numpy(), odW)
 
 
+def test_inactive_rows_may_hold_anything():
+    # inactive tokens are never read into the products: NaN and infinite h rows and
+    # out-of-range targets there change no bit of logp, lse, dh or dW (forward, two calls and
+    # the fused call)
+    from gpu_util import run_bwd
+    w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
+                               seed=192, T=0.9))
+    ref = [t.cpu() for t in run_bwd(w) + run_fused(w)]
+    off = np.nonzero(w.mask == 0)[0]
+    assert off.size > 0
+    r = np.random.default_rng(193)
+    poison = np.array([0x7FC0, 0x7F80, 0xFF80, 0x7F7F], dtype=np.uint16)  # NaN, +inf, -inf, max
+    w.h[off] = poison[r.integers(0, poison.size, (off.size, w.H))]
+    w.targets[off] = r.choice([-7, w.V, w.V + 1000], off.size)
+    got = [t.cpu() for t in run_bwd(w) + run_fused(w)]
+    names = ("logp", "lse", "dh", "dW", "fused logp", "fused lse", "fused dh", "fused dW")
+    for name, a, b in zip(names, got, ref):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
+    flush(f"  {off.size} inactive rows poisoned: every output keeps its bits")
+
+
 def test_all_masked():
     import linear_selected_token_amd as rlk
     w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
