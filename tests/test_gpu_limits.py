@@ -5,7 +5,9 @@
   - N = 2^22 tokens (the compaction walks 1024 blocks of 4096);
   - V = 2^22 entries (32768 partial columns per token in the merge);
   - the logits path at its largest vocabulary, 1,024,000 entries (a row's column statistics,
-    8 bytes per 128-entry column, fill 64 KB of LDS).
+    8 bytes per 128-entry column, fill 64 KB of LDS);
+  - the fused forward + backward at V = 2^22 (logp and lse over all active rows, sampled
+    dL/dh and dL/dW rows).
 Inputs are seeded normal draws made on the device; the oracle scores sampled rows from exact
 copies of them, within the 1e-3 gate."""
 import numpy as np
@@ -73,6 +75,44 @@ def test_most_tokens():
 
 def test_largest_vocabulary():
     _run(300, 64, 1 << 22, 1.0, 43, rows_extra=6)
+
+
+def test_fused_call_largest_vocabulary():
+    # the fused forward + backward at V = 2^22: 8 MiB of codes per token (256-token blocks, a
+    # 2.2 GB workspace), dL/dh tiles whose K is a whole half of the vocabulary (2^21 entries,
+    # 32768 K stages, W offsets past 2^31 bytes), 16384 vocabulary tiles of dL/dW
+    import linear_selected_token_amd as rlk
+    from gpu_util import assert_rows
+    N, H, V, T = 64, 256, 1 << 22, 1.0
+    r = np.random.default_rng(45)
+    h = _draw((N, H), 45)
+    W = _draw((V, H), 46, 1.0 / np.sqrt(H))
+    y = r.integers(0, V, N).astype(np.int32)
+    m = np.ones(N, np.uint8)
+    m[::5] = 0
+    adv = r.normal(0, 1, N).astype(np.float32)
+    dev = h.device
+    logp, lse, dh, dW = rlk.rlk_linear_logp_fwd_bwd(h, W, torch.from_numpy(y).to(dev),
+                                                    torch.from_numpy(m).to(dev), T,
+                                                    torch.from_numpy(adv).to(dev))
+    torch.cuda.synchronize()
+    act = np.nonzero(m)[0]
+    h64, W64 = _f64(h), _f64(W)
+    olp, olse = oracle.linear_logp(h64, W64, y, m, T)
+    err = float(np.abs(logp.cpu().numpy()[act] - olp[act]).max())
+    flush(f"  fused N={N} H={H} V={V}: max_abs_dlogp={err:.3e} over all {act.size} active rows")
+    assert err <= MAX_ABS_DLOGP
+    assert float(np.abs(lse.cpu().numpy()[act] - olse[act]).max()) <= MAX_ABS_DLOGP
+    rows = np.unique(np.concatenate([act[:2], act[-2:], r.choice(act, 4)]))
+    odh = oracle.grad_h_rows(h64, W64, y, m, T, adv, rows)
+    assert_rows("fused dh (sampled rows)", dh[torch.from_numpy(rows).to(dev)].cpu().numpy(),
+                odh, rows)
+    half = 1 << 21
+    vr = np.unique(np.concatenate([y[act[:4]], [0, 1, half - 1, half, V - 2, V - 1],
+                                   r.integers(0, V, 10)]))
+    odW = oracle.grad_W_rows(h64, W64, y, m, T, adv, vr, lse=olse)
+    assert_rows("fused dW (sampled rows)", dW[torch.from_numpy(vr).to(dev)].cpu().numpy(), odW,
+                vr)
 
 
 def test_logits_path_largest_vocabulary():
