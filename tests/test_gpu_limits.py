@@ -7,7 +7,7 @@
   - the logits path at its largest vocabulary, 1,024,000 entries (a row's column statistics,
     8 bytes per 128-entry column, fill 64 KB of LDS);
   - the fused forward + backward at V = 2^22 (logp and lse over all active rows, sampled
-    dL/dh and dL/dW rows).
+    dL/dh and dL/dW rows), and the two calls' backward on the same inputs.
 Inputs are seeded normal draws made on the device; the oracle scores sampled rows from exact
 copies of them, within the 1e-3 gate."""
 import numpy as np
@@ -77,7 +77,7 @@ def test_largest_vocabulary():
     _run(300, 64, 1 << 22, 1.0, 43, rows_extra=6)
 
 
-def test_fused_call_largest_vocabulary():
+def test_backward_largest_vocabulary():
     # the fused forward + backward at V = 2^22: 8 MiB of codes per token (256-token blocks, a
     # 2.2 GB workspace), dL/dh tiles whose K is a whole half of the vocabulary (2^21 entries,
     # 32768 K stages, W offsets past 2^31 bytes), 16384 vocabulary tiles of dL/dW
@@ -113,6 +113,15 @@ def test_fused_call_largest_vocabulary():
     odW = oracle.grad_W_rows(h64, W64, y, m, T, adv, vr, lse=olse)
     assert_rows("fused dW (sampled rows)", dW[torch.from_numpy(vr).to(dev)].cpu().numpy(), odW,
                 vr)
+    # the two calls on the same inputs: 128 vocabulary chunks of 32768 entries
+    yt, mt, at = (torch.from_numpy(x).to(dev) for x in (y, m, adv))
+    _, lse2 = rlk.rlk_linear_logp_fwd(h, W, yt, mt, T)
+    dh2, dW2 = rlk.rlk_linear_logp_bwd(h, W, yt, mt, T, at, lse2)
+    torch.cuda.synchronize()
+    assert_rows("two calls dh (sampled rows)",
+                dh2[torch.from_numpy(rows).to(dev)].cpu().numpy(), odh, rows)
+    assert_rows("two calls dW (sampled rows)",
+                dW2[torch.from_numpy(vr).to(dev)].cpu().numpy(), odW, vr)
 
 
 def test_logits_path_largest_vocabulary():
