@@ -7,7 +7,8 @@
   - the logits path at its largest vocabulary, 1,024,000 entries (a row's column statistics,
     8 bytes per 128-entry column, fill 64 KB of LDS);
   - the fused forward + backward at V = 2^22 (logp and lse over all active rows, sampled
-    dL/dh and dL/dW rows), and the two calls' backward on the same inputs.
+    dL/dh and dL/dW rows), and the two calls' backward on the same inputs;
+  - both backward forms at N = 2^22 - 1 tokens (dozens of token blocks).
 Inputs are seeded normal draws made on the device; the oracle scores sampled rows from exact
 copies of them, within the 1e-3 gate."""
 import numpy as np
@@ -122,6 +123,44 @@ def test_backward_largest_vocabulary():
                 dh2[torch.from_numpy(rows).to(dev)].cpu().numpy(), odh, rows)
     assert_rows("two calls dW (sampled rows)",
                 dW2[torch.from_numpy(vr).to(dev)].cpu().numpy(), odW, vr)
+
+
+def test_backward_most_tokens():
+    # both backward forms at N = 2^22 - 1 tokens (h just under 2^31 bytes at H = 256), in
+    # dozens of token blocks each
+    import linear_selected_token_amd as rlk
+    from gpu_util import assert_rows
+    N, H, V, T = (1 << 22) - 1, 256, 1000, 1.1
+    r = np.random.default_rng(47)
+    h = _draw((N, H), 47)
+    W = _draw((V, H), 48, 1.0 / np.sqrt(H))
+    y = r.integers(0, V, N).astype(np.int32)
+    m = np.ones(N, np.uint8)
+    m[::7] = 0
+    adv = r.normal(0, 1, N).astype(np.float32)
+    dev = h.device
+    yt, mt, at = (torch.from_numpy(x).to(dev) for x in (y, m, adv))
+    logp, lse, dh, dW = rlk.rlk_linear_logp_fwd_bwd(h, W, yt, mt, T, at)
+    _, lse2 = rlk.rlk_linear_logp_fwd(h, W, yt, mt, T)
+    dh2, dW2 = rlk.rlk_linear_logp_bwd(h, W, yt, mt, T, at, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    act = np.nonzero(m)[0]
+    rows = np.unique(np.concatenate([act[:2], act[-3:], r.choice(act, 12),
+                                     act[65536 * np.arange(1, 4) - 1], act[65536 * np.arange(1, 4)]]))
+    h64, W64 = _f64(h), _f64(W)
+    olp, olse = oracle.linear_logp(h64, W64, y, m, T)
+    err = float(np.abs(logp.cpu().numpy()[act] - olp[act]).max())
+    flush(f"  N={N} H={H} V={V}: max_abs_dlogp={err:.3e} over all {act.size} active rows")
+    assert err <= MAX_ABS_DLOGP
+    odh = oracle.grad_h_rows(h64, W64, y, m, T, adv, rows)
+    vr = np.unique(np.concatenate([[0, 255, 256, V - 1], r.integers(0, V, 12)]))
+    odW = oracle.grad_W_rows(h64, W64, y, m, T, adv, vr, lse=olse)
+    for name, gh, gw in (("fused", dh, dW), ("two calls", dh2, dW2)):
+        assert_rows(f"{name} dh (sampled rows)",
+                    gh[torch.from_numpy(rows).to(dev)].cpu().numpy(), odh, rows)
+        assert_rows(f"{name} dW (sampled rows)",
+                    gw[torch.from_numpy(vr).to(dev)].cpu().numpy(), odW, vr)
 
 
 def test_logits_path_largest_vocabulary():
