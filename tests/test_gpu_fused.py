@@ -70,6 +70,35 @@ def _full_compare(w):
     return dh, dW
 
 
+def _sweep_specs(n, seed):
+    """Seeded shapes across tile, column, piece and chunk edges: N in [1, 900], H in {256, 512,
+    768}, V in [1, 40000] (log-uniform), T in [0.5, 1.5]; one to three packed sequences."""
+    r = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        N = int(r.integers(1, 901))
+        n_seq = int(min(N, r.integers(1, 4)))
+        V = int(np.exp(r.uniform(0.0, np.log(40000.0)))) + 1
+        out.append(wl.scaled_spec(5, N=N, H=int(r.choice([256, 512, 768])), V=V, n_seq=n_seq,
+                                  len_lo=1, len_hi=N, seed=700 + k, T=float(r.uniform(0.5, 1.5))))
+    return out
+
+
+@pytest.mark.parametrize("spec", _sweep_specs(16, 211), ids=lambda s: f"N{s.N}-H{s.H}-V{s.V}")
+def test_random_shapes_sweep(spec):
+    # the fused call in full against the oracle (every active dh row, every dW row and tile),
+    # and the two calls' gradients beside it
+    from gpu_util import run_bwd
+    w = wl.make(spec)
+    dh, dW = _full_compare(w)
+    _, _, dh2, dW2 = run_bwd(w)
+    act = np.nonzero(w.mask)[0]
+    h64, W64 = oracle_inputs(w)
+    odh, odW = oracle.linear_logp_grads(h64, W64, w.targets, w.mask, w.T, w.adv)
+    assert_rows("two calls dh (every active row)", dh2.cpu().numpy()[act], odh[act], act)
+    assert_rows("two calls dW (every vocabulary row)", dW2.cpu().numpy(), odW)
+
+
 @pytest.mark.parametrize("T", [1.0, 0.7])
 def test_small_full(T):
     _full_compare(wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64,
