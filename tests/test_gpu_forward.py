@@ -42,6 +42,37 @@ def _compare(w, lp, lse, rows=None, tol=MAX_ABS_DLOGP):
     return d.max()
 
 
+def _sweep_specs(n, seed):
+    """Seeded forward shapes: N in [1, 2000], H a multiple of 64 in [64, 1024], V in [1, 70000]
+    (log-uniform), bf16 or fp32, T in [0.3, 2]."""
+    r = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        N = int(r.integers(1, 2001))
+        V = int(np.exp(r.uniform(0.0, np.log(70000.0)))) + 1
+        out.append(wl.scaled_spec(2, N=N, H=64 * int(r.integers(1, 17)), V=V,
+                                  dtype=str(r.choice(["bf16", "fp32"])),
+                                  n_seq=int(min(N, r.integers(1, 5))), len_lo=1, len_hi=N,
+                                  seed=800 + k, T=float(r.uniform(0.3, 2.0))))
+    return out
+
+
+@pytest.mark.parametrize("spec", _sweep_specs(16, 311),
+                         ids=lambda s: f"N{s.N}-H{s.H}-V{s.V}-{s.dtype}")
+def test_random_shapes_sweep(spec):
+    # logp and lse of every active token against the oracle, and the entropy forward's logp and
+    # lse bit-identical to the plain forward's
+    import linear_selected_token_amd as rlk
+    w = wl.make(spec)
+    d = upload(w)
+    lp, lse = run_fwd(w, d)
+    _compare(w, lp, lse)
+    lp2, lse2, _ = rlk.rlk_linear_logp_fwd_entropy(d["h"], d["W"], d["targets"], d["mask"], w.T)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(lp2.cpu().numpy()), bits(lp))
+    assert np.array_equal(bits(lse2.cpu().numpy()), bits(lse))
+
+
 def test_device_is_gfx950():
     import linear_selected_token_amd as rlk
     props = torch.cuda.get_device_properties(0)
