@@ -157,6 +157,40 @@ def _bwd(w, ht, Wt, reverse, coef):
     return dh.cpu().numpy(), dW.cpu().numpy()
 
 
+def _sweep_cases(n, seed):
+    """Seeded (spec, H_t, reverse) cases: N in [1, 700], H_s and H_t multiples of 256 up to 768,
+    V in [1, 40000] (log-uniform), T in [0.5, 1.5]."""
+    r = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        N = int(r.integers(1, 701))
+        V = int(np.exp(r.uniform(0.0, np.log(40000.0)))) + 1
+        spec = wl.scaled_spec(5, N=N, H=256 * int(r.integers(1, 4)), V=V,
+                              n_seq=int(min(N, r.integers(1, 4))), len_lo=1, len_hi=N,
+                              seed=900 + k, T=float(r.uniform(0.5, 1.5)))
+        out.append((spec, 256 * int(r.integers(1, 4)), bool(r.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _sweep_cases(10, 411),
+                         ids=lambda c: f"N{c[0].N}-Hs{c[0].H}-Ht{c[1]}-V{c[0].V}-"
+                                       f"{'rev' if c[2] else 'fwd'}")
+def test_random_shapes_sweep(case):
+    # both KL directions and both heads' lse of every active token, and the gradient of one
+    # direction (every dh_s and dW_s row), against the oracle
+    spec, Ht, reverse = case
+    w = wl.make(spec)
+    ht, Wt = _teacher(w, Ht, spec.seed + 50)
+    _check_fwd(w, ht, Wt)
+    c = np.random.default_rng(spec.seed + 51).uniform(0.5, 1.5, w.N).astype(np.float32)
+    dh, dW = _bwd(w, ht, Wt, reverse, c)
+    odh, odW = od.kl_grads(*(wl.as_f64(x) for x in (w.h, w.W, ht, Wt)), w.mask, w.T, c, reverse)
+    act = np.nonzero(w.mask)[0]
+    assert_rows("dh (every active row)", dh[act], odh[act], act)
+    assert_rows("dW (every vocabulary row)", dW, odW)
+    assert not dh[w.mask == 0].any()
+
+
 @pytest.mark.parametrize("reverse", [False, True])
 def test_bwd_small_full(reverse):
     w = wl.make(wl.scaled_spec(5, N=600, H=512, V=3000, n_seq=4, len_lo=64, len_hi=300,
