@@ -559,6 +559,13 @@ def test_entropy_bonus_fused():
                                           len_hi=300, seed=103, T=0.8)), 104)
 
 
+@pytest.mark.parametrize("spec", _sweep_specs(8, 212), ids=lambda s: f"N{s.N}-H{s.H}-V{s.V}")
+def test_entropy_bonus_fused_sweep(spec):
+    # the fused call with an entropy bonus over seeded random shapes: logp, lse and entropy
+    # bitwise the entropy forward's, gradients against the oracle in full
+    _check_entropy(wl.make(spec), spec.seed + 1)
+
+
 def test_entropy_bonus_fused_peaked():
     # h x 8: peaked softmaxes, where p ln p of the tail entries is tiny but their codes are far
     # from 0
