@@ -464,6 +464,13 @@ def test_ppo_fused_matches_chain_and_oracle():
                                       seed=101, T=0.9)), 102)
 
 
+@pytest.mark.parametrize("spec", _sweep_specs(6, 213), ids=lambda s: f"N{s.N}-H{s.H}-V{s.V}")
+def test_ppo_fused_sweep(spec):
+    # the fused PPO step over seeded random shapes: per-token outputs bitwise the chain of
+    # calls, gradients against the oracle's chain rule in full
+    _check_ppo(wl.make(spec), spec.seed + 1)
+
+
 def test_ppo_fused_token_blocks():
     # two token blocks over the Qwen3-8B vocabulary: each block's loss fragment sees its own
     # tokens' final logp
