@@ -111,3 +111,47 @@ def test_entropy_invariance_config3():
     fam = wl.Family(wl.CONFIGS[3])
     fam.use_targets(np.load(os.path.join(HERE, "golden", "cfg3_sampled_targets.npy")))
     assert _sweep(fam, 8, "entropy config3", fwd=_fwd_entropy) == 0
+
+
+def _fused_keyed(w):
+    """logp and lse bits and a digest of the dL/dh row's bytes of every active token of w, keyed
+    by (sequence, position), from one fused forward + backward call."""
+    import hashlib
+    import linear_selected_token_amd as rlk
+    d = upload(w)
+    logp, lse, dh, _ = rlk.rlk_linear_logp_fwd_bwd(d["h"], d["W"], d["targets"], d["mask"], w.T,
+                                                   d["adv"])
+    torch.cuda.synchronize()
+    lp, ls, dh = logp.cpu().numpy(), lse.cpu().numpy(), dh.cpu().numpy()
+    out = {}
+    for i, k in enumerate(w.key()):
+        if k[0] < 0 or not w.mask[i]:
+            continue
+        out[k] = (int(bits(lp[i:i + 1])[0]), int(bits(ls[i:i + 1])[0]),
+                  hashlib.sha1(dh[i].tobytes()).hexdigest())
+    return out
+
+
+def test_fused_invariance_config3():
+    """The fused forward + backward on the N=16384 workload (four token blocks of the default
+    workspace): each active token's logp, lse and dL/dh row bit-identical with 8 sequences alone
+    (one block each), shuffled, padded, all-active (five blocks) and a subset."""
+    fam = wl.Family(wl.CONFIGS[3])
+    fam.use_targets(np.load(os.path.join(HERE, "golden", "cfg3_sampled_targets.npy")))
+    ref = _fused_keyed(fam.batch())
+    cases = [(f"alone {s}", fam.alone(s)) for s in range(8)]
+    cases += [("shuffle", fam.shuffled(300)), ("padded", fam.padded(301)),
+              ("all active", fam.all_active()),
+              ("subset", fam.subset(list(range(0, fam.n_seq, 3))))]
+    total = checked = 0
+    for name, w in cases:
+        got = _fused_keyed(w)
+        m = _mismatches(ref, got)
+        total += m
+        checked += sum(1 for k in got if k in ref)
+        if m:
+            flush(f"  fused {name}: {m} mismatches")
+    flush(f"  fused config3: {total} mismatches over {checked} active-token comparisons "
+          "(logp, lse and the dL/dh row)")
+    assert checked > 0 and total == 0
+
